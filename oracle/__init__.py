@@ -1,0 +1,156 @@
+"""fp64 CPU oracle for the diagonal linear recurrence and the layers built on it.
+
+TEST INFRASTRUCTURE ONLY: the test-suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product library never does.  It
+shares no code with the HIP path.  The arithmetic lives in ``lrs_oracle.c``
+(plain sequential loops in double precision); this module only marshals numpy
+arrays into it and builds it with gcc.
+
+Every function takes the exact values the device path consumes (fp32 or bf16
+values, widened exactly to float64) and returns float64 arrays.
+
+Functions (page citations are in ``lrs_oracle.c``):
+  scan_fwd(a, b, h0)            h_t = a_t h_{t-1} + b_t over the last axis
+  scan_bwd(a, h, h0, g)         reverse-time adjoint -> (da, db, dh0)
+  sru_fwd(zf, zr, zx, bf, br)   SRU layer on [T, B, D] arrays -> (h, c_last)
+  rnn_seq(w, u, h0)             sequential h_t = tanh(w h_{t-1} + u_t)
+  deer(w, u, h0, ...)           Newton / DEER iterations -> (h, iters, deltas)
+
+Parity status: all five are pinned by tests/test_oracle_*.py against closed
+forms, exact rational brute force, adjoint identities, finite differences and
+Newton invariants.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lrs_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liblrs_oracle.so")
+_lib = None
+
+_c_dp = ctypes.POINTER(ctypes.c_double)
+_i64 = ctypes.c_int64
+
+
+def build(force: bool = True) -> str:
+    """Compile lrs_oracle.c with gcc into oracle/liblrs_oracle.so."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+               "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build(force=False)
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.lrs_oracle_scan_fwd.argtypes = [_c_dp, _c_dp, _c_dp, _c_dp, _i64, _i64, ctypes.c_int]
+    lib.lrs_oracle_scan_bwd.argtypes = [_c_dp, _c_dp, _c_dp, _c_dp, _c_dp, _c_dp, _c_dp,
+                                        _i64, _i64, ctypes.c_int]
+    lib.lrs_oracle_sru_fwd.argtypes = [_c_dp] * 8 + [_i64, _i64, _i64, ctypes.c_int]
+    lib.lrs_oracle_rnn_seq.argtypes = [_c_dp, _c_dp, _c_dp, _c_dp, _i64, _i64, _i64, ctypes.c_int]
+    lib.lrs_oracle_deer.argtypes = [_c_dp, _c_dp, _c_dp, _c_dp, _c_dp, _i64, _i64, _i64,
+                                    ctypes.c_double, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                    _c_dp, ctypes.c_int]
+    for fn in (lib.lrs_oracle_scan_fwd, lib.lrs_oracle_scan_bwd, lib.lrs_oracle_sru_fwd,
+               lib.lrs_oracle_rnn_seq, lib.lrs_oracle_deer):
+        fn.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _f64(x):
+    return None if x is None else np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data_as(_c_dp)
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise RuntimeError(f"oracle {name} failed with code {rc}")
+
+
+def scan_fwd(a, b, h0=None, nthreads: int = 0):
+    """h_t = a_t*h_{t-1} + b_t along the last axis.  a, b: [..., T]; h0: [...]."""
+    a, b, h0 = _f64(a), _f64(b), _f64(h0)
+    if a.shape != b.shape:
+        raise ValueError("a and b must have the same shape")
+    T = a.shape[-1] if a.ndim else 0
+    C = a.size // T if T else 0
+    if h0 is not None and h0.size != C:
+        raise ValueError("h0 must hold one value per channel")
+    h = np.empty_like(a)
+    _check(_load().lrs_oracle_scan_fwd(_ptr(a), _ptr(b), _ptr(h0), _ptr(h), C, T, nthreads),
+           "scan_fwd")
+    return h
+
+
+def scan_bwd(a, h, h0, g, nthreads: int = 0):
+    """Adjoint of scan_fwd for L = sum <g, h>.  Returns (da, db, dh0)."""
+    a, h, h0, g = _f64(a), _f64(h), _f64(h0), _f64(g)
+    if not (a.shape == h.shape == g.shape):
+        raise ValueError("a, h, g must have the same shape")
+    T = a.shape[-1]
+    C = a.size // T if T else 0
+    da, db = np.empty_like(a), np.empty_like(a)
+    dh0 = np.empty(a.shape[:-1], dtype=np.float64)
+    _check(_load().lrs_oracle_scan_bwd(_ptr(a), _ptr(h), _ptr(h0), _ptr(g), _ptr(da), _ptr(db),
+                                       _ptr(dh0), C, T, nthreads), "scan_bwd")
+    return da, db, dh0
+
+
+def sru_fwd(zf, zr, zx, bf, br, c0=None, nthreads: int = 0):
+    """SRU layer on [T, B, D] pre-activations.  Returns (h [T,B,D], c_last [B,D])."""
+    zf, zr, zx, bf, br, c0 = map(_f64, (zf, zr, zx, bf, br, c0))
+    if not (zf.shape == zr.shape == zx.shape) or zf.ndim != 3:
+        raise ValueError("zf, zr, zx must be [T, B, D]")
+    T, B, D = zf.shape
+    if bf.shape != (D,) or br.shape != (D,):
+        raise ValueError("bf, br must be [D]")
+    h = np.empty_like(zf)
+    c_last = np.empty((B, D), dtype=np.float64)
+    _check(_load().lrs_oracle_sru_fwd(_ptr(zf), _ptr(zr), _ptr(zx), _ptr(bf), _ptr(br), _ptr(c0),
+                                      _ptr(h), _ptr(c_last), T, B, D, nthreads), "sru_fwd")
+    return h, c_last
+
+
+def rnn_seq(w, u, h0=None, nthreads: int = 0):
+    """Sequential h_t = tanh(w_d h_{t-1} + u_t); u: [B, D, T], w: [D]."""
+    w, u, h0 = _f64(w), _f64(u), _f64(h0)
+    B, D, T = u.shape
+    if w.shape != (D,):
+        raise ValueError("w must be [D]")
+    h = np.empty_like(u)
+    _check(_load().lrs_oracle_rnn_seq(_ptr(w), _ptr(u), _ptr(h0), _ptr(h), B, D, T, nthreads),
+           "rnn_seq")
+    return h
+
+
+def deer(w, u, h0=None, h_init=None, eps: float = 1e-5, k_max: int = 5, nthreads: int = 0):
+    """DEER Newton iterations for h_t = tanh(w h_{t-1} + u_t).
+
+    Returns (h, iters, deltas) with deltas[i] = max |y^(i+1) - y^(i)|."""
+    w, u, h0, h_init = _f64(w), _f64(u), _f64(h0), _f64(h_init)
+    B, D, T = u.shape
+    if w.shape != (D,):
+        raise ValueError("w must be [D]")
+    h = np.empty_like(u)
+    iters = ctypes.c_int(0)
+    deltas = np.zeros(max(k_max, 1), dtype=np.float64)
+    _check(_load().lrs_oracle_deer(_ptr(w), _ptr(u), _ptr(h0), _ptr(h_init), _ptr(h), B, D, T,
+                                   float(eps), int(k_max), ctypes.byref(iters), _ptr(deltas),
+                                   nthreads), "deer")
+    return h, iters.value, deltas[: iters.value].copy()

@@ -1,0 +1,237 @@
+/*
+ * lrs_oracle.c -- plain, sequential fp64 reference for the diagonal linear
+ * recurrence, its reverse-time adjoint, the SRU cell-state layer and the DEER
+ * Newton solve of an element-wise nonlinear RNN.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file; only the test-suite, the smoke check and the CPU-baseline
+ * leg of the benchmark do.  It shares no code, header, helper or constant
+ * with the HIP kernels.
+ *
+ * Every loop below is the textbook definition written out one time step at a
+ * time, in double precision, with no blocking, reordering or fusion.  The
+ * callers hand in the exact values the device path sees (fp32 or bf16 values
+ * widened exactly to double).  The only parallelism is an optional OpenMP loop
+ * over independent channels, which does not change any arithmetic.
+ *
+ * Sources (four blog pages on one subject, cited by title and section):
+ *  [P1] "CUDA并行化RNN训练：从O(T)到O(log T)的工程实践与参数调优"
+ *       (CUDA-parallel RNN training, O(T) to O(log T)), body: the SRU
+ *       paragraph and the parallel-scan paragraph.
+ *  [P2] "RNN CUDA内核优化：实现序列长度无关的恒定推理延迟"
+ *       (RNN CUDA kernel optimisation, constant latency), body: the paragraph
+ *       on the LSTM cell state C_t = f_t*C_{t-1} + i_t*C~_t as a linear
+ *       recurrence with time-varying coefficients.
+ *  [P4] DEER page "cuda-parallel-rnn-training-logt-optimization", sections
+ *       "核心原理" (core principle: Newton in function space, the linear inverse
+ *       operator as a recurrence with an initial condition) and "工程实现"
+ *       (engineering: stop when ||y(i+1)-y(i)|| < eps or i reaches K_max).
+ *
+ * Conventions shared with the tests: a channel is one (batch, feature) pair;
+ * the time axis has T steps stored at index 0..T-1 for t = 1..T; h0 is the
+ * state at t = 0 and is not part of the output.  Layout of the scan and DEER
+ * arrays is channel-major [C, T] (time contiguous); the SRU arrays are
+ * [T, B, D] (feature contiguous), as the SRU workload states them.
+ *
+ * Parity status: every function here is pinned by tests in tests/ against
+ * closed forms, exact rational brute force, adjoint identities, finite
+ * differences or the Newton invariants (see tests/test_oracle_*.py).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL 1
+#define ORACLE_ENOMEM 2
+
+static void set_threads(int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+/* Forward recurrence h_t = a_t * h_{t-1} + b_t  ([P1] parallel-scan paragraph;
+ * [P2] cell-state paragraph).  h0 may be NULL (zero initial state). */
+int lrs_oracle_scan_fwd(const double *a, const double *b, const double *h0,
+                        double *h, int64_t C, int64_t T, int nthreads)
+{
+    if (C < 0 || T < 0 || (C * T > 0 && (!a || !b || !h))) return ORACLE_EINVAL;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t c = 0; c < C; ++c) {
+        const double *ac = a + c * T, *bc = b + c * T;
+        double *hc = h + c * T;
+        double state = h0 ? h0[c] : 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            state = ac[t] * state + bc[t];
+            hc[t] = state;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Reverse-time adjoint of the forward recurrence for the loss
+ * L = sum_t <g_t, h_t>, g = dL/dh given per step.  [P1] states that the
+ * backward pass is also a scan; the formulas are the chain rule:
+ *   lam_T = g_T,  lam_t = g_t + a_{t+1} * lam_{t+1}
+ *   dL/db_t = lam_t,  dL/da_t = lam_t * h_{t-1} (h_0 at t = 1),
+ *   dL/dh_0 = a_1 * lam_1.
+ * h is the forward output (steps 1..T); h0 may be NULL (zero); dh0 may be NULL. */
+int lrs_oracle_scan_bwd(const double *a, const double *h, const double *h0,
+                        const double *g, double *da, double *db, double *dh0,
+                        int64_t C, int64_t T, int nthreads)
+{
+    if (C < 0 || T < 0 || (C * T > 0 && (!a || !h || !g || !da || !db)))
+        return ORACLE_EINVAL;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t c = 0; c < C; ++c) {
+        const double *ac = a + c * T, *hc = h + c * T, *gc = g + c * T;
+        double *dac = da + c * T, *dbc = db + c * T;
+        double lam = 0.0;
+        for (int64_t t = T - 1; t >= 0; --t) {
+            double next = (t + 1 < T) ? ac[t + 1] * lam : 0.0;
+            lam = gc[t] + next;
+            double hprev = (t > 0) ? hc[t - 1] : (h0 ? h0[c] : 0.0);
+            dbc[t] = lam;
+            dac[t] = lam * hprev;
+        }
+        if (dh0) dh0[c] = (T > 0) ? ac[0] * lam : 0.0;
+    }
+    return ORACLE_OK;
+}
+
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/* SRU layer forward with precomputed pre-activations ([P1] SRU paragraph: a
+ * forget gate that does not wait for h_{t-1}, and a highway connection through
+ * the reset gate r).  The recurrent term v_f*c_{t-1} is absent, as in the
+ * workload this oracle serves, so the cell state is a linear recurrence:
+ *   f_t = sigma(zf_t + bf),  r_t = sigma(zr_t + br)
+ *   c_t = f_t * c_{t-1} + (1 - f_t) * zx_t
+ *   h_t = r_t * tanh(c_t) + (1 - r_t) * zx_t
+ * Arrays are [T, B, D]; bf, br are [D]; c0 is [B, D] or NULL (zero);
+ * c_last is [B, D] or NULL. */
+int lrs_oracle_sru_fwd(const double *zf, const double *zr, const double *zx,
+                       const double *bf, const double *br, const double *c0,
+                       double *h, double *c_last, int64_t T, int64_t B,
+                       int64_t D, int nthreads)
+{
+    if (T < 0 || B < 0 || D < 0) return ORACLE_EINVAL;
+    if (T * B * D > 0 && (!zf || !zr || !zx || !bf || !br || !h)) return ORACLE_EINVAL;
+    set_threads(nthreads);
+    const int64_t C = B * D;
+#pragma omp parallel for schedule(static)
+    for (int64_t ch = 0; ch < C; ++ch) {
+        const int64_t d = ch % D;
+        double c = c0 ? c0[ch] : 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t i = t * C + ch;
+            double f = sigmoid(zf[i] + bf[d]);
+            double r = sigmoid(zr[i] + br[d]);
+            c = f * c + (1.0 - f) * zx[i];
+            h[i] = r * tanh(c) + (1.0 - r) * zx[i];
+        }
+        if (c_last) c_last[ch] = c;
+    }
+    return ORACLE_OK;
+}
+
+/* Plain sequential nonlinear RNN h_t = tanh(w_d * h_{t-1} + u_t): the ground
+ * truth that the DEER iteration converges to ([P4] core principle).
+ * u, h are [B, D, T]; w is [D]; h0 is [B, D] or NULL. */
+int lrs_oracle_rnn_seq(const double *w, const double *u, const double *h0,
+                       double *h, int64_t B, int64_t D, int64_t T, int nthreads)
+{
+    if (B < 0 || D < 0 || T < 0) return ORACLE_EINVAL;
+    if (B * D * T > 0 && (!w || !u || !h)) return ORACLE_EINVAL;
+    set_threads(nthreads);
+    const int64_t C = B * D;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t ch = 0; ch < C; ++ch) {
+        const double wd = w[ch % D];
+        const double *uc = u + ch * T;
+        double *hc = h + ch * T;
+        double state = h0 ? h0[ch] : 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            state = tanh(wd * state + uc[t]);
+            hc[t] = state;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* DEER: solve the nonlinear recurrence as a root-finding problem by Newton's
+ * method in function space ([P4] core principle, three steps per iteration:
+ * evaluate f and its Jacobian, multiply by the Jacobian, apply the linear
+ * inverse operator, which for an RNN is a linear recurrence with an initial
+ * condition).  For the element-wise cell f(h_{t-1}, u_t) = tanh(w h_{t-1}+u_t)
+ * the Jacobian is diagonal, so one iteration from the iterate y reads
+ *   z_t   = tanh(w * y_{t-1} + u_t)
+ *   J_t   = w * (1 - z_t^2)
+ *   rhs_t = z_t - J_t * y_{t-1}
+ *   y'_t  = J_t * y'_{t-1} + rhs_t,   y'_0 = y_0 = h0
+ * and the linear recurrence is solved here sequentially.  Stop rule ([P4]
+ * engineering section): after iteration i (1-based) compute
+ * delta_i = max over all B*D*T entries of |y' - y|; stop when delta_i < eps
+ * or i == k_max.  h_init is the starting iterate (NULL: zero); the result is
+ * the last iterate.  deltas (length >= k_max) receives delta_1..delta_iters;
+ * *iters receives the number of iterations performed. */
+int lrs_oracle_deer(const double *w, const double *u, const double *h0,
+                    const double *h_init, double *h, int64_t B, int64_t D,
+                    int64_t T, double eps, int k_max, int *iters,
+                    double *deltas, int nthreads)
+{
+    if (B < 0 || D < 0 || T < 0 || k_max < 1 || !iters) return ORACLE_EINVAL;
+    const int64_t C = B * D, N = C * T;
+    if (N > 0 && (!w || !u || !h)) return ORACLE_EINVAL;
+    set_threads(nthreads);
+    double *y = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+    double *yn = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+    if (!y || !yn) { free(y); free(yn); return ORACLE_ENOMEM; }
+    if (h_init && N > 0) memcpy(y, h_init, (size_t)N * sizeof(double));
+    else memset(y, 0, (size_t)(N > 0 ? N : 1) * sizeof(double));
+
+    int done = 0;
+    for (int i = 1; i <= k_max; ++i) {
+        double delta = 0.0;
+        int saw_nan = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(max : delta) reduction(| : saw_nan)
+        for (int64_t ch = 0; ch < C; ++ch) {
+            const double wd = w[ch % D];
+            const double y0 = h0 ? h0[ch] : 0.0;
+            const double *uc = u + ch * T, *yc = y + ch * T;
+            double *ync = yn + ch * T;
+            double state = y0; /* y'_0 */
+            for (int64_t t = 0; t < T; ++t) {
+                double yprev = (t > 0) ? yc[t - 1] : y0;
+                double z = tanh(wd * yprev + uc[t]);
+                double J = wd * (1.0 - z * z);
+                double rhs = z - J * yprev;
+                state = J * state + rhs;
+                ync[t] = state;
+                double diff = fabs(state - yc[t]);
+                if (diff != diff) saw_nan = 1;
+                else if (diff > delta) delta = diff;
+            }
+        }
+        if (saw_nan) delta = NAN; /* a NaN difference never satisfies delta < eps */
+        double *tmp = y; y = yn; yn = tmp;
+        if (deltas) deltas[i - 1] = delta;
+        done = i;
+        if (delta < eps) break;
+    }
+    if (N > 0) memcpy(h, y, (size_t)N * sizeof(double));
+    *iters = done;
+    free(y);
+    free(yn);
+    return ORACLE_OK;
+}
