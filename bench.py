@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Benchmark of the diagonal linear-recurrence scan on one MI355X.
+
+Default workload (the headline metric): forward + backward fp32 scan,
+B=8, D=512, T=4096, [B,D,T] layout.  One step = lrs_scan_fwd then
+lrs_scan_bwd over the same resident inputs.  Other workloads (--workload):
+scan_long (T = 2^20), sru_fwd (bf16 SRU layer), deer (Newton solve),
+scan_fwd_small.
+
+Prints ONE JSON line.  `value` is scanned elements per second over the timed
+steps (inputs resident in HBM before timing starts).  `roofline` describes
+the dominant kernel: algorithmic bytes per launch divided by its average
+launch time, measured with HIP events recorded on the launch stream around
+every call inside the timed region.  `cpu_baseline` times the fp64 CPU oracle
+on the host cores over a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "scanned elements/sec (B·D·T) and % of HBM roofline, fwd+bwd, fp32"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+
+# algorithmic bytes per element of each kernel (every input read once, every
+# output written once; per-channel vectors are negligible)
+BYTES_PER_ELEM = {"scan_fwd_f32": 12, "scan_bwd_f32": 20, "sru_fwd_bf16": 8,
+                  "deer_iter_first": 8, "deer_iter": 12}
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
+
+
+def csrc_hash() -> str:
+    d = os.path.join(ROOT, "linear_recurrence_scan_diagonal_amd", "csrc")
+    h = hashlib.sha256()
+    for fn in sorted(os.listdir(d)):
+        with open(os.path.join(d, fn), "rb") as f:
+            h.update(fn.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key: str):
+    """HBM bytes per launch of a kernel from the committed counter summary, or
+    None when there is none or the kernels changed since it was taken."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("csrc_hash") != csrc_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel_key)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="scan_fwd_bwd",
+                   choices=["scan_fwd_bwd", "scan_long", "sru_fwd", "deer", "scan_fwd_small"])
+    p.add_argument("--layout", default="bdt", choices=["bdt", "tbd"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="minimum CPU time for the oracle baseline sample")
+    return p.parse_args()
+
+
+class KernelTimer:
+    """HIP events around each call, on the stream the call launches on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def run(self, name, fn):
+        t = self.torch
+        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        s.record()
+        out = fn()
+        e.record()
+        self.pairs.setdefault(name, []).append((s, e))
+        return out
+
+    def avg_ms(self, name):
+        ps = self.pairs.get(name, [])
+        return sum(s.elapsed_time(e) for s, e in ps) / max(1, len(ps))
+
+
+def cpu_threads() -> int:
+    n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); every channel is "
+              "independent, so several GPUs would each run this same per-GPU workload.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import linear_recurrence_scan_diagonal_amd as lrs
+    from linear_recurrence_scan_diagonal_amd import inputs as I
+
+    lrs.load()  # fail loudly if the HIP library is not built
+    dev = torch.device("cuda:0")
+    w = I.WORKLOADS[args.workload]
+    B, D, T = w.B, w.D, w.T
+    N = w.N
+    timer = KernelTimer(torch)
+    extra = {}
+
+    def to_dev(x_ct, layout):
+        if layout == "bdt":
+            return torch.from_numpy(np.ascontiguousarray(x_ct).reshape(B, D, T)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x_ct.T).reshape(T, B, D)).to(dev)
+
+    print(f"# generating inputs for {w.name}: {w.desc}", file=sys.stderr, flush=True)
+    if w.kind == "scan":
+        layout = args.layout
+        fwd_only = args.workload == "scan_fwd_small"
+        x = I.scan_inputs(w, with_grad=not fwd_only)
+        a, b = to_dev(x["a"], layout), to_dev(x["b"], layout)
+        g = None if fwd_only else to_dev(x["g"], layout)
+        h0 = torch.from_numpy(x["h0"].reshape(B, D)).to(dev)
+        h = torch.empty_like(a)
+        ga, gb = torch.empty_like(a), torch.empty_like(a)
+        gh0 = torch.empty((B, D), dtype=torch.float32, device=dev)
+        ws_bytes = lrs.scan_workspace_bytes(B, D, T, layout)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+        def step():
+            timer.run("scan_fwd_f32", lambda: lrs.scan_fwd(a, b, h0, layout=layout, out=h, workspace=ws))
+            if not fwd_only:
+                timer.run("scan_bwd_f32", lambda: lrs.scan_bwd(a, h, g, h0, layout=layout, grad_a=ga,
+                                                               grad_b=gb, grad_h0=gh0, workspace=ws))
+        kernels = ["scan_fwd_f32"] + ([] if fwd_only else ["scan_bwd_f32"])
+        dtype = "f32"
+        config = {"workload": w.name, "B": B, "D": D, "T": T, "layout": layout,
+                  "pass": "fwd" if fwd_only else "fwd+bwd"}
+    elif w.kind == "sru":
+        s = I.sru_inputs(w)
+        z = {k: torch.from_numpy(s[k].view(np.int16)).view(torch.bfloat16).to(dev)
+             for k in ("zf", "zr", "zx")}
+        bf = torch.from_numpy(s["bias_f"]).to(dev)
+        br = torch.from_numpy(s["bias_r"]).to(dev)
+        hs = torch.empty_like(z["zf"])
+        ws = torch.empty(max(1, lrs.load().lrs_sru_workspace_bytes(T, B, D)), dtype=torch.uint8,
+                         device=dev)
+
+        def step():
+            timer.run("sru_fwd_bf16", lambda: lrs.sru_fwd(z["zf"], z["zr"], z["zx"], bf, br, out=hs,
+                                                          workspace=ws))
+        kernels = ["sru_fwd_bf16"]
+        dtype = "bf16 I/O, f32 state"
+        config = {"workload": w.name, "B": B, "D": D, "T": T, "layout": "tbd"}
+    else:  # deer
+        x = I.deer_inputs(w)
+        wd = torch.from_numpy(x["w"]).to(dev)
+        u = torch.from_numpy(x["u"].reshape(B, D, T)).to(dev)
+        h0 = torch.from_numpy(x["h0"].reshape(B, D)).to(dev)
+        hd = torch.empty_like(u)
+        ws = torch.empty(lrs.load().lrs_deer_workspace_bytes(B, D, T, 5), dtype=torch.uint8,
+                         device=dev)
+        info_box = {}
+
+        def step():
+            _, info_box["info"] = timer.run("deer_solve", lambda: lrs.deer_solve(
+                wd, u, h0, None, eps=1e-5, k_max=5, out=hd, workspace=ws))
+        kernels = ["deer_solve"]
+        dtype = "f32"
+        config = {"workload": w.name, "B": B, "D": D, "T": T, "layout": "bdt", "eps": 1e-5,
+                  "k_max": 5}
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timer.pairs.clear()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    value = N / (ms_per_step / 1e3)
+
+    per_kernel = {k: timer.avg_ms(k) for k in kernels}
+    if w.kind == "scan":
+        bytes_step = sum(BYTES_PER_ELEM[k] * N for k in kernels)
+        dom = max(kernels, key=lambda k: per_kernel[k])
+        dom_bytes = BYTES_PER_ELEM[dom] * N
+        dom_ms = per_kernel[dom]
+    elif w.kind == "sru":
+        bytes_step = BYTES_PER_ELEM["sru_fwd_bf16"] * N
+        dom, dom_bytes, dom_ms = "sru_fwd_bf16", bytes_step, per_kernel["sru_fwd_bf16"]
+    else:
+        iters = info_box["info"]["iters"]
+        bytes_step = (BYTES_PER_ELEM["deer_iter_first"] + (iters - 1) * BYTES_PER_ELEM["deer_iter"]) * N
+        dom, dom_bytes, dom_ms = "deer_solve", bytes_step, per_kernel["deer_solve"]
+        extra["deer_iters"] = iters
+        extra["deer_deltas"] = info_box["info"]["deltas"]
+    achieved = dom_bytes / (dom_ms / 1e3) / 1e9
+    traffic = measured_traffic(dom)
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "algorithmic_bytes": dom_bytes,
+                "avg_launch_ms": round(dom_ms, 5)}
+    extra["per_kernel_ms"] = {k: round(v, 5) for k, v in per_kernel.items()}
+    extra["step_hbm_frac"] = round(bytes_step / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4)
+    extra["wall_s"] = round(wall, 3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args, np, I)
+
+    line = {"metric": METRIC, "value": value, "unit": "elements/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+            "data": "synthetic", "config": config, "roofline": roofline, "cpu_baseline": cpu,
+            **extra}
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, args, np, I):
+    """Time the fp64 oracle on the host cores over a bounded sample: whole
+    passes over the workload's channels (or a channel subset for the largest
+    workloads), repeated until at least --cpu-seconds of CPU time."""
+    import oracle
+    threads = cpu_threads()
+    C, T = w.C, w.T
+    if w.kind == "scan":
+        nch = C if C * T <= (1 << 26) else max(1, (1 << 26) // T)
+        ch = np.arange(nch)
+        x = I.scan_inputs(w, channels=ch, with_grad=w.name != "scan_fwd_small")
+        a, b = x["a"].astype(np.float64), x["b"].astype(np.float64)
+        h0 = x["h0"].astype(np.float64)
+        g = x["g"].astype(np.float64) if "g" in x else None
+
+        def once():
+            h = oracle.scan_fwd(a, b, h0, nthreads=threads)
+            if g is not None:
+                oracle.scan_bwd(a, h, h0, g, nthreads=threads)
+        sample = f"{nch} of {C} channels x T={T}, fwd{'+bwd' if g is not None else ''}"
+        n_el = nch * T
+    elif w.kind == "sru":
+        sub = I.scaled(w, B=1, D=min(w.D, 1024))
+        s = I.sru_inputs(sub)
+        z = [I.bf16_bits_to_f64(s[k]) for k in ("zf", "zr", "zx")]
+
+        def once():
+            oracle.sru_fwd(*z, s["bias_f"], s["bias_r"], nthreads=threads)
+        sample = f"B=1 of {w.B}, D={sub.D}, T={T} (same recipe)"
+        n_el = sub.N
+    else:
+        sub = I.scaled(w, B=1)
+        x = I.deer_inputs(sub)
+        u = x["u"].reshape(1, sub.D, T).astype(np.float64)
+
+        def once():
+            oracle.deer(x["w"], u, None, eps=1e-5, k_max=5, nthreads=threads)
+        sample = f"B=1 of {w.B}, D={sub.D}, T={T}, eps=1e-5, K_max=5"
+        n_el = sub.N
+    reps, t_total = 0, 0.0
+    while t_total < args.cpu_seconds and reps < 10000:
+        t0 = time.perf_counter()
+        once()
+        t_total += time.perf_counter() - t0
+        reps += 1
+    return {"value": n_el * reps / t_total, "unit": "elements/s", "cores": threads,
+            "kind": "oracle", "sample": f"{sample}; {reps} repetitions, {t_total:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/*
+ * lrs.h -- C ABI of liblrs.so: the diagonal linear-recurrence scan
+ * h_t = a_t (.) h_{t-1} + b_t on AMD MI355X (gfx950), with its reverse-time
+ * backward pass, a fused SRU layer and a DEER Newton solver built on it.
+ *
+ * Sources (four blog pages on one subject; cited by title and section):
+ *  [P1] "CUDA并行化RNN训练：从O(T)到O(log T)的工程实践与参数调优", body:
+ *       SRU paragraph (gates that do not wait for h_{t-1}, highway through the
+ *       reset gate), parallel-scan paragraph (associative step, forward and
+ *       backward passes both as log-depth scans), checklist item 2 (fuse all
+ *       element-wise work into one kernel).
+ *  [P2] "RNN CUDA内核优化：实现序列长度无关的恒定推理延迟", body: the cell state
+ *       C_t = f_t*C_{t-1} + i_t*C~_t is a linear recurrence with time-varying
+ *       coefficients, i.e. a prefix-scan problem.
+ *  [P4] DEER page "cuda-parallel-rnn-training-logt-optimization": section
+ *       "核心原理" (Newton in function space; the inverse operator is a linear
+ *       recurrence with an initial condition, solved by a parallel prefix scan)
+ *       and section "工程实现" (stop when ||y(i+1) - y(i)|| < eps or after K_max
+ *       iterations; example eps = 1e-5, K_max = 5).
+ *
+ * Conventions for every entry point
+ *  - A channel is one (batch b, feature d) pair; C = B*D channels.  The time
+ *    axis has T steps, stored at index 0..T-1 for t = 1..T.  h0 is the state at
+ *    t = 0; it is an input and is not part of the output.
+ *  - Layouts: LRS_LAYOUT_BDT = [B, D, T] (time contiguous, element (b,d,t) at
+ *    (b*D + d)*T + t); LRS_LAYOUT_TBD = [T, B, D] (feature contiguous, element
+ *    at (t*B + b)*D + d).  Per-channel arrays (h0, grad_h0, c0, c_last) are
+ *    [B, D] in both layouts; per-feature arrays (bias_f, bias_r, w) are [D].
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller; the library
+ *    never allocates, frees or retains memory.  Scratch space comes from the
+ *    caller's `workspace`, sized by the matching *_workspace_bytes query (a
+ *    size of 0 means no workspace is needed and `workspace` may be NULL).
+ *    Pointers must be aligned to their element size; 16-byte alignment of all
+ *    arrays (and T % 4 == 0 for [B,D,T] fp32) enables the widest accesses.
+ *  - `stream` is a hipStream_t passed as an opaque pointer (NULL = the null
+ *    stream).  Scan and SRU calls only enqueue work and return; DEER reads its
+ *    convergence test back to the host and returns after the solve.
+ *  - Errors are return codes (lrs_status); nothing is thrown and nothing
+ *    aborts.  Arguments are validated before any launch, so an error other
+ *    than LRS_ERR_HIP leaves all outputs untouched.  An empty problem
+ *    (B*D*T == 0) is valid and does nothing.
+ *  - Output arrays must not overlap input arrays unless a function says so.
+ *  - Calls that share a workspace must be ordered (same stream or synchronised).
+ */
+#ifndef LRS_H
+#define LRS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define LRS_API __attribute__((visibility("default")))
+#else
+#define LRS_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define LRS_OK 0
+#define LRS_ERR_INVALID_ARG 1 /* null/misaligned pointer, negative or overflowing size, bad enum */
+#define LRS_ERR_UNSUPPORTED 2 /* valid request this build does not implement (e.g. dtype) */
+#define LRS_ERR_WORKSPACE 3   /* workspace smaller than the query returned, or NULL */
+#define LRS_ERR_HIP 4         /* a HIP runtime call or kernel launch failed */
+#define LRS_ERR_NONFINITE 5   /* DEER: the last iteration's update was NaN or infinite */
+
+/* Layouts (see conventions above). */
+#define LRS_LAYOUT_BDT 0
+#define LRS_LAYOUT_TBD 1
+
+/* Element types of I/O tensors; the recurrence state is always fp32. */
+#define LRS_F32 0
+#define LRS_BF16 1
+
+/* Human-readable name of a return code (static string, never NULL). */
+LRS_API const char *lrs_status_string(int status);
+
+/* Library ABI version (major*100 + minor). */
+LRS_API int lrs_version(void);
+
+/* ---------------------------------------------------------------- scan --- */
+
+/* Workspace bytes needed by lrs_scan_fwd / lrs_scan_bwd for this shape
+ * (look-back status words when a channel spans more than one workgroup).
+ * Returns 0 for an invalid shape. */
+LRS_API size_t lrs_scan_workspace_bytes(int64_t B, int64_t D, int64_t T, int layout, int dtype);
+
+/* Forward scan ([P1] parallel-scan paragraph; [P2] cell-state paragraph):
+ *   h_t = a_t * h_{t-1} + b_t  for t = 1..T, every channel independently.
+ * a, b, h : [B,D,T] or [T,B,D] per `layout`, element type `dtype` (LRS_F32).
+ * h0      : [B,D] fp32, or NULL for a zero initial state.
+ * h must not overlap a, b or h0.  Arithmetic is fp32 with fused multiply-add;
+ * the association order of the scan is fixed by the launch shape. */
+LRS_API int lrs_scan_fwd(const void *a, const void *b, const float *h0, void *h, int64_t B, int64_t D,
+                 int64_t T, int layout, int dtype, void *workspace, size_t workspace_bytes,
+                 void *stream);
+
+/* Backward scan: reverse-time adjoint of lrs_scan_fwd for a loss L whose
+ * gradient with respect to h is grad_h ([P1]: the backward pass is also a
+ * log-depth scan).  With lam_{T+1} = 0:
+ *   lam_t = grad_h_t + a_{t+1} * lam_{t+1}
+ *   grad_b_t = lam_t,  grad_a_t = lam_t * h_{t-1} (h0 at t = 1),
+ *   grad_h0 = a_1 * lam_1.
+ * h is the forward output; h0 as in lrs_scan_fwd (NULL = zero).
+ * grad_a, grad_b: same shape/layout/dtype as a.  grad_h0: [B,D] fp32 or NULL.
+ * grad_b may be the same buffer as grad_h (lam overwrites the incoming
+ * gradient); no other overlap is allowed. */
+LRS_API int lrs_scan_bwd(const void *a, const void *h, const float *h0, const void *grad_h, void *grad_a,
+                 void *grad_b, float *grad_h0, int64_t B, int64_t D, int64_t T, int layout,
+                 int dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ----------------------------------------------------------------- SRU --- */
+
+/* Workspace bytes needed by lrs_sru_fwd for this shape (0 for an invalid one). */
+LRS_API size_t lrs_sru_workspace_bytes(int64_t T, int64_t B, int64_t D);
+
+/* Fused SRU layer forward ([P1] SRU paragraph and checklist item 2), with the
+ * input projections already applied (pre-activations z_*) and no recurrent
+ * term in the forget gate, so the cell state is a linear recurrence:
+ *   f_t = sigmoid(z_f,t + bias_f),  r_t = sigmoid(z_r,t + bias_r)
+ *   c_t = f_t * c_{t-1} + (1 - f_t) * z_x,t
+ *   h_t = r_t * tanh(c_t) + (1 - r_t) * z_x,t
+ * z_f, z_r, z_x, h : [T,B,D], element type io_dtype (LRS_BF16 or LRS_F32).
+ * bias_f, bias_r   : [D] fp32.   c0: [B,D] fp32 or NULL (zero).
+ * c_last           : [B,D] fp32 output (c_T) or NULL.
+ * Gates, state and activations are computed in fp32; h is rounded to io_dtype
+ * (nearest-even).  h must not overlap the inputs. */
+LRS_API int lrs_sru_fwd(const void *z_f, const void *z_r, const void *z_x, const float *bias_f,
+                const float *bias_r, const float *c0, void *h, float *c_last, int64_t T,
+                int64_t B, int64_t D, int io_dtype, void *workspace, size_t workspace_bytes,
+                void *stream);
+
+/* ---------------------------------------------------------------- DEER --- */
+
+/* Workspace bytes needed by lrs_deer_solve (a second iterate buffer of
+ * B*D*T floats, the per-iteration update norms and look-back status). */
+LRS_API size_t lrs_deer_workspace_bytes(int64_t B, int64_t D, int64_t T, int k_max);
+
+/* DEER Newton solve ([P4] core principle and engineering sections) of the
+ * element-wise nonlinear RNN  h_t = tanh(w_d * h_{t-1} + u_t),  [B,D,T] fp32.
+ * Iteration i (1-based) maps the iterate y to y' by
+ *   z_t = tanh(w y_{t-1} + u_t),  J_t = w (1 - z_t^2),
+ *   y'_t = J_t * y'_{t-1} + (z_t - J_t * y_{t-1}),   y'_0 = y_0 = h0,
+ * solving the linear recurrence with the parallel scan, and records
+ * delta_i = max over all B*D*T entries of |y' - y|.  It stops after the first
+ * iteration with delta_i < eps, or after k_max iterations.
+ * w       : [D] fp32 (one weight per feature, shared across the batch).
+ * u       : [B,D,T] fp32.       h0: [B,D] fp32 or NULL (zero).
+ * h_init  : [B,D,T] starting iterate, or NULL for zero (may equal h).
+ * h       : [B,D,T] output, the last iterate.
+ * iters_out (host, may be NULL): iterations performed (1..k_max).
+ * deltas_out (host, may be NULL): k_max floats; entries 0..iters-1 receive
+ *   delta_1..delta_iters, the rest 0.
+ * converged_out (host, may be NULL): 1 if the last delta < eps, else 0.
+ * Host-synchronous: one device-to-host read of the k_max norms after all
+ * iterations are enqueued (an iteration whose predecessor met the stop rule
+ * exits immediately on the device).  Returns LRS_ERR_NONFINITE, with all
+ * outputs written, when the last delta is NaN or infinite. */
+LRS_API int lrs_deer_solve(const float *w, const float *u, const float *h0, const float *h_init, float *h,
+                   int64_t B, int64_t D, int64_t T, float eps, int k_max, int *iters_out,
+                   float *deltas_out, int *converged_out, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LRS_H */

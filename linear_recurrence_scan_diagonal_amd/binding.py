@@ -1,0 +1,221 @@
+"""ctypes binding of liblrs.so (include/lrs.h), one Python function per entry point.
+
+Argument marshalling only: shapes and dtypes are checked, outputs and
+workspaces are allocated as torch device tensors, and the raw pointers plus the
+current HIP stream are handed to the C ABI.  Every step of the computation
+runs in the library's HIP kernels; there is no fallback of any kind, and a
+missing library raises at once.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblrs.so")
+
+LRS_OK, LRS_ERR_INVALID_ARG, LRS_ERR_UNSUPPORTED, LRS_ERR_WORKSPACE, LRS_ERR_HIP, \
+    LRS_ERR_NONFINITE = range(6)
+LAYOUTS = {"bdt": 0, "tbd": 1}
+DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+EXPORTS = ("lrs_status_string", "lrs_version", "lrs_scan_workspace_bytes", "lrs_scan_fwd",
+           "lrs_scan_bwd", "lrs_sru_workspace_bytes", "lrs_sru_fwd", "lrs_deer_workspace_bytes",
+           "lrs_deer_solve")
+
+_lib = None
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_sz = ctypes.c_size_t
+
+
+class LrsError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = load().lrs_status_string(code).decode() if _lib is not None else str(code)
+        super().__init__(f"{where}: {msg}")
+
+
+def load():
+    """Load liblrs.so (built by __graft_entry__.build()); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; "
+                           "g.build()'` first")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.lrs_status_string.argtypes = [_int]
+    lib.lrs_status_string.restype = ctypes.c_char_p
+    lib.lrs_version.argtypes = []
+    lib.lrs_version.restype = _int
+    lib.lrs_scan_workspace_bytes.argtypes = [_i64, _i64, _i64, _int, _int]
+    lib.lrs_scan_workspace_bytes.restype = _sz
+    lib.lrs_scan_fwd.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _sz, _vp]
+    lib.lrs_scan_fwd.restype = _int
+    lib.lrs_scan_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int,
+                                 _vp, _sz, _vp]
+    lib.lrs_scan_bwd.restype = _int
+    lib.lrs_sru_workspace_bytes.argtypes = [_i64, _i64, _i64]
+    lib.lrs_sru_workspace_bytes.restype = _sz
+    lib.lrs_sru_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp,
+                                _sz, _vp]
+    lib.lrs_sru_fwd.restype = _int
+    lib.lrs_deer_workspace_bytes.argtypes = [_i64, _i64, _i64, _int]
+    lib.lrs_deer_workspace_bytes.restype = _sz
+    lib.lrs_deer_solve.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_float, _int,
+                                   ctypes.POINTER(_int), ctypes.POINTER(ctypes.c_float),
+                                   ctypes.POINTER(_int), _vp, _sz, _vp]
+    lib.lrs_deer_solve.restype = _int
+    _lib = lib
+    return lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _check_dev(name, t, dtype, shape=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _workspace(nbytes: int, dev, workspace: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return None
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace needs {nbytes} bytes")
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+
+def _dims(x: torch.Tensor, layout: str):
+    if x.dim() != 3:
+        raise ValueError("expected a 3-d tensor")
+    if layout == "bdt":
+        B, D, T = x.shape
+    elif layout == "tbd":
+        T, B, D = x.shape
+    else:
+        raise ValueError(f"layout must be 'bdt' or 'tbd', got {layout!r}")
+    return int(B), int(D), int(T)
+
+
+def _call(rc: int, where: str):
+    if rc != LRS_OK:
+        raise LrsError(rc, where)
+
+
+def scan_workspace_bytes(B, D, T, layout="bdt", dtype=torch.float32) -> int:
+    return int(load().lrs_scan_workspace_bytes(B, D, T, LAYOUTS[layout], DTYPES[dtype]))
+
+
+def scan_fwd(a, b, h0=None, layout: str = "bdt", out=None, workspace=None):
+    """h_t = a_t*h_{t-1} + b_t.  a, b: [B,D,T] ('bdt') or [T,B,D] ('tbd'); h0: [B,D]."""
+    lib = load()
+    B, D, T = _dims(a, layout)
+    _check_dev("a", a, a.dtype, a.shape)
+    _check_dev("b", b, a.dtype, a.shape)
+    _check_dev("h0", h0, torch.float32, (B, D))
+    h = torch.empty_like(a) if out is None else out
+    _check_dev("out", h, a.dtype, a.shape)
+    nbytes = lib.lrs_scan_workspace_bytes(B, D, T, LAYOUTS[layout], DTYPES[a.dtype])
+    ws = _workspace(nbytes, a.device, workspace)
+    _call(lib.lrs_scan_fwd(_ptr(a), _ptr(b), _ptr(h0), _ptr(h), B, D, T, LAYOUTS[layout],
+                           DTYPES[a.dtype], _ptr(ws), nbytes, _stream(a.device)), "lrs_scan_fwd")
+    return h
+
+
+def scan_bwd(a, h, grad_h, h0=None, layout: str = "bdt", need_grad_h0: bool = True,
+             grad_a=None, grad_b=None, grad_h0=None, workspace=None):
+    """Reverse-time adjoint.  Returns (grad_a, grad_b, grad_h0 or None).
+    grad_b may be passed as grad_h itself (in-place)."""
+    lib = load()
+    B, D, T = _dims(a, layout)
+    for name, t in (("a", a), ("h", h), ("grad_h", grad_h)):
+        _check_dev(name, t, a.dtype, a.shape)
+    _check_dev("h0", h0, torch.float32, (B, D))
+    ga = torch.empty_like(a) if grad_a is None else grad_a
+    gb = torch.empty_like(a) if grad_b is None else grad_b
+    gh0 = None
+    if need_grad_h0:
+        gh0 = torch.empty((B, D), dtype=torch.float32, device=a.device) if grad_h0 is None else grad_h0
+    _check_dev("grad_a", ga, a.dtype, a.shape)
+    _check_dev("grad_b", gb, a.dtype, a.shape)
+    _check_dev("grad_h0", gh0, torch.float32, (B, D))
+    nbytes = lib.lrs_scan_workspace_bytes(B, D, T, LAYOUTS[layout], DTYPES[a.dtype])
+    ws = _workspace(nbytes, a.device, workspace)
+    _call(lib.lrs_scan_bwd(_ptr(a), _ptr(h), _ptr(h0), _ptr(grad_h), _ptr(ga), _ptr(gb), _ptr(gh0),
+                           B, D, T, LAYOUTS[layout], DTYPES[a.dtype], _ptr(ws), nbytes,
+                           _stream(a.device)), "lrs_scan_bwd")
+    return ga, gb, gh0
+
+
+def sru_fwd(z_f, z_r, z_x, bias_f, bias_r, c0=None, want_c_last: bool = False, out=None,
+            workspace=None):
+    """Fused SRU layer on [T,B,D] pre-activations (bf16 or fp32).  Returns h or (h, c_last)."""
+    lib = load()
+    if z_f.dim() != 3:
+        raise ValueError("z_f must be [T,B,D]")
+    T, B, D = (int(x) for x in z_f.shape)
+    io = z_f.dtype
+    for name, t in (("z_f", z_f), ("z_r", z_r), ("z_x", z_x)):
+        _check_dev(name, t, io, z_f.shape)
+    _check_dev("bias_f", bias_f, torch.float32, (D,))
+    _check_dev("bias_r", bias_r, torch.float32, (D,))
+    _check_dev("c0", c0, torch.float32, (B, D))
+    h = torch.empty_like(z_f) if out is None else out
+    _check_dev("out", h, io, z_f.shape)
+    c_last = torch.empty((B, D), dtype=torch.float32, device=z_f.device) if want_c_last else None
+    nbytes = lib.lrs_sru_workspace_bytes(T, B, D)
+    ws = _workspace(nbytes, z_f.device, workspace)
+    _call(lib.lrs_sru_fwd(_ptr(z_f), _ptr(z_r), _ptr(z_x), _ptr(bias_f), _ptr(bias_r), _ptr(c0),
+                          _ptr(h), _ptr(c_last), T, B, D, DTYPES[io], _ptr(ws), nbytes,
+                          _stream(z_f.device)), "lrs_sru_fwd")
+    return (h, c_last) if want_c_last else h
+
+
+def deer_solve(w, u, h0=None, h_init=None, eps: float = 1e-5, k_max: int = 5, out=None,
+               workspace=None):
+    """DEER Newton solve of h_t = tanh(w h_{t-1} + u_t); u: [B,D,T] fp32, w: [D].
+
+    Returns (h, info) with info = {"iters", "deltas", "converged", "status"}.
+    A non-finite final update is reported in info["status"] rather than raised."""
+    lib = load()
+    B, D, T = _dims(u, "bdt")
+    _check_dev("u", u, torch.float32, u.shape)
+    _check_dev("w", w, torch.float32, (D,))
+    _check_dev("h0", h0, torch.float32, (B, D))
+    _check_dev("h_init", h_init, torch.float32, u.shape)
+    h = torch.empty_like(u) if out is None else out
+    _check_dev("out", h, torch.float32, u.shape)
+    nbytes = lib.lrs_deer_workspace_bytes(B, D, T, k_max)
+    ws = _workspace(nbytes, u.device, workspace)
+    iters = ctypes.c_int(0)
+    conv = ctypes.c_int(0)
+    deltas = (ctypes.c_float * max(k_max, 1))()
+    rc = lib.lrs_deer_solve(_ptr(w), _ptr(u), _ptr(h0), _ptr(h_init), _ptr(h), B, D, T,
+                            float(eps), int(k_max), ctypes.byref(iters), deltas,
+                            ctypes.byref(conv), _ptr(ws), nbytes, _stream(u.device))
+    if rc not in (LRS_OK, LRS_ERR_NONFINITE):
+        raise LrsError(rc, "lrs_deer_solve")
+    info = {"iters": iters.value, "deltas": [float(deltas[i]) for i in range(iters.value)],
+            "converged": bool(conv.value), "status": int(rc)}
+    return h, info

@@ -1,0 +1,423 @@
+// lrs_api.hip -- the C ABI declared in include/lrs.h: argument validation,
+// workspace carving and launch-plan choice.  All device work is enqueued on
+// the caller's stream; nothing here allocates device memory.
+#include <math.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/lrs.h"
+#include "lrs_internal.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  return !__builtin_mul_overflow(a, b, out);
+}
+
+// B*D*T without overflow, and small enough that byte offsets fit in int64.
+bool shape_ok(int64_t B, int64_t D, int64_t T, int64_t* C, int64_t* N) {
+  if (B < 0 || D < 0 || T < 0) return false;
+  if (!mul_ok(B, D, C) || !mul_ok(*C, T, N)) return false;
+  return *N <= ((int64_t)1 << 60);
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool overlap(const void* p, size_t pn, const void* q, size_t qn) {
+  if (!p || !q || pn == 0 || qn == 0) return false;
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + qn && b < a + pn;
+}
+
+struct Carve {
+  char* base;
+  size_t used = 0;
+  explicit Carve(void* ws) : base((char*)ws) {}
+  template <typename T>
+  T* take(int64_t n) {
+    if (n <= 0) return nullptr;
+    T* p = (T*)(base + used);
+    used = align_up(used + (size_t)n * sizeof(T));
+    return p;
+  }
+};
+
+// Bytes to carve `nstatus` 64-bit words + `ntickets` counters (+ slack so the
+// caller's pointer need not be aligned).
+size_t lookback_bytes(int64_t nstatus, int64_t ntickets) {
+  if (nstatus <= 0) return 0;
+  return kAlign + align_up((size_t)nstatus * 8) + align_up((size_t)ntickets * 4);
+}
+
+void* align_ptr(void* p) { return (void*)(((uintptr_t)p + kAlign - 1) & ~(uintptr_t)(kAlign - 1)); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LRS_OK : LRS_ERR_HIP; }
+
+// Launch-size guard: HIP grids are limited to 2^32-1 work-items per dimension.
+bool grid_ok(int64_t blocks, int threads) { return blocks > 0 && blocks * threads < (1ll << 32); }
+
+int scan_ws_needs(int64_t C, int64_t T, int layout, size_t* bytes) {
+  if (layout == LRS_LAYOUT_BDT) {
+    const lrs::RowPlan p = lrs::plan_rows(T, 16);
+    *bytes = p.nchunk > 1 ? lookback_bytes(C * p.nchunk, C) : 0;
+  } else {
+    const lrs::ColPlan f = lrs::plan_scan_fwd_tbd(C, T), b = lrs::plan_scan_bwd_tbd(C, T);
+    const size_t bf = lookback_bytes(lrs::col_status_words(f), f.ncb);
+    const size_t bb = lookback_bytes(lrs::col_status_words(b), b.ncb);
+    *bytes = bf > bb ? bf : bb;
+  }
+  return LRS_OK;
+}
+
+}  // namespace
+
+// Fill dst[0..n) with src[0..n) or with zero (small per-channel outputs of
+// empty-time problems).
+namespace lrs {
+__global__ void k_copy_or_zero(float* __restrict__ dst, const float* __restrict__ src, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src ? src[i] : 0.0f;
+}
+hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t s) {
+  if (n <= 0 || !dst) return hipSuccess;
+  hipLaunchKernelGGL(k_copy_or_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dst, src,
+                     n);
+  return hipGetLastError();
+}
+}  // namespace lrs
+
+extern "C" {
+
+const char* lrs_status_string(int status) {
+  switch (status) {
+    case LRS_OK: return "LRS_OK";
+    case LRS_ERR_INVALID_ARG: return "LRS_ERR_INVALID_ARG: invalid argument";
+    case LRS_ERR_UNSUPPORTED: return "LRS_ERR_UNSUPPORTED: not supported by this build";
+    case LRS_ERR_WORKSPACE: return "LRS_ERR_WORKSPACE: workspace missing or too small";
+    case LRS_ERR_HIP: return "LRS_ERR_HIP: HIP runtime or launch failure";
+    case LRS_ERR_NONFINITE: return "LRS_ERR_NONFINITE: non-finite DEER update";
+    default: return "LRS_ERR_UNKNOWN";
+  }
+}
+
+int lrs_version(void) { return 100; }
+
+// ------------------------------------------------------------------- scan
+
+size_t lrs_scan_workspace_bytes(int64_t B, int64_t D, int64_t T, int layout, int dtype) {
+  int64_t C, N;
+  if (!shape_ok(B, D, T, &C, &N) || (layout != LRS_LAYOUT_BDT && layout != LRS_LAYOUT_TBD) ||
+      (dtype != LRS_F32 && dtype != LRS_BF16))
+    return 0;
+  if (N == 0) return 0;
+  size_t bytes = 0;
+  scan_ws_needs(C, T, layout, &bytes);
+  return bytes;
+}
+
+static int scan_common_checks(int64_t B, int64_t D, int64_t T, int layout, int dtype,
+                              int64_t* C, int64_t* N) {
+  if (!shape_ok(B, D, T, C, N)) return LRS_ERR_INVALID_ARG;
+  if (layout != LRS_LAYOUT_BDT && layout != LRS_LAYOUT_TBD) return LRS_ERR_INVALID_ARG;
+  if (dtype != LRS_F32 && dtype != LRS_BF16) return LRS_ERR_INVALID_ARG;
+  if (dtype != LRS_F32) return LRS_ERR_UNSUPPORTED;
+  return LRS_OK;
+}
+
+int lrs_scan_fwd(const void* a, const void* b, const float* h0, void* h, int64_t B, int64_t D,
+                 int64_t T, int layout, int dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  int64_t C, N;
+  int rc = scan_common_checks(B, D, T, layout, dtype, &C, &N);
+  if (rc != LRS_OK) return rc;
+  if (N == 0) return LRS_OK;
+  if (!a || !b || !h) return LRS_ERR_INVALID_ARG;
+  if (!aligned(a, 4) || !aligned(b, 4) || !aligned(h, 4) || (h0 && !aligned(h0, 4)))
+    return LRS_ERR_INVALID_ARG;
+  const size_t nbytes = (size_t)N * 4;
+  if (overlap(h, nbytes, a, nbytes) || overlap(h, nbytes, b, nbytes) ||
+      overlap(h, nbytes, h0, (size_t)C * 4))
+    return LRS_ERR_INVALID_ARG;
+  size_t need = 0;
+  scan_ws_needs(C, T, layout, &need);
+  if (need && (!workspace || workspace_bytes < need)) return LRS_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const bool al16 = aligned(a, 16) && aligned(b, 16) && aligned(h, 16);
+
+  if (layout == LRS_LAYOUT_BDT) {
+    const lrs::RowPlan p = lrs::plan_rows(T, 16);
+    if (!grid_ok(C * p.nchunk, p.nt)) return LRS_ERR_UNSUPPORTED;
+    uint64_t* status = nullptr;
+    unsigned* tickets = nullptr;
+    if (p.nchunk > 1) {
+      Carve cv(align_ptr(workspace));
+      status = cv.take<uint64_t>(C * p.nchunk);
+      tickets = cv.take<unsigned>(C);
+      rc = hip_status(lrs::launch_reset(status, C * p.nchunk, tickets, C, nullptr, 0, s));
+      if (rc != LRS_OK) return rc;
+    }
+    const int vec = al16 && (T % 4 == 0);
+    return hip_status(lrs::launch_scan_fwd_bdt((const float*)a, (const float*)b, h0, (float*)h, C,
+                                               T, p, vec, status, tickets, s));
+  }
+  const lrs::ColPlan p = lrs::plan_scan_fwd_tbd(C, T);
+  if (!grid_ok(p.ncb * p.ntb, p.nw * 64)) return LRS_ERR_UNSUPPORTED;
+  uint64_t* status = nullptr;
+  unsigned* tickets = nullptr;
+  const int64_t nst = lrs::col_status_words(p);
+  if (nst > 0) {
+    Carve cv(align_ptr(workspace));
+    status = cv.take<uint64_t>(nst);
+    tickets = cv.take<unsigned>(p.ncb);
+    rc = hip_status(lrs::launch_reset(status, nst, tickets, p.ncb, nullptr, 0, s));
+    if (rc != LRS_OK) return rc;
+  }
+  const int vec = al16 && (C % p.cpt == 0);
+  return hip_status(lrs::launch_scan_fwd_tbd((const float*)a, (const float*)b, h0, (float*)h, C, T,
+                                             p, vec, status, tickets, s));
+}
+
+int lrs_scan_bwd(const void* a, const void* h, const float* h0, const void* grad_h, void* grad_a,
+                 void* grad_b, float* grad_h0, int64_t B, int64_t D, int64_t T, int layout,
+                 int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int64_t C, N;
+  int rc = scan_common_checks(B, D, T, layout, dtype, &C, &N);
+  if (rc != LRS_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  if (N == 0) {
+    // no time steps: nothing depends on h0, so its gradient is zero
+    if (T == 0 && C > 0 && grad_h0) return hip_status(lrs::launch_copy_or_zero(grad_h0, nullptr, C, s));
+    return LRS_OK;
+  }
+  if (!a || !h || !grad_h || !grad_a || !grad_b) return LRS_ERR_INVALID_ARG;
+  if (!aligned(a, 4) || !aligned(h, 4) || !aligned(grad_h, 4) || !aligned(grad_a, 4) ||
+      !aligned(grad_b, 4) || (h0 && !aligned(h0, 4)) || (grad_h0 && !aligned(grad_h0, 4)))
+    return LRS_ERR_INVALID_ARG;
+  const size_t nb = (size_t)N * 4, cb = (size_t)C * 4;
+  // outputs must not overlap inputs, except grad_b == grad_h exactly
+  const void* ins[4] = {a, h, h0, grad_h};
+  const size_t insz[4] = {nb, nb, cb, nb};
+  for (int i = 0; i < 4; ++i) {
+    if (overlap(grad_a, nb, ins[i], insz[i])) return LRS_ERR_INVALID_ARG;
+    if (i != 3 && overlap(grad_b, nb, ins[i], insz[i])) return LRS_ERR_INVALID_ARG;
+    if (overlap(grad_h0, cb, ins[i], insz[i])) return LRS_ERR_INVALID_ARG;
+  }
+  if (grad_b != grad_h && overlap(grad_b, nb, grad_h, nb)) return LRS_ERR_INVALID_ARG;
+  if (overlap(grad_a, nb, grad_b, nb) || overlap(grad_h0, cb, grad_a, nb) ||
+      overlap(grad_h0, cb, grad_b, nb))
+    return LRS_ERR_INVALID_ARG;
+  size_t need = 0;
+  scan_ws_needs(C, T, layout, &need);
+  if (need && (!workspace || workspace_bytes < need)) return LRS_ERR_WORKSPACE;
+  const bool al16 = aligned(a, 16) && aligned(h, 16) && aligned(grad_h, 16) &&
+                    aligned(grad_a, 16) && aligned(grad_b, 16);
+
+  if (layout == LRS_LAYOUT_BDT) {
+    const lrs::RowPlan p = lrs::plan_rows(T, 16);
+    if (!grid_ok(C * p.nchunk, p.nt)) return LRS_ERR_UNSUPPORTED;
+    uint64_t* status = nullptr;
+    unsigned* tickets = nullptr;
+    if (p.nchunk > 1) {
+      Carve cv(align_ptr(workspace));
+      status = cv.take<uint64_t>(C * p.nchunk);
+      tickets = cv.take<unsigned>(C);
+      rc = hip_status(lrs::launch_reset(status, C * p.nchunk, tickets, C, nullptr, 0, s));
+      if (rc != LRS_OK) return rc;
+    }
+    const int vec = al16 && (T % 4 == 0);
+    return hip_status(lrs::launch_scan_bwd_bdt((const float*)a, (const float*)h, h0,
+                                               (const float*)grad_h, (float*)grad_a,
+                                               (float*)grad_b, grad_h0, C, T, p, vec, status,
+                                               tickets, s));
+  }
+  const lrs::ColPlan p = lrs::plan_scan_bwd_tbd(C, T);
+  if (!grid_ok(p.ncb * p.ntb, p.nw * 64)) return LRS_ERR_UNSUPPORTED;
+  uint64_t* status = nullptr;
+  unsigned* tickets = nullptr;
+  const int64_t nst = lrs::col_status_words(p);
+  if (nst > 0) {
+    Carve cv(align_ptr(workspace));
+    status = cv.take<uint64_t>(nst);
+    tickets = cv.take<unsigned>(p.ncb);
+    rc = hip_status(lrs::launch_reset(status, nst, tickets, p.ncb, nullptr, 0, s));
+    if (rc != LRS_OK) return rc;
+  }
+  const int vec = al16 && (C % p.cpt == 0);
+  return hip_status(lrs::launch_scan_bwd_tbd((const float*)a, (const float*)h, h0,
+                                             (const float*)grad_h, (float*)grad_a, (float*)grad_b,
+                                             grad_h0, C, T, p, vec, status, tickets, s));
+}
+
+// -------------------------------------------------------------------- SRU
+
+size_t lrs_sru_workspace_bytes(int64_t T, int64_t B, int64_t D) {
+  int64_t C, N;
+  if (!shape_ok(B, D, T, &C, &N) || N == 0) return 0;
+  size_t b1 = 0, b2 = 0;
+  {
+    const lrs::ColPlan p = lrs::plan_sru(C, T, LRS_BF16);
+    b1 = lookback_bytes(lrs::col_status_words(p), p.ncb);
+  }
+  {
+    const lrs::ColPlan p = lrs::plan_sru(C, T, LRS_F32);
+    b2 = lookback_bytes(lrs::col_status_words(p), p.ncb);
+  }
+  return b1 > b2 ? b1 : b2;
+}
+
+int lrs_sru_fwd(const void* z_f, const void* z_r, const void* z_x, const float* bias_f,
+                const float* bias_r, const float* c0, void* h, float* c_last, int64_t T,
+                int64_t B, int64_t D, int io_dtype, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  int64_t C, N;
+  if (!shape_ok(B, D, T, &C, &N)) return LRS_ERR_INVALID_ARG;
+  if (io_dtype != LRS_F32 && io_dtype != LRS_BF16) return LRS_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (N == 0) {
+    if (T == 0 && C > 0 && c_last) return hip_status(lrs::launch_copy_or_zero(c_last, c0, C, s));
+    return LRS_OK;
+  }
+  if (!z_f || !z_r || !z_x || !bias_f || !bias_r || !h) return LRS_ERR_INVALID_ARG;
+  const size_t es = io_dtype == LRS_BF16 ? 2 : 4;
+  if (!aligned(z_f, es) || !aligned(z_r, es) || !aligned(z_x, es) || !aligned(h, es) ||
+      !aligned(bias_f, 4) || !aligned(bias_r, 4) || (c0 && !aligned(c0, 4)) ||
+      (c_last && !aligned(c_last, 4)))
+    return LRS_ERR_INVALID_ARG;
+  const size_t nb = (size_t)N * es, cb = (size_t)C * 4, db = (size_t)D * 4;
+  const void* ins[6] = {z_f, z_r, z_x, bias_f, bias_r, c0};
+  const size_t insz[6] = {nb, nb, nb, db, db, cb};
+  for (int i = 0; i < 6; ++i)
+    if (overlap(h, nb, ins[i], insz[i]) || overlap(c_last, cb, ins[i], insz[i]))
+      return LRS_ERR_INVALID_ARG;
+  if (overlap(h, nb, c_last, cb)) return LRS_ERR_INVALID_ARG;
+  const lrs::ColPlan p = lrs::plan_sru(C, T, io_dtype);
+  if (!grid_ok(p.ncb * p.ntb, p.nw * 64)) return LRS_ERR_UNSUPPORTED;
+  const int64_t nst = lrs::col_status_words(p);
+  const size_t need = lookback_bytes(nst, p.ncb);
+  if (need && (!workspace || workspace_bytes < need)) return LRS_ERR_WORKSPACE;
+  uint64_t* status = nullptr;
+  unsigned* tickets = nullptr;
+  if (nst > 0) {
+    Carve cv(align_ptr(workspace));
+    status = cv.take<uint64_t>(nst);
+    tickets = cv.take<unsigned>(p.ncb);
+    const int rc = hip_status(lrs::launch_reset(status, nst, tickets, p.ncb, nullptr, 0, s));
+    if (rc != LRS_OK) return rc;
+  }
+  const size_t rowbytes = (size_t)p.cpt * es;
+  const int vec = aligned(z_f, rowbytes) && aligned(z_r, rowbytes) && aligned(z_x, rowbytes) &&
+                  aligned(h, rowbytes) && (C % p.cpt == 0);
+  return hip_status(lrs::launch_sru_fwd(z_f, z_r, z_x, bias_f, bias_r, c0, h, c_last, T, B, D,
+                                        io_dtype, p, vec, status, tickets, s));
+}
+
+// ------------------------------------------------------------------- DEER
+
+static lrs::RowPlan deer_plan(int64_t T) { return lrs::plan_rows(T, 32); }
+
+size_t lrs_deer_workspace_bytes(int64_t B, int64_t D, int64_t T, int k_max) {
+  int64_t C, N;
+  if (!shape_ok(B, D, T, &C, &N) || k_max < 1) return 0;
+  if (N == 0) return 0;
+  const lrs::RowPlan p = deer_plan(T);
+  size_t bytes = kAlign + align_up((size_t)k_max * 4) + align_up((size_t)N * 4);
+  if (p.nchunk > 1) bytes += align_up((size_t)(C * p.nchunk) * 8) + align_up((size_t)C * 4);
+  return bytes;
+}
+
+int lrs_deer_solve(const float* w, const float* u, const float* h0, const float* h_init, float* h,
+                   int64_t B, int64_t D, int64_t T, float eps, int k_max, int* iters_out,
+                   float* deltas_out, int* converged_out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int64_t C, N;
+  if (!shape_ok(B, D, T, &C, &N) || k_max < 1 || k_max > 1000000) return LRS_ERR_INVALID_ARG;
+  if (N == 0) {
+    if (iters_out) *iters_out = 0;
+    if (converged_out) *converged_out = 1;
+    if (deltas_out) memset(deltas_out, 0, sizeof(float) * (size_t)k_max);
+    return LRS_OK;
+  }
+  if (!w || !u || !h) return LRS_ERR_INVALID_ARG;
+  if (!aligned(w, 4) || !aligned(u, 4) || !aligned(h, 4) || (h0 && !aligned(h0, 4)) ||
+      (h_init && !aligned(h_init, 4)))
+    return LRS_ERR_INVALID_ARG;
+  const size_t nb = (size_t)N * 4, cb = (size_t)C * 4;
+  if (overlap(h, nb, w, (size_t)D * 4) || overlap(h, nb, u, nb) || overlap(h, nb, h0, cb))
+    return LRS_ERR_INVALID_ARG;
+  if (h_init && h_init != h && overlap(h, nb, h_init, nb)) return LRS_ERR_INVALID_ARG;
+  const size_t need = lrs_deer_workspace_bytes(B, D, T, k_max);
+  if (!workspace || workspace_bytes < need) return LRS_ERR_WORKSPACE;
+  const lrs::RowPlan p = deer_plan(T);
+  if (!grid_ok(C * p.nchunk, p.nt)) return LRS_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+
+  Carve cv(align_ptr(workspace));
+  uint32_t* delta_bits = cv.take<uint32_t>(k_max);
+  float* ybuf = cv.take<float>(N);
+  uint64_t* status = nullptr;
+  unsigned* tickets = nullptr;
+  if (p.nchunk > 1) {
+    status = cv.take<uint64_t>(C * p.nchunk);
+    tickets = cv.take<unsigned>(C);
+  }
+  if (overlap(ybuf, nb, u, nb) || overlap(ybuf, nb, h, nb) || overlap(ybuf, nb, h_init, nb))
+    return LRS_ERR_INVALID_ARG;
+
+  // ping-pong: iteration i writes P[i % 2]; if the starting iterate lives in h,
+  // iteration 0 must not write h, so the roles swap
+  float* P[2] = {h, ybuf};
+  if (h_init == h) { P[0] = ybuf; P[1] = h; }
+  const int vec = aligned(u, 16) && aligned(h, 16) && aligned(ybuf, 16) &&
+                  (!h_init || aligned(h_init, 16)) && (T % 4 == 0);
+  int rc = hip_status(lrs::launch_reset(status, p.nchunk > 1 ? C * p.nchunk : 0, tickets,
+                                        p.nchunk > 1 ? C : 0, delta_bits, k_max, s));
+  if (rc != LRS_OK) return rc;
+  for (int i = 0; i < k_max; ++i) {
+    if (i > 0 && p.nchunk > 1) {
+      rc = hip_status(lrs::launch_reset(status, C * p.nchunk, tickets, C, nullptr, 0, s));
+      if (rc != LRS_OK) return rc;
+    }
+    const float* y = (i == 0) ? h_init : P[(i - 1) & 1];
+    rc = hip_status(lrs::launch_deer_iter(w, u, y, h0, P[i & 1], C, D, T, p, vec, status,
+                                          tickets, delta_bits, i, eps, s));
+    if (rc != LRS_OK) return rc;
+  }
+  std::vector<uint32_t> dbits((size_t)k_max);
+  if (hipMemcpyAsync(dbits.data(), delta_bits, sizeof(uint32_t) * (size_t)k_max,
+                     hipMemcpyDeviceToHost, s) != hipSuccess)
+    return LRS_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return LRS_ERR_HIP;
+  int iters = k_max;
+  float last = 0.0f;
+  for (int i = 0; i < k_max; ++i) {
+    float d;
+    memcpy(&d, &dbits[(size_t)i], 4);
+    last = d;
+    if (d < eps) {
+      iters = i + 1;
+      break;
+    }
+  }
+  float* result = P[(iters - 1) & 1];
+  if (result != h) {
+    if (hipMemcpyAsync(h, result, nb, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return LRS_ERR_HIP;
+  }
+  if (iters_out) *iters_out = iters;
+  if (converged_out) *converged_out = (last < eps) ? 1 : 0;
+  if (deltas_out) {
+    for (int i = 0; i < k_max; ++i) {
+      float d = 0.0f;
+      if (i < iters) memcpy(&d, &dbits[(size_t)i], 4);
+      deltas_out[i] = d;
+    }
+  }
+  return isfinite(last) ? LRS_OK : LRS_ERR_NONFINITE;
+}
+
+}  // extern "C"

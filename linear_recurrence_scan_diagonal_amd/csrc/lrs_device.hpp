@@ -1,0 +1,189 @@
+// lrs_device.hpp -- device building blocks for the diagonal linear-recurrence
+// scan on gfx950 (CDNA4, wave64).
+//
+// The recurrence h_t = a_t*h_{t-1} + b_t is a composition of affine maps
+// x -> a*x + b.  Composition is associative, which is what lets the sequence be
+// evaluated as a parallel prefix scan (page "CUDA并行化RNN训练：从O(T)到O(log T)
+// 的工程实践与参数调优", body, parallel-scan paragraph: treat the step as an
+// associative operation and divide and conquer; page "RNN CUDA内核优化：实现序列
+// 长度无关的恒定推理延迟", body: the cell-state update is a linear recurrence with
+// time-varying coefficients, a prefix-scan problem).
+//
+// Levels used by every kernel in this library:
+//   1. thread strip  : each lane folds K consecutive steps serially (FMA);
+//   2. wave64 scan   : 6 DPP steps (row_shr 1,2,4,8; row_bcast 15,31);
+//   3. block scan    : per-wave aggregates combined through LDS;
+//   4. chunk carry   : decoupled look-back over per-chunk status words in HBM,
+//                      so a channel longer than one workgroup's chunk is still
+//                      a single pass over memory.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lrs {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// One Hillis-Steele step across lanes: lane i combines with the lane that the
+// DPP control selects (an earlier lane in scan order).  Lanes whose source is
+// outside the selected rows keep the identity (1, 0), via DPP's "old" value.
+// The earlier element is the left operand:
+//   (A_e, B_e) o (A, B) = (A_e*A, A*B_e + B).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void dpp_combine(float& A, float& B) {
+  const float Ae = as_f32((uint32_t)__builtin_amdgcn_update_dpp(
+      (int)as_u32(1.0f), (int)as_u32(A), CTRL, ROW_MASK, 0xf, false));
+  const float Be = as_f32((uint32_t)__builtin_amdgcn_update_dpp(
+      0, (int)as_u32(B), CTRL, ROW_MASK, 0xf, false));
+  B = __builtin_fmaf(A, Be, B);
+  A = Ae * A;
+}
+
+// Inclusive scan of (A, B) over the 64 lanes of a wave, lane order = scan order.
+__device__ __forceinline__ void wave_scan(float& A, float& B) {
+  dpp_combine<0x111, 0xf>(A, B);  // row_shr:1
+  dpp_combine<0x112, 0xf>(A, B);  // row_shr:2
+  dpp_combine<0x114, 0xf>(A, B);  // row_shr:4
+  dpp_combine<0x118, 0xf>(A, B);  // row_shr:8
+  dpp_combine<0x142, 0xa>(A, B);  // row_bcast:15 into rows 1 and 3
+  dpp_combine<0x143, 0xc>(A, B);  // row_bcast:31 into rows 2 and 3
+}
+
+// Value of the previous lane (wave_shr:1); lane 0 receives `lane0`.
+__device__ __forceinline__ float wave_shift_up(float x, float lane0) {
+  return as_f32((uint32_t)__builtin_amdgcn_update_dpp((int)as_u32(lane0), (int)as_u32(x),
+                                                      0x138, 0xf, 0xf, false));
+}
+
+// Maximum of a 32-bit unsigned value over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)v, off, kWave);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Look-back status words.  One 64-bit word per (channel, chunk), written and
+// read with relaxed agent-scope atomics (coherent across the XCDs' L2s), so the
+// payload travels in the same word as its state and no fences are needed.
+//   0xFFFFFFFF'FFFFFFFF        not ready (the reset value)
+//   lo = A bits, hi = B bits   aggregate (A, B) of this chunk alone
+//   lo = 0xFFFFFFFE, hi = x    inclusive: the state at the end of the chunk
+// A is canonicalised so that neither marker can occur as a real A: any NaN is
+// replaced by the default quiet NaN 0x7FC00000.
+// ---------------------------------------------------------------------------
+constexpr uint64_t kStatusEmpty = ~0ull;
+constexpr uint32_t kIncTag = 0xFFFFFFFEu;
+
+__device__ __forceinline__ uint64_t pack_agg(float A, float B) {
+  uint32_t a = (A != A) ? 0x7FC00000u : as_u32(A);
+  return (uint64_t)a | ((uint64_t)as_u32(B) << 32);
+}
+__device__ __forceinline__ uint64_t pack_inc(float x) {
+  return (uint64_t)kIncTag | ((uint64_t)as_u32(x) << 32);
+}
+__device__ __forceinline__ void status_store(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t status_load(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Single-lane look-back: returns the state entering chunk `c`, given the status
+// words of chunks 0..c-1 of one channel (st points at chunk 0, consecutive
+// chunks `stride` words apart).  Walks back over aggregates until it meets an
+// inclusive state.  Chunk indices come from a per-channel ticket, so every
+// predecessor is resident or finished and the spin terminates.
+//
+// Safety net: a predecessor publishes its aggregate within microseconds of
+// starting, so a wait of kSpinLimit polls (~0.1 s) can only mean corrupted
+// status words; the carry then becomes NaN, which poisons the outputs of this
+// channel instead of hanging the device.
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+__device__ __forceinline__ float lookback_carry(const uint64_t* st, int c, int64_t stride) {
+  float accA = 1.0f, accB = 0.0f;  // composition of chunks p+1 .. c-1
+  int p = c - 1;
+  uint32_t spins = 0;
+  while (true) {
+    const uint64_t v = status_load(st + (int64_t)p * stride);
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    if (v == kStatusEmpty) {
+      if (++spins > kSpinLimit) return __builtin_nanf("");
+      __builtin_amdgcn_s_sleep(1);
+      continue;
+    }
+    if (lo == kIncTag) return __builtin_fmaf(accA, as_f32(hi), accB);
+    // the aggregate of chunk p precedes the chunks accumulated so far
+    accB = __builtin_fmaf(accA, as_f32(hi), accB);
+    accA = accA * as_f32(lo);
+    --p;
+  }
+}
+
+__device__ __forceinline__ unsigned take_ticket(unsigned* counter) {
+  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Strip loads/stores: K consecutive floats starting at element t0 of a row of
+// length T.  Full in-range strips use 16-byte accesses when `vec` is true
+// (row starts and base pointers 16-byte aligned); the ragged tail is
+// predicated element by element and filled with `fill`.
+// ---------------------------------------------------------------------------
+template <int K>
+__device__ __forceinline__ void load_strip(const float* __restrict__ row, int64_t t0, int64_t T,
+                                           bool vec, float fill, float (&v)[K]) {
+  if (vec && t0 + K <= T) {
+    static_assert(K % 4 == 0, "strip length must be a multiple of 4");
+#pragma unroll
+    for (int q = 0; q < K / 4; ++q) {
+      const float4 x = *reinterpret_cast<const float4*>(row + t0 + 4 * q);
+      v[4 * q + 0] = x.x;
+      v[4 * q + 1] = x.y;
+      v[4 * q + 2] = x.z;
+      v[4 * q + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < K; ++j) v[j] = (t0 + j < T) ? row[t0 + j] : fill;
+  }
+}
+
+template <int K>
+__device__ __forceinline__ void store_strip(float* __restrict__ row, int64_t t0, int64_t T,
+                                            bool vec, const float (&v)[K]) {
+  if (vec && t0 + K <= T) {
+#pragma unroll
+    for (int q = 0; q < K / 4; ++q) {
+      *reinterpret_cast<float4*>(row + t0 + 4 * q) =
+          make_float4(v[4 * q + 0], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      if (t0 + j < T) row[t0 + j] = v[j];
+  }
+}
+
+// tanh from its definition through exp: tanh(x) = 1 - 2/(exp(2x) + 1).
+// Saturates correctly at both ends (exp overflow -> 1, underflow -> -1);
+// absolute error a few fp32 ulps of 1.
+__device__ __forceinline__ float tanh_fast(float x) {
+  const float e = __expf(2.0f * x);
+  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+}
+
+// logistic sigmoid 1/(1 + exp(-x))
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+
+}  // namespace lrs

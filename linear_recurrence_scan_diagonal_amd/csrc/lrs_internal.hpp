@@ -1,0 +1,59 @@
+// lrs_internal.hpp -- host-side plumbing shared by the kernel files and the
+// C ABI implementation (launch plans and launchers).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lrs {
+
+// Time-contiguous kernels: NT threads x K steps per chunk, nchunk chunks per channel.
+struct RowPlan {
+  int nt = 256;
+  int k = 4;
+  int64_t nchunk = 1;
+};
+RowPlan plan_rows(int64_t T, int kmax_strip);
+
+// Feature-contiguous kernels: blocks of 64*cpt channels x nw*l steps.
+struct ColPlan {
+  int nw = 8, l = 8, cpt = 4;
+  int64_t ncb = 1, ntb = 1;
+};
+ColPlan plan_cols(int64_t C, int64_t T, int nw, int l, int cpt);
+ColPlan plan_scan_fwd_tbd(int64_t C, int64_t T);
+ColPlan plan_scan_bwd_tbd(int64_t C, int64_t T);
+ColPlan plan_sru(int64_t C, int64_t T, int io_dtype);
+int64_t col_status_words(const ColPlan& p);
+
+// Resets look-back state: status words to "not ready", tickets and the
+// optional 32-bit words `zero` to 0.  Plain stores from a kernel, so the call
+// is safe inside captured graphs.
+hipError_t launch_reset(uint64_t* status, int64_t nstatus, unsigned* tickets, int64_t ntickets,
+                        uint32_t* zero, int64_t nzero, hipStream_t stream);
+
+hipError_t launch_scan_fwd_bdt(const float* a, const float* b, const float* h0, float* h,
+                               int64_t C, int64_t T, const RowPlan& p, int vec, uint64_t* status,
+                               unsigned* tickets, hipStream_t stream);
+hipError_t launch_scan_bwd_bdt(const float* a, const float* h, const float* h0, const float* g,
+                               float* da, float* db, float* dh0, int64_t C, int64_t T,
+                               const RowPlan& p, int vec, uint64_t* status, unsigned* tickets,
+                               hipStream_t stream);
+hipError_t launch_deer_iter(const float* w, const float* u, const float* y, const float* h0,
+                            float* yn, int64_t C, int64_t D, int64_t T, const RowPlan& p, int vec,
+                            uint64_t* status, unsigned* tickets, uint32_t* delta_bits, int iter,
+                            float eps, hipStream_t stream);
+
+hipError_t launch_scan_fwd_tbd(const float* a, const float* b, const float* h0, float* h,
+                               int64_t C, int64_t T, const ColPlan& p, int vec, uint64_t* status,
+                               unsigned* tickets, hipStream_t stream);
+hipError_t launch_scan_bwd_tbd(const float* a, const float* h, const float* h0, const float* g,
+                               float* da, float* db, float* dh0, int64_t C, int64_t T,
+                               const ColPlan& p, int vec, uint64_t* status, unsigned* tickets,
+                               hipStream_t stream);
+hipError_t launch_sru_fwd(const void* zf, const void* zr, const void* zx, const float* bias_f,
+                          const float* bias_r, const float* c0, void* h, float* c_last, int64_t T,
+                          int64_t B, int64_t D, int io_dtype, const ColPlan& p, int vec,
+                          uint64_t* status, unsigned* tickets, hipStream_t stream);
+
+}  // namespace lrs

@@ -51,15 +51,18 @@ def _workers() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
-def series(seed: int, tag: str, dist, channels, T: int) -> np.ndarray:
-    """float64 [len(channels), T]: per-channel streams, time order."""
+def series(seed: int, tag: str, dist, channels, T: int, dtype=np.float64) -> np.ndarray:
+    """[len(channels), T] per-channel streams in time order, drawn in float64.
+
+    dtype=np.float32 rounds each row once to fp32 as it is drawn (same values
+    as to_f32(series(...)), without holding the float64 array)."""
     channels = np.asarray(list(channels), dtype=np.int64)
-    out = np.empty((channels.size, T), dtype=np.float64)
+    out = np.empty((channels.size, T), dtype=dtype)
     t = TAGS[tag]
 
     def fill(lo, hi):
         for i in range(lo, hi):
-            out[i] = _draw(_rng(seed, t, int(channels[i])), dist, T)
+            out[i] = _draw(_rng(seed, t, int(channels[i])), dist, T)  # one rounding on assignment
 
     n = channels.size
     step = max(1, (n + _workers() * 4 - 1) // (_workers() * 4))
@@ -176,12 +179,13 @@ def scan_inputs(w: Workload, channels=None, with_grad: bool = True) -> dict:
 
     channels defaults to all B*D channels; h0 is returned as [len(channels)]."""
     ch = np.arange(w.C) if channels is None else np.asarray(channels)
-    out = {"a": to_f32(series(w.seed, "a", w.dists["a"], ch, w.T)),
-           "b": to_f32(series(w.seed, "b", w.dists["b"], ch, w.T))}
+    f32 = np.float32
+    out = {"a": series(w.seed, "a", w.dists["a"], ch, w.T, f32),
+           "b": series(w.seed, "b", w.dists["b"], ch, w.T, f32)}
     h0 = to_f32(params(w.seed, "h0", w.dists.get("h0", ("const", 0, 0)), (w.C,)))
     out["h0"] = h0[ch]
     if with_grad and "g" in w.dists:
-        out["g"] = to_f32(series(w.seed, "g", w.dists["g"], ch, w.T))
+        out["g"] = series(w.seed, "g", w.dists["g"], ch, w.T, f32)
     return out
 
 
@@ -201,7 +205,7 @@ def deer_inputs(w: Workload, channels=None) -> dict:
     """fp32 w [D], u [len(channels), T] (channel-major), h0 [len(channels)]."""
     ch = np.arange(w.C) if channels is None else np.asarray(channels)
     out = {"w": to_f32(params(w.seed, "w", w.dists["w"], (w.D,))),
-           "u": to_f32(series(w.seed, "u", w.dists["u"], ch, w.T))}
+           "u": series(w.seed, "u", w.dists["u"], ch, w.T, np.float32)}
     h0 = to_f32(params(w.seed, "h0", w.dists.get("h0", ("const", 0, 0)), (w.C,)))
     out["h0"] = h0[ch]
     return out

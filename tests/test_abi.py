@@ -1,0 +1,126 @@
+"""The C-ABI library loads without a GPU, exports every function include/lrs.h
+declares, and its host-side validation and workspace queries behave as the
+header states.  No call here reaches a HIP runtime function."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lrs.h")
+LIB = os.path.join(ROOT, "linear_recurrence_scan_diagonal_amd", "liblrs.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="liblrs.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"LRS_API\s+[\w\s\*]*?\b(lrs_\w+)\s*\(", text)))
+
+
+def header_constants():
+    text = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"#define\s+(LRS_\w+)\s+(\d+)", text)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from linear_recurrence_scan_diagonal_amd import binding
+    return binding.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 9, names
+    raw = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(raw, n), f"{n} declared in lrs.h but not exported"
+
+
+def test_binding_covers_exports():
+    from linear_recurrence_scan_diagonal_amd import binding
+    assert sorted(binding.EXPORTS) == declared_functions()
+
+
+def test_constants_match_binding():
+    from linear_recurrence_scan_diagonal_amd import binding
+    c = header_constants()
+    assert c["LRS_OK"] == binding.LRS_OK and c["LRS_ERR_NONFINITE"] == binding.LRS_ERR_NONFINITE
+    assert c["LRS_ERR_WORKSPACE"] == binding.LRS_ERR_WORKSPACE
+    assert c["LRS_LAYOUT_BDT"] == binding.LAYOUTS["bdt"] and c["LRS_LAYOUT_TBD"] == binding.LAYOUTS["tbd"]
+    assert c["LRS_F32"] == 0 and c["LRS_BF16"] == 1
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert lib.lrs_status_string(code).startswith(b"LRS_")
+    assert lib.lrs_status_string(99) == b"LRS_ERR_UNKNOWN"
+    assert lib.lrs_version() >= 100
+
+
+def test_scan_workspace_queries(lib):
+    # a channel that fits one workgroup needs no look-back workspace
+    assert lib.lrs_scan_workspace_bytes(8, 512, 4096, 0, 0) == 0
+    # a million-step channel does: one 8-byte word per chunk plus one ticket per channel
+    big = lib.lrs_scan_workspace_bytes(2, 256, 1 << 20, 0, 0)
+    assert big >= 512 * 256 * 8 + 512 * 4
+    assert lib.lrs_scan_workspace_bytes(-1, 1, 1, 0, 0) == 0
+    assert lib.lrs_scan_workspace_bytes(1, 1, 1, 7, 0) == 0
+    assert lib.lrs_scan_workspace_bytes(1 << 40, 1 << 40, 2, 0, 0) == 0  # overflow
+    assert lib.lrs_deer_workspace_bytes(16, 512, 8192, 5) >= 16 * 512 * 8192 * 4
+    assert lib.lrs_deer_workspace_bytes(1, 1, 1, 0) == 0
+
+
+def test_validation_before_any_launch(lib):
+    from linear_recurrence_scan_diagonal_amd import binding as b
+    p = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+    null = None
+    # negative size, bad layout, bad dtype, unsupported dtype, null pointers, misalignment
+    assert lib.lrs_scan_fwd(p, p, null, p, -1, 1, 1, 0, 0, null, 0, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_scan_fwd(p, p, null, p, 1, 1, 1, 5, 0, null, 0, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_scan_fwd(p, p, null, p, 1, 1, 1, 0, 9, null, 0, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_scan_fwd(p, p, null, p, 1, 1, 4, 0, 1, null, 0, null) == b.LRS_ERR_UNSUPPORTED
+    assert lib.lrs_scan_fwd(null, p, null, p, 1, 1, 4, 0, 0, null, 0, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_scan_fwd(ctypes.c_void_p(0x1002), p, null, ctypes.c_void_p(0x9000), 1, 1, 4, 0, 0,
+                            null, 0, null) == b.LRS_ERR_INVALID_ARG
+    # output overlapping an input
+    assert lib.lrs_scan_fwd(p, ctypes.c_void_p(0x8000), null, ctypes.c_void_p(0x1008), 1, 1, 64, 0,
+                            0, null, 0, null) == b.LRS_ERR_INVALID_ARG
+    # a multi-chunk channel without workspace
+    assert lib.lrs_scan_fwd(ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000000), null,
+                            ctypes.c_void_p(0x400000000), 1, 1, 1 << 20, 0, 0, null, 0,
+                            null) == b.LRS_ERR_WORKSPACE
+    # empty problems are valid and do nothing
+    assert lib.lrs_scan_fwd(null, null, null, null, 0, 5, 7, 0, 0, null, 0, null) == b.LRS_OK
+    assert lib.lrs_scan_fwd(null, null, null, null, 3, 5, 0, 1, 0, null, 0, null) == b.LRS_OK
+    # backward: grad_a aliasing a is rejected, grad_b == grad_h is accepted past the alias check
+    q = ctypes.c_void_p
+    assert lib.lrs_scan_bwd(q(0x10000), q(0x20000), null, q(0x30000), q(0x10000), q(0x40000), null,
+                            1, 1, 64, 0, 0, null, 0, null) == b.LRS_ERR_INVALID_ARG
+    # SRU and DEER argument checks
+    assert lib.lrs_sru_fwd(p, p, p, p, p, null, p, null, 4, 1, 1, 3, null, 0, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_sru_fwd(null, p, p, p, p, null, p, null, 4, 1, 1, 1, null, 0, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_deer_solve(p, p, null, null, p, 1, 1, 4, ctypes.c_float(1e-5), 0, None, None, None,
+                              null, 0, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_deer_solve(q(0x10000), q(0x20000), null, null, q(0x90000), 1, 1, 4,
+                              ctypes.c_float(1e-5), 5, None, None, None, null, 0,
+                              null) == b.LRS_ERR_WORKSPACE
+
+
+def test_product_path_has_no_fallback():
+    """The package never imports the oracle, and the binding raises when the
+    library is absent instead of computing anything itself."""
+    pkg = os.path.join(ROOT, "linear_recurrence_scan_diagonal_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            src = open(os.path.join(pkg, fn)).read()
+            assert "import oracle" not in src and "from oracle" not in src, fn
+    from linear_recurrence_scan_diagonal_amd import binding
+    saved, saved_lib = binding.LIB_PATH, binding._lib
+    try:
+        binding.LIB_PATH, binding._lib = "/nonexistent/liblrs.so", None
+        with pytest.raises(RuntimeError):
+            binding.load()
+    finally:
+        binding.LIB_PATH, binding._lib = saved, saved_lib

@@ -1,0 +1,174 @@
+"""GPU parity of the forward and backward scans against the fp64 oracle.
+
+Bar: max |gpu - oracle| / (1 + |oracle|) <= 1e-5 for every fp32 output tensor
+(h, dL/da, dL/db, dL/dh0).  Integer-valued inputs whose partial results are
+exact in fp32 must match bit for bit, whatever association order the kernels
+use (this is what catches look-back ordering or visibility bugs)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import linear_recurrence_scan_diagonal_amd as lrs
+from linear_recurrence_scan_diagonal_amd import inputs as I
+from conftest import relerr
+from gpu_util import DEV, from_dev, log, to_dev
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+LAYOUTS = ["bdt", "tbd"]
+
+
+def run_scan(x, B, D, T, layout, h0=True, bwd=True):
+    a = to_dev(x["a"], B, D, T, layout)
+    b = to_dev(x["b"], B, D, T, layout)
+    h0d = torch.from_numpy(x["h0"].reshape(B, D)).to(DEV) if h0 else None
+    h = lrs.scan_fwd(a, b, h0d, layout=layout)
+    out = {"h": h}
+    if bwd:
+        g = to_dev(x["g"], B, D, T, layout)
+        da, db, dh0 = lrs.scan_bwd(a, h, g, h0d, layout=layout)
+        out.update(da=da, db=db, dh0=dh0)
+    torch.cuda.synchronize()
+    res = {k: from_dev(v, B, D, T, layout) for k, v in out.items() if k != "dh0"}
+    if bwd:
+        res["dh0"] = out["dh0"].cpu().numpy().reshape(B * D)
+    return res
+
+
+def oracle_scan(x, h0=True, bwd=True):
+    h0v = x["h0"] if h0 else None
+    h = oracle.scan_fwd(x["a"], x["b"], h0v)
+    res = {"h": h}
+    if bwd:
+        res["da"], res["db"], res["dh0"] = oracle.scan_bwd(x["a"], h, h0v, x["g"])
+    return res
+
+
+def compare(got, ref, tol=TOL, tag=""):
+    errs = {k: relerr(got[k], ref[k]) for k in ref}
+    log(f"{tag} errors: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= tol, f"{tag}: {k} relerr {v:.3e} > {tol}"
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_scan_fwd_small_workload(layout):
+    w = I.WORKLOADS["scan_fwd_small"]
+    log(f"scan_fwd_small {layout} B={w.B} D={w.D} T={w.T}")
+    x = I.scan_inputs(w, with_grad=False)
+    got = run_scan(x, w.B, w.D, w.T, layout, bwd=False)
+    compare(got, oracle_scan(x, bwd=False), tag=f"scan_fwd_small/{layout}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_scan_fwd_bwd_workload(layout):
+    w = I.WORKLOADS["scan_fwd_bwd"]
+    log(f"scan_fwd_bwd {layout} B={w.B} D={w.D} T={w.T}")
+    x = I.scan_inputs(w)
+    got = run_scan(x, w.B, w.D, w.T, layout)
+    compare(got, oracle_scan(x), tag=f"scan_fwd_bwd/{layout}")
+
+
+SHAPES = [(1, 1, 1), (1, 3, 2), (2, 3, 5), (1, 7, 255), (3, 5, 1000), (1, 64, 1023),
+          (2, 33, 4095), (1, 17, 4096), (1, 9, 4097), (2, 3, 8191), (1, 5, 12345),
+          (1, 2, 40000), (3, 100, 129), (1, 300, 700), (1, 257, 64)]
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("B,D,T", SHAPES)
+def test_ragged_shapes(layout, B, D, T):
+    log(f"ragged {layout} B={B} D={D} T={T}")
+    w = I.scaled(I.WORKLOADS["scan_fwd_bwd"], B=B, D=D, T=T, seed=7000 + B * 131 + D * 7 + T)
+    x = I.scan_inputs(w)
+    compare(run_scan(x, B, D, T, layout), oracle_scan(x), tag=f"ragged/{layout}/{B}x{D}x{T}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_backward_alone_and_in_place(layout):
+    """Backward fed the oracle's h rounded to fp32 (same input on both sides),
+    and with grad_b written over grad_h."""
+    B, D, T = 2, 40, 9000
+    log(f"bwd alone {layout}")
+    w = I.scaled(I.WORKLOADS["scan_fwd_bwd"], B=B, D=D, T=T, seed=8101)
+    x = I.scan_inputs(w)
+    h32 = oracle.scan_fwd(x["a"], x["b"], x["h0"]).astype(np.float32)
+    ref = dict(zip(("da", "db", "dh0"), oracle.scan_bwd(x["a"], h32, x["h0"], x["g"])))
+    a = to_dev(x["a"], B, D, T, layout)
+    h = to_dev(h32, B, D, T, layout)
+    g = to_dev(x["g"], B, D, T, layout)
+    h0 = torch.from_numpy(x["h0"].reshape(B, D)).to(DEV)
+    da, db, dh0 = lrs.scan_bwd(a, h, g, h0, layout=layout, grad_b=g)
+    torch.cuda.synchronize()
+    assert db.data_ptr() == g.data_ptr()
+    got = {"da": from_dev(da, B, D, T, layout), "db": from_dev(db, B, D, T, layout),
+           "dh0": dh0.cpu().numpy().reshape(-1)}
+    compare(got, ref, tag=f"bwd-alone/{layout}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_exact_integer_inputs_bitwise(layout):
+    """a in {-1, 0, 1}, b, g, h0 small integers: every partial result is an integer
+    below 2^24, so any association order gives the same fp32 bits.  T spans
+    dozens of look-back chunks."""
+    B, D, T = 1, 6, 300_000
+    log(f"exact-integer {layout} T={T}")
+    rng = np.random.default_rng(4242)
+    a = rng.choice(np.array([-1.0, 0.0, 1.0, 1.0, 1.0], dtype=np.float32), size=(B * D, T))
+    b = rng.integers(-2, 3, size=(B * D, T)).astype(np.float32)
+    g = rng.integers(-2, 3, size=(B * D, T)).astype(np.float32)
+    h0 = rng.integers(-3, 4, size=B * D).astype(np.float32)
+    x = {"a": a, "b": b, "g": g, "h0": h0}
+    got = run_scan(x, B, D, T, layout)
+    ref = oracle_scan(x)
+    assert np.max(np.abs(ref["h"])) < 2 ** 24 and np.max(np.abs(ref["db"])) < 2 ** 24
+    for k in ("h", "db", "dh0"):
+        assert np.array_equal(got[k], ref[k].astype(np.float32)), k
+    # da = lam * h_{t-1}: one rounding of an exact product
+    assert np.array_equal(got["da"], ref["da"].astype(np.float32))
+
+
+def test_scan_long_workload():
+    """Million-step channels: every channel crosses 256 look-back chunks.
+    Compared on sampled channels (full rows) against the oracle."""
+    w = I.WORKLOADS["scan_long"]
+    log(f"scan_long B={w.B} D={w.D} T={w.T}: generating inputs")
+    x = I.scan_inputs(w)
+    B, D, T = w.B, w.D, w.T
+    log("scan_long: running on GPU")
+    a = to_dev(x["a"], B, D, T, "bdt")
+    b = to_dev(x["b"], B, D, T, "bdt")
+    g = to_dev(x["g"], B, D, T, "bdt")
+    h = lrs.scan_fwd(a, b, None)
+    da, db, dh0 = lrs.scan_bwd(a, h, g, None)
+    torch.cuda.synchronize()
+    sample = [0, 1, 2, 255, 256, 300, 510, 511]
+    sx = {k: x[k][sample] for k in ("a", "b", "g")}
+    sx["h0"] = x["h0"][sample]
+    ref = oracle_scan(sx, h0=False)
+    got = {"h": h.view(-1, T)[sample].cpu().numpy(), "da": da.view(-1, T)[sample].cpu().numpy(),
+           "db": db.view(-1, T)[sample].cpu().numpy(),
+           "dh0": dh0.view(-1)[sample].cpu().numpy()}
+    compare(got, ref, tag="scan_long")
+    # whole-array invariants: finite everywhere, and the adjoint identity
+    # <g, h> = <lam, b> per channel (h0 = 0) on every channel, in float64
+    assert torch.isfinite(h).all() and torch.isfinite(da).all() and torch.isfinite(db).all()
+    lhs = (g.double() * h.double()).sum(-1).view(-1)
+    rhs = (db.double() * b.double()).sum(-1).view(-1)
+    rel = ((lhs - rhs).abs() / (1 + lhs.abs())).max().item()
+    log(f"scan_long adjoint identity rel {rel:.2e}")
+    assert rel < 1e-3
+
+
+def test_layouts_agree_and_repeat():
+    """The two layouts give the same results within the bar, and repeated runs
+    of the multi-chunk path stay within the bar of each other."""
+    B, D, T = 2, 64, 20000
+    w = I.scaled(I.WORKLOADS["scan_fwd_bwd"], B=B, D=D, T=T, seed=9090)
+    x = I.scan_inputs(w)
+    r1 = run_scan(x, B, D, T, "bdt")
+    r2 = run_scan(x, B, D, T, "tbd")
+    r3 = run_scan(x, B, D, T, "bdt")
+    for k in r1:
+        assert relerr(r2[k], r1[k]) <= 2 * TOL
+        assert relerr(r3[k], r1[k]) <= 2 * TOL
