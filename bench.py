@@ -7,11 +7,14 @@ lrs_scan_bwd over the same resident inputs.  Other workloads (--workload):
 scan_long (T = 2^20), sru_fwd (bf16 SRU layer), deer (Newton solve),
 scan_fwd_small.
 
-Prints ONE JSON line.  `value` is scanned elements per second over the timed
-steps (inputs resident in HBM before timing starts).  `roofline` describes
+Prints ONE JSON line.  `value` is scanned elements per second over K timed
+steps launched back to back from Python (inputs resident in HBM before timing
+starts; HIP events only at the two ends of the region).  `roofline` describes
 the dominant kernel: algorithmic bytes per launch divided by its average
 launch time, measured with HIP events recorded on the launch stream around
-every call inside the timed region.  `cpu_baseline` times the fp64 CPU oracle
+every call over a second run of K timed steps (those per-call events add a
+few microseconds between launches, which is why they are kept out of the
+first region).  `cpu_baseline` times the fp64 CPU oracle
 on the host cores over a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -69,6 +72,10 @@ def parse():
                    choices=["scan_fwd_bwd", "scan_long", "sru_fwd", "deer", "scan_fwd_small"])
     p.add_argument("--layout", default="bdt", choices=["bdt", "tbd"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--graph", action="store_true",
+                   help="also time the step captured as a HIP graph and replayed")
+    p.add_argument("--no-stream-ref", action="store_true",
+                   help="skip the read-2/write-1 stream reference kernel")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time for the oracle baseline sample")
     return p.parse_args()
@@ -80,8 +87,11 @@ class KernelTimer:
     def __init__(self, torch):
         self.torch = torch
         self.pairs = {}
+        self.enabled = True
 
     def run(self, name, fn):
+        if not self.enabled:
+            return fn()
         t = self.torch
         s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
         s.record()
@@ -190,18 +200,38 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    def timed(fn, steps):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        t0.record()
+        for _ in range(steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps, time.perf_counter() - w0
+
+    # (1) eager steps, HIP events only at the two ends of the timed region
+    timer.enabled = False
+    ms_per_step, wall = timed(step, args.steps)
+    extra["timing"] = "eager launches, events at both ends"
+    # (2) the same step captured once as a HIP graph and replayed (reported
+    #     beside the eager figure).  DEER reads its stop test back to the host
+    #     and is never captured.
+    if w.kind != "deer" and args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(2):
+            graph.replay()
+        extra["ms_per_step_graph"] = round(timed(graph.replay, args.steps)[0], 5)
+    # (3) eager steps with HIP events around every call, on the launch stream:
+    #     per-kernel launch durations for the roofline
+    timer.enabled = True
     timer.pairs.clear()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0.record()
-    for _ in range(args.steps):
-        step()
-    t1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_per_step = t0.elapsed_time(t1) / args.steps
+    timed(step, args.steps)
     value = N / (ms_per_step / 1e3)
 
     per_kernel = {k: timer.avg_ms(k) for k in kernels}
@@ -229,6 +259,9 @@ def main():
     extra["step_hbm_frac"] = round(bytes_step / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4)
     extra["wall_s"] = round(wall, 3)
 
+    if not args.no_stream_ref:
+        extra["stream_ref"] = stream_reference(torch, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args, np, I)
@@ -239,6 +272,32 @@ def main():
             "data": "synthetic", "config": config, "roofline": roofline, "cpu_baseline": cpu,
             **extra}
     print(json.dumps(line), flush=True)
+
+
+STREAM_REF_ELEMS = 1 << 26  # 256 MiB per fp32 operand
+
+
+def stream_reference(torch, dev, reps: int = 10):
+    """Practical HBM ceiling on this device: torch's elementwise add z = x + y
+    over three 256 MiB fp32 arrays (reads 512 MiB, writes 256 MiB per call,
+    far beyond the caches).  Its per-dispatch counters also calibrate the
+    FETCH_SIZE / WRITE_SIZE readings of the scan kernels."""
+    x = torch.ones(STREAM_REF_ELEMS, device=dev)
+    y = torch.ones(STREAM_REF_ELEMS, device=dev)
+    z = torch.empty(STREAM_REF_ELEMS, device=dev)
+    for _ in range(3):
+        torch.add(x, y, out=z)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        torch.add(x, y, out=z)
+    e.record()
+    torch.cuda.synchronize()
+    sec = s.elapsed_time(e) / 1e3 / reps
+    gbs = 3 * 4 * STREAM_REF_ELEMS / sec / 1e9
+    return {"kernel": "torch add, read 2 x 256 MiB + write 256 MiB", "GB/s": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def cpu_baseline(w, args, np, I):

@@ -63,7 +63,7 @@ bool grid_ok(int64_t blocks, int threads) { return blocks > 0 && blocks * thread
 
 int scan_ws_needs(int64_t C, int64_t T, int layout, size_t* bytes) {
   if (layout == LRS_LAYOUT_BDT) {
-    const lrs::RowPlan p = lrs::plan_rows(T, 16);
+    const lrs::RowPlan p = lrs::plan_scan_rows(C, T);
     *bytes = p.nchunk > 1 ? lookback_bytes(C * p.nchunk, C) : 0;
   } else {
     const lrs::ColPlan f = lrs::plan_scan_fwd_tbd(C, T), b = lrs::plan_scan_bwd_tbd(C, T);
@@ -150,8 +150,8 @@ int lrs_scan_fwd(const void* a, const void* b, const float* h0, void* h, int64_t
   const bool al16 = aligned(a, 16) && aligned(b, 16) && aligned(h, 16);
 
   if (layout == LRS_LAYOUT_BDT) {
-    const lrs::RowPlan p = lrs::plan_rows(T, 16);
-    if (!grid_ok(C * p.nchunk, p.nt)) return LRS_ERR_UNSUPPORTED;
+    const lrs::RowPlan p = lrs::plan_scan_rows(C, T);
+    if (!grid_ok(C * p.nchunk, p.threads())) return LRS_ERR_UNSUPPORTED;
     uint64_t* status = nullptr;
     unsigned* tickets = nullptr;
     if (p.nchunk > 1) {
@@ -218,8 +218,8 @@ int lrs_scan_bwd(const void* a, const void* h, const float* h0, const void* grad
                     aligned(grad_a, 16) && aligned(grad_b, 16);
 
   if (layout == LRS_LAYOUT_BDT) {
-    const lrs::RowPlan p = lrs::plan_rows(T, 16);
-    if (!grid_ok(C * p.nchunk, p.nt)) return LRS_ERR_UNSUPPORTED;
+    const lrs::RowPlan p = lrs::plan_scan_rows(C, T);
+    if (!grid_ok(C * p.nchunk, p.threads())) return LRS_ERR_UNSUPPORTED;
     uint64_t* status = nullptr;
     unsigned* tickets = nullptr;
     if (p.nchunk > 1) {
@@ -318,13 +318,13 @@ int lrs_sru_fwd(const void* z_f, const void* z_r, const void* z_x, const float* 
 
 // ------------------------------------------------------------------- DEER
 
-static lrs::RowPlan deer_plan(int64_t T) { return lrs::plan_rows(T, 32); }
+static lrs::RowPlan deer_plan(int64_t C, int64_t T) { return lrs::plan_deer_rows(C, T); }
 
 size_t lrs_deer_workspace_bytes(int64_t B, int64_t D, int64_t T, int k_max) {
   int64_t C, N;
   if (!shape_ok(B, D, T, &C, &N) || k_max < 1) return 0;
   if (N == 0) return 0;
-  const lrs::RowPlan p = deer_plan(T);
+  const lrs::RowPlan p = deer_plan(C, T);
   size_t bytes = kAlign + align_up((size_t)k_max * 4) + align_up((size_t)N * 4);
   if (p.nchunk > 1) bytes += align_up((size_t)(C * p.nchunk) * 8) + align_up((size_t)C * 4);
   return bytes;
@@ -352,8 +352,8 @@ int lrs_deer_solve(const float* w, const float* u, const float* h0, const float*
   if (h_init && h_init != h && overlap(h, nb, h_init, nb)) return LRS_ERR_INVALID_ARG;
   const size_t need = lrs_deer_workspace_bytes(B, D, T, k_max);
   if (!workspace || workspace_bytes < need) return LRS_ERR_WORKSPACE;
-  const lrs::RowPlan p = deer_plan(T);
-  if (!grid_ok(C * p.nchunk, p.nt)) return LRS_ERR_UNSUPPORTED;
+  const lrs::RowPlan p = deer_plan(C, T);
+  if (!grid_ok(C * p.nchunk, p.threads())) return LRS_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
 
   Carve cv(align_ptr(workspace));

@@ -10,7 +10,7 @@
 // time-varying coefficients, a prefix-scan problem).
 //
 // Levels used by every kernel in this library:
-//   1. thread strip  : each lane folds K consecutive steps serially (FMA);
+//   1. lane fold     : each lane folds a few consecutive steps serially (FMA);
 //   2. wave64 scan   : 6 DPP steps (row_shr 1,2,4,8; row_bcast 15,31);
 //   3. block scan    : per-wave aggregates combined through LDS;
 //   4. chunk carry   : decoupled look-back over per-chunk status words in HBM,
@@ -133,44 +133,49 @@ __device__ __forceinline__ unsigned take_ticket(unsigned* counter) {
 }
 
 // ---------------------------------------------------------------------------
-// Strip loads/stores: K consecutive floats starting at element t0 of a row of
-// length T.  Full in-range strips use 16-byte accesses when `vec` is true
-// (row starts and base pointers 16-byte aligned); the ragged tail is
-// predicated element by element and filled with `fill`.
+// Group loads/stores: the 4 consecutive floats starting at element p of a row
+// of length T.  In-range groups use one 16-byte access when `vec` is true (row
+// starts and base pointers 16-byte aligned, p a multiple of 4); the ragged
+// tail is predicated element by element, out-of-range elements read as `fill`
+// and are not written.
 // ---------------------------------------------------------------------------
-template <int K>
-__device__ __forceinline__ void load_strip(const float* __restrict__ row, int64_t t0, int64_t T,
-                                           bool vec, float fill, float (&v)[K]) {
-  if (vec && t0 + K <= T) {
-    static_assert(K % 4 == 0, "strip length must be a multiple of 4");
-#pragma unroll
-    for (int q = 0; q < K / 4; ++q) {
-      const float4 x = *reinterpret_cast<const float4*>(row + t0 + 4 * q);
-      v[4 * q + 0] = x.x;
-      v[4 * q + 1] = x.y;
-      v[4 * q + 2] = x.z;
-      v[4 * q + 3] = x.w;
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// NT selects the nontemporal (streaming) cache policy for the 16-byte access.
+template <bool NT = false>
+__device__ __forceinline__ float4 load_group(const float* __restrict__ row, int64_t p, int64_t T,
+                                             bool vec, float fill) {
+  if (vec && p + 4 <= T) {
+    if (NT) {
+      const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(row + p));
+      return make_float4(v.x, v.y, v.z, v.w);
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < K; ++j) v[j] = (t0 + j < T) ? row[t0 + j] : fill;
+    return *reinterpret_cast<const float4*>(row + p);
   }
+  float4 v;
+  v.x = (p < T) ? row[p] : fill;
+  v.y = (p + 1 < T) ? row[p + 1] : fill;
+  v.z = (p + 2 < T) ? row[p + 2] : fill;
+  v.w = (p + 3 < T) ? row[p + 3] : fill;
+  return v;
 }
 
-template <int K>
-__device__ __forceinline__ void store_strip(float* __restrict__ row, int64_t t0, int64_t T,
-                                            bool vec, const float (&v)[K]) {
-  if (vec && t0 + K <= T) {
-#pragma unroll
-    for (int q = 0; q < K / 4; ++q) {
-      *reinterpret_cast<float4*>(row + t0 + 4 * q) =
-          make_float4(v[4 * q + 0], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+template <bool NT = false>
+__device__ __forceinline__ void store_group(float* __restrict__ row, int64_t p, int64_t T,
+                                            bool vec, float4 v) {
+  if (vec && p + 4 <= T) {
+    if (NT) {
+      const f32x4_t x = {v.x, v.y, v.z, v.w};
+      __builtin_nontemporal_store(x, reinterpret_cast<f32x4_t*>(row + p));
+    } else {
+      *reinterpret_cast<float4*>(row + p) = v;
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < K; ++j)
-      if (t0 + j < T) row[t0 + j] = v[j];
+    return;
   }
+  if (p < T) row[p] = v.x;
+  if (p + 1 < T) row[p + 1] = v.y;
+  if (p + 2 < T) row[p + 2] = v.z;
+  if (p + 3 < T) row[p + 3] = v.w;
 }
 
 // tanh from its definition through exp: tanh(x) = 1 - 2/(exp(2x) + 1).

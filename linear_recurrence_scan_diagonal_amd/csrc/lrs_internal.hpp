@@ -7,13 +7,18 @@
 
 namespace lrs {
 
-// Time-contiguous kernels: NT threads x K steps per chunk, nchunk chunks per channel.
+// Time-contiguous kernels: chunks of nw waves x r rows x 256 steps, nchunk
+// chunks per channel.
 struct RowPlan {
-  int nt = 256;
-  int k = 4;
+  int nw = 8;
+  int r = 2;
   int64_t nchunk = 1;
+  bool stream = false;  // nontemporal loads and stores (arrays far larger than the caches)
+  int threads() const { return nw * 64; }
+  int64_t chunk() const { return (int64_t)nw * r * 256; }
 };
-RowPlan plan_rows(int64_t T, int kmax_strip);
+RowPlan plan_scan_rows(int64_t C, int64_t T);
+RowPlan plan_deer_rows(int64_t C, int64_t T);
 
 // Feature-contiguous kernels: blocks of 64*cpt channels x nw*l steps.
 struct ColPlan {

@@ -3,14 +3,22 @@
 // engineering section recommends for the input, state and Jacobian arrays).
 //
 // Work decomposition (same for all three kernels):
-//   * a workgroup of NT threads owns one chunk of NT*K consecutive steps of one
-//     channel; lane-contiguous strips of K steps are folded serially in
-//     registers, then scanned across the wave (DPP) and across waves (LDS);
+//   * a workgroup of NW waves owns one chunk of CH = NW*R*256 consecutive steps
+//     of one channel; each wave owns R "rows" of 256 consecutive steps and in
+//     every row lane l owns 4 consecutive steps, so each row is one fully
+//     coalesced 1 KiB access per array (16 bytes per lane);
+//   * per row: each lane folds its 4 steps serially (FMA), the 64 lane maps are
+//     scanned across the wave with DPP, the row maps are chained in registers,
+//     and the wave maps are combined through LDS;
 //   * a channel longer than one chunk is split into chunks (the page's
-//     T = N*S sub-sequence split, one block per sub-sequence); the state entering
-//     a chunk comes from a decoupled look-back over per-chunk status words, and
-//     chunk order comes from a per-channel ticket so the wait always terminates;
-//   * every input byte is read once and every output byte written once.
+//     T = N*S sub-sequence split, one block per sub-sequence); the state
+//     entering a chunk comes from a decoupled look-back over per-chunk status
+//     words, and chunk order comes from a per-channel ticket so the wait always
+//     terminates;
+//   * every input byte is read once and every output byte written once; the
+//     values a step needs from its neighbour (a_{t+1}, h_{t-1}) come from the
+//     neighbouring lane through DPP, from the neighbouring row through a
+//     readlane, and only at wave edges from memory (one scalar per wave).
 //
 // Kernels:
 //   k_scan_fwd_bdt : h_t = a_t h_{t-1} + b_t
@@ -22,29 +30,30 @@
 
 namespace lrs {
 
-template <int NT>
+template <int NW>
 struct BlockShared {
-  float wA[NT / kWave];
-  float wB[NT / kWave];
-  uint32_t wmax[NT / kWave];
+  float wA[NW];
+  float wB[NW];
+  uint32_t wmax[NW];
   float carry;
   int chunk;
 };
 
-// Combine per-wave inclusive results: every thread gets the composition of the
-// waves before its own (PA, PB) and of the whole block (TA, TB).
-template <int NT>
-__device__ __forceinline__ void block_combine(float A, float B, BlockShared<NT>& s, float& PA,
+// Per-wave maps (uniform within each wave) combined in wave order: every
+// thread gets the composition of the waves before its own (PA, PB) and of the
+// whole block (TA, TB).
+template <int NW>
+__device__ __forceinline__ void block_combine(float WA, float WB, BlockShared<NW>& s, float& PA,
                                               float& PB, float& TA, float& TB) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  if (lane == kWave - 1) {
-    s.wA[wid] = A;
-    s.wB[wid] = B;
+  if (lane == 0) {
+    s.wA[wid] = WA;
+    s.wB[wid] = WB;
   }
   __syncthreads();
   PA = 1.0f; PB = 0.0f; TA = 1.0f; TB = 0.0f;
 #pragma unroll
-  for (int w = 0; w < NT / kWave; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const float wa = s.wA[w], wb = s.wB[w];
     if (w < wid) {
       PB = __builtin_fmaf(wa, PB, wb);
@@ -58,9 +67,9 @@ __device__ __forceinline__ void block_combine(float A, float B, BlockShared<NT>&
 // State entering logical chunk c of a channel.  Single-chunk channels use x0
 // directly; otherwise thread 0 publishes this chunk's aggregate, looks back,
 // publishes the inclusive state and shares the carry through LDS.
-template <int NT>
+template <int NW>
 __device__ __forceinline__ float chunk_carry(bool multi, int c, float TA, float TB, float x0,
-                                             uint64_t* st, BlockShared<NT>& s) {
+                                             uint64_t* st, BlockShared<NW>& s) {
   if (!multi) return x0;
   if (threadIdx.x == 0) {
     float x_in = x0;
@@ -75,131 +84,182 @@ __device__ __forceinline__ float chunk_carry(bool multi, int c, float TA, float 
   return s.carry;
 }
 
-template <int NT>
+template <int NW>
 __device__ __forceinline__ int chunk_ticket(bool multi, unsigned* tickets, int64_t ch,
-                                            BlockShared<NT>& s) {
+                                            BlockShared<NW>& s) {
   if (!multi) return 0;
   if (threadIdx.x == 0) s.chunk = (int)take_ticket(tickets + ch);
   __syncthreads();
   return s.chunk;
 }
 
-// ---------------------------------------------------------------------------
-// forward scan
-// ---------------------------------------------------------------------------
-template <int NT, int K>
-__global__ __launch_bounds__(NT) void k_scan_fwd_bdt(const float* __restrict__ a,
-                                                     const float* __restrict__ b,
-                                                     const float* __restrict__ h0,
-                                                     float* __restrict__ h, int64_t T, int64_t C,
-                                                     int nchunk, int vec,
-                                                     uint64_t* __restrict__ status,
-                                                     unsigned* __restrict__ tickets) {
-  __shared__ BlockShared<NT> s;
-  const bool multi = nchunk > 1;
-  const int64_t ch = multi ? (int64_t)(blockIdx.x % (uint64_t)C) : (int64_t)blockIdx.x;
-  const int c = chunk_ticket<NT>(multi, tickets, ch, s);
-  const int64_t t0 = (int64_t)c * (NT * K) + (int64_t)threadIdx.x * K;
-  const float* arow = a + ch * T;
-  const float* brow = b + ch * T;
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(v), lane));
+}
 
-  float av[K], bv[K];
-  load_strip<K>(arow, t0, T, vec, 1.0f, av);
-  load_strip<K>(brow, t0, T, vec, 0.0f, bv);
+// Value of the next lane (wave_shl:1); lane 63 receives `lane63`.
+__device__ __forceinline__ float wave_shift_down(float x, float lane63) {
+  return as_f32((uint32_t)__builtin_amdgcn_update_dpp((int)as_u32(lane63), (int)as_u32(x), 0x130,
+                                                      0xf, 0xf, false));
+}
 
-  float A = av[0], B = bv[0];
+// Chain the R row maps of a wave into the wave's map.
+template <int R>
+__device__ __forceinline__ void chain_rows(const float (&RA)[R], const float (&RB)[R], float& WA,
+                                           float& WB) {
+  WA = RA[0];
+  WB = RB[0];
 #pragma unroll
-  for (int j = 1; j < K; ++j) {
-    B = __builtin_fmaf(av[j], B, bv[j]);
-    A = A * av[j];
+  for (int r = 1; r < R; ++r) {
+    WB = __builtin_fmaf(RA[r], WB, RB[r]);
+    WA = WA * RA[r];
   }
-  wave_scan(A, B);
-  float PA, PB, TA, TB;
-  block_combine<NT>(A, B, s, PA, PB, TA, TB);
-  const float x0 = h0 ? h0[ch] : 0.0f;
-  const float x_in = chunk_carry<NT>(multi, c, TA, TB, x0, status + ch * nchunk, s);
-
-  const float xw = __builtin_fmaf(PA, x_in, PB);  // state entering this wave
-  const float xe = __builtin_fmaf(A, xw, B);      // state at the end of this lane's strip
-  float x = wave_shift_up(xe, xw);                // state entering this lane's strip
-#pragma unroll
-  for (int j = 0; j < K; ++j) {
-    x = __builtin_fmaf(av[j], x, bv[j]);
-    bv[j] = x;
-  }
-  store_strip<K>(h + ch * T, t0, T, vec, bv);
 }
 
 // ---------------------------------------------------------------------------
-// backward (reverse-time) scan.  Logical chunk 0 is the last physical chunk and
-// lane order runs backwards in time, so the same forward combine applies.
-// grad_b may alias grad_h: each thread reads its own g strip before writing.
+// forward scan
 // ---------------------------------------------------------------------------
-template <int NT, int K>
-__global__ __launch_bounds__(NT) void k_scan_bwd_bdt(const float* __restrict__ a,
-                                                     const float* __restrict__ h,
-                                                     const float* __restrict__ h0, const float* g,
-                                                     float* __restrict__ da, float* db,
-                                                     float* __restrict__ dh0, int64_t T, int64_t C,
-                                                     int nchunk, int vec,
-                                                     uint64_t* __restrict__ status,
-                                                     unsigned* __restrict__ tickets) {
-  __shared__ BlockShared<NT> s;
+template <int NW, int R, bool NTL = false, bool NTS = false>
+__global__ __launch_bounds__(NW* kWave) void k_scan_fwd_bdt(
+    const float* __restrict__ a, const float* __restrict__ b, const float* __restrict__ h0,
+    float* __restrict__ h, int64_t T, int64_t C, int nchunk, int vec,
+    uint64_t* __restrict__ status, unsigned* __restrict__ tickets) {
+  constexpr int S = R * 256, CH = NW * S;
+  __shared__ BlockShared<NW> s;
   const bool multi = nchunk > 1;
   const int64_t ch = multi ? (int64_t)(blockIdx.x % (uint64_t)C) : (int64_t)blockIdx.x;
-  const int c = chunk_ticket<NT>(multi, tickets, ch, s);
+  const int c = chunk_ticket<NW>(multi, tickets, ch, s);
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const int64_t base = (int64_t)c * CH + (int64_t)wid * S + 4 * lane;
+  const float* arow = a + ch * T;
+  const float* brow = b + ch * T;
+
+  float4 a4[R], b4[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    a4[r] = load_group<NTL>(arow, base + r * 256, T, vec, 1.0f);
+    b4[r] = load_group<NTL>(brow, base + r * 256, T, vec, 0.0f);
+  }
+  float Ai[R], Bi[R], RA[R], RB[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float A = a4[r].x, B = b4[r].x;
+    B = __builtin_fmaf(a4[r].y, B, b4[r].y); A = A * a4[r].y;
+    B = __builtin_fmaf(a4[r].z, B, b4[r].z); A = A * a4[r].z;
+    B = __builtin_fmaf(a4[r].w, B, b4[r].w); A = A * a4[r].w;
+    wave_scan(A, B);
+    Ai[r] = A; Bi[r] = B;
+    RA[r] = readlane_f(A, kWave - 1);
+    RB[r] = readlane_f(B, kWave - 1);
+  }
+  float WA, WB, PA, PB, TA, TB;
+  chain_rows<R>(RA, RB, WA, WB);
+  block_combine<NW>(WA, WB, s, PA, PB, TA, TB);
+  const float x0 = h0 ? h0[ch] : 0.0f;
+  const float x_in = chunk_carry<NW>(multi, c, TA, TB, x0, status + ch * nchunk, s);
+
+  float xr = __builtin_fmaf(PA, x_in, PB);  // state entering this wave's first row
+  float* hrow = h + ch * T;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float x = wave_shift_up(__builtin_fmaf(Ai[r], xr, Bi[r]), xr);  // entering this lane's group
+    float4 o;
+    x = __builtin_fmaf(a4[r].x, x, b4[r].x); o.x = x;
+    x = __builtin_fmaf(a4[r].y, x, b4[r].y); o.y = x;
+    x = __builtin_fmaf(a4[r].z, x, b4[r].z); o.z = x;
+    x = __builtin_fmaf(a4[r].w, x, b4[r].w); o.w = x;
+    store_group<NTS>(hrow, base + r * 256, T, vec, o);
+    xr = __builtin_fmaf(RA[r], xr, RB[r]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// backward (reverse-time) scan.  Scan order is descending time: logical chunk 0
+// is the last physical chunk, logical wave w takes the w-th segment counted
+// from the chunk's end, logical row r the r-th row counted from the segment's
+// end, and lane l the l-th group counted from the row's end, so the forward
+// combine applies unchanged.  grad_b may alias grad_h: each element of g is
+// read by the thread that writes the same element of grad_b, before it writes.
+// ---------------------------------------------------------------------------
+template <int NW, int R, bool NTL = false, bool NTS = false>
+__global__ __launch_bounds__(NW* kWave) void k_scan_bwd_bdt(
+    const float* __restrict__ a, const float* __restrict__ h, const float* __restrict__ h0,
+    const float* g, float* __restrict__ da, float* db, float* __restrict__ dh0, int64_t T,
+    int64_t C, int nchunk, int vec, uint64_t* __restrict__ status,
+    unsigned* __restrict__ tickets) {
+  constexpr int S = R * 256, CH = NW * S;
+  __shared__ BlockShared<NW> s;
+  const bool multi = nchunk > 1;
+  const int64_t ch = multi ? (int64_t)(blockIdx.x % (uint64_t)C) : (int64_t)blockIdx.x;
+  const int c = chunk_ticket<NW>(multi, tickets, ch, s);
   const int pc = nchunk - 1 - c;
-  const int64_t t0 = (int64_t)pc * (NT * K) + (int64_t)(NT - 1 - (int)threadIdx.x) * K;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const int64_t wend = (int64_t)(pc + 1) * CH - (int64_t)wid * S;  // physical end of the segment
+  const int64_t wbeg = wend - S;
   const float* arow = a + ch * T;
   const float* hrow = h + ch * T;
   const float* grow = g + ch * T;
 
-  float av[K], hv[K], gv[K];
-  load_strip<K>(arow, t0, T, vec, 1.0f, av);
-  load_strip<K>(hrow, t0, T, vec, 0.0f, hv);
-  load_strip<K>(grow, t0, T, vec, 0.0f, gv);
+  int64_t p0[R];
+  float4 a4[R], h4[R], g4[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    p0[r] = wend - (int64_t)(r + 1) * 256 + 4 * (kWave - 1 - lane);
+    a4[r] = load_group<NTL>(arow, p0[r], T, vec, 1.0f);
+    h4[r] = load_group<NTL>(hrow, p0[r], T, vec, 0.0f);
+    g4[r] = load_group<NTL>(grow, p0[r], T, vec, 0.0f);
+  }
   const float x0h = h0 ? h0[ch] : 0.0f;
-  // halo: a_{t+1} for the strip's last step, h_{t-1} for its first step
-  const float a_next = (t0 + K < T) ? arow[t0 + K] : (t0 + K == T ? 0.0f : 1.0f);
-  const float h_prev = (t0 > 0 && t0 <= T) ? hrow[t0 - 1] : x0h;
+  // wave-edge halos (uniform): a just past the segment, h just before it
+  const float a_after = (wend < T) ? arow[wend] : 1.0f;
+  const float h_before = (wbeg > 0) ? ((wbeg - 1 < T) ? hrow[wbeg - 1] : 0.0f) : x0h;
 
-  // alpha_i = a_{t0+i+1}: zero at the last real step, identity past the end
-  float al[K];
+  float al[R][4], hp[R], Ai[R], Bi[R], RA[R], RB[R];
 #pragma unroll
-  for (int i = 0; i < K - 1; ++i) al[i] = av[i + 1];
-  al[K - 1] = a_next;
-  if (t0 + K > T - 1) {
+  for (int r = 0; r < R; ++r) {
+    // alpha for element p is a_{p+1}; the group's last alpha comes from the next group
+    const float fa = (r > 0) ? readlane_f(a4[r - 1].x, kWave - 1) : a_after;
+    al[r][3] = wave_shift_up(a4[r].x, fa);
+    al[r][2] = a4[r].w;
+    al[r][1] = a4[r].z;
+    al[r][0] = a4[r].y;
+    if (p0[r] + 4 > T - 1) {  // the last real step has no successor
 #pragma unroll
-    for (int i = 0; i < K - 1; ++i)
-      if (t0 + i + 1 == T) al[i] = 0.0f;
+      for (int j = 0; j < 4; ++j)
+        if (p0[r] + j == T - 1) al[r][j] = 0.0f;
+    }
+    const float fh = (r < R - 1) ? readlane_f(h4[r + 1].w, 0) : h_before;
+    hp[r] = wave_shift_down(h4[r].w, fh);  // h at p0 - 1
+    float A = al[r][3], B = g4[r].w;
+    B = __builtin_fmaf(al[r][2], B, g4[r].z); A = A * al[r][2];
+    B = __builtin_fmaf(al[r][1], B, g4[r].y); A = A * al[r][1];
+    B = __builtin_fmaf(al[r][0], B, g4[r].x); A = A * al[r][0];
+    wave_scan(A, B);
+    Ai[r] = A; Bi[r] = B;
+    RA[r] = readlane_f(A, kWave - 1);
+    RB[r] = readlane_f(B, kWave - 1);
   }
+  float WA, WB, PA, PB, TA, TB;
+  chain_rows<R>(RA, RB, WA, WB);
+  block_combine<NW>(WA, WB, s, PA, PB, TA, TB);
+  const float x_in = chunk_carry<NW>(multi, c, TA, TB, 0.0f, status + ch * nchunk, s);
 
-  // fold the strip in scan order (descending time)
-  float A = al[K - 1], B = gv[K - 1];
+  float xr = __builtin_fmaf(PA, x_in, PB);
+  float* darow = da + ch * T;
+  float* dbrow = db + ch * T;
 #pragma unroll
-  for (int i = K - 2; i >= 0; --i) {
-    B = __builtin_fmaf(al[i], B, gv[i]);
-    A = A * al[i];
+  for (int r = 0; r < R; ++r) {
+    const float x = wave_shift_up(__builtin_fmaf(Ai[r], xr, Bi[r]), xr);  // lam past the group
+    const float l3 = __builtin_fmaf(al[r][3], x, g4[r].w);
+    const float l2 = __builtin_fmaf(al[r][2], l3, g4[r].z);
+    const float l1 = __builtin_fmaf(al[r][1], l2, g4[r].y);
+    const float l0 = __builtin_fmaf(al[r][0], l1, g4[r].x);
+    store_group<NTS>(darow, p0[r], T, vec,
+                     make_float4(l0 * hp[r], l1 * h4[r].x, l2 * h4[r].y, l3 * h4[r].z));
+    store_group<NTS>(dbrow, p0[r], T, vec, make_float4(l0, l1, l2, l3));
+    if (dh0 && p0[r] == 0) dh0[ch] = a4[r].x * l0;
+    xr = __builtin_fmaf(RA[r], xr, RB[r]);
   }
-  wave_scan(A, B);
-  float PA, PB, TA, TB;
-  block_combine<NT>(A, B, s, PA, PB, TA, TB);
-  const float x_in = chunk_carry<NT>(multi, c, TA, TB, 0.0f, status + ch * nchunk, s);
-
-  const float xw = __builtin_fmaf(PA, x_in, PB);
-  const float xe = __builtin_fmaf(A, xw, B);
-  float x = wave_shift_up(xe, xw);  // lam entering this strip from the right
-  float dav[K];
-#pragma unroll
-  for (int i = K - 1; i >= 0; --i) {
-    x = __builtin_fmaf(al[i], x, gv[i]);
-    const float hp = (i > 0) ? hv[i - 1] : h_prev;
-    dav[i] = x * hp;
-    gv[i] = x;
-  }
-  if (dh0 && t0 == 0) dh0[ch] = av[0] * x;
-  store_strip<K>(da + ch * T, t0, T, vec, dav);
-  store_strip<K>(db + ch * T, t0, T, vec, gv);
 }
 
 // ---------------------------------------------------------------------------
@@ -214,87 +274,99 @@ __global__ __launch_bounds__(NT) void k_scan_bwd_bdt(const float* __restrict__ a
 // rule delta < eps (DEER page, engineering section); a skipped iteration
 // leaves its slot at 0, so later ones skip as well.
 // ---------------------------------------------------------------------------
-template <int NT, int K>
-__global__ __launch_bounds__(NT) void k_deer_iter(const float* __restrict__ w,
-                                                  const float* __restrict__ u,
-                                                  const float* __restrict__ y,
-                                                  const float* __restrict__ h0,
-                                                  float* __restrict__ yn, int64_t T, int64_t C,
-                                                  int64_t D, int nchunk, int vec,
-                                                  uint64_t* __restrict__ status,
-                                                  unsigned* __restrict__ tickets,
-                                                  uint32_t* __restrict__ delta_bits, int iter,
-                                                  float eps) {
-  if (iter > 0) {
-    const uint32_t prev = __hip_atomic_load(delta_bits + iter - 1, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-    if (as_f32(prev) < eps) return;
-  }
-  __shared__ BlockShared<NT> s;
+template <int NW, int R>
+__global__ __launch_bounds__(NW* kWave) void k_deer_iter(
+    const float* __restrict__ w, const float* __restrict__ u, const float* __restrict__ y,
+    const float* __restrict__ h0, float* __restrict__ yn, int64_t T, int64_t C, int64_t D,
+    int nchunk, int vec, uint64_t* __restrict__ status, unsigned* __restrict__ tickets,
+    uint32_t* __restrict__ delta_bits, int iter, float eps) {
+  constexpr int S = R * 256, CH = NW * S;
+  __shared__ BlockShared<NW> s;
+  // The previous iteration's norm was completed by the previous kernel, so a
+  // plain (cached, wave-uniform) load sees it; a cache-bypassing atomic read
+  // of one address from every workgroup would serialise in the memory system.
+  if (iter > 0 && as_f32(delta_bits[iter - 1]) < eps) return;
   const bool multi = nchunk > 1;
   const int64_t ch = multi ? (int64_t)(blockIdx.x % (uint64_t)C) : (int64_t)blockIdx.x;
-  const int c = chunk_ticket<NT>(multi, tickets, ch, s);
-  const int64_t t0 = (int64_t)c * (NT * K) + (int64_t)threadIdx.x * K;
+  const int c = chunk_ticket<NW>(multi, tickets, ch, s);
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const int64_t wbeg = (int64_t)c * CH + (int64_t)wid * S;
+  const int64_t base = wbeg + 4 * lane;
   const float wd = w[ch % D];
   const float x0 = h0 ? h0[ch] : 0.0f;
+  const float* urow = u + ch * T;
+  const float* yrow = y ? y + ch * T : nullptr;
 
-  float uv[K], yv[K];
-  load_strip<K>(u + ch * T, t0, T, vec, 0.0f, uv);
-  if (y) {
-    load_strip<K>(y + ch * T, t0, T, vec, 0.0f, yv);
-  } else {
+  float4 u4[R], y4[R];
 #pragma unroll
-    for (int j = 0; j < K; ++j) yv[j] = 0.0f;
+  for (int r = 0; r < R; ++r) {
+    u4[r] = load_group(urow, base + r * 256, T, vec, 0.0f);
+    y4[r] = yrow ? load_group(yrow, base + r * 256, T, vec, 0.0f) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  const float y_prev = (t0 > 0 && t0 <= T) ? (y ? y[ch * T + t0 - 1] : 0.0f) : x0;
+  // y just before the wave's segment (h0 at the start of the sequence)
+  const float y_before = (wbeg > 0) ? ((yrow && wbeg - 1 < T) ? yrow[wbeg - 1] : 0.0f) : x0;
 
-  float Jv[K], rv[K];
+  float J[R][4], rh[R][4], Ai[R], Bi[R], RA[R], RB[R];
 #pragma unroll
-  for (int j = 0; j < K; ++j) {
-    const float yp = (j > 0) ? yv[j - 1] : y_prev;
-    const float z = tanh_fast(__builtin_fmaf(wd, yp, uv[j]));
-    const float J = wd * __builtin_fmaf(-z, z, 1.0f);
-    Jv[j] = J;
-    rv[j] = __builtin_fmaf(-J, yp, z);
-  }
-  if (t0 + K > T) {
+  for (int r = 0; r < R; ++r) {
+    const float fy = (r > 0) ? readlane_f(y4[r - 1].w, kWave - 1) : y_before;
+    const float yp[4] = {wave_shift_up(y4[r].w, fy), y4[r].x, y4[r].y, y4[r].z};
+    const float uv[4] = {u4[r].x, u4[r].y, u4[r].z, u4[r].w};
 #pragma unroll
-    for (int j = 0; j < K; ++j)
-      if (t0 + j >= T) { Jv[j] = 1.0f; rv[j] = 0.0f; }
+    for (int j = 0; j < 4; ++j) {
+      const float z = tanh_fast(__builtin_fmaf(wd, yp[j], uv[j]));
+      J[r][j] = wd * __builtin_fmaf(-z, z, 1.0f);
+      rh[r][j] = __builtin_fmaf(-J[r][j], yp[j], z);
+    }
+    const int64_t p = base + r * 256;
+    if (p + 4 > T) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (p + j >= T) { J[r][j] = 1.0f; rh[r][j] = 0.0f; }
+    }
+    float A = J[r][0], B = rh[r][0];
+#pragma unroll
+    for (int j = 1; j < 4; ++j) {
+      B = __builtin_fmaf(J[r][j], B, rh[r][j]);
+      A = A * J[r][j];
+    }
+    wave_scan(A, B);
+    Ai[r] = A; Bi[r] = B;
+    RA[r] = readlane_f(A, kWave - 1);
+    RB[r] = readlane_f(B, kWave - 1);
   }
+  float WA, WB, PA, PB, TA, TB;
+  chain_rows<R>(RA, RB, WA, WB);
+  block_combine<NW>(WA, WB, s, PA, PB, TA, TB);
+  const float x_in = chunk_carry<NW>(multi, c, TA, TB, x0, status + ch * nchunk, s);
 
-  float A = Jv[0], B = rv[0];
-#pragma unroll
-  for (int j = 1; j < K; ++j) {
-    B = __builtin_fmaf(Jv[j], B, rv[j]);
-    A = A * Jv[j];
-  }
-  wave_scan(A, B);
-  float PA, PB, TA, TB;
-  block_combine<NT>(A, B, s, PA, PB, TA, TB);
-  const float x_in = chunk_carry<NT>(multi, c, TA, TB, x0, status + ch * nchunk, s);
-
-  const float xw = __builtin_fmaf(PA, x_in, PB);
-  const float xe = __builtin_fmaf(A, xw, B);
-  float x = wave_shift_up(xe, xw);
+  float xr = __builtin_fmaf(PA, x_in, PB);
+  float* ynrow = yn + ch * T;
   uint32_t dmax = 0;
 #pragma unroll
-  for (int j = 0; j < K; ++j) {
-    x = __builtin_fmaf(Jv[j], x, rv[j]);
-    const uint32_t d = as_u32(fabsf(x - yv[j]));
-    if (t0 + j < T) dmax = d > dmax ? d : dmax;
-    rv[j] = x;
+  for (int r = 0; r < R; ++r) {
+    float x = wave_shift_up(__builtin_fmaf(Ai[r], xr, Bi[r]), xr);
+    const int64_t p = base + r * 256;
+    const float yo[4] = {y4[r].x, y4[r].y, y4[r].z, y4[r].w};
+    float o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x = __builtin_fmaf(J[r][j], x, rh[r][j]);
+      o[j] = x;
+      const uint32_t d = as_u32(fabsf(x - yo[j]));
+      if (p + j < T) dmax = d > dmax ? d : dmax;
+    }
+    store_group(ynrow, p, T, vec, make_float4(o[0], o[1], o[2], o[3]));
+    xr = __builtin_fmaf(RA[r], xr, RB[r]);
   }
-  store_strip<K>(yn + ch * T, t0, T, vec, rv);
 
   dmax = wave_max_u32(dmax);
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   if (lane == 0) s.wmax[wid] = dmax;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < NT / kWave; ++i) m = s.wmax[i] > m ? s.wmax[i] : m;
+    for (int i = 0; i < NW; ++i) m = s.wmax[i] > m ? s.wmax[i] : m;
     __hip_atomic_fetch_max(delta_bits + iter, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -302,65 +374,116 @@ __global__ __launch_bounds__(NT) void k_deer_iter(const float* __restrict__ w,
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+// Chunk shapes (waves x rows of 256 steps).  A channel that fits one chunk
+// takes the smallest single-chunk shape that covers it; a longer channel is
+// split into chunks of the multi-chunk shape and uses the look-back.  Tile
+// choices come from measured sweeps on MI355X: 8x2 for channels of up to 4096
+// steps, 4x2 chunks (more resident workgroups per CU) for longer scans, and
+// 8x4 for the DEER iteration, whose per-step transcendental work favours
+// more rows per wave.
 namespace {
-constexpr int kNT = 256;
+struct Shape { int nw, r; };
+constexpr Shape kScanSingle[] = {{1, 1}, {2, 1}, {4, 1}, {8, 1}, {8, 2}};
+constexpr Shape kScanMulti = {4, 2};
+constexpr Shape kDeerSingle[] = {{1, 1}, {2, 1}, {4, 1}, {8, 1}, {8, 2}, {8, 4}};
+constexpr Shape kDeerMulti = {8, 4};
+// arrays of at least this many bytes are streamed with nontemporal accesses
+constexpr int64_t kStreamBytes = (int64_t)256 << 20;
 
-template <int K>
-constexpr int chunk_of() { return kNT * K; }
-
+template <size_t N>
+RowPlan pick(int64_t T, const Shape (&single)[N], Shape multi) {
+  RowPlan p;
+  for (size_t i = 0; i < N; ++i) {
+    const int64_t chunk = (int64_t)single[i].nw * single[i].r * 256;
+    if (chunk >= T) {
+      p.nw = single[i].nw;
+      p.r = single[i].r;
+      p.nchunk = 1;
+      return p;
+    }
+  }
+  p.nw = multi.nw;
+  p.r = multi.r;
+  p.nchunk = (T + p.chunk() - 1) / p.chunk();
+  return p;
+}
 }  // namespace
 
-RowPlan plan_rows(int64_t T, int kmax_strip) {
-  RowPlan p;
-  p.nt = kNT;
-  int K = 4;
-  while (K < kmax_strip && (int64_t)kNT * K < T) K *= 2;
-  p.k = K;
-  const int64_t chunk = (int64_t)kNT * K;
-  p.nchunk = (T + chunk - 1) / chunk;
-  if (p.nchunk < 1) p.nchunk = 1;
+RowPlan plan_scan_rows(int64_t C, int64_t T) {
+  RowPlan p = pick(T, kScanSingle, kScanMulti);
+  p.stream = C * T * 4 >= kStreamBytes && p.nchunk > 1;
   return p;
 }
 
-#define LRS_DISPATCH_K(K_, ...)                        \
-  switch (K_) {                                        \
-    case 4: { constexpr int KK = 4; __VA_ARGS__; } break;   \
-    case 8: { constexpr int KK = 8; __VA_ARGS__; } break;   \
-    case 16: { constexpr int KK = 16; __VA_ARGS__; } break; \
-    case 32: { constexpr int KK = 32; __VA_ARGS__; } break; \
-    default: return hipErrorInvalidValue;              \
-  }
+RowPlan plan_deer_rows(int64_t C, int64_t T) {
+  RowPlan p = pick(T, kDeerSingle, kDeerMulti);
+  p.stream = false;
+  return p;
+}
+
+// Dispatch on the (waves, rows) shape and the streaming flag.
+#define LRS_SHAPE_CASE(NW_, R_, ...) \
+  if (p.nw == NW_ && p.r == R_) { constexpr int NW = NW_, RR = R_; __VA_ARGS__; return hipGetLastError(); }
 
 hipError_t launch_scan_fwd_bdt(const float* a, const float* b, const float* h0, float* h,
                                int64_t C, int64_t T, const RowPlan& p, int vec,
                                uint64_t* status, unsigned* tickets, hipStream_t stream) {
-  const uint64_t grid = (uint64_t)C * (uint64_t)p.nchunk;
-  LRS_DISPATCH_K(p.k, hipLaunchKernelGGL((k_scan_fwd_bdt<kNT, KK>), dim3((unsigned)grid),
-                                         dim3(kNT), 0, stream, a, b, h0, h, T, C, (int)p.nchunk,
-                                         vec, status, tickets));
-  return hipGetLastError();
+  const dim3 grid((unsigned)((uint64_t)C * (uint64_t)p.nchunk));
+#define LRS_FWD(NTF) hipLaunchKernelGGL((k_scan_fwd_bdt<NW, RR, NTF, NTF>), grid, dim3(NW * kWave), 0, \
+                                        stream, a, b, h0, h, T, C, (int)p.nchunk, vec, status, tickets)
+  if (p.stream) {
+    LRS_SHAPE_CASE(4, 2, LRS_FWD(true))
+  } else {
+    LRS_SHAPE_CASE(1, 1, LRS_FWD(false))
+    LRS_SHAPE_CASE(2, 1, LRS_FWD(false))
+    LRS_SHAPE_CASE(4, 1, LRS_FWD(false))
+    LRS_SHAPE_CASE(8, 1, LRS_FWD(false))
+    LRS_SHAPE_CASE(8, 2, LRS_FWD(false))
+    LRS_SHAPE_CASE(4, 2, LRS_FWD(false))
+  }
+#undef LRS_FWD
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_scan_bwd_bdt(const float* a, const float* h, const float* h0, const float* g,
                                float* da, float* db, float* dh0, int64_t C, int64_t T,
                                const RowPlan& p, int vec, uint64_t* status, unsigned* tickets,
                                hipStream_t stream) {
-  const uint64_t grid = (uint64_t)C * (uint64_t)p.nchunk;
-  LRS_DISPATCH_K(p.k, hipLaunchKernelGGL((k_scan_bwd_bdt<kNT, KK>), dim3((unsigned)grid),
-                                         dim3(kNT), 0, stream, a, h, h0, g, da, db, dh0, T, C,
-                                         (int)p.nchunk, vec, status, tickets));
-  return hipGetLastError();
+  const dim3 grid((unsigned)((uint64_t)C * (uint64_t)p.nchunk));
+#define LRS_BWD(NTF) hipLaunchKernelGGL((k_scan_bwd_bdt<NW, RR, NTF, NTF>), grid, dim3(NW * kWave), 0, \
+                                        stream, a, h, h0, g, da, db, dh0, T, C, (int)p.nchunk, vec, \
+                                        status, tickets)
+  if (p.stream) {
+    LRS_SHAPE_CASE(4, 2, LRS_BWD(true))
+  } else {
+    LRS_SHAPE_CASE(1, 1, LRS_BWD(false))
+    LRS_SHAPE_CASE(2, 1, LRS_BWD(false))
+    LRS_SHAPE_CASE(4, 1, LRS_BWD(false))
+    LRS_SHAPE_CASE(8, 1, LRS_BWD(false))
+    LRS_SHAPE_CASE(8, 2, LRS_BWD(false))
+    LRS_SHAPE_CASE(4, 2, LRS_BWD(false))
+  }
+#undef LRS_BWD
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_deer_iter(const float* w, const float* u, const float* y, const float* h0,
                             float* yn, int64_t C, int64_t D, int64_t T, const RowPlan& p, int vec,
                             uint64_t* status, unsigned* tickets, uint32_t* delta_bits, int iter,
                             float eps, hipStream_t stream) {
-  const uint64_t grid = (uint64_t)C * (uint64_t)p.nchunk;
-  LRS_DISPATCH_K(p.k, hipLaunchKernelGGL((k_deer_iter<kNT, KK>), dim3((unsigned)grid), dim3(kNT),
-                                         0, stream, w, u, y, h0, yn, T, C, D, (int)p.nchunk, vec,
-                                         status, tickets, delta_bits, iter, eps));
-  return hipGetLastError();
+  const dim3 grid((unsigned)((uint64_t)C * (uint64_t)p.nchunk));
+#define LRS_DEER hipLaunchKernelGGL((k_deer_iter<NW, RR>), grid, dim3(NW * kWave), 0, stream, w, u, y, \
+                                    h0, yn, T, C, D, (int)p.nchunk, vec, status, tickets, delta_bits, \
+                                    iter, eps)
+  LRS_SHAPE_CASE(1, 1, LRS_DEER)
+  LRS_SHAPE_CASE(2, 1, LRS_DEER)
+  LRS_SHAPE_CASE(4, 1, LRS_DEER)
+  LRS_SHAPE_CASE(8, 1, LRS_DEER)
+  LRS_SHAPE_CASE(8, 2, LRS_DEER)
+  LRS_SHAPE_CASE(8, 4, LRS_DEER)
+#undef LRS_DEER
+  return hipErrorInvalidValue;
 }
+#undef LRS_SHAPE_CASE
 
 }  // namespace lrs

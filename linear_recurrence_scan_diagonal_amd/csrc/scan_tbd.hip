@@ -3,17 +3,20 @@
 // contiguous, fully coalesced access, and time runs serially inside a thread.
 //
 // Work decomposition:
-//   * a workgroup of NW waves owns a block of CW = 64*CPT channels over a
-//     block of TW = NW*L time steps; wave w takes L consecutive steps, each
-//     lane CPT consecutive channels;
+//   * a workgroup of NW waves owns a tile of CW = 64*CPT channels by TW = NW*L
+//     time steps; wave w takes L consecutive steps, each lane CPT consecutive
+//     channels;
 //   * per channel, each thread folds its L steps into one affine map, the
-//     waves' maps are combined through LDS, and the state entering the time
-//     block comes from a lane-parallel decoupled look-back over per-channel
-//     status words (one 64-bit word per channel and time block); time-block
-//     order comes from a per-channel-block ticket;
-//   * every input byte is read once and every output byte written once
-//     (the backward kernel also reads one halo row above and below each
-//     thread's steps; those hit in cache).
+//     waves' maps are combined through LDS, and the state entering the tile
+//     comes from a lane-parallel decoupled look-back over per-channel status
+//     words (one 64-bit word per channel and time block); time-block order
+//     comes from a per-channel-block ticket;
+//   * a wave addresses its rows through a wave-uniform row pointer plus a
+//     32-bit lane offset (scalar-base global loads), and tiles that lie fully
+//     inside the array run without any per-element predication;
+//   * every input byte is read once and every output byte written once (the
+//     backward kernel also reads one row above and one below each wave's
+//     steps; those hit in cache).
 //
 // Kernels:
 //   k_scan_fwd_tbd : h_t = a_t h_{t-1} + b_t
@@ -35,73 +38,82 @@ struct ColShared {
   int chunk;
 };
 
-// ---- CPT-wide row access --------------------------------------------------
+// ---- CPT-wide row access ------------------------------------------------
+// `p` is a wave-uniform row pointer, `off` the lane's element offset.  FULL
+// rows are in range and aligned; otherwise `nvalid` channels are in range
+// (0 for a row past the end) and the rest read as `fill` / are not written.
 
-template <int CPT>
-__device__ __forceinline__ void load_row(const float* __restrict__ p, int nvalid, bool vec,
+template <int CPT, bool FULL>
+__device__ __forceinline__ void load_row(const float* __restrict__ p, uint32_t off, int nvalid,
                                          float fill, float (&v)[CPT]) {
-  if (vec && nvalid == CPT) {
+  if (FULL) {
     if constexpr (CPT == 4) {
-      const float4 x = *reinterpret_cast<const float4*>(p);
+      const float4 x = *reinterpret_cast<const float4*>(p + off);
       v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
     } else if constexpr (CPT == 2) {
-      const float2 x = *reinterpret_cast<const float2*>(p);
+      const float2 x = *reinterpret_cast<const float2*>(p + off);
       v[0] = x.x; v[1] = x.y;
     } else {
 #pragma unroll
-      for (int k = 0; k < CPT; ++k) v[k] = p[k];
+      for (int k = 0; k < CPT; ++k) v[k] = p[off + k];
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) v[k] = (k < nvalid) ? p[k] : fill;
+    for (int k = 0; k < CPT; ++k) v[k] = (k < nvalid) ? p[off + k] : fill;
   }
 }
 
-template <int CPT>
-__device__ __forceinline__ void store_row(float* __restrict__ p, int nvalid, bool vec,
+template <int CPT, bool FULL>
+__device__ __forceinline__ void store_row(float* __restrict__ p, uint32_t off, int nvalid,
                                           const float (&v)[CPT]) {
-  if (vec && nvalid == CPT) {
+  if (FULL) {
     if constexpr (CPT == 4) {
-      *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(p + off) = make_float4(v[0], v[1], v[2], v[3]);
     } else if constexpr (CPT == 2) {
-      *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+      *reinterpret_cast<float2*>(p + off) = make_float2(v[0], v[1]);
     } else {
 #pragma unroll
-      for (int k = 0; k < CPT; ++k) p[k] = v[k];
+      for (int k = 0; k < CPT; ++k) p[off + k] = v[k];
     }
   } else {
 #pragma unroll
     for (int k = 0; k < CPT; ++k)
-      if (k < nvalid) p[k] = v[k];
+      if (k < nvalid) p[off + k] = v[k];
   }
 }
 
-// bf16 rows: raw 16-bit patterns, widened exactly to fp32 on use.
-template <int CPT>
-__device__ __forceinline__ void load_row_bf16(const uint16_t* __restrict__ p, int nvalid, bool vec,
-                                              uint16_t (&v)[CPT]) {
-  if (vec && nvalid == CPT) {
-    if constexpr (CPT == 4) {
-      const uint2 x = *reinterpret_cast<const uint2*>(p);
-      v[0] = (uint16_t)x.x; v[1] = (uint16_t)(x.x >> 16);
-      v[2] = (uint16_t)x.y; v[3] = (uint16_t)(x.y >> 16);
-    } else if constexpr (CPT == 8) {
-      const uint4 x = *reinterpret_cast<const uint4*>(p);
-      v[0] = (uint16_t)x.x; v[1] = (uint16_t)(x.x >> 16);
-      v[2] = (uint16_t)x.y; v[3] = (uint16_t)(x.y >> 16);
-      v[4] = (uint16_t)x.z; v[5] = (uint16_t)(x.z >> 16);
-      v[6] = (uint16_t)x.w; v[7] = (uint16_t)(x.w >> 16);
+// bf16 rows are kept as packed pairs (CPT/2 words) and widened on use.
+template <int CPT, bool FULL>
+__device__ __forceinline__ void load_row_bf16(const uint16_t* __restrict__ p, uint32_t off,
+                                              int nvalid, uint32_t (&w)[CPT / 2]) {
+  static_assert(CPT % 2 == 0, "bf16 rows hold an even number of channels");
+  if (FULL) {
+    if constexpr (CPT == 2) {
+      w[0] = *reinterpret_cast<const uint32_t*>(p + off);
+    } else if constexpr (CPT == 4) {
+      const uint2 x = *reinterpret_cast<const uint2*>(p + off);
+      w[0] = x.x; w[1] = x.y;
     } else {
-#pragma unroll
-      for (int k = 0; k < CPT; ++k) v[k] = p[k];
+      static_assert(CPT == 8, "bf16 rows of 2, 4 or 8 channels");
+      const uint4 x = *reinterpret_cast<const uint4*>(p + off);
+      w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) v[k] = (k < nvalid) ? p[k] : (uint16_t)0;
+    for (int k = 0; k < CPT / 2; ++k) {
+      const uint32_t lo = (2 * k < nvalid) ? p[off + 2 * k] : 0u;
+      const uint32_t hi = (2 * k + 1 < nvalid) ? p[off + 2 * k + 1] : 0u;
+      w[k] = lo | (hi << 16);
+    }
   }
 }
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return as_f32((uint32_t)v << 16); }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return as_f32(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return as_f32(w & 0xFFFF0000u); }
+template <int CPT>
+__device__ __forceinline__ float bf16_get(const uint32_t (&w)[CPT / 2], int k) {
+  return (k & 1) ? bf16_hi(w[k >> 1]) : bf16_lo(w[k >> 1]);
+}
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -113,98 +125,101 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, b);
 }
 
-template <int CPT>
-__device__ __forceinline__ void store_row_bf16(uint16_t* __restrict__ p, int nvalid, bool vec,
+template <int CPT, bool FULL>
+__device__ __forceinline__ void store_row_bf16(uint16_t* __restrict__ p, uint32_t off, int nvalid,
                                                const float (&v)[CPT]) {
-  static_assert(CPT % 2 == 0, "bf16 rows hold an even number of channels");
   uint32_t w[CPT / 2];
 #pragma unroll
   for (int k = 0; k < CPT / 2; ++k) w[k] = pack_bf16x2(v[2 * k], v[2 * k + 1]);
-  if (vec && nvalid == CPT) {
-    if constexpr (CPT == 4) {
-      *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
-    } else if constexpr (CPT == 8) {
-      *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  if (FULL) {
+    if constexpr (CPT == 2) {
+      *reinterpret_cast<uint32_t*>(p + off) = w[0];
+    } else if constexpr (CPT == 4) {
+      *reinterpret_cast<uint2*>(p + off) = make_uint2(w[0], w[1]);
     } else {
-#pragma unroll
-      for (int k = 0; k < CPT / 2; ++k) reinterpret_cast<uint32_t*>(p)[k] = w[k];
+      *reinterpret_cast<uint4*>(p + off) = make_uint4(w[0], w[1], w[2], w[3]);
     }
   } else {
 #pragma unroll
     for (int k = 0; k < CPT; ++k)
-      if (k < nvalid) p[k] = (uint16_t)(w[k / 2] >> (16 * (k & 1)));
+      if (k < nvalid) p[off + k] = (uint16_t)(w[k / 2] >> (16 * (k & 1)));
   }
 }
 
 // ---- block-level pieces ----------------------------------------------------
 
-// Per channel: composition of the waves before this one (PA, PB) and of the
-// whole block (TA, TB).  Wave order is scan order.
-template <int NW, int CPT>
-__device__ __forceinline__ void col_block_combine(const float (&A)[CPT], const float (&B)[CPT],
-                                                  ColShared<NW, CPT>& s, float (&PA)[CPT],
-                                                  float (&PB)[CPT], float (&TA)[CPT],
-                                                  float (&TB)[CPT]) {
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-#pragma unroll
-  for (int k = 0; k < CPT; ++k) {
-    s.A[wid][lane * CPT + k] = A[k];
-    s.B[wid][lane * CPT + k] = B[k];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < CPT; ++k) {
-    PA[k] = 1.0f; PB[k] = 0.0f; TA[k] = 1.0f; TB[k] = 0.0f;
-  }
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      const float wa = s.A[w][lane * CPT + k], wb = s.B[w][lane * CPT + k];
-      if (w < wid) {
-        PB[k] = __builtin_fmaf(wa, PB[k], wb);
-        PA[k] = PA[k] * wa;
-      }
-      TB[k] = __builtin_fmaf(wa, TB[k], wb);
-      TA[k] = TA[k] * wa;
-    }
-  }
-}
-
-// State entering logical time block tb for each of this lane's channels.
-// Wave 0 publishes aggregates, looks back and publishes inclusive states.
+// Per channel, the state entering this wave's first step.  Each wave publishes
+// its per-channel maps in LDS; the last wave composes all of them into the
+// block's map, runs the look-back (multi-block) and shares the carries; every
+// wave then composes the maps of the waves before it (wave order = scan order).
 // st points at this channel block's status row for time block 0; time blocks
 // are CW words apart.
 template <int NW, int CPT>
-__device__ __forceinline__ void col_chunk_carry(bool multi, int tb, int nvc,
-                                                const float (&TA)[CPT], const float (&TB)[CPT],
+__device__ __forceinline__ void col_enter_state(const float (&A)[CPT], const float (&B)[CPT],
+                                                bool multi, int tb, int nvc,
                                                 const float (&x0)[CPT], uint64_t* st,
-                                                ColShared<NW, CPT>& s, float (&carry)[CPT]) {
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+                                                ColShared<NW, CPT>& s, float (&x)[CPT]) {
   constexpr int CW = kWave * CPT;
-  if (!multi) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int j0 = lane * CPT;
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) carry[k] = x0[k];
-    return;
-  }
-  if (wid == 0) {
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      const int j = lane * CPT + k;
-      float x_in = x0[k];
-      if (k < nvc) {
-        if (tb > 0) {
-          status_store(st + (int64_t)tb * CW + j, pack_agg(TA[k], TB[k]));
-          x_in = lookback_carry(st + j, tb, CW);
-        }
-        status_store(st + (int64_t)tb * CW + j, pack_inc(__builtin_fmaf(TA[k], x_in, TB[k])));
-      }
-      s.carry[j] = x_in;
-    }
+  for (int k = 0; k < CPT; ++k) {
+    s.A[wid][j0 + k] = A[k];
+    s.B[wid][j0 + k] = B[k];
   }
   __syncthreads();
+  float carry[CPT];
+  if (multi) {
+    if (wid == NW - 1) {
+      float TA[CPT], TB[CPT];
 #pragma unroll
-  for (int k = 0; k < CPT; ++k) carry[k] = s.carry[lane * CPT + k];
+      for (int k = 0; k < CPT; ++k) { TA[k] = 1.0f; TB[k] = 0.0f; }
+      for (int w = 0; w < NW; ++w) {
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+          const float wa = s.A[w][j0 + k], wb = s.B[w][j0 + k];
+          TB[k] = __builtin_fmaf(wa, TB[k], wb);
+          TA[k] = TA[k] * wa;
+        }
+      }
+      // publish every aggregate before waiting on any predecessor
+      if (tb > 0) {
+#pragma unroll
+        for (int k = 0; k < CPT; ++k)
+          if (k < nvc) status_store(st + (int64_t)tb * CW + j0 + k, pack_agg(TA[k], TB[k]));
+      }
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        const int j = j0 + k;
+        float x_in = x0[k];
+        if (k < nvc) {
+          if (tb > 0) x_in = lookback_carry(st + j, tb, CW);
+          status_store(st + (int64_t)tb * CW + j, pack_inc(__builtin_fmaf(TA[k], x_in, TB[k])));
+        }
+        s.carry[j] = x_in;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) carry[k] = s.carry[j0 + k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) carry[k] = x0[k];
+  }
+  float PA[CPT], PB[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) { PA[k] = 1.0f; PB[k] = 0.0f; }
+  for (int w = 0; w < wid; ++w) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const float wa = s.A[w][j0 + k], wb = s.B[w][j0 + k];
+      PB[k] = __builtin_fmaf(wa, PB[k], wb);
+      PA[k] = PA[k] * wa;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) x[k] = __builtin_fmaf(PA[k], carry[k], PB[k]);
 }
 
 template <int NW, int CPT>
@@ -220,31 +235,47 @@ __device__ __forceinline__ int clamp_valid(int64_t n, int cpt) {
   return n <= 0 ? 0 : (n >= cpt ? cpt : (int)n);
 }
 
+// Geometry of one thread inside its workgroup tile.
+struct ColPos {
+  int64_t row0;   // first time step of this wave (wave-uniform)
+  int64_t c0;     // first channel of this lane
+  uint32_t off;   // lane's element offset inside a row of the tile
+  int nvc;        // channels of this lane inside [0, C)
+};
+
+template <int NW, int L, int CPT>
+__device__ __forceinline__ ColPos col_pos(int tb, int cb, int64_t C) {
+  ColPos q;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  q.row0 = (int64_t)tb * (NW * L) + (int64_t)wid * L;
+  q.off = (uint32_t)(lane * CPT);
+  q.c0 = (int64_t)cb * (kWave * CPT) + q.off;
+  q.nvc = clamp_valid(C - q.c0, CPT);
+  return q;
+}
+
 // ---------------------------------------------------------------------------
 // forward scan, [T, B, D]
 // ---------------------------------------------------------------------------
-template <int NW, int L, int CPT>
-__global__ __launch_bounds__(NW* kWave) void k_scan_fwd_tbd(
-    const float* __restrict__ a, const float* __restrict__ b, const float* __restrict__ h0,
-    float* __restrict__ h, int64_t T, int64_t C, int ncb, int ntb, int vec,
-    uint64_t* __restrict__ status, unsigned* __restrict__ tickets) {
-  constexpr int CW = kWave * CPT, TW = NW * L;
-  __shared__ ColShared<NW, CPT> s;
-  const bool multi = ntb > 1;
-  const int cb = (int)(blockIdx.x % (unsigned)ncb);
-  const int tb = col_ticket<NW, CPT>(multi, tickets, cb, s);
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  const int64_t c0 = (int64_t)cb * CW + lane * CPT;
-  const int nvc = clamp_valid(C - c0, CPT);
-  const int64_t tw0 = (int64_t)tb * TW + (int64_t)wid * L;
-
+template <int NW, int L, int CPT, bool FULL>
+__device__ __forceinline__ void scan_fwd_tile(const float* __restrict__ a,
+                                              const float* __restrict__ b,
+                                              const float* __restrict__ h0, float* __restrict__ h,
+                                              int64_t T, int64_t C, int tb, int cb, bool multi,
+                                              uint64_t* st, ColShared<NW, CPT>& s) {
+  const ColPos q = col_pos<NW, L, CPT>(tb, cb, C);
+  const int64_t cbase = (int64_t)cb * (kWave * CPT);
   float av[L][CPT], bv[L][CPT];
+  const float* ap = a + q.row0 * C + cbase;
+  const float* bp = b + q.row0 * C + cbase;
 #pragma unroll
   for (int i = 0; i < L; ++i) {
-    const int nv = (tw0 + i < T) ? nvc : 0;
-    const int64_t off = (tw0 + i) * C + c0;
-    load_row<CPT>(a + off, nv, vec, 1.0f, av[i]);
-    load_row<CPT>(b + off, nv, vec, 0.0f, bv[i]);
+    const int nv = (FULL || q.row0 + i < T) ? q.nvc : 0;
+    load_row<CPT, FULL>(ap, q.off, nv, 1.0f, av[i]);
+    load_row<CPT, FULL>(bp, q.off, nv, 0.0f, bv[i]);
+    ap += C;
+    bp += C;
   }
   float A[CPT], B[CPT];
 #pragma unroll
@@ -257,13 +288,11 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_fwd_tbd(
       A[k] = A[k] * av[i][k];
     }
   }
-  float PA[CPT], PB[CPT], TA[CPT], TB[CPT], x0[CPT], x[CPT];
-  col_block_combine<NW, CPT>(A, B, s, PA, PB, TA, TB);
+  float x0[CPT], x[CPT];
 #pragma unroll
-  for (int k = 0; k < CPT; ++k) x0[k] = (h0 && k < nvc) ? h0[c0 + k] : 0.0f;
-  col_chunk_carry<NW, CPT>(multi, tb, nvc, TA, TB, x0, status + (int64_t)cb * ntb * CW, s, x);
-#pragma unroll
-  for (int k = 0; k < CPT; ++k) x[k] = __builtin_fmaf(PA[k], x[k], PB[k]);
+  for (int k = 0; k < CPT; ++k) x0[k] = (h0 && k < q.nvc) ? h0[q.c0 + k] : 0.0f;
+  col_enter_state<NW, CPT>(A, B, multi, tb, q.nvc, x0, st, s, x);
+  float* hp = h + q.row0 * C + cbase;
 #pragma unroll
   for (int i = 0; i < L; ++i) {
 #pragma unroll
@@ -271,63 +300,88 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_fwd_tbd(
       x[k] = __builtin_fmaf(av[i][k], x[k], bv[i][k]);
       bv[i][k] = x[k];
     }
-    const int nv = (tw0 + i < T) ? nvc : 0;
-    store_row<CPT>(h + (tw0 + i) * C + c0, nv, vec, bv[i]);
+    const int nv = (FULL || q.row0 + i < T) ? q.nvc : 0;
+    store_row<CPT, FULL>(hp, q.off, nv, bv[i]);
+    hp += C;
   }
 }
 
-// ---------------------------------------------------------------------------
-// backward scan, [T, B, D]: logical time block 0 is the last physical block,
-// wave 0 takes the latest steps of the block, each thread runs time backwards.
-// ---------------------------------------------------------------------------
 template <int NW, int L, int CPT>
-__global__ __launch_bounds__(NW* kWave) void k_scan_bwd_tbd(
-    const float* __restrict__ a, const float* __restrict__ h, const float* __restrict__ h0,
-    const float* g, float* __restrict__ da, float* db, float* __restrict__ dh0, int64_t T,
-    int64_t C, int ncb, int ntb, int vec, uint64_t* __restrict__ status,
-    unsigned* __restrict__ tickets) {
+__global__ __launch_bounds__(NW* kWave) void k_scan_fwd_tbd(
+    const float* __restrict__ a, const float* __restrict__ b, const float* __restrict__ h0,
+    float* __restrict__ h, int64_t T, int64_t C, int ncb, int ntb, int vec,
+    uint64_t* __restrict__ status, unsigned* __restrict__ tickets) {
   constexpr int CW = kWave * CPT, TW = NW * L;
   __shared__ ColShared<NW, CPT> s;
   const bool multi = ntb > 1;
   const int cb = (int)(blockIdx.x % (unsigned)ncb);
   const int tb = col_ticket<NW, CPT>(multi, tickets, cb, s);
+  uint64_t* st = status + (int64_t)cb * ntb * CW;
+  const bool full = vec && ((int64_t)(tb + 1) * TW <= T) && ((int64_t)(cb + 1) * CW <= C);
+  if (full)
+    scan_fwd_tile<NW, L, CPT, true>(a, b, h0, h, T, C, tb, cb, multi, st, s);
+  else
+    scan_fwd_tile<NW, L, CPT, false>(a, b, h0, h, T, C, tb, cb, multi, st, s);
+}
+
+// ---------------------------------------------------------------------------
+// backward scan, [T, B, D]: logical time block 0 is the last physical block,
+// wave 0 takes the latest steps of the block, each thread runs time backwards.
+// grad_b may alias grad_h (each element of g is read by the thread that
+// writes the same element of grad_b, before it writes).
+// ---------------------------------------------------------------------------
+template <int NW, int L, int CPT, bool FULL>
+__device__ __forceinline__ void scan_bwd_tile(const float* __restrict__ a,
+                                              const float* __restrict__ h,
+                                              const float* __restrict__ h0, const float* g,
+                                              float* __restrict__ da, float* db,
+                                              float* __restrict__ dh0, int64_t T, int64_t C,
+                                              int tb, int ntb, int cb, bool multi, uint64_t* st,
+                                              ColShared<NW, CPT>& s) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int ptb = ntb - 1 - tb;
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  const int64_t c0 = (int64_t)cb * CW + lane * CPT;
-  const int nvc = clamp_valid(C - c0, CPT);
-  const int64_t tw0 = (int64_t)ptb * TW + (int64_t)(NW - 1 - wid) * L;
+  const uint32_t off = (uint32_t)(lane * CPT);
+  const int64_t cbase = (int64_t)cb * (kWave * CPT);
+  const int64_t c0 = cbase + off;
+  const int nvc = FULL ? CPT : clamp_valid(C - c0, CPT);
+  const int64_t row0 = (int64_t)ptb * (NW * L) + (int64_t)(NW - 1 - wid) * L;
 
   float av[L + 1][CPT], hv[L][CPT], gv[L][CPT], hp[CPT];
-#pragma unroll
-  for (int i = 0; i < L; ++i) {
-    const int nv = (tw0 + i < T) ? nvc : 0;
-    const int64_t off = (tw0 + i) * C + c0;
-    load_row<CPT>(a + off, nv, vec, 1.0f, av[i]);
-    load_row<CPT>(h + off, nv, vec, 0.0f, hv[i]);
-    load_row<CPT>(g + off, nv, vec, 0.0f, gv[i]);
-  }
-  // halo rows: a at t = tw0+L (0 exactly one past the end, 1 beyond),
-  // h at t = tw0-1 (h0 for the first step)
   {
-    const int64_t tn = tw0 + L;
+    const float* ap = a + row0 * C + cbase;
+    const float* hpp = h + row0 * C + cbase;
+    const float* gp = g + row0 * C + cbase;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int nv = (FULL || row0 + i < T) ? nvc : 0;
+      load_row<CPT, FULL>(ap, off, nv, 1.0f, av[i]);
+      load_row<CPT, FULL>(hpp, off, nv, 0.0f, hv[i]);
+      load_row<CPT, FULL>(gp, off, nv, 0.0f, gv[i]);
+      ap += C;
+      hpp += C;
+      gp += C;
+    }
+    // halo rows (wave-uniform branches): a at row0+L (0 exactly one past the
+    // end, 1 beyond), h at row0-1 (h0 before the first step)
+    const int64_t tn = row0 + L;
     if (tn < T) {
-      load_row<CPT>(a + tn * C + c0, nvc, vec, 1.0f, av[L]);
+      load_row<CPT, FULL>(ap, off, nvc, 1.0f, av[L]);
     } else {
 #pragma unroll
       for (int k = 0; k < CPT; ++k) av[L][k] = (tn == T) ? 0.0f : 1.0f;
     }
-    if (tw0 > 0 && tw0 <= T) {
-      load_row<CPT>(h + (tw0 - 1) * C + c0, nvc, vec, 0.0f, hp);
+    if (row0 > 0 && row0 <= T) {
+      load_row<CPT, FULL>(h + (row0 - 1) * C + cbase, off, nvc, 0.0f, hp);
     } else {
 #pragma unroll
       for (int k = 0; k < CPT; ++k) hp[k] = (h0 && k < nvc) ? h0[c0 + k] : 0.0f;
     }
   }
-  // alpha_i = a_{t+1}; zero at the last real step
-  if (tw0 + L > T - 1) {
+  if (!FULL && row0 + L > T - 1) {  // alpha of the last real step is zero
 #pragma unroll
     for (int i = 0; i < L; ++i)
-      if (tw0 + i + 1 == T) {
+      if (row0 + i + 1 == T) {
 #pragma unroll
         for (int k = 0; k < CPT; ++k) av[i + 1][k] = 0.0f;
       }
@@ -343,13 +397,12 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_bwd_tbd(
       A[k] = A[k] * av[i + 1][k];
     }
   }
-  float PA[CPT], PB[CPT], TA[CPT], TB[CPT], zero[CPT], x[CPT];
-  col_block_combine<NW, CPT>(A, B, s, PA, PB, TA, TB);
+  float zero[CPT], x[CPT];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) zero[k] = 0.0f;
-  col_chunk_carry<NW, CPT>(multi, tb, nvc, TA, TB, zero, status + (int64_t)cb * ntb * CW, s, x);
-#pragma unroll
-  for (int k = 0; k < CPT; ++k) x[k] = __builtin_fmaf(PA[k], x[k], PB[k]);
+  col_enter_state<NW, CPT>(A, B, multi, tb, nvc, zero, st, s, x);
+  float* dap = da + (row0 + L - 1) * C + cbase;
+  float* dbp = db + (row0 + L - 1) * C + cbase;
 #pragma unroll
   for (int i = L - 1; i >= 0; --i) {
     float dav[CPT];
@@ -359,95 +412,134 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_bwd_tbd(
       dav[k] = x[k] * (i > 0 ? hv[i - 1][k] : hp[k]);
       gv[i][k] = x[k];
     }
-    const int nv = (tw0 + i < T) ? nvc : 0;
-    const int64_t off = (tw0 + i) * C + c0;
-    store_row<CPT>(da + off, nv, vec, dav);
-    store_row<CPT>(db + off, nv, vec, gv[i]);
+    const int nv = (FULL || row0 + i < T) ? nvc : 0;
+    store_row<CPT, FULL>(dap, off, nv, dav);
+    store_row<CPT, FULL>(dbp, off, nv, gv[i]);
+    dap -= C;
+    dbp -= C;
   }
-  if (dh0 && tw0 == 0) {
+  if (dh0 && row0 == 0) {
 #pragma unroll
     for (int k = 0; k < CPT; ++k)
       if (k < nvc) dh0[c0 + k] = av[0][k] * x[k];
   }
 }
 
-// ---------------------------------------------------------------------------
-// fused SRU forward, [T, B, D]:
-//   f = sigmoid(zf + bf[d]), r = sigmoid(zr + br[d]),
-//   c_t = f c_{t-1} + (1 - f) zx,   h = r tanh(c) + (1 - r) zx
-// IO is bf16 (raw uint16) or fp32; gates and state are fp32.
-// ---------------------------------------------------------------------------
-template <typename IO, int CPT>
-struct IoRow;
-
-template <int CPT>
-struct IoRow<uint16_t, CPT> {
-  uint16_t v[CPT];
-  __device__ __forceinline__ void load(const uint16_t* p, int nvalid, bool vec) {
-    load_row_bf16<CPT>(p, nvalid, vec, v);
-  }
-  __device__ __forceinline__ float get(int k) const { return bf16_to_f32(v[k]); }
-  static __device__ __forceinline__ void store(uint16_t* p, int nvalid, bool vec,
-                                               const float (&x)[CPT]) {
-    store_row_bf16<CPT>(p, nvalid, vec, x);
-  }
-};
-
-template <int CPT>
-struct IoRow<float, CPT> {
-  float v[CPT];
-  __device__ __forceinline__ void load(const float* p, int nvalid, bool vec) {
-    load_row<CPT>(p, nvalid, vec, 0.0f, v);
-  }
-  __device__ __forceinline__ float get(int k) const { return v[k]; }
-  static __device__ __forceinline__ void store(float* p, int nvalid, bool vec,
-                                               const float (&x)[CPT]) {
-    store_row<CPT>(p, nvalid, vec, x);
-  }
-};
-
-template <typename IO, int NW, int L, int CPT>
-__global__ __launch_bounds__(NW* kWave) void k_sru_fwd(
-    const IO* __restrict__ zf, const IO* __restrict__ zr, const IO* __restrict__ zx,
-    const float* __restrict__ bias_f, const float* __restrict__ bias_r,
-    const float* __restrict__ c0p, IO* __restrict__ h, float* __restrict__ c_last, int64_t T,
-    int64_t C, int64_t D, int ncb, int ntb, int vec, uint64_t* __restrict__ status,
+template <int NW, int L, int CPT>
+__global__ __launch_bounds__(NW* kWave) void k_scan_bwd_tbd(
+    const float* __restrict__ a, const float* __restrict__ h, const float* __restrict__ h0,
+    const float* g, float* __restrict__ da, float* db, float* __restrict__ dh0, int64_t T,
+    int64_t C, int ncb, int ntb, int vec, uint64_t* __restrict__ status,
     unsigned* __restrict__ tickets) {
   constexpr int CW = kWave * CPT, TW = NW * L;
   __shared__ ColShared<NW, CPT> s;
   const bool multi = ntb > 1;
   const int cb = (int)(blockIdx.x % (unsigned)ncb);
   const int tb = col_ticket<NW, CPT>(multi, tickets, cb, s);
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  const int64_t c0 = (int64_t)cb * CW + lane * CPT;
-  const int nvc = clamp_valid(C - c0, CPT);
-  const int64_t tw0 = (int64_t)tb * TW + (int64_t)wid * L;
+  uint64_t* st = status + (int64_t)cb * ntb * CW;
+  const int ptb = ntb - 1 - tb;
+  const bool full = vec && ((int64_t)(ptb + 1) * TW <= T) && ((int64_t)(cb + 1) * CW <= C);
+  if (full)
+    scan_bwd_tile<NW, L, CPT, true>(a, h, h0, g, da, db, dh0, T, C, tb, ntb, cb, multi, st, s);
+  else
+    scan_bwd_tile<NW, L, CPT, false>(a, h, h0, g, da, db, dh0, T, C, tb, ntb, cb, multi, st, s);
+}
 
-  float bf[CPT], br[CPT];
-#pragma unroll
-  for (int k = 0; k < CPT; ++k) {
-    const int64_t d = (k < nvc) ? (c0 + k) % D : 0;
-    bf[k] = bias_f[d];
-    br[k] = bias_r[d];
+// ---------------------------------------------------------------------------
+// fused SRU forward, [T, B, D]:
+//   f = sigmoid(zf + bf[d]), r = sigmoid(zr + br[d]),
+//   c_t = f c_{t-1} + (1 - f) zx,   h = r tanh(c) + (1 - r) zx
+// Gates and state are fp32.  sigmoid(x) = 1/(1 + 2^(-x log2 e)) and
+// tanh(c) = 1 - 2/(1 + 2^(2 c log2 e)), each one v_exp_f32 and one v_rcp_f32;
+// the biases are pre-scaled by -log2 e so each gate input is a single FMA.
+// ---------------------------------------------------------------------------
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <typename IO, int CPT>
+struct SruRow;
+
+template <int CPT>
+struct SruRow<uint16_t, CPT> {
+  uint32_t w[CPT / 2];
+  template <bool FULL>
+  __device__ __forceinline__ void load(const uint16_t* p, uint32_t off, int nv) {
+    load_row_bf16<CPT, FULL>(p, off, nv, w);
   }
+  __device__ __forceinline__ float get(int k) const { return bf16_get<CPT>(w, k); }
+  template <bool FULL>
+  static __device__ __forceinline__ void store(uint16_t* p, uint32_t off, int nv,
+                                               const float (&x)[CPT]) {
+    store_row_bf16<CPT, FULL>(p, off, nv, x);
+  }
+};
 
-  float av[L][CPT], bv[L][CPT];
-  IoRow<IO, CPT> rr[L], xr[L];
-#pragma unroll
-  for (int i = 0; i < L; ++i) {
-    const int nv = (tw0 + i < T) ? nvc : 0;
-    const int64_t off = (tw0 + i) * C + c0;
-    IoRow<IO, CPT> fr;
-    fr.load(zf + off, nv, vec);
-    rr[i].load(zr + off, nv, vec);
-    xr[i].load(zx + off, nv, vec);
+template <int CPT>
+struct SruRow<float, CPT> {
+  float v[CPT];
+  template <bool FULL>
+  __device__ __forceinline__ void load(const float* p, uint32_t off, int nv) {
+    load_row<CPT, FULL>(p, off, nv, 0.0f, v);
+  }
+  __device__ __forceinline__ float get(int k) const { return v[k]; }
+  template <bool FULL>
+  static __device__ __forceinline__ void store(float* p, uint32_t off, int nv,
+                                               const float (&x)[CPT]) {
+    store_row<CPT, FULL>(p, off, nv, x);
+  }
+};
+
+template <typename IO, int NW, int L, int CPT, bool FULL>
+__device__ __forceinline__ void sru_tile(const IO* __restrict__ zf, const IO* __restrict__ zr,
+                                         const IO* __restrict__ zx,
+                                         const float* __restrict__ bias_f,
+                                         const float* __restrict__ bias_r,
+                                         const float* __restrict__ c0p, IO* __restrict__ h,
+                                         float* __restrict__ c_last, int64_t T, int64_t C,
+                                         int64_t D, int tb, int cb, bool multi, uint64_t* st,
+                                         ColShared<NW, CPT>& s) {
+  const ColPos q = col_pos<NW, L, CPT>(tb, cb, C);
+  const int64_t cbase = (int64_t)cb * (kWave * CPT);
+  // per-channel gate biases, pre-scaled by -log2(e)
+  float nbf[CPT], nbr[CPT];
+  {
+    int64_t d = (q.nvc > 0) ? q.c0 % D : 0;
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
-      const float f = sigmoid_fast(fr.get(k) + bf[k]);
-      const float zxv = xr[i].get(k);
-      const bool valid = k < nv;
-      av[i][k] = valid ? f : 1.0f;
-      bv[i][k] = valid ? __builtin_fmaf(-f, zxv, zxv) : 0.0f;  // (1 - f) * zx
+      const int64_t dk = (k < q.nvc) ? d : 0;
+      nbf[k] = -kLog2e * bias_f[dk];
+      nbr[k] = -kLog2e * bias_r[dk];
+      d = (d + 1 == D) ? 0 : d + 1;
+    }
+  }
+  float av[L][CPT], bv[L][CPT];
+  SruRow<IO, CPT> rr[L], xr[L];
+  {
+    const IO* fp = zf + q.row0 * C + cbase;
+    const IO* rp = zr + q.row0 * C + cbase;
+    const IO* xp = zx + q.row0 * C + cbase;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int nv = (FULL || q.row0 + i < T) ? q.nvc : 0;
+      SruRow<IO, CPT> fr;
+      fr.template load<FULL>(fp, q.off, nv);
+      rr[i].template load<FULL>(rp, q.off, nv);
+      xr[i].template load<FULL>(xp, q.off, nv);
+      fp += C;
+      rp += C;
+      xp += C;
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        const float f = __builtin_amdgcn_rcpf(
+            1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(fr.get(k), -kLog2e, nbf[k])));
+        const float zxv = xr[i].get(k);
+        if (FULL || k < nv) {
+          av[i][k] = f;
+          bv[i][k] = __builtin_fmaf(-f, zxv, zxv);  // (1 - f) * zx
+        } else {
+          av[i][k] = 1.0f;
+          bv[i][k] = 0.0f;
+        }
+      }
     }
   }
   float A[CPT], B[CPT];
@@ -461,31 +553,56 @@ __global__ __launch_bounds__(NW* kWave) void k_sru_fwd(
       A[k] = A[k] * av[i][k];
     }
   }
-  float PA[CPT], PB[CPT], TA[CPT], TB[CPT], x0[CPT], x[CPT];
-  col_block_combine<NW, CPT>(A, B, s, PA, PB, TA, TB);
+  float x0[CPT], x[CPT];
 #pragma unroll
-  for (int k = 0; k < CPT; ++k) x0[k] = (c0p && k < nvc) ? c0p[c0 + k] : 0.0f;
-  col_chunk_carry<NW, CPT>(multi, tb, nvc, TA, TB, x0, status + (int64_t)cb * ntb * CW, s, x);
-#pragma unroll
-  for (int k = 0; k < CPT; ++k) x[k] = __builtin_fmaf(PA[k], x[k], PB[k]);
+  for (int k = 0; k < CPT; ++k) x0[k] = (c0p && k < q.nvc) ? c0p[q.c0 + k] : 0.0f;
+  col_enter_state<NW, CPT>(A, B, multi, tb, q.nvc, x0, st, s, x);
+  IO* hp = h + q.row0 * C + cbase;
 #pragma unroll
   for (int i = 0; i < L; ++i) {
     float out[CPT];
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
       x[k] = __builtin_fmaf(av[i][k], x[k], bv[i][k]);
-      const float r = sigmoid_fast(rr[i].get(k) + br[k]);
+      const float r = __builtin_amdgcn_rcpf(
+          1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(rr[i].get(k), -kLog2e, nbr[k])));
+      const float th = __builtin_fmaf(
+          -2.0f, __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f((2.0f * kLog2e) * x[k])),
+          1.0f);
       const float zxv = xr[i].get(k);
-      out[k] = __builtin_fmaf(r, tanh_fast(x[k]) - zxv, zxv);  // r tanh(c) + (1 - r) zx
+      out[k] = __builtin_fmaf(r, th - zxv, zxv);  // r tanh(c) + (1 - r) zx
     }
-    const int nv = (tw0 + i < T) ? nvc : 0;
-    IoRow<IO, CPT>::store(h + (tw0 + i) * C + c0, nv, vec, out);
-    if (c_last && tw0 + i == T - 1) {
+    const int nv = (FULL || q.row0 + i < T) ? q.nvc : 0;
+    SruRow<IO, CPT>::template store<FULL>(hp, q.off, nv, out);
+    hp += C;
+    if (c_last && q.row0 + i == T - 1) {
 #pragma unroll
       for (int k = 0; k < CPT; ++k)
-        if (k < nvc) c_last[c0 + k] = x[k];
+        if (k < q.nvc) c_last[q.c0 + k] = x[k];
     }
   }
+}
+
+template <typename IO, int NW, int L, int CPT>
+__global__ __launch_bounds__(NW* kWave) void k_sru_fwd(
+    const IO* __restrict__ zf, const IO* __restrict__ zr, const IO* __restrict__ zx,
+    const float* __restrict__ bias_f, const float* __restrict__ bias_r,
+    const float* __restrict__ c0p, IO* __restrict__ h, float* __restrict__ c_last, int64_t T,
+    int64_t C, int64_t D, int ncb, int ntb, int vec, uint64_t* __restrict__ status,
+    unsigned* __restrict__ tickets) {
+  constexpr int CW = kWave * CPT, TW = NW * L;
+  __shared__ ColShared<NW, CPT> s;
+  const bool multi = ntb > 1;
+  const int cb = (int)(blockIdx.x % (unsigned)ncb);
+  const int tb = col_ticket<NW, CPT>(multi, tickets, cb, s);
+  uint64_t* st = status + (int64_t)cb * ntb * CW;
+  const bool full = vec && ((int64_t)(tb + 1) * TW <= T) && ((int64_t)(cb + 1) * CW <= C);
+  if (full)
+    sru_tile<IO, NW, L, CPT, true>(zf, zr, zx, bias_f, bias_r, c0p, h, c_last, T, C, D, tb, cb,
+                                   multi, st, s);
+  else
+    sru_tile<IO, NW, L, CPT, false>(zf, zr, zx, bias_f, bias_r, c0p, h, c_last, T, C, D, tb, cb,
+                                    multi, st, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -505,20 +622,28 @@ ColPlan plan_cols(int64_t C, int64_t T, int nw, int l, int cpt) {
 
 int64_t col_status_words(const ColPlan& p) { return p.ntb > 1 ? p.ncb * p.ntb * kWave * p.cpt : 0; }
 
-// fp32 scans: forward uses 8 waves x 8 steps x 4 channels per lane,
-// backward 8 waves x 8 steps x 2 channels per lane (three input streams).
-ColPlan plan_scan_fwd_tbd(int64_t C, int64_t T) { return plan_cols(C, T, 8, 8, 4); }
-ColPlan plan_scan_bwd_tbd(int64_t C, int64_t T) { return plan_cols(C, T, 8, 8, 2); }
+// Tile shapes (waves along time x steps per lane x channels per lane).
+namespace {
+constexpr int kFwdNW = 8, kFwdL = 16, kFwdCPT = 1;
+constexpr int kBwdNW = 8, kBwdL = 16, kBwdCPT = 1;
+constexpr int kSruNW = 8, kSruL = 8, kSruCPT = 2;           // bf16 I/O
+constexpr int kSruF32NW = 8, kSruF32L = 8, kSruF32CPT = 2;  // fp32 I/O
+}  // namespace
+
+ColPlan plan_scan_fwd_tbd(int64_t C, int64_t T) { return plan_cols(C, T, kFwdNW, kFwdL, kFwdCPT); }
+ColPlan plan_scan_bwd_tbd(int64_t C, int64_t T) { return plan_cols(C, T, kBwdNW, kBwdL, kBwdCPT); }
 ColPlan plan_sru(int64_t C, int64_t T, int io_dtype) {
-  return io_dtype == 1 ? plan_cols(C, T, 8, 8, 4) : plan_cols(C, T, 8, 8, 4);
+  return io_dtype == 1 ? plan_cols(C, T, kSruNW, kSruL, kSruCPT)
+                       : plan_cols(C, T, kSruF32NW, kSruF32L, kSruF32CPT);
 }
 
 hipError_t launch_scan_fwd_tbd(const float* a, const float* b, const float* h0, float* h,
                                int64_t C, int64_t T, const ColPlan& p, int vec, uint64_t* status,
                                unsigned* tickets, hipStream_t stream) {
   const uint64_t grid = (uint64_t)p.ncb * (uint64_t)p.ntb;
-  hipLaunchKernelGGL((k_scan_fwd_tbd<8, 8, 4>), dim3((unsigned)grid), dim3(8 * kWave), 0, stream,
-                     a, b, h0, h, T, C, (int)p.ncb, (int)p.ntb, vec, status, tickets);
+  hipLaunchKernelGGL((k_scan_fwd_tbd<kFwdNW, kFwdL, kFwdCPT>), dim3((unsigned)grid),
+                     dim3(kFwdNW * kWave), 0, stream, a, b, h0, h, T, C, (int)p.ncb, (int)p.ntb,
+                     vec, status, tickets);
   return hipGetLastError();
 }
 
@@ -527,9 +652,9 @@ hipError_t launch_scan_bwd_tbd(const float* a, const float* h, const float* h0, 
                                const ColPlan& p, int vec, uint64_t* status, unsigned* tickets,
                                hipStream_t stream) {
   const uint64_t grid = (uint64_t)p.ncb * (uint64_t)p.ntb;
-  hipLaunchKernelGGL((k_scan_bwd_tbd<8, 8, 2>), dim3((unsigned)grid), dim3(8 * kWave), 0, stream,
-                     a, h, h0, g, da, db, dh0, T, C, (int)p.ncb, (int)p.ntb, vec, status,
-                     tickets);
+  hipLaunchKernelGGL((k_scan_bwd_tbd<kBwdNW, kBwdL, kBwdCPT>), dim3((unsigned)grid),
+                     dim3(kBwdNW * kWave), 0, stream, a, h, h0, g, da, db, dh0, T, C, (int)p.ncb,
+                     (int)p.ntb, vec, status, tickets);
   return hipGetLastError();
 }
 
@@ -540,15 +665,15 @@ hipError_t launch_sru_fwd(const void* zf, const void* zr, const void* zx, const 
   const uint64_t grid = (uint64_t)p.ncb * (uint64_t)p.ntb;
   const int64_t C = B * D;
   if (io_dtype == 1) {
-    hipLaunchKernelGGL((k_sru_fwd<uint16_t, 8, 8, 4>), dim3((unsigned)grid), dim3(8 * kWave), 0,
-                       stream, (const uint16_t*)zf, (const uint16_t*)zr, (const uint16_t*)zx,
-                       bias_f, bias_r, c0, (uint16_t*)h, c_last, T, C, D, (int)p.ncb, (int)p.ntb,
-                       vec, status, tickets);
+    hipLaunchKernelGGL((k_sru_fwd<uint16_t, kSruNW, kSruL, kSruCPT>), dim3((unsigned)grid),
+                       dim3(kSruNW * kWave), 0, stream, (const uint16_t*)zf, (const uint16_t*)zr,
+                       (const uint16_t*)zx, bias_f, bias_r, c0, (uint16_t*)h, c_last, T, C, D,
+                       (int)p.ncb, (int)p.ntb, vec, status, tickets);
   } else {
-    hipLaunchKernelGGL((k_sru_fwd<float, 8, 8, 4>), dim3((unsigned)grid), dim3(8 * kWave), 0,
-                       stream, (const float*)zf, (const float*)zr, (const float*)zx, bias_f,
-                       bias_r, c0, (float*)h, c_last, T, C, D, (int)p.ncb, (int)p.ntb, vec,
-                       status, tickets);
+    hipLaunchKernelGGL((k_sru_fwd<float, kSruF32NW, kSruF32L, kSruF32CPT>), dim3((unsigned)grid),
+                       dim3(kSruF32NW * kWave), 0, stream, (const float*)zf, (const float*)zr,
+                       (const float*)zx, bias_f, bias_r, c0, (float*)h, c_last, T, C, D,
+                       (int)p.ncb, (int)p.ntb, vec, status, tickets);
   }
   return hipGetLastError();
 }

@@ -1,0 +1,86 @@
+"""The scan and SRU entry points captured in a HIP graph give the eager results
+on every replay.  Replays are interleaved with unrelated eager launches and
+host synchronisations.  Single-chunk channels use one fixed association order,
+so those replays must match the eager run bit for bit; multi-chunk channels
+(look-back carries, reset kernel inside the graph) may combine chunk
+aggregates in a timing-dependent order and are held to the parity bar."""
+import numpy as np
+import pytest
+import torch
+
+import linear_recurrence_scan_diagonal_amd as lrs
+from linear_recurrence_scan_diagonal_amd import inputs as I
+from conftest import relerr
+from gpu_util import DEV, bf16_dev, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def scan_case(B, D, T, layout, seed):
+    w = I.scaled(I.WORKLOADS["scan_fwd_bwd"], B=B, D=D, T=T, seed=seed)
+    x = I.scan_inputs(w)
+    t = {k: to_dev(x[k], B, D, T, layout) for k in ("a", "b", "g")}
+    t["h0"] = torch.from_numpy(x["h0"].reshape(B, D)).to(DEV)
+    out = {"h": torch.empty_like(t["a"]), "da": torch.empty_like(t["a"]),
+           "db": torch.empty_like(t["a"]),
+           "dh0": torch.empty((B, D), dtype=torch.float32, device=DEV)}
+    ws = torch.empty(max(1, lrs.scan_workspace_bytes(B, D, T, layout)), dtype=torch.uint8,
+                     device=DEV)
+
+    def step():
+        lrs.scan_fwd(t["a"], t["b"], t["h0"], layout=layout, out=out["h"], workspace=ws)
+        lrs.scan_bwd(t["a"], out["h"], t["g"], t["h0"], layout=layout, grad_a=out["da"],
+                     grad_b=out["db"], grad_h0=out["dh0"], workspace=ws)
+    return step, out
+
+
+@pytest.mark.parametrize("layout", ["bdt", "tbd"])
+@pytest.mark.parametrize("B,D,T,exact", [(2, 64, 4096, True), (1, 8, 20000, False)])
+def test_scan_graph_replay(layout, B, D, T, exact):
+    log(f"graph replay scan {layout} B={B} D={D} T={T}")
+    step, out = scan_case(B, D, T, layout, seed=3100 + T)
+    step()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in out.items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    other_step, _ = scan_case(1, 3, 777, layout, seed=99)
+    for rep in range(4):
+        for v in out.values():
+            v.fill_(float("nan"))
+        other_step()              # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in out:
+            if exact and layout == "bdt":
+                assert torch.equal(out[k], ref[k]), (rep, k)
+            else:
+                assert relerr(out[k].cpu().numpy(), ref[k].cpu().numpy()) <= 1e-5, (rep, k)
+
+
+def test_sru_graph_replay():
+    w = I.scaled(I.WORKLOADS["sru_fwd"], B=4, D=256, T=700, seed=3300)
+    s = I.sru_inputs(w)
+    z = {k: bf16_dev(s[k]) for k in ("zf", "zr", "zx")}
+    bf = torch.from_numpy(s["bias_f"]).to(DEV)
+    br = torch.from_numpy(s["bias_r"]).to(DEV)
+    h = torch.empty_like(z["zf"])
+    ws = torch.empty(max(1, lrs.load().lrs_sru_workspace_bytes(w.T, w.B, w.D)), dtype=torch.uint8,
+                     device=DEV)
+
+    def step():
+        lrs.sru_fwd(z["zf"], z["zr"], z["zx"], bf, br, out=h, workspace=ws)
+    step()
+    torch.cuda.synchronize()
+    ref = h.float().clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        h.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert relerr(h.float().cpu().numpy(), ref.cpu().numpy()) <= 1e-5, rep
