@@ -49,18 +49,128 @@ def csrc_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_key: str):
-    """HBM bytes per launch of a kernel from the committed counter summary, or
-    None when there is none or the kernels changed since it was taken."""
+def measured_traffic(workload: str, kernel_key: str):
+    """HBM bytes per launch of a kernel on a workload from the committed
+    counter summary, or None when there is none or the kernel sources changed
+    since the counters were taken."""
     try:
         with open(COUNTERS_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("csrc_hash") != csrc_hash():
+    k = rec.get(f"{workload}/{kernel_key}")
+    if k is None or k.get("csrc_hash") != csrc_hash():
         return None
-    k = rec.get("kernels", {}).get(kernel_key)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+    return k.get("hbm_bytes_per_launch")
+
+
+# rocprof kernel names of each timed entry point (substring match)
+KERNEL_NAMES = {"scan_fwd_f32": ("k_scan_fwd_bdt", "k_scan_fwd_tbd"),
+                "scan_bwd_f32": ("k_scan_bwd_bdt", "k_scan_bwd_tbd"),
+                "sru_fwd_bf16": ("k_sru_fwd<unsigned short",),
+                "deer_solve": ("k_deer_iter",)}
+CALIB_NAME = "CUDAFunctor_add<float>"  # the stream reference kernel
+CALIB_READ = 2 * 4 * (1 << 26)
+CALIB_WRITE = 4 * (1 << 26)
+
+
+def summarize(args):
+    """Turn rocprofv3 CSV output (kernel trace + stats, and one --pmc run each
+    for FETCH_SIZE and WRITE_SIZE) into profiles/<kernel>__<workload>.md and
+    the per-launch HBM traffic record in profiles/hbm_counters.json."""
+    import csv
+    import glob
+    d = args.summarize
+    wl = args.workload
+    tag = wl if args.layout == "bdt" else f"{wl}_{args.layout}"  # output and record name
+    cmd_base = f"python3 bench.py --workload {wl}" + (f" --layout {args.layout}" if args.layout != "bdt" else "")
+
+    def rows(pattern):
+        out = []
+        for f in sorted(glob.glob(os.path.join(d, pattern), recursive=True)):
+            with open(f) as fh:
+                out.extend(csv.DictReader(fh))
+        return out
+
+    stats = rows(f"trace_{tag}/**/*kernel_stats.csv")
+    pmc = {c: rows(f"{c.lower()}_{tag}/**/*counter_collection.csv") for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    bench_line = None
+    for f in glob.glob(os.path.join(d, f"trace_{tag}.json")):
+        with open(f) as fh:
+            for line in fh:
+                if line.startswith("{"):
+                    bench_line = json.loads(line)
+
+    def per_dispatch(counter, pat):
+        vals = [float(r["Counter_Value"]) * 1024 for r in pmc[counter] if pat in r["Kernel_Name"]]
+        return sum(vals) / len(vals) if vals else None
+
+    factor = {}
+    for c, known in (("FETCH_SIZE", CALIB_READ), ("WRITE_SIZE", CALIB_WRITE)):
+        v = per_dispatch(c, CALIB_NAME)
+        factor[c] = known / v if v else None
+    try:
+        with open(COUNTERS_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    lines = [f"# rocprofv3 summary: workload `{tag}`", "",
+             "Commands (repo root, one MI355X):", "",
+             f"    rocprofv3 --kernel-trace --stats -f csv -d <out>/trace_{tag} -o t -- {cmd_base} --steps 20 --warmup 3 --no-cpu-baseline > <out>/trace_{tag}.json",
+             f"    rocprofv3 --pmc FETCH_SIZE -f csv -d <out>/fetch_size_{tag} -o p -- {cmd_base} --steps 3 --warmup 1 --no-cpu-baseline",
+             f"    rocprofv3 --pmc WRITE_SIZE -f csv -d <out>/write_size_{tag} -o p -- {cmd_base} --steps 3 --warmup 1 --no-cpu-baseline",
+             f"    python3 bench.py --summarize <out> --workload {wl}" + (f" --layout {args.layout}" if args.layout != "bdt" else ""),
+             "", "## Kernel trace (--stats)", "",
+             "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for r in stats:
+        if "lrs::" in r["Name"] or CALIB_NAME in r["Name"]:
+            lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
+                         f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} |")
+    if bench_line:
+        lines += ["", "Same run, bench.py's own per-call HIP-event averages (ms): "
+                  f"{bench_line.get('per_kernel_ms')}; value {bench_line['value']:.4g} elements/s, "
+                  f"{bench_line['ms_per_step']:.5f} ms/step."]
+    lines += ["", "## HBM traffic (--pmc, per dispatch)", "",
+              f"Calibration: torch add over 3 x 256 MiB reads {CALIB_READ} B and writes {CALIB_WRITE} B; "
+              f"its FETCH_SIZE/WRITE_SIZE scale to those byte counts by factors "
+              f"{factor['FETCH_SIZE'] and round(factor['FETCH_SIZE'], 3)} and "
+              f"{factor['WRITE_SIZE'] and round(factor['WRITE_SIZE'], 3)}.", "",
+              "| kernel | raw FETCH KiB | raw WRITE KiB | scaled HBM bytes | algorithmic bytes | ratio |",
+              "|---|---|---|---|---|---|"]
+    from linear_recurrence_scan_diagonal_amd import inputs as I
+    w = I.WORKLOADS[wl]
+    algo = {"scan_fwd_f32": BYTES_PER_ELEM["scan_fwd_f32"] * w.N,
+            "scan_bwd_f32": BYTES_PER_ELEM["scan_bwd_f32"] * w.N,
+            "sru_fwd_bf16": BYTES_PER_ELEM["sru_fwd_bf16"] * w.N,
+            "deer_solve": None}
+    for key, pats in KERNEL_NAMES.items():
+        for pat in pats:
+            f_ = per_dispatch("FETCH_SIZE", pat)
+            w_ = per_dispatch("WRITE_SIZE", pat)
+            if f_ is None or w_ is None or not factor["FETCH_SIZE"] or not factor["WRITE_SIZE"]:
+                continue
+            hbm = f_ * factor["FETCH_SIZE"] + w_ * factor["WRITE_SIZE"]
+            a = algo[key]
+            if key == "deer_solve":
+                # one launch per Newton iteration: first iteration 8 B/elem, then 12 B/elem
+                n_it = len([r for r in pmc["FETCH_SIZE"] if pat in r["Kernel_Name"]])
+                a = None
+                hbm_solve = hbm * 5  # five iterations per solve on this workload
+                rec[f"{tag}/{key}"] = {"hbm_bytes_per_launch": round(hbm_solve), "csrc_hash": csrc_hash(),
+                                      "per_iteration_bytes": round(hbm), "dispatches": n_it}
+            else:
+                rec[f"{tag}/{key}"] = {"hbm_bytes_per_launch": round(hbm), "csrc_hash": csrc_hash(),
+                                      "algorithmic_bytes": a}
+            lines.append(f"| `{pat}` | {f_/1024:.0f} | {w_/1024:.0f} | {hbm:.4g} | "
+                         f"{a if a else 'n/a'} | {hbm / a if a else float('nan'):.3f} |")
+    lines += ["", f"Kernel sources hash: `{csrc_hash()}` (bench.py reports `traffic` only while it matches)."]
+    os.makedirs(os.path.dirname(COUNTERS_FILE), exist_ok=True)
+    with open(COUNTERS_FILE, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    out = os.path.join(ROOT, "profiles", f"{tag}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {out}")
 
 
 def parse():
@@ -76,6 +186,8 @@ def parse():
                    help="also time the step captured as a HIP graph and replayed")
     p.add_argument("--no-stream-ref", action="store_true",
                    help="skip the read-2/write-1 stream reference kernel")
+    p.add_argument("--summarize", metavar="DIR",
+                   help="summarise rocprofv3 CSV output under DIR into profiles/ and exit")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time for the oracle baseline sample")
     return p.parse_args()
@@ -115,6 +227,9 @@ def cpu_threads() -> int:
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); every channel is "
               "independent, so several GPUs would each run this same per-GPU workload.",
@@ -250,7 +365,7 @@ def main():
         extra["deer_iters"] = iters
         extra["deer_deltas"] = info_box["info"]["deltas"]
     achieved = dom_bytes / (dom_ms / 1e3) / 1e9
-    traffic = measured_traffic(dom)
+    traffic = measured_traffic(w.name if args.layout == "bdt" else f"{w.name}_{args.layout}", dom)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes": dom_bytes,
