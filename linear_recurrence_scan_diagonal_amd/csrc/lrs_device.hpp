@@ -128,6 +128,42 @@ __device__ __forceinline__ float lookback_carry(const uint64_t* st, int c, int64
   }
 }
 
+// Wave-wide look-back, run by all 64 lanes of one wave: lane j inspects the
+// status of chunk p - j, so one poll covers 64 predecessors.  Aggregates of
+// the nearest predecessors are folded in order (nearest first) until an
+// inclusive state is found; if the nearest unfolded predecessor has published
+// nothing yet, the wave sleeps and polls again.  Returns the state entering
+// chunk c (uniform across the wave).
+__device__ __forceinline__ float lookback_carry_wave(const uint64_t* st, int c, int64_t stride) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float accA = 1.0f, accB = 0.0f;  // composition of the chunks already folded
+  int p = c - 1;                   // nearest predecessor not yet folded
+  uint32_t spins = 0;
+  while (true) {
+    const int idx = p - lane;
+    const uint64_t v = (idx >= 0) ? status_load(st + (int64_t)idx * stride) : kStatusEmpty;
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    const uint64_t inc = __ballot(v != kStatusEmpty && lo == kIncTag);
+    const uint64_t emp = __ballot(v == kStatusEmpty);
+    const int first_inc = inc ? (int)__builtin_ctzll(inc) : kWave;
+    const int first_emp = emp ? (int)__builtin_ctzll(emp) : kWave;
+    const int n = first_inc < first_emp ? first_inc : first_emp;  // lanes 0..n-1: aggregates
+    for (int j = 0; j < n; ++j) {
+      const float A = as_f32((uint32_t)__builtin_amdgcn_readlane((int)lo, j));
+      const float B = as_f32((uint32_t)__builtin_amdgcn_readlane((int)hi, j));
+      accB = __builtin_fmaf(accA, B, accB);
+      accA = accA * A;
+    }
+    if (first_inc < first_emp)
+      return __builtin_fmaf(accA, as_f32((uint32_t)__builtin_amdgcn_readlane((int)hi, n)), accB);
+    p -= n;
+    if (n == 0) {
+      if (++spins > kSpinLimit) return __builtin_nanf("");
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+}
+
 __device__ __forceinline__ unsigned take_ticket(unsigned* counter) {
   return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -160,6 +196,26 @@ __device__ __forceinline__ float4 load_group(const float* __restrict__ row, int6
   return v;
 }
 
+// Full-range variants: the whole group is in range and aligned (no checks).
+template <bool NT = false>
+__device__ __forceinline__ float4 load_group_full(const float* __restrict__ row, int64_t p) {
+  if (NT) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(row + p));
+    return make_float4(v.x, v.y, v.z, v.w);
+  }
+  return *reinterpret_cast<const float4*>(row + p);
+}
+
+template <bool NT = false>
+__device__ __forceinline__ void store_group_full(float* __restrict__ row, int64_t p, float4 v) {
+  if (NT) {
+    const f32x4_t x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4_t*>(row + p));
+  } else {
+    *reinterpret_cast<float4*>(row + p) = v;
+  }
+}
+
 template <bool NT = false>
 __device__ __forceinline__ void store_group(float* __restrict__ row, int64_t p, int64_t T,
                                             bool vec, float4 v) {
@@ -176,6 +232,19 @@ __device__ __forceinline__ void store_group(float* __restrict__ row, int64_t p, 
   if (p + 1 < T) row[p + 1] = v.y;
   if (p + 2 < T) row[p + 2] = v.z;
   if (p + 3 < T) row[p + 3] = v.w;
+}
+
+// FULL selects the unchecked access; otherwise the checked one above.
+template <bool FULL, bool NT>
+__device__ __forceinline__ float4 ld4(const float* __restrict__ row, int64_t p, int64_t T, bool vec,
+                                      float fill) {
+  return FULL ? load_group_full<NT>(row, p) : load_group<NT>(row, p, T, vec, fill);
+}
+template <bool FULL, bool NT>
+__device__ __forceinline__ void st4(float* __restrict__ row, int64_t p, int64_t T, bool vec,
+                                    float4 v) {
+  if (FULL) store_group_full<NT>(row, p, v);
+  else store_group<NT>(row, p, T, vec, v);
 }
 
 // tanh from its definition through exp: tanh(x) = 1 - 2/(exp(2x) + 1).
