@@ -325,7 +325,8 @@ size_t lrs_deer_workspace_bytes(int64_t B, int64_t D, int64_t T, int k_max) {
   if (!shape_ok(B, D, T, &C, &N) || k_max < 1) return 0;
   if (N == 0) return 0;
   const lrs::RowPlan p = deer_plan(C, T);
-  size_t bytes = kAlign + align_up((size_t)k_max * 4) + align_up((size_t)N * 4);
+  size_t bytes = kAlign + align_up(((size_t)lrs::kDeltaSetWords + (size_t)k_max) * 4) +
+                 align_up((size_t)N * 4);
   if (p.nchunk > 1) bytes += align_up((size_t)(C * p.nchunk) * 8) + align_up((size_t)C * 4);
   return bytes;
 }
@@ -357,7 +358,9 @@ int lrs_deer_solve(const float* w, const float* u, const float* h0, const float*
   hipStream_t s = (hipStream_t)stream;
 
   Carve cv(align_ptr(workspace));
-  uint32_t* delta_bits = cv.take<uint32_t>(k_max);
+  // norm slot sets followed by the per-iteration norms, cleared together
+  uint32_t* delta_bits = cv.take<uint32_t>(lrs::kDeltaSetWords + k_max);
+  uint32_t* delta_out = delta_bits + lrs::kDeltaSetWords;
   float* ybuf = cv.take<float>(N);
   uint64_t* status = nullptr;
   unsigned* tickets = nullptr;
@@ -375,7 +378,8 @@ int lrs_deer_solve(const float* w, const float* u, const float* h0, const float*
   const int vec = aligned(u, 16) && aligned(h, 16) && aligned(ybuf, 16) &&
                   (!h_init || aligned(h_init, 16)) && (T % 4 == 0);
   int rc = hip_status(lrs::launch_reset(status, p.nchunk > 1 ? C * p.nchunk : 0, tickets,
-                                        p.nchunk > 1 ? C : 0, delta_bits, k_max, s));
+                                        p.nchunk > 1 ? C : 0, delta_bits,
+                                        lrs::kDeltaSetWords + k_max, s));
   if (rc != LRS_OK) return rc;
   for (int i = 0; i < k_max; ++i) {
     if (i > 0 && p.nchunk > 1) {
@@ -384,11 +388,13 @@ int lrs_deer_solve(const float* w, const float* u, const float* h0, const float*
     }
     const float* y = (i == 0) ? h_init : P[(i - 1) & 1];
     rc = hip_status(lrs::launch_deer_iter(w, u, y, h0, P[i & 1], C, D, T, p, vec, status,
-                                          tickets, delta_bits, i, eps, s));
+                                          tickets, delta_bits, delta_out, i, eps, s));
     if (rc != LRS_OK) return rc;
   }
+  rc = hip_status(lrs::launch_deer_last_delta(delta_bits, delta_out, k_max - 1, s));
+  if (rc != LRS_OK) return rc;
   std::vector<uint32_t> dbits((size_t)k_max);
-  if (hipMemcpyAsync(dbits.data(), delta_bits, sizeof(uint32_t) * (size_t)k_max,
+  if (hipMemcpyAsync(dbits.data(), delta_out, sizeof(uint32_t) * (size_t)k_max,
                      hipMemcpyDeviceToHost, s) != hipSuccess)
     return LRS_ERR_HIP;
   if (hipStreamSynchronize(s) != hipSuccess) return LRS_ERR_HIP;

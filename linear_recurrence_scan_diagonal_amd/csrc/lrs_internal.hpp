@@ -14,6 +14,7 @@ struct RowPlan {
   int r = 2;
   int64_t nchunk = 1;
   bool stream = false;  // nontemporal loads and stores (arrays far larger than the caches)
+  int sub = 1;          // sequential sub-chunks per workgroup (single-workgroup channels)
   int threads() const { return nw * 64; }
   int64_t chunk() const { return (int64_t)nw * r * 256; }
 };
@@ -44,10 +45,17 @@ hipError_t launch_scan_bwd_bdt(const float* a, const float* h, const float* h0, 
                                float* da, float* db, float* dh0, int64_t C, int64_t T,
                                const RowPlan& p, int vec, uint64_t* status, unsigned* tickets,
                                hipStream_t stream);
+// DEER update norms: three rotating sets of kDeltaSlots words, kDeltaStride
+// words apart (one cache line per slot).
+constexpr int kDeltaSlots = 64;
+constexpr int kDeltaStride = 32;
+constexpr int64_t kDeltaSetWords = 3 * kDeltaSlots * kDeltaStride;
+hipError_t launch_deer_last_delta(const uint32_t* delta_bits, uint32_t* delta_out, int last,
+                                  hipStream_t stream);
 hipError_t launch_deer_iter(const float* w, const float* u, const float* y, const float* h0,
                             float* yn, int64_t C, int64_t D, int64_t T, const RowPlan& p, int vec,
-                            uint64_t* status, unsigned* tickets, uint32_t* delta_bits, int iter,
-                            float eps, hipStream_t stream);
+                            uint64_t* status, unsigned* tickets, uint32_t* delta_bits,
+                            uint32_t* delta_out, int iter, float eps, hipStream_t stream);
 
 hipError_t launch_scan_fwd_tbd(const float* a, const float* b, const float* h0, float* h,
                                int64_t C, int64_t T, const ColPlan& p, int vec, uint64_t* status,

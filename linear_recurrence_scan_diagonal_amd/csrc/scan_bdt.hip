@@ -324,25 +324,24 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_bwd_bdt(
 // rule delta < eps (DEER page, engineering section); a skipped iteration
 // leaves its slot at 0, so later ones skip as well.
 // ---------------------------------------------------------------------------
-template <int NW, int R>
-__global__ __launch_bounds__(NW* kWave) void k_deer_iter(
-    const float* __restrict__ w, const float* __restrict__ u, const float* __restrict__ y,
-    const float* __restrict__ h0, float* __restrict__ yn, int64_t T, int64_t C, int64_t D,
-    int nchunk, int vec, uint64_t* __restrict__ status, unsigned* __restrict__ tickets,
-    uint32_t* __restrict__ delta_bits, int iter, float eps) {
+// One chunk (chunk index c of the channel) of a DEER iteration.  x_start is
+// the state entering the chunk when the caller knows it (multi == false);
+// returns the state leaving the chunk and folds |y' - y| into dmax.
+template <int NW, int R, bool FULL>
+__device__ __forceinline__ float deer_chunk(const float* __restrict__ w, const float* __restrict__ u,
+                                            const float* __restrict__ y,
+                                            const float* __restrict__ h0, float* __restrict__ yn,
+                                            int64_t T, int64_t D, int64_t ch, int c, bool multi,
+                                            float x_start, int vec, uint64_t* st,
+                                            uint32_t& dmax, BlockShared<NW>& s) {
   constexpr int S = R * 256, CH = NW * S;
-  __shared__ BlockShared<NW> s;
-  // The previous iteration's norm was completed by the previous kernel, so a
-  // plain (cached, wave-uniform) load sees it; a cache-bypassing atomic read
-  // of one address from every workgroup would serialise in the memory system.
-  if (iter > 0 && as_f32(delta_bits[iter - 1]) < eps) return;
-  const bool multi = nchunk > 1;
-  const int64_t ch = multi ? chunk_channel(blockIdx.x, C, nchunk) : (int64_t)blockIdx.x;
-  const int c = chunk_ticket<NW>(multi, tickets, ch, s);
+  // tanh(v) = 1 - 2 / (1 + 2^(v * 2 log2 e)); the scale is folded into w and u
+  constexpr float k2l2e = 2.0f * 1.4426950408889634f;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   const int64_t wbeg = (int64_t)c * CH + (int64_t)wid * S;
   const int64_t base = wbeg + 4 * lane;
   const float wd = w[ch % D];
+  const float ws = wd * k2l2e;
   const float x0 = h0 ? h0[ch] : 0.0f;
   const float* urow = u + ch * T;
   const float* yrow = y ? y + ch * T : nullptr;
@@ -350,35 +349,44 @@ __global__ __launch_bounds__(NW* kWave) void k_deer_iter(
   float4 u4[R], y4[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    u4[r] = load_group(urow, base + r * 256, T, vec, 0.0f);
-    y4[r] = yrow ? load_group(yrow, base + r * 256, T, vec, 0.0f) : make_float4(0.f, 0.f, 0.f, 0.f);
+    u4[r] = ld4<FULL, false>(urow, base + r * 256, T, vec, 0.0f);
+    y4[r] = yrow ? ld4<FULL, false>(yrow, base + r * 256, T, vec, 0.0f)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   // y just before the wave's segment (h0 at the start of the sequence)
   const float y_before = (wbeg > 0) ? ((yrow && wbeg - 1 < T) ? yrow[wbeg - 1] : 0.0f) : x0;
 
-  float J[R][4], rh[R][4], Ai[R], Bi[R], RA[R], RB[R];
+  // Only z = tanh(w y_{t-1} + u_t) and the first y_{t-1} of each group are kept
+  // for the output pass, which recomputes J = w (1 - z^2) and uses
+  // y'_t = J (y'_{t-1} - y_{t-1}) + z (the same recurrence with rhs = z - J y_{t-1}).
+  float z[R][4], yf[R], Ai[R], Bi[R], RA[R], RB[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const float fy = (r > 0) ? readlane_f(y4[r - 1].w, kWave - 1) : y_before;
-    const float yp[4] = {wave_shift_up(y4[r].w, fy), y4[r].x, y4[r].y, y4[r].z};
+    yf[r] = wave_shift_up(y4[r].w, fy);
+    const float yp[4] = {yf[r], y4[r].x, y4[r].y, y4[r].z};
     const float uv[4] = {u4[r].x, u4[r].y, u4[r].z, u4[r].w};
+    float J[4], rh[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float z = tanh_fast(__builtin_fmaf(wd, yp[j], uv[j]));
-      J[r][j] = wd * __builtin_fmaf(-z, z, 1.0f);
-      rh[r][j] = __builtin_fmaf(-J[r][j], yp[j], z);
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(ws, yp[j], k2l2e * uv[j]));
+      z[r][j] = __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + e), 1.0f);
+      J[j] = __builtin_fmaf(-wd * z[r][j], z[r][j], wd);  // w (1 - z^2)
+      rh[j] = __builtin_fmaf(-J[j], yp[j], z[r][j]);      // z - J y_{t-1}
     }
-    const int64_t p = base + r * 256;
-    if (p + 4 > T) {
+    if (!FULL) {
+      const int64_t p = base + r * 256;
+      if (p + 4 > T) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (p + j >= T) { J[r][j] = 1.0f; rh[r][j] = 0.0f; }
+        for (int j = 0; j < 4; ++j)
+          if (p + j >= T) { J[j] = 1.0f; rh[j] = 0.0f; }
+      }
     }
-    float A = J[r][0], B = rh[r][0];
+    float A = J[0], B = rh[0];
 #pragma unroll
     for (int j = 1; j < 4; ++j) {
-      B = __builtin_fmaf(J[r][j], B, rh[r][j]);
-      A = A * J[r][j];
+      B = __builtin_fmaf(J[j], B, rh[j]);
+      A = A * J[j];
     }
     wave_scan(A, B);
     Ai[r] = A; Bi[r] = B;
@@ -388,28 +396,46 @@ __global__ __launch_bounds__(NW* kWave) void k_deer_iter(
   float WA, WB, PA, PB, TA, TB;
   chain_rows<R>(RA, RB, WA, WB);
   block_combine<NW>(WA, WB, s, PA, PB, TA, TB);
-  const float x_in = chunk_carry<NW>(multi, c, TA, TB, x0, status + ch * nchunk, s);
+  const float x_in = multi ? chunk_carry<NW>(true, c, TA, TB, x0, st, s) : x_start;
 
   float xr = __builtin_fmaf(PA, x_in, PB);
   float* ynrow = yn + ch * T;
-  uint32_t dmax = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     float x = wave_shift_up(__builtin_fmaf(Ai[r], xr, Bi[r]), xr);
     const int64_t p = base + r * 256;
     const float yo[4] = {y4[r].x, y4[r].y, y4[r].z, y4[r].w};
+    const float yp[4] = {yf[r], y4[r].x, y4[r].y, y4[r].z};
     float o[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      x = __builtin_fmaf(J[r][j], x, rh[r][j]);
+      const float Jj = __builtin_fmaf(-wd * z[r][j], z[r][j], wd);
+      x = __builtin_fmaf(Jj, x - yp[j], z[r][j]);
       o[j] = x;
       const uint32_t d = as_u32(fabsf(x - yo[j]));
-      if (p + j < T) dmax = d > dmax ? d : dmax;
+      if (FULL || p + j < T) dmax = d > dmax ? d : dmax;
     }
-    store_group(ynrow, p, T, vec, make_float4(o[0], o[1], o[2], o[3]));
+    st4<FULL, false>(ynrow, p, T, vec, make_float4(o[0], o[1], o[2], o[3]));
     xr = __builtin_fmaf(RA[r], xr, RB[r]);
   }
+  return __builtin_fmaf(TA, x_in, TB);
+}
 
+// The update norm of an iteration is accumulated in kDeltaSlots words on
+// separate cache lines (workgroup b uses slot b % kDeltaSlots), so thousands of
+// workgroups do not serialise on one atomic address.  Three such sets rotate:
+// iteration i accumulates into set i % 3, reads the norm of iteration i - 1
+// from set (i - 1) % 3, and its workgroup 0 clears set (i + 1) % 3 for the
+// next iteration and stores the folded norm of iteration i - 1 in out[i - 1].
+__device__ __forceinline__ uint32_t* delta_set(uint32_t* delta_bits, int iter) {
+  return delta_bits + (iter % 3) * (kDeltaSlots * kDeltaStride);
+}
+
+// Fold a workgroup's max |y' - y| into its slot of the iteration.
+template <int NW>
+__device__ __forceinline__ void deer_publish_delta(uint32_t dmax, uint32_t* __restrict__ delta_bits,
+                                                   int iter, BlockShared<NW>& s) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   dmax = wave_max_u32(dmax);
   if (lane == 0) s.wmax[wid] = dmax;
   __syncthreads();
@@ -417,8 +443,80 @@ __global__ __launch_bounds__(NW* kWave) void k_deer_iter(
     uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < NW; ++i) m = s.wmax[i] > m ? s.wmax[i] : m;
-    __hip_atomic_fetch_max(delta_bits + iter, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t* slot = delta_set(delta_bits, iter) + (blockIdx.x % kDeltaSlots) * kDeltaStride;
+    __hip_atomic_fetch_max(slot, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+// Bookkeeping at the start of iteration iter > 0: every workgroup folds the
+// previous iteration's slots (completed by the previous kernel, so plain loads
+// see them) and gets the norm through LDS; workgroup 0 also records it and
+// clears the set the next iteration accumulates into.
+template <int NW>
+__device__ __forceinline__ float deer_prev_delta(uint32_t* __restrict__ delta_bits,
+                                                 uint32_t* __restrict__ delta_out, int iter,
+                                                 BlockShared<NW>& s) {
+  static_assert(kDeltaSlots == kWave, "one slot per lane");
+  if (threadIdx.x < kWave) {
+    uint32_t v = delta_set(delta_bits, iter - 1)[threadIdx.x * kDeltaStride];
+    v = wave_max_u32(v);
+    if (blockIdx.x == 0) {
+      delta_set(delta_bits, iter + 1)[threadIdx.x * kDeltaStride] = 0u;
+      if (threadIdx.x == 0) delta_out[iter - 1] = v;
+    }
+    if (threadIdx.x == 0) s.wmax[0] = v;
+  }
+  __syncthreads();
+  const float d = as_f32(s.wmax[0]);
+  __syncthreads();  // s.wmax is reused by deer_publish_delta
+  return d;
+}
+
+// Record the norm of the last iteration (one wave).
+__global__ __launch_bounds__(kWave) void k_deer_last_delta(const uint32_t* __restrict__ delta_bits,
+                                                           uint32_t* __restrict__ delta_out,
+                                                           int last) {
+  uint32_t v = delta_bits[(last % 3) * (kDeltaSlots * kDeltaStride) + threadIdx.x * kDeltaStride];
+  v = wave_max_u32(v);
+  if (threadIdx.x == 0) delta_out[last] = v;
+}
+
+// MULTI: a channel spans several workgroups (look-back).  Otherwise one
+// workgroup owns the whole channel and walks it as SUB sequential sub-chunks
+// of NW*R*256 steps, carrying the state between them in registers (fewer
+// registers than one tile of SUB times the rows, and no look-back).
+template <int NW, int R, bool MULTI = false, int SUB = 1>
+__global__ __launch_bounds__(NW* kWave) void k_deer_iter(
+    const float* __restrict__ w, const float* __restrict__ u, const float* __restrict__ y,
+    const float* __restrict__ h0, float* __restrict__ yn, int64_t T, int64_t C, int64_t D,
+    int nchunk, int vec, uint64_t* __restrict__ status, unsigned* __restrict__ tickets,
+    uint32_t* __restrict__ delta_bits, uint32_t* __restrict__ delta_out, int iter, float eps) {
+  constexpr int CH = NW * R * 256;
+  __shared__ BlockShared<NW> s;
+  // stop rule of the previous iteration (uniform across the whole grid)
+  if (iter > 0 && deer_prev_delta<NW>(delta_bits, delta_out, iter, s) < eps) return;
+  uint32_t dmax = 0;
+  if (MULTI) {
+    const int64_t ch = chunk_channel(blockIdx.x, C, nchunk);
+    const int c = chunk_ticket<NW>(true, tickets, ch, s);
+    uint64_t* st = status + ch * nchunk;
+    if (vec && (int64_t)(c + 1) * CH <= T)
+      deer_chunk<NW, R, true>(w, u, y, h0, yn, T, D, ch, c, true, 0.0f, vec, st, dmax, s);
+    else
+      deer_chunk<NW, R, false>(w, u, y, h0, yn, T, D, ch, c, true, 0.0f, vec, st, dmax, s);
+  } else {
+    const int64_t ch = blockIdx.x;
+    float x = h0 ? h0[ch] : 0.0f;
+#pragma unroll 1
+    for (int c = 0; c < SUB && (int64_t)c * CH < T; ++c) {
+      if (c > 0) __syncthreads();  // LDS of the previous sub-chunk fully read
+      if (vec && (int64_t)(c + 1) * CH <= T)
+        x = deer_chunk<NW, R, true>(w, u, y, h0, yn, T, D, ch, c, false, x, vec, nullptr, dmax, s);
+      else
+        x = deer_chunk<NW, R, false>(w, u, y, h0, yn, T, D, ch, c, false, x, vec, nullptr, dmax, s);
+    }
+  }
+  deer_publish_delta<NW>(dmax, delta_bits, iter, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -434,8 +532,11 @@ namespace {
 struct Shape { int nw, r; };
 constexpr Shape kScanSingle[] = {{1, 1}, {2, 1}, {4, 1}, {8, 1}, {8, 2}};
 constexpr Shape kScanMulti = {8, 2};
-constexpr Shape kDeerSingle[] = {{1, 1}, {2, 1}, {4, 1}, {8, 1}, {8, 2}, {8, 4}};
-constexpr Shape kDeerMulti = {8, 4};
+constexpr Shape kDeerSingle[] = {{1, 1}, {2, 1}, {4, 1}, {8, 1}, {8, 2}};
+constexpr Shape kDeerMulti = {8, 2};
+// a DEER channel of up to kDeerSub chunks of the largest single shape stays in
+// one workgroup, walked as sequential sub-chunks
+constexpr int kDeerSub = 2;
 // Arrays of at least this many bytes (the size of the memory-side cache) are
 // streamed with nontemporal loads and stores: measured +8% at 2 GiB per array;
 // smaller arrays keep the default policy, whose cache reuse between the forward
@@ -468,8 +569,14 @@ RowPlan plan_scan_rows(int64_t C, int64_t T) {
 }
 
 RowPlan plan_deer_rows(int64_t C, int64_t T) {
+  (void)C;
   RowPlan p = pick(T, kDeerSingle, kDeerMulti);
   p.stream = false;
+  p.sub = 1;
+  if (p.nchunk > 1 && p.nchunk <= kDeerSub) {  // one workgroup walks the channel
+    p.sub = (int)p.nchunk;
+    p.nchunk = 1;
+  }
   return p;
 }
 
@@ -532,20 +639,32 @@ hipError_t launch_scan_bwd_bdt(const float* a, const float* h, const float* h0, 
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_deer_last_delta(const uint32_t* delta_bits, uint32_t* delta_out, int last,
+                                  hipStream_t stream) {
+  hipLaunchKernelGGL(k_deer_last_delta, dim3(1), dim3(kWave), 0, stream, delta_bits, delta_out,
+                     last);
+  return hipGetLastError();
+}
+
 hipError_t launch_deer_iter(const float* w, const float* u, const float* y, const float* h0,
                             float* yn, int64_t C, int64_t D, int64_t T, const RowPlan& p, int vec,
-                            uint64_t* status, unsigned* tickets, uint32_t* delta_bits, int iter,
-                            float eps, hipStream_t stream) {
+                            uint64_t* status, unsigned* tickets, uint32_t* delta_bits,
+                            uint32_t* delta_out, int iter, float eps, hipStream_t stream) {
   const dim3 grid((unsigned)((uint64_t)C * (uint64_t)p.nchunk));
-#define LRS_DEER hipLaunchKernelGGL((k_deer_iter<NW, RR>), grid, dim3(NW * kWave), 0, stream, w, u, y, \
-                                    h0, yn, T, C, D, (int)p.nchunk, vec, status, tickets, delta_bits, \
-                                    iter, eps)
-  LRS_SHAPE_CASE(1, 1, LRS_DEER)
-  LRS_SHAPE_CASE(2, 1, LRS_DEER)
-  LRS_SHAPE_CASE(4, 1, LRS_DEER)
-  LRS_SHAPE_CASE(8, 1, LRS_DEER)
-  LRS_SHAPE_CASE(8, 2, LRS_DEER)
-  LRS_SHAPE_CASE(8, 4, LRS_DEER)
+#define LRS_DEER(M, SB) hipLaunchKernelGGL((k_deer_iter<NW, RR, M, SB>), grid, dim3(NW * kWave), 0, \
+                                           stream, w, u, y, h0, yn, T, C, D, (int)p.nchunk, vec, \
+                                           status, tickets, delta_bits, delta_out, iter, eps)
+  if (p.nchunk > 1) {
+    LRS_SHAPE_CASE(kDeerMulti.nw, kDeerMulti.r, LRS_DEER(true, 1))
+  } else if (p.sub == 2) {
+    LRS_SHAPE_CASE(8, 2, LRS_DEER(false, 2))
+  } else {
+    LRS_SHAPE_CASE(1, 1, LRS_DEER(false, 1))
+    LRS_SHAPE_CASE(2, 1, LRS_DEER(false, 1))
+    LRS_SHAPE_CASE(4, 1, LRS_DEER(false, 1))
+    LRS_SHAPE_CASE(8, 1, LRS_DEER(false, 1))
+    LRS_SHAPE_CASE(8, 2, LRS_DEER(false, 1))
+  }
 #undef LRS_DEER
   return hipErrorInvalidValue;
 }
