@@ -63,8 +63,10 @@ bool grid_ok(int64_t blocks, int threads) { return blocks > 0 && blocks * thread
 
 int scan_ws_needs(int64_t C, int64_t T, int layout, size_t* bytes) {
   if (layout == LRS_LAYOUT_BDT) {
-    const lrs::RowPlan p = lrs::plan_scan_rows(C, T);
-    *bytes = p.nchunk > 1 ? lookback_bytes(C * p.nchunk, C) : 0;
+    const lrs::RowPlan f = lrs::plan_scan_fwd_rows(C, T), b = lrs::plan_scan_bwd_rows(C, T);
+    const size_t bf = f.nchunk > 1 ? lookback_bytes(C * f.nchunk, C) : 0;
+    const size_t bb = b.nchunk > 1 ? lookback_bytes(C * b.nchunk, C) : 0;
+    *bytes = bf > bb ? bf : bb;
   } else {
     const lrs::ColPlan f = lrs::plan_scan_fwd_tbd(C, T), b = lrs::plan_scan_bwd_tbd(C, T);
     const size_t bf = lookback_bytes(lrs::col_status_words(f), f.ncb);
@@ -150,7 +152,7 @@ int lrs_scan_fwd(const void* a, const void* b, const float* h0, void* h, int64_t
   const bool al16 = aligned(a, 16) && aligned(b, 16) && aligned(h, 16);
 
   if (layout == LRS_LAYOUT_BDT) {
-    const lrs::RowPlan p = lrs::plan_scan_rows(C, T);
+    const lrs::RowPlan p = lrs::plan_scan_fwd_rows(C, T);
     if (!grid_ok(C * p.nchunk, p.threads())) return LRS_ERR_UNSUPPORTED;
     uint64_t* status = nullptr;
     unsigned* tickets = nullptr;
@@ -218,7 +220,7 @@ int lrs_scan_bwd(const void* a, const void* h, const float* h0, const void* grad
                     aligned(grad_a, 16) && aligned(grad_b, 16);
 
   if (layout == LRS_LAYOUT_BDT) {
-    const lrs::RowPlan p = lrs::plan_scan_rows(C, T);
+    const lrs::RowPlan p = lrs::plan_scan_bwd_rows(C, T);
     if (!grid_ok(C * p.nchunk, p.threads())) return LRS_ERR_UNSUPPORTED;
     uint64_t* status = nullptr;
     unsigned* tickets = nullptr;

@@ -18,7 +18,8 @@ struct RowPlan {
   int threads() const { return nw * 64; }
   int64_t chunk() const { return (int64_t)nw * r * 256; }
 };
-RowPlan plan_scan_rows(int64_t C, int64_t T);
+RowPlan plan_scan_fwd_rows(int64_t C, int64_t T);
+RowPlan plan_scan_bwd_rows(int64_t C, int64_t T);
 RowPlan plan_deer_rows(int64_t C, int64_t T);
 
 // Feature-contiguous kernels: blocks of 64*cpt channels x nw*l steps.

@@ -526,12 +526,14 @@ __global__ __launch_bounds__(NW* kWave) void k_deer_iter(
 // takes the smallest single-chunk shape that covers it; a longer channel is
 // split into chunks of the multi-chunk shape and uses the look-back.  Tile
 // choices come from measured sweeps on MI355X: 8x2 for channels of up to 4096
-// steps and for the chunks of longer scans, and 8x4 for the DEER iteration,
-// whose per-step transcendental work favours more rows per wave.
+// steps; for longer scans the chunk must be large enough to amortise the wait
+// on its predecessors (8x4 forward, 16x4 backward: about 4 points of HBM
+// bandwidth over 8x2 at 2^20 steps); the DEER iteration keeps 8x2 chunks.
 namespace {
 struct Shape { int nw, r; };
 constexpr Shape kScanSingle[] = {{1, 1}, {2, 1}, {4, 1}, {8, 1}, {8, 2}};
-constexpr Shape kScanMulti = {8, 2};
+constexpr Shape kScanFwdMulti = {8, 4};
+constexpr Shape kScanBwdMulti = {16, 4};
 constexpr Shape kDeerSingle[] = {{1, 1}, {2, 1}, {4, 1}, {8, 1}, {8, 2}};
 constexpr Shape kDeerMulti = {8, 2};
 // a DEER channel of up to kDeerSub chunks of the largest single shape stays in
@@ -562,8 +564,14 @@ RowPlan pick(int64_t T, const Shape (&single)[N], Shape multi) {
 }
 }  // namespace
 
-RowPlan plan_scan_rows(int64_t C, int64_t T) {
-  RowPlan p = pick(T, kScanSingle, kScanMulti);
+RowPlan plan_scan_fwd_rows(int64_t C, int64_t T) {
+  RowPlan p = pick(T, kScanSingle, kScanFwdMulti);
+  p.stream = C * T * 4 >= kStreamBytes;
+  return p;
+}
+
+RowPlan plan_scan_bwd_rows(int64_t C, int64_t T) {
+  RowPlan p = pick(T, kScanSingle, kScanBwdMulti);
   p.stream = C * T * 4 >= kStreamBytes;
   return p;
 }
@@ -592,20 +600,22 @@ hipError_t launch_scan_fwd_bdt(const float* a, const float* b, const float* h0, 
                                            0, stream, a, b, h0, h, T, C, (int)p.nchunk, vec, status, \
                                            tickets)
   if (p.nchunk > 1) {
-    if (p.stream) { LRS_SHAPE_CASE(8, 2, LRS_FWD(true, true)) }
-    else { LRS_SHAPE_CASE(8, 2, LRS_FWD(false, true)) }
+    if (p.stream) { LRS_SHAPE_CASE(kScanFwdMulti.nw, kScanFwdMulti.r, LRS_FWD(true, true)) }
+    else { LRS_SHAPE_CASE(kScanFwdMulti.nw, kScanFwdMulti.r, LRS_FWD(false, true)) }
   } else if (p.stream) {
     LRS_SHAPE_CASE(1, 1, LRS_FWD(true, false))
     LRS_SHAPE_CASE(2, 1, LRS_FWD(true, false))
     LRS_SHAPE_CASE(4, 1, LRS_FWD(true, false))
     LRS_SHAPE_CASE(8, 1, LRS_FWD(true, false))
     LRS_SHAPE_CASE(8, 2, LRS_FWD(true, false))
+    LRS_SHAPE_CASE(kScanFwdMulti.nw, kScanFwdMulti.r, LRS_FWD(true, false))
   } else {
     LRS_SHAPE_CASE(1, 1, LRS_FWD(false, false))
     LRS_SHAPE_CASE(2, 1, LRS_FWD(false, false))
     LRS_SHAPE_CASE(4, 1, LRS_FWD(false, false))
     LRS_SHAPE_CASE(8, 1, LRS_FWD(false, false))
     LRS_SHAPE_CASE(8, 2, LRS_FWD(false, false))
+    LRS_SHAPE_CASE(kScanFwdMulti.nw, kScanFwdMulti.r, LRS_FWD(false, false))
   }
 #undef LRS_FWD
   return hipErrorInvalidValue;
@@ -620,20 +630,22 @@ hipError_t launch_scan_bwd_bdt(const float* a, const float* h, const float* h0, 
                                            0, stream, a, h, h0, g, da, db, dh0, T, C, (int)p.nchunk, \
                                            vec, status, tickets)
   if (p.nchunk > 1) {
-    if (p.stream) { LRS_SHAPE_CASE(8, 2, LRS_BWD(true, true)) }
-    else { LRS_SHAPE_CASE(8, 2, LRS_BWD(false, true)) }
+    if (p.stream) { LRS_SHAPE_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_BWD(true, true)) }
+    else { LRS_SHAPE_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_BWD(false, true)) }
   } else if (p.stream) {
     LRS_SHAPE_CASE(1, 1, LRS_BWD(true, false))
     LRS_SHAPE_CASE(2, 1, LRS_BWD(true, false))
     LRS_SHAPE_CASE(4, 1, LRS_BWD(true, false))
     LRS_SHAPE_CASE(8, 1, LRS_BWD(true, false))
     LRS_SHAPE_CASE(8, 2, LRS_BWD(true, false))
+    LRS_SHAPE_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_BWD(true, false))
   } else {
     LRS_SHAPE_CASE(1, 1, LRS_BWD(false, false))
     LRS_SHAPE_CASE(2, 1, LRS_BWD(false, false))
     LRS_SHAPE_CASE(4, 1, LRS_BWD(false, false))
     LRS_SHAPE_CASE(8, 1, LRS_BWD(false, false))
     LRS_SHAPE_CASE(8, 2, LRS_BWD(false, false))
+    LRS_SHAPE_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_BWD(false, false))
   }
 #undef LRS_BWD
   return hipErrorInvalidValue;
