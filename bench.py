@@ -20,6 +20,7 @@ on the host cores over a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -126,8 +127,28 @@ def summarize(args):
         if "lrs::" in r["Name"] or CALIB_NAME in r["Name"]:
             lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
                          f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} |")
+    # an entry point that needs look-back state launches the reset kernel
+    # first; bench.py's events bracket the whole call
+    reset = [r for r in stats if "k_reset" in r["Name"]]
+    reset_us = float(reset[0]["AverageNs"]) / 1e3 if reset else 0.0
+    reset_calls = int(reset[0]["Calls"]) if reset else 0
+    ep = []
+    mains = [r for r in stats for key, pats in KERNEL_NAMES.items()
+             if key != "deer_solve" and any(p in r["Name"] for p in pats)]
+    main_calls = sum(int(r["Calls"]) for r in mains)
+    for key, pats in KERNEL_NAMES.items():
+        for r in stats:
+            if any(p in r["Name"] for p in pats) and key != "deer_solve":
+                share = reset_calls / main_calls if main_calls else 0.0
+                ep.append(f"{key}: {float(r['AverageNs'])/1e3:.2f} us kernel"
+                          + (f" + {share:.0f} x {reset_us:.2f} us reset = "
+                             f"{float(r['AverageNs'])/1e3 + share * reset_us:.2f} us per call"
+                             if share >= 1 else ""))
+    if ep:
+        lines += ["", "Per entry-point call (rocprof averages): " + "; ".join(ep) + "."]
     if bench_line:
-        lines += ["", "Same run, bench.py's own per-call HIP-event averages (ms): "
+        lines += ["", "Same run, bench.py's own per-kernel HIP-event averages (ms, one event "
+                  "after each entry-point call of queued steps): "
                   f"{bench_line.get('per_kernel_ms')}; value {bench_line['value']:.4g} elements/s, "
                   f"{bench_line['ms_per_step']:.5f} ms/step."]
     lines += ["", "## HBM traffic (--pmc, per dispatch)", "",
@@ -194,7 +215,8 @@ def parse():
 
 
 class KernelTimer:
-    """HIP events around each call, on the stream the call launches on."""
+    """HIP events (device-scope release) around each call, on the stream the
+    call launches on."""
 
     def __init__(self, torch):
         self.torch = torch
@@ -204,17 +226,85 @@ class KernelTimer:
     def run(self, name, fn):
         if not self.enabled:
             return fn()
-        t = self.torch
-        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-        s.record()
+        stream = self.torch.cuda.current_stream().cuda_stream
+        s, e = DeviceEvent(), DeviceEvent()
+        s.record(stream)
         out = fn()
-        e.record()
+        e.record(stream)
         self.pairs.setdefault(name, []).append((s, e))
         return out
 
     def avg_ms(self, name):
         ps = self.pairs.get(name, [])
-        return sum(s.elapsed_time(e) for s, e in ps) / max(1, len(ps))
+        return sum(s.ms_until(e) for s, e in ps) / max(1, len(ps))
+
+
+class DeviceEvent:
+    """A HIP timing event recorded with a device-scope release
+    (hipEventReleaseToDevice) instead of the default system-scope one, whose
+    cache writeback would add several microseconds to every interval that
+    ends in it.  Uses the HIP runtime the process already loaded (torch's)."""
+
+    _hip = None
+    RELEASE_TO_DEVICE = 0x40000000
+
+    @classmethod
+    def hip(cls):
+        if cls._hip is None:
+            cls._hip = ctypes.CDLL("libamdhip64.so.7")
+        return cls._hip
+
+    def __init__(self):
+        self.h = ctypes.c_void_p()
+        rc = self.hip().hipEventCreateWithFlags(ctypes.byref(self.h),
+                                                ctypes.c_uint(self.RELEASE_TO_DEVICE))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream):
+        rc = self.hip().hipEventRecord(self.h, ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def ms_until(self, later):
+        ms = ctypes.c_float()
+        rc = self.hip().hipEventElapsedTime(ctypes.byref(ms), self.h, later.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.h:
+            self._hip.hipEventDestroy(self.h)
+
+
+def step_kernel_ms(torch, calls, reps):
+    """Average duration of each entry point of the step, from HIP events
+    recorded on the launch stream after every call of `reps` consecutive
+    steps.  A GPU-side spin issued first lets the host queue all of them
+    before the device reaches the first, so host launch latency stays out of
+    the measurement, and each kernel sees the same cache state as in the
+    timed steps (the previous kernel of the step ran just before it)."""
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = [DeviceEvent() for _ in range(reps * len(calls) + 1)]
+    torch.cuda.synchronize()
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(5_000_000)
+    ev[0].record(stream)
+    i = 1
+    for _ in range(reps):
+        for fn in calls.values():
+            fn()
+            ev[i].record(stream)
+            i += 1
+    torch.cuda.synchronize()
+    out = {k: 0.0 for k in calls}
+    i = 1
+    for _ in range(reps):
+        for k in calls:
+            out[k] += ev[i - 1].ms_until(ev[i]) / reps
+            i += 1
+    return out
 
 
 def cpu_threads() -> int:
@@ -269,12 +359,15 @@ def main():
         ws_bytes = lrs.scan_workspace_bytes(B, D, T, layout)
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
+        calls = {"scan_fwd_f32": lambda: lrs.scan_fwd(a, b, h0, layout=layout, out=h, workspace=ws)}
+        if not fwd_only:
+            calls["scan_bwd_f32"] = lambda: lrs.scan_bwd(a, h, g, h0, layout=layout, grad_a=ga,
+                                                         grad_b=gb, grad_h0=gh0, workspace=ws)
+
         def step():
-            timer.run("scan_fwd_f32", lambda: lrs.scan_fwd(a, b, h0, layout=layout, out=h, workspace=ws))
-            if not fwd_only:
-                timer.run("scan_bwd_f32", lambda: lrs.scan_bwd(a, h, g, h0, layout=layout, grad_a=ga,
-                                                               grad_b=gb, grad_h0=gh0, workspace=ws))
-        kernels = ["scan_fwd_f32"] + ([] if fwd_only else ["scan_bwd_f32"])
+            for fn in calls.values():
+                fn()
+        kernels = list(calls)
         dtype = "f32"
         config = {"workload": w.name, "B": B, "D": D, "T": T, "layout": layout,
                   "pass": "fwd" if fwd_only else "fwd+bwd"}
@@ -288,10 +381,12 @@ def main():
         ws = torch.empty(max(1, lrs.load().lrs_sru_workspace_bytes(T, B, D)), dtype=torch.uint8,
                          device=dev)
 
+        calls = {"sru_fwd_bf16": lambda: lrs.sru_fwd(z["zf"], z["zr"], z["zx"], bf, br, out=hs,
+                                                     workspace=ws)}
+
         def step():
-            timer.run("sru_fwd_bf16", lambda: lrs.sru_fwd(z["zf"], z["zr"], z["zx"], bf, br, out=hs,
-                                                          workspace=ws))
-        kernels = ["sru_fwd_bf16"]
+            calls["sru_fwd_bf16"]()
+        kernels = list(calls)
         dtype = "bf16 I/O, f32 state"
         config = {"workload": w.name, "B": B, "D": D, "T": T, "layout": "tbd"}
     else:  # deer
@@ -307,6 +402,7 @@ def main():
         def step():
             _, info_box["info"] = timer.run("deer_solve", lambda: lrs.deer_solve(
                 wd, u, h0, None, eps=1e-5, k_max=5, out=hd, workspace=ws))
+        calls = None  # the solve reads its stop test back to the host: timed per call
         kernels = ["deer_solve"]
         dtype = "f32"
         config = {"workload": w.name, "B": B, "D": D, "T": T, "layout": "bdt", "eps": 1e-5,
@@ -342,14 +438,21 @@ def main():
         for _ in range(2):
             graph.replay()
         extra["ms_per_step_graph"] = round(timed(graph.replay, args.steps)[0], 5)
-    # (3) eager steps with HIP events around every call, on the launch stream:
-    #     per-kernel launch durations for the roofline
-    timer.enabled = True
-    timer.pairs.clear()
-    timed(step, args.steps)
+    # (3) per-kernel launch durations for the roofline: `steps` more steps
+    #     with a HIP event after every entry point, on its launch stream
+    #     (DEER: events around every solve)
+    if calls is not None:
+        per_kernel = step_kernel_ms(torch, calls, args.steps)
+        extra["per_kernel_timing"] = ("HIP event (device-scope release) after every call of "
+                                      "queued steps")
+    else:
+        timer.enabled = True
+        timer.pairs.clear()
+        timed(step, args.steps)
+        per_kernel = {k: timer.avg_ms(k) for k in kernels}
+        extra["per_kernel_timing"] = "HIP events around every solve"
     value = N / (ms_per_step / 1e3)
 
-    per_kernel = {k: timer.avg_ms(k) for k in kernels}
     if w.kind == "scan":
         bytes_step = sum(BYTES_PER_ELEM[k] * N for k in kernels)
         dom = max(kernels, key=lambda k: per_kernel[k])

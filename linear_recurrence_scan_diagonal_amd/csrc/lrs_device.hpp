@@ -164,6 +164,81 @@ __device__ __forceinline__ float lookback_carry_wave(const uint64_t* st, int c, 
   }
 }
 
+// Look-back for the CPT channels of one lane together.  Channel k's status
+// words for blocks 0, 1, ... are st[k], st[k + stride], ...  Each poll loads
+// the W nearest unfolded predecessors of every unresolved channel at once, so
+// the usual case (nearest predecessor has its aggregate, the one before it is
+// inclusive) costs a single round trip.  `seen[k][i]` is an earlier snapshot
+// of block c-1-i (kStatusEmpty where none was taken) and serves as the first
+// poll; a snapshot is always safe to use, since a published word never
+// changes except from aggregate to inclusive.  Writes the state entering
+// block c of channels k < nv into carry[k]; NaN after kSpinLimit polls that
+// found a channel's nearest unfolded predecessor unpublished.
+template <int CPT, int W>
+__device__ __forceinline__ void lookback_cols(const uint64_t* st, int64_t stride, int c, int nv,
+                                              const uint64_t (&seen)[CPT][W],
+                                              float (&carry)[CPT]) {
+  float accA[CPT], accB[CPT];
+  int p[CPT];
+  bool done[CPT];
+  uint64_t v[CPT][W];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    accA[k] = 1.0f;
+    accB[k] = 0.0f;
+    p[k] = c - 1;
+    done[k] = k >= nv;
+#pragma unroll
+    for (int i = 0; i < W; ++i) v[k][i] = seen[k][i];
+  }
+  uint32_t spins = 0;
+  while (true) {
+    bool pending = false, stalled = false;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      bool stop = done[k];
+#pragma unroll
+      for (int i = 0; i < W; ++i) {
+        if (stop) continue;
+        const uint64_t s = v[k][i];
+        const uint32_t lo = (uint32_t)s, hi = (uint32_t)(s >> 32);
+        if (s == kStatusEmpty) {
+          stop = true;
+          stalled |= (i == 0);
+        } else if (lo == kIncTag) {
+          carry[k] = __builtin_fmaf(accA[k], as_f32(hi), accB[k]);
+          done[k] = true;
+          stop = true;
+        } else {  // aggregate of block p[k], which precedes those folded so far
+          accB[k] = __builtin_fmaf(accA[k], as_f32(hi), accB[k]);
+          accA[k] = accA[k] * as_f32(lo);
+          --p[k];
+        }
+      }
+      pending |= !done[k];
+    }
+    if (!pending) return;
+    if (stalled) {
+      if (++spins > kSpinLimit) {
+#pragma unroll
+        for (int k = 0; k < CPT; ++k)
+          if (!done[k]) carry[k] = __builtin_nanf("");
+        return;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    // block 0 is always published inclusive, so a walk never passes it
+#pragma unroll
+    for (int k = 0; k < CPT; ++k)
+#pragma unroll
+      for (int i = 0; i < W; ++i) {
+        const int idx = p[k] - i;
+        v[k][i] = (!done[k] && idx >= 0) ? status_load(st + (int64_t)idx * stride + k)
+                                         : kStatusEmpty;
+      }
+  }
+}
+
 __device__ __forceinline__ unsigned take_ticket(unsigned* counter) {
   return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -148,9 +148,12 @@ __device__ __forceinline__ void store_row_bf16(uint16_t* __restrict__ p, uint32_
 
 // ---- block-level pieces ----------------------------------------------------
 
+// Look-back window: predecessors polled per channel at once.
+constexpr int kColWindow = 2;
+
 // Per channel, the state entering this wave's first step.  Each wave publishes
-// its per-channel maps in LDS; the last wave composes all of them into the
-// block's map, runs the look-back (multi-block) and shares the carries; every
+// its per-channel maps in LDS; the last CPT waves compose them into the block's
+// per-channel maps, run the look-back (multi-block) and share the carries; every
 // wave then composes the maps of the waves before it (wave order = scan order).
 // st points at this channel block's status row for time block 0; time blocks
 // are CW words apart.
@@ -171,34 +174,38 @@ __device__ __forceinline__ void col_enter_state(const float (&A)[CPT], const flo
   __syncthreads();
   float carry[CPT];
   if (multi) {
-    if (wid == NW - 1) {
-      float TA[CPT], TB[CPT];
-#pragma unroll
-      for (int k = 0; k < CPT; ++k) { TA[k] = 1.0f; TB[k] = 0.0f; }
+    static_assert(NW >= CPT, "one look-back wave per channel of a lane");
+    if (wid >= NW - CPT) {
+      // wave NW-CPT+k resolves channel lane*CPT+k of every lane: one channel
+      // per lane keeps the look-back's registers off the other waves' paths
+      const int k = wid - (NW - CPT);
+      const int j = j0 + k;
+      float TA = 1.0f, TB = 0.0f;
       for (int w = 0; w < NW; ++w) {
+        const float wa = s.A[w][j], wb = s.B[w][j];
+        TB = __builtin_fmaf(wa, TB, wb);
+        TA = TA * wa;
+      }
+      float x_in = x0[0];
 #pragma unroll
-        for (int k = 0; k < CPT; ++k) {
-          const float wa = s.A[w][j0 + k], wb = s.B[w][j0 + k];
-          TB[k] = __builtin_fmaf(wa, TB[k], wb);
-          TA[k] = TA[k] * wa;
+      for (int kk = 1; kk < CPT; ++kk)
+        if (kk == k) x_in = x0[kk];
+      if (k < nvc) {
+        if (tb > 0) {
+          status_store(st + (int64_t)tb * CW + j, pack_agg(TA, TB));
+          uint64_t seen[1][kColWindow];
+#pragma unroll
+          for (int i = 0; i < kColWindow; ++i) {
+            const int idx = tb - 1 - i;
+            seen[0][i] = idx >= 0 ? status_load(st + (int64_t)idx * CW + j) : kStatusEmpty;
+          }
+          float xr[1];
+          lookback_cols<1, kColWindow>(st + j, CW, tb, 1, seen, xr);
+          x_in = xr[0];
         }
+        status_store(st + (int64_t)tb * CW + j, pack_inc(__builtin_fmaf(TA, x_in, TB)));
       }
-      // publish every aggregate before waiting on any predecessor
-      if (tb > 0) {
-#pragma unroll
-        for (int k = 0; k < CPT; ++k)
-          if (k < nvc) status_store(st + (int64_t)tb * CW + j0 + k, pack_agg(TA[k], TB[k]));
-      }
-#pragma unroll
-      for (int k = 0; k < CPT; ++k) {
-        const int j = j0 + k;
-        float x_in = x0[k];
-        if (k < nvc) {
-          if (tb > 0) x_in = lookback_carry(st + j, tb, CW);
-          status_store(st + (int64_t)tb * CW + j, pack_inc(__builtin_fmaf(TA[k], x_in, TB[k])));
-        }
-        s.carry[j] = x_in;
-      }
+      s.carry[j] = x_in;
     }
     __syncthreads();
 #pragma unroll
@@ -626,7 +633,7 @@ int64_t col_status_words(const ColPlan& p) { return p.ntb > 1 ? p.ncb * p.ntb * 
 namespace {
 constexpr int kFwdNW = 8, kFwdL = 16, kFwdCPT = 1;
 constexpr int kBwdNW = 8, kBwdL = 16, kBwdCPT = 1;
-constexpr int kSruNW = 8, kSruL = 8, kSruCPT = 2;           // bf16 I/O
+constexpr int kSruNW = 4, kSruL = 16, kSruCPT = 2;          // bf16 I/O
 constexpr int kSruF32NW = 8, kSruF32L = 8, kSruF32CPT = 2;  // fp32 I/O
 }  // namespace
 
