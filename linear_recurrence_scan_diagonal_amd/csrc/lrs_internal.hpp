@@ -7,6 +7,13 @@
 
 namespace lrs {
 
+// A call whose arrays (all it reads and writes) total at least this many bytes,
+// twice the memory-side cache, streams them with nontemporal loads and stores:
+// none of its data can still be cached for the next call, and keeping it out of
+// the caches measured 8-12% faster.  Smaller calls keep the default policy, so
+// that e.g. a backward pass finds part of the forward pass's data in cache.
+constexpr int64_t kStreamFootprint = (int64_t)512 << 20;
+
 // Time-contiguous kernels: chunks of nw waves x r rows x 256 steps, nchunk
 // chunks per channel.
 struct RowPlan {
@@ -26,6 +33,7 @@ RowPlan plan_deer_rows(int64_t C, int64_t T);
 struct ColPlan {
   int nw = 8, l = 8, cpt = 4;
   int64_t ncb = 1, ntb = 1;
+  bool stream = false;  // nontemporal loads and stores (see kStreamFootprint)
 };
 ColPlan plan_cols(int64_t C, int64_t T, int nw, int l, int cpt);
 ColPlan plan_scan_fwd_tbd(int64_t C, int64_t T);

@@ -327,7 +327,7 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_bwd_bdt(
 // One chunk (chunk index c of the channel) of a DEER iteration.  x_start is
 // the state entering the chunk when the caller knows it (multi == false);
 // returns the state leaving the chunk and folds |y' - y| into dmax.
-template <int NW, int R, bool FULL>
+template <int NW, int R, bool FULL, bool NT>
 __device__ __forceinline__ float deer_chunk(const float* __restrict__ w, const float* __restrict__ u,
                                             const float* __restrict__ y,
                                             const float* __restrict__ h0, float* __restrict__ yn,
@@ -349,8 +349,8 @@ __device__ __forceinline__ float deer_chunk(const float* __restrict__ w, const f
   float4 u4[R], y4[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    u4[r] = ld4<FULL, false>(urow, base + r * 256, T, vec, 0.0f);
-    y4[r] = yrow ? ld4<FULL, false>(yrow, base + r * 256, T, vec, 0.0f)
+    u4[r] = ld4<FULL, NT>(urow, base + r * 256, T, vec, 0.0f);
+    y4[r] = yrow ? ld4<FULL, NT>(yrow, base + r * 256, T, vec, 0.0f)
                  : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   // y just before the wave's segment (h0 at the start of the sequence)
@@ -415,7 +415,7 @@ __device__ __forceinline__ float deer_chunk(const float* __restrict__ w, const f
       const uint32_t d = as_u32(fabsf(x - yo[j]));
       if (FULL || p + j < T) dmax = d > dmax ? d : dmax;
     }
-    st4<FULL, false>(ynrow, p, T, vec, make_float4(o[0], o[1], o[2], o[3]));
+    st4<FULL, NT>(ynrow, p, T, vec, make_float4(o[0], o[1], o[2], o[3]));
     xr = __builtin_fmaf(RA[r], xr, RB[r]);
   }
   return __builtin_fmaf(TA, x_in, TB);
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(kWave) void k_deer_last_delta(const uint32_t* __res
 // workgroup owns the whole channel and walks it as SUB sequential sub-chunks
 // of NW*R*256 steps, carrying the state between them in registers (fewer
 // registers than one tile of SUB times the rows, and no look-back).
-template <int NW, int R, bool MULTI = false, int SUB = 1>
+template <int NW, int R, bool MULTI = false, int SUB = 1, bool NT = false>
 __global__ __launch_bounds__(NW* kWave) void k_deer_iter(
     const float* __restrict__ w, const float* __restrict__ u, const float* __restrict__ y,
     const float* __restrict__ h0, float* __restrict__ yn, int64_t T, int64_t C, int64_t D,
@@ -501,9 +501,9 @@ __global__ __launch_bounds__(NW* kWave) void k_deer_iter(
     const int c = chunk_ticket<NW>(true, tickets, ch, s);
     uint64_t* st = status + ch * nchunk;
     if (vec && (int64_t)(c + 1) * CH <= T)
-      deer_chunk<NW, R, true>(w, u, y, h0, yn, T, D, ch, c, true, 0.0f, vec, st, dmax, s);
+      deer_chunk<NW, R, true, NT>(w, u, y, h0, yn, T, D, ch, c, true, 0.0f, vec, st, dmax, s);
     else
-      deer_chunk<NW, R, false>(w, u, y, h0, yn, T, D, ch, c, true, 0.0f, vec, st, dmax, s);
+      deer_chunk<NW, R, false, NT>(w, u, y, h0, yn, T, D, ch, c, true, 0.0f, vec, st, dmax, s);
   } else {
     const int64_t ch = blockIdx.x;
     float x = h0 ? h0[ch] : 0.0f;
@@ -511,9 +511,9 @@ __global__ __launch_bounds__(NW* kWave) void k_deer_iter(
     for (int c = 0; c < SUB && (int64_t)c * CH < T; ++c) {
       if (c > 0) __syncthreads();  // LDS of the previous sub-chunk fully read
       if (vec && (int64_t)(c + 1) * CH <= T)
-        x = deer_chunk<NW, R, true>(w, u, y, h0, yn, T, D, ch, c, false, x, vec, nullptr, dmax, s);
+        x = deer_chunk<NW, R, true, NT>(w, u, y, h0, yn, T, D, ch, c, false, x, vec, nullptr, dmax, s);
       else
-        x = deer_chunk<NW, R, false>(w, u, y, h0, yn, T, D, ch, c, false, x, vec, nullptr, dmax, s);
+        x = deer_chunk<NW, R, false, NT>(w, u, y, h0, yn, T, D, ch, c, false, x, vec, nullptr, dmax, s);
     }
   }
   deer_publish_delta<NW>(dmax, delta_bits, iter, s);
@@ -539,12 +539,6 @@ constexpr Shape kDeerMulti = {8, 2};
 // a DEER channel of up to kDeerSub chunks of the largest single shape stays in
 // one workgroup, walked as sequential sub-chunks
 constexpr int kDeerSub = 2;
-// Arrays of at least this many bytes (the size of the memory-side cache) are
-// streamed with nontemporal loads and stores: measured +8% at 2 GiB per array;
-// smaller arrays keep the default policy, whose cache reuse between the forward
-// and the backward pass is worth more.
-constexpr int64_t kStreamBytes = (int64_t)256 << 20;
-
 template <size_t N>
 RowPlan pick(int64_t T, const Shape (&single)[N], Shape multi) {
   RowPlan p;
@@ -566,20 +560,20 @@ RowPlan pick(int64_t T, const Shape (&single)[N], Shape multi) {
 
 RowPlan plan_scan_fwd_rows(int64_t C, int64_t T) {
   RowPlan p = pick(T, kScanSingle, kScanFwdMulti);
-  p.stream = C * T * 4 >= kStreamBytes;
+  p.stream = 3 * C * T * 4 >= kStreamFootprint;  // a, b, h
   return p;
 }
 
 RowPlan plan_scan_bwd_rows(int64_t C, int64_t T) {
   RowPlan p = pick(T, kScanSingle, kScanBwdMulti);
-  p.stream = C * T * 4 >= kStreamBytes;
+  p.stream = 5 * C * T * 4 >= kStreamFootprint;  // a, h, g, grad_a, grad_b
   return p;
 }
 
 RowPlan plan_deer_rows(int64_t C, int64_t T) {
-  (void)C;
   RowPlan p = pick(T, kDeerSingle, kDeerMulti);
-  p.stream = false;
+  p.stream = 3 * C * T * 4 >= kStreamFootprint;  // u, y, y'
+
   p.sub = 1;
   if (p.nchunk > 1 && p.nchunk <= kDeerSub) {  // one workgroup walks the channel
     p.sub = (int)p.nchunk;
@@ -663,19 +657,30 @@ hipError_t launch_deer_iter(const float* w, const float* u, const float* y, cons
                             uint64_t* status, unsigned* tickets, uint32_t* delta_bits,
                             uint32_t* delta_out, int iter, float eps, hipStream_t stream) {
   const dim3 grid((unsigned)((uint64_t)C * (uint64_t)p.nchunk));
-#define LRS_DEER(M, SB) hipLaunchKernelGGL((k_deer_iter<NW, RR, M, SB>), grid, dim3(NW * kWave), 0, \
-                                           stream, w, u, y, h0, yn, T, C, D, (int)p.nchunk, vec, \
-                                           status, tickets, delta_bits, delta_out, iter, eps)
+#define LRS_DEER(M, SB, NTF) hipLaunchKernelGGL((k_deer_iter<NW, RR, M, SB, NTF>), grid, dim3(NW * kWave), \
+                                                0, stream, w, u, y, h0, yn, T, C, D, (int)p.nchunk, \
+                                                vec, status, tickets, delta_bits, delta_out, iter, eps)
+  // the first iteration from y = 0 reads u only and is slightly faster with
+  // the default policy
+  const bool nt = p.stream && y != nullptr;
   if (p.nchunk > 1) {
-    LRS_SHAPE_CASE(kDeerMulti.nw, kDeerMulti.r, LRS_DEER(true, 1))
+    if (nt) { LRS_SHAPE_CASE(kDeerMulti.nw, kDeerMulti.r, LRS_DEER(true, 1, true)) }
+    else { LRS_SHAPE_CASE(kDeerMulti.nw, kDeerMulti.r, LRS_DEER(true, 1, false)) }
   } else if (p.sub == 2) {
-    LRS_SHAPE_CASE(8, 2, LRS_DEER(false, 2))
+    if (nt) { LRS_SHAPE_CASE(8, 2, LRS_DEER(false, 2, true)) }
+    else { LRS_SHAPE_CASE(8, 2, LRS_DEER(false, 2, false)) }
+  } else if (nt) {
+    LRS_SHAPE_CASE(1, 1, LRS_DEER(false, 1, true))
+    LRS_SHAPE_CASE(2, 1, LRS_DEER(false, 1, true))
+    LRS_SHAPE_CASE(4, 1, LRS_DEER(false, 1, true))
+    LRS_SHAPE_CASE(8, 1, LRS_DEER(false, 1, true))
+    LRS_SHAPE_CASE(8, 2, LRS_DEER(false, 1, true))
   } else {
-    LRS_SHAPE_CASE(1, 1, LRS_DEER(false, 1))
-    LRS_SHAPE_CASE(2, 1, LRS_DEER(false, 1))
-    LRS_SHAPE_CASE(4, 1, LRS_DEER(false, 1))
-    LRS_SHAPE_CASE(8, 1, LRS_DEER(false, 1))
-    LRS_SHAPE_CASE(8, 2, LRS_DEER(false, 1))
+    LRS_SHAPE_CASE(1, 1, LRS_DEER(false, 1, false))
+    LRS_SHAPE_CASE(2, 1, LRS_DEER(false, 1, false))
+    LRS_SHAPE_CASE(4, 1, LRS_DEER(false, 1, false))
+    LRS_SHAPE_CASE(8, 1, LRS_DEER(false, 1, false))
+    LRS_SHAPE_CASE(8, 2, LRS_DEER(false, 1, false))
   }
 #undef LRS_DEER
   return hipErrorInvalidValue;

@@ -42,20 +42,36 @@ struct ColShared {
 // `p` is a wave-uniform row pointer, `off` the lane's element offset.  FULL
 // rows are in range and aligned; otherwise `nvalid` channels are in range
 // (0 for a row past the end) and the rest read as `fill` / are not written.
+// NT selects the nontemporal (streaming) cache policy for FULL rows.
 
-template <int CPT, bool FULL>
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+template <bool NT, typename V>
+__device__ __forceinline__ V ldv(const V* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool NT, typename V>
+__device__ __forceinline__ void stv(V* p, V v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+template <int CPT, bool FULL, bool NT = false>
 __device__ __forceinline__ void load_row(const float* __restrict__ p, uint32_t off, int nvalid,
                                          float fill, float (&v)[CPT]) {
   if (FULL) {
     if constexpr (CPT == 4) {
-      const float4 x = *reinterpret_cast<const float4*>(p + off);
+      const f32x4_t x = ldv<NT>(reinterpret_cast<const f32x4_t*>(p + off));
       v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
     } else if constexpr (CPT == 2) {
-      const float2 x = *reinterpret_cast<const float2*>(p + off);
+      const f32x2_t x = ldv<NT>(reinterpret_cast<const f32x2_t*>(p + off));
       v[0] = x.x; v[1] = x.y;
     } else {
 #pragma unroll
-      for (int k = 0; k < CPT; ++k) v[k] = p[off + k];
+      for (int k = 0; k < CPT; ++k) v[k] = ldv<NT>(p + off + k);
     }
   } else {
 #pragma unroll
@@ -63,17 +79,17 @@ __device__ __forceinline__ void load_row(const float* __restrict__ p, uint32_t o
   }
 }
 
-template <int CPT, bool FULL>
+template <int CPT, bool FULL, bool NT = false>
 __device__ __forceinline__ void store_row(float* __restrict__ p, uint32_t off, int nvalid,
                                           const float (&v)[CPT]) {
   if (FULL) {
     if constexpr (CPT == 4) {
-      *reinterpret_cast<float4*>(p + off) = make_float4(v[0], v[1], v[2], v[3]);
+      stv<NT>(reinterpret_cast<f32x4_t*>(p + off), f32x4_t{v[0], v[1], v[2], v[3]});
     } else if constexpr (CPT == 2) {
-      *reinterpret_cast<float2*>(p + off) = make_float2(v[0], v[1]);
+      stv<NT>(reinterpret_cast<f32x2_t*>(p + off), f32x2_t{v[0], v[1]});
     } else {
 #pragma unroll
-      for (int k = 0; k < CPT; ++k) p[off + k] = v[k];
+      for (int k = 0; k < CPT; ++k) stv<NT>(p + off + k, v[k]);
     }
   } else {
 #pragma unroll
@@ -83,19 +99,19 @@ __device__ __forceinline__ void store_row(float* __restrict__ p, uint32_t off, i
 }
 
 // bf16 rows are kept as packed pairs (CPT/2 words) and widened on use.
-template <int CPT, bool FULL>
+template <int CPT, bool FULL, bool NT = false>
 __device__ __forceinline__ void load_row_bf16(const uint16_t* __restrict__ p, uint32_t off,
                                               int nvalid, uint32_t (&w)[CPT / 2]) {
   static_assert(CPT % 2 == 0, "bf16 rows hold an even number of channels");
   if (FULL) {
     if constexpr (CPT == 2) {
-      w[0] = *reinterpret_cast<const uint32_t*>(p + off);
+      w[0] = ldv<NT>(reinterpret_cast<const uint32_t*>(p + off));
     } else if constexpr (CPT == 4) {
-      const uint2 x = *reinterpret_cast<const uint2*>(p + off);
+      const u32x2_t x = ldv<NT>(reinterpret_cast<const u32x2_t*>(p + off));
       w[0] = x.x; w[1] = x.y;
     } else {
       static_assert(CPT == 8, "bf16 rows of 2, 4 or 8 channels");
-      const uint4 x = *reinterpret_cast<const uint4*>(p + off);
+      const u32x4_t x = ldv<NT>(reinterpret_cast<const u32x4_t*>(p + off));
       w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
     }
   } else {
@@ -116,7 +132,6 @@ __device__ __forceinline__ float bf16_get(const uint32_t (&w)[CPT / 2], int k) {
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // Round pairs of fp32 to bf16 (nearest-even, gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -125,7 +140,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, b);
 }
 
-template <int CPT, bool FULL>
+template <int CPT, bool FULL, bool NT = false>
 __device__ __forceinline__ void store_row_bf16(uint16_t* __restrict__ p, uint32_t off, int nvalid,
                                                const float (&v)[CPT]) {
   uint32_t w[CPT / 2];
@@ -133,11 +148,11 @@ __device__ __forceinline__ void store_row_bf16(uint16_t* __restrict__ p, uint32_
   for (int k = 0; k < CPT / 2; ++k) w[k] = pack_bf16x2(v[2 * k], v[2 * k + 1]);
   if (FULL) {
     if constexpr (CPT == 2) {
-      *reinterpret_cast<uint32_t*>(p + off) = w[0];
+      stv<NT>(reinterpret_cast<uint32_t*>(p + off), w[0]);
     } else if constexpr (CPT == 4) {
-      *reinterpret_cast<uint2*>(p + off) = make_uint2(w[0], w[1]);
+      stv<NT>(reinterpret_cast<u32x2_t*>(p + off), u32x2_t{w[0], w[1]});
     } else {
-      *reinterpret_cast<uint4*>(p + off) = make_uint4(w[0], w[1], w[2], w[3]);
+      stv<NT>(reinterpret_cast<u32x4_t*>(p + off), u32x4_t{w[0], w[1], w[2], w[3]});
     }
   } else {
 #pragma unroll
@@ -265,7 +280,7 @@ __device__ __forceinline__ ColPos col_pos(int tb, int cb, int64_t C) {
 // ---------------------------------------------------------------------------
 // forward scan, [T, B, D]
 // ---------------------------------------------------------------------------
-template <int NW, int L, int CPT, bool FULL>
+template <int NW, int L, int CPT, bool FULL, bool NT>
 __device__ __forceinline__ void scan_fwd_tile(const float* __restrict__ a,
                                               const float* __restrict__ b,
                                               const float* __restrict__ h0, float* __restrict__ h,
@@ -279,8 +294,8 @@ __device__ __forceinline__ void scan_fwd_tile(const float* __restrict__ a,
 #pragma unroll
   for (int i = 0; i < L; ++i) {
     const int nv = (FULL || q.row0 + i < T) ? q.nvc : 0;
-    load_row<CPT, FULL>(ap, q.off, nv, 1.0f, av[i]);
-    load_row<CPT, FULL>(bp, q.off, nv, 0.0f, bv[i]);
+    load_row<CPT, FULL, NT>(ap, q.off, nv, 1.0f, av[i]);
+    load_row<CPT, FULL, NT>(bp, q.off, nv, 0.0f, bv[i]);
     ap += C;
     bp += C;
   }
@@ -308,12 +323,12 @@ __device__ __forceinline__ void scan_fwd_tile(const float* __restrict__ a,
       bv[i][k] = x[k];
     }
     const int nv = (FULL || q.row0 + i < T) ? q.nvc : 0;
-    store_row<CPT, FULL>(hp, q.off, nv, bv[i]);
+    store_row<CPT, FULL, NT>(hp, q.off, nv, bv[i]);
     hp += C;
   }
 }
 
-template <int NW, int L, int CPT>
+template <int NW, int L, int CPT, bool NT>
 __global__ __launch_bounds__(NW* kWave) void k_scan_fwd_tbd(
     const float* __restrict__ a, const float* __restrict__ b, const float* __restrict__ h0,
     float* __restrict__ h, int64_t T, int64_t C, int ncb, int ntb, int vec,
@@ -326,9 +341,9 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_fwd_tbd(
   uint64_t* st = status + (int64_t)cb * ntb * CW;
   const bool full = vec && ((int64_t)(tb + 1) * TW <= T) && ((int64_t)(cb + 1) * CW <= C);
   if (full)
-    scan_fwd_tile<NW, L, CPT, true>(a, b, h0, h, T, C, tb, cb, multi, st, s);
+    scan_fwd_tile<NW, L, CPT, true, NT>(a, b, h0, h, T, C, tb, cb, multi, st, s);
   else
-    scan_fwd_tile<NW, L, CPT, false>(a, b, h0, h, T, C, tb, cb, multi, st, s);
+    scan_fwd_tile<NW, L, CPT, false, NT>(a, b, h0, h, T, C, tb, cb, multi, st, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -337,7 +352,7 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_fwd_tbd(
 // grad_b may alias grad_h (each element of g is read by the thread that
 // writes the same element of grad_b, before it writes).
 // ---------------------------------------------------------------------------
-template <int NW, int L, int CPT, bool FULL>
+template <int NW, int L, int CPT, bool FULL, bool NT>
 __device__ __forceinline__ void scan_bwd_tile(const float* __restrict__ a,
                                               const float* __restrict__ h,
                                               const float* __restrict__ h0, const float* g,
@@ -362,9 +377,9 @@ __device__ __forceinline__ void scan_bwd_tile(const float* __restrict__ a,
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       const int nv = (FULL || row0 + i < T) ? nvc : 0;
-      load_row<CPT, FULL>(ap, off, nv, 1.0f, av[i]);
-      load_row<CPT, FULL>(hpp, off, nv, 0.0f, hv[i]);
-      load_row<CPT, FULL>(gp, off, nv, 0.0f, gv[i]);
+      load_row<CPT, FULL, NT>(ap, off, nv, 1.0f, av[i]);
+      load_row<CPT, FULL, NT>(hpp, off, nv, 0.0f, hv[i]);
+      load_row<CPT, FULL, NT>(gp, off, nv, 0.0f, gv[i]);
       ap += C;
       hpp += C;
       gp += C;
@@ -420,8 +435,8 @@ __device__ __forceinline__ void scan_bwd_tile(const float* __restrict__ a,
       gv[i][k] = x[k];
     }
     const int nv = (FULL || row0 + i < T) ? nvc : 0;
-    store_row<CPT, FULL>(dap, off, nv, dav);
-    store_row<CPT, FULL>(dbp, off, nv, gv[i]);
+    store_row<CPT, FULL, NT>(dap, off, nv, dav);
+    store_row<CPT, FULL, NT>(dbp, off, nv, gv[i]);
     dap -= C;
     dbp -= C;
   }
@@ -432,7 +447,7 @@ __device__ __forceinline__ void scan_bwd_tile(const float* __restrict__ a,
   }
 }
 
-template <int NW, int L, int CPT>
+template <int NW, int L, int CPT, bool NT>
 __global__ __launch_bounds__(NW* kWave) void k_scan_bwd_tbd(
     const float* __restrict__ a, const float* __restrict__ h, const float* __restrict__ h0,
     const float* g, float* __restrict__ da, float* db, float* __restrict__ dh0, int64_t T,
@@ -447,9 +462,11 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_bwd_tbd(
   const int ptb = ntb - 1 - tb;
   const bool full = vec && ((int64_t)(ptb + 1) * TW <= T) && ((int64_t)(cb + 1) * CW <= C);
   if (full)
-    scan_bwd_tile<NW, L, CPT, true>(a, h, h0, g, da, db, dh0, T, C, tb, ntb, cb, multi, st, s);
+    scan_bwd_tile<NW, L, CPT, true, NT>(a, h, h0, g, da, db, dh0, T, C, tb, ntb, cb, multi, st,
+                                        s);
   else
-    scan_bwd_tile<NW, L, CPT, false>(a, h, h0, g, da, db, dh0, T, C, tb, ntb, cb, multi, st, s);
+    scan_bwd_tile<NW, L, CPT, false, NT>(a, h, h0, g, da, db, dh0, T, C, tb, ntb, cb, multi, st,
+                                         s);
 }
 
 // ---------------------------------------------------------------------------
@@ -468,34 +485,34 @@ struct SruRow;
 template <int CPT>
 struct SruRow<uint16_t, CPT> {
   uint32_t w[CPT / 2];
-  template <bool FULL>
+  template <bool FULL, bool NT>
   __device__ __forceinline__ void load(const uint16_t* p, uint32_t off, int nv) {
-    load_row_bf16<CPT, FULL>(p, off, nv, w);
+    load_row_bf16<CPT, FULL, NT>(p, off, nv, w);
   }
   __device__ __forceinline__ float get(int k) const { return bf16_get<CPT>(w, k); }
-  template <bool FULL>
+  template <bool FULL, bool NT>
   static __device__ __forceinline__ void store(uint16_t* p, uint32_t off, int nv,
                                                const float (&x)[CPT]) {
-    store_row_bf16<CPT, FULL>(p, off, nv, x);
+    store_row_bf16<CPT, FULL, NT>(p, off, nv, x);
   }
 };
 
 template <int CPT>
 struct SruRow<float, CPT> {
   float v[CPT];
-  template <bool FULL>
+  template <bool FULL, bool NT>
   __device__ __forceinline__ void load(const float* p, uint32_t off, int nv) {
-    load_row<CPT, FULL>(p, off, nv, 0.0f, v);
+    load_row<CPT, FULL, NT>(p, off, nv, 0.0f, v);
   }
   __device__ __forceinline__ float get(int k) const { return v[k]; }
-  template <bool FULL>
+  template <bool FULL, bool NT>
   static __device__ __forceinline__ void store(float* p, uint32_t off, int nv,
                                                const float (&x)[CPT]) {
-    store_row<CPT, FULL>(p, off, nv, x);
+    store_row<CPT, FULL, NT>(p, off, nv, x);
   }
 };
 
-template <typename IO, int NW, int L, int CPT, bool FULL>
+template <typename IO, int NW, int L, int CPT, bool FULL, bool NT>
 __device__ __forceinline__ void sru_tile(const IO* __restrict__ zf, const IO* __restrict__ zr,
                                          const IO* __restrict__ zx,
                                          const float* __restrict__ bias_f,
@@ -528,9 +545,9 @@ __device__ __forceinline__ void sru_tile(const IO* __restrict__ zf, const IO* __
     for (int i = 0; i < L; ++i) {
       const int nv = (FULL || q.row0 + i < T) ? q.nvc : 0;
       SruRow<IO, CPT> fr;
-      fr.template load<FULL>(fp, q.off, nv);
-      rr[i].template load<FULL>(rp, q.off, nv);
-      xr[i].template load<FULL>(xp, q.off, nv);
+      fr.template load<FULL, NT>(fp, q.off, nv);
+      rr[i].template load<FULL, NT>(rp, q.off, nv);
+      xr[i].template load<FULL, NT>(xp, q.off, nv);
       fp += C;
       rp += C;
       xp += C;
@@ -580,7 +597,7 @@ __device__ __forceinline__ void sru_tile(const IO* __restrict__ zf, const IO* __
       out[k] = __builtin_fmaf(r, th - zxv, zxv);  // r tanh(c) + (1 - r) zx
     }
     const int nv = (FULL || q.row0 + i < T) ? q.nvc : 0;
-    SruRow<IO, CPT>::template store<FULL>(hp, q.off, nv, out);
+    SruRow<IO, CPT>::template store<FULL, NT>(hp, q.off, nv, out);
     hp += C;
     if (c_last && q.row0 + i == T - 1) {
 #pragma unroll
@@ -590,7 +607,7 @@ __device__ __forceinline__ void sru_tile(const IO* __restrict__ zf, const IO* __
   }
 }
 
-template <typename IO, int NW, int L, int CPT>
+template <typename IO, int NW, int L, int CPT, bool NT>
 __global__ __launch_bounds__(NW* kWave) void k_sru_fwd(
     const IO* __restrict__ zf, const IO* __restrict__ zr, const IO* __restrict__ zx,
     const float* __restrict__ bias_f, const float* __restrict__ bias_r,
@@ -605,10 +622,10 @@ __global__ __launch_bounds__(NW* kWave) void k_sru_fwd(
   uint64_t* st = status + (int64_t)cb * ntb * CW;
   const bool full = vec && ((int64_t)(tb + 1) * TW <= T) && ((int64_t)(cb + 1) * CW <= C);
   if (full)
-    sru_tile<IO, NW, L, CPT, true>(zf, zr, zx, bias_f, bias_r, c0p, h, c_last, T, C, D, tb, cb,
+    sru_tile<IO, NW, L, CPT, true, NT>(zf, zr, zx, bias_f, bias_r, c0p, h, c_last, T, C, D, tb, cb,
                                    multi, st, s);
   else
-    sru_tile<IO, NW, L, CPT, false>(zf, zr, zx, bias_f, bias_r, c0p, h, c_last, T, C, D, tb, cb,
+    sru_tile<IO, NW, L, CPT, false, NT>(zf, zr, zx, bias_f, bias_r, c0p, h, c_last, T, C, D, tb, cb,
                                     multi, st, s);
 }
 
@@ -637,20 +654,35 @@ constexpr int kSruNW = 4, kSruL = 16, kSruCPT = 2;          // bf16 I/O
 constexpr int kSruF32NW = 8, kSruF32L = 8, kSruF32CPT = 2;  // fp32 I/O
 }  // namespace
 
-ColPlan plan_scan_fwd_tbd(int64_t C, int64_t T) { return plan_cols(C, T, kFwdNW, kFwdL, kFwdCPT); }
-ColPlan plan_scan_bwd_tbd(int64_t C, int64_t T) { return plan_cols(C, T, kBwdNW, kBwdL, kBwdCPT); }
+ColPlan plan_scan_fwd_tbd(int64_t C, int64_t T) {
+  ColPlan p = plan_cols(C, T, kFwdNW, kFwdL, kFwdCPT);
+  p.stream = 3 * C * T * 4 >= kStreamFootprint;  // a, b, h
+  return p;
+}
+ColPlan plan_scan_bwd_tbd(int64_t C, int64_t T) {
+  ColPlan p = plan_cols(C, T, kBwdNW, kBwdL, kBwdCPT);
+  p.stream = 5 * C * T * 4 >= kStreamFootprint;  // a, h, g, grad_a, grad_b
+  return p;
+}
 ColPlan plan_sru(int64_t C, int64_t T, int io_dtype) {
-  return io_dtype == 1 ? plan_cols(C, T, kSruNW, kSruL, kSruCPT)
-                       : plan_cols(C, T, kSruF32NW, kSruF32L, kSruF32CPT);
+  ColPlan p = io_dtype == 1 ? plan_cols(C, T, kSruNW, kSruL, kSruCPT)
+                            : plan_cols(C, T, kSruF32NW, kSruF32L, kSruF32CPT);
+  p.stream = 4 * C * T * (io_dtype == 1 ? 2 : 4) >= kStreamFootprint;  // z_f, z_r, z_x, h
+  return p;
 }
 
 hipError_t launch_scan_fwd_tbd(const float* a, const float* b, const float* h0, float* h,
                                int64_t C, int64_t T, const ColPlan& p, int vec, uint64_t* status,
                                unsigned* tickets, hipStream_t stream) {
   const uint64_t grid = (uint64_t)p.ncb * (uint64_t)p.ntb;
-  hipLaunchKernelGGL((k_scan_fwd_tbd<kFwdNW, kFwdL, kFwdCPT>), dim3((unsigned)grid),
-                     dim3(kFwdNW * kWave), 0, stream, a, b, h0, h, T, C, (int)p.ncb, (int)p.ntb,
-                     vec, status, tickets);
+  if (p.stream)
+    hipLaunchKernelGGL((k_scan_fwd_tbd<kFwdNW, kFwdL, kFwdCPT, true>), dim3((unsigned)grid),
+                       dim3(kFwdNW * kWave), 0, stream, a, b, h0, h, T, C, (int)p.ncb, (int)p.ntb,
+                       vec, status, tickets);
+  else
+    hipLaunchKernelGGL((k_scan_fwd_tbd<kFwdNW, kFwdL, kFwdCPT, false>), dim3((unsigned)grid),
+                       dim3(kFwdNW * kWave), 0, stream, a, b, h0, h, T, C, (int)p.ncb, (int)p.ntb,
+                       vec, status, tickets);
   return hipGetLastError();
 }
 
@@ -659,9 +691,14 @@ hipError_t launch_scan_bwd_tbd(const float* a, const float* h, const float* h0, 
                                const ColPlan& p, int vec, uint64_t* status, unsigned* tickets,
                                hipStream_t stream) {
   const uint64_t grid = (uint64_t)p.ncb * (uint64_t)p.ntb;
-  hipLaunchKernelGGL((k_scan_bwd_tbd<kBwdNW, kBwdL, kBwdCPT>), dim3((unsigned)grid),
-                     dim3(kBwdNW * kWave), 0, stream, a, h, h0, g, da, db, dh0, T, C, (int)p.ncb,
-                     (int)p.ntb, vec, status, tickets);
+  if (p.stream)
+    hipLaunchKernelGGL((k_scan_bwd_tbd<kBwdNW, kBwdL, kBwdCPT, true>), dim3((unsigned)grid),
+                       dim3(kBwdNW * kWave), 0, stream, a, h, h0, g, da, db, dh0, T, C,
+                       (int)p.ncb, (int)p.ntb, vec, status, tickets);
+  else
+    hipLaunchKernelGGL((k_scan_bwd_tbd<kBwdNW, kBwdL, kBwdCPT, false>), dim3((unsigned)grid),
+                       dim3(kBwdNW * kWave), 0, stream, a, h, h0, g, da, db, dh0, T, C,
+                       (int)p.ncb, (int)p.ntb, vec, status, tickets);
   return hipGetLastError();
 }
 
@@ -671,17 +708,18 @@ hipError_t launch_sru_fwd(const void* zf, const void* zr, const void* zx, const 
                           uint64_t* status, unsigned* tickets, hipStream_t stream) {
   const uint64_t grid = (uint64_t)p.ncb * (uint64_t)p.ntb;
   const int64_t C = B * D;
+#define LRS_SRU(IO, NW_, L_, CPT_, NTF)                                                          \
+  hipLaunchKernelGGL((k_sru_fwd<IO, NW_, L_, CPT_, NTF>), dim3((unsigned)grid), dim3(NW_ * kWave), \
+                     0, stream, (const IO*)zf, (const IO*)zr, (const IO*)zx, bias_f, bias_r, c0,  \
+                     (IO*)h, c_last, T, C, D, (int)p.ncb, (int)p.ntb, vec, status, tickets)
   if (io_dtype == 1) {
-    hipLaunchKernelGGL((k_sru_fwd<uint16_t, kSruNW, kSruL, kSruCPT>), dim3((unsigned)grid),
-                       dim3(kSruNW * kWave), 0, stream, (const uint16_t*)zf, (const uint16_t*)zr,
-                       (const uint16_t*)zx, bias_f, bias_r, c0, (uint16_t*)h, c_last, T, C, D,
-                       (int)p.ncb, (int)p.ntb, vec, status, tickets);
+    if (p.stream) LRS_SRU(uint16_t, kSruNW, kSruL, kSruCPT, true);
+    else LRS_SRU(uint16_t, kSruNW, kSruL, kSruCPT, false);
   } else {
-    hipLaunchKernelGGL((k_sru_fwd<float, kSruF32NW, kSruF32L, kSruF32CPT>), dim3((unsigned)grid),
-                       dim3(kSruF32NW * kWave), 0, stream, (const float*)zf, (const float*)zr,
-                       (const float*)zx, bias_f, bias_r, c0, (float*)h, c_last, T, C, D,
-                       (int)p.ncb, (int)p.ntb, vec, status, tickets);
+    if (p.stream) LRS_SRU(float, kSruF32NW, kSruF32L, kSruF32CPT, true);
+    else LRS_SRU(float, kSruF32NW, kSruF32L, kSruF32CPT, false);
   }
+#undef LRS_SRU
   return hipGetLastError();
 }
 

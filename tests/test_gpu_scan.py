@@ -161,33 +161,38 @@ def test_scan_long_workload():
     assert rel < 1e-3
 
 
-def test_streamed_single_chunk():
-    """Arrays of 256 MiB and more take the nontemporal (streaming) variants:
-    32768 channels of 2048 steps, each one chunk.  Sampled channels are
-    compared with the oracle; the adjoint identity is checked on all."""
-    B, D, T = 32, 1024, 2048
+@pytest.mark.parametrize("layout", ["bdt", "tbd"])
+def test_streamed(layout):
+    """Calls whose arrays total 512 MiB or more take the nontemporal (streaming)
+    variants: 16384 channels of 4096 steps, 256 MiB per array.  Sampled
+    channels are compared with the oracle; the adjoint identity is checked on
+    all of them."""
+    B, D, T = 16, 1024, 4096
     w = I.scaled(I.WORKLOADS["scan_fwd_bwd"], B=B, D=D, T=T, seed=8202)
-    log(f"streamed single-chunk B={B} D={D} T={T}: generating inputs")
+    log(f"streamed {layout} B={B} D={D} T={T}: generating inputs")
     x = I.scan_inputs(w)
-    a = to_dev(x["a"], B, D, T, "bdt")
-    b = to_dev(x["b"], B, D, T, "bdt")
-    g = to_dev(x["g"], B, D, T, "bdt")
+    a = to_dev(x["a"], B, D, T, layout)
+    b = to_dev(x["b"], B, D, T, layout)
+    g = to_dev(x["g"], B, D, T, layout)
     h0 = torch.from_numpy(x["h0"].reshape(B, D)).to(DEV)
-    h = lrs.scan_fwd(a, b, h0)
-    da, db, dh0 = lrs.scan_bwd(a, h, g, h0)
+    h = lrs.scan_fwd(a, b, h0, layout=layout)
+    da, db, dh0 = lrs.scan_bwd(a, h, g, h0, layout=layout)
     torch.cuda.synchronize()
-    sample = [0, 1, 77, 4095, 4096, 20000, 32766, 32767]
+    C = B * D
+
+    def rows(t):  # [C, T] view of a device array in either layout
+        return t.view(C, T) if layout == "bdt" else t.view(T, C).t()
+    sample = [0, 1, 77, 4095, 4096, 9000, C - 2, C - 1]
     sx = {k: x[k][sample] for k in ("a", "b", "g", "h0")}
     ref = oracle_scan(sx)
-    got = {"h": h.view(-1, T)[sample].cpu().numpy(), "da": da.view(-1, T)[sample].cpu().numpy(),
-           "db": db.view(-1, T)[sample].cpu().numpy(),
-           "dh0": dh0.view(-1)[sample].cpu().numpy()}
-    compare(got, ref, tag="streamed")
+    got = {"h": rows(h)[sample].cpu().numpy(), "da": rows(da)[sample].cpu().numpy(),
+           "db": rows(db)[sample].cpu().numpy(), "dh0": dh0.view(-1)[sample].cpu().numpy()}
+    compare(got, ref, tag=f"streamed/{layout}")
     # <g, h> = <lam, b> + dh0 * h0 per channel
-    lhs = (g.double() * h.double()).sum(-1).view(-1)
-    rhs = (db.double() * b.double()).sum(-1).view(-1) + (dh0.double() * h0.double()).view(-1)
+    lhs = (rows(g).double() * rows(h).double()).sum(-1)
+    rhs = (rows(db).double() * rows(b).double()).sum(-1) + (dh0.double() * h0.double()).view(-1)
     rel = ((lhs - rhs).abs() / (1 + lhs.abs())).max().item()
-    log(f"streamed adjoint identity rel {rel:.2e}")
+    log(f"streamed {layout} adjoint identity rel {rel:.2e}")
     assert rel < 1e-3
 
 
