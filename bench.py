@@ -214,31 +214,6 @@ def parse():
     return p.parse_args()
 
 
-class KernelTimer:
-    """HIP events (device-scope release) around each call, on the stream the
-    call launches on."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = {}
-        self.enabled = True
-
-    def run(self, name, fn):
-        if not self.enabled:
-            return fn()
-        stream = self.torch.cuda.current_stream().cuda_stream
-        s, e = DeviceEvent(), DeviceEvent()
-        s.record(stream)
-        out = fn()
-        e.record(stream)
-        self.pairs.setdefault(name, []).append((s, e))
-        return out
-
-    def avg_ms(self, name):
-        ps = self.pairs.get(name, [])
-        return sum(s.ms_until(e) for s, e in ps) / max(1, len(ps))
-
-
 class DeviceEvent:
     """A HIP timing event recorded with a device-scope release
     (hipEventReleaseToDevice) instead of the default system-scope one, whose
@@ -337,7 +312,6 @@ def main():
     w = I.WORKLOADS[args.workload]
     B, D, T = w.B, w.D, w.T
     N = w.N
-    timer = KernelTimer(torch)
     extra = {}
 
     def to_dev(x_ct, layout):
@@ -397,12 +371,18 @@ def main():
         hd = torch.empty_like(u)
         ws = torch.empty(lrs.load().lrs_deer_workspace_bytes(B, D, T, 5), dtype=torch.uint8,
                          device=dev)
-        info_box = {}
+
+        # the timed solve is the asynchronous form (no host outputs): the
+        # iteration record is read once afterwards with deer_stats
+        def solve_async():
+            lrs.deer_solve(wd, u, h0, None, eps=1e-5, k_max=5, out=hd, workspace=ws, sync=False)
+
+        def solve_sync():
+            return lrs.deer_solve(wd, u, h0, None, eps=1e-5, k_max=5, out=hd, workspace=ws)
+        calls = {"deer_solve": solve_async}
 
         def step():
-            _, info_box["info"] = timer.run("deer_solve", lambda: lrs.deer_solve(
-                wd, u, h0, None, eps=1e-5, k_max=5, out=hd, workspace=ws))
-        calls = None  # the solve reads its stop test back to the host: timed per call
+            solve_async()
         kernels = ["deer_solve"]
         dtype = "f32"
         config = {"workload": w.name, "B": B, "D": D, "T": T, "layout": "bdt", "eps": 1e-5,
@@ -425,13 +405,11 @@ def main():
         return t0.elapsed_time(t1) / steps, time.perf_counter() - w0
 
     # (1) eager steps, HIP events only at the two ends of the timed region
-    timer.enabled = False
     ms_per_step, wall = timed(step, args.steps)
     extra["timing"] = "eager launches, events at both ends"
     # (2) the same step captured once as a HIP graph and replayed (reported
-    #     beside the eager figure).  DEER reads its stop test back to the host
-    #     and is never captured.
-    if w.kind != "deer" and args.graph:
+    #     beside the eager figure); DEER is captured in its asynchronous form
+    if args.graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             step()
@@ -440,17 +418,13 @@ def main():
         extra["ms_per_step_graph"] = round(timed(graph.replay, args.steps)[0], 5)
     # (3) per-kernel launch durations for the roofline: `steps` more steps
     #     with a HIP event after every entry point, on its launch stream
-    #     (DEER: events around every solve)
-    if calls is not None:
-        per_kernel = step_kernel_ms(torch, calls, args.steps)
-        extra["per_kernel_timing"] = ("HIP event (device-scope release) after every call of "
-                                      "queued steps")
-    else:
-        timer.enabled = True
-        timer.pairs.clear()
-        timed(step, args.steps)
-        per_kernel = {k: timer.avg_ms(k) for k in kernels}
-        extra["per_kernel_timing"] = "HIP events around every solve"
+    per_kernel = step_kernel_ms(torch, calls, args.steps)
+    extra["per_kernel_timing"] = ("HIP event (device-scope release) after every call of "
+                                  "queued steps")
+    if w.kind == "deer":
+        # the synchronous form reads the record back after every solve
+        extra["ms_per_step_sync"] = round(timed(solve_sync, args.steps)[0], 5)
+        info = lrs.deer_stats(ws, 5)
     value = N / (ms_per_step / 1e3)
 
     if w.kind == "scan":
@@ -462,11 +436,11 @@ def main():
         bytes_step = BYTES_PER_ELEM["sru_fwd_bf16"] * N
         dom, dom_bytes, dom_ms = "sru_fwd_bf16", bytes_step, per_kernel["sru_fwd_bf16"]
     else:
-        iters = info_box["info"]["iters"]
+        iters = info["iters"]
         bytes_step = (BYTES_PER_ELEM["deer_iter_first"] + (iters - 1) * BYTES_PER_ELEM["deer_iter"]) * N
         dom, dom_bytes, dom_ms = "deer_solve", bytes_step, per_kernel["deer_solve"]
         extra["deer_iters"] = iters
-        extra["deer_deltas"] = info_box["info"]["deltas"]
+        extra["deer_deltas"] = info["deltas"]
     achieved = dom_bytes / (dom_ms / 1e3) / 1e9
     traffic = measured_traffic(w.name if args.layout == "bdt" else f"{w.name}_{args.layout}", dom)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),

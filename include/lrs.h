@@ -154,14 +154,29 @@ LRS_API size_t lrs_deer_workspace_bytes(int64_t B, int64_t D, int64_t T, int k_m
  * deltas_out (host, may be NULL): k_max floats; entries 0..iters-1 receive
  *   delta_1..delta_iters, the rest 0.
  * converged_out (host, may be NULL): 1 if the last delta < eps, else 0.
- * Host-synchronous: one device-to-host read of the k_max norms after all
- * iterations are enqueued (an iteration whose predecessor met the stop rule
- * exits immediately on the device).  Returns LRS_ERR_NONFINITE, with all
- * outputs written, when the last delta is NaN or infinite. */
+ * An iteration whose predecessor met the stop rule exits immediately on the
+ * device, so all k_max iterations are enqueued without host involvement; a
+ * final device step leaves the last iterate in h and records the iteration
+ * count, convergence flag and norms in the workspace.
+ * If any of iters_out, deltas_out, converged_out is given, the call then
+ * reads that record back (one device-to-host copy; waits for the stream) and
+ * returns LRS_ERR_NONFINITE, with all outputs written, when the last delta is
+ * NaN or infinite.  If all three are NULL the call is asynchronous: it returns
+ * LRS_OK once everything is enqueued (and may be captured in a HIP graph);
+ * lrs_deer_stats reads the record later. */
 LRS_API int lrs_deer_solve(const float *w, const float *u, const float *h0, const float *h_init, float *h,
                    int64_t B, int64_t D, int64_t T, float eps, int k_max, int *iters_out,
                    float *deltas_out, int *converged_out, void *workspace,
                    size_t workspace_bytes, void *stream);
+
+/* Record of the most recent lrs_deer_solve that used this workspace with this
+ * k_max (same meaning of iters_out, deltas_out, converged_out as there; each
+ * may be NULL).  Waits for `stream`, on which that solve must have been
+ * enqueued.  Returns LRS_ERR_NONFINITE when that solve's last delta was NaN or
+ * infinite, LRS_ERR_WORKSPACE for a workspace too small for k_max, and
+ * LRS_ERR_HIP if the workspace holds no finished solve record. */
+LRS_API int lrs_deer_stats(const void *workspace, size_t workspace_bytes, int k_max,
+                   int *iters_out, float *deltas_out, int *converged_out, void *stream);
 
 #ifdef __cplusplus
 }

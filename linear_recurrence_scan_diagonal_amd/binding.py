@@ -24,7 +24,7 @@ DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 EXPORTS = ("lrs_status_string", "lrs_version", "lrs_scan_workspace_bytes", "lrs_scan_fwd",
            "lrs_scan_bwd", "lrs_sru_workspace_bytes", "lrs_sru_fwd", "lrs_deer_workspace_bytes",
-           "lrs_deer_solve")
+           "lrs_deer_solve", "lrs_deer_stats")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -71,6 +71,9 @@ def load():
                                    ctypes.POINTER(_int), ctypes.POINTER(ctypes.c_float),
                                    ctypes.POINTER(_int), _vp, _sz, _vp]
     lib.lrs_deer_solve.restype = _int
+    lib.lrs_deer_stats.argtypes = [_vp, _sz, _int, ctypes.POINTER(_int),
+                                   ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_int), _vp]
+    lib.lrs_deer_stats.restype = _int
     _lib = lib
     return lib
 
@@ -193,11 +196,13 @@ def sru_fwd(z_f, z_r, z_x, bias_f, bias_r, c0=None, want_c_last: bool = False, o
 
 
 def deer_solve(w, u, h0=None, h_init=None, eps: float = 1e-5, k_max: int = 5, out=None,
-               workspace=None):
+               workspace=None, sync: bool = True):
     """DEER Newton solve of h_t = tanh(w h_{t-1} + u_t); u: [B,D,T] fp32, w: [D].
 
-    Returns (h, info) with info = {"iters", "deltas", "converged", "status"}.
-    A non-finite final update is reported in info["status"] rather than raised."""
+    sync=True: returns (h, info) with info = {"iters", "deltas", "converged",
+    "status"}; a non-finite final update is reported in info["status"] rather
+    than raised.  sync=False: enqueues the solve without waiting and returns
+    (h, workspace); deer_stats(workspace, k_max) reads info later."""
     lib = load()
     B, D, T = _dims(u, "bdt")
     _check_dev("u", u, torch.float32, u.shape)
@@ -208,6 +213,13 @@ def deer_solve(w, u, h0=None, h_init=None, eps: float = 1e-5, k_max: int = 5, ou
     _check_dev("out", h, torch.float32, u.shape)
     nbytes = lib.lrs_deer_workspace_bytes(B, D, T, k_max)
     ws = _workspace(nbytes, u.device, workspace)
+    if not sync:
+        rc = lib.lrs_deer_solve(_ptr(w), _ptr(u), _ptr(h0), _ptr(h_init), _ptr(h), B, D, T,
+                                float(eps), int(k_max), None, None, None, _ptr(ws), nbytes,
+                                _stream(u.device))
+        if rc != LRS_OK:
+            raise LrsError(rc, "lrs_deer_solve")
+        return h, ws
     iters = ctypes.c_int(0)
     conv = ctypes.c_int(0)
     deltas = (ctypes.c_float * max(k_max, 1))()
@@ -219,3 +231,21 @@ def deer_solve(w, u, h0=None, h_init=None, eps: float = 1e-5, k_max: int = 5, ou
     info = {"iters": iters.value, "deltas": [float(deltas[i]) for i in range(iters.value)],
             "converged": bool(conv.value), "status": int(rc)}
     return h, info
+
+
+def deer_stats(workspace, k_max: int = 5):
+    """Record of the last solve run with `workspace` (see deer_solve): waits for
+    the current stream and returns {"iters", "deltas", "converged", "status"}."""
+    lib = load()
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
+        raise TypeError("workspace must be the device tensor a solve used")
+    iters = ctypes.c_int(0)
+    conv = ctypes.c_int(0)
+    deltas = (ctypes.c_float * max(k_max, 1))()
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = lib.lrs_deer_stats(_ptr(workspace), nbytes, int(k_max), ctypes.byref(iters), deltas,
+                            ctypes.byref(conv), _stream(workspace.device))
+    if rc not in (LRS_OK, LRS_ERR_NONFINITE):
+        raise LrsError(rc, "lrs_deer_stats")
+    return {"iters": iters.value, "deltas": [float(deltas[i]) for i in range(iters.value)],
+            "converged": bool(conv.value), "status": int(rc)}

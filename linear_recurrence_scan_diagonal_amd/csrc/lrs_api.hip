@@ -322,13 +322,54 @@ int lrs_sru_fwd(const void* z_f, const void* z_r, const void* z_x, const float* 
 
 static lrs::RowPlan deer_plan(int64_t C, int64_t T) { return lrs::plan_deer_rows(C, T); }
 
+// The workspace starts with the norm slot sets, the solve record and the
+// per-iteration norms (cleared together at the start of a solve).
+static size_t deer_record_bytes(int k_max) {
+  return align_up(((size_t)lrs::kDeltaSetWords + lrs::kDeerRecordWords + (size_t)k_max) * 4);
+}
+
+struct DeerRecord {
+  uint32_t* delta_bits;  // slot sets
+  int* rec;              // {iterations, converged, non-finite, unused}
+  uint32_t* delta_out;   // k_max norms
+};
+
+static DeerRecord carve_deer_record(Carve& cv, int k_max) {
+  DeerRecord r;
+  r.delta_bits = cv.take<uint32_t>(lrs::kDeltaSetWords + lrs::kDeerRecordWords + k_max);
+  r.rec = reinterpret_cast<int*>(r.delta_bits + lrs::kDeltaSetWords);
+  r.delta_out = r.delta_bits + lrs::kDeltaSetWords + lrs::kDeerRecordWords;
+  return r;
+}
+
+// Read a finished solve's record and norms to the host (waits for the stream).
+static int read_deer_record(const DeerRecord& r, int k_max, int* iters_out, float* deltas_out,
+                            int* converged_out, hipStream_t s) {
+  std::vector<uint32_t> buf((size_t)lrs::kDeerRecordWords + (size_t)k_max);
+  if (hipMemcpyAsync(buf.data(), r.rec, sizeof(uint32_t) * buf.size(), hipMemcpyDeviceToHost,
+                     s) != hipSuccess)
+    return LRS_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return LRS_ERR_HIP;
+  const int iters = (int)buf[0];
+  if (iters < 1 || iters > k_max) return LRS_ERR_HIP;  // no finished solve in this workspace
+  if (iters_out) *iters_out = iters;
+  if (converged_out) *converged_out = (int)buf[1];
+  if (deltas_out) {
+    for (int i = 0; i < k_max; ++i) {
+      float d = 0.0f;
+      if (i < iters) memcpy(&d, &buf[(size_t)lrs::kDeerRecordWords + i], 4);
+      deltas_out[i] = d;
+    }
+  }
+  return buf[2] ? LRS_ERR_NONFINITE : LRS_OK;
+}
+
 size_t lrs_deer_workspace_bytes(int64_t B, int64_t D, int64_t T, int k_max) {
   int64_t C, N;
   if (!shape_ok(B, D, T, &C, &N) || k_max < 1) return 0;
   if (N == 0) return 0;
   const lrs::RowPlan p = deer_plan(C, T);
-  size_t bytes = kAlign + align_up(((size_t)lrs::kDeltaSetWords + (size_t)k_max) * 4) +
-                 align_up((size_t)N * 4);
+  size_t bytes = kAlign + deer_record_bytes(k_max) + align_up((size_t)N * 4);
   if (p.nchunk > 1) bytes += align_up((size_t)(C * p.nchunk) * 8) + align_up((size_t)C * 4);
   return bytes;
 }
@@ -360,9 +401,9 @@ int lrs_deer_solve(const float* w, const float* u, const float* h0, const float*
   hipStream_t s = (hipStream_t)stream;
 
   Carve cv(align_ptr(workspace));
-  // norm slot sets followed by the per-iteration norms, cleared together
-  uint32_t* delta_bits = cv.take<uint32_t>(lrs::kDeltaSetWords + k_max);
-  uint32_t* delta_out = delta_bits + lrs::kDeltaSetWords;
+  const DeerRecord r = carve_deer_record(cv, k_max);
+  uint32_t* delta_bits = r.delta_bits;
+  uint32_t* delta_out = r.delta_out;
   float* ybuf = cv.take<float>(N);
   uint64_t* status = nullptr;
   unsigned* tickets = nullptr;
@@ -381,7 +422,7 @@ int lrs_deer_solve(const float* w, const float* u, const float* h0, const float*
                   (!h_init || aligned(h_init, 16)) && (T % 4 == 0);
   int rc = hip_status(lrs::launch_reset(status, p.nchunk > 1 ? C * p.nchunk : 0, tickets,
                                         p.nchunk > 1 ? C : 0, delta_bits,
-                                        lrs::kDeltaSetWords + k_max, s));
+                                        lrs::kDeltaSetWords + lrs::kDeerRecordWords + k_max, s));
   if (rc != LRS_OK) return rc;
   for (int i = 0; i < k_max; ++i) {
     if (i > 0 && p.nchunk > 1) {
@@ -393,39 +434,21 @@ int lrs_deer_solve(const float* w, const float* u, const float* h0, const float*
                                           tickets, delta_bits, delta_out, i, eps, s));
     if (rc != LRS_OK) return rc;
   }
-  rc = hip_status(lrs::launch_deer_last_delta(delta_bits, delta_out, k_max - 1, s));
+  rc = hip_status(lrs::launch_deer_finish(delta_bits, delta_out, r.rec, k_max, eps, s));
   if (rc != LRS_OK) return rc;
-  std::vector<uint32_t> dbits((size_t)k_max);
-  if (hipMemcpyAsync(dbits.data(), delta_out, sizeof(uint32_t) * (size_t)k_max,
-                     hipMemcpyDeviceToHost, s) != hipSuccess)
-    return LRS_ERR_HIP;
-  if (hipStreamSynchronize(s) != hipSuccess) return LRS_ERR_HIP;
-  int iters = k_max;
-  float last = 0.0f;
-  for (int i = 0; i < k_max; ++i) {
-    float d;
-    memcpy(&d, &dbits[(size_t)i], 4);
-    last = d;
-    if (d < eps) {
-      iters = i + 1;
-      break;
-    }
-  }
-  float* result = P[(iters - 1) & 1];
-  if (result != h) {
-    if (hipMemcpyAsync(h, result, nb, hipMemcpyDeviceToDevice, s) != hipSuccess)
-      return LRS_ERR_HIP;
-  }
-  if (iters_out) *iters_out = iters;
-  if (converged_out) *converged_out = (last < eps) ? 1 : 0;
-  if (deltas_out) {
-    for (int i = 0; i < k_max; ++i) {
-      float d = 0.0f;
-      if (i < iters) memcpy(&d, &dbits[(size_t)i], 4);
-      deltas_out[i] = d;
-    }
-  }
-  return isfinite(last) ? LRS_OK : LRS_ERR_NONFINITE;
+  rc = hip_status(lrs::launch_deer_select(P[0], P[1], h, N, r.rec, s));
+  if (rc != LRS_OK) return rc;
+  if (!iters_out && !deltas_out && !converged_out) return LRS_OK;  // asynchronous form
+  return read_deer_record(r, k_max, iters_out, deltas_out, converged_out, s);
+}
+
+int lrs_deer_stats(const void* workspace, size_t workspace_bytes, int k_max, int* iters_out,
+                   float* deltas_out, int* converged_out, void* stream) {
+  if (k_max < 1 || k_max > 1000000) return LRS_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < kAlign + deer_record_bytes(k_max)) return LRS_ERR_WORKSPACE;
+  Carve cv(align_ptr(const_cast<void*>(workspace)));
+  const DeerRecord r = carve_deer_record(cv, k_max);
+  return read_deer_record(r, k_max, iters_out, deltas_out, converged_out, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -59,8 +59,12 @@ hipError_t launch_scan_bwd_bdt(const float* a, const float* h, const float* h0, 
 constexpr int kDeltaSlots = 64;
 constexpr int kDeltaStride = 32;
 constexpr int64_t kDeltaSetWords = 3 * kDeltaSlots * kDeltaStride;
-hipError_t launch_deer_last_delta(const uint32_t* delta_bits, uint32_t* delta_out, int last,
-                                  hipStream_t stream);
+// Solve record written by the finish kernel: iterations, converged, non-finite.
+constexpr int kDeerRecordWords = 4;
+hipError_t launch_deer_finish(const uint32_t* delta_bits, uint32_t* delta_out, int* rec,
+                              int k_max, float eps, hipStream_t stream);
+hipError_t launch_deer_select(const float* p0, const float* p1, float* h, int64_t n,
+                              const int* rec, hipStream_t stream);
 hipError_t launch_deer_iter(const float* w, const float* u, const float* y, const float* h0,
                             float* yn, int64_t C, int64_t D, int64_t T, const RowPlan& p, int vec,
                             uint64_t* status, unsigned* tickets, uint32_t* delta_bits,

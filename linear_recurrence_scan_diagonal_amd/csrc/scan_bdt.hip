@@ -472,13 +472,57 @@ __device__ __forceinline__ float deer_prev_delta(uint32_t* __restrict__ delta_bi
   return d;
 }
 
-// Record the norm of the last iteration (one wave).
-__global__ __launch_bounds__(kWave) void k_deer_last_delta(const uint32_t* __restrict__ delta_bits,
-                                                           uint32_t* __restrict__ delta_out,
-                                                           int last) {
-  uint32_t v = delta_bits[(last % 3) * (kDeltaSlots * kDeltaStride) + threadIdx.x * kDeltaStride];
+// End of a solve (one wave): fold the last iteration's slots into
+// out[k_max - 1] and write the solve record rec = {iterations performed,
+// converged, last norm non-finite}.  An iteration counts as performed unless
+// the one before it met the stop rule (it then exits on entry), so the count
+// is one past the first norm below eps, or k_max.
+__global__ __launch_bounds__(kWave) void k_deer_finish(const uint32_t* __restrict__ delta_bits,
+                                                       uint32_t* __restrict__ out,
+                                                       int* __restrict__ rec, int k_max,
+                                                       float eps) {
+  const int lane = threadIdx.x;
+  const int last = k_max - 1;
+  uint32_t v = delta_bits[(last % 3) * (kDeltaSlots * kDeltaStride) + lane * kDeltaStride];
   v = wave_max_u32(v);
-  if (threadIdx.x == 0) delta_out[last] = v;
+  int first = k_max;  // first index with norm < eps
+  for (int i0 = 0; i0 < k_max; i0 += kWave) {
+    const int i = i0 + lane;
+    const float d = (i < last) ? as_f32(out[i]) : as_f32(v);
+    const uint64_t hit = __ballot(i < k_max && d < eps);
+    if (hit) {
+      first = i0 + (int)__builtin_ctzll(hit);
+      break;
+    }
+  }
+  if (lane == 0) {
+    out[last] = v;
+    const int iters = first < k_max ? first + 1 : k_max;
+    const float d = (iters - 1 < last) ? as_f32(out[iters - 1]) : as_f32(v);
+    rec[0] = iters;
+    rec[1] = d < eps ? 1 : 0;
+    rec[2] = (d - d != 0.0f) ? 1 : 0;  // NaN or infinite
+  }
+}
+
+// Leave the solve's last iterate in h: it sits in p0 or p1 according to the
+// parity of the iteration count; copy it unless that buffer is h.
+__global__ __launch_bounds__(256) void k_deer_select(const float* __restrict__ p0,
+                                                     const float* __restrict__ p1,
+                                                     float* __restrict__ h, int64_t n,
+                                                     const int* __restrict__ rec) {
+  const float* src = ((rec[0] - 1) & 1) ? p1 : p0;
+  if (src == h) return;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if ((((uintptr_t)src | (uintptr_t)h) & 15) == 0) {
+    const int64_t n4 = n / 4;
+    for (int64_t i = tid; i < n4; i += stride)
+      reinterpret_cast<float4*>(h)[i] = reinterpret_cast<const float4*>(src)[i];
+    for (int64_t i = n4 * 4 + tid; i < n; i += stride) h[i] = src[i];
+  } else {
+    for (int64_t i = tid; i < n; i += stride) h[i] = src[i];
+  }
 }
 
 // MULTI: a channel spans several workgroups (look-back).  Otherwise one
@@ -645,10 +689,20 @@ hipError_t launch_scan_bwd_bdt(const float* a, const float* h, const float* h0, 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_deer_last_delta(const uint32_t* delta_bits, uint32_t* delta_out, int last,
-                                  hipStream_t stream) {
-  hipLaunchKernelGGL(k_deer_last_delta, dim3(1), dim3(kWave), 0, stream, delta_bits, delta_out,
-                     last);
+hipError_t launch_deer_finish(const uint32_t* delta_bits, uint32_t* delta_out, int* rec,
+                              int k_max, float eps, hipStream_t stream) {
+  hipLaunchKernelGGL(k_deer_finish, dim3(1), dim3(kWave), 0, stream, delta_bits, delta_out, rec,
+                     k_max, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_deer_select(const float* p0, const float* p1, float* h, int64_t n,
+                              const int* rec, hipStream_t stream) {
+  int64_t blocks = (n / 4 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(k_deer_select, dim3((unsigned)blocks), dim3(256), 0, stream, p0, p1, h, n,
+                     rec);
   return hipGetLastError();
 }
 

@@ -174,9 +174,10 @@ constexpr int kColWindow = 2;
 // are CW words apart.
 template <int NW, int CPT>
 __device__ __forceinline__ void col_enter_state(const float (&A)[CPT], const float (&B)[CPT],
-                                                bool multi, int tb, int nvc,
-                                                const float (&x0)[CPT], uint64_t* st,
-                                                ColShared<NW, CPT>& s, float (&x)[CPT]) {
+                                                bool multi, int tb, const float (&x0)[CPT],
+                                                const float* x0p, int64_t cbase, int cvalid,
+                                                uint64_t* st, ColShared<NW, CPT>& s,
+                                                float (&x)[CPT]) {
   constexpr int CW = kWave * CPT;
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -191,21 +192,18 @@ __device__ __forceinline__ void col_enter_state(const float (&A)[CPT], const flo
   if (multi) {
     static_assert(NW >= CPT, "one look-back wave per channel of a lane");
     if (wid >= NW - CPT) {
-      // wave NW-CPT+k resolves channel lane*CPT+k of every lane: one channel
-      // per lane keeps the look-back's registers off the other waves' paths
-      const int k = wid - (NW - CPT);
-      const int j = j0 + k;
+      // wave NW-CPT+k resolves channels 64k .. 64k+63 of the tile, one per
+      // lane: the look-back's registers stay off the other waves' paths, and
+      // each wave's status words are contiguous (whole cache lines)
+      const int j = (wid - (NW - CPT)) * kWave + lane;
       float TA = 1.0f, TB = 0.0f;
       for (int w = 0; w < NW; ++w) {
         const float wa = s.A[w][j], wb = s.B[w][j];
         TB = __builtin_fmaf(wa, TB, wb);
         TA = TA * wa;
       }
-      float x_in = x0[0];
-#pragma unroll
-      for (int kk = 1; kk < CPT; ++kk)
-        if (kk == k) x_in = x0[kk];
-      if (k < nvc) {
+      float x_in = 0.0f;
+      if (j < cvalid) {
         if (tb > 0) {
           status_store(st + (int64_t)tb * CW + j, pack_agg(TA, TB));
           uint64_t seen[1][kColWindow];
@@ -217,6 +215,8 @@ __device__ __forceinline__ void col_enter_state(const float (&A)[CPT], const flo
           float xr[1];
           lookback_cols<1, kColWindow>(st + j, CW, tb, 1, seen, xr);
           x_in = xr[0];
+        } else if (x0p) {
+          x_in = x0p[cbase + j];
         }
         status_store(st + (int64_t)tb * CW + j, pack_inc(__builtin_fmaf(TA, x_in, TB)));
       }
@@ -313,7 +313,8 @@ __device__ __forceinline__ void scan_fwd_tile(const float* __restrict__ a,
   float x0[CPT], x[CPT];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) x0[k] = (h0 && k < q.nvc) ? h0[q.c0 + k] : 0.0f;
-  col_enter_state<NW, CPT>(A, B, multi, tb, q.nvc, x0, st, s, x);
+  col_enter_state<NW, CPT>(A, B, multi, tb, x0, h0, cbase, clamp_valid(C - cbase, kWave * CPT),
+                           st, s, x);
   float* hp = h + q.row0 * C + cbase;
 #pragma unroll
   for (int i = 0; i < L; ++i) {
@@ -422,7 +423,8 @@ __device__ __forceinline__ void scan_bwd_tile(const float* __restrict__ a,
   float zero[CPT], x[CPT];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) zero[k] = 0.0f;
-  col_enter_state<NW, CPT>(A, B, multi, tb, nvc, zero, st, s, x);
+  col_enter_state<NW, CPT>(A, B, multi, tb, zero, nullptr, cbase,
+                           clamp_valid(C - cbase, kWave * CPT), st, s, x);
   float* dap = da + (row0 + L - 1) * C + cbase;
   float* dbp = db + (row0 + L - 1) * C + cbase;
 #pragma unroll
@@ -580,7 +582,8 @@ __device__ __forceinline__ void sru_tile(const IO* __restrict__ zf, const IO* __
   float x0[CPT], x[CPT];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) x0[k] = (c0p && k < q.nvc) ? c0p[q.c0 + k] : 0.0f;
-  col_enter_state<NW, CPT>(A, B, multi, tb, q.nvc, x0, st, s, x);
+  col_enter_state<NW, CPT>(A, B, multi, tb, x0, c0p, cbase, clamp_valid(C - cbase, kWave * CPT),
+                           st, s, x);
   IO* hp = h + q.row0 * C + cbase;
 #pragma unroll
   for (int i = 0; i < L; ++i) {

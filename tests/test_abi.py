@@ -32,7 +32,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     raw = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(raw, n), f"{n} declared in lrs.h but not exported"
@@ -107,6 +107,9 @@ def test_validation_before_any_launch(lib):
     assert lib.lrs_deer_solve(q(0x10000), q(0x20000), null, null, q(0x90000), 1, 1, 4,
                               ctypes.c_float(1e-5), 5, None, None, None, null, 0,
                               null) == b.LRS_ERR_WORKSPACE
+    assert lib.lrs_deer_stats(null, 0, 5, None, None, None, null) == b.LRS_ERR_WORKSPACE
+    assert lib.lrs_deer_stats(p, 1 << 20, 0, None, None, None, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_deer_stats(p, 64, 5, None, None, None, null) == b.LRS_ERR_WORKSPACE
 
 
 def test_product_path_has_no_fallback():
