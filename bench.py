@@ -282,6 +282,25 @@ def step_kernel_ms(torch, calls, reps):
     return out
 
 
+def cold_kernel_ms(torch, calls, reps, flush):
+    """Average duration of each entry point when every call starts with cold
+    caches: a 1 GiB buffer is read (summed) just before it, which evicts the
+    L2s and the memory-side cache without leaving dirty lines whose write-back
+    would compete with the call; the call is bracketed by two HIP events."""
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {k: 0.0 for k in calls}
+    for _ in range(reps):
+        for k, fn in calls.items():
+            flush.sum()
+            s, e = DeviceEvent(), DeviceEvent()
+            s.record(stream)
+            fn()
+            e.record(stream)
+            torch.cuda.synchronize()
+            out[k] += s.ms_until(e) / reps
+    return out
+
+
 def cpu_threads() -> int:
     n = os.cpu_count() or 1
     env = os.environ.get("OMP_NUM_THREADS")
@@ -426,6 +445,10 @@ def main():
         extra["ms_per_step_sync"] = round(timed(solve_sync, args.steps)[0], 5)
         info = lrs.deer_stats(ws, 5)
     value = N / (ms_per_step / 1e3)
+    # (4) the same entry points with cold caches before every call
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    cold = cold_kernel_ms(torch, calls, max(3, args.steps // 2), flush)
+    del flush
 
     if w.kind == "scan":
         bytes_step = sum(BYTES_PER_ELEM[k] * N for k in kernels)
@@ -449,6 +472,12 @@ def main():
                 "avg_launch_ms": round(dom_ms, 5)}
     extra["per_kernel_ms"] = {k: round(v, 5) for k, v in per_kernel.items()}
     extra["step_hbm_frac"] = round(bytes_step / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4)
+    cold_ms = sum(cold.values())
+    extra["cold"] = {"per_kernel_ms": {k: round(v, 5) for k, v in cold.items()},
+                     "ms_per_step": round(cold_ms, 5),
+                     "step_hbm_frac": round(bytes_step / (cold_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "how": "1 GiB read before every call (evicts L2 and the memory-side "
+                            "cache), HIP events around the call"}
     extra["wall_s"] = round(wall, 3)
 
     if not args.no_stream_ref:
