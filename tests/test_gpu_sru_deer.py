@@ -45,6 +45,18 @@ def test_sru_workload_bf16():
     assert eh <= 2e-2 and ec <= 1e-5
 
 
+def test_sru_streamed_f32_with_c0():
+    """fp32 I/O at B=32 D=1024 T=2048 (1 GiB of arrays, the streaming variant)
+    with a nonzero c0, against the oracle."""
+    w = I.scaled(I.WORKLOADS["sru_fwd"], seed=5900)
+    c0 = np.random.default_rng(5900).normal(size=(w.B, w.D)).astype(np.float32)
+    log(f"sru streamed f32 B={w.B} D={w.D} T={w.T}")
+    h, c, ref_h, ref_c = sru_case(w, "f32", c0=c0)
+    eh, ec = relerr(h, ref_h), relerr(c, ref_c)
+    log(f"sru streamed f32 errors: h={eh:.2e} c_last={ec:.2e}")
+    assert eh <= 1e-5 and ec <= 1e-5
+
+
 @pytest.mark.parametrize("B,D,T", [(1, 1, 1), (1, 2, 3), (2, 3, 65), (1, 6, 64), (3, 50, 200),
                                    (1, 258, 513), (2, 128, 1000)])
 @pytest.mark.parametrize("io", ["bf16", "f32"])
@@ -114,6 +126,19 @@ def test_deer_ragged(B, D, T):
     w = I.scaled(I.WORKLOADS["deer"], B=B, D=D, T=T, seed=6000 + T)
     h, info, ref_h, ref_it, _, _ = deer_case(w)
     assert info["iters"] == ref_it and relerr(h, ref_h) <= 1e-5
+
+
+def test_deer_streamed_multichunk():
+    """65536-step channels: 16 look-back chunks per channel, arrays large enough
+    (3 x 256 MiB per iteration) for the streaming variant."""
+    w = I.scaled(I.WORKLOADS["deer"], B=1, D=1024, T=65536, seed=6500)
+    log(f"deer streamed multi-chunk B={w.B} D={w.D} T={w.T}")
+    h, info, ref_h, ref_it, ref_d, _ = deer_case(w)
+    e = relerr(h, ref_h)
+    log(f"deer streamed: iters {info['iters']} vs {ref_it}; h relerr {e:.2e}")
+    assert info["iters"] == ref_it and e <= 1e-5
+    for dg, do in zip(info["deltas"], ref_d):
+        assert abs(dg - do) <= 1e-5 + 1e-3 * do
 
 
 @pytest.mark.parametrize("alias", [False, True])
