@@ -63,8 +63,9 @@ def _load():
     lib.lrs_oracle_deer.argtypes = [_c_dp, _c_dp, _c_dp, _c_dp, _c_dp, _i64, _i64, _i64,
                                     ctypes.c_double, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                                     _c_dp, ctypes.c_int]
+    lib.lrs_oracle_sru_bwd.argtypes = [_c_dp] * 14 + [_i64, _i64, _i64, ctypes.c_int]
     for fn in (lib.lrs_oracle_scan_fwd, lib.lrs_oracle_scan_bwd, lib.lrs_oracle_sru_fwd,
-               lib.lrs_oracle_rnn_seq, lib.lrs_oracle_deer):
+               lib.lrs_oracle_rnn_seq, lib.lrs_oracle_deer, lib.lrs_oracle_sru_bwd):
         fn.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -125,6 +126,26 @@ def sru_fwd(zf, zr, zx, bf, br, c0=None, nthreads: int = 0):
     _check(_load().lrs_oracle_sru_fwd(_ptr(zf), _ptr(zr), _ptr(zx), _ptr(bf), _ptr(br), _ptr(c0),
                                       _ptr(h), _ptr(c_last), T, B, D, nthreads), "sru_fwd")
     return h, c_last
+
+
+def sru_bwd(zf, zr, zx, bf, br, gh, c0=None, gcl=None, nthreads: int = 0):
+    """Gradients of the SRU layer for upstream dL/dh = gh [T,B,D] and
+    dL/dc_T = gcl [B,D].  Returns dict dzf, dzr, dzx [T,B,D], dbf, dbr [D], dc0 [B,D]."""
+    zf, zr, zx, bf, br, gh, c0, gcl = map(_f64, (zf, zr, zx, bf, br, gh, c0, gcl))
+    if not (zf.shape == zr.shape == zx.shape == gh.shape) or zf.ndim != 3:
+        raise ValueError("zf, zr, zx, gh must be [T, B, D]")
+    T, B, D = zf.shape
+    if bf.shape != (D,) or br.shape != (D,):
+        raise ValueError("bf, br must be [D]")
+    out = {k: np.empty_like(zf) for k in ("dzf", "dzr", "dzx")}
+    out["dbf"] = np.empty(D)
+    out["dbr"] = np.empty(D)
+    out["dc0"] = np.empty((B, D))
+    _check(_load().lrs_oracle_sru_bwd(_ptr(zf), _ptr(zr), _ptr(zx), _ptr(bf), _ptr(br), _ptr(c0),
+                                      _ptr(gh), _ptr(gcl), _ptr(out["dzf"]), _ptr(out["dzr"]),
+                                      _ptr(out["dzx"]), _ptr(out["dbf"]), _ptr(out["dbr"]),
+                                      _ptr(out["dc0"]), T, B, D, nthreads), "sru_bwd")
+    return out
 
 
 def rnn_seq(w, u, h0=None, nthreads: int = 0):

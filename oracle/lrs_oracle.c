@@ -145,6 +145,83 @@ int lrs_oracle_sru_fwd(const double *zf, const double *zr, const double *zx,
     return ORACLE_OK;
 }
 
+/* Reverse-mode derivative of the SRU layer above ([P1] SRU paragraph; the
+ * page states that the backward pass is also a scan, the formulas are the
+ * chain rule applied to the forward definition).  With the upstream gradient
+ * gh_t = dL/dh_t and gcl = dL/dc_T (NULL = 0), the total gradient of the cell
+ * state runs backwards in time:
+ *   gc_t = gh_t r_t (1 - tanh^2 c_t) + f_{t+1} gc_{t+1},   gc_T starts from gcl,
+ * and the inputs' gradients are
+ *   dzx_t = gh_t (1 - r_t) + gc_t (1 - f_t)
+ *   dzr_t = gh_t (tanh c_t - zx_t) r_t (1 - r_t)
+ *   dzf_t = gc_t (c_{t-1} - zx_t) f_t (1 - f_t)
+ *   dc0   = f_1 gc_1,   dbf[d] = sum over b, t of dzf,   dbr[d] = sum of dzr.
+ * The cell states are recomputed by the forward loop of each channel first.
+ * Arrays as for lrs_oracle_sru_fwd; dzf, dzr, dzx are [T, B, D]; dbf, dbr
+ * are [D]; dc0 is [B, D] or NULL. */
+int lrs_oracle_sru_bwd(const double *zf, const double *zr, const double *zx,
+                       const double *bf, const double *br, const double *c0,
+                       const double *gh, const double *gcl, double *dzf,
+                       double *dzr, double *dzx, double *dbf, double *dbr,
+                       double *dc0, int64_t T, int64_t B, int64_t D, int nthreads)
+{
+    if (T < 0 || B < 0 || D < 0) return ORACLE_EINVAL;
+    if (T * B * D > 0 && (!zf || !zr || !zx || !bf || !br || !gh || !dzf || !dzr || !dzx ||
+                          !dbf || !dbr))
+        return ORACLE_EINVAL;
+    set_threads(nthreads);
+    const int64_t C = B * D;
+    double *sf = calloc((size_t)(C > 0 ? C : 1), sizeof(double));
+    double *sr = calloc((size_t)(C > 0 ? C : 1), sizeof(double));
+    if (!sf || !sr) { free(sf); free(sr); return ORACLE_ENOMEM; }
+    int fail = 0;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t ch = 0; ch < C; ++ch) {
+        const int64_t d = ch % D;
+        double *c = malloc((size_t)(T > 0 ? T : 1) * sizeof(double));
+        if (!c) { fail = 1; continue; }
+        /* forward: cell states c_1..c_T */
+        double state = c0 ? c0[ch] : 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t i = t * C + ch;
+            const double f = sigmoid(zf[i] + bf[d]);
+            state = f * state + (1.0 - f) * zx[i];
+            c[t] = state;
+        }
+        /* reverse: carry = f_{t+1} gc_{t+1} (gcl at the end of the sequence) */
+        double carry = gcl ? gcl[ch] : 0.0;
+        double acc_f = 0.0, acc_r = 0.0;
+        for (int64_t t = T - 1; t >= 0; --t) {
+            const int64_t i = t * C + ch;
+            const double f = sigmoid(zf[i] + bf[d]);
+            const double r = sigmoid(zr[i] + br[d]);
+            const double th = tanh(c[t]);
+            const double gc = gh[i] * r * (1.0 - th * th) + carry;
+            const double cprev = t > 0 ? c[t - 1] : (c0 ? c0[ch] : 0.0);
+            dzx[i] = gh[i] * (1.0 - r) + gc * (1.0 - f);
+            dzr[i] = gh[i] * (th - zx[i]) * r * (1.0 - r);
+            dzf[i] = gc * (cprev - zx[i]) * f * (1.0 - f);
+            acc_f += dzf[i];
+            acc_r += dzr[i];
+            carry = f * gc;
+        }
+        if (dc0) dc0[ch] = carry;
+        sf[ch] = acc_f;
+        sr[ch] = acc_r;
+        free(c);
+    }
+    if (!fail) {
+        for (int64_t d = 0; d < D; ++d) { dbf[d] = 0.0; dbr[d] = 0.0; }
+        for (int64_t ch = 0; ch < C; ++ch) {  /* fixed order: deterministic sums */
+            dbf[ch % D] += sf[ch];
+            dbr[ch % D] += sr[ch];
+        }
+    }
+    free(sf);
+    free(sr);
+    return fail ? ORACLE_ENOMEM : ORACLE_OK;
+}
+
 /* Plain sequential nonlinear RNN h_t = tanh(w_d * h_{t-1} + u_t): the ground
  * truth that the DEER iteration converges to ([P4] core principle).
  * u, h are [B, D, T]; w is [D]; h0 is [B, D] or NULL. */
