@@ -33,8 +33,9 @@
  *    Pointers must be aligned to their element size; 16-byte alignment of all
  *    arrays (and T % 4 == 0 for [B,D,T] fp32) enables the widest accesses.
  *  - `stream` is a hipStream_t passed as an opaque pointer (NULL = the null
- *    stream).  Scan and SRU calls only enqueue work and return; DEER reads its
- *    convergence test back to the host and returns after the solve.
+ *    stream).  Scan and SRU calls only enqueue work and return; DEER does the
+ *    same when it is given no host outputs, and otherwise reads its solve
+ *    record back to the host and returns after the solve.
  *  - Errors are return codes (lrs_status); nothing is thrown and nothing
  *    aborts.  Arguments are validated before any launch, so an error other
  *    than LRS_ERR_HIP leaves all outputs untouched.  An empty problem
@@ -125,12 +126,42 @@ LRS_API size_t lrs_sru_workspace_bytes(int64_t T, int64_t B, int64_t D);
  * z_f, z_r, z_x, h : [T,B,D], element type io_dtype (LRS_BF16 or LRS_F32).
  * bias_f, bias_r   : [D] fp32.   c0: [B,D] fp32 or NULL (zero).
  * c_last           : [B,D] fp32 output (c_T) or NULL.
+ * c_states         : [T,B,D] fp32 output (every c_t, as lrs_sru_bwd needs
+ *                    them) or NULL.
  * Gates, state and activations are computed in fp32; h is rounded to io_dtype
- * (nearest-even).  h must not overlap the inputs. */
+ * (nearest-even).  No output may overlap an input or another output. */
 LRS_API int lrs_sru_fwd(const void *z_f, const void *z_r, const void *z_x, const float *bias_f,
-                const float *bias_r, const float *c0, void *h, float *c_last, int64_t T,
-                int64_t B, int64_t D, int io_dtype, void *workspace, size_t workspace_bytes,
-                void *stream);
+                const float *bias_r, const float *c0, void *h, float *c_last, float *c_states,
+                int64_t T, int64_t B, int64_t D, int io_dtype, void *workspace,
+                size_t workspace_bytes, void *stream);
+
+/* Workspace bytes needed by lrs_sru_bwd for this shape (0 for an invalid one). */
+LRS_API size_t lrs_sru_bwd_workspace_bytes(int64_t T, int64_t B, int64_t D);
+
+/* SRU layer backward ([P1] SRU paragraph and parallel-scan paragraph: the
+ * backward pass is also a scan; the formulas are the chain rule of
+ * lrs_sru_fwd).  Given the upstream gradients gh_t = dL/dh_t and dL/dc_T, the
+ * gradient of the cell state runs backwards in time,
+ *   gc_t = gh_t r_t (1 - tanh^2 c_t) + f_{t+1} gc_{t+1}   (gc_T adds dL/dc_T),
+ * and
+ *   dL/dz_x = gh (1 - r) + gc (1 - f),  dL/dz_r = gh (tanh c - z_x) r (1 - r),
+ *   dL/dz_f = gc (c_{t-1} - z_x) f (1 - f),  dL/dc0 = f_1 gc_1,
+ *   dL/dbias_f[d], dL/dbias_r[d] = sums of dL/dz_f, dL/dz_r over batch and time.
+ * z_f, z_r, z_x, grad_h, grad_z*: [T,B,D], element type io_dtype.
+ * bias_f, bias_r: [D] fp32.   c0: [B,D] fp32 or NULL (zero).
+ * c_states   : [T,B,D] fp32, the cell states lrs_sru_fwd wrote for the same
+ *              inputs.
+ * grad_c_last: [B,D] fp32 (dL/dc_T) or NULL (zero).
+ * grad_bias_f, grad_bias_r: [D] fp32 outputs (overwritten; the sums are taken
+ *              in a fixed order, so results do not depend on scheduling).
+ * grad_c0    : [B,D] fp32 output or NULL.
+ * No output may overlap an input or another output. */
+LRS_API int lrs_sru_bwd(const void *z_f, const void *z_r, const void *z_x, const float *bias_f,
+                const float *bias_r, const float *c0, const float *c_states,
+                const void *grad_h, const float *grad_c_last, void *grad_zf, void *grad_zr,
+                void *grad_zx, float *grad_bias_f, float *grad_bias_r, float *grad_c0,
+                int64_t T, int64_t B, int64_t D, int io_dtype, void *workspace,
+                size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------- DEER --- */
 

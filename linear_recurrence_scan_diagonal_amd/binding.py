@@ -24,7 +24,7 @@ DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 EXPORTS = ("lrs_status_string", "lrs_version", "lrs_scan_workspace_bytes", "lrs_scan_fwd",
            "lrs_scan_bwd", "lrs_sru_workspace_bytes", "lrs_sru_fwd", "lrs_deer_workspace_bytes",
-           "lrs_deer_solve", "lrs_deer_stats")
+           "lrs_deer_solve", "lrs_deer_stats", "lrs_sru_bwd_workspace_bytes", "lrs_sru_bwd")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -62,8 +62,12 @@ def load():
     lib.lrs_scan_bwd.restype = _int
     lib.lrs_sru_workspace_bytes.argtypes = [_i64, _i64, _i64]
     lib.lrs_sru_workspace_bytes.restype = _sz
-    lib.lrs_sru_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp,
-                                _sz, _vp]
+    lib.lrs_sru_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int,
+                                _vp, _sz, _vp]
+    lib.lrs_sru_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64]
+    lib.lrs_sru_bwd_workspace_bytes.restype = _sz
+    lib.lrs_sru_bwd.argtypes = [_vp] * 15 + [_i64, _i64, _i64, _int, _vp, _sz, _vp]
+    lib.lrs_sru_bwd.restype = _int
     lib.lrs_sru_fwd.restype = _int
     lib.lrs_deer_workspace_bytes.argtypes = [_i64, _i64, _i64, _int]
     lib.lrs_deer_workspace_bytes.restype = _sz
@@ -172,8 +176,10 @@ def scan_bwd(a, h, grad_h, h0=None, layout: str = "bdt", need_grad_h0: bool = Tr
 
 
 def sru_fwd(z_f, z_r, z_x, bias_f, bias_r, c0=None, want_c_last: bool = False, out=None,
-            workspace=None):
-    """Fused SRU layer on [T,B,D] pre-activations (bf16 or fp32).  Returns h or (h, c_last)."""
+            workspace=None, c_states=None):
+    """Fused SRU layer on [T,B,D] pre-activations (bf16 or fp32).  Returns h or
+    (h, c_last).  c_states, if given, is a [T,B,D] fp32 tensor that receives
+    every cell state (the input sru_bwd needs)."""
     lib = load()
     if z_f.dim() != 3:
         raise ValueError("z_f must be [T,B,D]")
@@ -184,15 +190,47 @@ def sru_fwd(z_f, z_r, z_x, bias_f, bias_r, c0=None, want_c_last: bool = False, o
     _check_dev("bias_f", bias_f, torch.float32, (D,))
     _check_dev("bias_r", bias_r, torch.float32, (D,))
     _check_dev("c0", c0, torch.float32, (B, D))
+    _check_dev("c_states", c_states, torch.float32, z_f.shape)
     h = torch.empty_like(z_f) if out is None else out
     _check_dev("out", h, io, z_f.shape)
     c_last = torch.empty((B, D), dtype=torch.float32, device=z_f.device) if want_c_last else None
     nbytes = lib.lrs_sru_workspace_bytes(T, B, D)
     ws = _workspace(nbytes, z_f.device, workspace)
     _call(lib.lrs_sru_fwd(_ptr(z_f), _ptr(z_r), _ptr(z_x), _ptr(bias_f), _ptr(bias_r), _ptr(c0),
-                          _ptr(h), _ptr(c_last), T, B, D, DTYPES[io], _ptr(ws), nbytes,
-                          _stream(z_f.device)), "lrs_sru_fwd")
+                          _ptr(h), _ptr(c_last), _ptr(c_states), T, B, D, DTYPES[io], _ptr(ws),
+                          nbytes, _stream(z_f.device)), "lrs_sru_fwd")
     return (h, c_last) if want_c_last else h
+
+
+def sru_bwd(z_f, z_r, z_x, bias_f, bias_r, c_states, grad_h, c0=None, grad_c_last=None,
+            out=None, workspace=None):
+    """Backward of sru_fwd.  c_states: the [T,B,D] fp32 cell states sru_fwd
+    saved; grad_h: dL/dh in the I/O type; grad_c_last: dL/dc_T [B,D] or None.
+    Returns (grad_zf, grad_zr, grad_zx, grad_bias_f, grad_bias_r, grad_c0)."""
+    lib = load()
+    T, B, D = (int(x) for x in z_f.shape)
+    io = z_f.dtype
+    for name, t in (("z_f", z_f), ("z_r", z_r), ("z_x", z_x), ("grad_h", grad_h)):
+        _check_dev(name, t, io, z_f.shape)
+    _check_dev("bias_f", bias_f, torch.float32, (D,))
+    _check_dev("bias_r", bias_r, torch.float32, (D,))
+    _check_dev("c_states", c_states, torch.float32, z_f.shape)
+    _check_dev("c0", c0, torch.float32, (B, D))
+    _check_dev("grad_c_last", grad_c_last, torch.float32, (B, D))
+    dev = z_f.device
+    if out is None:
+        out = (torch.empty_like(z_f), torch.empty_like(z_f), torch.empty_like(z_f),
+               torch.empty(D, dtype=torch.float32, device=dev),
+               torch.empty(D, dtype=torch.float32, device=dev),
+               torch.empty((B, D), dtype=torch.float32, device=dev))
+    dzf, dzr, dzx, dbf, dbr, dc0 = out
+    nbytes = lib.lrs_sru_bwd_workspace_bytes(T, B, D)
+    ws = _workspace(nbytes, dev, workspace)
+    _call(lib.lrs_sru_bwd(_ptr(z_f), _ptr(z_r), _ptr(z_x), _ptr(bias_f), _ptr(bias_r), _ptr(c0),
+                          _ptr(c_states), _ptr(grad_h), _ptr(grad_c_last), _ptr(dzf), _ptr(dzr),
+                          _ptr(dzx), _ptr(dbf), _ptr(dbr), _ptr(dc0), T, B, D, DTYPES[io],
+                          _ptr(ws), nbytes, _stream(dev)), "lrs_sru_bwd")
+    return dzf, dzr, dzx, dbf, dbr, dc0
 
 
 def deer_solve(w, u, h0=None, h_init=None, eps: float = 1e-5, k_max: int = 5, out=None,

@@ -273,9 +273,9 @@ size_t lrs_sru_workspace_bytes(int64_t T, int64_t B, int64_t D) {
 }
 
 int lrs_sru_fwd(const void* z_f, const void* z_r, const void* z_x, const float* bias_f,
-                const float* bias_r, const float* c0, void* h, float* c_last, int64_t T,
-                int64_t B, int64_t D, int io_dtype, void* workspace, size_t workspace_bytes,
-                void* stream) {
+                const float* bias_r, const float* c0, void* h, float* c_last, float* c_states,
+                int64_t T, int64_t B, int64_t D, int io_dtype, void* workspace,
+                size_t workspace_bytes, void* stream) {
   int64_t C, N;
   if (!shape_ok(B, D, T, &C, &N)) return LRS_ERR_INVALID_ARG;
   if (io_dtype != LRS_F32 && io_dtype != LRS_BF16) return LRS_ERR_INVALID_ARG;
@@ -288,15 +288,18 @@ int lrs_sru_fwd(const void* z_f, const void* z_r, const void* z_x, const float* 
   const size_t es = io_dtype == LRS_BF16 ? 2 : 4;
   if (!aligned(z_f, es) || !aligned(z_r, es) || !aligned(z_x, es) || !aligned(h, es) ||
       !aligned(bias_f, 4) || !aligned(bias_r, 4) || (c0 && !aligned(c0, 4)) ||
-      (c_last && !aligned(c_last, 4)))
+      (c_last && !aligned(c_last, 4)) || (c_states && !aligned(c_states, 4)))
     return LRS_ERR_INVALID_ARG;
-  const size_t nb = (size_t)N * es, cb = (size_t)C * 4, db = (size_t)D * 4;
+  const size_t nb = (size_t)N * es, cb = (size_t)C * 4, db = (size_t)D * 4, sb = (size_t)N * 4;
   const void* ins[6] = {z_f, z_r, z_x, bias_f, bias_r, c0};
   const size_t insz[6] = {nb, nb, nb, db, db, cb};
   for (int i = 0; i < 6; ++i)
-    if (overlap(h, nb, ins[i], insz[i]) || overlap(c_last, cb, ins[i], insz[i]))
+    if (overlap(h, nb, ins[i], insz[i]) || overlap(c_last, cb, ins[i], insz[i]) ||
+        overlap(c_states, sb, ins[i], insz[i]))
       return LRS_ERR_INVALID_ARG;
-  if (overlap(h, nb, c_last, cb)) return LRS_ERR_INVALID_ARG;
+  if (overlap(h, nb, c_last, cb) || overlap(h, nb, c_states, sb) ||
+      overlap(c_last, cb, c_states, sb))
+    return LRS_ERR_INVALID_ARG;
   const lrs::ColPlan p = lrs::plan_sru(C, T, io_dtype);
   if (!grid_ok(p.ncb * p.ntb, p.nw * 64)) return LRS_ERR_UNSUPPORTED;
   const int64_t nst = lrs::col_status_words(p);
@@ -313,9 +316,90 @@ int lrs_sru_fwd(const void* z_f, const void* z_r, const void* z_x, const float* 
   }
   const size_t rowbytes = (size_t)p.cpt * es;
   const int vec = aligned(z_f, rowbytes) && aligned(z_r, rowbytes) && aligned(z_x, rowbytes) &&
-                  aligned(h, rowbytes) && (C % p.cpt == 0);
-  return hip_status(lrs::launch_sru_fwd(z_f, z_r, z_x, bias_f, bias_r, c0, h, c_last, T, B, D,
-                                        io_dtype, p, vec, status, tickets, s));
+                  aligned(h, rowbytes) && (!c_states || aligned(c_states, (size_t)p.cpt * 4)) &&
+                  (C % p.cpt == 0);
+  return hip_status(lrs::launch_sru_fwd(z_f, z_r, z_x, bias_f, bias_r, c0, h, c_last, c_states, T,
+                                        B, D, io_dtype, p, vec, status, tickets, s));
+}
+
+// SRU backward: look-back state plus 2 * ntb * C floats of bias partials.
+static size_t sru_bwd_ws(const lrs::ColPlan& p, int64_t C) {
+  return lookback_bytes(lrs::col_status_words(p), p.ncb) +
+         align_up((size_t)(2 * p.ntb * C) * 4);
+}
+
+size_t lrs_sru_bwd_workspace_bytes(int64_t T, int64_t B, int64_t D) {
+  int64_t C, N;
+  if (!shape_ok(B, D, T, &C, &N) || N == 0) return 0;
+  const size_t b1 = sru_bwd_ws(lrs::plan_sru_bwd(C, T, LRS_BF16), C);
+  const size_t b2 = sru_bwd_ws(lrs::plan_sru_bwd(C, T, LRS_F32), C);
+  return kAlign + (b1 > b2 ? b1 : b2);
+}
+
+int lrs_sru_bwd(const void* z_f, const void* z_r, const void* z_x, const float* bias_f,
+                const float* bias_r, const float* c0, const float* c_states, const void* grad_h,
+                const float* grad_c_last, void* grad_zf, void* grad_zr, void* grad_zx,
+                float* grad_bias_f, float* grad_bias_r, float* grad_c0, int64_t T, int64_t B,
+                int64_t D, int io_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int64_t C, N;
+  if (!shape_ok(B, D, T, &C, &N)) return LRS_ERR_INVALID_ARG;
+  if (io_dtype != LRS_F32 && io_dtype != LRS_BF16) return LRS_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (N == 0) {
+    // no steps: the bias gradients are empty sums; dL/dc0 = dL/dc_T
+    int rc = LRS_OK;
+    if (D > 0 && grad_bias_f) rc = hip_status(lrs::launch_copy_or_zero(grad_bias_f, nullptr, D, s));
+    if (rc == LRS_OK && D > 0 && grad_bias_r)
+      rc = hip_status(lrs::launch_copy_or_zero(grad_bias_r, nullptr, D, s));
+    if (rc == LRS_OK && T == 0 && C > 0 && grad_c0)
+      rc = hip_status(lrs::launch_copy_or_zero(grad_c0, grad_c_last, C, s));
+    return rc;
+  }
+  if (!z_f || !z_r || !z_x || !bias_f || !bias_r || !c_states || !grad_h || !grad_zf ||
+      !grad_zr || !grad_zx || !grad_bias_f || !grad_bias_r)
+    return LRS_ERR_INVALID_ARG;
+  const size_t es = io_dtype == LRS_BF16 ? 2 : 4;
+  const void* io[7] = {z_f, z_r, z_x, grad_h, grad_zf, grad_zr, grad_zx};
+  for (int i = 0; i < 7; ++i)
+    if (!aligned(io[i], es)) return LRS_ERR_INVALID_ARG;
+  if (!aligned(bias_f, 4) || !aligned(bias_r, 4) || !aligned(c_states, 4) ||
+      (c0 && !aligned(c0, 4)) || (grad_c_last && !aligned(grad_c_last, 4)) ||
+      !aligned(grad_bias_f, 4) || !aligned(grad_bias_r, 4) || (grad_c0 && !aligned(grad_c0, 4)))
+    return LRS_ERR_INVALID_ARG;
+  const size_t nb = (size_t)N * es, cb = (size_t)C * 4, db = (size_t)D * 4, sb = (size_t)N * 4;
+  const void* ins[8] = {z_f, z_r, z_x, grad_h, c_states, bias_f, bias_r, c0};
+  const size_t insz[8] = {nb, nb, nb, nb, sb, db, db, cb};
+  const void* outs[6] = {grad_zf, grad_zr, grad_zx, grad_bias_f, grad_bias_r, grad_c0};
+  const size_t outsz[6] = {nb, nb, nb, db, db, cb};
+  for (int o = 0; o < 6; ++o) {
+    for (int i = 0; i < 8; ++i)
+      if (overlap(outs[o], outsz[o], ins[i], insz[i])) return LRS_ERR_INVALID_ARG;
+    if (overlap(outs[o], outsz[o], grad_c_last, cb)) return LRS_ERR_INVALID_ARG;
+    for (int o2 = o + 1; o2 < 6; ++o2)
+      if (overlap(outs[o], outsz[o], outs[o2], outsz[o2])) return LRS_ERR_INVALID_ARG;
+  }
+  const lrs::ColPlan p = lrs::plan_sru_bwd(C, T, io_dtype);
+  if (!grid_ok(p.ncb * p.ntb, p.nw * 64)) return LRS_ERR_UNSUPPORTED;
+  const size_t need = lrs_sru_bwd_workspace_bytes(T, B, D);
+  if (!workspace || workspace_bytes < need) return LRS_ERR_WORKSPACE;
+  Carve cv(align_ptr(workspace));
+  float* part = cv.take<float>(2 * p.ntb * C);
+  uint64_t* status = nullptr;
+  unsigned* tickets = nullptr;
+  const int64_t nst = lrs::col_status_words(p);
+  if (nst > 0) {
+    status = cv.take<uint64_t>(nst);
+    tickets = cv.take<unsigned>(p.ncb);
+    const int rc = hip_status(lrs::launch_reset(status, nst, tickets, p.ncb, nullptr, 0, s));
+    if (rc != LRS_OK) return rc;
+  }
+  const size_t rowbytes = (size_t)p.cpt * es;
+  int vec = (C % p.cpt == 0) && aligned(c_states, (size_t)p.cpt * 4);
+  for (int i = 0; i < 7; ++i) vec = vec && aligned(io[i], rowbytes);
+  return hip_status(lrs::launch_sru_bwd(z_f, z_r, z_x, bias_f, bias_r, c0, c_states, grad_h,
+                                        grad_c_last, grad_zf, grad_zr, grad_zx, grad_bias_f,
+                                        grad_bias_r, grad_c0, part, T, B, D, io_dtype, p, vec,
+                                        status, tickets, s));
 }
 
 // ------------------------------------------------------------------- DEER

@@ -78,8 +78,18 @@ hipError_t launch_scan_bwd_tbd(const float* a, const float* h, const float* h0, 
                                const ColPlan& p, int vec, uint64_t* status, unsigned* tickets,
                                hipStream_t stream);
 hipError_t launch_sru_fwd(const void* zf, const void* zr, const void* zx, const float* bias_f,
-                          const float* bias_r, const float* c0, void* h, float* c_last, int64_t T,
-                          int64_t B, int64_t D, int io_dtype, const ColPlan& p, int vec,
-                          uint64_t* status, unsigned* tickets, hipStream_t stream);
+                          const float* bias_r, const float* c0, void* h, float* c_last,
+                          float* c_states, int64_t T, int64_t B, int64_t D, int io_dtype,
+                          const ColPlan& p, int vec, uint64_t* status, unsigned* tickets,
+                          hipStream_t stream);
+ColPlan plan_sru_bwd(int64_t C, int64_t T, int io_dtype);
+// Launches the backward kernel and the bias-gradient reduction; `part` holds
+// 2 * ntb * B * D floats of per-tile partial sums.
+hipError_t launch_sru_bwd(const void* zf, const void* zr, const void* zx, const float* bias_f,
+                          const float* bias_r, const float* c0, const float* cs, const void* gh,
+                          const float* gcl, void* dzf, void* dzr, void* dzx, float* dbf,
+                          float* dbr, float* dc0, float* part, int64_t T, int64_t B, int64_t D,
+                          int io_dtype, const ColPlan& p, int vec, uint64_t* status,
+                          unsigned* tickets, hipStream_t stream);
 
 }  // namespace lrs

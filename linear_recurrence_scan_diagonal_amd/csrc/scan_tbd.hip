@@ -520,7 +520,8 @@ __device__ __forceinline__ void sru_tile(const IO* __restrict__ zf, const IO* __
                                          const float* __restrict__ bias_f,
                                          const float* __restrict__ bias_r,
                                          const float* __restrict__ c0p, IO* __restrict__ h,
-                                         float* __restrict__ c_last, int64_t T, int64_t C,
+                                         float* __restrict__ c_last, float* __restrict__ cs,
+                                         int64_t T, int64_t C,
                                          int64_t D, int tb, int cb, bool multi, uint64_t* st,
                                          ColShared<NW, CPT>& s) {
   const ColPos q = col_pos<NW, L, CPT>(tb, cb, C);
@@ -602,6 +603,7 @@ __device__ __forceinline__ void sru_tile(const IO* __restrict__ zf, const IO* __
     const int nv = (FULL || q.row0 + i < T) ? q.nvc : 0;
     SruRow<IO, CPT>::template store<FULL, NT>(hp, q.off, nv, out);
     hp += C;
+    if (cs) store_row<CPT, FULL, NT>(cs + (q.row0 + i) * C + cbase, q.off, nv, x);
     if (c_last && q.row0 + i == T - 1) {
 #pragma unroll
       for (int k = 0; k < CPT; ++k)
@@ -614,7 +616,8 @@ template <typename IO, int NW, int L, int CPT, bool NT>
 __global__ __launch_bounds__(NW* kWave) void k_sru_fwd(
     const IO* __restrict__ zf, const IO* __restrict__ zr, const IO* __restrict__ zx,
     const float* __restrict__ bias_f, const float* __restrict__ bias_r,
-    const float* __restrict__ c0p, IO* __restrict__ h, float* __restrict__ c_last, int64_t T,
+    const float* __restrict__ c0p, IO* __restrict__ h, float* __restrict__ c_last,
+    float* __restrict__ cs, int64_t T,
     int64_t C, int64_t D, int ncb, int ntb, int vec, uint64_t* __restrict__ status,
     unsigned* __restrict__ tickets) {
   constexpr int CW = kWave * CPT, TW = NW * L;
@@ -625,11 +628,241 @@ __global__ __launch_bounds__(NW* kWave) void k_sru_fwd(
   uint64_t* st = status + (int64_t)cb * ntb * CW;
   const bool full = vec && ((int64_t)(tb + 1) * TW <= T) && ((int64_t)(cb + 1) * CW <= C);
   if (full)
-    sru_tile<IO, NW, L, CPT, true, NT>(zf, zr, zx, bias_f, bias_r, c0p, h, c_last, T, C, D, tb, cb,
+    sru_tile<IO, NW, L, CPT, true, NT>(zf, zr, zx, bias_f, bias_r, c0p, h, c_last, cs, T, C, D, tb, cb,
                                    multi, st, s);
   else
-    sru_tile<IO, NW, L, CPT, false, NT>(zf, zr, zx, bias_f, bias_r, c0p, h, c_last, T, C, D, tb, cb,
+    sru_tile<IO, NW, L, CPT, false, NT>(zf, zr, zx, bias_f, bias_r, c0p, h, c_last, cs, T, C, D, tb, cb,
                                     multi, st, s);
+}
+
+// ---------------------------------------------------------------------------
+// SRU backward, [T, B, D] (reverse time, as k_scan_bwd_tbd: logical time block
+// 0 is the last physical block, wave 0 takes its latest steps).  With the cell
+// states c saved by the forward pass, the gradient of the cell state runs
+//   gc_t = e_t + f_{t+1} gc_{t+1},   e_t = gh_t r_t (1 - tanh^2 c_t),
+// from dL/dc_T after the last step (f beyond the sequence counts as 1), and
+//   dzx = gh (1 - r) + gc (1 - f),   dzr = gh (tanh c - zx) r (1 - r),
+//   dzf = gc (c_{t-1} - zx) f (1 - f),   dc0 = f_1 gc_1.
+// r and tanh c are recomputed in the output pass instead of being kept.  Each
+// tile writes its per-channel sums of dzf and dzr over its steps; k_col_sum
+// adds them up per feature for the bias gradients, in a fixed order.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float sru_sigmoid(float z, float nb) {
+  // nb = -log2(e) * bias
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(z, -kLog2e, nb)));
+}
+__device__ __forceinline__ float sru_tanh(float v) {
+  return __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f((2.0f * kLog2e) * v)),
+                        1.0f);
+}
+
+template <typename IO, int NW, int L, int CPT, bool FULL, bool NT>
+__device__ __forceinline__ void sru_bwd_tile(
+    const IO* __restrict__ zf, const IO* __restrict__ zr, const IO* __restrict__ zx,
+    const float* __restrict__ bias_f, const float* __restrict__ bias_r,
+    const float* __restrict__ c0p, const float* __restrict__ cs, const IO* __restrict__ gh,
+    const float* __restrict__ gcl, IO* __restrict__ dzf, IO* __restrict__ dzr,
+    IO* __restrict__ dzx, float* __restrict__ dc0, float* __restrict__ part, int64_t T,
+    int64_t C, int64_t D, int tb, int ntb, int cb, bool multi, uint64_t* st,
+    ColShared<NW, CPT>& s) {
+  constexpr int CW = kWave * CPT;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int ptb = ntb - 1 - tb;
+  const uint32_t off = (uint32_t)(lane * CPT);
+  const int64_t cbase = (int64_t)cb * CW;
+  const int64_t c0i = cbase + off;
+  const int nvc = FULL ? CPT : clamp_valid(C - c0i, CPT);
+  const int64_t row0 = (int64_t)ptb * (NW * L) + (int64_t)(NW - 1 - wid) * L;
+  float nbf[CPT], nbr[CPT];
+  {
+    int64_t d = (nvc > 0) ? c0i % D : 0;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int64_t dk = (k < nvc) ? d : 0;
+      nbf[k] = -kLog2e * bias_f[dk];
+      nbr[k] = -kLog2e * bias_r[dk];
+      d = (d + 1 == D) ? 0 : d + 1;
+    }
+  }
+  // f at rows row0 .. row0+L-1, and f[L] for the step after the wave (1 at
+  // and beyond the end of the sequence); c at the wave's rows and just before
+  float f[L + 1][CPT], c[L][CPT], cp[CPT];
+  SruRow<IO, CPT> rr[L], xr[L], gr[L];
+  {
+    const IO* fp = zf + row0 * C + cbase;
+    const IO* rp = zr + row0 * C + cbase;
+    const IO* xp = zx + row0 * C + cbase;
+    const IO* gp = gh + row0 * C + cbase;
+    const float* cq = cs + row0 * C + cbase;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int nv = (FULL || row0 + i < T) ? nvc : 0;
+      SruRow<IO, CPT> fr;
+      fr.template load<FULL, NT>(fp, off, nv);
+      rr[i].template load<FULL, NT>(rp, off, nv);
+      xr[i].template load<FULL, NT>(xp, off, nv);
+      gr[i].template load<FULL, NT>(gp, off, nv);
+      load_row<CPT, FULL, NT>(cq, off, nv, 0.0f, c[i]);
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) f[i][k] = (FULL || k < nv) ? sru_sigmoid(fr.get(k), nbf[k]) : 1.0f;
+      fp += C;
+      rp += C;
+      xp += C;
+      gp += C;
+      cq += C;
+    }
+    const int64_t tn = row0 + L;
+    if (tn < T) {
+      SruRow<IO, CPT> fr;
+      fr.template load<FULL, false>(zf + tn * C + cbase, off, nvc);
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) f[L][k] = (FULL || k < nvc) ? sru_sigmoid(fr.get(k), nbf[k]) : 1.0f;
+    } else {
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) f[L][k] = 1.0f;
+    }
+    if (row0 > 0 && row0 <= T) {
+      load_row<CPT, FULL, false>(cs + (row0 - 1) * C + cbase, off, nvc, 0.0f, cp);
+    } else {
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) cp[k] = (c0p && k < nvc) ? c0p[c0i + k] : 0.0f;
+    }
+  }
+  // e_t with r_t and tanh c_t (rows and channels out of range have gh = 0)
+  auto e_at = [&](int i, int k, float& r, float& th) {
+    r = sru_sigmoid(rr[i].get(k), nbr[k]);
+    th = sru_tanh(c[i][k]);
+    const float gr_ = gr[i].get(k) * r;
+    return __builtin_fmaf(-gr_ * th, th, gr_);
+  };
+  float A[CPT], B[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    float r, th;
+    A[k] = f[L][k];
+    B[k] = e_at(L - 1, k, r, th);
+#pragma unroll
+    for (int i = L - 2; i >= 0; --i) {
+      B[k] = __builtin_fmaf(f[i + 1][k], B[k], e_at(i, k, r, th));
+      A[k] = A[k] * f[i + 1][k];
+    }
+  }
+  float x0[CPT], x[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) x0[k] = (gcl && k < nvc) ? gcl[c0i + k] : 0.0f;
+  col_enter_state<NW, CPT>(A, B, multi, tb, x0, gcl, cbase, clamp_valid(C - cbase, CW), st, s, x);
+  float pf[CPT], pr[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) { pf[k] = 0.0f; pr[k] = 0.0f; }
+  IO* qf = dzf + (row0 + L - 1) * C + cbase;
+  IO* qr = dzr + (row0 + L - 1) * C + cbase;
+  IO* qx = dzx + (row0 + L - 1) * C + cbase;
+#pragma unroll
+  for (int i = L - 1; i >= 0; --i) {
+    float of[CPT], orr[CPT], ox[CPT];
+    const bool row_ok = FULL || row0 + i < T;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      float r, th;
+      const float e = e_at(i, k, r, th);
+      x[k] = __builtin_fmaf(f[i + 1][k], x[k], e);  // gc_t
+      const float g = gr[i].get(k), z = xr[i].get(k), fi = f[i][k];
+      const float cprev = (i > 0) ? c[i - 1][k] : cp[k];
+      ox[k] = __builtin_fmaf(g, 1.0f - r, x[k] * (1.0f - fi));
+      orr[k] = g * (th - z) * (r * (1.0f - r));
+      of[k] = x[k] * (cprev - z) * (fi * (1.0f - fi));
+      if (FULL || (row_ok && k < nvc)) {
+        pf[k] += of[k];
+        pr[k] += orr[k];
+      }
+    }
+    const int nv = row_ok ? nvc : 0;
+    SruRow<IO, CPT>::template store<FULL, NT>(qf, off, nv, of);
+    SruRow<IO, CPT>::template store<FULL, NT>(qr, off, nv, orr);
+    SruRow<IO, CPT>::template store<FULL, NT>(qx, off, nv, ox);
+    qf -= C;
+    qr -= C;
+    qx -= C;
+  }
+  if (dc0 && row0 == 0) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k)
+      if (k < nvc) dc0[c0i + k] = f[0][k] * x[k];
+  }
+  // per-tile bias partials, waves added in a fixed order
+  __syncthreads();  // every wave is past its last read of s.A / s.B
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    s.A[wid][off + k] = pf[k];
+    s.B[wid][off + k] = pr[k];
+  }
+  __syncthreads();
+  if (wid == 0) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      float sf = 0.0f, sr = 0.0f;
+      for (int w = 0; w < NW; ++w) {
+        sf += s.A[w][off + k];
+        sr += s.B[w][off + k];
+      }
+      if (k < nvc) {
+        part[(int64_t)tb * C + c0i + k] = sf;
+        part[((int64_t)ntb + tb) * C + c0i + k] = sr;
+      }
+    }
+  }
+}
+
+template <typename IO, int NW, int L, int CPT, bool NT>
+__global__ __launch_bounds__(NW* kWave) void k_sru_bwd(
+    const IO* __restrict__ zf, const IO* __restrict__ zr, const IO* __restrict__ zx,
+    const float* __restrict__ bias_f, const float* __restrict__ bias_r,
+    const float* __restrict__ c0p, const float* __restrict__ cs, const IO* __restrict__ gh,
+    const float* __restrict__ gcl, IO* __restrict__ dzf, IO* __restrict__ dzr,
+    IO* __restrict__ dzx, float* __restrict__ dc0, float* __restrict__ part, int64_t T,
+    int64_t C, int64_t D, int ncb, int ntb, int vec, uint64_t* __restrict__ status,
+    unsigned* __restrict__ tickets) {
+  constexpr int CW = kWave * CPT, TW = NW * L;
+  __shared__ ColShared<NW, CPT> s;
+  const bool multi = ntb > 1;
+  const int cb = (int)(blockIdx.x % (unsigned)ncb);
+  const int tb = col_ticket<NW, CPT>(multi, tickets, cb, s);
+  uint64_t* st = status + (int64_t)cb * ntb * CW;
+  const int ptb = ntb - 1 - tb;
+  const bool full = vec && ((int64_t)(ptb + 1) * TW <= T) && ((int64_t)(cb + 1) * CW <= C);
+  if (full)
+    sru_bwd_tile<IO, NW, L, CPT, true, NT>(zf, zr, zx, bias_f, bias_r, c0p, cs, gh, gcl, dzf, dzr,
+                                           dzx, dc0, part, T, C, D, tb, ntb, cb, multi, st, s);
+  else
+    sru_bwd_tile<IO, NW, L, CPT, false, NT>(zf, zr, zx, bias_f, bias_r, c0p, cs, gh, gcl, dzf,
+                                            dzr, dzx, dc0, part, T, C, D, tb, ntb, cb, multi, st,
+                                            s);
+}
+
+// Column sums of the two [R, D] partial matrices (blockIdx.y selects one):
+// out[d] = sum over rows of part[row * D + d].  Sixteen waves each add every
+// sixteenth row, then the sixteen partial sums are added in wave order, so the
+// result does not depend on scheduling.
+__global__ __launch_bounds__(1024) void k_col_sum(const float* __restrict__ part,
+                                                  float* __restrict__ out_f,
+                                                  float* __restrict__ out_r, int64_t R,
+                                                  int64_t D) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const int64_t d = (int64_t)blockIdx.x * kWave + lane;
+  const float* m = part + (int64_t)blockIdx.y * R * D;
+  __shared__ float red[16][kWave];
+  float acc = 0.0f;
+  if (d < D)
+    for (int64_t r = wid; r < R; r += 16) acc += m[r * D + d];
+  red[wid][lane] = acc;
+  __syncthreads();
+  if (wid == 0 && d < D) {
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) t += red[w][lane];
+    (blockIdx.y == 0 ? out_f : out_r)[d] = t;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -655,6 +888,7 @@ constexpr int kFwdNW = 8, kFwdL = 16, kFwdCPT = 1;
 constexpr int kBwdNW = 8, kBwdL = 16, kBwdCPT = 1;
 constexpr int kSruNW = 4, kSruL = 16, kSruCPT = 2;          // bf16 I/O
 constexpr int kSruF32NW = 8, kSruF32L = 8, kSruF32CPT = 2;  // fp32 I/O
+constexpr int kSruBwdNW = 8, kSruBwdL = 8, kSruBwdCPT = 2;  // backward, both I/O types
 }  // namespace
 
 ColPlan plan_scan_fwd_tbd(int64_t C, int64_t T) {
@@ -665,6 +899,12 @@ ColPlan plan_scan_fwd_tbd(int64_t C, int64_t T) {
 ColPlan plan_scan_bwd_tbd(int64_t C, int64_t T) {
   ColPlan p = plan_cols(C, T, kBwdNW, kBwdL, kBwdCPT);
   p.stream = 5 * C * T * 4 >= kStreamFootprint;  // a, h, g, grad_a, grad_b
+  return p;
+}
+ColPlan plan_sru_bwd(int64_t C, int64_t T, int io_dtype) {
+  ColPlan p = plan_cols(C, T, kSruBwdNW, kSruBwdL, kSruBwdCPT);
+  // z_f, z_r, z_x, grad_h, the three gradients (io type) and the cell states
+  p.stream = C * T * (7 * (io_dtype == 1 ? 2 : 4) + 4) >= kStreamFootprint;
   return p;
 }
 ColPlan plan_sru(int64_t C, int64_t T, int io_dtype) {
@@ -706,7 +946,8 @@ hipError_t launch_scan_bwd_tbd(const float* a, const float* h, const float* h0, 
 }
 
 hipError_t launch_sru_fwd(const void* zf, const void* zr, const void* zx, const float* bias_f,
-                          const float* bias_r, const float* c0, void* h, float* c_last, int64_t T,
+                          const float* bias_r, const float* c0, void* h, float* c_last,
+                          float* c_states, int64_t T,
                           int64_t B, int64_t D, int io_dtype, const ColPlan& p, int vec,
                           uint64_t* status, unsigned* tickets, hipStream_t stream) {
   const uint64_t grid = (uint64_t)p.ncb * (uint64_t)p.ntb;
@@ -714,7 +955,7 @@ hipError_t launch_sru_fwd(const void* zf, const void* zr, const void* zx, const 
 #define LRS_SRU(IO, NW_, L_, CPT_, NTF)                                                          \
   hipLaunchKernelGGL((k_sru_fwd<IO, NW_, L_, CPT_, NTF>), dim3((unsigned)grid), dim3(NW_ * kWave), \
                      0, stream, (const IO*)zf, (const IO*)zr, (const IO*)zx, bias_f, bias_r, c0,  \
-                     (IO*)h, c_last, T, C, D, (int)p.ncb, (int)p.ntb, vec, status, tickets)
+                     (IO*)h, c_last, c_states, T, C, D, (int)p.ncb, (int)p.ntb, vec, status, tickets)
   if (io_dtype == 1) {
     if (p.stream) LRS_SRU(uint16_t, kSruNW, kSruL, kSruCPT, true);
     else LRS_SRU(uint16_t, kSruNW, kSruL, kSruCPT, false);
@@ -723,6 +964,37 @@ hipError_t launch_sru_fwd(const void* zf, const void* zr, const void* zx, const 
     else LRS_SRU(float, kSruF32NW, kSruF32L, kSruF32CPT, false);
   }
 #undef LRS_SRU
+  return hipGetLastError();
+}
+
+hipError_t launch_sru_bwd(const void* zf, const void* zr, const void* zx, const float* bias_f,
+                          const float* bias_r, const float* c0, const float* cs, const void* gh,
+                          const float* gcl, void* dzf, void* dzr, void* dzx, float* dbf,
+                          float* dbr, float* dc0, float* part, int64_t T, int64_t B, int64_t D,
+                          int io_dtype, const ColPlan& p, int vec, uint64_t* status,
+                          unsigned* tickets, hipStream_t stream) {
+  const uint64_t grid = (uint64_t)p.ncb * (uint64_t)p.ntb;
+  const int64_t C = B * D;
+#define LRS_SRUB(IO, NTF)                                                                         \
+  hipLaunchKernelGGL((k_sru_bwd<IO, kSruBwdNW, kSruBwdL, kSruBwdCPT, NTF>), dim3((unsigned)grid), \
+                     dim3(kSruBwdNW * kWave), 0, stream, (const IO*)zf, (const IO*)zr,             \
+                     (const IO*)zx, bias_f, bias_r, c0, cs, (const IO*)gh, gcl, (IO*)dzf,          \
+                     (IO*)dzr, (IO*)dzx, dc0, part, T, C, D, (int)p.ncb, (int)p.ntb, vec, status, \
+                     tickets)
+  if (io_dtype == 1) {
+    if (p.stream) LRS_SRUB(uint16_t, true);
+    else LRS_SRUB(uint16_t, false);
+  } else {
+    if (p.stream) LRS_SRUB(float, true);
+    else LRS_SRUB(float, false);
+  }
+#undef LRS_SRUB
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // bias gradients: column sums over (time block, batch) rows of the partials
+  const int64_t R = p.ntb * B;
+  hipLaunchKernelGGL(k_col_sum, dim3((unsigned)((D + kWave - 1) / kWave), 2), dim3(1024), 0,
+                     stream, part, dbf, dbr, R, D);
   return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 TAGS = {"a": 1, "b": 2, "h0": 3, "g": 4, "zf": 5, "zr": 6, "zx": 7, "bias_f": 8,
-        "bias_r": 9, "w": 10, "u": 11, "h_init": 12}
+        "bias_r": 9, "w": 10, "u": 11, "h_init": 12, "gh": 13, "gcl": 14}
 
 
 def _rng(*key) -> np.random.Generator:
@@ -152,6 +152,15 @@ WORKLOADS = {
         {"zf": ("normal", 0.0, 1.0), "zr": ("normal", 0.0, 1.0), "zx": ("normal", 0.0, 1.0),
          "bias_f": ("normal", -1.0, 0.1), "bias_r": ("normal", -1.0, 0.1)},
         "SRU forward, bf16 I/O fp32 state, B=32 D=1024 T=2048, z~N(0,1), b_f,b_r~N(-1,0.1), c0=0"),
+    # SRU forward (saving the cell states) and backward at the SRU shape; the
+    # upstream gradient dL/dh ~ N(0,1) as for the scan workloads
+    "sru_fwd_bwd": Workload(
+        "sru_fwd_bwd", "sru", 32, 1024, 2048, 1006,
+        {"zf": ("normal", 0.0, 1.0), "zr": ("normal", 0.0, 1.0), "zx": ("normal", 0.0, 1.0),
+         "bias_f": ("normal", -1.0, 0.1), "bias_r": ("normal", -1.0, 0.1),
+         "gh": ("normal", 0.0, 1.0)},
+        "SRU forward + backward, bf16 I/O fp32 state, B=32 D=1024 T=2048, z~N(0,1), "
+        "b_f,b_r~N(-1,0.1), c0=0, dL/dh~N(0,1)"),
     # very long forward + backward scan, fp32
     "scan_long": Workload(
         "scan_long", "scan", 2, 256, 1 << 20, 1004,
@@ -198,6 +207,19 @@ def sru_inputs(w: Workload) -> dict:
         out[k] = np.ascontiguousarray(per_channel.T).reshape(w.T, w.B, w.D)
     out["bias_f"] = to_f32(params(w.seed, "bias_f", w.dists["bias_f"], (w.D,)))
     out["bias_r"] = to_f32(params(w.seed, "bias_r", w.dists["bias_r"], (w.D,)))
+    return out
+
+
+def sru_grad_inputs(w: Workload, with_gcl: bool = False) -> dict:
+    """Upstream gradients for the SRU backward: dL/dh as bf16 bit patterns
+    [T, B, D] uint16 (drawn like the pre-activations), and optionally
+    dL/dc_T as fp32 [B, D] from N(0,1)."""
+    ch = np.arange(w.C)
+    dist = w.dists.get("gh", ("normal", 0.0, 1.0))
+    per_channel = to_bf16_bits(series(w.seed, "gh", dist, ch, w.T))
+    out = {"gh": np.ascontiguousarray(per_channel.T).reshape(w.T, w.B, w.D)}
+    if with_gcl:
+        out["gcl"] = to_f32(params(w.seed, "gcl", ("normal", 0.0, 1.0), (w.C,))).reshape(w.B, w.D)
     return out
 
 

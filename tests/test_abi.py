@@ -32,7 +32,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     raw = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(raw, n), f"{n} declared in lrs.h but not exported"
@@ -71,6 +71,9 @@ def test_scan_workspace_queries(lib):
     assert lib.lrs_scan_workspace_bytes(1 << 40, 1 << 40, 2, 0, 0) == 0  # overflow
     assert lib.lrs_deer_workspace_bytes(16, 512, 8192, 5) >= 16 * 512 * 8192 * 4
     assert lib.lrs_deer_workspace_bytes(1, 1, 1, 0) == 0
+    # SRU backward: per-tile bias partials (2 floats per channel and time block)
+    assert lib.lrs_sru_bwd_workspace_bytes(2048, 32, 1024) >= 2 * 32 * 32768 * 4
+    assert lib.lrs_sru_bwd_workspace_bytes(-1, 1, 1) == 0
 
 
 def test_validation_before_any_launch(lib):
@@ -100,8 +103,26 @@ def test_validation_before_any_launch(lib):
     assert lib.lrs_scan_bwd(q(0x10000), q(0x20000), null, q(0x30000), q(0x10000), q(0x40000), null,
                             1, 1, 64, 0, 0, null, 0, null) == b.LRS_ERR_INVALID_ARG
     # SRU and DEER argument checks
-    assert lib.lrs_sru_fwd(p, p, p, p, p, null, p, null, 4, 1, 1, 3, null, 0, null) == b.LRS_ERR_INVALID_ARG
-    assert lib.lrs_sru_fwd(null, p, p, p, p, null, p, null, 4, 1, 1, 1, null, 0, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_sru_fwd(p, p, p, p, p, null, p, null, null, 4, 1, 1, 3, null, 0,
+                           null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_sru_fwd(null, p, p, p, p, null, p, null, null, 4, 1, 1, 1, null, 0,
+                           null) == b.LRS_ERR_INVALID_ARG
+    # the saved cell states must not overlap an input
+    assert lib.lrs_sru_fwd(q(0x10000), q(0x20000), q(0x30000), q(0x40000), q(0x50000), null,
+                           q(0x60000), null, q(0x10000), 4, 1, 1, 1, null, 0,
+                           null) == b.LRS_ERR_INVALID_ARG
+    # SRU backward: missing saved states, bad dtype, an output overlapping an input
+    assert lib.lrs_sru_bwd(p, p, p, p, p, null, null, p, null, p, p, p, p, p, null, 4, 1, 1, 1,
+                           null, 0, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_sru_bwd(p, p, p, p, p, null, p, p, null, p, p, p, p, p, null, 4, 1, 1, 7,
+                           null, 0, null) == b.LRS_ERR_INVALID_ARG
+    zs = [q(0x10000 * (i + 1)) for i in range(12)]
+    assert lib.lrs_sru_bwd(zs[0], zs[1], zs[2], zs[3], zs[4], null, zs[5], zs[6], null,
+                           zs[0], zs[7], zs[8], zs[9], zs[10], null, 4, 1, 1, 1, null, 0,
+                           null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_sru_bwd(zs[0], zs[1], zs[2], zs[3], zs[4], null, zs[5], zs[6], null,
+                           zs[11], zs[7], zs[8], zs[9], zs[10], null, 4, 1, 1, 1, null, 0,
+                           null) == b.LRS_ERR_WORKSPACE
     assert lib.lrs_deer_solve(p, p, null, null, p, 1, 1, 4, ctypes.c_float(1e-5), 0, None, None, None,
                               null, 0, null) == b.LRS_ERR_INVALID_ARG
     assert lib.lrs_deer_solve(q(0x10000), q(0x20000), null, null, q(0x90000), 1, 1, 4,
