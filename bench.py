@@ -37,6 +37,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
 # algorithmic bytes per element of each kernel (every input read once, every
 # output written once; per-channel vectors are negligible)
 BYTES_PER_ELEM = {"scan_fwd_f32": 12, "scan_bwd_f32": 20, "sru_fwd_bf16": 8,
+                  "sru_fwd_save_bf16": 12,  # + the fp32 cell states for the backward
+                  "sru_bwd_bf16": 18,       # z_f, z_r, z_x, dL/dh, c in; three gradients out
                   "deer_iter_first": 8, "deer_iter": 12}
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
 
@@ -69,7 +71,16 @@ def measured_traffic(workload: str, kernel_key: str):
 KERNEL_NAMES = {"scan_fwd_f32": ("k_scan_fwd_bdt", "k_scan_fwd_tbd"),
                 "scan_bwd_f32": ("k_scan_bwd_bdt", "k_scan_bwd_tbd"),
                 "sru_fwd_bf16": ("k_sru_fwd<unsigned short",),
+                "sru_fwd_save_bf16": ("k_sru_fwd<unsigned short",),
+                "sru_bwd_bf16": ("k_sru_bwd<unsigned short",),
                 "deer_solve": ("k_deer_iter",)}
+# entry points timed by each workload
+WORKLOAD_KERNELS = {"scan_fwd_small": ("scan_fwd_f32",),
+                    "scan_fwd_bwd": ("scan_fwd_f32", "scan_bwd_f32"),
+                    "scan_long": ("scan_fwd_f32", "scan_bwd_f32"),
+                    "sru_fwd": ("sru_fwd_bf16",),
+                    "sru_fwd_bwd": ("sru_fwd_save_bf16", "sru_bwd_bf16"),
+                    "deer": ("deer_solve",)}
 CALIB_NAME = "CUDAFunctor_add<float>"  # the stream reference kernel
 CALIB_READ = 2 * 4 * (1 << 26)
 CALIB_WRITE = 4 * (1 << 26)
@@ -133,10 +144,12 @@ def summarize(args):
     reset_us = float(reset[0]["AverageNs"]) / 1e3 if reset else 0.0
     reset_calls = int(reset[0]["Calls"]) if reset else 0
     ep = []
-    mains = [r for r in stats for key, pats in KERNEL_NAMES.items()
-             if key != "deer_solve" and any(p in r["Name"] for p in pats)]
+    keys = WORKLOAD_KERNELS[wl]
+    mains = [r for r in stats for key in keys
+             if key != "deer_solve" and any(p in r["Name"] for p in KERNEL_NAMES[key])]
     main_calls = sum(int(r["Calls"]) for r in mains)
-    for key, pats in KERNEL_NAMES.items():
+    for key in keys:
+        pats = KERNEL_NAMES[key]
         for r in stats:
             if any(p in r["Name"] for p in pats) and key != "deer_solve":
                 share = reset_calls / main_calls if main_calls else 0.0
@@ -160,18 +173,15 @@ def summarize(args):
               "|---|---|---|---|---|---|"]
     from linear_recurrence_scan_diagonal_amd import inputs as I
     w = I.WORKLOADS[wl]
-    algo = {"scan_fwd_f32": BYTES_PER_ELEM["scan_fwd_f32"] * w.N,
-            "scan_bwd_f32": BYTES_PER_ELEM["scan_bwd_f32"] * w.N,
-            "sru_fwd_bf16": BYTES_PER_ELEM["sru_fwd_bf16"] * w.N,
-            "deer_solve": None}
-    for key, pats in KERNEL_NAMES.items():
+    for key in WORKLOAD_KERNELS[wl]:
+        pats = KERNEL_NAMES[key]
         for pat in pats:
             f_ = per_dispatch("FETCH_SIZE", pat)
             w_ = per_dispatch("WRITE_SIZE", pat)
             if f_ is None or w_ is None or not factor["FETCH_SIZE"] or not factor["WRITE_SIZE"]:
                 continue
             hbm = f_ * factor["FETCH_SIZE"] + w_ * factor["WRITE_SIZE"]
-            a = algo[key]
+            a = BYTES_PER_ELEM[key] * w.N if key in BYTES_PER_ELEM else None
             if key == "deer_solve":
                 # one launch per Newton iteration: first iteration 8 B/elem, then 12 B/elem
                 n_it = len([r for r in pmc["FETCH_SIZE"] if pat in r["Kernel_Name"]])
@@ -200,7 +210,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="scan_fwd_bwd",
-                   choices=["scan_fwd_bwd", "scan_long", "sru_fwd", "deer", "scan_fwd_small"])
+                   choices=["scan_fwd_bwd", "scan_long", "sru_fwd", "sru_fwd_bwd", "deer",
+                            "scan_fwd_small"])
     p.add_argument("--layout", default="bdt", choices=["bdt", "tbd"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", action="store_true",
@@ -374,14 +385,31 @@ def main():
         ws = torch.empty(max(1, lrs.load().lrs_sru_workspace_bytes(T, B, D)), dtype=torch.uint8,
                          device=dev)
 
-        calls = {"sru_fwd_bf16": lambda: lrs.sru_fwd(z["zf"], z["zr"], z["zx"], bf, br, out=hs,
-                                                     workspace=ws)}
+        if w.name == "sru_fwd":
+            calls = {"sru_fwd_bf16": lambda: lrs.sru_fwd(z["zf"], z["zr"], z["zx"], bf, br, out=hs,
+                                                         workspace=ws)}
+        else:  # forward saving the cell states, then the backward
+            gh = torch.from_numpy(I.sru_grad_inputs(w)["gh"].view(np.int16)).view(
+                torch.bfloat16).to(dev)
+            cs = torch.empty((T, B, D), dtype=torch.float32, device=dev)
+            grads = (torch.empty_like(z["zf"]), torch.empty_like(z["zf"]), torch.empty_like(z["zf"]),
+                     torch.empty(D, dtype=torch.float32, device=dev),
+                     torch.empty(D, dtype=torch.float32, device=dev),
+                     torch.empty((B, D), dtype=torch.float32, device=dev))
+            wsb = torch.empty(max(1, lrs.load().lrs_sru_bwd_workspace_bytes(T, B, D)),
+                              dtype=torch.uint8, device=dev)
+            calls = {"sru_fwd_save_bf16": lambda: lrs.sru_fwd(z["zf"], z["zr"], z["zx"], bf, br,
+                                                              out=hs, workspace=ws, c_states=cs),
+                     "sru_bwd_bf16": lambda: lrs.sru_bwd(z["zf"], z["zr"], z["zx"], bf, br, cs, gh,
+                                                         out=grads, workspace=wsb)}
 
         def step():
-            calls["sru_fwd_bf16"]()
+            for fn in calls.values():
+                fn()
         kernels = list(calls)
         dtype = "bf16 I/O, f32 state"
-        config = {"workload": w.name, "B": B, "D": D, "T": T, "layout": "tbd"}
+        config = {"workload": w.name, "B": B, "D": D, "T": T, "layout": "tbd",
+                  "pass": "fwd+bwd" if w.name == "sru_fwd_bwd" else "fwd"}
     else:  # deer
         x = I.deer_inputs(w)
         wd = torch.from_numpy(x["w"]).to(dev)
@@ -456,8 +484,9 @@ def main():
         dom_bytes = BYTES_PER_ELEM[dom] * N
         dom_ms = per_kernel[dom]
     elif w.kind == "sru":
-        bytes_step = BYTES_PER_ELEM["sru_fwd_bf16"] * N
-        dom, dom_bytes, dom_ms = "sru_fwd_bf16", bytes_step, per_kernel["sru_fwd_bf16"]
+        bytes_step = sum(BYTES_PER_ELEM[k] * N for k in kernels)
+        dom = max(kernels, key=lambda k: per_kernel[k])
+        dom_bytes, dom_ms = BYTES_PER_ELEM[dom] * N, per_kernel[dom]
     else:
         iters = info["iters"]
         bytes_step = (BYTES_PER_ELEM["deer_iter_first"] + (iters - 1) * BYTES_PER_ELEM["deer_iter"]) * N
@@ -547,9 +576,15 @@ def cpu_baseline(w, args, np, I):
         s = I.sru_inputs(sub)
         z = [I.bf16_bits_to_f64(s[k]) for k in ("zf", "zr", "zx")]
 
+        with_bwd = w.name == "sru_fwd_bwd"
+        gh64 = I.bf16_bits_to_f64(I.sru_grad_inputs(sub)["gh"]) if with_bwd else None
+
         def once():
             oracle.sru_fwd(*z, s["bias_f"], s["bias_r"], nthreads=threads)
-        sample = f"B=1 of {w.B}, D={sub.D}, T={T} (same recipe)"
+            if with_bwd:
+                oracle.sru_bwd(*z, s["bias_f"], s["bias_r"], gh64, nthreads=threads)
+        sample = (f"B=1 of {w.B}, D={sub.D}, T={T} (same recipe), "
+                  f"fwd{'+bwd' if with_bwd else ''}")
         n_el = sub.N
     else:
         sub = I.scaled(w, B=1)

@@ -322,17 +322,20 @@ int lrs_sru_fwd(const void* z_f, const void* z_r, const void* z_x, const float* 
                                         B, D, io_dtype, p, vec, status, tickets, s));
 }
 
-// SRU backward: look-back state plus 2 * ntb * C floats of bias partials.
-static size_t sru_bwd_ws(const lrs::ColPlan& p, int64_t C) {
+// SRU backward: look-back state, 2 * ntb * C floats of per-tile bias partials
+// and the fp64 stage of their reduction.
+static size_t sru_bwd_ws(const lrs::ColPlan& p, int64_t B, int64_t D) {
+  const int64_t C = B * D;
   return lookback_bytes(lrs::col_status_words(p), p.ncb) +
-         align_up((size_t)(2 * p.ntb * C) * 4);
+         align_up((size_t)(2 * p.ntb * C) * 4) +
+         align_up((size_t)(2 * lrs::col_sum_blocks(p.ntb * B) * D) * 8);
 }
 
 size_t lrs_sru_bwd_workspace_bytes(int64_t T, int64_t B, int64_t D) {
   int64_t C, N;
   if (!shape_ok(B, D, T, &C, &N) || N == 0) return 0;
-  const size_t b1 = sru_bwd_ws(lrs::plan_sru_bwd(C, T, LRS_BF16), C);
-  const size_t b2 = sru_bwd_ws(lrs::plan_sru_bwd(C, T, LRS_F32), C);
+  const size_t b1 = sru_bwd_ws(lrs::plan_sru_bwd(C, T, LRS_BF16), B, D);
+  const size_t b2 = sru_bwd_ws(lrs::plan_sru_bwd(C, T, LRS_F32), B, D);
   return kAlign + (b1 > b2 ? b1 : b2);
 }
 
@@ -384,6 +387,7 @@ int lrs_sru_bwd(const void* z_f, const void* z_r, const void* z_x, const float* 
   if (!workspace || workspace_bytes < need) return LRS_ERR_WORKSPACE;
   Carve cv(align_ptr(workspace));
   float* part = cv.take<float>(2 * p.ntb * C);
+  double* acc = cv.take<double>(2 * lrs::col_sum_blocks(p.ntb * B) * D);
   uint64_t* status = nullptr;
   unsigned* tickets = nullptr;
   const int64_t nst = lrs::col_status_words(p);
@@ -398,8 +402,8 @@ int lrs_sru_bwd(const void* z_f, const void* z_r, const void* z_x, const float* 
   for (int i = 0; i < 7; ++i) vec = vec && aligned(io[i], rowbytes);
   return hip_status(lrs::launch_sru_bwd(z_f, z_r, z_x, bias_f, bias_r, c0, c_states, grad_h,
                                         grad_c_last, grad_zf, grad_zr, grad_zx, grad_bias_f,
-                                        grad_bias_r, grad_c0, part, T, B, D, io_dtype, p, vec,
-                                        status, tickets, s));
+                                        grad_bias_r, grad_c0, part, acc, T, B, D, io_dtype, p,
+                                        vec, status, tickets, s));
 }
 
 // ------------------------------------------------------------------- DEER

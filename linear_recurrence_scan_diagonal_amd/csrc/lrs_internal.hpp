@@ -84,12 +84,14 @@ hipError_t launch_sru_fwd(const void* zf, const void* zr, const void* zx, const 
                           hipStream_t stream);
 ColPlan plan_sru_bwd(int64_t C, int64_t T, int io_dtype);
 // Launches the backward kernel and the bias-gradient reduction; `part` holds
-// 2 * ntb * B * D floats of per-tile partial sums.
+// 2 * ntb * B * D floats of per-tile partial sums, `acc` 2 * col_sum_blocks(ntb
+// * B) * D doubles.
+int64_t col_sum_blocks(int64_t R);
 hipError_t launch_sru_bwd(const void* zf, const void* zr, const void* zx, const float* bias_f,
                           const float* bias_r, const float* c0, const float* cs, const void* gh,
                           const float* gcl, void* dzf, void* dzr, void* dzx, float* dbf,
-                          float* dbr, float* dc0, float* part, int64_t T, int64_t B, int64_t D,
-                          int io_dtype, const ColPlan& p, int vec, uint64_t* status,
+                          float* dbr, float* dc0, float* part, double* acc, int64_t T, int64_t B,
+                          int64_t D, int io_dtype, const ColPlan& p, int vec, uint64_t* status,
                           unsigned* tickets, hipStream_t stream);
 
 }  // namespace lrs

@@ -644,7 +644,7 @@ __global__ __launch_bounds__(NW* kWave) void k_sru_fwd(
 //   dzx = gh (1 - r) + gc (1 - f),   dzr = gh (tanh c - zx) r (1 - r),
 //   dzf = gc (c_{t-1} - zx) f (1 - f),   dc0 = f_1 gc_1.
 // r and tanh c are recomputed in the output pass instead of being kept.  Each
-// tile writes its per-channel sums of dzf and dzr over its steps; k_col_sum
+// tile writes its per-channel sums of dzf and dzr over its steps; a two-stage column sum
 // adds them up per feature for the bias gradients, in a fixed order.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float sru_sigmoid(float z, float nb) {
@@ -840,29 +840,52 @@ __global__ __launch_bounds__(NW* kWave) void k_sru_bwd(
                                             s);
 }
 
-// Column sums of the two [R, D] partial matrices (blockIdx.y selects one):
-// out[d] = sum over rows of part[row * D + d].  Sixteen waves each add every
-// sixteenth row, then the sixteen partial sums are added in wave order, so the
-// result does not depend on scheduling.
-__global__ __launch_bounds__(1024) void k_col_sum(const float* __restrict__ part,
-                                                  float* __restrict__ out_f,
-                                                  float* __restrict__ out_r, int64_t R,
-                                                  int64_t D) {
+// Column sums of the two [R, D] partial matrices, in two fixed-order stages
+// accumulated in fp64 (a bias gradient adds up B*T terms).  Stage 1: block
+// (x, y, z) adds rows [z*rpb, (z+1)*rpb) of matrix y for 64 columns (sixteen
+// waves take every sixteenth row, then their sums are added in wave order) and
+// writes one double per column to acc[(y * nrb + z) * D + d].  Stage 2 adds
+// the nrb doubles of each column in order.  Results do not depend on
+// scheduling.
+__global__ __launch_bounds__(1024) void k_col_sum_part(const float* __restrict__ part,
+                                                       double* __restrict__ acc, int64_t R,
+                                                       int64_t D, int64_t rpb) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   const int64_t d = (int64_t)blockIdx.x * kWave + lane;
   const float* m = part + (int64_t)blockIdx.y * R * D;
-  __shared__ float red[16][kWave];
-  float acc = 0.0f;
+  const int64_t r0 = (int64_t)blockIdx.z * rpb;
+  const int64_t r1 = r0 + rpb < R ? r0 + rpb : R;
+  __shared__ double red[16][kWave];
+  double a = 0.0;
   if (d < D)
-    for (int64_t r = wid; r < R; r += 16) acc += m[r * D + d];
-  red[wid][lane] = acc;
+    for (int64_t r = r0 + wid; r < r1; r += 16) a += (double)m[r * D + d];
+  red[wid][lane] = a;
   __syncthreads();
   if (wid == 0 && d < D) {
-    float t = 0.0f;
+    double t = 0.0;
 #pragma unroll
     for (int w = 0; w < 16; ++w) t += red[w][lane];
-    (blockIdx.y == 0 ? out_f : out_r)[d] = t;
+    acc[((int64_t)blockIdx.y * gridDim.z + blockIdx.z) * D + d] = t;
   }
+}
+
+__global__ __launch_bounds__(256) void k_col_sum_final(const double* __restrict__ acc,
+                                                       float* __restrict__ out_f,
+                                                       float* __restrict__ out_r, int nrb,
+                                                       int64_t D) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // 0 .. 2D-1
+  if (i >= 2 * D) return;
+  const int64_t y = i / D, d = i - y * D;
+  double t = 0.0;
+  for (int z = 0; z < nrb; ++z) t += acc[(y * nrb + z) * D + d];
+  (y == 0 ? out_f : out_r)[d] = (float)t;
+}
+
+// Stage-1 row blocks of the bias reduction for R rows.
+int64_t col_sum_blocks(int64_t R) {
+  int64_t nrb = (R + 63) / 64;
+  if (nrb > 4096) nrb = 4096;
+  return nrb < 1 ? 1 : nrb;
 }
 
 // ---------------------------------------------------------------------------
@@ -888,7 +911,7 @@ constexpr int kFwdNW = 8, kFwdL = 16, kFwdCPT = 1;
 constexpr int kBwdNW = 8, kBwdL = 16, kBwdCPT = 1;
 constexpr int kSruNW = 4, kSruL = 16, kSruCPT = 2;          // bf16 I/O
 constexpr int kSruF32NW = 8, kSruF32L = 8, kSruF32CPT = 2;  // fp32 I/O
-constexpr int kSruBwdNW = 8, kSruBwdL = 8, kSruBwdCPT = 2;  // backward, both I/O types
+constexpr int kSruBwdNW = 4, kSruBwdL = 8, kSruBwdCPT = 2;  // backward, both I/O types
 }  // namespace
 
 ColPlan plan_scan_fwd_tbd(int64_t C, int64_t T) {
@@ -970,8 +993,8 @@ hipError_t launch_sru_fwd(const void* zf, const void* zr, const void* zx, const 
 hipError_t launch_sru_bwd(const void* zf, const void* zr, const void* zx, const float* bias_f,
                           const float* bias_r, const float* c0, const float* cs, const void* gh,
                           const float* gcl, void* dzf, void* dzr, void* dzx, float* dbf,
-                          float* dbr, float* dc0, float* part, int64_t T, int64_t B, int64_t D,
-                          int io_dtype, const ColPlan& p, int vec, uint64_t* status,
+                          float* dbr, float* dc0, float* part, double* acc, int64_t T, int64_t B,
+                          int64_t D, int io_dtype, const ColPlan& p, int vec, uint64_t* status,
                           unsigned* tickets, hipStream_t stream) {
   const uint64_t grid = (uint64_t)p.ncb * (uint64_t)p.ntb;
   const int64_t C = B * D;
@@ -993,8 +1016,13 @@ hipError_t launch_sru_bwd(const void* zf, const void* zr, const void* zx, const 
   if (e != hipSuccess) return e;
   // bias gradients: column sums over (time block, batch) rows of the partials
   const int64_t R = p.ntb * B;
-  hipLaunchKernelGGL(k_col_sum, dim3((unsigned)((D + kWave - 1) / kWave), 2), dim3(1024), 0,
-                     stream, part, dbf, dbr, R, D);
+  const int64_t nrb = col_sum_blocks(R), rpb = (R + nrb - 1) / nrb;
+  hipLaunchKernelGGL(k_col_sum_part, dim3((unsigned)((D + kWave - 1) / kWave), 2, (unsigned)nrb),
+                     dim3(1024), 0, stream, part, acc, R, D, rpb);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_col_sum_final, dim3((unsigned)((2 * D + 255) / 256)), dim3(256), 0, stream,
+                     acc, dbf, dbr, (int)nrb, D);
   return hipGetLastError();
 }
 
