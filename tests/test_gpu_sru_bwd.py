@@ -76,3 +76,19 @@ def test_sru_bwd_deterministic_bias_sums():
     a, _ = sru_bwd_case(w, "f32")
     b, _ = sru_bwd_case(w, "f32")
     assert np.array_equal(a["dbf"], b["dbf"]) and np.array_equal(a["dbr"], b["dbr"])
+
+
+def test_sru_bwd_empty_time():
+    """T = 0: the bias gradients are empty sums and dL/dc0 = dL/dc_T."""
+    B, D = 2, 5
+    e = torch.empty((0, B, D), dtype=torch.bfloat16, device=DEV)
+    cs = torch.empty((0, B, D), dtype=torch.float32, device=DEV)
+    bias = torch.zeros(D, device=DEV)
+    gcl = torch.arange(B * D, dtype=torch.float32, device=DEV).reshape(B, D)
+    out = (torch.empty_like(e), torch.empty_like(e), torch.empty_like(e),
+           torch.full((D,), 7.0, device=DEV), torch.full((D,), 7.0, device=DEV),
+           torch.full((B, D), 7.0, device=DEV))
+    _, _, _, dbf, dbr, dc0 = lrs.sru_bwd(e, e, e, bias, bias, cs, e, grad_c_last=gcl, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(dbf, torch.zeros_like(dbf)) and torch.equal(dbr, torch.zeros_like(dbr))
+    assert torch.equal(dc0, gcl)
