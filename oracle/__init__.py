@@ -64,8 +64,10 @@ def _load():
                                     ctypes.c_double, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                                     _c_dp, ctypes.c_int]
     lib.lrs_oracle_sru_bwd.argtypes = [_c_dp] * 14 + [_i64, _i64, _i64, ctypes.c_int]
+    lib.lrs_oracle_deer_bwd.argtypes = [_c_dp] * 7 + [_i64, _i64, _i64, ctypes.c_int]
     for fn in (lib.lrs_oracle_scan_fwd, lib.lrs_oracle_scan_bwd, lib.lrs_oracle_sru_fwd,
-               lib.lrs_oracle_rnn_seq, lib.lrs_oracle_deer, lib.lrs_oracle_sru_bwd):
+               lib.lrs_oracle_rnn_seq, lib.lrs_oracle_deer, lib.lrs_oracle_sru_bwd,
+               lib.lrs_oracle_deer_bwd):
         fn.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -146,6 +148,21 @@ def sru_bwd(zf, zr, zx, bf, br, gh, c0=None, gcl=None, nthreads: int = 0):
                                       _ptr(out["dzx"]), _ptr(out["dbf"]), _ptr(out["dbr"]),
                                       _ptr(out["dc0"]), T, B, D, nthreads), "sru_bwd")
     return out
+
+
+def deer_bwd(w, h, g, h0=None, nthreads: int = 0):
+    """Adjoint of h_t = tanh(w h_{t-1} + u_t) at the solution h [B,D,T] for the
+    upstream gradient g.  Returns (du [B,D,T], dw [D], dh0 [B,D])."""
+    w, h, g, h0 = map(_f64, (w, h, g, h0))
+    B, D, T = h.shape
+    if g.shape != h.shape or w.shape != (D,):
+        raise ValueError("g must match h [B, D, T]; w must be [D]")
+    du = np.empty_like(h)
+    dw = np.empty(D)
+    dh0 = np.empty((B, D))
+    _check(_load().lrs_oracle_deer_bwd(_ptr(w), _ptr(h0), _ptr(h), _ptr(g), _ptr(du), _ptr(dw),
+                                       _ptr(dh0), B, D, T, nthreads), "deer_bwd")
+    return du, dw, dh0
 
 
 def rnn_seq(w, u, h0=None, nthreads: int = 0):

@@ -222,6 +222,49 @@ int lrs_oracle_sru_bwd(const double *zf, const double *zr, const double *zx,
     return fail ? ORACLE_ENOMEM : ORACLE_OK;
 }
 
+/* Adjoint of the nonlinear RNN h_t = tanh(w_d h_{t-1} + u_t) at a solution h
+ * (the DEER solve's result, [P4] core principle; the backward pass as a
+ * reverse-time scan, [P1] parallel-scan paragraph).  With s_t = 1 - h_t^2 and
+ * the upstream gradient g_t = dL/dh_t:
+ *   lam_T = g_T,   lam_t = g_t + w s_{t+1} lam_{t+1},
+ *   dL/du_t = s_t lam_t,   dL/dh0 = w s_1 lam_1,
+ *   dL/dw[d] = sum over b, t of s_t lam_t h_{t-1}   (h_0 = h0).
+ * u is not needed: at the solution, tanh(w h_{t-1} + u_t) = h_t.
+ * h, g, du are [B, D, T]; w is [D]; h0, dh0 are [B, D] or NULL. */
+int lrs_oracle_deer_bwd(const double *w, const double *h0, const double *h,
+                        const double *g, double *du, double *dw, double *dh0,
+                        int64_t B, int64_t D, int64_t T, int nthreads)
+{
+    if (B < 0 || D < 0 || T < 0) return ORACLE_EINVAL;
+    if (B * D * T > 0 && (!w || !h || !g || !du || !dw)) return ORACLE_EINVAL;
+    set_threads(nthreads);
+    const int64_t C = B * D;
+    double *part = calloc((size_t)(C > 0 ? C : 1), sizeof(double));
+    if (!part) return ORACLE_ENOMEM;
+#pragma omp parallel for schedule(static)
+    for (int64_t ch = 0; ch < C; ++ch) {
+        const double wd = w[ch % D];
+        const double *hc = h + ch * T, *gc = g + ch * T;
+        double *duc = du + ch * T;
+        double lam_next = 0.0, s_next = 0.0, acc = 0.0;
+        for (int64_t t = T - 1; t >= 0; --t) {
+            const double s = 1.0 - hc[t] * hc[t];
+            const double lam = gc[t] + (t + 1 < T ? wd * s_next * lam_next : 0.0);
+            const double hprev = t > 0 ? hc[t - 1] : (h0 ? h0[ch] : 0.0);
+            duc[t] = s * lam;
+            acc += s * lam * hprev;
+            lam_next = lam;
+            s_next = s;
+        }
+        if (dh0) dh0[ch] = T > 0 ? wd * s_next * lam_next : 0.0;
+        part[ch] = acc;
+    }
+    for (int64_t d = 0; d < D; ++d) dw[d] = 0.0;
+    for (int64_t ch = 0; ch < C; ++ch) dw[ch % D] += part[ch];  /* fixed order */
+    free(part);
+    return ORACLE_OK;
+}
+
 /* Plain sequential nonlinear RNN h_t = tanh(w_d * h_{t-1} + u_t): the ground
  * truth that the DEER iteration converges to ([P4] core principle).
  * u, h are [B, D, T]; w is [D]; h0 is [B, D] or NULL. */
