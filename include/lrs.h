@@ -209,6 +209,27 @@ LRS_API int lrs_deer_solve(const float *w, const float *u, const float *h0, cons
 LRS_API int lrs_deer_stats(const void *workspace, size_t workspace_bytes, int k_max,
                    int *iters_out, float *deltas_out, int *converged_out, void *stream);
 
+/* Workspace bytes needed by lrs_deer_bwd (0 for an invalid or empty shape). */
+LRS_API size_t lrs_deer_bwd_workspace_bytes(int64_t B, int64_t D, int64_t T);
+
+/* Backward of the nonlinear RNN h_t = tanh(w_d * h_{t-1} + u_t) at its
+ * solution h (the result of lrs_deer_solve; [P4] core principle: the solve
+ * returns the sequential solution, so its derivative is that of the
+ * recurrence), computed as a reverse-time scan ([P1] parallel-scan paragraph:
+ * the backward pass is also a log-depth scan).  With s_t = 1 - h_t^2 and
+ * g_t = dL/dh_t:
+ *   lam_T = g_T,  lam_t = g_t + w s_{t+1} lam_{t+1},
+ *   dL/du_t = s_t lam_t,  dL/dh0 = w s_1 lam_1,
+ *   dL/dw[d] = sum over batch and time of s_t lam_t h_{t-1}   (h_0 = h0).
+ * w: [D] fp32.  h0: [B,D] fp32 or NULL (zero).  h, grad_h: [B,D,T] fp32.
+ * grad_u: [B,D,T] output.  grad_w: [D] output (overwritten; summed in a fixed
+ * order, so results do not depend on scheduling).  grad_h0: [B,D] or NULL.
+ * No output may overlap an input or another output.  If the solve stopped at
+ * K_max before convergence, this is the derivative at the returned iterate. */
+LRS_API int lrs_deer_bwd(const float *w, const float *h0, const float *h, const float *grad_h,
+                 float *grad_u, float *grad_w, float *grad_h0, int64_t B, int64_t D, int64_t T,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,8 @@ DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 EXPORTS = ("lrs_status_string", "lrs_version", "lrs_scan_workspace_bytes", "lrs_scan_fwd",
            "lrs_scan_bwd", "lrs_sru_workspace_bytes", "lrs_sru_fwd", "lrs_deer_workspace_bytes",
-           "lrs_deer_solve", "lrs_deer_stats", "lrs_sru_bwd_workspace_bytes", "lrs_sru_bwd")
+           "lrs_deer_solve", "lrs_deer_stats", "lrs_sru_bwd_workspace_bytes", "lrs_sru_bwd",
+           "lrs_deer_bwd_workspace_bytes", "lrs_deer_bwd")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -78,6 +79,10 @@ def load():
     lib.lrs_deer_stats.argtypes = [_vp, _sz, _int, ctypes.POINTER(_int),
                                    ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_int), _vp]
     lib.lrs_deer_stats.restype = _int
+    lib.lrs_deer_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64]
+    lib.lrs_deer_bwd_workspace_bytes.restype = _sz
+    lib.lrs_deer_bwd.argtypes = [_vp] * 7 + [_i64, _i64, _i64, _vp, _sz, _vp]
+    lib.lrs_deer_bwd.restype = _int
     _lib = lib
     return lib
 
@@ -269,6 +274,27 @@ def deer_solve(w, u, h0=None, h_init=None, eps: float = 1e-5, k_max: int = 5, ou
     info = {"iters": iters.value, "deltas": [float(deltas[i]) for i in range(iters.value)],
             "converged": bool(conv.value), "status": int(rc)}
     return h, info
+
+
+def deer_bwd(w, h, grad_h, h0=None, want_grad_h0: bool = True, out=None, workspace=None):
+    """Backward of h_t = tanh(w h_{t-1} + u_t) at the solution h [B,D,T] (e.g.
+    deer_solve's result) for dL/dh = grad_h.  Returns (grad_u, grad_w, grad_h0)."""
+    lib = load()
+    B, D, T = _dims(h, "bdt")
+    _check_dev("h", h, torch.float32, h.shape)
+    _check_dev("grad_h", grad_h, torch.float32, h.shape)
+    _check_dev("w", w, torch.float32, (D,))
+    _check_dev("h0", h0, torch.float32, (B, D))
+    dev = h.device
+    if out is None:
+        out = (torch.empty_like(h), torch.empty(D, dtype=torch.float32, device=dev),
+               torch.empty((B, D), dtype=torch.float32, device=dev) if want_grad_h0 else None)
+    gu, gw, gh0 = out
+    nbytes = lib.lrs_deer_bwd_workspace_bytes(B, D, T)
+    ws = _workspace(nbytes, dev, workspace)
+    _call(lib.lrs_deer_bwd(_ptr(w), _ptr(h0), _ptr(h), _ptr(grad_h), _ptr(gu), _ptr(gw), _ptr(gh0),
+                           B, D, T, _ptr(ws), nbytes, _stream(dev)), "lrs_deer_bwd")
+    return gu, gw, gh0
 
 
 def deer_stats(workspace, k_max: int = 5):

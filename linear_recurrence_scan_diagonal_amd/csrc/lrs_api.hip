@@ -530,6 +530,67 @@ int lrs_deer_solve(const float* w, const float* u, const float* h0, const float*
   return read_deer_record(r, k_max, iters_out, deltas_out, converged_out, s);
 }
 
+// DEER backward: look-back state, nchunk * C floats of dL/dw partials and the
+// fp64 stage of their reduction.
+size_t lrs_deer_bwd_workspace_bytes(int64_t B, int64_t D, int64_t T) {
+  int64_t C, N;
+  if (!shape_ok(B, D, T, &C, &N) || N == 0) return 0;
+  const lrs::RowPlan p = lrs::plan_deer_bwd_rows(C, T);
+  size_t bytes = kAlign + align_up((size_t)(p.nchunk * C) * 4) +
+                 align_up((size_t)(lrs::col_sum_blocks(p.nchunk * B) * D) * 8);
+  if (p.nchunk > 1) bytes += lookback_bytes(C * p.nchunk, C);
+  return bytes;
+}
+
+int lrs_deer_bwd(const float* w, const float* h0, const float* h, const float* grad_h,
+                 float* grad_u, float* grad_w, float* grad_h0, int64_t B, int64_t D, int64_t T,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  int64_t C, N;
+  if (!shape_ok(B, D, T, &C, &N)) return LRS_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (N == 0) {
+    // no steps: dL/dw is an empty sum and nothing depends on h0
+    int rc = LRS_OK;
+    if (D > 0 && grad_w) rc = hip_status(lrs::launch_copy_or_zero(grad_w, nullptr, D, s));
+    if (rc == LRS_OK && T == 0 && C > 0 && grad_h0)
+      rc = hip_status(lrs::launch_copy_or_zero(grad_h0, nullptr, C, s));
+    return rc;
+  }
+  if (!w || !h || !grad_h || !grad_u || !grad_w) return LRS_ERR_INVALID_ARG;
+  if (!aligned(w, 4) || !aligned(h, 4) || !aligned(grad_h, 4) || !aligned(grad_u, 4) ||
+      !aligned(grad_w, 4) || (h0 && !aligned(h0, 4)) || (grad_h0 && !aligned(grad_h0, 4)))
+    return LRS_ERR_INVALID_ARG;
+  const size_t nb = (size_t)N * 4, cb = (size_t)C * 4, db = (size_t)D * 4;
+  const void* ins[4] = {w, h0, h, grad_h};
+  const size_t insz[4] = {db, cb, nb, nb};
+  const void* outs[3] = {grad_u, grad_w, grad_h0};
+  const size_t outsz[3] = {nb, db, cb};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 4; ++i)
+      if (overlap(outs[o], outsz[o], ins[i], insz[i])) return LRS_ERR_INVALID_ARG;
+    for (int o2 = o + 1; o2 < 3; ++o2)
+      if (overlap(outs[o], outsz[o], outs[o2], outsz[o2])) return LRS_ERR_INVALID_ARG;
+  }
+  const lrs::RowPlan p = lrs::plan_deer_bwd_rows(C, T);
+  if (!grid_ok(C * p.nchunk, p.threads())) return LRS_ERR_UNSUPPORTED;
+  const size_t need = lrs_deer_bwd_workspace_bytes(B, D, T);
+  if (!workspace || workspace_bytes < need) return LRS_ERR_WORKSPACE;
+  Carve cv(align_ptr(workspace));
+  float* part = cv.take<float>(p.nchunk * C);
+  double* acc = cv.take<double>(lrs::col_sum_blocks(p.nchunk * B) * D);
+  uint64_t* status = nullptr;
+  unsigned* tickets = nullptr;
+  if (p.nchunk > 1) {
+    status = cv.take<uint64_t>(C * p.nchunk);
+    tickets = cv.take<unsigned>(C);
+    const int rc = hip_status(lrs::launch_reset(status, C * p.nchunk, tickets, C, nullptr, 0, s));
+    if (rc != LRS_OK) return rc;
+  }
+  const int vec = aligned(h, 16) && aligned(grad_h, 16) && aligned(grad_u, 16) && (T % 4 == 0);
+  return hip_status(lrs::launch_deer_bwd(w, h, h0, grad_h, grad_u, grad_w, grad_h0, part, acc, B,
+                                         D, T, p, vec, status, tickets, s));
+}
+
 int lrs_deer_stats(const void* workspace, size_t workspace_bytes, int k_max, int* iters_out,
                    float* deltas_out, int* converged_out, void* stream) {
   if (k_max < 1 || k_max > 1000000) return LRS_ERR_INVALID_ARG;

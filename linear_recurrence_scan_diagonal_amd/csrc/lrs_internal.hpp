@@ -28,6 +28,7 @@ struct RowPlan {
 RowPlan plan_scan_fwd_rows(int64_t C, int64_t T);
 RowPlan plan_scan_bwd_rows(int64_t C, int64_t T);
 RowPlan plan_deer_rows(int64_t C, int64_t T);
+RowPlan plan_deer_bwd_rows(int64_t C, int64_t T);
 
 // Feature-contiguous kernels: blocks of 64*cpt channels x nw*l steps.
 struct ColPlan {
@@ -65,6 +66,12 @@ hipError_t launch_deer_finish(const uint32_t* delta_bits, uint32_t* delta_out, i
                               int k_max, float eps, hipStream_t stream);
 hipError_t launch_deer_select(const float* p0, const float* p1, float* h, int64_t n,
                               const int* rec, hipStream_t stream);
+// Adjoint of the nonlinear RNN at its solution: the reverse scan kernel, then
+// dL/dw from `part` (nchunk * B * D floats) via launch_col_sums.
+hipError_t launch_deer_bwd(const float* w, const float* h, const float* h0, const float* g,
+                           float* du, float* dw, float* dh0, float* part, double* acc, int64_t B,
+                           int64_t D, int64_t T, const RowPlan& p, int vec, uint64_t* status,
+                           unsigned* tickets, hipStream_t stream);
 hipError_t launch_deer_iter(const float* w, const float* u, const float* y, const float* h0,
                             float* yn, int64_t C, int64_t D, int64_t T, const RowPlan& p, int vec,
                             uint64_t* status, unsigned* tickets, uint32_t* delta_bits,
@@ -83,10 +90,16 @@ hipError_t launch_sru_fwd(const void* zf, const void* zr, const void* zx, const 
                           const ColPlan& p, int vec, uint64_t* status, unsigned* tickets,
                           hipStream_t stream);
 ColPlan plan_sru_bwd(int64_t C, int64_t T, int io_dtype);
-// Launches the backward kernel and the bias-gradient reduction; `part` holds
-// 2 * ntb * B * D floats of per-tile partial sums, `acc` 2 * col_sum_blocks(ntb
-// * B) * D doubles.
+// Per-feature parameter gradients: column sums of nmat consecutive [R, D]
+// matrices of partial sums (R = partials per feature), accumulated in fp64 in a
+// fixed order into out0 (and out1 for nmat = 2).  `acc` holds
+// nmat * col_sum_blocks(R) * D doubles.
 int64_t col_sum_blocks(int64_t R);
+hipError_t launch_col_sums(const float* part, int nmat, int64_t R, int64_t D, double* acc,
+                           float* out0, float* out1, hipStream_t stream);
+
+// Launches the SRU backward kernel and the bias-gradient reduction; `part`
+// holds 2 * ntb * B * D floats of per-tile partial sums.
 hipError_t launch_sru_bwd(const void* zf, const void* zr, const void* zx, const float* bias_f,
                           const float* bias_r, const float* c0, const float* cs, const void* gh,
                           const float* gcl, void* dzf, void* dzr, void* dzx, float* dbf,

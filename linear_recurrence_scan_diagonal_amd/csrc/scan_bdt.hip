@@ -313,6 +313,140 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_bwd_bdt(
 }
 
 // ---------------------------------------------------------------------------
+// Adjoint of the nonlinear RNN h_t = tanh(w h_{t-1} + u_t) at its solution h
+// (the DEER solve's result): with s_t = 1 - h_t^2, the same reverse-time scan
+// as k_scan_bwd_bdt with coefficient a_t = w s_t built from h on the fly,
+//   lam_t = g_t + a_{t+1} lam_{t+1},   dL/du_t = s_t lam_t,   dL/dh0 = a_1 lam_1,
+// and dL/dw[d] = sum over the batch and time of s_t lam_t h_{t-1}: each chunk
+// writes its channel's partial sum (waves added in a fixed order), and a
+// two-stage column sum over (chunk, batch) rows finishes it.  Reads h and g,
+// writes dL/du: 12 bytes per element.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  // fixed butterfly order: every lane ends with the same, reproducible sum
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+template <int NW, int R, bool NT, bool FULL>
+__device__ __forceinline__ void deer_bwd_chunk(const float* __restrict__ w,
+                                               const float* __restrict__ h,
+                                               const float* __restrict__ h0,
+                                               const float* __restrict__ g,
+                                               float* __restrict__ du, float* __restrict__ dh0,
+                                               float* __restrict__ part, int64_t T, int64_t C,
+                                               int64_t D, int64_t ch, int c, int pc, bool multi,
+                                               int vec, uint64_t* st, BlockShared<NW>& s) {
+  constexpr int S = R * 256, CH = NW * S;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const int64_t wend = (int64_t)(pc + 1) * CH - (int64_t)wid * S;  // physical end of the segment
+  const int64_t wbeg = wend - S;
+  const float wd = w[ch % D];
+  const float* hrow = h + ch * T;
+  const float* grow = g + ch * T;
+  // a_p = w (1 - h_p^2) for p < T and 0 at and past T (no step after the end)
+  auto coef = [&](float hv, int64_t p) {
+    return (FULL || p < T) ? wd * __builtin_fmaf(-hv, hv, 1.0f) : 0.0f;
+  };
+  const int64_t pb = wend - 256 + 4 * (kWave - 1 - lane);  // this lane's group in row 0
+  float4 h4[R], g4[R], a4[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    h4[r] = ld4<FULL, NT>(hrow, pb - r * 256, T, vec, 0.0f);
+    g4[r] = ld4<FULL, NT>(grow, pb - r * 256, T, vec, 0.0f);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t p = pb - r * 256;
+    a4[r] = make_float4(coef(h4[r].x, p), coef(h4[r].y, p + 1), coef(h4[r].z, p + 2),
+                        coef(h4[r].w, p + 3));
+  }
+  const float x0h = h0 ? h0[ch] : 0.0f;
+  // wave-edge halos (uniform): coefficient just past the segment, h just before it
+  const float a_after = (wend < T) ? coef(hrow[wend], wend) : 0.0f;
+  const float h_before = (wbeg > 0) ? ((wbeg - 1 < T) ? hrow[wbeg - 1] : 0.0f) : x0h;
+
+  float an[R], hp[R], Ai[R], Bi[R], RA[R], RB[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float fa = (r > 0) ? readlane_f(a4[r - 1].x, kWave - 1) : a_after;
+    an[r] = wave_shift_up(a4[r].x, fa);
+    const float fh = (r < R - 1) ? readlane_f(h4[r + 1].w, 0) : h_before;
+    hp[r] = wave_shift_down(h4[r].w, fh);  // h at the group's first step - 1
+    float A = an[r], B = g4[r].w;
+    B = __builtin_fmaf(a4[r].w, B, g4[r].z); A = A * a4[r].w;
+    B = __builtin_fmaf(a4[r].z, B, g4[r].y); A = A * a4[r].z;
+    B = __builtin_fmaf(a4[r].y, B, g4[r].x); A = A * a4[r].y;
+    wave_scan(A, B);
+    Ai[r] = A; Bi[r] = B;
+    RA[r] = readlane_f(A, kWave - 1);
+    RB[r] = readlane_f(B, kWave - 1);
+  }
+  float WA, WB, PA, PB, TA, TB;
+  chain_rows<R>(RA, RB, WA, WB);
+  block_combine<NW>(WA, WB, s, PA, PB, TA, TB);
+  const float x_in = chunk_carry<NW>(multi, c, TA, TB, 0.0f, st, s);
+
+  float xr = __builtin_fmaf(PA, x_in, PB);
+  float* durow = du + ch * T;
+  // this lane's part of sum s_t lam_t h_{t-1}, in fp64: a chunk adds up to
+  // 16384 terms before the per-feature sum over the batch
+  double acc = 0.0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float x = wave_shift_up(__builtin_fmaf(Ai[r], xr, Bi[r]), xr);  // lam past the group
+    const float l3 = __builtin_fmaf(an[r], x, g4[r].w);
+    const float l2 = __builtin_fmaf(a4[r].w, l3, g4[r].z);
+    const float l1 = __builtin_fmaf(a4[r].z, l2, g4[r].y);
+    const float l0 = __builtin_fmaf(a4[r].y, l1, g4[r].x);
+    const float u0 = __builtin_fmaf(-h4[r].x, h4[r].x, 1.0f) * l0;
+    const float u1 = __builtin_fmaf(-h4[r].y, h4[r].y, 1.0f) * l1;
+    const float u2 = __builtin_fmaf(-h4[r].z, h4[r].z, 1.0f) * l2;
+    const float u3 = __builtin_fmaf(-h4[r].w, h4[r].w, 1.0f) * l3;
+    const int64_t p = pb - r * 256;
+    st4<FULL, NT>(durow, p, T, vec, make_float4(u0, u1, u2, u3));
+    // steps at or past T have lam = 0, so they add nothing
+    acc += (double)(u0 * hp[r]) + (double)(u1 * h4[r].x) + (double)(u2 * h4[r].y) +
+           (double)(u3 * h4[r].z);
+    if (dh0 && p == 0) dh0[ch] = a4[r].x * l0;
+    xr = __builtin_fmaf(RA[r], xr, RB[r]);
+  }
+  // per-chunk partial of dL/dw: lanes by a fixed butterfly, waves in order
+  acc = wave_sum_f64(acc);
+  __shared__ double wsum[NW];
+  if (lane == 0) wsum[wid] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) t += wsum[i];
+    part[(int64_t)c * C + ch] = (float)t;
+  }
+}
+
+template <int NW, int R, bool NT = false, bool MULTI = false>
+__global__ __launch_bounds__(NW* kWave) void k_deer_bwd(
+    const float* __restrict__ w, const float* __restrict__ h, const float* __restrict__ h0,
+    const float* __restrict__ g, float* __restrict__ du, float* __restrict__ dh0,
+    float* __restrict__ part, int64_t T, int64_t C, int64_t D, int nchunk, int vec,
+    uint64_t* __restrict__ status, unsigned* __restrict__ tickets) {
+  constexpr int CH = NW * R * 256;
+  __shared__ BlockShared<NW> s;
+  constexpr bool multi = MULTI;
+  const int64_t ch = multi ? chunk_channel(blockIdx.x, C, nchunk) : (int64_t)blockIdx.x;
+  const int c = chunk_ticket<NW>(multi, tickets, ch, s);
+  const int pc = nchunk - 1 - c;
+  uint64_t* st = status + ch * nchunk;
+  if (vec && (int64_t)(pc + 1) * CH <= T)
+    deer_bwd_chunk<NW, R, NT, true>(w, h, h0, g, du, dh0, part, T, C, D, ch, c, pc, multi, vec,
+                                    st, s);
+  else
+    deer_bwd_chunk<NW, R, NT, false>(w, h, h0, g, du, dh0, part, T, C, D, ch, c, pc, multi, vec,
+                                     st, s);
+}
+
+// ---------------------------------------------------------------------------
 // DEER iteration: from the iterate y (NULL = all zero) build
 //   z_t = tanh(w y_{t-1} + u_t), J_t = w (1 - z_t^2), rhs_t = z_t - J_t y_{t-1}
 // (DEER page, core principle: evaluate f and its Jacobian, multiply by the
@@ -614,6 +748,12 @@ RowPlan plan_scan_bwd_rows(int64_t C, int64_t T) {
   return p;
 }
 
+RowPlan plan_deer_bwd_rows(int64_t C, int64_t T) {
+  RowPlan p = pick(T, kScanSingle, kScanBwdMulti);
+  p.stream = 3 * C * T * 4 >= kStreamFootprint;  // h, g, grad_u
+  return p;
+}
+
 RowPlan plan_deer_rows(int64_t C, int64_t T) {
   RowPlan p = pick(T, kDeerSingle, kDeerMulti);
   p.stream = 3 * C * T * 4 >= kStreamFootprint;  // u, y, y'
@@ -687,6 +827,38 @@ hipError_t launch_scan_bwd_bdt(const float* a, const float* h, const float* h0, 
   }
 #undef LRS_BWD
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_deer_bwd(const float* w, const float* h, const float* h0, const float* g,
+                           float* du, float* dw, float* dh0, float* part, double* acc, int64_t B,
+                           int64_t D, int64_t T, const RowPlan& p, int vec, uint64_t* status,
+                           unsigned* tickets, hipStream_t stream) {
+  const int64_t C = B * D;
+  const dim3 grid((unsigned)((uint64_t)C * (uint64_t)p.nchunk));
+  hipError_t e = hipErrorInvalidValue;
+#define LRS_DB(NTF, M) hipLaunchKernelGGL((k_deer_bwd<NW, RR, NTF, M>), grid, dim3(NW * kWave), 0, \
+                                          stream, w, h, h0, g, du, dh0, part, T, C, D,         \
+                                          (int)p.nchunk, vec, status, tickets)
+#define LRS_DB_CASE(NW_, R_, ...) \
+  if (p.nw == NW_ && p.r == R_) { constexpr int NW = NW_, RR = R_; __VA_ARGS__; e = hipGetLastError(); }
+  if (p.nchunk > 1) {
+    if (p.stream) { LRS_DB_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_DB(true, true)) }
+    else { LRS_DB_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_DB(false, true)) }
+  } else if (p.stream) {
+    LRS_DB_CASE(1, 1, LRS_DB(true, false)) else LRS_DB_CASE(2, 1, LRS_DB(true, false))
+    else LRS_DB_CASE(4, 1, LRS_DB(true, false)) else LRS_DB_CASE(8, 1, LRS_DB(true, false))
+    else LRS_DB_CASE(8, 2, LRS_DB(true, false))
+    else LRS_DB_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_DB(true, false))
+  } else {
+    LRS_DB_CASE(1, 1, LRS_DB(false, false)) else LRS_DB_CASE(2, 1, LRS_DB(false, false))
+    else LRS_DB_CASE(4, 1, LRS_DB(false, false)) else LRS_DB_CASE(8, 1, LRS_DB(false, false))
+    else LRS_DB_CASE(8, 2, LRS_DB(false, false))
+    else LRS_DB_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_DB(false, false))
+  }
+#undef LRS_DB_CASE
+#undef LRS_DB
+  if (e != hipSuccess) return e;
+  return launch_col_sums(part, 1, p.nchunk * B, D, acc, dw, nullptr, stream);
 }
 
 hipError_t launch_deer_finish(const uint32_t* delta_bits, uint32_t* delta_out, int* rec,

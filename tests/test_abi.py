@@ -32,7 +32,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     raw = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(raw, n), f"{n} declared in lrs.h but not exported"
@@ -74,6 +74,9 @@ def test_scan_workspace_queries(lib):
     # SRU backward: per-tile bias partials (2 floats per channel and time block)
     assert lib.lrs_sru_bwd_workspace_bytes(2048, 32, 1024) >= 2 * 32 * 32768 * 4
     assert lib.lrs_sru_bwd_workspace_bytes(-1, 1, 1) == 0
+    # DEER backward: one dL/dw partial per channel and chunk
+    assert lib.lrs_deer_bwd_workspace_bytes(16, 512, 8192) >= 16 * 512 * 4
+    assert lib.lrs_deer_bwd_workspace_bytes(1, 1, -3) == 0
 
 
 def test_validation_before_any_launch(lib):
@@ -129,6 +132,13 @@ def test_validation_before_any_launch(lib):
                               ctypes.c_float(1e-5), 5, None, None, None, null, 0,
                               null) == b.LRS_ERR_WORKSPACE
     assert lib.lrs_deer_stats(null, 0, 5, None, None, None, null) == b.LRS_ERR_WORKSPACE
+    # DEER backward: missing h, an output overlapping an input, missing workspace
+    assert lib.lrs_deer_bwd(p, null, null, p, p, p, null, 1, 1, 4, null, 0,
+                            null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_deer_bwd(q(0x10000), null, q(0x20000), q(0x30000), q(0x20000), q(0x40000), null,
+                            1, 1, 4, null, 0, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_deer_bwd(q(0x10000), null, q(0x20000), q(0x30000), q(0x50000), q(0x40000), null,
+                            1, 1, 4, null, 0, null) == b.LRS_ERR_WORKSPACE
     assert lib.lrs_deer_stats(p, 1 << 20, 0, None, None, None, null) == b.LRS_ERR_INVALID_ARG
     assert lib.lrs_deer_stats(p, 64, 5, None, None, None, null) == b.LRS_ERR_WORKSPACE
 
