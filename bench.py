@@ -39,7 +39,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
 BYTES_PER_ELEM = {"scan_fwd_f32": 12, "scan_bwd_f32": 20, "sru_fwd_bf16": 8,
                   "sru_fwd_save_bf16": 12,  # + the fp32 cell states for the backward
                   "sru_bwd_bf16": 18,       # z_f, z_r, z_x, dL/dh, c in; three gradients out
-                  "deer_iter_first": 8, "deer_iter": 12}
+                  "deer_iter_first": 8, "deer_iter": 12,
+                  "deer_bwd_f32": 12}       # h, dL/dh in; dL/du out
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
 
 
@@ -73,14 +74,16 @@ KERNEL_NAMES = {"scan_fwd_f32": ("k_scan_fwd_bdt", "k_scan_fwd_tbd"),
                 "sru_fwd_bf16": ("k_sru_fwd<unsigned short",),
                 "sru_fwd_save_bf16": ("k_sru_fwd<unsigned short",),
                 "sru_bwd_bf16": ("k_sru_bwd<unsigned short",),
-                "deer_solve": ("k_deer_iter",)}
+                "deer_solve": ("k_deer_iter",),
+                "deer_bwd_f32": ("k_deer_bwd",)}
 # entry points timed by each workload
 WORKLOAD_KERNELS = {"scan_fwd_small": ("scan_fwd_f32",),
                     "scan_fwd_bwd": ("scan_fwd_f32", "scan_bwd_f32"),
                     "scan_long": ("scan_fwd_f32", "scan_bwd_f32"),
                     "sru_fwd": ("sru_fwd_bf16",),
                     "sru_fwd_bwd": ("sru_fwd_save_bf16", "sru_bwd_bf16"),
-                    "deer": ("deer_solve",)}
+                    "deer": ("deer_solve",),
+                    "deer_fwd_bwd": ("deer_solve", "deer_bwd_f32")}
 CALIB_NAME = "CUDAFunctor_add<float>"  # the stream reference kernel
 CALIB_READ = 2 * 4 * (1 << 26)
 CALIB_WRITE = 4 * (1 << 26)
@@ -211,7 +214,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="scan_fwd_bwd",
                    choices=["scan_fwd_bwd", "scan_long", "sru_fwd", "sru_fwd_bwd", "deer",
-                            "scan_fwd_small"])
+                            "deer_fwd_bwd", "scan_fwd_small"])
     p.add_argument("--layout", default="bdt", choices=["bdt", "tbd"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", action="store_true",
@@ -427,13 +430,22 @@ def main():
         def solve_sync():
             return lrs.deer_solve(wd, u, h0, None, eps=1e-5, k_max=5, out=hd, workspace=ws)
         calls = {"deer_solve": solve_async}
+        if w.name == "deer_fwd_bwd":  # then the backward at the solution
+            gd = torch.from_numpy(I.series(w.seed, "g", w.dists["g"], np.arange(w.C), T,
+                                           np.float32).reshape(B, D, T)).to(dev)
+            dgrads = (torch.empty_like(u), torch.empty(D, dtype=torch.float32, device=dev),
+                      torch.empty((B, D), dtype=torch.float32, device=dev))
+            wsd = torch.empty(max(1, lrs.load().lrs_deer_bwd_workspace_bytes(B, D, T)),
+                              dtype=torch.uint8, device=dev)
+            calls["deer_bwd_f32"] = lambda: lrs.deer_bwd(wd, hd, gd, h0, out=dgrads, workspace=wsd)
 
         def step():
-            solve_async()
-        kernels = ["deer_solve"]
+            for fn in calls.values():
+                fn()
+        kernels = list(calls)
         dtype = "f32"
         config = {"workload": w.name, "B": B, "D": D, "T": T, "layout": "bdt", "eps": 1e-5,
-                  "k_max": 5}
+                  "k_max": 5, "pass": "solve+bwd" if w.name == "deer_fwd_bwd" else "solve"}
 
     for _ in range(args.warmup):
         step()
@@ -489,8 +501,9 @@ def main():
         dom_bytes, dom_ms = BYTES_PER_ELEM[dom] * N, per_kernel[dom]
     else:
         iters = info["iters"]
-        bytes_step = (BYTES_PER_ELEM["deer_iter_first"] + (iters - 1) * BYTES_PER_ELEM["deer_iter"]) * N
-        dom, dom_bytes, dom_ms = "deer_solve", bytes_step, per_kernel["deer_solve"]
+        solve_bytes = (BYTES_PER_ELEM["deer_iter_first"] + (iters - 1) * BYTES_PER_ELEM["deer_iter"]) * N
+        bytes_step = solve_bytes + sum(BYTES_PER_ELEM[k] * N for k in kernels if k != "deer_solve")
+        dom, dom_bytes, dom_ms = "deer_solve", solve_bytes, per_kernel["deer_solve"]
         extra["deer_iters"] = iters
         extra["deer_deltas"] = info["deltas"]
     achieved = dom_bytes / (dom_ms / 1e3) / 1e9
@@ -591,9 +604,16 @@ def cpu_baseline(w, args, np, I):
         x = I.deer_inputs(sub)
         u = x["u"].reshape(1, sub.D, T).astype(np.float64)
 
+        with_bwd = w.name == "deer_fwd_bwd"
+        g64 = (I.series(w.seed, "g", w.dists["g"], np.arange(sub.C), T).reshape(1, sub.D, T)
+               if with_bwd else None)
+
         def once():
-            oracle.deer(x["w"], u, None, eps=1e-5, k_max=5, nthreads=threads)
-        sample = f"B=1 of {w.B}, D={sub.D}, T={T}, eps=1e-5, K_max=5"
+            hs, _, _ = oracle.deer(x["w"], u, None, eps=1e-5, k_max=5, nthreads=threads)
+            if with_bwd:
+                oracle.deer_bwd(x["w"], hs, g64, nthreads=threads)
+        sample = (f"B=1 of {w.B}, D={sub.D}, T={T}, eps=1e-5, K_max=5"
+                  f"{', solve+bwd' if with_bwd else ''}")
         n_el = sub.N
     reps, t_total = 0, 0.0
     while t_total < args.cpu_seconds and reps < 10000:

@@ -174,6 +174,13 @@ WORKLOADS = {
         {"w": ("uniform", -0.9, 0.9), "u": ("normal", 0.0, 1.0), "h0": ("const", 0.0, 0.0)},
         "DEER Newton solve, fp32, B=16 D=512 T=8192, w~U(-0.9,0.9) per feature, u~N(0,1), "
         "h0=0, h_init=0, eps=1e-5, K_max=5"),
+    # the DEER solve followed by the backward at its solution, dL/dh ~ N(0,1)
+    "deer_fwd_bwd": Workload(
+        "deer_fwd_bwd", "deer", 16, 512, 8192, 1007,
+        {"w": ("uniform", -0.9, 0.9), "u": ("normal", 0.0, 1.0), "h0": ("const", 0.0, 0.0),
+         "g": ("normal", 0.0, 1.0)},
+        "DEER solve + backward, fp32, B=16 D=512 T=8192, as the DEER workload plus "
+        "dL/dh~N(0,1)"),
 }
 
 
