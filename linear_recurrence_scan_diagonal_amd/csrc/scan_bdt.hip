@@ -701,15 +701,17 @@ __global__ __launch_bounds__(NW* kWave) void k_deer_iter(
 // host side
 // ---------------------------------------------------------------------------
 // Chunk shapes (waves x rows of 256 steps).  A channel that fits one chunk
-// takes the smallest single-chunk shape that covers it; a longer channel is
-// split into chunks of the multi-chunk shape and uses the look-back.  Tile
-// choices come from measured sweeps on MI355X: 8x2 for channels of up to 4096
-// steps; for longer scans the chunk must be large enough to amortise the wait
-// on its predecessors (8x4 forward, 16x4 backward: about 4 points of HBM
-// bandwidth over 8x2 at 2^20 steps); the DEER iteration keeps 8x2 chunks.
+// takes the smallest single-chunk shape that covers it (up to 8x4, 8192
+// steps); a longer channel is split into chunks of the multi-chunk shape and
+// uses the look-back.  Tile choices come from measured sweeps on MI355X: for
+// long scans the chunk must be large enough to amortise the wait on its
+// predecessors (8x4 forward, 16x4 backward: about 4 points of HBM bandwidth
+// over 8x2 at 2^20 steps), but a 16-wave chunk holding a whole channel is slow
+// (DEER backward at 8192 steps: 214 us as one 16x4 chunk, 125 us as 8x4); the
+// DEER iteration keeps 8x2 chunks.
 namespace {
 struct Shape { int nw, r; };
-constexpr Shape kScanSingle[] = {{1, 1}, {2, 1}, {4, 1}, {8, 1}, {8, 2}};
+constexpr Shape kScanSingle[] = {{1, 1}, {2, 1}, {4, 1}, {8, 1}, {8, 2}, {8, 4}};
 constexpr Shape kScanFwdMulti = {8, 4};
 constexpr Shape kScanBwdMulti = {16, 4};
 constexpr Shape kDeerSingle[] = {{1, 1}, {2, 1}, {4, 1}, {8, 1}, {8, 2}};
@@ -729,8 +731,13 @@ RowPlan pick(int64_t T, const Shape (&single)[N], Shape multi) {
       return p;
     }
   }
-  p.nw = multi.nw;
-  p.r = multi.r;
+  // a multi-chunk shape larger than the channel would run it as one chunk of
+  // 16 waves, which measured far slower than two chunks of the largest
+  // single shape; those take over until the channel spans two multi chunks
+  Shape m = multi;
+  if ((int64_t)m.nw * m.r * 256 >= T) m = single[N - 1];
+  p.nw = m.nw;
+  p.r = m.r;
   p.nchunk = (T + p.chunk() - 1) / p.chunk();
   return p;
 }
@@ -786,14 +793,14 @@ hipError_t launch_scan_fwd_bdt(const float* a, const float* b, const float* h0, 
     LRS_SHAPE_CASE(4, 1, LRS_FWD(true, false))
     LRS_SHAPE_CASE(8, 1, LRS_FWD(true, false))
     LRS_SHAPE_CASE(8, 2, LRS_FWD(true, false))
-    LRS_SHAPE_CASE(kScanFwdMulti.nw, kScanFwdMulti.r, LRS_FWD(true, false))
+    LRS_SHAPE_CASE(8, 4, LRS_FWD(true, false))
   } else {
     LRS_SHAPE_CASE(1, 1, LRS_FWD(false, false))
     LRS_SHAPE_CASE(2, 1, LRS_FWD(false, false))
     LRS_SHAPE_CASE(4, 1, LRS_FWD(false, false))
     LRS_SHAPE_CASE(8, 1, LRS_FWD(false, false))
     LRS_SHAPE_CASE(8, 2, LRS_FWD(false, false))
-    LRS_SHAPE_CASE(kScanFwdMulti.nw, kScanFwdMulti.r, LRS_FWD(false, false))
+    LRS_SHAPE_CASE(8, 4, LRS_FWD(false, false))
   }
 #undef LRS_FWD
   return hipErrorInvalidValue;
@@ -808,22 +815,27 @@ hipError_t launch_scan_bwd_bdt(const float* a, const float* h, const float* h0, 
                                            0, stream, a, h, h0, g, da, db, dh0, T, C, (int)p.nchunk, \
                                            vec, status, tickets)
   if (p.nchunk > 1) {
-    if (p.stream) { LRS_SHAPE_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_BWD(true, true)) }
-    else { LRS_SHAPE_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_BWD(false, true)) }
+    if (p.stream) {
+      LRS_SHAPE_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_BWD(true, true))
+      LRS_SHAPE_CASE(8, 4, LRS_BWD(true, true))
+    } else {
+      LRS_SHAPE_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_BWD(false, true))
+      LRS_SHAPE_CASE(8, 4, LRS_BWD(false, true))
+    }
   } else if (p.stream) {
     LRS_SHAPE_CASE(1, 1, LRS_BWD(true, false))
     LRS_SHAPE_CASE(2, 1, LRS_BWD(true, false))
     LRS_SHAPE_CASE(4, 1, LRS_BWD(true, false))
     LRS_SHAPE_CASE(8, 1, LRS_BWD(true, false))
     LRS_SHAPE_CASE(8, 2, LRS_BWD(true, false))
-    LRS_SHAPE_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_BWD(true, false))
+    LRS_SHAPE_CASE(8, 4, LRS_BWD(true, false))
   } else {
     LRS_SHAPE_CASE(1, 1, LRS_BWD(false, false))
     LRS_SHAPE_CASE(2, 1, LRS_BWD(false, false))
     LRS_SHAPE_CASE(4, 1, LRS_BWD(false, false))
     LRS_SHAPE_CASE(8, 1, LRS_BWD(false, false))
     LRS_SHAPE_CASE(8, 2, LRS_BWD(false, false))
-    LRS_SHAPE_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_BWD(false, false))
+    LRS_SHAPE_CASE(8, 4, LRS_BWD(false, false))
   }
 #undef LRS_BWD
   return hipErrorInvalidValue;
@@ -842,18 +854,23 @@ hipError_t launch_deer_bwd(const float* w, const float* h, const float* h0, cons
 #define LRS_DB_CASE(NW_, R_, ...) \
   if (p.nw == NW_ && p.r == R_) { constexpr int NW = NW_, RR = R_; __VA_ARGS__; e = hipGetLastError(); }
   if (p.nchunk > 1) {
-    if (p.stream) { LRS_DB_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_DB(true, true)) }
-    else { LRS_DB_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_DB(false, true)) }
+    if (p.stream) {
+      LRS_DB_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_DB(true, true))
+      else LRS_DB_CASE(8, 4, LRS_DB(true, true))
+    } else {
+      LRS_DB_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_DB(false, true))
+      else LRS_DB_CASE(8, 4, LRS_DB(false, true))
+    }
   } else if (p.stream) {
     LRS_DB_CASE(1, 1, LRS_DB(true, false)) else LRS_DB_CASE(2, 1, LRS_DB(true, false))
     else LRS_DB_CASE(4, 1, LRS_DB(true, false)) else LRS_DB_CASE(8, 1, LRS_DB(true, false))
     else LRS_DB_CASE(8, 2, LRS_DB(true, false))
-    else LRS_DB_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_DB(true, false))
+    else LRS_DB_CASE(8, 4, LRS_DB(true, false))
   } else {
     LRS_DB_CASE(1, 1, LRS_DB(false, false)) else LRS_DB_CASE(2, 1, LRS_DB(false, false))
     else LRS_DB_CASE(4, 1, LRS_DB(false, false)) else LRS_DB_CASE(8, 1, LRS_DB(false, false))
     else LRS_DB_CASE(8, 2, LRS_DB(false, false))
-    else LRS_DB_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_DB(false, false))
+    else LRS_DB_CASE(8, 4, LRS_DB(false, false))
   }
 #undef LRS_DB_CASE
 #undef LRS_DB
