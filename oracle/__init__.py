@@ -13,10 +13,12 @@ Functions (page citations are in ``lrs_oracle.c``):
   scan_fwd(a, b, h0)            h_t = a_t h_{t-1} + b_t over the last axis
   scan_bwd(a, h, h0, g)         reverse-time adjoint -> (da, db, dh0)
   sru_fwd(zf, zr, zx, bf, br)   SRU layer on [T, B, D] arrays -> (h, c_last)
+  sru_bwd(zf, ..., gh, c0, gcl) SRU layer gradients -> dict of six arrays
   rnn_seq(w, u, h0)             sequential h_t = tanh(w h_{t-1} + u_t)
   deer(w, u, h0, ...)           Newton / DEER iterations -> (h, iters, deltas)
+  deer_bwd(w, h, g, h0)         adjoint of the RNN at its solution -> (du, dw, dh0)
 
-Parity status: all five are pinned by tests/test_oracle_*.py against closed
+Parity status: all seven are pinned by tests/test_oracle_*.py against closed
 forms, exact rational brute force, adjoint identities, finite differences and
 Newton invariants.
 """
