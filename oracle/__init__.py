@@ -14,11 +14,13 @@ Functions (page citations are in ``lrs_oracle.c``):
   scan_bwd(a, h, h0, g)         reverse-time adjoint -> (da, db, dh0)
   sru_fwd(zf, zr, zx, bf, br)   SRU layer on [T, B, D] arrays -> (h, c_last)
   sru_bwd(zf, ..., gh, c0, gcl) SRU layer gradients -> dict of six arrays
+  lstm_fwd(zf, zi, zc, zo, c0)  LSTM cell-state layer, input-only gates -> (h, c_last)
+  lstm_bwd(..., gh, c0, gcl)    its gradients -> dict of five arrays
   rnn_seq(w, u, h0)             sequential h_t = tanh(w h_{t-1} + u_t)
   deer(w, u, h0, ...)           Newton / DEER iterations -> (h, iters, deltas)
   deer_bwd(w, h, g, h0)         adjoint of the RNN at its solution -> (du, dw, dh0)
 
-Parity status: all seven are pinned by tests/test_oracle_*.py against closed
+Parity status: all nine are pinned by tests/test_oracle_*.py against closed
 forms, exact rational brute force, adjoint identities, finite differences and
 Newton invariants.
 """
@@ -67,9 +69,11 @@ def _load():
                                     _c_dp, ctypes.c_int]
     lib.lrs_oracle_sru_bwd.argtypes = [_c_dp] * 14 + [_i64, _i64, _i64, ctypes.c_int]
     lib.lrs_oracle_deer_bwd.argtypes = [_c_dp] * 7 + [_i64, _i64, _i64, ctypes.c_int]
+    lib.lrs_oracle_lstm_fwd.argtypes = [_c_dp] * 7 + [_i64, _i64, _i64, ctypes.c_int]
+    lib.lrs_oracle_lstm_bwd.argtypes = [_c_dp] * 12 + [_i64, _i64, _i64, ctypes.c_int]
     for fn in (lib.lrs_oracle_scan_fwd, lib.lrs_oracle_scan_bwd, lib.lrs_oracle_sru_fwd,
                lib.lrs_oracle_rnn_seq, lib.lrs_oracle_deer, lib.lrs_oracle_sru_bwd,
-               lib.lrs_oracle_deer_bwd):
+               lib.lrs_oracle_deer_bwd, lib.lrs_oracle_lstm_fwd, lib.lrs_oracle_lstm_bwd):
         fn.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -149,6 +153,38 @@ def sru_bwd(zf, zr, zx, bf, br, gh, c0=None, gcl=None, nthreads: int = 0):
                                       _ptr(gh), _ptr(gcl), _ptr(out["dzf"]), _ptr(out["dzr"]),
                                       _ptr(out["dzx"]), _ptr(out["dbf"]), _ptr(out["dbr"]),
                                       _ptr(out["dc0"]), T, B, D, nthreads), "sru_bwd")
+    return out
+
+
+def _lstm_shapes(zs):
+    if not all(z.shape == zs[0].shape for z in zs) or zs[0].ndim != 3:
+        raise ValueError("zf, zi, zc, zo (and gh) must be [T, B, D] arrays of one shape")
+    return zs[0].shape
+
+
+def lstm_fwd(zf, zi, zc, zo, c0=None, nthreads: int = 0):
+    """LSTM cell-state layer with input-only gates on [T, B, D] pre-activations.
+    Returns (h [T,B,D], c_last [B,D])."""
+    zf, zi, zc, zo, c0 = map(_f64, (zf, zi, zc, zo, c0))
+    T, B, D = _lstm_shapes((zf, zi, zc, zo))
+    h = np.empty_like(zf)
+    c_last = np.empty((B, D))
+    _check(_load().lrs_oracle_lstm_fwd(_ptr(zf), _ptr(zi), _ptr(zc), _ptr(zo), _ptr(c0), _ptr(h),
+                                       _ptr(c_last), T, B, D, nthreads), "lstm_fwd")
+    return h, c_last
+
+
+def lstm_bwd(zf, zi, zc, zo, gh, c0=None, gcl=None, nthreads: int = 0):
+    """Gradients of lstm_fwd for dL/dh = gh [T,B,D] and dL/dc_T = gcl [B,D].
+    Returns dict dzf, dzi, dzc, dzo [T,B,D] and dc0 [B,D]."""
+    zf, zi, zc, zo, gh, c0, gcl = map(_f64, (zf, zi, zc, zo, gh, c0, gcl))
+    T, B, D = _lstm_shapes((zf, zi, zc, zo, gh))
+    out = {k: np.empty_like(zf) for k in ("dzf", "dzi", "dzc", "dzo")}
+    out["dc0"] = np.empty((B, D))
+    _check(_load().lrs_oracle_lstm_bwd(_ptr(zf), _ptr(zi), _ptr(zc), _ptr(zo), _ptr(c0), _ptr(gh),
+                                       _ptr(gcl), _ptr(out["dzf"]), _ptr(out["dzi"]),
+                                       _ptr(out["dzc"]), _ptr(out["dzo"]), _ptr(out["dc0"]), T, B,
+                                       D, nthreads), "lstm_bwd")
     return out
 
 

@@ -1,7 +1,7 @@
 /*
  * lrs_oracle.c -- plain, sequential fp64 reference for the diagonal linear
- * recurrence, its reverse-time adjoint, the SRU cell-state layer and the DEER
- * Newton solve of an element-wise nonlinear RNN.
+ * recurrence, its reverse-time adjoint, the SRU and LSTM cell-state layers and
+ * the DEER Newton solve of an element-wise nonlinear RNN.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
  * calls this file; only the test-suite, the smoke check and the CPU-baseline
@@ -30,8 +30,8 @@
  * Conventions shared with the tests: a channel is one (batch, feature) pair;
  * the time axis has T steps stored at index 0..T-1 for t = 1..T; h0 is the
  * state at t = 0 and is not part of the output.  Layout of the scan and DEER
- * arrays is channel-major [C, T] (time contiguous); the SRU arrays are
- * [T, B, D] (feature contiguous), as the SRU workload states them.
+ * arrays is channel-major [C, T] (time contiguous); the SRU and LSTM arrays
+ * are [T, B, D] (feature contiguous), as the SRU workload states them.
  *
  * Parity status: every function here is pinned by tests in tests/ against
  * closed forms, exact rational brute force, adjoint identities, finite
@@ -219,6 +219,91 @@ int lrs_oracle_sru_bwd(const double *zf, const double *zr, const double *zx,
     }
     free(sf);
     free(sr);
+    return fail ? ORACLE_ENOMEM : ORACLE_OK;
+}
+
+/* LSTM cell-state layer with every gate computed from the inputs alone
+ * ([P2] the LSTM cell state C_t = f_t*C_{t-1} + i_t*C~_t read as a linear
+ * recurrence with coefficient f_t and input i_t*C~_t; the model-change step
+ * of its deployment list asks for gates that do not depend on h_{t-1}).
+ * The pre-activations (input projections plus biases, made outside) are
+ * z_f, z_i, z_c, z_o, all [T, B, D]:
+ *   f = sigmoid(z_f), i = sigmoid(z_i), g = tanh(z_c), o = sigmoid(z_o),
+ *   c_t = f_t c_{t-1} + i_t g_t,   h_t = o_t tanh(c_t).
+ * c0 [B, D] (NULL = 0); h [T, B, D]; c_last [B, D] or NULL. */
+int lrs_oracle_lstm_fwd(const double *zf, const double *zi, const double *zc,
+                        const double *zo, const double *c0, double *h, double *c_last,
+                        int64_t T, int64_t B, int64_t D, int nthreads)
+{
+    if (T < 0 || B < 0 || D < 0) return ORACLE_EINVAL;
+    if (T * B * D > 0 && (!zf || !zi || !zc || !zo || !h)) return ORACLE_EINVAL;
+    set_threads(nthreads);
+    const int64_t C = B * D;
+#pragma omp parallel for schedule(static)
+    for (int64_t ch = 0; ch < C; ++ch) {
+        double c = c0 ? c0[ch] : 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t k = t * C + ch;
+            const double f = sigmoid(zf[k]), i = sigmoid(zi[k]);
+            const double g = tanh(zc[k]), o = sigmoid(zo[k]);
+            c = f * c + i * g;
+            h[k] = o * tanh(c);
+        }
+        if (c_last) c_last[ch] = c;
+    }
+    return ORACLE_OK;
+}
+
+/* Reverse-mode derivative of the LSTM cell-state layer above (the chain rule
+ * of its definition; the cell-state gradient is again a reverse-time linear
+ * recurrence, [P1] parallel-scan paragraph).  With gh_t = dL/dh_t and
+ * gcl = dL/dc_T (NULL = 0):
+ *   gc_t = gh_t o_t (1 - tanh^2 c_t) + f_{t+1} gc_{t+1},   gc_T starts from gcl,
+ *   dz_o = gh_t tanh(c_t) o_t (1 - o_t),   dz_f = gc_t c_{t-1} f_t (1 - f_t),
+ *   dz_i = gc_t g_t i_t (1 - i_t),         dz_c = gc_t i_t (1 - g_t^2),
+ *   dc0  = f_1 gc_1.
+ * The cell states are recomputed by each channel's forward loop first.
+ * dzf, dzi, dzc, dzo are [T, B, D]; dc0 is [B, D] or NULL. */
+int lrs_oracle_lstm_bwd(const double *zf, const double *zi, const double *zc,
+                        const double *zo, const double *c0, const double *gh,
+                        const double *gcl, double *dzf, double *dzi, double *dzc,
+                        double *dzo, double *dc0, int64_t T, int64_t B, int64_t D,
+                        int nthreads)
+{
+    if (T < 0 || B < 0 || D < 0) return ORACLE_EINVAL;
+    if (T * B * D > 0 && (!zf || !zi || !zc || !zo || !gh || !dzf || !dzi || !dzc || !dzo))
+        return ORACLE_EINVAL;
+    set_threads(nthreads);
+    const int64_t C = B * D;
+    int fail = 0;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t ch = 0; ch < C; ++ch) {
+        double *c = malloc((size_t)(T > 0 ? T : 1) * sizeof(double));
+        if (!c) { fail = 1; continue; }
+        double state = c0 ? c0[ch] : 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t k = t * C + ch;
+            state = sigmoid(zf[k]) * state + sigmoid(zi[k]) * tanh(zc[k]);
+            c[t] = state;
+        }
+        /* reverse: carry = f_{t+1} gc_{t+1} (gcl at the end of the sequence) */
+        double carry = gcl ? gcl[ch] : 0.0;
+        for (int64_t t = T - 1; t >= 0; --t) {
+            const int64_t k = t * C + ch;
+            const double f = sigmoid(zf[k]), i = sigmoid(zi[k]);
+            const double g = tanh(zc[k]), o = sigmoid(zo[k]);
+            const double th = tanh(c[t]);
+            const double gc = gh[k] * o * (1.0 - th * th) + carry;
+            const double cprev = t > 0 ? c[t - 1] : (c0 ? c0[ch] : 0.0);
+            dzo[k] = gh[k] * th * o * (1.0 - o);
+            dzf[k] = gc * cprev * f * (1.0 - f);
+            dzi[k] = gc * g * i * (1.0 - i);
+            dzc[k] = gc * i * (1.0 - g * g);
+            carry = f * gc;
+        }
+        if (dc0) dc0[ch] = carry;
+        free(c);
+    }
     return fail ? ORACLE_ENOMEM : ORACLE_OK;
 }
 
