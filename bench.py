@@ -4,8 +4,9 @@
 Default workload (the headline metric): forward + backward fp32 scan,
 B=8, D=512, T=4096, [B,D,T] layout.  One step = lrs_scan_fwd then
 lrs_scan_bwd over the same resident inputs.  Other workloads (--workload):
-scan_long (T = 2^20), sru_fwd (bf16 SRU layer), deer (Newton solve),
-scan_fwd_small.
+scan_long (T = 2^20), sru_fwd / sru_fwd_bwd (bf16 SRU layer), lstm_fwd_bwd
+(bf16 LSTM cell-state layer with input-only gates), deer / deer_fwd_bwd
+(Newton solve, and its backward), scan_fwd_small.
 
 Prints ONE JSON line.  `value` is scanned elements per second over K timed
 steps launched back to back from Python (inputs resident in HBM before timing
@@ -40,7 +41,9 @@ BYTES_PER_ELEM = {"scan_fwd_f32": 12, "scan_bwd_f32": 20, "sru_fwd_bf16": 8,
                   "sru_fwd_save_bf16": 12,  # + the fp32 cell states for the backward
                   "sru_bwd_bf16": 18,       # z_f, z_r, z_x, dL/dh, c in; three gradients out
                   "deer_iter_first": 8, "deer_iter": 12,
-                  "deer_bwd_f32": 12}       # h, dL/dh in; dL/du out
+                  "deer_bwd_f32": 12,       # h, dL/dh in; dL/du out
+                  "lstm_fwd_save_bf16": 14,  # four pre-activations in; h and c out
+                  "lstm_bwd_bf16": 22}       # four pre-activations, dL/dh, c in; four gradients out
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
 
 
@@ -75,7 +78,9 @@ KERNEL_NAMES = {"scan_fwd_f32": ("k_scan_fwd_bdt", "k_scan_fwd_tbd"),
                 "sru_fwd_save_bf16": ("k_sru_fwd<unsigned short",),
                 "sru_bwd_bf16": ("k_sru_bwd<unsigned short",),
                 "deer_solve": ("k_deer_iter",),
-                "deer_bwd_f32": ("k_deer_bwd",)}
+                "deer_bwd_f32": ("k_deer_bwd",),
+                "lstm_fwd_save_bf16": ("k_lstm_fwd<unsigned short",),
+                "lstm_bwd_bf16": ("k_lstm_bwd<unsigned short",)}
 # entry points timed by each workload
 WORKLOAD_KERNELS = {"scan_fwd_small": ("scan_fwd_f32",),
                     "scan_fwd_bwd": ("scan_fwd_f32", "scan_bwd_f32"),
@@ -83,7 +88,8 @@ WORKLOAD_KERNELS = {"scan_fwd_small": ("scan_fwd_f32",),
                     "sru_fwd": ("sru_fwd_bf16",),
                     "sru_fwd_bwd": ("sru_fwd_save_bf16", "sru_bwd_bf16"),
                     "deer": ("deer_solve",),
-                    "deer_fwd_bwd": ("deer_solve", "deer_bwd_f32")}
+                    "deer_fwd_bwd": ("deer_solve", "deer_bwd_f32"),
+                    "lstm_fwd_bwd": ("lstm_fwd_save_bf16", "lstm_bwd_bf16")}
 CALIB_NAME = "CUDAFunctor_add<float>"  # the stream reference kernel
 CALIB_READ = 2 * 4 * (1 << 26)
 CALIB_WRITE = 4 * (1 << 26)
@@ -174,6 +180,11 @@ def summarize(args):
               f"{factor['WRITE_SIZE'] and round(factor['WRITE_SIZE'], 3)}.", "",
               "| kernel | raw FETCH KiB | raw WRITE KiB | scaled HBM bytes | algorithmic bytes | ratio |",
               "|---|---|---|---|---|---|"]
+    # the sources the profiled run was built from (its bench line), else these
+    src_hash = (bench_line or {}).get("csrc_hash") or csrc_hash()
+    if src_hash != csrc_hash():
+        print(f"note: the profiled run used kernel sources {src_hash}, this tree has {csrc_hash()}",
+              file=sys.stderr)
     from linear_recurrence_scan_diagonal_amd import inputs as I
     w = I.WORKLOADS[wl]
     for key in WORKLOAD_KERNELS[wl]:
@@ -190,14 +201,15 @@ def summarize(args):
                 n_it = len([r for r in pmc["FETCH_SIZE"] if pat in r["Kernel_Name"]])
                 a = None
                 hbm_solve = hbm * 5  # five iterations per solve on this workload
-                rec[f"{tag}/{key}"] = {"hbm_bytes_per_launch": round(hbm_solve), "csrc_hash": csrc_hash(),
+                rec[f"{tag}/{key}"] = {"hbm_bytes_per_launch": round(hbm_solve), "csrc_hash": src_hash,
                                       "per_iteration_bytes": round(hbm), "dispatches": n_it}
             else:
-                rec[f"{tag}/{key}"] = {"hbm_bytes_per_launch": round(hbm), "csrc_hash": csrc_hash(),
+                rec[f"{tag}/{key}"] = {"hbm_bytes_per_launch": round(hbm), "csrc_hash": src_hash,
                                       "algorithmic_bytes": a}
             lines.append(f"| `{pat}` | {f_/1024:.0f} | {w_/1024:.0f} | {hbm:.4g} | "
                          f"{a if a else 'n/a'} | {hbm / a if a else float('nan'):.3f} |")
-    lines += ["", f"Kernel sources hash: `{csrc_hash()}` (bench.py reports `traffic` only while it matches)."]
+    lines += ["", f"Kernel sources hash of the profiled run: `{src_hash}` (bench.py reports "
+              "`traffic` only while it matches the sources it runs)."]
     os.makedirs(os.path.dirname(COUNTERS_FILE), exist_ok=True)
     with open(COUNTERS_FILE, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
@@ -213,8 +225,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="scan_fwd_bwd",
-                   choices=["scan_fwd_bwd", "scan_long", "sru_fwd", "sru_fwd_bwd", "deer",
-                            "deer_fwd_bwd", "scan_fwd_small"])
+                   choices=["scan_fwd_bwd", "scan_long", "sru_fwd", "sru_fwd_bwd", "lstm_fwd_bwd",
+                            "deer", "deer_fwd_bwd", "scan_fwd_small"])
     p.add_argument("--layout", default="bdt", choices=["bdt", "tbd"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", action="store_true",
@@ -413,6 +425,30 @@ def main():
         dtype = "bf16 I/O, f32 state"
         config = {"workload": w.name, "B": B, "D": D, "T": T, "layout": "tbd",
                   "pass": "fwd+bwd" if w.name == "sru_fwd_bwd" else "fwd"}
+    elif w.kind == "lstm":  # forward saving the cell states, then the backward
+        s = I.lstm_inputs(w)
+        s["gh"] = I.sru_grad_inputs(w)["gh"]
+        z = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(dev)
+             for k, v in s.items()}
+        hs = torch.empty_like(z["zf"])
+        cs = torch.empty((T, B, D), dtype=torch.float32, device=dev)
+        grads = tuple(torch.empty_like(z["zf"]) for _ in range(4)) + (
+            torch.empty((B, D), dtype=torch.float32, device=dev),)
+        ws = torch.empty(max(1, lrs.load().lrs_lstm_workspace_bytes(T, B, D)), dtype=torch.uint8,
+                         device=dev)
+        zg = (z["zf"], z["zi"], z["zc"], z["zo"])
+        calls = {"lstm_fwd_save_bf16": lambda: lrs.lstm_fwd(*zg, out=hs, workspace=ws,
+                                                            c_states=cs),
+                 "lstm_bwd_bf16": lambda: lrs.lstm_bwd(*zg, cs, z["gh"], out=grads,
+                                                       workspace=ws)}
+
+        def step():
+            for fn in calls.values():
+                fn()
+        kernels = list(calls)
+        dtype = "bf16 I/O, f32 state"
+        config = {"workload": w.name, "B": B, "D": D, "T": T, "layout": "tbd",
+                  "pass": "fwd+bwd"}
     else:  # deer
         x = I.deer_inputs(w)
         wd = torch.from_numpy(x["w"]).to(dev)
@@ -495,7 +531,7 @@ def main():
         dom = max(kernels, key=lambda k: per_kernel[k])
         dom_bytes = BYTES_PER_ELEM[dom] * N
         dom_ms = per_kernel[dom]
-    elif w.kind == "sru":
+    elif w.kind in ("sru", "lstm"):
         bytes_step = sum(BYTES_PER_ELEM[k] * N for k in kernels)
         dom = max(kernels, key=lambda k: per_kernel[k])
         dom_bytes, dom_ms = BYTES_PER_ELEM[dom] * N, per_kernel[dom]
@@ -533,7 +569,7 @@ def main():
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
             "data": "synthetic", "config": config, "roofline": roofline, "cpu_baseline": cpu,
-            **extra}
+            **extra, "csrc_hash": csrc_hash()}
     print(json.dumps(line), flush=True)
 
 
@@ -598,6 +634,17 @@ def cpu_baseline(w, args, np, I):
                 oracle.sru_bwd(*z, s["bias_f"], s["bias_r"], gh64, nthreads=threads)
         sample = (f"B=1 of {w.B}, D={sub.D}, T={T} (same recipe), "
                   f"fwd{'+bwd' if with_bwd else ''}")
+        n_el = sub.N
+    elif w.kind == "lstm":
+        sub = I.scaled(w, B=1, D=min(w.D, 1024))
+        s = I.lstm_inputs(sub)
+        z = [I.bf16_bits_to_f64(s[k]) for k in ("zf", "zi", "zc", "zo")]
+        gh64 = I.bf16_bits_to_f64(I.sru_grad_inputs(sub)["gh"])
+
+        def once():
+            oracle.lstm_fwd(*z, nthreads=threads)
+            oracle.lstm_bwd(*z, gh64, nthreads=threads)
+        sample = f"B=1 of {w.B}, D={sub.D}, T={T} (same recipe), fwd+bwd"
         n_el = sub.N
     else:
         sub = I.scaled(w, B=1)

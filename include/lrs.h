@@ -1,7 +1,8 @@
 /*
  * lrs.h -- C ABI of liblrs.so: the diagonal linear-recurrence scan
  * h_t = a_t (.) h_{t-1} + b_t on AMD MI355X (gfx950), with its reverse-time
- * backward pass, a fused SRU layer and a DEER Newton solver built on it.
+ * backward pass, fused SRU and LSTM cell-state layers and a DEER Newton solver
+ * built on it.
  *
  * Sources (four blog pages on one subject; cited by title and section):
  *  [P1] "CUDA并行化RNN训练：从O(T)到O(log T)的工程实践与参数调优", body:
@@ -11,7 +12,8 @@
  *       element-wise work into one kernel).
  *  [P2] "RNN CUDA内核优化：实现序列长度无关的恒定推理延迟", body: the cell state
  *       C_t = f_t*C_{t-1} + i_t*C~_t is a linear recurrence with time-varying
- *       coefficients, i.e. a prefix-scan problem.
+ *       coefficients, i.e. a prefix-scan problem; the deployment list's first
+ *       step (change the model so the recurrent part is linear).
  *  [P4] DEER page "cuda-parallel-rnn-training-logt-optimization": section
  *       "核心原理" (Newton in function space; the inverse operator is a linear
  *       recurrence with an initial condition, solved by a parallel prefix scan)
@@ -33,7 +35,7 @@
  *    Pointers must be aligned to their element size; 16-byte alignment of all
  *    arrays (and T % 4 == 0 for [B,D,T] fp32) enables the widest accesses.
  *  - `stream` is a hipStream_t passed as an opaque pointer (NULL = the null
- *    stream).  Scan and SRU calls only enqueue work and return; DEER does the
+ *    stream).  Scan, SRU and LSTM calls only enqueue work and return; DEER does the
  *    same when it is given no host outputs, and otherwise reads its solve
  *    record back to the host and returns after the solve.
  *  - Errors are return codes (lrs_status); nothing is thrown and nothing
@@ -162,6 +164,52 @@ LRS_API int lrs_sru_bwd(const void *z_f, const void *z_r, const void *z_x, const
                 void *grad_zx, float *grad_bias_f, float *grad_bias_r, float *grad_c0,
                 int64_t T, int64_t B, int64_t D, int io_dtype, void *workspace,
                 size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------- LSTM --- */
+
+/* Workspace bytes needed by lrs_lstm_fwd and lrs_lstm_bwd for this shape, in
+ * either I/O type (0 for an invalid or empty shape). */
+LRS_API size_t lrs_lstm_workspace_bytes(int64_t T, int64_t B, int64_t D);
+
+/* Fused LSTM cell-state layer forward with every gate computed from the
+ * inputs alone ([P2] cell-state paragraph: C_t = f_t*C_{t-1} + i_t*C~_t is a
+ * linear recurrence once the gates do not read h_{t-1}, as its deployment
+ * list's model-change step asks; [P1] checklist item 2: one kernel for all
+ * element-wise work).  With the pre-activations z_* (input projection plus
+ * bias, made by the caller):
+ *   f = sigmoid(z_f), i = sigmoid(z_i), g = tanh(z_c), o = sigmoid(z_o)
+ *   c_t = f_t * c_{t-1} + i_t * g_t,   h_t = o_t * tanh(c_t)
+ * z_f, z_i, z_c, z_o, h : [T,B,D], element type io_dtype (LRS_BF16 or LRS_F32).
+ * c0       : [B,D] fp32 or NULL (zero).
+ * c_last   : [B,D] fp32 output (c_T) or NULL.
+ * c_states : [T,B,D] fp32 output (every c_t, as lrs_lstm_bwd needs them) or NULL.
+ * Gates, state and activations are fp32; h is rounded to io_dtype
+ * (nearest-even).  No output may overlap an input or another output. */
+LRS_API int lrs_lstm_fwd(const void *z_f, const void *z_i, const void *z_c, const void *z_o,
+                         const float *c0, void *h, float *c_last, float *c_states, int64_t T,
+                         int64_t B, int64_t D, int io_dtype, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/* LSTM cell-state layer backward (the chain rule of lrs_lstm_fwd; the
+ * cell-state gradient is a reverse-time linear recurrence, [P1] parallel-scan
+ * paragraph).  Given gh_t = dL/dh_t and dL/dc_T:
+ *   gc_t = gh_t o_t (1 - tanh^2 c_t) + f_{t+1} gc_{t+1}   (gc_T adds dL/dc_T),
+ *   dL/dz_o = gh tanh(c) o (1 - o),   dL/dz_f = gc c_{t-1} f (1 - f),
+ *   dL/dz_i = gc g i (1 - i),         dL/dz_c = gc i (1 - g^2),
+ *   dL/dc0 = f_1 gc_1.
+ * z_*, grad_h, grad_z*: [T,B,D], element type io_dtype.  c0: [B,D] fp32 or NULL.
+ * c_states   : [T,B,D] fp32, the cell states lrs_lstm_fwd wrote for the same
+ *              inputs and c0.
+ * grad_c_last: [B,D] fp32 (dL/dc_T) or NULL (zero).
+ * grad_c0    : [B,D] fp32 output or NULL.
+ * The biases live inside the pre-activations, so their gradients are the
+ * callers' sums of grad_z* over batch and time.
+ * No output may overlap an input or another output. */
+LRS_API int lrs_lstm_bwd(const void *z_f, const void *z_i, const void *z_c, const void *z_o,
+                         const float *c0, const float *c_states, const void *grad_h,
+                         const float *grad_c_last, void *grad_zf, void *grad_zi, void *grad_zc,
+                         void *grad_zo, float *grad_c0, int64_t T, int64_t B, int64_t D,
+                         int io_dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------- DEER --- */
 

@@ -25,7 +25,8 @@ DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 EXPORTS = ("lrs_status_string", "lrs_version", "lrs_scan_workspace_bytes", "lrs_scan_fwd",
            "lrs_scan_bwd", "lrs_sru_workspace_bytes", "lrs_sru_fwd", "lrs_deer_workspace_bytes",
            "lrs_deer_solve", "lrs_deer_stats", "lrs_sru_bwd_workspace_bytes", "lrs_sru_bwd",
-           "lrs_deer_bwd_workspace_bytes", "lrs_deer_bwd")
+           "lrs_deer_bwd_workspace_bytes", "lrs_deer_bwd", "lrs_lstm_workspace_bytes",
+           "lrs_lstm_fwd", "lrs_lstm_bwd")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -70,6 +71,12 @@ def load():
     lib.lrs_sru_bwd.argtypes = [_vp] * 15 + [_i64, _i64, _i64, _int, _vp, _sz, _vp]
     lib.lrs_sru_bwd.restype = _int
     lib.lrs_sru_fwd.restype = _int
+    lib.lrs_lstm_workspace_bytes.argtypes = [_i64, _i64, _i64]
+    lib.lrs_lstm_workspace_bytes.restype = _sz
+    lib.lrs_lstm_fwd.argtypes = [_vp] * 8 + [_i64, _i64, _i64, _int, _vp, _sz, _vp]
+    lib.lrs_lstm_fwd.restype = _int
+    lib.lrs_lstm_bwd.argtypes = [_vp] * 13 + [_i64, _i64, _i64, _int, _vp, _sz, _vp]
+    lib.lrs_lstm_bwd.restype = _int
     lib.lrs_deer_workspace_bytes.argtypes = [_i64, _i64, _i64, _int]
     lib.lrs_deer_workspace_bytes.restype = _sz
     lib.lrs_deer_solve.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_float, _int,
@@ -236,6 +243,62 @@ def sru_bwd(z_f, z_r, z_x, bias_f, bias_r, c_states, grad_h, c0=None, grad_c_las
                           _ptr(dzx), _ptr(dbf), _ptr(dbr), _ptr(dc0), T, B, D, DTYPES[io],
                           _ptr(ws), nbytes, _stream(dev)), "lrs_sru_bwd")
     return dzf, dzr, dzx, dbf, dbr, dc0
+
+
+def lstm_fwd(z_f, z_i, z_c, z_o, c0=None, want_c_last: bool = False, out=None, workspace=None,
+             c_states=None):
+    """LSTM cell-state layer with input-only gates on [T,B,D] pre-activations
+    (bf16 or fp32).  Returns h or (h, c_last).  c_states, if given, is a
+    [T,B,D] fp32 tensor that receives every cell state (lstm_bwd's input)."""
+    lib = load()
+    if z_f.dim() != 3:
+        raise ValueError("z_f must be [T,B,D]")
+    T, B, D = (int(x) for x in z_f.shape)
+    io = z_f.dtype
+    for name, t in (("z_f", z_f), ("z_i", z_i), ("z_c", z_c), ("z_o", z_o)):
+        _check_dev(name, t, io, z_f.shape)
+    _check_dev("c0", c0, torch.float32, (B, D))
+    _check_dev("c_states", c_states, torch.float32, z_f.shape)
+    h = torch.empty_like(z_f) if out is None else out
+    _check_dev("out", h, io, z_f.shape)
+    c_last = torch.empty((B, D), dtype=torch.float32, device=z_f.device) if want_c_last else None
+    nbytes = lib.lrs_lstm_workspace_bytes(T, B, D)
+    ws = _workspace(nbytes, z_f.device, workspace)
+    _call(lib.lrs_lstm_fwd(_ptr(z_f), _ptr(z_i), _ptr(z_c), _ptr(z_o), _ptr(c0), _ptr(h),
+                           _ptr(c_last), _ptr(c_states), T, B, D, DTYPES[io], _ptr(ws), nbytes,
+                           _stream(z_f.device)), "lrs_lstm_fwd")
+    return (h, c_last) if want_c_last else h
+
+
+def lstm_bwd(z_f, z_i, z_c, z_o, c_states, grad_h, c0=None, grad_c_last=None,
+             want_grad_c0: bool = True, out=None, workspace=None):
+    """Backward of lstm_fwd.  c_states: the [T,B,D] fp32 cell states lstm_fwd
+    saved; grad_h: dL/dh in the I/O type; grad_c_last: dL/dc_T [B,D] or None.
+    Returns (grad_zf, grad_zi, grad_zc, grad_zo, grad_c0 or None)."""
+    lib = load()
+    T, B, D = (int(x) for x in z_f.shape)
+    io = z_f.dtype
+    for name, t in (("z_f", z_f), ("z_i", z_i), ("z_c", z_c), ("z_o", z_o), ("grad_h", grad_h)):
+        _check_dev(name, t, io, z_f.shape)
+    _check_dev("c_states", c_states, torch.float32, z_f.shape)
+    _check_dev("c0", c0, torch.float32, (B, D))
+    _check_dev("grad_c_last", grad_c_last, torch.float32, (B, D))
+    dev = z_f.device
+    if out is None:
+        out = (torch.empty_like(z_f), torch.empty_like(z_f), torch.empty_like(z_f),
+               torch.empty_like(z_f),
+               torch.empty((B, D), dtype=torch.float32, device=dev) if want_grad_c0 else None)
+    dzf, dzi, dzc, dzo, dc0 = out
+    for name, t in (("grad_zf", dzf), ("grad_zi", dzi), ("grad_zc", dzc), ("grad_zo", dzo)):
+        _check_dev(name, t, io, z_f.shape)
+    _check_dev("grad_c0", dc0, torch.float32, (B, D))
+    nbytes = lib.lrs_lstm_workspace_bytes(T, B, D)
+    ws = _workspace(nbytes, dev, workspace)
+    _call(lib.lrs_lstm_bwd(_ptr(z_f), _ptr(z_i), _ptr(z_c), _ptr(z_o), _ptr(c0), _ptr(c_states),
+                           _ptr(grad_h), _ptr(grad_c_last), _ptr(dzf), _ptr(dzi), _ptr(dzc),
+                           _ptr(dzo), _ptr(dc0), T, B, D, DTYPES[io], _ptr(ws), nbytes,
+                           _stream(dev)), "lrs_lstm_bwd")
+    return dzf, dzi, dzc, dzo, dc0
 
 
 def deer_solve(w, u, h0=None, h_init=None, eps: float = 1e-5, k_max: int = 5, out=None,

@@ -406,6 +406,129 @@ int lrs_sru_bwd(const void* z_f, const void* z_r, const void* z_x, const float* 
                                         vec, status, tickets, s));
 }
 
+// ------------------------------------------------------------------- LSTM
+
+size_t lrs_lstm_workspace_bytes(int64_t T, int64_t B, int64_t D) {
+  int64_t C, N;
+  if (!shape_ok(B, D, T, &C, &N) || N == 0) return 0;
+  size_t need = 0;
+  for (int io = 0; io < 2; ++io) {
+    const lrs::ColPlan ps[3] = {lrs::plan_lstm(C, T, io, false), lrs::plan_lstm(C, T, io, true),
+                                lrs::plan_lstm_bwd(C, T, io)};
+    for (const lrs::ColPlan& p : ps) {
+      const size_t b = lookback_bytes(lrs::col_status_words(p), p.ncb);
+      need = b > need ? b : need;
+    }
+  }
+  return need;
+}
+
+// Carves and resets the look-back state of a [T,B,D] plan.
+static int col_lookback(const lrs::ColPlan& p, void* workspace, size_t workspace_bytes,
+                        hipStream_t s, uint64_t** status, unsigned** tickets) {
+  *status = nullptr;
+  *tickets = nullptr;
+  const int64_t nst = lrs::col_status_words(p);
+  const size_t need = lookback_bytes(nst, p.ncb);
+  if (need && (!workspace || workspace_bytes < need)) return LRS_ERR_WORKSPACE;
+  if (nst == 0) return LRS_OK;
+  Carve cv(align_ptr(workspace));
+  *status = cv.take<uint64_t>(nst);
+  *tickets = cv.take<unsigned>(p.ncb);
+  return hip_status(lrs::launch_reset(*status, nst, *tickets, p.ncb, nullptr, 0, s));
+}
+
+int lrs_lstm_fwd(const void* z_f, const void* z_i, const void* z_c, const void* z_o,
+                 const float* c0, void* h, float* c_last, float* c_states, int64_t T, int64_t B,
+                 int64_t D, int io_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int64_t C, N;
+  if (!shape_ok(B, D, T, &C, &N)) return LRS_ERR_INVALID_ARG;
+  if (io_dtype != LRS_F32 && io_dtype != LRS_BF16) return LRS_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (N == 0) {
+    if (T == 0 && C > 0 && c_last) return hip_status(lrs::launch_copy_or_zero(c_last, c0, C, s));
+    return LRS_OK;
+  }
+  if (!z_f || !z_i || !z_c || !z_o || !h) return LRS_ERR_INVALID_ARG;
+  const size_t es = io_dtype == LRS_BF16 ? 2 : 4;
+  if (!aligned(z_f, es) || !aligned(z_i, es) || !aligned(z_c, es) || !aligned(z_o, es) ||
+      !aligned(h, es) || (c0 && !aligned(c0, 4)) || (c_last && !aligned(c_last, 4)) ||
+      (c_states && !aligned(c_states, 4)))
+    return LRS_ERR_INVALID_ARG;
+  const size_t nb = (size_t)N * es, cb = (size_t)C * 4, sb = (size_t)N * 4;
+  const void* ins[5] = {z_f, z_i, z_c, z_o, c0};
+  const size_t insz[5] = {nb, nb, nb, nb, cb};
+  for (int i = 0; i < 5; ++i)
+    if (overlap(h, nb, ins[i], insz[i]) || overlap(c_last, cb, ins[i], insz[i]) ||
+        overlap(c_states, sb, ins[i], insz[i]))
+      return LRS_ERR_INVALID_ARG;
+  if (overlap(h, nb, c_last, cb) || overlap(h, nb, c_states, sb) ||
+      overlap(c_last, cb, c_states, sb))
+    return LRS_ERR_INVALID_ARG;
+  const lrs::ColPlan p = lrs::plan_lstm(C, T, io_dtype, c_states != nullptr);
+  if (!grid_ok(p.ncb * p.ntb, p.nw * 64)) return LRS_ERR_UNSUPPORTED;
+  uint64_t* status;
+  unsigned* tickets;
+  const int rc = col_lookback(p, workspace, workspace_bytes, s, &status, &tickets);
+  if (rc != LRS_OK) return rc;
+  const size_t rowbytes = (size_t)p.cpt * es;
+  const int vec = aligned(z_f, rowbytes) && aligned(z_i, rowbytes) && aligned(z_c, rowbytes) &&
+                  aligned(z_o, rowbytes) && aligned(h, rowbytes) &&
+                  (!c_states || aligned(c_states, (size_t)p.cpt * 4)) && (C % p.cpt == 0);
+  return hip_status(lrs::launch_lstm_fwd(z_f, z_i, z_c, z_o, c0, h, c_last, c_states, T, C,
+                                         io_dtype, p, vec, status, tickets, s));
+}
+
+int lrs_lstm_bwd(const void* z_f, const void* z_i, const void* z_c, const void* z_o,
+                 const float* c0, const float* c_states, const void* grad_h,
+                 const float* grad_c_last, void* grad_zf, void* grad_zi, void* grad_zc,
+                 void* grad_zo, float* grad_c0, int64_t T, int64_t B, int64_t D, int io_dtype,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  int64_t C, N;
+  if (!shape_ok(B, D, T, &C, &N)) return LRS_ERR_INVALID_ARG;
+  if (io_dtype != LRS_F32 && io_dtype != LRS_BF16) return LRS_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (N == 0) {
+    // no steps: dL/dc0 = dL/dc_T
+    if (T == 0 && C > 0 && grad_c0)
+      return hip_status(lrs::launch_copy_or_zero(grad_c0, grad_c_last, C, s));
+    return LRS_OK;
+  }
+  if (!z_f || !z_i || !z_c || !z_o || !c_states || !grad_h || !grad_zf || !grad_zi ||
+      !grad_zc || !grad_zo)
+    return LRS_ERR_INVALID_ARG;
+  const size_t es = io_dtype == LRS_BF16 ? 2 : 4;
+  const void* io[9] = {z_f, z_i, z_c, z_o, grad_h, grad_zf, grad_zi, grad_zc, grad_zo};
+  for (int i = 0; i < 9; ++i)
+    if (!aligned(io[i], es)) return LRS_ERR_INVALID_ARG;
+  if (!aligned(c_states, 4) || (c0 && !aligned(c0, 4)) ||
+      (grad_c_last && !aligned(grad_c_last, 4)) || (grad_c0 && !aligned(grad_c0, 4)))
+    return LRS_ERR_INVALID_ARG;
+  const size_t nb = (size_t)N * es, cb = (size_t)C * 4, sb = (size_t)N * 4;
+  const void* ins[8] = {z_f, z_i, z_c, z_o, grad_h, c_states, c0, grad_c_last};
+  const size_t insz[8] = {nb, nb, nb, nb, nb, sb, cb, cb};
+  const void* outs[5] = {grad_zf, grad_zi, grad_zc, grad_zo, grad_c0};
+  const size_t outsz[5] = {nb, nb, nb, nb, cb};
+  for (int o = 0; o < 5; ++o) {
+    for (int i = 0; i < 8; ++i)
+      if (overlap(outs[o], outsz[o], ins[i], insz[i])) return LRS_ERR_INVALID_ARG;
+    for (int o2 = o + 1; o2 < 5; ++o2)
+      if (overlap(outs[o], outsz[o], outs[o2], outsz[o2])) return LRS_ERR_INVALID_ARG;
+  }
+  const lrs::ColPlan p = lrs::plan_lstm_bwd(C, T, io_dtype);
+  if (!grid_ok(p.ncb * p.ntb, p.nw * 64)) return LRS_ERR_UNSUPPORTED;
+  uint64_t* status;
+  unsigned* tickets;
+  const int rc = col_lookback(p, workspace, workspace_bytes, s, &status, &tickets);
+  if (rc != LRS_OK) return rc;
+  const size_t rowbytes = (size_t)p.cpt * es;
+  int vec = (C % p.cpt == 0) && aligned(c_states, (size_t)p.cpt * 4);
+  for (int i = 0; i < 9; ++i) vec = vec && aligned(io[i], rowbytes);
+  return hip_status(lrs::launch_lstm_bwd(z_f, z_i, z_c, z_o, c0, c_states, grad_h, grad_c_last,
+                                         grad_zf, grad_zi, grad_zc, grad_zo, grad_c0, T, C,
+                                         io_dtype, p, vec, status, tickets, s));
+}
+
 // ------------------------------------------------------------------- DEER
 
 static lrs::RowPlan deer_plan(int64_t C, int64_t T) { return lrs::plan_deer_rows(C, T); }

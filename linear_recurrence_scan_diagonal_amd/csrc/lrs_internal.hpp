@@ -107,4 +107,18 @@ hipError_t launch_sru_bwd(const void* zf, const void* zr, const void* zx, const 
                           int64_t D, int io_dtype, const ColPlan& p, int vec, uint64_t* status,
                           unsigned* tickets, hipStream_t stream);
 
+// LSTM cell-state layer with input-only gates (gated_cell.hip).  `save`: the
+// forward also writes the cell states.
+ColPlan plan_lstm(int64_t C, int64_t T, int io_dtype, bool save);
+ColPlan plan_lstm_bwd(int64_t C, int64_t T, int io_dtype);
+hipError_t launch_lstm_fwd(const void* zf, const void* zi, const void* zc, const void* zo,
+                           const float* c0, void* h, float* c_last, float* c_states, int64_t T,
+                           int64_t C, int io_dtype, const ColPlan& p, int vec, uint64_t* status,
+                           unsigned* tickets, hipStream_t stream);
+hipError_t launch_lstm_bwd(const void* zf, const void* zi, const void* zc, const void* zo,
+                           const float* c0, const float* cs, const void* gh, const float* gcl,
+                           void* dzf, void* dzi, void* dzc, void* dzo, float* dc0, int64_t T,
+                           int64_t C, int io_dtype, const ColPlan& p, int vec, uint64_t* status,
+                           unsigned* tickets, hipStream_t stream);
+
 }  // namespace lrs

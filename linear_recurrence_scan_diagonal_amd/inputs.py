@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the scan, SRU and DEER workloads.
+"""Seeded synthetic inputs for the scan, SRU, LSTM and DEER workloads.
 
 This module only draws random numbers and converts number formats; it holds
 none of the method's arithmetic, so both the device path and the CPU oracle
@@ -18,7 +18,7 @@ Recipe (the same everywhere):
     draws from [lo, hi).
 
 Array tags: a=1, b=2, h0=3, g=4, zf=5, zr=6, zx=7, bias_f=8, bias_r=9, w=10,
-u=11, h_init=12.
+u=11, h_init=12, gh=13, gcl=14, zi=15, zc=16, zo=17.
 """
 from __future__ import annotations
 
@@ -29,7 +29,8 @@ from dataclasses import dataclass, field
 import numpy as np
 
 TAGS = {"a": 1, "b": 2, "h0": 3, "g": 4, "zf": 5, "zr": 6, "zx": 7, "bias_f": 8,
-        "bias_r": 9, "w": 10, "u": 11, "h_init": 12, "gh": 13, "gcl": 14}
+        "bias_r": 9, "w": 10, "u": 11, "h_init": 12, "gh": 13, "gcl": 14, "zi": 15, "zc": 16,
+        "zo": 17}
 
 
 def _rng(*key) -> np.random.Generator:
@@ -116,7 +117,7 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "scan", "sru" or "deer"
+    kind: str                 # "scan", "sru", "lstm" or "deer"
     B: int
     D: int
     T: int
@@ -161,6 +162,14 @@ WORKLOADS = {
          "gh": ("normal", 0.0, 1.0)},
         "SRU forward + backward, bf16 I/O fp32 state, B=32 D=1024 T=2048, z~N(0,1), "
         "b_f,b_r~N(-1,0.1), c0=0, dL/dh~N(0,1)"),
+    # LSTM cell-state layer with input-only gates, forward (saving the cell
+    # states) and backward, at the SRU shape
+    "lstm_fwd_bwd": Workload(
+        "lstm_fwd_bwd", "lstm", 32, 1024, 2048, 1008,
+        {"zf": ("normal", 0.0, 1.0), "zi": ("normal", 0.0, 1.0), "zc": ("normal", 0.0, 1.0),
+         "zo": ("normal", 0.0, 1.0), "gh": ("normal", 0.0, 1.0)},
+        "LSTM cell-state layer (input-only gates) forward + backward, bf16 I/O fp32 state, "
+        "B=32 D=1024 T=2048, z_f,z_i,z_c,z_o~N(0,1), c0=0, dL/dh~N(0,1)"),
     # very long forward + backward scan, fp32
     "scan_long": Workload(
         "scan_long", "scan", 2, 256, 1 << 20, 1004,
@@ -217,8 +226,18 @@ def sru_inputs(w: Workload) -> dict:
     return out
 
 
+def lstm_inputs(w: Workload) -> dict:
+    """bf16 bit patterns of the pre-activations zf, zi, zc, zo as [T, B, D] uint16."""
+    ch = np.arange(w.C)
+    out = {}
+    for k in ("zf", "zi", "zc", "zo"):
+        per_channel = to_bf16_bits(series(w.seed, k, w.dists[k], ch, w.T))  # [C, T]
+        out[k] = np.ascontiguousarray(per_channel.T).reshape(w.T, w.B, w.D)
+    return out
+
+
 def sru_grad_inputs(w: Workload, with_gcl: bool = False) -> dict:
-    """Upstream gradients for the SRU backward: dL/dh as bf16 bit patterns
+    """Upstream gradients for the SRU (and LSTM) backward: dL/dh as bf16 bit patterns
     [T, B, D] uint16 (drawn like the pre-activations), and optionally
     dL/dc_T as fp32 [B, D] from N(0,1)."""
     ch = np.arange(w.C)

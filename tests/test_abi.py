@@ -32,7 +32,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 17, names
     raw = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(raw, n), f"{n} declared in lrs.h but not exported"
@@ -77,6 +77,10 @@ def test_scan_workspace_queries(lib):
     # DEER backward: one dL/dw partial per channel and chunk
     assert lib.lrs_deer_bwd_workspace_bytes(16, 512, 8192) >= 16 * 512 * 4
     assert lib.lrs_deer_bwd_workspace_bytes(1, 1, -3) == 0
+    # LSTM: look-back words once a channel spans several time blocks
+    assert lib.lrs_lstm_workspace_bytes(2048, 32, 1024) >= 32 * 1024 * (2048 // 64) * 8
+    assert lib.lrs_lstm_workspace_bytes(16, 4, 8) == 0
+    assert lib.lrs_lstm_workspace_bytes(-1, 1, 1) == 0
 
 
 def test_validation_before_any_launch(lib):
@@ -139,6 +143,27 @@ def test_validation_before_any_launch(lib):
                             1, 1, 4, null, 0, null) == b.LRS_ERR_INVALID_ARG
     assert lib.lrs_deer_bwd(q(0x10000), null, q(0x20000), q(0x30000), q(0x50000), q(0x40000), null,
                             1, 1, 4, null, 0, null) == b.LRS_ERR_WORKSPACE
+    # LSTM forward: bad dtype, missing gate, saved states overlapping an input,
+    # a multi-block time axis without workspace
+    assert lib.lrs_lstm_fwd(p, p, p, p, null, p, null, null, 4, 1, 1, 2, null, 0,
+                            null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_lstm_fwd(p, null, p, p, null, p, null, null, 4, 1, 1, 1, null, 0,
+                            null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_lstm_fwd(zs[0], zs[1], zs[2], zs[3], null, zs[4], null, zs[2], 4, 1, 1, 1,
+                            null, 0, null) == b.LRS_ERR_INVALID_ARG
+    big = [q(0x1000000 * (i + 1)) for i in range(12)]
+    assert lib.lrs_lstm_fwd(big[0], big[1], big[2], big[3], null, big[4], null, null, 1024, 1, 1,
+                            1, null, 0, null) == b.LRS_ERR_WORKSPACE
+    # LSTM backward: missing saved states, a gradient overlapping another,
+    # a multi-block time axis without workspace
+    assert lib.lrs_lstm_bwd(p, p, p, p, null, null, p, null, p, p, p, p, null, 4, 1, 1, 1, null,
+                            0, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_lstm_bwd(big[0], big[1], big[2], big[3], null, big[4], big[5], null, big[6],
+                            big[7], big[7], big[8], null, 4, 1, 1, 1, null, 0,
+                            null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_lstm_bwd(big[0], big[1], big[2], big[3], null, big[4], big[5], null, big[6],
+                            big[7], big[8], big[9], null, 1024, 1, 1, 1, null, 0,
+                            null) == b.LRS_ERR_WORKSPACE
     assert lib.lrs_deer_stats(p, 1 << 20, 0, None, None, None, null) == b.LRS_ERR_INVALID_ARG
     assert lib.lrs_deer_stats(p, 64, 5, None, None, None, null) == b.LRS_ERR_WORKSPACE
 
