@@ -4,7 +4,8 @@
 Default workload (the headline metric): forward + backward fp32 scan,
 B=8, D=512, T=4096, [B,D,T] layout.  One step = lrs_scan_fwd then
 lrs_scan_bwd over the same resident inputs.  Other workloads (--workload):
-scan_long (T = 2^20), sru_fwd / sru_fwd_bwd (bf16 SRU layer), lstm_fwd_bwd
+scan_fused (the same step as one lrs_scan_fwd_bwd call), scan_long (T = 2^20),
+sru_fwd / sru_fwd_bwd (bf16 SRU layer), lstm_fwd_bwd
 (bf16 LSTM cell-state layer with input-only gates), deer / deer_fwd_bwd
 (Newton solve, and its backward), scan_fwd_small.
 
@@ -40,6 +41,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
 BYTES_PER_ELEM = {"scan_fwd_f32": 12, "scan_bwd_f32": 20, "sru_fwd_bf16": 8,
                   "sru_fwd_save_bf16": 12,  # + the fp32 cell states for the backward
                   "sru_bwd_bf16": 18,       # z_f, z_r, z_x, dL/dh, c in; three gradients out
+                  "scan_fused_f32": 24,     # a, b, dL/dh in; h, dL/da, dL/db out
                   "deer_iter_first": 8, "deer_iter": 12,
                   "deer_bwd_f32": 12,       # h, dL/dh in; dL/du out
                   "lstm_fwd_save_bf16": 14,  # four pre-activations in; h and c out
@@ -74,6 +76,7 @@ def measured_traffic(workload: str, kernel_key: str):
 # rocprof kernel names of each timed entry point (substring match)
 KERNEL_NAMES = {"scan_fwd_f32": ("k_scan_fwd_bdt", "k_scan_fwd_tbd"),
                 "scan_bwd_f32": ("k_scan_bwd_bdt", "k_scan_bwd_tbd"),
+                "scan_fused_f32": ("k_scan_fused_bdt",),
                 "sru_fwd_bf16": ("k_sru_fwd<unsigned short",),
                 "sru_fwd_save_bf16": ("k_sru_fwd<unsigned short",),
                 "sru_bwd_bf16": ("k_sru_bwd<unsigned short",),
@@ -85,6 +88,7 @@ KERNEL_NAMES = {"scan_fwd_f32": ("k_scan_fwd_bdt", "k_scan_fwd_tbd"),
 WORKLOAD_KERNELS = {"scan_fwd_small": ("scan_fwd_f32",),
                     "scan_fwd_bwd": ("scan_fwd_f32", "scan_bwd_f32"),
                     "scan_long": ("scan_fwd_f32", "scan_bwd_f32"),
+                    "scan_fused": ("scan_fused_f32",),
                     "sru_fwd": ("sru_fwd_bf16",),
                     "sru_fwd_bwd": ("sru_fwd_save_bf16", "sru_bwd_bf16"),
                     "deer": ("deer_solve",),
@@ -225,7 +229,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="scan_fwd_bwd",
-                   choices=["scan_fwd_bwd", "scan_long", "sru_fwd", "sru_fwd_bwd", "lstm_fwd_bwd",
+                   choices=["scan_fwd_bwd", "scan_fused", "scan_long", "sru_fwd", "sru_fwd_bwd", "lstm_fwd_bwd",
                             "deer", "deer_fwd_bwd", "scan_fwd_small"])
     p.add_argument("--layout", default="bdt", choices=["bdt", "tbd"])
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -379,7 +383,10 @@ def main():
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
         calls = {"scan_fwd_f32": lambda: lrs.scan_fwd(a, b, h0, layout=layout, out=h, workspace=ws)}
-        if not fwd_only:
+        if args.workload == "scan_fused":
+            calls = {"scan_fused_f32": lambda: lrs.scan_fwd_bwd(a, b, g, h0, layout=layout,
+                                                                out=(h, ga, gb, gh0), workspace=ws)}
+        elif not fwd_only:
             calls["scan_bwd_f32"] = lambda: lrs.scan_bwd(a, h, g, h0, layout=layout, grad_a=ga,
                                                          grad_b=gb, grad_h0=gh0, workspace=ws)
 
@@ -389,7 +396,8 @@ def main():
         kernels = list(calls)
         dtype = "f32"
         config = {"workload": w.name, "B": B, "D": D, "T": T, "layout": layout,
-                  "pass": "fwd" if fwd_only else "fwd+bwd"}
+                  "pass": "fwd" if fwd_only else ("fwd+bwd, one call" if args.workload == "scan_fused"
+                                                   else "fwd+bwd")}
     elif w.kind == "sru":
         s = I.sru_inputs(w)
         z = {k: torch.from_numpy(s[k].view(np.int16)).view(torch.bfloat16).to(dev)

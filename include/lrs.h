@@ -114,6 +114,22 @@ LRS_API int lrs_scan_bwd(const void *a, const void *h, const float *h0, const vo
                  void *grad_b, float *grad_h0, int64_t B, int64_t D, int64_t T, int layout,
                  int dtype, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Forward and backward scan in one call: the results of lrs_scan_fwd followed
+ * by lrs_scan_bwd on the same inputs ([P1] parallel-scan paragraph: both
+ * passes are scans).  For [B,D,T] channels of at most 8192 steps, one kernel
+ * does both with h kept on chip, reading a, b, grad_h and writing h, grad_a,
+ * grad_b (24 bytes per element instead of 32); h may then be NULL (the
+ * backward with the forward recomputed, 20 bytes per element).  Other shapes
+ * and layouts run the two passes and need h.
+ * Arrays as for lrs_scan_fwd / lrs_scan_bwd; workspace as lrs_scan_workspace_bytes.
+ * grad_b may be the same buffer as grad_h; no other output may overlap an
+ * input or another output.  Returns LRS_ERR_UNSUPPORTED when h is NULL and
+ * the shape needs the two passes. */
+LRS_API int lrs_scan_fwd_bwd(const void *a, const void *b, const float *h0, const void *grad_h,
+                             void *h, void *grad_a, void *grad_b, float *grad_h0, int64_t B,
+                             int64_t D, int64_t T, int layout, int dtype, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
 /* ----------------------------------------------------------------- SRU --- */
 
 /* Workspace bytes needed by lrs_sru_fwd for this shape (0 for an invalid one). */

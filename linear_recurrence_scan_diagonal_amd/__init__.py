@@ -10,7 +10,7 @@ ctypes layer: argument marshalling only, no compute and no fallback).
 DEER_DEFAULT_EPS = 1e-5
 DEER_DEFAULT_KMAX = 5
 
-_BINDING_NAMES = ("scan_fwd", "scan_bwd", "sru_fwd", "sru_bwd", "deer_solve", "deer_stats",
+_BINDING_NAMES = ("scan_fwd", "scan_bwd", "scan_fwd_bwd", "sru_fwd", "sru_bwd", "deer_solve", "deer_stats",
                   "deer_bwd", "lstm_fwd", "lstm_bwd", "scan_workspace_bytes",
                   "LrsError", "load")
 

@@ -26,7 +26,7 @@ EXPORTS = ("lrs_status_string", "lrs_version", "lrs_scan_workspace_bytes", "lrs_
            "lrs_scan_bwd", "lrs_sru_workspace_bytes", "lrs_sru_fwd", "lrs_deer_workspace_bytes",
            "lrs_deer_solve", "lrs_deer_stats", "lrs_sru_bwd_workspace_bytes", "lrs_sru_bwd",
            "lrs_deer_bwd_workspace_bytes", "lrs_deer_bwd", "lrs_lstm_workspace_bytes",
-           "lrs_lstm_fwd", "lrs_lstm_bwd")
+           "lrs_lstm_fwd", "lrs_lstm_bwd", "lrs_scan_fwd_bwd")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -62,6 +62,8 @@ def load():
     lib.lrs_scan_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int,
                                  _vp, _sz, _vp]
     lib.lrs_scan_bwd.restype = _int
+    lib.lrs_scan_fwd_bwd.argtypes = [_vp] * 8 + [_i64, _i64, _i64, _int, _int, _vp, _sz, _vp]
+    lib.lrs_scan_fwd_bwd.restype = _int
     lib.lrs_sru_workspace_bytes.argtypes = [_i64, _i64, _i64]
     lib.lrs_sru_workspace_bytes.restype = _sz
     lib.lrs_sru_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int,
@@ -185,6 +187,32 @@ def scan_bwd(a, h, grad_h, h0=None, layout: str = "bdt", need_grad_h0: bool = Tr
                            B, D, T, LAYOUTS[layout], DTYPES[a.dtype], _ptr(ws), nbytes,
                            _stream(a.device)), "lrs_scan_bwd")
     return ga, gb, gh0
+
+
+def scan_fwd_bwd(a, b, grad_h, h0=None, layout: str = "bdt", want_h: bool = True,
+                 need_grad_h0: bool = True, out=None, workspace=None):
+    """scan_fwd then scan_bwd in one call (one kernel for [B,D,T] channels of
+    up to 8192 steps).  Returns (h or None, grad_a, grad_b, grad_h0 or None).
+    want_h=False skips writing h (only where one kernel does both passes).
+    out: optional (h, grad_a, grad_b, grad_h0) tensors; grad_b may be grad_h."""
+    lib = load()
+    B, D, T = _dims(a, layout)
+    for name, t in (("a", a), ("b", b), ("grad_h", grad_h)):
+        _check_dev(name, t, a.dtype, a.shape)
+    _check_dev("h0", h0, torch.float32, (B, D))
+    if out is None:
+        out = (torch.empty_like(a) if want_h else None, torch.empty_like(a), torch.empty_like(a),
+               torch.empty((B, D), dtype=torch.float32, device=a.device) if need_grad_h0 else None)
+    h, ga, gb, gh0 = out
+    for name, t in (("h", h), ("grad_a", ga), ("grad_b", gb)):
+        _check_dev(name, t, a.dtype, a.shape)
+    _check_dev("grad_h0", gh0, torch.float32, (B, D))
+    nbytes = lib.lrs_scan_workspace_bytes(B, D, T, LAYOUTS[layout], DTYPES[a.dtype])
+    ws = _workspace(nbytes, a.device, workspace)
+    _call(lib.lrs_scan_fwd_bwd(_ptr(a), _ptr(b), _ptr(h0), _ptr(grad_h), _ptr(h), _ptr(ga),
+                               _ptr(gb), _ptr(gh0), B, D, T, LAYOUTS[layout], DTYPES[a.dtype],
+                               _ptr(ws), nbytes, _stream(a.device)), "lrs_scan_fwd_bwd")
+    return h, ga, gb, gh0
 
 
 def sru_fwd(z_f, z_r, z_x, bias_f, bias_r, c0=None, want_c_last: bool = False, out=None,

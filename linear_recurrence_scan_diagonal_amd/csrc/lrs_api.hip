@@ -255,6 +255,58 @@ int lrs_scan_bwd(const void* a, const void* h, const float* h0, const void* grad
                                              grad_h0, C, T, p, vec, status, tickets, s));
 }
 
+int lrs_scan_fwd_bwd(const void* a, const void* b, const float* h0, const void* grad_h, void* h,
+                     void* grad_a, void* grad_b, float* grad_h0, int64_t B, int64_t D, int64_t T,
+                     int layout, int dtype, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  int64_t C, N;
+  int rc = scan_common_checks(B, D, T, layout, dtype, &C, &N);
+  if (rc != LRS_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  if (N == 0) {
+    if (T == 0 && C > 0 && grad_h0) return hip_status(lrs::launch_copy_or_zero(grad_h0, nullptr, C, s));
+    return LRS_OK;
+  }
+  if (!a || !b || !grad_h || !grad_a || !grad_b) return LRS_ERR_INVALID_ARG;
+  if (!aligned(a, 4) || !aligned(b, 4) || !aligned(grad_h, 4) || !aligned(grad_a, 4) ||
+      !aligned(grad_b, 4) || (h && !aligned(h, 4)) || (h0 && !aligned(h0, 4)) ||
+      (grad_h0 && !aligned(grad_h0, 4)))
+    return LRS_ERR_INVALID_ARG;
+  const size_t nb = (size_t)N * 4, cb = (size_t)C * 4;
+  // outputs must not overlap inputs or each other, except grad_b == grad_h exactly
+  const void* ins[4] = {a, b, h0, grad_h};
+  const size_t insz[4] = {nb, nb, cb, nb};
+  const void* outs[4] = {h, grad_a, grad_b, grad_h0};
+  const size_t outsz[4] = {nb, nb, nb, cb};
+  for (int o = 0; o < 4; ++o) {
+    for (int i = 0; i < 4; ++i) {
+      if (o == 2 && i == 3 && grad_b == grad_h) continue;
+      if (overlap(outs[o], outsz[o], ins[i], insz[i])) return LRS_ERR_INVALID_ARG;
+    }
+    for (int o2 = o + 1; o2 < 4; ++o2)
+      if (overlap(outs[o], outsz[o], outs[o2], outsz[o2])) return LRS_ERR_INVALID_ARG;
+  }
+  const lrs::RowPlan p = lrs::plan_scan_fused_rows(C, T);
+  if (layout == LRS_LAYOUT_BDT && p.nchunk == 1) {
+    if (!grid_ok(C, p.threads())) return LRS_ERR_UNSUPPORTED;
+    const bool al16 = aligned(a, 16) && aligned(b, 16) && aligned(grad_h, 16) &&
+                      aligned(grad_a, 16) && aligned(grad_b, 16) && (!h || aligned(h, 16));
+    const int vec = al16 && (T % 4 == 0);
+    return hip_status(lrs::launch_scan_fused_bdt((const float*)a, (const float*)b, h0,
+                                                 (const float*)grad_h, (float*)h, (float*)grad_a,
+                                                 (float*)grad_b, grad_h0, C, T, p, vec, s));
+  }
+  // the two passes, h stored between them (both validated before the first launch)
+  if (!h) return LRS_ERR_UNSUPPORTED;
+  size_t need = 0;
+  scan_ws_needs(C, T, layout, &need);
+  if (need && (!workspace || workspace_bytes < need)) return LRS_ERR_WORKSPACE;
+  rc = lrs_scan_fwd(a, b, h0, h, B, D, T, layout, dtype, workspace, workspace_bytes, stream);
+  if (rc != LRS_OK) return rc;
+  return lrs_scan_bwd(a, h, h0, grad_h, grad_a, grad_b, grad_h0, B, D, T, layout, dtype,
+                      workspace, workspace_bytes, stream);
+}
+
 // -------------------------------------------------------------------- SRU
 
 size_t lrs_sru_workspace_bytes(int64_t T, int64_t B, int64_t D) {

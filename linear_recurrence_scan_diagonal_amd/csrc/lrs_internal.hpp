@@ -28,6 +28,7 @@ struct RowPlan {
 RowPlan plan_scan_fwd_rows(int64_t C, int64_t T);
 RowPlan plan_scan_bwd_rows(int64_t C, int64_t T);
 RowPlan plan_deer_rows(int64_t C, int64_t T);
+RowPlan plan_scan_fused_rows(int64_t C, int64_t T);
 RowPlan plan_deer_bwd_rows(int64_t C, int64_t T);
 
 // Feature-contiguous kernels: blocks of 64*cpt channels x nw*l steps.
@@ -55,6 +56,10 @@ hipError_t launch_scan_bwd_bdt(const float* a, const float* h, const float* h0, 
                                float* da, float* db, float* dh0, int64_t C, int64_t T,
                                const RowPlan& p, int vec, uint64_t* status, unsigned* tickets,
                                hipStream_t stream);
+// Forward and backward scan in one pass; the plan must be single-chunk.
+hipError_t launch_scan_fused_bdt(const float* a, const float* b, const float* h0, const float* g,
+                                 float* h, float* da, float* db, float* dh0, int64_t C, int64_t T,
+                                 const RowPlan& p, int vec, hipStream_t stream);
 // DEER update norms: three rotating sets of kDeltaSlots words, kDeltaStride
 // words apart (one cache line per slot).
 constexpr int kDeltaSlots = 64;

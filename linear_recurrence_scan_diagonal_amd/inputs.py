@@ -147,6 +147,13 @@ WORKLOADS = {
          "g": ("normal", 0.0, 1.0)},
         "forward+backward linear scan, fp32, B=8 D=512 T=4096, a~U(0.8,0.999), b~N(0,1), "
         "h0~N(0,1), dL/dh~N(0,1)"),
+    # the same forward + backward scan as one lrs_scan_fwd_bwd call (same inputs)
+    "scan_fused": Workload(
+        "scan_fused", "scan", 8, 512, 4096, 1002,
+        {"a": ("uniform", 0.8, 0.999), "b": ("normal", 0.0, 1.0), "h0": ("normal", 0.0, 1.0),
+         "g": ("normal", 0.0, 1.0)},
+        "forward+backward linear scan in one call, fp32, B=8 D=512 T=4096, inputs as "
+        "scan_fwd_bwd"),
     # SRU layer forward, bf16 I/O, fp32 state, [T, B, D]
     "sru_fwd": Workload(
         "sru_fwd", "sru", 32, 1024, 2048, 1003,

@@ -32,7 +32,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     raw = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(raw, n), f"{n} declared in lrs.h but not exported"
@@ -164,6 +164,16 @@ def test_validation_before_any_launch(lib):
     assert lib.lrs_lstm_bwd(big[0], big[1], big[2], big[3], null, big[4], big[5], null, big[6],
                             big[7], big[8], big[9], null, 1024, 1, 1, 1, null, 0,
                             null) == b.LRS_ERR_WORKSPACE
+    # fused forward + backward: h may be left out only where one kernel does
+    # both passes ([B,D,T], T <= 8192); an output overlapping an input
+    assert lib.lrs_scan_fwd_bwd(big[0], big[1], null, big[2], null, big[3], big[4], null, 1, 1,
+                                16384, 0, 0, null, 0, null) == b.LRS_ERR_UNSUPPORTED
+    assert lib.lrs_scan_fwd_bwd(big[0], big[1], null, big[2], null, big[3], big[4], null, 1, 1,
+                                64, 1, 0, null, 0, null) == b.LRS_ERR_UNSUPPORTED
+    assert lib.lrs_scan_fwd_bwd(big[0], big[1], null, big[2], big[1], big[3], big[4], null, 1, 1,
+                                64, 0, 0, null, 0, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_scan_fwd_bwd(big[0], big[1], null, big[2], big[5], big[3], big[4], null, 1, 1,
+                                1 << 20, 0, 0, null, 0, null) == b.LRS_ERR_WORKSPACE
     assert lib.lrs_deer_stats(p, 1 << 20, 0, None, None, None, null) == b.LRS_ERR_INVALID_ARG
     assert lib.lrs_deer_stats(p, 64, 5, None, None, None, null) == b.LRS_ERR_WORKSPACE
 
