@@ -4,7 +4,8 @@
 Default workload (the headline metric): forward + backward fp32 scan,
 B=8, D=512, T=4096, [B,D,T] layout.  One step = lrs_scan_fwd then
 lrs_scan_bwd over the same resident inputs.  Other workloads (--workload):
-scan_fused (the same step as one lrs_scan_fwd_bwd call), scan_long (T = 2^20),
+scan_fused (the same step as one lrs_scan_fwd_bwd call), scan_short (T = 32,
+sequential kernels), scan_long (T = 2^20),
 sru_fwd / sru_fwd_bwd (bf16 SRU layer), lstm_fwd_bwd
 (bf16 LSTM cell-state layer with input-only gates), deer / deer_fwd_bwd
 (Newton solve, and its backward), scan_fwd_small.
@@ -89,6 +90,7 @@ WORKLOAD_KERNELS = {"scan_fwd_small": ("scan_fwd_f32",),
                     "scan_fwd_bwd": ("scan_fwd_f32", "scan_bwd_f32"),
                     "scan_long": ("scan_fwd_f32", "scan_bwd_f32"),
                     "scan_fused": ("scan_fused_f32",),
+                    "scan_short": ("scan_fwd_f32", "scan_bwd_f32"),
                     "sru_fwd": ("sru_fwd_bf16",),
                     "sru_fwd_bwd": ("sru_fwd_save_bf16", "sru_bwd_bf16"),
                     "deer": ("deer_solve",),
@@ -229,7 +231,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="scan_fwd_bwd",
-                   choices=["scan_fwd_bwd", "scan_fused", "scan_long", "sru_fwd", "sru_fwd_bwd", "lstm_fwd_bwd",
+                   choices=["scan_fwd_bwd", "scan_fused", "scan_short", "scan_long", "sru_fwd", "sru_fwd_bwd", "lstm_fwd_bwd",
                             "deer", "deer_fwd_bwd", "scan_fwd_small"])
     p.add_argument("--layout", default="bdt", choices=["bdt", "tbd"])
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -237,6 +239,9 @@ def parse():
                    help="also time the step captured as a HIP graph and replayed")
     p.add_argument("--no-stream-ref", action="store_true",
                    help="skip the read-2/write-1 stream reference kernel")
+    p.add_argument("--crossover", action="store_true",
+                   help="time the sequential and the parallel scan kernels at T = 4 .. 8192 "
+                        "(2^24 elements) and print a table, instead of the bench line")
     p.add_argument("--summarize", metavar="DIR",
                    help="summarise rocprofv3 CSV output under DIR into profiles/ and exit")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -358,6 +363,9 @@ def main():
 
     lrs.load()  # fail loudly if the HIP library is not built
     dev = torch.device("cuda:0")
+    if args.crossover:
+        crossover(args, np, torch, lrs, I, dev)
+        return
     w = I.WORKLOADS[args.workload]
     B, D, T = w.B, w.D, w.T
     N = w.N
@@ -579,6 +587,66 @@ def main():
             "data": "synthetic", "config": config, "roofline": roofline, "cpu_baseline": cpu,
             **extra, "csrc_hash": csrc_hash()}
     print(json.dumps(line), flush=True)
+
+
+def crossover(args, np, torch, lrs, I, dev):
+    """Sequential (one lane per channel) vs parallel scan kernels for short
+    channels: the headline workload's 2^24 elements of a, b, dL/dh regrouped
+    as [1, 2^24/T, T] for T = 4 .. 8192, each kernel forced through the
+    crossover overrides the library reads (LRS_SERIAL_FWD_MAX_T /
+    LRS_SERIAL_BWD_MAX_T), timed with HIP events over --steps calls."""
+    w = I.WORKLOADS["scan_fwd_bwd"]
+    x = I.scan_inputs(w)
+    N = w.N
+    flat = {k: torch.from_numpy(np.ascontiguousarray(x[k]).reshape(-1)).to(dev)
+            for k in ("a", "b", "g")}
+    h = torch.empty(N, device=dev)
+    ga, gb = torch.empty(N, device=dev), torch.empty(N, device=dev)
+    ws = torch.empty(max(1, lrs.scan_workspace_bytes(1, N // 4, 4)), dtype=torch.uint8,
+                     device=dev)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(args.steps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) * 1e3 / args.steps
+
+    env = os.environ
+    keys = ("LRS_SERIAL_FWD_MAX_T", "LRS_SERIAL_BWD_MAX_T")
+    saved = {k: env.get(k) for k in keys}
+    rows = []
+    T = 4
+    while T <= 8192:
+        D = N // T
+        a, b, g = (flat[k].view(1, D, T) for k in ("a", "b", "g"))
+        hv, gav, gbv = h.view(1, D, T), ga.view(1, D, T), gb.view(1, D, T)
+        res = {}
+        for mode, lim in (("serial", str(1 << 40)), ("parallel", "0")):
+            for k in keys:
+                env[k] = lim
+            res[mode] = (timed(lambda: lrs.scan_fwd(a, b, None, out=hv, workspace=ws)),
+                         timed(lambda: lrs.scan_bwd(a, hv, g, None, need_grad_h0=False,
+                                                    grad_a=gav, grad_b=gbv, workspace=ws)))
+        for k in keys:
+            if saved[k] is None:
+                env.pop(k, None)
+            else:
+                env[k] = saved[k]
+        rows.append((T, D, res["serial"], res["parallel"]))
+        T *= 2
+    pct = lambda us, bpe: 100.0 * bpe * N / (us * 1e-6) / 1e9 / HBM_PEAK_GBS
+    print(f"# crossover, {N} elements (fwd 12 B, bwd 20 B per element), us and % of 8 TB/s")
+    print("| T | channels | serial fwd | parallel fwd | serial bwd | parallel bwd |")
+    print("|---|---|---|---|---|---|")
+    for T, D, (sf, sb), (pf, pb) in rows:
+        print(f"| {T} | {D} | {sf:.1f} ({pct(sf, 12):.0f}%) | {pf:.1f} ({pct(pf, 12):.0f}%) | "
+              f"{sb:.1f} ({pct(sb, 20):.0f}%) | {pb:.1f} ({pct(pb, 20):.0f}%) |", flush=True)
 
 
 STREAM_REF_ELEMS = 1 << 26  # 256 MiB per fp32 operand

@@ -287,7 +287,10 @@ int lrs_scan_fwd_bwd(const void* a, const void* b, const float* h0, const void* 
       if (overlap(outs[o], outsz[o], outs[o2], outsz[o2])) return LRS_ERR_INVALID_ARG;
   }
   const lrs::RowPlan p = lrs::plan_scan_fused_rows(C, T);
-  if (layout == LRS_LAYOUT_BDT && p.nchunk == 1) {
+  // channels short enough for the sequential kernels run those two passes
+  // when h is wanted anyway (one lane per channel beats a mostly idle workgroup)
+  const bool short_pair = h && lrs::plan_scan_fwd_rows(C, T).serial;
+  if (layout == LRS_LAYOUT_BDT && p.nchunk == 1 && !short_pair) {
     if (!grid_ok(C, p.threads())) return LRS_ERR_UNSUPPORTED;
     const bool al16 = aligned(a, 16) && aligned(b, 16) && aligned(grad_h, 16) &&
                       aligned(grad_a, 16) && aligned(grad_b, 16) && (!h || aligned(h, 16));

@@ -22,6 +22,7 @@ struct RowPlan {
   int64_t nchunk = 1;
   bool stream = false;  // nontemporal loads and stores (arrays far larger than the caches)
   int sub = 1;          // sequential sub-chunks per workgroup (single-workgroup channels)
+  bool serial = false;  // short channels: one lane walks each channel (scan_serial.hip)
   int threads() const { return nw * 64; }
   int64_t chunk() const { return (int64_t)nw * r * 256; }
 };
@@ -56,6 +57,12 @@ hipError_t launch_scan_bwd_bdt(const float* a, const float* h, const float* h0, 
                                float* da, float* db, float* dh0, int64_t C, int64_t T,
                                const RowPlan& p, int vec, uint64_t* status, unsigned* tickets,
                                hipStream_t stream);
+// Sequential per-channel scans (one lane per channel) for short channels.
+hipError_t launch_scan_fwd_serial(const float* a, const float* b, const float* h0, float* h,
+                                  int64_t C, int64_t T, int vec, hipStream_t stream);
+hipError_t launch_scan_bwd_serial(const float* a, const float* h, const float* h0, const float* g,
+                                  float* da, float* db, float* dh0, int64_t C, int64_t T, int vec,
+                                  hipStream_t stream);
 // Forward and backward scan in one pass; the plan must be single-chunk.
 hipError_t launch_scan_fused_bdt(const float* a, const float* b, const float* h0, const float* g,
                                  float* h, float* da, float* db, float* dh0, int64_t C, int64_t T,

@@ -154,6 +154,13 @@ WORKLOADS = {
          "g": ("normal", 0.0, 1.0)},
         "forward+backward linear scan in one call, fp32, B=8 D=512 T=4096, inputs as "
         "scan_fwd_bwd"),
+    # forward + backward scan of many short channels (sequential kernels)
+    "scan_short": Workload(
+        "scan_short", "scan", 256, 2048, 32, 1009,
+        {"a": ("uniform", 0.8, 0.999), "b": ("normal", 0.0, 1.0), "h0": ("normal", 0.0, 1.0),
+         "g": ("normal", 0.0, 1.0)},
+        "forward+backward linear scan of short channels, fp32, B=256 D=2048 T=32, "
+        "distributions as scan_fwd_bwd"),
     # SRU layer forward, bf16 I/O, fp32 state, [T, B, D]
     "sru_fwd": Workload(
         "sru_fwd", "sru", 32, 1024, 2048, 1003,
