@@ -16,11 +16,13 @@ Functions (page citations are in ``lrs_oracle.c``):
   sru_bwd(zf, ..., gh, c0, gcl) SRU layer gradients -> dict of six arrays
   lstm_fwd(zf, zi, zc, zo, c0)  LSTM cell-state layer, input-only gates -> (h, c_last)
   lstm_bwd(..., gh, c0, gcl)    its gradients -> dict of five arrays
+  sru_nl_seq(zf, ..., vf, c0)   SRU with v_f*c_{t-1} in the forget gate, sequential
+  sru_deer(zf, ..., vf, c0)     the same by DEER Newton iterations -> (h, c, iters, deltas)
   rnn_seq(w, u, h0)             sequential h_t = tanh(w h_{t-1} + u_t)
   deer(w, u, h0, ...)           Newton / DEER iterations -> (h, iters, deltas)
   deer_bwd(w, h, g, h0)         adjoint of the RNN at its solution -> (du, dw, dh0)
 
-Parity status: all nine are pinned by tests/test_oracle_*.py against closed
+Parity status: all eleven are pinned by tests/test_oracle_*.py against closed
 forms, exact rational brute force, adjoint identities, finite differences and
 Newton invariants.
 """
@@ -71,6 +73,12 @@ def _load():
     lib.lrs_oracle_deer_bwd.argtypes = [_c_dp] * 7 + [_i64, _i64, _i64, ctypes.c_int]
     lib.lrs_oracle_lstm_fwd.argtypes = [_c_dp] * 7 + [_i64, _i64, _i64, ctypes.c_int]
     lib.lrs_oracle_lstm_bwd.argtypes = [_c_dp] * 12 + [_i64, _i64, _i64, ctypes.c_int]
+    lib.lrs_oracle_sru_nl_seq.argtypes = [_c_dp] * 9 + [_i64, _i64, _i64, ctypes.c_int]
+    lib.lrs_oracle_sru_deer.argtypes = [_c_dp] * 10 + [_i64, _i64, _i64, ctypes.c_double,
+                                                       ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                                       _c_dp, ctypes.c_int]
+    lib.lrs_oracle_sru_nl_seq.restype = ctypes.c_int
+    lib.lrs_oracle_sru_deer.restype = ctypes.c_int
     for fn in (lib.lrs_oracle_scan_fwd, lib.lrs_oracle_scan_bwd, lib.lrs_oracle_sru_fwd,
                lib.lrs_oracle_rnn_seq, lib.lrs_oracle_deer, lib.lrs_oracle_sru_bwd,
                lib.lrs_oracle_deer_bwd, lib.lrs_oracle_lstm_fwd, lib.lrs_oracle_lstm_bwd):
@@ -186,6 +194,45 @@ def lstm_bwd(zf, zi, zc, zo, gh, c0=None, gcl=None, nthreads: int = 0):
                                        _ptr(out["dzc"]), _ptr(out["dzo"]), _ptr(out["dc0"]), T, B,
                                        D, nthreads), "lstm_bwd")
     return out
+
+
+def _sru_nl_args(zf, zr, zx, bf, br, vf, c0):
+    zf, zr, zx, bf, br, vf, c0 = map(_f64, (zf, zr, zx, bf, br, vf, c0))
+    if not (zf.shape == zr.shape == zx.shape) or zf.ndim != 3:
+        raise ValueError("zf, zr, zx must be [T, B, D]")
+    D = zf.shape[2]
+    if bf.shape != (D,) or br.shape != (D,) or vf.shape != (D,):
+        raise ValueError("bf, br, vf must be [D]")
+    return zf, zr, zx, bf, br, vf, c0
+
+
+def sru_nl_seq(zf, zr, zx, bf, br, vf, c0=None, nthreads: int = 0):
+    """SRU layer whose forget gate reads v_f * c_{t-1}, by the sequential loop.
+    Returns (h [T,B,D], c [T,B,D])."""
+    zf, zr, zx, bf, br, vf, c0 = _sru_nl_args(zf, zr, zx, bf, br, vf, c0)
+    T, B, D = zf.shape
+    h, c = np.empty_like(zf), np.empty_like(zf)
+    _check(_load().lrs_oracle_sru_nl_seq(_ptr(zf), _ptr(zr), _ptr(zx), _ptr(bf), _ptr(br),
+                                         _ptr(vf), _ptr(c0), _ptr(c), _ptr(h), T, B, D, nthreads),
+           "sru_nl_seq")
+    return h, c
+
+
+def sru_deer(zf, zr, zx, bf, br, vf, c0=None, c_init=None, eps: float = 1e-5, k_max: int = 5,
+             nthreads: int = 0):
+    """The same layer's cell states by DEER Newton iterations.
+    Returns (h, c, iters, deltas)."""
+    zf, zr, zx, bf, br, vf, c0 = _sru_nl_args(zf, zr, zx, bf, br, vf, c0)
+    c_init = _f64(c_init)
+    T, B, D = zf.shape
+    h, c = np.empty_like(zf), np.empty_like(zf)
+    iters = ctypes.c_int(0)
+    deltas = np.zeros(max(k_max, 1))
+    _check(_load().lrs_oracle_sru_deer(_ptr(zf), _ptr(zr), _ptr(zx), _ptr(bf), _ptr(br), _ptr(vf),
+                                       _ptr(c0), _ptr(c_init), _ptr(c), _ptr(h), T, B, D,
+                                       float(eps), int(k_max), ctypes.byref(iters), _ptr(deltas),
+                                       nthreads), "sru_deer")
+    return h, c, iters.value, deltas[: iters.value].copy()
 
 
 def deer_bwd(w, h, g, h0=None, nthreads: int = 0):

@@ -307,6 +307,113 @@ int lrs_oracle_lstm_bwd(const double *zf, const double *zi, const double *zc,
     return fail ? ORACLE_ENOMEM : ORACLE_OK;
 }
 
+/* SRU layer with the forget gate reading the previous cell state ([P1] SRU
+ * paragraph: f_t = sigmoid(W_f x_t + v_f (.) c_{t-1} + b_f)); the reset gate
+ * and the highway output are as in lrs_oracle_sru_fwd.  With v_f != 0 the
+ * cell recurrence is element-wise nonlinear:
+ *   f_t = sigmoid(zf_t + bf[d] + vf[d] * c_{t-1})
+ *   c_t = f_t * c_{t-1} + (1 - f_t) * zx_t,   h_t = r_t tanh(c_t) + (1 - r_t) zx_t.
+ * This is the plain sequential loop (the ground truth for the Newton solve
+ * below).  Arrays [T, B, D]; bf, br, vf [D]; c0 [B, D] or NULL; c [T, B, D]
+ * receives every cell state, h the outputs (either may be NULL). */
+int lrs_oracle_sru_nl_seq(const double *zf, const double *zr, const double *zx,
+                          const double *bf, const double *br, const double *vf,
+                          const double *c0, double *c, double *h, int64_t T, int64_t B,
+                          int64_t D, int nthreads)
+{
+    if (T < 0 || B < 0 || D < 0) return ORACLE_EINVAL;
+    if (T * B * D > 0 && (!zf || !zr || !zx || !bf || !br || !vf)) return ORACLE_EINVAL;
+    set_threads(nthreads);
+    const int64_t C = B * D;
+#pragma omp parallel for schedule(static)
+    for (int64_t ch = 0; ch < C; ++ch) {
+        const int64_t d = ch % D;
+        double state = c0 ? c0[ch] : 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t i = t * C + ch;
+            const double f = sigmoid(zf[i] + bf[d] + vf[d] * state);
+            state = f * state + (1.0 - f) * zx[i];
+            if (c) c[i] = state;
+            if (h) {
+                const double r = sigmoid(zr[i] + br[d]);
+                h[i] = r * tanh(state) + (1.0 - r) * zx[i];
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* The same layer's cell states by DEER ([P4] core principle: Newton's method
+ * on the whole sequence, the inverse operator a linear recurrence with an
+ * initial condition; engineering section: stop when the update's norm is
+ * below eps or after k_max iterations).  With F(c_{t-1}) = f (c_{t-1} - zx) + zx
+ * the cell map and its derivative (diagonal Jacobian)
+ *   J_t = f + (c_{t-1} - zx) f (1 - f) vf[d],
+ * one iteration from the iterate y (y_{-1} = c0 fixed) solves
+ *   y'_t = J_t y'_{t-1} + (F(y_{t-1}) - J_t y_{t-1})
+ * sequentially, with f and J evaluated at y_{t-1}.  delta_i = max over all
+ * entries of |y' - y|; stop at delta_i < eps or i == k_max.  c_init is the
+ * starting iterate (NULL: zero).  c receives the last iterate; h, if not NULL,
+ * the layer output computed from it.  deltas (length >= k_max) gets
+ * delta_1..delta_iters and *iters the iteration count. */
+int lrs_oracle_sru_deer(const double *zf, const double *zr, const double *zx,
+                        const double *bf, const double *br, const double *vf,
+                        const double *c0, const double *c_init, double *c, double *h,
+                        int64_t T, int64_t B, int64_t D, double eps, int k_max, int *iters,
+                        double *deltas, int nthreads)
+{
+    if (T < 0 || B < 0 || D < 0 || k_max < 1 || !iters) return ORACLE_EINVAL;
+    const int64_t C = B * D, N = C * T;
+    if (N > 0 && (!zf || !zr || !zx || !bf || !br || !vf || !c)) return ORACLE_EINVAL;
+    set_threads(nthreads);
+    double *y = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+    double *yn = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+    if (!y || !yn) { free(y); free(yn); return ORACLE_ENOMEM; }
+    if (c_init && N > 0) memcpy(y, c_init, (size_t)N * sizeof(double));
+    else memset(y, 0, (size_t)(N > 0 ? N : 1) * sizeof(double));
+    int done = 0;
+    for (int i = 1; i <= k_max; ++i) {
+        double delta = 0.0;
+        int saw_nan = 0;
+#pragma omp parallel for schedule(static) reduction(max : delta) reduction(| : saw_nan)
+        for (int64_t ch = 0; ch < C; ++ch) {
+            const int64_t d = ch % D;
+            const double start = c0 ? c0[ch] : 0.0;
+            double state = start; /* y'_{-1} */
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t k = t * C + ch;
+                const double yprev = t > 0 ? y[k - C] : start;
+                const double f = sigmoid(zf[k] + bf[d] + vf[d] * yprev);
+                const double F = f * (yprev - zx[k]) + zx[k];
+                const double J = f + (yprev - zx[k]) * f * (1.0 - f) * vf[d];
+                state = J * state + (F - J * yprev);
+                yn[k] = state;
+                const double diff = fabs(state - y[k]);
+                if (diff != diff) saw_nan = 1;
+                else if (diff > delta) delta = diff;
+            }
+        }
+        if (saw_nan) delta = NAN;
+        double *tmp = y; y = yn; yn = tmp;
+        if (deltas) deltas[i - 1] = delta;
+        done = i;
+        if (delta < eps) break;
+    }
+    if (N > 0) memcpy(c, y, (size_t)N * sizeof(double));
+    if (h) {
+#pragma omp parallel for schedule(static)
+        for (int64_t k = 0; k < N; ++k) {
+            const int64_t d = k % D;
+            const double r = sigmoid(zr[k] + br[d]);
+            h[k] = r * tanh(y[k]) + (1.0 - r) * zx[k];
+        }
+    }
+    *iters = done;
+    free(y);
+    free(yn);
+    return ORACLE_OK;
+}
+
 /* Adjoint of the nonlinear RNN h_t = tanh(w_d h_{t-1} + u_t) at a solution h
  * (the DEER solve's result, [P4] core principle; the backward pass as a
  * reverse-time scan, [P1] parallel-scan paragraph).  With s_t = 1 - h_t^2 and
