@@ -6,7 +6,8 @@ B=8, D=512, T=4096, [B,D,T] layout.  One step = lrs_scan_fwd then
 lrs_scan_bwd over the same resident inputs.  Other workloads (--workload):
 scan_fused (the same step as one lrs_scan_fwd_bwd call), scan_short (T = 32,
 sequential kernels), scan_long (T = 2^20),
-sru_fwd / sru_fwd_bwd (bf16 SRU layer), lstm_fwd_bwd
+sru_fwd / sru_fwd_bwd (bf16 SRU layer), sru_deer (SRU with v_f*c_{t-1}
+by DEER), lstm_fwd_bwd
 (bf16 LSTM cell-state layer with input-only gates), deer / deer_fwd_bwd
 (Newton solve, and its backward), scan_fwd_small.
 
@@ -45,6 +46,9 @@ BYTES_PER_ELEM = {"scan_fwd_f32": 12, "scan_bwd_f32": 20, "sru_fwd_bf16": 8,
                   "scan_fused_f32": 24,     # a, b, dL/dh in; h, dL/da, dL/db out
                   "deer_iter_first": 8, "deer_iter": 12,
                   "deer_bwd_f32": 12,       # h, dL/dh in; dL/du out
+                  "sru_deer_iter_first": 8,  # z_f, z_x in; c' out (from c = 0)
+                  "sru_deer_iter": 12,       # z_f, z_x, c in; c' out
+                  "sru_deer_out": 10,        # z_r, z_x, c in; h out
                   "lstm_fwd_save_bf16": 14,  # four pre-activations in; h and c out
                   "lstm_bwd_bf16": 22}       # four pre-activations, dL/dh, c in; four gradients out
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
@@ -82,6 +86,7 @@ KERNEL_NAMES = {"scan_fwd_f32": ("k_scan_fwd_bdt", "k_scan_fwd_tbd"),
                 "sru_fwd_save_bf16": ("k_sru_fwd<unsigned short",),
                 "sru_bwd_bf16": ("k_sru_bwd<unsigned short",),
                 "deer_solve": ("k_deer_iter",),
+                "sru_deer_bf16": ("k_sru_deer_iter<unsigned short",),
                 "deer_bwd_f32": ("k_deer_bwd",),
                 "lstm_fwd_save_bf16": ("k_lstm_fwd<unsigned short",),
                 "lstm_bwd_bf16": ("k_lstm_bwd<unsigned short",)}
@@ -95,7 +100,10 @@ WORKLOAD_KERNELS = {"scan_fwd_small": ("scan_fwd_f32",),
                     "sru_fwd_bwd": ("sru_fwd_save_bf16", "sru_bwd_bf16"),
                     "deer": ("deer_solve",),
                     "deer_fwd_bwd": ("deer_solve", "deer_bwd_f32"),
+                    "sru_deer": ("sru_deer_bf16",),
                     "lstm_fwd_bwd": ("lstm_fwd_save_bf16", "lstm_bwd_bf16")}
+# entry points that launch one kernel per Newton iteration
+SOLVE_KEYS = ("deer_solve", "sru_deer_bf16")
 CALIB_NAME = "CUDAFunctor_add<float>"  # the stream reference kernel
 CALIB_READ = 2 * 4 * (1 << 26)
 CALIB_WRITE = 4 * (1 << 26)
@@ -161,12 +169,12 @@ def summarize(args):
     ep = []
     keys = WORKLOAD_KERNELS[wl]
     mains = [r for r in stats for key in keys
-             if key != "deer_solve" and any(p in r["Name"] for p in KERNEL_NAMES[key])]
+             if key not in SOLVE_KEYS and any(p in r["Name"] for p in KERNEL_NAMES[key])]
     main_calls = sum(int(r["Calls"]) for r in mains)
     for key in keys:
         pats = KERNEL_NAMES[key]
         for r in stats:
-            if any(p in r["Name"] for p in pats) and key != "deer_solve":
+            if any(p in r["Name"] for p in pats) and key not in SOLVE_KEYS:
                 share = reset_calls / main_calls if main_calls else 0.0
                 ep.append(f"{key}: {float(r['AverageNs'])/1e3:.2f} us kernel"
                           + (f" + {share:.0f} x {reset_us:.2f} us reset = "
@@ -202,7 +210,7 @@ def summarize(args):
                 continue
             hbm = f_ * factor["FETCH_SIZE"] + w_ * factor["WRITE_SIZE"]
             a = BYTES_PER_ELEM[key] * w.N if key in BYTES_PER_ELEM else None
-            if key == "deer_solve":
+            if key in SOLVE_KEYS:
                 # one launch per Newton iteration: first iteration 8 B/elem, then 12 B/elem
                 n_it = len([r for r in pmc["FETCH_SIZE"] if pat in r["Kernel_Name"]])
                 a = None
@@ -231,7 +239,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="scan_fwd_bwd",
-                   choices=["scan_fwd_bwd", "scan_fused", "scan_short", "scan_long", "sru_fwd", "sru_fwd_bwd", "lstm_fwd_bwd",
+                   choices=["scan_fwd_bwd", "scan_fused", "scan_short", "scan_long", "sru_fwd",
+                            "sru_deer", "sru_fwd_bwd", "lstm_fwd_bwd",
                             "deer", "deer_fwd_bwd", "scan_fwd_small"])
     p.add_argument("--layout", default="bdt", choices=["bdt", "tbd"])
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -465,6 +474,28 @@ def main():
         dtype = "bf16 I/O, f32 state"
         config = {"workload": w.name, "B": B, "D": D, "T": T, "layout": "tbd",
                   "pass": "fwd+bwd"}
+    elif w.kind == "sru_deer":
+        s = I.sru_inputs(w)
+        z = {k: torch.from_numpy(s[k].view(np.int16)).view(torch.bfloat16).to(dev)
+             for k in ("zf", "zr", "zx")}
+        pr = {k: torch.from_numpy(v).to(dev) for k, v in
+              (("bf", s["bias_f"]), ("br", s["bias_r"]), ("vf", I.sru_vf(w)))}
+        hs = torch.empty_like(z["zf"])
+        cs = torch.empty((T, B, D), dtype=torch.float32, device=dev)
+        ws = torch.empty(lrs.load().lrs_sru_deer_workspace_bytes(T, B, D, 5), dtype=torch.uint8,
+                         device=dev)
+
+        def sru_solve():
+            lrs.sru_deer_fwd(z["zf"], z["zr"], z["zx"], pr["bf"], pr["br"], pr["vf"], eps=1e-5,
+                             k_max=5, out=hs, c_states=cs, workspace=ws, sync=False)
+        calls = {"sru_deer_bf16": sru_solve}
+
+        def step():
+            sru_solve()
+        kernels = list(calls)
+        dtype = "bf16 I/O, f32 state"
+        config = {"workload": w.name, "B": B, "D": D, "T": T, "layout": "tbd", "eps": 1e-5,
+                  "k_max": 5, "pass": "solve"}
     else:  # deer
         x = I.deer_inputs(w)
         wd = torch.from_numpy(x["w"]).to(dev)
@@ -532,6 +563,8 @@ def main():
     per_kernel = step_kernel_ms(torch, calls, args.steps)
     extra["per_kernel_timing"] = ("HIP event (device-scope release) after every call of "
                                   "queued steps")
+    if w.kind == "sru_deer":
+        info = lrs.deer_stats(ws, 5)
     if w.kind == "deer":
         # the synchronous form reads the record back after every solve
         extra["ms_per_step_sync"] = round(timed(solve_sync, args.steps)[0], 5)
@@ -551,6 +584,13 @@ def main():
         bytes_step = sum(BYTES_PER_ELEM[k] * N for k in kernels)
         dom = max(kernels, key=lambda k: per_kernel[k])
         dom_bytes, dom_ms = BYTES_PER_ELEM[dom] * N, per_kernel[dom]
+    elif w.kind == "sru_deer":
+        iters = info["iters"]
+        bytes_step = (BYTES_PER_ELEM["sru_deer_iter_first"] + (iters - 1) *
+                      BYTES_PER_ELEM["sru_deer_iter"] + BYTES_PER_ELEM["sru_deer_out"]) * N
+        dom, dom_bytes, dom_ms = "sru_deer_bf16", bytes_step, per_kernel["sru_deer_bf16"]
+        extra["deer_iters"] = iters
+        extra["deer_deltas"] = info["deltas"]
     else:
         iters = info["iters"]
         solve_bytes = (BYTES_PER_ELEM["deer_iter_first"] + (iters - 1) * BYTES_PER_ELEM["deer_iter"]) * N
@@ -710,6 +750,16 @@ def cpu_baseline(w, args, np, I):
                 oracle.sru_bwd(*z, s["bias_f"], s["bias_r"], gh64, nthreads=threads)
         sample = (f"B=1 of {w.B}, D={sub.D}, T={T} (same recipe), "
                   f"fwd{'+bwd' if with_bwd else ''}")
+        n_el = sub.N
+    elif w.kind == "sru_deer":
+        sub = I.scaled(w, B=1, D=min(w.D, 1024))
+        s = I.sru_inputs(sub)
+        z = [I.bf16_bits_to_f64(s[k]) for k in ("zf", "zr", "zx")]
+        vf = I.sru_vf(sub)
+
+        def once():
+            oracle.sru_deer(*z, s["bias_f"], s["bias_r"], vf, eps=1e-5, k_max=5, nthreads=threads)
+        sample = f"B=1 of {w.B}, D={sub.D}, T={T} (same recipe), eps=1e-5, K_max=5"
         n_el = sub.N
     elif w.kind == "lstm":
         sub = I.scaled(w, B=1, D=min(w.D, 1024))

@@ -185,6 +185,39 @@ LRS_API int lrs_sru_bwd(const void *z_f, const void *z_r, const void *z_x, const
                 int64_t T, int64_t B, int64_t D, int io_dtype, void *workspace,
                 size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------- SRU by DEER --- */
+
+/* Workspace bytes needed by lrs_sru_deer_fwd (0 for an invalid or empty shape). */
+LRS_API size_t lrs_sru_deer_workspace_bytes(int64_t T, int64_t B, int64_t D, int k_max);
+
+/* SRU layer whose forget gate also reads the previous cell state ([P1] SRU
+ * paragraph, f_t = sigmoid(W_f x_t + v_f (.) c_{t-1} + b_f)), solved by DEER
+ * ([P4] core principle: Newton's method on the whole sequence, the linear
+ * inverse operator a recurrence solved by the parallel scan; engineering
+ * section: stop when ||c' - c||_inf < eps or after k_max iterations):
+ *   f_t = sigmoid(z_f,t + bias_f + v_f * c_{t-1}),  r_t = sigmoid(z_r,t + bias_r)
+ *   c_t = f_t * c_{t-1} + (1 - f_t) * z_x,t,        h_t = r_t tanh(c_t) + (1 - r_t) z_x,t
+ * Each iteration linearises the cell map around the current iterate (diagonal
+ * Jacobian J_t = f + (c_{t-1} - z_x) f (1 - f) v_f) and solves the resulting
+ * linear recurrence with the [T,B,D] scan; with v_f = 0 the first iteration
+ * is already lrs_sru_fwd's cell state.
+ * z_f, z_r, z_x, h: [T,B,D] in io_dtype.  bias_f, bias_r, v_f: [D] fp32.
+ * c0: [B,D] fp32 or NULL (zero).  c_init: starting iterate [T,B,D] fp32 or NULL
+ * (zero); it may be c_states itself (warm start in place).
+ * c_states: [T,B,D] fp32 output, the last iterate (the cell states, as
+ * lrs_sru_bwd takes them for the v_f = 0 layer).  c_last: [B,D] or NULL.
+ * iters_out, deltas_out (k_max floats), converged_out: host outputs as for
+ * lrs_deer_solve; with all three NULL the call only enqueues work and
+ * lrs_deer_stats reads the record from the workspace afterwards.
+ * Returns LRS_ERR_NONFINITE if the last update was NaN or infinite. */
+LRS_API int lrs_sru_deer_fwd(const void *z_f, const void *z_r, const void *z_x,
+                             const float *bias_f, const float *bias_r, const float *v_f,
+                             const float *c0, const float *c_init, void *h, float *c_states,
+                             float *c_last, int64_t T, int64_t B, int64_t D, int io_dtype,
+                             float eps, int k_max, int *iters_out, float *deltas_out,
+                             int *converged_out, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
 /* ---------------------------------------------------------------- LSTM --- */
 
 /* Workspace bytes needed by lrs_lstm_fwd and lrs_lstm_bwd for this shape, in
@@ -268,8 +301,8 @@ LRS_API int lrs_deer_solve(const float *w, const float *u, const float *h0, cons
                    float *deltas_out, int *converged_out, void *workspace,
                    size_t workspace_bytes, void *stream);
 
-/* Record of the most recent lrs_deer_solve that used this workspace with this
- * k_max (same meaning of iters_out, deltas_out, converged_out as there; each
+/* Record of the most recent lrs_deer_solve or lrs_sru_deer_fwd that used this
+ * workspace with this k_max (same meaning of iters_out, deltas_out, converged_out as there; each
  * may be NULL).  Waits for `stream`, on which that solve must have been
  * enqueued.  Returns LRS_ERR_NONFINITE when that solve's last delta was NaN or
  * infinite, LRS_ERR_WORKSPACE for a workspace too small for k_max, and

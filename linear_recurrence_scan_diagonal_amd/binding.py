@@ -26,7 +26,8 @@ EXPORTS = ("lrs_status_string", "lrs_version", "lrs_scan_workspace_bytes", "lrs_
            "lrs_scan_bwd", "lrs_sru_workspace_bytes", "lrs_sru_fwd", "lrs_deer_workspace_bytes",
            "lrs_deer_solve", "lrs_deer_stats", "lrs_sru_bwd_workspace_bytes", "lrs_sru_bwd",
            "lrs_deer_bwd_workspace_bytes", "lrs_deer_bwd", "lrs_lstm_workspace_bytes",
-           "lrs_lstm_fwd", "lrs_lstm_bwd", "lrs_scan_fwd_bwd")
+           "lrs_lstm_fwd", "lrs_lstm_bwd", "lrs_scan_fwd_bwd", "lrs_sru_deer_workspace_bytes",
+           "lrs_sru_deer_fwd")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -73,6 +74,11 @@ def load():
     lib.lrs_sru_bwd.argtypes = [_vp] * 15 + [_i64, _i64, _i64, _int, _vp, _sz, _vp]
     lib.lrs_sru_bwd.restype = _int
     lib.lrs_sru_fwd.restype = _int
+    lib.lrs_sru_deer_workspace_bytes.argtypes = [_i64, _i64, _i64, _int]
+    lib.lrs_sru_deer_workspace_bytes.restype = _sz
+    lib.lrs_sru_deer_fwd.argtypes = [_vp] * 11 + [_i64, _i64, _i64, _int, ctypes.c_float, _int,
+                                                  _vp, _vp, _vp, _vp, _sz, _vp]
+    lib.lrs_sru_deer_fwd.restype = _int
     lib.lrs_lstm_workspace_bytes.argtypes = [_i64, _i64, _i64]
     lib.lrs_lstm_workspace_bytes.restype = _sz
     lib.lrs_lstm_fwd.argtypes = [_vp] * 8 + [_i64, _i64, _i64, _int, _vp, _sz, _vp]
@@ -271,6 +277,53 @@ def sru_bwd(z_f, z_r, z_x, bias_f, bias_r, c_states, grad_h, c0=None, grad_c_las
                           _ptr(dzx), _ptr(dbf), _ptr(dbr), _ptr(dc0), T, B, D, DTYPES[io],
                           _ptr(ws), nbytes, _stream(dev)), "lrs_sru_bwd")
     return dzf, dzr, dzx, dbf, dbr, dc0
+
+
+def sru_deer_fwd(z_f, z_r, z_x, bias_f, bias_r, v_f, c0=None, c_init=None, eps: float = 1e-5,
+                 k_max: int = 5, want_c_last: bool = False, out=None, c_states=None,
+                 workspace=None, sync: bool = True):
+    """SRU layer with v_f * c_{t-1} in the forget gate, by DEER.  Returns
+    (h, c_states, c_last or None, info) where info = {"iters", "deltas",
+    "converged"} when sync, else None (read it later with deer_stats on the
+    returned workspace: info is then (h, c_states, c_last, workspace))."""
+    lib = load()
+    if z_f.dim() != 3:
+        raise ValueError("z_f must be [T,B,D]")
+    T, B, D = (int(x) for x in z_f.shape)
+    io = z_f.dtype
+    for name, t in (("z_f", z_f), ("z_r", z_r), ("z_x", z_x)):
+        _check_dev(name, t, io, z_f.shape)
+    for name, t in (("bias_f", bias_f), ("bias_r", bias_r), ("v_f", v_f)):
+        _check_dev(name, t, torch.float32, (D,))
+    _check_dev("c0", c0, torch.float32, (B, D))
+    _check_dev("c_init", c_init, torch.float32, z_f.shape)
+    h = torch.empty_like(z_f) if out is None else out
+    _check_dev("out", h, io, z_f.shape)
+    cs = torch.empty(z_f.shape, dtype=torch.float32, device=z_f.device) if c_states is None \
+        else c_states
+    _check_dev("c_states", cs, torch.float32, z_f.shape)
+    c_last = torch.empty((B, D), dtype=torch.float32, device=z_f.device) if want_c_last else None
+    nbytes = lib.lrs_sru_deer_workspace_bytes(T, B, D, int(k_max))
+    ws = _workspace(nbytes, z_f.device, workspace)
+    if sync:
+        iters = ctypes.c_int(0)
+        conv = ctypes.c_int(0)
+        deltas = (ctypes.c_float * max(1, int(k_max)))()
+        rc = lib.lrs_sru_deer_fwd(_ptr(z_f), _ptr(z_r), _ptr(z_x), _ptr(bias_f), _ptr(bias_r),
+                                  _ptr(v_f), _ptr(c0), _ptr(c_init), _ptr(h), _ptr(cs),
+                                  _ptr(c_last), T, B, D, DTYPES[io], float(eps), int(k_max),
+                                  ctypes.byref(iters), deltas, ctypes.byref(conv), _ptr(ws),
+                                  nbytes, _stream(z_f.device))
+        _call(rc, "lrs_sru_deer_fwd")
+        info = {"iters": iters.value, "deltas": [float(deltas[i]) for i in range(iters.value)],
+                "converged": bool(conv.value)}
+        return h, cs, c_last, info
+    _call(lib.lrs_sru_deer_fwd(_ptr(z_f), _ptr(z_r), _ptr(z_x), _ptr(bias_f), _ptr(bias_r),
+                               _ptr(v_f), _ptr(c0), _ptr(c_init), _ptr(h), _ptr(cs),
+                               _ptr(c_last), T, B, D, DTYPES[io], float(eps), int(k_max), None,
+                               None, None, _ptr(ws), nbytes, _stream(z_f.device)),
+          "lrs_sru_deer_fwd")
+    return h, cs, c_last, ws
 
 
 def lstm_fwd(z_f, z_i, z_c, z_o, c0=None, want_c_last: bool = False, out=None, workspace=None,

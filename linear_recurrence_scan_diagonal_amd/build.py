@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "liblrs.so")
 
-SOURCES = ["common.hip", "scan_bdt.hip", "scan_tbd.hip", "scan_serial.hip", "gated_cell.hip", "lrs_api.hip"]
+SOURCES = ["common.hip", "scan_bdt.hip", "scan_tbd.hip", "scan_serial.hip", "gated_cell.hip", "sru_deer.hip", "lrs_api.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops

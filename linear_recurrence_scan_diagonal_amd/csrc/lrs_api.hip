@@ -708,6 +708,114 @@ int lrs_deer_solve(const float* w, const float* u, const float* h0, const float*
   return read_deer_record(r, k_max, iters_out, deltas_out, converged_out, s);
 }
 
+// ------------------------------------------------------- SRU by DEER
+
+// Workspace: the solve record (first, so lrs_deer_stats reads it), a second
+// cell-state buffer and the look-back state of the [T,B,D] tile.
+size_t lrs_sru_deer_workspace_bytes(int64_t T, int64_t B, int64_t D, int k_max) {
+  int64_t C, N;
+  if (!shape_ok(B, D, T, &C, &N) || N == 0 || k_max < 1 || k_max > 1000000) return 0;
+  size_t need = 0;
+  for (int io = 0; io < 2; ++io) {
+    const lrs::ColPlan p = lrs::plan_sru_deer(C, T, io);
+    const size_t b = lookback_bytes(lrs::col_status_words(p), p.ncb);
+    need = b > need ? b : need;
+  }
+  return kAlign + deer_record_bytes(k_max) + align_up((size_t)N * 4) + need;
+}
+
+int lrs_sru_deer_fwd(const void* z_f, const void* z_r, const void* z_x, const float* bias_f,
+                     const float* bias_r, const float* v_f, const float* c0, const float* c_init,
+                     void* h, float* c_states, float* c_last, int64_t T, int64_t B, int64_t D,
+                     int io_dtype, float eps, int k_max, int* iters_out, float* deltas_out,
+                     int* converged_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int64_t C, N;
+  if (!shape_ok(B, D, T, &C, &N) || k_max < 1 || k_max > 1000000) return LRS_ERR_INVALID_ARG;
+  if (io_dtype != LRS_F32 && io_dtype != LRS_BF16) return LRS_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (N == 0) {
+    if (iters_out) *iters_out = 0;
+    if (converged_out) *converged_out = 1;
+    if (deltas_out) memset(deltas_out, 0, sizeof(float) * (size_t)k_max);
+    if (T == 0 && C > 0 && c_last) return hip_status(lrs::launch_copy_or_zero(c_last, c0, C, s));
+    return LRS_OK;
+  }
+  if (!z_f || !z_r || !z_x || !bias_f || !bias_r || !v_f || !h || !c_states)
+    return LRS_ERR_INVALID_ARG;
+  const size_t es = io_dtype == LRS_BF16 ? 2 : 4;
+  if (!aligned(z_f, es) || !aligned(z_r, es) || !aligned(z_x, es) || !aligned(h, es) ||
+      !aligned(bias_f, 4) || !aligned(bias_r, 4) || !aligned(v_f, 4) || !aligned(c_states, 4) ||
+      (c0 && !aligned(c0, 4)) || (c_init && !aligned(c_init, 4)) ||
+      (c_last && !aligned(c_last, 4)))
+    return LRS_ERR_INVALID_ARG;
+  const size_t nb = (size_t)N * es, cb = (size_t)C * 4, db = (size_t)D * 4, sb = (size_t)N * 4;
+  const void* ins[7] = {z_f, z_r, z_x, bias_f, bias_r, v_f, c0};
+  const size_t insz[7] = {nb, nb, nb, db, db, db, cb};
+  const void* outs[3] = {h, c_states, c_last};
+  const size_t outsz[3] = {nb, sb, cb};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 7; ++i)
+      if (overlap(outs[o], outsz[o], ins[i], insz[i])) return LRS_ERR_INVALID_ARG;
+    if (!(o == 1 && c_init == c_states) && overlap(outs[o], outsz[o], c_init, sb))
+      return LRS_ERR_INVALID_ARG;
+    for (int o2 = o + 1; o2 < 3; ++o2)
+      if (overlap(outs[o], outsz[o], outs[o2], outsz[o2])) return LRS_ERR_INVALID_ARG;
+  }
+  const size_t need = lrs_sru_deer_workspace_bytes(T, B, D, k_max);
+  if (!workspace || workspace_bytes < need) return LRS_ERR_WORKSPACE;
+  const lrs::ColPlan p = lrs::plan_sru_deer(C, T, io_dtype);
+  if (!grid_ok(p.ncb * p.ntb, p.nw * 64)) return LRS_ERR_UNSUPPORTED;
+
+  Carve cv(align_ptr(workspace));
+  const DeerRecord r = carve_deer_record(cv, k_max);
+  float* ybuf = cv.take<float>(N);
+  const int64_t nst = lrs::col_status_words(p);
+  uint64_t* status = nullptr;
+  unsigned* tickets = nullptr;
+  if (nst > 0) {
+    status = cv.take<uint64_t>(nst);
+    tickets = cv.take<unsigned>(p.ncb);
+  }
+  const void* all[10] = {z_f, z_r, z_x, bias_f, bias_r, v_f, c0, c_init, h, c_states};
+  const size_t allsz[10] = {nb, nb, nb, db, db, db, cb, sb, nb, sb};
+  for (int i = 0; i < 10; ++i)
+    if (overlap(ybuf, sb, all[i], allsz[i])) return LRS_ERR_INVALID_ARG;
+
+  // ping-pong as in lrs_deer_solve: iteration i writes P[i % 2]; a start in
+  // c_states itself swaps the roles so that iteration 0 does not overwrite it
+  float* P[2] = {c_states, ybuf};
+  if (c_init == c_states) { P[0] = ybuf; P[1] = c_states; }
+  const size_t rowbytes = (size_t)p.cpt * es;
+  const int vec = aligned(z_f, rowbytes) && aligned(z_x, rowbytes) &&
+                  aligned(c_states, (size_t)p.cpt * 4) && aligned(ybuf, (size_t)p.cpt * 4) &&
+                  (!c_init || aligned(c_init, (size_t)p.cpt * 4)) && (C % p.cpt == 0);
+  int rc = hip_status(lrs::launch_reset(status, nst, tickets, nst > 0 ? p.ncb : 0, r.delta_bits,
+                                        lrs::kDeltaSetWords + lrs::kDeerRecordWords + k_max, s));
+  if (rc != LRS_OK) return rc;
+  for (int i = 0; i < k_max; ++i) {
+    if (i > 0 && nst > 0) {
+      rc = hip_status(lrs::launch_reset(status, nst, tickets, p.ncb, nullptr, 0, s));
+      if (rc != LRS_OK) return rc;
+    }
+    const float* y = (i == 0) ? c_init : P[(i - 1) & 1];
+    rc = hip_status(lrs::launch_sru_deer_iter(z_f, z_x, bias_f, v_f, c0, y, P[i & 1], T, C, D,
+                                              io_dtype, p, vec, status, tickets, r.delta_bits,
+                                              r.delta_out, i, eps, s));
+    if (rc != LRS_OK) return rc;
+  }
+  rc = hip_status(lrs::launch_deer_finish(r.delta_bits, r.delta_out, r.rec, k_max, eps, s));
+  if (rc != LRS_OK) return rc;
+  rc = hip_status(lrs::launch_deer_select(P[0], P[1], c_states, N, r.rec, s));
+  if (rc != LRS_OK) return rc;
+  const int vec4 = (C % 4 == 0) && aligned(z_r, 4 * es) && aligned(z_x, 4 * es) &&
+                   aligned(h, 4 * es) && aligned(c_states, 16);
+  rc = hip_status(lrs::launch_sru_deer_out(z_r, z_x, bias_r, c_states, h, c_last, N, C, D,
+                                           io_dtype, vec4, s));
+  if (rc != LRS_OK) return rc;
+  if (!iters_out && !deltas_out && !converged_out) return LRS_OK;  // asynchronous form
+  return read_deer_record(r, k_max, iters_out, deltas_out, converged_out, s);
+}
+
 // DEER backward: look-back state, nchunk * C floats of dL/dw partials and the
 // fp64 stage of their reduction.
 size_t lrs_deer_bwd_workspace_bytes(int64_t B, int64_t D, int64_t T) {

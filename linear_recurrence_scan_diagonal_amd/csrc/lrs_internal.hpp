@@ -133,4 +133,16 @@ hipError_t launch_lstm_bwd(const void* zf, const void* zi, const void* zc, const
                            int64_t C, int io_dtype, const ColPlan& p, int vec, uint64_t* status,
                            unsigned* tickets, hipStream_t stream);
 
+// SRU with v_f * c_{t-1} in the forget gate, by DEER (sru_deer.hip).
+ColPlan plan_sru_deer(int64_t C, int64_t T, int io_dtype);
+hipError_t launch_sru_deer_iter(const void* zf, const void* zx, const float* bias_f,
+                                const float* v_f, const float* c0, const float* y, float* yn,
+                                int64_t T, int64_t C, int64_t D, int io_dtype, const ColPlan& p,
+                                int vec, uint64_t* status, unsigned* tickets,
+                                uint32_t* delta_bits, uint32_t* delta_out, int iter, float eps,
+                                hipStream_t stream);
+hipError_t launch_sru_deer_out(const void* zr, const void* zx, const float* bias_r,
+                               const float* c, void* h, float* c_last, int64_t N, int64_t C,
+                               int64_t D, int io_dtype, int vec, hipStream_t stream);
+
 }  // namespace lrs

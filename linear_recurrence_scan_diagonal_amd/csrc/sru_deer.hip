@@ -1,0 +1,328 @@
+// sru_deer.hip -- SRU layer whose forget gate reads the previous cell state,
+// solved by DEER Newton iterations ([T, B, D] layout).
+//
+// Page "CUDA并行化RNN训练：从O(T)到O(log T)的工程实践与参数调优", SRU paragraph:
+// the forget gate is f_t = sigmoid(W_f x_t + v_f (.) c_{t-1} + b_f).  With
+// v_f != 0 the cell recurrence c_t = f_t c_{t-1} + (1 - f_t) z_x,t is
+// element-wise nonlinear, so the linear scan alone cannot solve it.  The DEER
+// page ("cuda-parallel-rnn-training-logt-optimization", core principle)
+// solves such a recurrence by Newton's method on the whole sequence: with
+// F(c) = f(c) (c - z_x) + z_x and its derivative (the Jacobian is diagonal)
+//   J_t = f + (c_{t-1} - z_x) f (1 - f) v_f,
+// one iteration from the iterate y is the linear recurrence
+//   y'_t = J_t y'_{t-1} + F(y_{t-1}) - J_t y_{t-1},   y'_{-1} = c0,
+// solved by the [T,B,D] scan tile (lrs_tbd.hpp), which also folds
+// max |y' - y| into the iteration's norm slots.  The stop rule, the norm
+// slots and the solve record are those of the tanh RNN solve (engineering
+// section: ||y' - y|| < eps or K_max iterations).  k_sru_deer_out then forms
+// h = r tanh(c) + (1 - r) z_x from the solution.
+#include "lrs_tbd.hpp"
+
+namespace lrs {
+
+template <int NW>
+struct DeltaShared {
+  uint32_t wmax[NW];
+};
+
+template <typename IO, int NW, int L, int CPT, bool FULL, bool NT>
+__device__ __forceinline__ void sru_deer_tile(const IO* __restrict__ zf, const IO* __restrict__ zx,
+                                              const float* __restrict__ bias_f,
+                                              const float* __restrict__ v_f,
+                                              const float* __restrict__ c0p,
+                                              const float* __restrict__ y, float* __restrict__ yn,
+                                              int64_t T, int64_t C, int64_t D, int tb, int cb,
+                                              bool multi, uint64_t* st, ColShared<NW, CPT>& s,
+                                              uint32_t& dmax) {
+  const ColPos q = col_pos<NW, L, CPT>(tb, cb, C);
+  const int64_t cbase = (int64_t)cb * (kWave * CPT);
+  float nbf[CPT], vf[CPT];
+  {
+    int64_t d = (q.nvc > 0) ? q.c0 % D : 0;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int64_t dk = (k < q.nvc) ? d : 0;
+      nbf[k] = -kLog2e * bias_f[dk];
+      vf[k] = v_f[dk];
+      d = (d + 1 == D) ? 0 : d + 1;
+    }
+  }
+  // the iterate just before this wave's steps (c0 before the first step; a
+  // missing iterate is zero)
+  float yp[CPT];
+  if (q.row0 == 0) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) yp[k] = (c0p && k < q.nvc) ? c0p[q.c0 + k] : 0.0f;
+  } else if (y && q.row0 <= T) {
+    load_row<CPT, FULL, false>(y + (q.row0 - 1) * C + cbase, q.off, q.nvc, 0.0f, yp);
+  } else {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) yp[k] = 0.0f;
+  }
+  // per step: J and the constant term F(y_{t-1}) - J y_{t-1} of the affine map
+  float Jv[L][CPT], Bv[L][CPT], yo[L][CPT];
+  {
+    const IO* fp = zf + q.row0 * C + cbase;
+    const IO* xp = zx + q.row0 * C + cbase;
+    const float* yq = y ? y + q.row0 * C + cbase : nullptr;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int nv = (FULL || q.row0 + i < T) ? q.nvc : 0;
+      IoRow<IO, CPT> fr, xr;
+      fr.template load<FULL, NT>(fp, q.off, nv);
+      xr.template load<FULL, NT>(xp, q.off, nv);
+      if (yq) {
+        load_row<CPT, FULL, NT>(yq, q.off, nv, 0.0f, yo[i]);
+        yq += C;
+      } else {
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) yo[i][k] = 0.0f;
+      }
+      fp += C;
+      xp += C;
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        const float prev = (i > 0) ? yo[i - 1][k] : yp[k];
+        if (FULL || k < nv) {
+          const float z = __builtin_fmaf(vf[k], prev, fr.get(k));
+          const float f = fast_sigmoid(z, nbf[k]);
+          const float dx = prev - xr.get(k);
+          const float F = __builtin_fmaf(f, dx, xr.get(k));
+          const float J = __builtin_fmaf(dx * (f - f * f), vf[k], f);
+          Jv[i][k] = J;
+          Bv[i][k] = __builtin_fmaf(-J, prev, F);
+        } else {  // identity map past the end
+          Jv[i][k] = 1.0f;
+          Bv[i][k] = 0.0f;
+        }
+      }
+    }
+  }
+  float A[CPT], B[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    A[k] = Jv[0][k];
+    B[k] = Bv[0][k];
+#pragma unroll
+    for (int i = 1; i < L; ++i) {
+      B[k] = __builtin_fmaf(Jv[i][k], B[k], Bv[i][k]);
+      A[k] = A[k] * Jv[i][k];
+    }
+  }
+  float x0[CPT], x[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) x0[k] = (c0p && k < q.nvc) ? c0p[q.c0 + k] : 0.0f;
+  col_enter_state<NW, CPT>(A, B, multi, tb, x0, c0p, cbase, clamp_valid(C - cbase, kWave * CPT),
+                           st, s, x);
+  float* op = yn + q.row0 * C + cbase;
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const bool row_ok = FULL || q.row0 + i < T;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      x[k] = __builtin_fmaf(Jv[i][k], x[k], Bv[i][k]);
+      const uint32_t d = as_u32(fabsf(x[k] - yo[i][k]));
+      if (FULL || (row_ok && k < q.nvc)) dmax = d > dmax ? d : dmax;
+    }
+    store_row<CPT, FULL, NT>(op, q.off, row_ok ? q.nvc : 0, x);
+    op += C;
+  }
+}
+
+// One Newton iteration.  Iteration iter > 0 first folds the norm of
+// iteration iter - 1 (completed by the previous launch) and exits when it met
+// the stop rule; workgroup 0 records that norm and clears the slot set the next
+// iteration uses.  The slot sets rotate over three iterations.
+template <typename IO, int NW, int L, int CPT, bool NT>
+__global__ __launch_bounds__(NW* kWave) void k_sru_deer_iter(
+    const IO* __restrict__ zf, const IO* __restrict__ zx, const float* __restrict__ bias_f,
+    const float* __restrict__ v_f, const float* __restrict__ c0p, const float* __restrict__ y,
+    float* __restrict__ yn, int64_t T, int64_t C, int64_t D, int ncb, int ntb, int vec,
+    uint64_t* __restrict__ status, unsigned* __restrict__ tickets,
+    uint32_t* __restrict__ delta_bits, uint32_t* __restrict__ delta_out, int iter, float eps) {
+  constexpr int CW = kWave * CPT, TW = NW * L;
+  __shared__ ColShared<NW, CPT> s;
+  __shared__ DeltaShared<NW> ds;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  constexpr int64_t kSet = kDeltaSlots * kDeltaStride;
+  if (iter > 0) {
+    if (threadIdx.x < kWave) {
+      uint32_t v = delta_bits[((iter - 1) % 3) * kSet + lane * kDeltaStride];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)v, off, kWave);
+        v = v > o ? v : o;
+      }
+      if (blockIdx.x == 0) {
+        delta_bits[((iter + 1) % 3) * kSet + lane * kDeltaStride] = 0u;
+        if (lane == 0) delta_out[iter - 1] = v;
+      }
+      if (lane == 0) ds.wmax[0] = v;
+    }
+    __syncthreads();
+    const float prev_delta = as_f32(ds.wmax[0]);
+    __syncthreads();
+    if (prev_delta < eps) return;  // the same decision in every workgroup
+  }
+  const bool multi = ntb > 1;
+  const int cb = (int)(blockIdx.x % (unsigned)ncb);
+  const int tb = col_ticket<NW, CPT>(multi, tickets, cb, s);
+  uint64_t* st = status + (int64_t)cb * ntb * CW;
+  const bool full = vec && ((int64_t)(tb + 1) * TW <= T) && ((int64_t)(cb + 1) * CW <= C);
+  uint32_t dmax = 0;
+  if (full)
+    sru_deer_tile<IO, NW, L, CPT, true, NT>(zf, zx, bias_f, v_f, c0p, y, yn, T, C, D, tb, cb,
+                                            multi, st, s, dmax);
+  else
+    sru_deer_tile<IO, NW, L, CPT, false, NT>(zf, zx, bias_f, v_f, c0p, y, yn, T, C, D, tb, cb,
+                                             multi, st, s, dmax);
+  // this workgroup's max |y' - y| into its slot of the iteration's set
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)dmax, off, kWave);
+    dmax = dmax > o ? dmax : o;
+  }
+  if (lane == 0) ds.wmax[wid] = dmax;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) m = ds.wmax[w] > m ? ds.wmax[w] : m;
+    uint32_t* slot = delta_bits + (iter % 3) * kSet + (blockIdx.x % kDeltaSlots) * kDeltaStride;
+    __hip_atomic_fetch_max(slot, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// h = r tanh(c) + (1 - r) z_x with r = sigmoid(z_r + b_r), and c_T, from the
+// solved cell states.  Each thread takes groups of 4 consecutive elements
+// (16-byte state loads, 8- or 16-byte I/O loads) when VEC, else single
+// elements; grid-stride.
+template <typename IO>
+__device__ __forceinline__ float io_get(const IO* p, int64_t i) {
+  if constexpr (sizeof(IO) == 2) return as_f32((uint32_t)p[i] << 16);
+  else return p[i];
+}
+
+template <typename IO, bool VEC, bool NT>
+__global__ __launch_bounds__(256) void k_sru_deer_out(const IO* __restrict__ zr,
+                                                      const IO* __restrict__ zx,
+                                                      const float* __restrict__ bias_r,
+                                                      const float* __restrict__ c,
+                                                      IO* __restrict__ h,
+                                                      float* __restrict__ c_last, int64_t N,
+                                                      int64_t C, int64_t D) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (VEC) {
+    // feature index of the group's first element, advanced by the stride
+    // without a division per group
+    const int64_t dstep = (4 * stride) % D;
+    int64_t d0 = (4 * tid) % D;
+    for (int64_t j = tid; j < N / 4; j += stride) {
+      const int64_t i = 4 * j;
+      float r4[4], x4[4];
+      if constexpr (sizeof(IO) == 2) {
+        const u32x2_t rw = ldv<NT>(reinterpret_cast<const u32x2_t*>(zr + i));
+        const u32x2_t xw = ldv<NT>(reinterpret_cast<const u32x2_t*>(zx + i));
+        r4[0] = bf16_lo(rw.x); r4[1] = bf16_hi(rw.x); r4[2] = bf16_lo(rw.y); r4[3] = bf16_hi(rw.y);
+        x4[0] = bf16_lo(xw.x); x4[1] = bf16_hi(xw.x); x4[2] = bf16_lo(xw.y); x4[3] = bf16_hi(xw.y);
+      } else {
+        const f32x4_t rv = ldv<NT>(reinterpret_cast<const f32x4_t*>(zr + i));
+        const f32x4_t xv = ldv<NT>(reinterpret_cast<const f32x4_t*>(zx + i));
+        r4[0] = rv.x; r4[1] = rv.y; r4[2] = rv.z; r4[3] = rv.w;
+        x4[0] = xv.x; x4[1] = xv.y; x4[2] = xv.z; x4[3] = xv.w;
+      }
+      const f32x4_t cv = ldv<NT>(reinterpret_cast<const f32x4_t*>(c + i));
+      const float c4[4] = {cv.x, cv.y, cv.z, cv.w};
+      float o[4];
+      int64_t d = d0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float r = fast_sigmoid(r4[k], -kLog2e * bias_r[d]);
+        o[k] = __builtin_fmaf(r, fast_tanh(c4[k]) - x4[k], x4[k]);
+        d = (d + 1 == D) ? 0 : d + 1;
+      }
+      IoRow<IO, 4>::template store<true, NT>(h + i, 0, 4, o);
+      if (c_last && i >= N - C) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) c_last[i + k - (N - C)] = c4[k];
+      }
+      d0 += dstep;
+      if (d0 >= D) d0 -= D;
+    }
+  } else {
+    for (int64_t i = tid; i < N; i += stride) {
+      const float zxv = io_get(zx, i);
+      const float r = fast_sigmoid(io_get(zr, i), -kLog2e * bias_r[i % D]);
+      const float ci = c[i];
+      float o[1] = {__builtin_fmaf(r, fast_tanh(ci) - zxv, zxv)};
+      if constexpr (sizeof(IO) == 2) {
+        h[i] = (uint16_t)(pack_bf16x2(o[0], 0.0f) & 0xFFFFu);
+      } else {
+        h[i] = o[0];
+      }
+      if (c_last && i >= N - C) c_last[i - (N - C)] = ci;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kSdNW = 8, kSdL = 8, kSdCPT = 2;
+}
+
+ColPlan plan_sru_deer(int64_t C, int64_t T, int io_dtype) {
+  ColPlan p = plan_cols(C, T, kSdNW, kSdL, kSdCPT);
+  // z_f, z_x (io type), the iterate and the next iterate
+  p.stream = C * T * (2 * (io_dtype == 1 ? 2 : 4) + 8) >= kStreamFootprint;
+  return p;
+}
+
+hipError_t launch_sru_deer_iter(const void* zf, const void* zx, const float* bias_f,
+                                const float* v_f, const float* c0, const float* y, float* yn,
+                                int64_t T, int64_t C, int64_t D, int io_dtype, const ColPlan& p,
+                                int vec, uint64_t* status, unsigned* tickets,
+                                uint32_t* delta_bits, uint32_t* delta_out, int iter, float eps,
+                                hipStream_t stream) {
+  const uint64_t grid = (uint64_t)p.ncb * (uint64_t)p.ntb;
+#define LRS_SD(IO, NTF)                                                                        \
+  hipLaunchKernelGGL((k_sru_deer_iter<IO, kSdNW, kSdL, kSdCPT, NTF>), dim3((unsigned)grid),   \
+                     dim3(kSdNW * kWave), 0, stream, (const IO*)zf, (const IO*)zx, bias_f, v_f, \
+                     c0, y, yn, T, C, D, (int)p.ncb, (int)p.ntb, vec, status, tickets,          \
+                     delta_bits, delta_out, iter, eps)
+  if (io_dtype == 1) {
+    if (p.stream) LRS_SD(uint16_t, true);
+    else LRS_SD(uint16_t, false);
+  } else {
+    if (p.stream) LRS_SD(float, true);
+    else LRS_SD(float, false);
+  }
+#undef LRS_SD
+  return hipGetLastError();
+}
+
+hipError_t launch_sru_deer_out(const void* zr, const void* zx, const float* bias_r,
+                               const float* c, void* h, float* c_last, int64_t N, int64_t C,
+                               int64_t D, int io_dtype, int vec, hipStream_t stream) {
+  int64_t blocks = ((vec ? N / 4 : N) + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  if (blocks < 1) blocks = 1;
+  // z_r, z_x, h in the I/O type and the fp32 cell states
+  const bool nt = N * (3 * (io_dtype == 1 ? 2 : 4) + 4) >= kStreamFootprint;
+#define LRS_SDO(IO, V, NTF)                                                                      \
+  hipLaunchKernelGGL((k_sru_deer_out<IO, V, NTF>), dim3((unsigned)blocks), dim3(256), 0, stream, \
+                     (const IO*)zr, (const IO*)zx, bias_r, c, (IO*)h, c_last, N, C, D)
+  if (io_dtype == 1) {
+    if (vec) { if (nt) LRS_SDO(uint16_t, true, true); else LRS_SDO(uint16_t, true, false); }
+    else LRS_SDO(uint16_t, false, false);
+  } else {
+    if (vec) { if (nt) LRS_SDO(float, true, true); else LRS_SDO(float, true, false); }
+    else LRS_SDO(float, false, false);
+  }
+#undef LRS_SDO
+  return hipGetLastError();
+}
+
+}  // namespace lrs

@@ -18,7 +18,7 @@ Recipe (the same everywhere):
     draws from [lo, hi).
 
 Array tags: a=1, b=2, h0=3, g=4, zf=5, zr=6, zx=7, bias_f=8, bias_r=9, w=10,
-u=11, h_init=12, gh=13, gcl=14, zi=15, zc=16, zo=17.
+u=11, h_init=12, gh=13, gcl=14, zi=15, zc=16, zo=17, vf=18.
 """
 from __future__ import annotations
 
@@ -30,7 +30,7 @@ import numpy as np
 
 TAGS = {"a": 1, "b": 2, "h0": 3, "g": 4, "zf": 5, "zr": 6, "zx": 7, "bias_f": 8,
         "bias_r": 9, "w": 10, "u": 11, "h_init": 12, "gh": 13, "gcl": 14, "zi": 15, "zc": 16,
-        "zo": 17}
+        "zo": 17, "vf": 18}
 
 
 def _rng(*key) -> np.random.Generator:
@@ -117,7 +117,7 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "scan", "sru", "lstm" or "deer"
+    kind: str                 # "scan", "sru", "sru_deer", "lstm" or "deer"
     B: int
     D: int
     T: int
@@ -176,6 +176,15 @@ WORKLOADS = {
          "gh": ("normal", 0.0, 1.0)},
         "SRU forward + backward, bf16 I/O fp32 state, B=32 D=1024 T=2048, z~N(0,1), "
         "b_f,b_r~N(-1,0.1), c0=0, dL/dh~N(0,1)"),
+    # SRU whose forget gate reads v_f * c_{t-1}, solved by DEER, at the SRU shape
+    "sru_deer": Workload(
+        "sru_deer", "sru_deer", 32, 1024, 2048, 1010,
+        {"zf": ("normal", 0.0, 1.0), "zr": ("normal", 0.0, 1.0), "zx": ("normal", 0.0, 1.0),
+         "bias_f": ("normal", -1.0, 0.1), "bias_r": ("normal", -1.0, 0.1),
+         "vf": ("uniform", -0.25, 0.25)},
+        "SRU with v_f*c_{t-1} in the forget gate by DEER, bf16 I/O fp32 state, B=32 D=1024 "
+        "T=2048, z~N(0,1), b_f,b_r~N(-1,0.1), v_f~U(-0.25,0.25), c0=0, c_init=0, eps=1e-5, "
+        "K_max=5"),
     # LSTM cell-state layer with input-only gates, forward (saving the cell
     # states) and backward, at the SRU shape
     "lstm_fwd_bwd": Workload(
@@ -238,6 +247,11 @@ def sru_inputs(w: Workload) -> dict:
     out["bias_f"] = to_f32(params(w.seed, "bias_f", w.dists["bias_f"], (w.D,)))
     out["bias_r"] = to_f32(params(w.seed, "bias_r", w.dists["bias_r"], (w.D,)))
     return out
+
+
+def sru_vf(w: Workload) -> np.ndarray:
+    """fp32 v_f [D] (the forget gate's weight on c_{t-1})."""
+    return to_f32(params(w.seed, "vf", w.dists["vf"], (w.D,)))
 
 
 def lstm_inputs(w: Workload) -> dict:
