@@ -301,6 +301,24 @@ LRS_API int lrs_deer_solve(const float *w, const float *u, const float *h0, cons
                    float *deltas_out, int *converged_out, void *workspace,
                    size_t workspace_bytes, void *stream);
 
+/* Workspace bytes needed by lrs_deer_solve_seq (0 for an invalid or empty shape). */
+LRS_API size_t lrs_deer_seq_workspace_bytes(int64_t B, int64_t D, int64_t T, int k_max);
+
+/* lrs_deer_solve with per-sequence stopping ([P4] engineering section's stop
+ * rule applied to each sequence on its own): sequence b (its D channels)
+ * keeps its own norm delta_b = max over its D*T entries of |y' - y| and stops
+ * iterating once delta_b < eps, while the others go on, up to k_max.  Each
+ * sequence's result is its last iterate, exactly what lrs_deer_solve returns
+ * for that sequence alone.  iters_out[b], converged_out[b] (host arrays of B
+ * ints, each may be NULL) receive the per-sequence iteration counts and
+ * convergence flags; with both NULL the call only enqueues work.  Other
+ * arguments as for lrs_deer_solve.  B is limited to 65535.  Returns
+ * LRS_ERR_NONFINITE when some sequence's last update was NaN or infinite. */
+LRS_API int lrs_deer_solve_seq(const float *w, const float *u, const float *h0,
+                               const float *h_init, float *h, int64_t B, int64_t D, int64_t T,
+                               float eps, int k_max, int *iters_out, int *converged_out,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
 /* Record of the most recent lrs_deer_solve or lrs_sru_deer_fwd that used this
  * workspace with this k_max (same meaning of iters_out, deltas_out, converged_out as there; each
  * may be NULL).  Waits for `stream`, on which that solve must have been

@@ -27,7 +27,7 @@ EXPORTS = ("lrs_status_string", "lrs_version", "lrs_scan_workspace_bytes", "lrs_
            "lrs_deer_solve", "lrs_deer_stats", "lrs_sru_bwd_workspace_bytes", "lrs_sru_bwd",
            "lrs_deer_bwd_workspace_bytes", "lrs_deer_bwd", "lrs_lstm_workspace_bytes",
            "lrs_lstm_fwd", "lrs_lstm_bwd", "lrs_scan_fwd_bwd", "lrs_sru_deer_workspace_bytes",
-           "lrs_sru_deer_fwd")
+           "lrs_sru_deer_fwd", "lrs_deer_seq_workspace_bytes", "lrs_deer_solve_seq")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -74,6 +74,11 @@ def load():
     lib.lrs_sru_bwd.argtypes = [_vp] * 15 + [_i64, _i64, _i64, _int, _vp, _sz, _vp]
     lib.lrs_sru_bwd.restype = _int
     lib.lrs_sru_fwd.restype = _int
+    lib.lrs_deer_seq_workspace_bytes.argtypes = [_i64, _i64, _i64, _int]
+    lib.lrs_deer_seq_workspace_bytes.restype = _sz
+    lib.lrs_deer_solve_seq.argtypes = [_vp] * 5 + [_i64, _i64, _i64, ctypes.c_float, _int, _vp,
+                                                   _vp, _vp, _sz, _vp]
+    lib.lrs_deer_solve_seq.restype = _int
     lib.lrs_sru_deer_workspace_bytes.argtypes = [_i64, _i64, _i64, _int]
     lib.lrs_sru_deer_workspace_bytes.restype = _sz
     lib.lrs_sru_deer_fwd.argtypes = [_vp] * 11 + [_i64, _i64, _i64, _int, ctypes.c_float, _int,
@@ -282,10 +287,10 @@ def sru_bwd(z_f, z_r, z_x, bias_f, bias_r, c_states, grad_h, c0=None, grad_c_las
 def sru_deer_fwd(z_f, z_r, z_x, bias_f, bias_r, v_f, c0=None, c_init=None, eps: float = 1e-5,
                  k_max: int = 5, want_c_last: bool = False, out=None, c_states=None,
                  workspace=None, sync: bool = True):
-    """SRU layer with v_f * c_{t-1} in the forget gate, by DEER.  Returns
-    (h, c_states, c_last or None, info) where info = {"iters", "deltas",
-    "converged"} when sync, else None (read it later with deer_stats on the
-    returned workspace: info is then (h, c_states, c_last, workspace))."""
+    """SRU layer with v_f * c_{t-1} in the forget gate, by DEER.  sync=True:
+    returns (h, c_states, c_last or None, info), info = {"iters", "deltas",
+    "converged", "status"} as for deer_solve.  sync=False: returns
+    (h, c_states, c_last, workspace); deer_stats(workspace, k_max) reads info."""
     lib = load()
     if z_f.dim() != 3:
         raise ValueError("z_f must be [T,B,D]")
@@ -314,9 +319,10 @@ def sru_deer_fwd(z_f, z_r, z_x, bias_f, bias_r, v_f, c0=None, c_init=None, eps: 
                                   _ptr(c_last), T, B, D, DTYPES[io], float(eps), int(k_max),
                                   ctypes.byref(iters), deltas, ctypes.byref(conv), _ptr(ws),
                                   nbytes, _stream(z_f.device))
-        _call(rc, "lrs_sru_deer_fwd")
+        if rc not in (LRS_OK, LRS_ERR_NONFINITE):
+            raise LrsError(rc, "lrs_sru_deer_fwd")
         info = {"iters": iters.value, "deltas": [float(deltas[i]) for i in range(iters.value)],
-                "converged": bool(conv.value)}
+                "converged": bool(conv.value), "status": int(rc)}
         return h, cs, c_last, info
     _call(lib.lrs_sru_deer_fwd(_ptr(z_f), _ptr(z_r), _ptr(z_x), _ptr(bias_f), _ptr(bias_r),
                                _ptr(v_f), _ptr(c0), _ptr(c_init), _ptr(h), _ptr(cs),
@@ -418,6 +424,45 @@ def deer_solve(w, u, h0=None, h_init=None, eps: float = 1e-5, k_max: int = 5, ou
     info = {"iters": iters.value, "deltas": [float(deltas[i]) for i in range(iters.value)],
             "converged": bool(conv.value), "status": int(rc)}
     return h, info
+
+
+def deer_solve_seq(w, u, h0=None, h_init=None, eps: float = 1e-5, k_max: int = 5, out=None,
+                   workspace=None, sync: bool = True):
+    """deer_solve with per-sequence stopping (each batch entry stops on its own
+    norm).  Returns (h, iters[B], converged[B]) when sync, else (h, workspace)."""
+    lib = load()
+    B, D, T = (int(x) for x in u.shape)
+    _check_dev("u", u, torch.float32, u.shape)
+    _check_dev("w", w, torch.float32, (D,))
+    _check_dev("h0", h0, torch.float32, (B, D))
+    _check_dev("h_init", h_init, torch.float32, u.shape)
+    h = torch.empty_like(u) if out is None else out
+    _check_dev("out", h, torch.float32, u.shape)
+    nbytes = lib.lrs_deer_seq_workspace_bytes(B, D, T, int(k_max))
+    ws = _workspace(nbytes, u.device, workspace)
+    if sync:
+        iters = (ctypes.c_int * max(B, 1))()
+        conv = (ctypes.c_int * max(B, 1))()
+        rc = lib.lrs_deer_solve_seq(_ptr(w), _ptr(u), _ptr(h0), _ptr(h_init), _ptr(h), B, D, T,
+                                    float(eps), int(k_max), iters, conv, _ptr(ws), nbytes,
+                                    _stream(u.device))
+        if rc not in (LRS_OK, LRS_ERR_NONFINITE):  # non-finite updates show as not converged
+            raise LrsError(rc, "lrs_deer_solve_seq")
+        return h, [int(iters[b]) for b in range(B)], [bool(conv[b]) for b in range(B)]
+    _call(lib.lrs_deer_solve_seq(_ptr(w), _ptr(u), _ptr(h0), _ptr(h_init), _ptr(h), B, D, T,
+                                 float(eps), int(k_max), None, None, _ptr(ws), nbytes,
+                                 _stream(u.device)), "lrs_deer_solve_seq")
+    return h, ws
+
+
+def deer_eps_schedule(step: int, total_steps: int, early: float = 1e-4, late: float = 1e-6) -> float:
+    """Tolerance for training step `step` of `total_steps`: the DEER page's
+    engineering section suggests a loose eps early in training and a tight one
+    late; this interpolates log-linearly from `early` to `late`."""
+    if total_steps <= 1:
+        return float(late)
+    frac = min(max(step / (total_steps - 1), 0.0), 1.0)
+    return float(early * (late / early) ** frac)
 
 
 def deer_bwd(w, h, grad_h, h0=None, want_grad_h0: bool = True, out=None, workspace=None):

@@ -708,6 +708,105 @@ int lrs_deer_solve(const float* w, const float* u, const float* h0, const float*
   return read_deer_record(r, k_max, iters_out, deltas_out, converged_out, s);
 }
 
+// ------------------------------------------- DEER, per-sequence stopping
+
+// Workspace: per-sequence norm slots (three sets), norms and records, the
+// second iterate buffer and the look-back state.
+size_t lrs_deer_seq_workspace_bytes(int64_t B, int64_t D, int64_t T, int k_max) {
+  int64_t C, N;
+  if (!shape_ok(B, D, T, &C, &N) || N == 0 || k_max < 1 || k_max > 1000000) return 0;
+  const lrs::RowPlan p = deer_plan(C, T);
+  size_t bytes = kAlign + align_up((size_t)(3 * B * lrs::kSeqSlots * lrs::kDeltaStride) * 4) +
+                 align_up((size_t)(B * k_max) * 4) + align_up((size_t)(B * 4) * 4) +
+                 align_up((size_t)N * 4);
+  if (p.nchunk > 1) bytes += align_up((size_t)(C * p.nchunk) * 8) + align_up((size_t)C * 4);
+  return bytes;
+}
+
+int lrs_deer_solve_seq(const float* w, const float* u, const float* h0, const float* h_init,
+                       float* h, int64_t B, int64_t D, int64_t T, float eps, int k_max,
+                       int* iters_out, int* converged_out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  int64_t C, N;
+  if (!shape_ok(B, D, T, &C, &N) || k_max < 1 || k_max > 1000000) return LRS_ERR_INVALID_ARG;
+  if (N == 0) {
+    for (int64_t b = 0; b < B; ++b) {
+      if (iters_out) iters_out[b] = 0;
+      if (converged_out) converged_out[b] = 1;
+    }
+    return LRS_OK;
+  }
+  if (B > 65535) return LRS_ERR_UNSUPPORTED;
+  if (!w || !u || !h) return LRS_ERR_INVALID_ARG;
+  if (!aligned(w, 4) || !aligned(u, 4) || !aligned(h, 4) || (h0 && !aligned(h0, 4)) ||
+      (h_init && !aligned(h_init, 4)))
+    return LRS_ERR_INVALID_ARG;
+  const size_t nb = (size_t)N * 4, cb = (size_t)C * 4;
+  if (overlap(h, nb, w, (size_t)D * 4) || overlap(h, nb, u, nb) || overlap(h, nb, h0, cb))
+    return LRS_ERR_INVALID_ARG;
+  if (h_init && h_init != h && overlap(h, nb, h_init, nb)) return LRS_ERR_INVALID_ARG;
+  const size_t need = lrs_deer_seq_workspace_bytes(B, D, T, k_max);
+  if (!workspace || workspace_bytes < need) return LRS_ERR_WORKSPACE;
+  const lrs::RowPlan p = deer_plan(C, T);
+  if (!grid_ok(C * p.nchunk, p.threads())) return LRS_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+
+  Carve cv(align_ptr(workspace));
+  const int64_t nslots = 3 * B * lrs::kSeqSlots * lrs::kDeltaStride;
+  uint32_t* seq_slots = cv.take<uint32_t>(nslots);
+  uint32_t* seq_delta = cv.take<uint32_t>(B * k_max);
+  int* seq_rec = cv.take<int>(B * 4);
+  float* ybuf = cv.take<float>(N);
+  uint64_t* status = nullptr;
+  unsigned* tickets = nullptr;
+  if (p.nchunk > 1) {
+    status = cv.take<uint64_t>(C * p.nchunk);
+    tickets = cv.take<unsigned>(C);
+  }
+  if (overlap(ybuf, nb, u, nb) || overlap(ybuf, nb, h, nb) || overlap(ybuf, nb, h_init, nb))
+    return LRS_ERR_INVALID_ARG;
+  float* P[2] = {h, ybuf};
+  if (h_init == h) { P[0] = ybuf; P[1] = h; }
+  const int vec = aligned(u, 16) && aligned(h, 16) && aligned(ybuf, 16) &&
+                  (!h_init || aligned(h_init, 16)) && (T % 4 == 0);
+  // slots, norms and records are contiguous: one reset clears them all
+  int rc = hip_status(lrs::launch_reset(status, p.nchunk > 1 ? C * p.nchunk : 0, tickets,
+                                        p.nchunk > 1 ? C : 0, seq_slots,
+                                        (int64_t)((char*)(seq_rec + B * 4) - (char*)seq_slots) / 4,
+                                        s));
+  if (rc != LRS_OK) return rc;
+  for (int i = 0; i < k_max; ++i) {
+    if (i > 0) {
+      rc = hip_status(lrs::launch_deer_seq_book(seq_slots, seq_delta, B, k_max, i, s));
+      if (rc == LRS_OK && p.nchunk > 1)
+        rc = hip_status(lrs::launch_reset(status, C * p.nchunk, tickets, C, nullptr, 0, s));
+      if (rc != LRS_OK) return rc;
+    }
+    const float* y = (i == 0) ? h_init : P[(i - 1) & 1];
+    rc = hip_status(lrs::launch_deer_iter(w, u, y, h0, P[i & 1], C, D, T, p, vec, status, tickets,
+                                          nullptr, nullptr, i, eps, s, seq_slots, seq_delta,
+                                          k_max));
+    if (rc != LRS_OK) return rc;
+  }
+  rc = hip_status(lrs::launch_deer_seq_book(seq_slots, seq_delta, B, k_max, k_max, s));
+  if (rc == LRS_OK) rc = hip_status(lrs::launch_deer_seq_finish(seq_delta, seq_rec, B, k_max, eps, s));
+  if (rc == LRS_OK) rc = hip_status(lrs::launch_deer_seq_select(P[0], P[1], h, B, D * T, seq_rec, s));
+  if (rc != LRS_OK) return rc;
+  if (!iters_out && !converged_out) return LRS_OK;  // asynchronous form
+  std::vector<int> rec((size_t)B * 4);
+  if (hipMemcpyAsync(rec.data(), seq_rec, sizeof(int) * rec.size(), hipMemcpyDeviceToHost, s) !=
+      hipSuccess)
+    return LRS_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return LRS_ERR_HIP;
+  int nonfinite = 0;
+  for (int64_t b = 0; b < B; ++b) {
+    if (iters_out) iters_out[b] = rec[4 * b];
+    if (converged_out) converged_out[b] = rec[4 * b + 1];
+    nonfinite |= rec[4 * b + 2];
+  }
+  return nonfinite ? LRS_ERR_NONFINITE : LRS_OK;
+}
+
 // ------------------------------------------------------- SRU by DEER
 
 // Workspace: the solve record (first, so lrs_deer_stats reads it), a second

@@ -84,10 +84,22 @@ hipError_t launch_deer_bwd(const float* w, const float* h, const float* h0, cons
                            float* du, float* dw, float* dh0, float* part, double* acc, int64_t B,
                            int64_t D, int64_t T, const RowPlan& p, int vec, uint64_t* status,
                            unsigned* tickets, hipStream_t stream);
+// One Newton iteration.  seq_slots != nullptr: per-sequence stopping (norm
+// slots kSeqSlots per sequence per set, three sets; seq_delta[seq * k_max + i]
+// holds sequence seq's norm of iteration i once k_deer_seq_book folded it).
+constexpr int kSeqSlots = 4;
 hipError_t launch_deer_iter(const float* w, const float* u, const float* y, const float* h0,
                             float* yn, int64_t C, int64_t D, int64_t T, const RowPlan& p, int vec,
                             uint64_t* status, unsigned* tickets, uint32_t* delta_bits,
-                            uint32_t* delta_out, int iter, float eps, hipStream_t stream);
+                            uint32_t* delta_out, int iter, float eps, hipStream_t stream,
+                            uint32_t* seq_slots = nullptr, const uint32_t* seq_delta = nullptr,
+                            int k_max = 0);
+hipError_t launch_deer_seq_book(uint32_t* seq_slots, uint32_t* seq_delta, int64_t nseq, int k_max,
+                                int iter, hipStream_t stream);
+hipError_t launch_deer_seq_finish(const uint32_t* seq_delta, int* seq_rec, int64_t nseq,
+                                  int k_max, float eps, hipStream_t stream);
+hipError_t launch_deer_seq_select(const float* p0, const float* p1, float* h, int64_t nseq,
+                                  int64_t n, const int* seq_rec, hipStream_t stream);
 
 hipError_t launch_scan_fwd_tbd(const float* a, const float* b, const float* h0, float* h,
                                int64_t C, int64_t T, const ColPlan& p, int vec, uint64_t* status,

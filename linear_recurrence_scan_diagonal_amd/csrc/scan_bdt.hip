@@ -832,19 +832,31 @@ __global__ __launch_bounds__(256) void k_deer_select(const float* __restrict__ p
 // workgroup owns the whole channel and walks it as SUB sequential sub-chunks
 // of NW*R*256 steps, carrying the state between them in registers (fewer
 // registers than one tile of SUB times the rows, and no look-back).
+//
+// Per-sequence stopping (seq_slots != nullptr): every sequence (batch entry,
+// D consecutive channels) keeps its own norm; a workgroup exits when its
+// sequence's norm of the previous iteration (folded into seq_delta by
+// k_deer_seq_book before this launch) met the stop rule, and folds its update
+// into its sequence's slots instead of the global ones.
 template <int NW, int R, bool MULTI = false, int SUB = 1, bool NT = false>
 __global__ __launch_bounds__(NW* kWave) void k_deer_iter(
     const float* __restrict__ w, const float* __restrict__ u, const float* __restrict__ y,
     const float* __restrict__ h0, float* __restrict__ yn, int64_t T, int64_t C, int64_t D,
     int nchunk, int vec, uint64_t* __restrict__ status, unsigned* __restrict__ tickets,
-    uint32_t* __restrict__ delta_bits, uint32_t* __restrict__ delta_out, int iter, float eps) {
+    uint32_t* __restrict__ delta_bits, uint32_t* __restrict__ delta_out, int iter, float eps,
+    uint32_t* __restrict__ seq_slots, const uint32_t* __restrict__ seq_delta, int k_max) {
   constexpr int CH = NW * R * 256;
   __shared__ BlockShared<NW> s;
-  // stop rule of the previous iteration (uniform across the whole grid)
-  if (iter > 0 && deer_prev_delta<NW>(delta_bits, delta_out, iter, s) < eps) return;
+  const int64_t ch0 = MULTI ? chunk_channel(blockIdx.x, C, nchunk) : (int64_t)blockIdx.x;
+  const int64_t seq = ch0 / D;
+  if (seq_slots) {
+    if (iter > 0 && as_f32(seq_delta[seq * k_max + iter - 1]) < eps) return;
+  } else if (iter > 0 && deer_prev_delta<NW>(delta_bits, delta_out, iter, s) < eps) {
+    return;  // stop rule of the previous iteration (uniform across the whole grid)
+  }
   uint32_t dmax = 0;
   if (MULTI) {
-    const int64_t ch = chunk_channel(blockIdx.x, C, nchunk);
+    const int64_t ch = ch0;
     const int c = chunk_ticket<NW>(true, tickets, ch, s);
     uint64_t* st = status + ch * nchunk;
     if (vec && (int64_t)(c + 1) * CH <= T)
@@ -863,7 +875,74 @@ __global__ __launch_bounds__(NW* kWave) void k_deer_iter(
         x = deer_chunk<NW, R, false, NT>(w, u, y, h0, yn, T, D, ch, c, false, x, vec, nullptr, dmax, s);
     }
   }
-  deer_publish_delta<NW>(dmax, delta_bits, iter, s);
+  if (seq_slots) {
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    dmax = wave_max_u32(dmax);
+    if (lane == 0) s.wmax[wid] = dmax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) m = s.wmax[i] > m ? s.wmax[i] : m;
+      const int64_t nseq = C / D;
+      uint32_t* slot = seq_slots + (int64_t)(iter % 3) * nseq * kSeqSlots * kDeltaStride +
+                       (seq * kSeqSlots + (int64_t)(blockIdx.x % kSeqSlots)) * kDeltaStride;
+      __hip_atomic_fetch_max(slot, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else {
+    deer_publish_delta<NW>(dmax, delta_bits, iter, s);
+  }
+}
+
+// Per-sequence bookkeeping before iteration iter (and once after the last):
+// fold each sequence's slots of iteration iter - 1 into seq_delta[seq][iter - 1]
+// and clear its slots of the set iteration iter + 1 will use.
+__global__ __launch_bounds__(256) void k_deer_seq_book(uint32_t* __restrict__ seq_slots,
+                                                       uint32_t* __restrict__ seq_delta,
+                                                       int64_t nseq, int k_max, int iter) {
+  const int64_t set = nseq * kSeqSlots * kDeltaStride;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nseq;
+       b += (int64_t)gridDim.x * blockDim.x) {
+    uint32_t v = 0;
+    for (int k = 0; k < kSeqSlots; ++k) {
+      const uint32_t x = seq_slots[(int64_t)((iter - 1) % 3) * set + (b * kSeqSlots + k) * kDeltaStride];
+      v = x > v ? x : v;
+      seq_slots[(int64_t)((iter + 1) % 3) * set + (b * kSeqSlots + k) * kDeltaStride] = 0u;
+    }
+    seq_delta[b * k_max + iter - 1] = v;
+  }
+}
+
+// Per-sequence record {iterations, converged, non-finite, 0}: the iteration
+// count is one past the first norm below eps, or k_max.
+__global__ __launch_bounds__(256) void k_deer_seq_finish(const uint32_t* __restrict__ seq_delta,
+                                                         int* __restrict__ seq_rec, int64_t nseq,
+                                                         int k_max, float eps) {
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nseq;
+       b += (int64_t)gridDim.x * blockDim.x) {
+    int iters = k_max;
+    for (int i = 0; i < k_max; ++i)
+      if (as_f32(seq_delta[b * k_max + i]) < eps) { iters = i + 1; break; }
+    const float d = as_f32(seq_delta[b * k_max + iters - 1]);
+    seq_rec[4 * b + 0] = iters;
+    seq_rec[4 * b + 1] = d < eps ? 1 : 0;
+    seq_rec[4 * b + 2] = (d - d != 0.0f) ? 1 : 0;
+    seq_rec[4 * b + 3] = 0;
+  }
+}
+
+// Leave each sequence's last iterate in h (blockIdx.y = sequence of n floats).
+__global__ __launch_bounds__(256) void k_deer_seq_select(const float* __restrict__ p0,
+                                                         const float* __restrict__ p1,
+                                                         float* __restrict__ h, int64_t n,
+                                                         const int* __restrict__ seq_rec) {
+  const int64_t b = blockIdx.y;
+  const float* src = (((seq_rec[4 * b] - 1) & 1) ? p1 : p0) + b * n;
+  float* dst = h + b * n;
+  if (src == dst) return;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    dst[i] = src[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -1126,11 +1205,13 @@ hipError_t launch_deer_select(const float* p0, const float* p1, float* h, int64_
 hipError_t launch_deer_iter(const float* w, const float* u, const float* y, const float* h0,
                             float* yn, int64_t C, int64_t D, int64_t T, const RowPlan& p, int vec,
                             uint64_t* status, unsigned* tickets, uint32_t* delta_bits,
-                            uint32_t* delta_out, int iter, float eps, hipStream_t stream) {
+                            uint32_t* delta_out, int iter, float eps, hipStream_t stream,
+                            uint32_t* seq_slots, const uint32_t* seq_delta, int k_max) {
   const dim3 grid((unsigned)((uint64_t)C * (uint64_t)p.nchunk));
 #define LRS_DEER(M, SB, NTF) hipLaunchKernelGGL((k_deer_iter<NW, RR, M, SB, NTF>), grid, dim3(NW * kWave), \
                                                 0, stream, w, u, y, h0, yn, T, C, D, (int)p.nchunk, \
-                                                vec, status, tickets, delta_bits, delta_out, iter, eps)
+                                                vec, status, tickets, delta_bits, delta_out, iter, eps, \
+                                                seq_slots, seq_delta, k_max)
   // the first iteration from y = 0 reads u only and is slightly faster with
   // the default policy
   const bool nt = p.stream && y != nullptr;
@@ -1155,6 +1236,32 @@ hipError_t launch_deer_iter(const float* w, const float* u, const float* y, cons
   }
 #undef LRS_DEER
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_deer_seq_book(uint32_t* seq_slots, uint32_t* seq_delta, int64_t nseq, int k_max,
+                                int iter, hipStream_t stream) {
+  const unsigned blocks = (unsigned)((nseq + 255) / 256 < 1024 ? (nseq + 255) / 256 : 1024);
+  hipLaunchKernelGGL(k_deer_seq_book, dim3(blocks), dim3(256), 0, stream, seq_slots, seq_delta,
+                     nseq, k_max, iter);
+  return hipGetLastError();
+}
+
+hipError_t launch_deer_seq_finish(const uint32_t* seq_delta, int* seq_rec, int64_t nseq,
+                                  int k_max, float eps, hipStream_t stream) {
+  const unsigned blocks = (unsigned)((nseq + 255) / 256 < 1024 ? (nseq + 255) / 256 : 1024);
+  hipLaunchKernelGGL(k_deer_seq_finish, dim3(blocks), dim3(256), 0, stream, seq_delta, seq_rec,
+                     nseq, k_max, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_deer_seq_select(const float* p0, const float* p1, float* h, int64_t nseq,
+                                  int64_t n, const int* seq_rec, hipStream_t stream) {
+  int64_t bx = (n + 255) / 256;
+  if (bx > 1024) bx = 1024;
+  if (bx < 1) bx = 1;
+  hipLaunchKernelGGL(k_deer_seq_select, dim3((unsigned)bx, (unsigned)nseq), dim3(256), 0, stream,
+                     p0, p1, h, n, seq_rec);
+  return hipGetLastError();
 }
 #undef LRS_SHAPE_CASE
 

@@ -32,7 +32,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 22, names
     raw = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(raw, n), f"{n} declared in lrs.h but not exported"
@@ -194,3 +194,14 @@ def test_product_path_has_no_fallback():
             binding.load()
     finally:
         binding.LIB_PATH, binding._lib = saved, saved_lib
+
+
+def test_deer_eps_schedule():
+    """Log-linear from the loose to the tight tolerance over training."""
+    from linear_recurrence_scan_diagonal_amd import binding as b
+    assert b.deer_eps_schedule(0, 101) == pytest.approx(1e-4)
+    assert b.deer_eps_schedule(100, 101) == pytest.approx(1e-6)
+    assert b.deer_eps_schedule(50, 101) == pytest.approx(1e-5)
+    vals = [b.deer_eps_schedule(i, 11) for i in range(11)]
+    assert all(x > y for x, y in zip(vals, vals[1:]))
+    assert b.deer_eps_schedule(5, 1) == 1e-6 and b.deer_eps_schedule(500, 101) == pytest.approx(1e-6)
