@@ -630,11 +630,12 @@ def main():
 
 
 def crossover(args, np, torch, lrs, I, dev):
-    """Sequential (one lane per channel) vs parallel scan kernels for short
-    channels: the headline workload's 2^24 elements of a, b, dL/dh regrouped
-    as [1, 2^24/T, T] for T = 4 .. 8192, each kernel forced through the
-    crossover overrides the library reads (LRS_SERIAL_FWD_MAX_T /
-    LRS_SERIAL_BWD_MAX_T), timed with HIP events over --steps calls."""
+    """Kernel families for short channels: sequential (one lane per channel),
+    packed (whole channels per workgroup) and one channel per workgroup, on
+    the headline workload's 2^24 elements of a, b, dL/dh regrouped as
+    [1, 2^24/T, T] for T = 4 .. 8192, each forced through the overrides the
+    library reads (LRS_SERIAL_FWD_MAX_T, LRS_SERIAL_BWD_MAX_T,
+    LRS_PACKED_MAX_T), timed with HIP events over --steps calls."""
     w = I.WORKLOADS["scan_fwd_bwd"]
     x = I.scan_inputs(w)
     N = w.N
@@ -658,7 +659,10 @@ def crossover(args, np, torch, lrs, I, dev):
         return s.elapsed_time(e) * 1e3 / args.steps
 
     env = os.environ
-    keys = ("LRS_SERIAL_FWD_MAX_T", "LRS_SERIAL_BWD_MAX_T")
+    keys = ("LRS_SERIAL_FWD_MAX_T", "LRS_SERIAL_BWD_MAX_T", "LRS_PACKED_MAX_T")
+    big = str(1 << 40)
+    modes = (("sequential", (big, big, "0")), ("packed", ("0", "0", big)),
+             ("one channel per workgroup", ("0", "0", "0")))
     saved = {k: env.get(k) for k in keys}
     rows = []
     T = 4
@@ -667,8 +671,11 @@ def crossover(args, np, torch, lrs, I, dev):
         a, b, g = (flat[k].view(1, D, T) for k in ("a", "b", "g"))
         hv, gav, gbv = h.view(1, D, T), ga.view(1, D, T), gb.view(1, D, T)
         res = {}
-        for mode, lim in (("serial", str(1 << 40)), ("parallel", "0")):
-            for k in keys:
+        for mode, lims in modes:
+            if mode == "packed" and T > 2048:
+                res[mode] = None  # no channel fits a packed workgroup
+                continue
+            for k, lim in zip(keys, lims):
                 env[k] = lim
             res[mode] = (timed(lambda: lrs.scan_fwd(a, b, None, out=hv, workspace=ws)),
                          timed(lambda: lrs.scan_bwd(a, hv, g, None, need_grad_h0=False,
@@ -678,15 +685,19 @@ def crossover(args, np, torch, lrs, I, dev):
                 env.pop(k, None)
             else:
                 env[k] = saved[k]
-        rows.append((T, D, res["serial"], res["parallel"]))
+        rows.append((T, D, res))
         T *= 2
     pct = lambda us, bpe: 100.0 * bpe * N / (us * 1e-6) / 1e9 / HBM_PEAK_GBS
+    cell = lambda v, bpe: "n/a" if v is None else f"{v:.1f} ({pct(v, bpe):.0f}%)"
     print(f"# crossover, {N} elements (fwd 12 B, bwd 20 B per element), us and % of 8 TB/s")
-    print("| T | channels | serial fwd | parallel fwd | serial bwd | parallel bwd |")
-    print("|---|---|---|---|---|---|")
-    for T, D, (sf, sb), (pf, pb) in rows:
-        print(f"| {T} | {D} | {sf:.1f} ({pct(sf, 12):.0f}%) | {pf:.1f} ({pct(pf, 12):.0f}%) | "
-              f"{sb:.1f} ({pct(sb, 20):.0f}%) | {pb:.1f} ({pct(pb, 20):.0f}%) |", flush=True)
+    print("| T | channels | " + " | ".join(f"{m} fwd | {m} bwd" for m, _ in modes) + " |")
+    print("|---|---|" + "---|---|" * len(modes))
+    for T, D, res in rows:
+        cells = []
+        for m, _ in modes:
+            v = res[m]
+            cells += [cell(None if v is None else v[0], 12), cell(None if v is None else v[1], 20)]
+        print(f"| {T} | {D} | " + " | ".join(cells) + " |", flush=True)
 
 
 STREAM_REF_ELEMS = 1 << 26  # 256 MiB per fp32 operand

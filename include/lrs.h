@@ -44,10 +44,11 @@
  *    (B*D*T == 0) is valid and does nothing.
  *  - Output arrays must not overlap input arrays unless a function says so.
  *  - Calls that share a workspace must be ordered (same stream or synchronised).
- *  - [B,D,T] scans of short channels run sequential per-channel kernels (one
- *    lane per channel) below a measured crossover (T <= 64 forward, T <= 32
- *    backward); the environment variables LRS_SERIAL_FWD_MAX_T and
- *    LRS_SERIAL_BWD_MAX_T (integers, read at every call) override it.
+ *  - [B,D,T] scans of short channels pack whole channels into each workgroup
+ *    (T <= 64) or, for the shortest (T <= 4), run one lane per channel; the
+ *    limits are measured crossovers, and the environment variables
+ *    LRS_PACKED_MAX_T, LRS_SERIAL_FWD_MAX_T and LRS_SERIAL_BWD_MAX_T
+ *    (integers, read at every call) override them.
  */
 #ifndef LRS_H
 #define LRS_H

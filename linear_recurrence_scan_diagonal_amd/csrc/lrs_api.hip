@@ -61,6 +61,14 @@ int hip_status(hipError_t e) { return e == hipSuccess ? LRS_OK : LRS_ERR_HIP; }
 // Launch-size guard: HIP grids are limited to 2^32-1 work-items per dimension.
 bool grid_ok(int64_t blocks, int threads) { return blocks > 0 && blocks * threads < (1ll << 32); }
 
+// Launch guard of a [B,D,T] scan plan (sequential: 256 channels per
+// workgroup; packed: p.packed channels per workgroup; else one per chunk).
+bool rows_grid_ok(const lrs::RowPlan& p, int64_t C) {
+  if (p.serial) return grid_ok((C + 255) / 256, 256);
+  if (p.packed) return grid_ok((C + p.packed - 1) / p.packed, p.threads());
+  return grid_ok(C * p.nchunk, p.threads());
+}
+
 int scan_ws_needs(int64_t C, int64_t T, int layout, size_t* bytes) {
   if (layout == LRS_LAYOUT_BDT) {
     const lrs::RowPlan f = lrs::plan_scan_fwd_rows(C, T), b = lrs::plan_scan_bwd_rows(C, T);
@@ -153,7 +161,7 @@ int lrs_scan_fwd(const void* a, const void* b, const float* h0, void* h, int64_t
 
   if (layout == LRS_LAYOUT_BDT) {
     const lrs::RowPlan p = lrs::plan_scan_fwd_rows(C, T);
-    if (!grid_ok(C * p.nchunk, p.threads())) return LRS_ERR_UNSUPPORTED;
+    if (!rows_grid_ok(p, C)) return LRS_ERR_UNSUPPORTED;
     uint64_t* status = nullptr;
     unsigned* tickets = nullptr;
     if (p.nchunk > 1) {
@@ -163,7 +171,8 @@ int lrs_scan_fwd(const void* a, const void* b, const float* h0, void* h, int64_t
       rc = hip_status(lrs::launch_reset(status, C * p.nchunk, tickets, C, nullptr, 0, s));
       if (rc != LRS_OK) return rc;
     }
-    const int vec = al16 && (T % 4 == 0);
+    // packed blocks start 16-byte aligned whatever T is
+    const int vec = al16 && (p.packed || T % 4 == 0);
     return hip_status(lrs::launch_scan_fwd_bdt((const float*)a, (const float*)b, h0, (float*)h, C,
                                                T, p, vec, status, tickets, s));
   }
@@ -221,7 +230,7 @@ int lrs_scan_bwd(const void* a, const void* h, const float* h0, const void* grad
 
   if (layout == LRS_LAYOUT_BDT) {
     const lrs::RowPlan p = lrs::plan_scan_bwd_rows(C, T);
-    if (!grid_ok(C * p.nchunk, p.threads())) return LRS_ERR_UNSUPPORTED;
+    if (!rows_grid_ok(p, C)) return LRS_ERR_UNSUPPORTED;
     uint64_t* status = nullptr;
     unsigned* tickets = nullptr;
     if (p.nchunk > 1) {
@@ -231,7 +240,7 @@ int lrs_scan_bwd(const void* a, const void* h, const float* h0, const void* grad
       rc = hip_status(lrs::launch_reset(status, C * p.nchunk, tickets, C, nullptr, 0, s));
       if (rc != LRS_OK) return rc;
     }
-    const int vec = al16 && (T % 4 == 0);
+    const int vec = al16 && (p.packed || T % 4 == 0);
     return hip_status(lrs::launch_scan_bwd_bdt((const float*)a, (const float*)h, h0,
                                                (const float*)grad_h, (float*)grad_a,
                                                (float*)grad_b, grad_h0, C, T, p, vec, status,
@@ -287,9 +296,10 @@ int lrs_scan_fwd_bwd(const void* a, const void* b, const float* h0, const void* 
       if (overlap(outs[o], outsz[o], outs[o2], outsz[o2])) return LRS_ERR_INVALID_ARG;
   }
   const lrs::RowPlan p = lrs::plan_scan_fused_rows(C, T);
-  // channels short enough for the sequential kernels run those two passes
-  // when h is wanted anyway (one lane per channel beats a mostly idle workgroup)
-  const bool short_pair = h && lrs::plan_scan_fwd_rows(C, T).serial;
+  // short channels run the sequential or packed passes when h is wanted anyway
+  // (the one-kernel form gives each channel a mostly idle workgroup)
+  const lrs::RowPlan pf = lrs::plan_scan_fwd_rows(C, T);
+  const bool short_pair = h && (pf.serial || pf.packed);
   if (layout == LRS_LAYOUT_BDT && p.nchunk == 1 && !short_pair) {
     if (!grid_ok(C, p.threads())) return LRS_ERR_UNSUPPORTED;
     const bool al16 = aligned(a, 16) && aligned(b, 16) && aligned(grad_h, 16) &&

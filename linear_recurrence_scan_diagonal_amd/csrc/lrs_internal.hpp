@@ -23,6 +23,7 @@ struct RowPlan {
   bool stream = false;  // nontemporal loads and stores (arrays far larger than the caches)
   int sub = 1;          // sequential sub-chunks per workgroup (single-workgroup channels)
   bool serial = false;  // short channels: one lane walks each channel (scan_serial.hip)
+  int packed = 0;       // short channels: k whole channels per 8-wave, 2048-step workgroup
   int threads() const { return nw * 64; }
   int64_t chunk() const { return (int64_t)nw * r * 256; }
 };
@@ -63,6 +64,12 @@ hipError_t launch_scan_fwd_serial(const float* a, const float* b, const float* h
 hipError_t launch_scan_bwd_serial(const float* a, const float* h, const float* h0, const float* g,
                                   float* da, float* db, float* dh0, int64_t C, int64_t T, int vec,
                                   hipStream_t stream);
+// Packed short channels (plan.packed = channels per workgroup).
+hipError_t launch_scan_fwd_packed(const float* a, const float* b, const float* h0, float* h,
+                                  int64_t C, int64_t T, int k, int vec, hipStream_t stream);
+hipError_t launch_scan_bwd_packed(const float* a, const float* h, const float* h0, const float* g,
+                                  float* da, float* db, float* dh0, int64_t C, int64_t T, int k,
+                                  int vec, hipStream_t stream);
 // Forward and backward scan in one pass; the plan must be single-chunk.
 hipError_t launch_scan_fused_bdt(const float* a, const float* b, const float* h0, const float* g,
                                  float* h, float* da, float* db, float* dh0, int64_t C, int64_t T,

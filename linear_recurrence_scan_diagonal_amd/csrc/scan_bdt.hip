@@ -482,6 +482,168 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_fused_bdt(
 }
 
 // ---------------------------------------------------------------------------
+// Short channels, packed: a workgroup takes k whole consecutive channels
+// (k*T contiguous elements of the [B,D,T] arrays) and scans them as one
+// sequence in which each channel's first step is a reset (coefficient 0,
+// input a_1 h0 + b_1), so the single-chunk scan above yields every channel's
+// own recurrence with fully coalesced rows, where the one-channel-per-
+// workgroup kernels would leave most lanes idle.  The backward resets the
+// other way: the coefficient after a channel's last step is 0, h before its
+// first step is its h0, and grad_h0 is a_1 lam_1 of each channel.
+// Positions inside the packed block are below 2^31 (k*T <= chunk size).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void set4(float4& v, int j, float x) {
+  if (j == 0) v.x = x; else if (j == 1) v.y = x; else if (j == 2) v.z = x; else v.w = x;
+}
+__device__ __forceinline__ float get4(const float4& v, int j) {
+  return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
+}
+
+template <int NW, int R>
+__global__ __launch_bounds__(NW* kWave) void k_scan_fwd_packed(
+    const float* __restrict__ a, const float* __restrict__ b, const float* __restrict__ h0,
+    float* __restrict__ h, int64_t T, int64_t C, int k, int vec) {
+  constexpr int S = R * 256;
+  __shared__ BlockShared<NW> s;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const int64_t c0 = (int64_t)blockIdx.x * k;
+  const int64_t nch = (C - c0 < k) ? C - c0 : k;
+  const int64_t len = nch * T;
+  const float* arow = a + c0 * T;
+  const float* brow = b + c0 * T;
+  const uint32_t Tu = (uint32_t)T;
+  const int64_t base = (int64_t)wid * S + 4 * lane;
+  float4 a4[R], b4[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t p = base + r * 256;
+    a4[r] = ld4<false, false>(arow, p, len, vec, 0.0f);
+    b4[r] = ld4<false, false>(brow, p, len, vec, 0.0f);
+    uint32_t m = (uint32_t)p % Tu, cl = (uint32_t)p / Tu;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (m == 0 && p + j < len) {  // channel start: reset, fold h0
+        const float aj = get4(a4[r], j), bj = get4(b4[r], j);
+        set4(b4[r], j, h0 ? __builtin_fmaf(aj, h0[c0 + cl], bj) : bj);
+        set4(a4[r], j, 0.0f);
+      }
+      if (++m == Tu) { m = 0; ++cl; }
+    }
+  }
+  float Ai[R], Bi[R], RA[R], RB[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float A = a4[r].x, B = b4[r].x;
+    B = __builtin_fmaf(a4[r].y, B, b4[r].y); A = A * a4[r].y;
+    B = __builtin_fmaf(a4[r].z, B, b4[r].z); A = A * a4[r].z;
+    B = __builtin_fmaf(a4[r].w, B, b4[r].w); A = A * a4[r].w;
+    wave_scan(A, B);
+    Ai[r] = A; Bi[r] = B;
+    RA[r] = readlane_f(A, kWave - 1);
+    RB[r] = readlane_f(B, kWave - 1);
+  }
+  float WA, WB, PA, PB, TA, TB;
+  chain_rows<R>(RA, RB, WA, WB);
+  block_combine<NW>(WA, WB, s, PA, PB, TA, TB);
+  float xr = PB;  // the block starts with a reset: no carry in
+  float* hrow = h + c0 * T;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float x = wave_shift_up(__builtin_fmaf(Ai[r], xr, Bi[r]), xr);
+    float4 o;
+    x = __builtin_fmaf(a4[r].x, x, b4[r].x); o.x = x;
+    x = __builtin_fmaf(a4[r].y, x, b4[r].y); o.y = x;
+    x = __builtin_fmaf(a4[r].z, x, b4[r].z); o.z = x;
+    x = __builtin_fmaf(a4[r].w, x, b4[r].w); o.w = x;
+    st4<false, false>(hrow, base + r * 256, len, vec, o);
+    xr = __builtin_fmaf(RA[r], xr, RB[r]);
+  }
+}
+
+template <int NW, int R>
+__global__ __launch_bounds__(NW* kWave) void k_scan_bwd_packed(
+    const float* __restrict__ a, const float* __restrict__ h, const float* __restrict__ h0,
+    const float* g, float* __restrict__ da, float* db, float* __restrict__ dh0, int64_t T,
+    int64_t C, int k, int vec) {
+  constexpr int S = R * 256, CH = NW * S;
+  __shared__ BlockShared<NW> s;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const int64_t c0 = (int64_t)blockIdx.x * k;
+  const int64_t nch = (C - c0 < k) ? C - c0 : k;
+  const int64_t len = nch * T;
+  const float* arow = a + c0 * T;
+  const float* hrow = h + c0 * T;
+  const float* grow = g + c0 * T;
+  const uint32_t Tu = (uint32_t)T;
+  const int64_t wend = (int64_t)CH - (int64_t)wid * S;  // end of this wave's segment
+  const int64_t wbeg = wend - S;
+  const int64_t pb = wend - 256 + 4 * (kWave - 1 - lane);  // this lane's group in row 0
+  float4 a4[R], h4[R], g4[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t p = pb - r * 256;
+    a4[r] = ld4<false, false>(arow, p, len, vec, 0.0f);
+    h4[r] = ld4<false, false>(hrow, p, len, vec, 0.0f);
+    g4[r] = ld4<false, false>(grow, p, len, vec, 0.0f);
+    uint32_t m = (uint32_t)p % Tu;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (m == 0) set4(a4[r], j, 0.0f);  // no coefficient into a channel's first step
+      if (++m == Tu) m = 0;
+    }
+  }
+  const float a_after = (wend < len && (uint32_t)wend % Tu != 0) ? arow[wend] : 0.0f;
+  const float h_before = (wbeg > 0 && wbeg - 1 < len) ? hrow[wbeg - 1] : 0.0f;
+  float an[R], hp[R], Ai[R], Bi[R], RA[R], RB[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float fa = (r > 0) ? readlane_f(a4[r - 1].x, kWave - 1) : a_after;
+    an[r] = wave_shift_up(a4[r].x, fa);
+    const float fh = (r < R - 1) ? readlane_f(h4[r + 1].w, 0) : h_before;
+    hp[r] = wave_shift_down(h4[r].w, fh);
+    float A = an[r], B = g4[r].w;
+    B = __builtin_fmaf(a4[r].w, B, g4[r].z); A = A * a4[r].w;
+    B = __builtin_fmaf(a4[r].z, B, g4[r].y); A = A * a4[r].z;
+    B = __builtin_fmaf(a4[r].y, B, g4[r].x); A = A * a4[r].y;
+    wave_scan(A, B);
+    Ai[r] = A; Bi[r] = B;
+    RA[r] = readlane_f(A, kWave - 1);
+    RB[r] = readlane_f(B, kWave - 1);
+  }
+  float WA, WB, PA, PB, TA, TB;
+  chain_rows<R>(RA, RB, WA, WB);
+  block_combine<NW>(WA, WB, s, PA, PB, TA, TB);
+  float xr = PB;  // lam past the block is 0
+  float* darow = da + c0 * T;
+  float* dbrow = db + c0 * T;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float x = wave_shift_up(__builtin_fmaf(Ai[r], xr, Bi[r]), xr);
+    float l[4];
+    l[3] = __builtin_fmaf(an[r], x, g4[r].w);
+    l[2] = __builtin_fmaf(a4[r].w, l[3], g4[r].z);
+    l[1] = __builtin_fmaf(a4[r].z, l[2], g4[r].y);
+    l[0] = __builtin_fmaf(a4[r].y, l[1], g4[r].x);
+    const int64_t p = pb - r * 256;
+    float hv[4] = {hp[r], h4[r].x, h4[r].y, h4[r].z};  // h before each step
+    uint32_t m = (uint32_t)p % Tu, cl = (uint32_t)p / Tu;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (m == 0 && p + j < len) {  // a channel's first step: h before it is its h0
+        const float x0 = h0 ? h0[c0 + cl] : 0.0f;
+        hv[j] = x0;
+        if (dh0) dh0[c0 + cl] = arow[p + j] * l[j];
+      }
+      if (++m == Tu) { m = 0; ++cl; }
+    }
+    st4<false, false>(darow, p, len, vec,
+                      make_float4(l[0] * hv[0], l[1] * hv[1], l[2] * hv[2], l[3] * hv[3]));
+    st4<false, false>(dbrow, p, len, vec, make_float4(l[0], l[1], l[2], l[3]));
+    xr = __builtin_fmaf(RA[r], xr, RB[r]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Adjoint of the nonlinear RNN h_t = tanh(w h_{t-1} + u_t) at its solution h
 // (the DEER solve's result): with s_t = 1 - h_t^2, the same reverse-time scan
 // as k_scan_bwd_bdt with coefficient a_t = w s_t built from h on the fly,
@@ -991,16 +1153,20 @@ RowPlan pick(int64_t T, const Shape (&single)[N], Shape multi) {
 }
 }  // namespace
 
-// Channels this short run the sequential per-channel kernels: measured
-// crossover with the parallel single-chunk kernels (2^24 and 2^26 elements,
-// T = 4 .. 8192): forward 55 vs 61 us at T = 64, 50 vs 33 us at T = 128;
-// backward 97 vs 140 us at T = 32, 124 vs 80 us at T = 64.
-// The environment variables LRS_SERIAL_FWD_MAX_T / LRS_SERIAL_BWD_MAX_T
-// override the crossover (e.g. 0 = never sequential), read at every call.
-constexpr int64_t kSerialFwdMaxT = 64;
-constexpr int64_t kSerialBwdMaxT = 32;
+// Short channels.  Measured on 2^24 elements (bench.py --crossover): the
+// packed kernels (k whole channels per 2048-step workgroup) run at 76-82% of
+// peak forward and 62-69% backward for every T up to 2048, against 3-43% /
+// 4-53% for one channel per workgroup below T = 128 (T = 64: 31 vs 58 us
+// forward, 63 vs 79 us backward; at T = 128 both forms are within 4%); the
+// sequential kernels (one lane per channel) only beat them at T <= 4.
+// LRS_SERIAL_FWD_MAX_T, LRS_SERIAL_BWD_MAX_T and LRS_PACKED_MAX_T override
+// the limits (read at every call, e.g. 0 = never).
+constexpr int64_t kSerialFwdMaxT = 4;
+constexpr int64_t kSerialBwdMaxT = 4;
+constexpr int64_t kPackedMaxT = 64;
+constexpr int64_t kPackedSteps = 2048;  // 8 waves x 1 row of 256 steps
 
-static int64_t serial_max_t(const char* name, int64_t dflt) {
+static int64_t env_max_t(const char* name, int64_t dflt) {
   const char* v = getenv(name);
   if (!v || !*v) return dflt;
   char* end = nullptr;
@@ -1008,19 +1174,37 @@ static int64_t serial_max_t(const char* name, int64_t dflt) {
   return (end && *end == '\0') ? (int64_t)x : dflt;
 }
 
+// Channels per packed workgroup: as many as fit, a multiple that keeps every
+// block 16-byte aligned (k*T divisible by 4); 0 if none fits.
+static int packed_channels(int64_t T) {
+  if (T < 1 || T > kPackedSteps) return 0;
+  int64_t k = kPackedSteps / T;
+  const int64_t q = (T % 4 == 0) ? 1 : (T % 2 == 0 ? 2 : 4);
+  k -= k % q;
+  return (int)k;
+}
+
+static void plan_short(RowPlan& p, int64_t T, const char* serial_env, int64_t serial_dflt) {
+  p.serial = T <= env_max_t(serial_env, serial_dflt);
+  if (!p.serial && T <= env_max_t("LRS_PACKED_MAX_T", kPackedMaxT)) p.packed = packed_channels(T);
+  if (p.serial || p.packed) {
+    p.nchunk = 1;
+    p.nw = 8;
+    p.r = 1;
+  }
+}
+
 RowPlan plan_scan_fwd_rows(int64_t C, int64_t T) {
   RowPlan p = pick(T, kScanSingle, kScanFwdMulti);
   p.stream = 3 * C * T * 4 >= kStreamFootprint;  // a, b, h
-  p.serial = T <= serial_max_t("LRS_SERIAL_FWD_MAX_T", kSerialFwdMaxT);
-  if (p.serial) p.nchunk = 1;
+  plan_short(p, T, "LRS_SERIAL_FWD_MAX_T", kSerialFwdMaxT);
   return p;
 }
 
 RowPlan plan_scan_bwd_rows(int64_t C, int64_t T) {
   RowPlan p = pick(T, kScanSingle, kScanBwdMulti);
   p.stream = 5 * C * T * 4 >= kStreamFootprint;  // a, h, g, grad_a, grad_b
-  p.serial = T <= serial_max_t("LRS_SERIAL_BWD_MAX_T", kSerialBwdMaxT);
-  if (p.serial) p.nchunk = 1;
+  plan_short(p, T, "LRS_SERIAL_BWD_MAX_T", kSerialBwdMaxT);
   return p;
 }
 
@@ -1057,6 +1241,7 @@ hipError_t launch_scan_fwd_bdt(const float* a, const float* b, const float* h0, 
                                int64_t C, int64_t T, const RowPlan& p, int vec,
                                uint64_t* status, unsigned* tickets, hipStream_t stream) {
   if (p.serial) return launch_scan_fwd_serial(a, b, h0, h, C, T, vec, stream);
+  if (p.packed) return launch_scan_fwd_packed(a, b, h0, h, C, T, p.packed, vec, stream);
   const dim3 grid((unsigned)((uint64_t)C * (uint64_t)p.nchunk));
 #define LRS_FWD(NTF, M) hipLaunchKernelGGL((k_scan_fwd_bdt<NW, RR, NTF, NTF, M>), grid, dim3(NW * kWave), \
                                            0, stream, a, b, h0, h, T, C, (int)p.nchunk, vec, status, \
@@ -1088,6 +1273,7 @@ hipError_t launch_scan_bwd_bdt(const float* a, const float* h, const float* h0, 
                                const RowPlan& p, int vec, uint64_t* status, unsigned* tickets,
                                hipStream_t stream) {
   if (p.serial) return launch_scan_bwd_serial(a, h, h0, g, da, db, dh0, C, T, vec, stream);
+  if (p.packed) return launch_scan_bwd_packed(a, h, h0, g, da, db, dh0, C, T, p.packed, vec, stream);
   const dim3 grid((unsigned)((uint64_t)C * (uint64_t)p.nchunk));
 #define LRS_BWD(NTF, M) hipLaunchKernelGGL((k_scan_bwd_bdt<NW, RR, NTF, NTF, M>), grid, dim3(NW * kWave), \
                                            0, stream, a, h, h0, g, da, db, dh0, T, C, (int)p.nchunk, \
@@ -1117,6 +1303,23 @@ hipError_t launch_scan_bwd_bdt(const float* a, const float* h, const float* h0, 
   }
 #undef LRS_BWD
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_scan_fwd_packed(const float* a, const float* b, const float* h0, float* h,
+                                  int64_t C, int64_t T, int k, int vec, hipStream_t stream) {
+  const dim3 grid((unsigned)((C + k - 1) / k));
+  hipLaunchKernelGGL((k_scan_fwd_packed<8, 1>), grid, dim3(8 * kWave), 0, stream, a, b, h0, h, T,
+                     C, k, vec);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_bwd_packed(const float* a, const float* h, const float* h0, const float* g,
+                                  float* da, float* db, float* dh0, int64_t C, int64_t T, int k,
+                                  int vec, hipStream_t stream) {
+  const dim3 grid((unsigned)((C + k - 1) / k));
+  hipLaunchKernelGGL((k_scan_bwd_packed<8, 1>), grid, dim3(8 * kWave), 0, stream, a, h, h0, g, da,
+                     db, dh0, T, C, k, vec);
+  return hipGetLastError();
 }
 
 hipError_t launch_scan_fused_bdt(const float* a, const float* b, const float* h0, const float* g,

@@ -1,10 +1,11 @@
 """Short channels on the GPU: the sequential per-channel kernels (one lane per
-channel, chosen below the measured crossover) against the fp64 oracle, to the
-fp32 bar 1e-5, on the [B,D,T] layout: every T around the crossover and the
-16-byte/element-wise paths (T divisible by 4 or not, unrolled blocks and
-remainders), channel counts that leave a partial workgroup, grad_b written
-over grad_h, both kernels forced at the same T through the crossover
-overrides, and bit-exact integer inputs."""
+channel) and the packed kernels (whole channels per workgroup, resets at
+channel starts), chosen below the measured crossovers, against the fp64
+oracle, to the fp32 bar 1e-5, on the [B,D,T] layout: every T around the
+crossovers and the 16-byte/element-wise paths (T divisible by 4 or not,
+channels straddling rows and waves, partial last blocks), grad_b written over
+grad_h, each kernel family forced at the same T through the overrides, and
+bit-exact integer inputs."""
 import numpy as np
 import pytest
 import torch
@@ -16,7 +17,7 @@ from test_gpu_scan import compare, oracle_scan, run_scan
 
 pytestmark = pytest.mark.gpu
 
-SHORT = [1, 2, 3, 4, 5, 7, 8, 12, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128]
+SHORT = [1, 2, 3, 4, 5, 7, 8, 12, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 255, 257]
 
 
 @pytest.mark.parametrize("T", SHORT)
@@ -27,13 +28,17 @@ def test_short_channels(B, D, T):
     compare(run_scan(x, B, D, T, "bdt"), oracle_scan(x), tag=f"short/{B}x{D}x{T}")
 
 
-@pytest.mark.parametrize("mode", ["serial", "parallel"])
-@pytest.mark.parametrize("T", [6, 16, 40, 300, 1000, 4096])
+@pytest.mark.parametrize("mode", ["serial", "packed", "parallel"])
+@pytest.mark.parametrize("T", [3, 6, 16, 40, 300, 1000, 2047, 4096])
 def test_forced_kernel(monkeypatch, mode, T):
-    """Either kernel at any T through LRS_SERIAL_FWD_MAX_T / LRS_SERIAL_BWD_MAX_T."""
-    lim = str(1 << 40) if mode == "serial" else "0"
-    monkeypatch.setenv("LRS_SERIAL_FWD_MAX_T", lim)
-    monkeypatch.setenv("LRS_SERIAL_BWD_MAX_T", lim)
+    """Each kernel family at any T through LRS_SERIAL_FWD_MAX_T,
+    LRS_SERIAL_BWD_MAX_T and LRS_PACKED_MAX_T (packed falls back to one
+    channel per workgroup where no channel fits a packed block)."""
+    big = str(1 << 40)
+    ser = big if mode == "serial" else "0"
+    monkeypatch.setenv("LRS_SERIAL_FWD_MAX_T", ser)
+    monkeypatch.setenv("LRS_SERIAL_BWD_MAX_T", ser)
+    monkeypatch.setenv("LRS_PACKED_MAX_T", big if mode == "packed" else "0")
     B, D = 2, 333
     w = I.scaled(I.WORKLOADS["scan_fwd_bwd"], B=B, D=D, T=T, seed=9600 + T)
     x = I.scan_inputs(w)
