@@ -79,8 +79,10 @@ def measured_traffic(workload: str, kernel_key: str):
 
 
 # rocprof kernel names of each timed entry point (substring match)
-KERNEL_NAMES = {"scan_fwd_f32": ("k_scan_fwd_bdt", "k_scan_fwd_tbd"),
-                "scan_bwd_f32": ("k_scan_bwd_bdt", "k_scan_bwd_tbd"),
+KERNEL_NAMES = {"scan_fwd_f32": ("k_scan_fwd_bdt", "k_scan_fwd_tbd", "k_scan_fwd_serial",
+                                 "k_scan_fwd_packed"),
+                "scan_bwd_f32": ("k_scan_bwd_bdt", "k_scan_bwd_tbd", "k_scan_bwd_serial",
+                                 "k_scan_bwd_packed"),
                 "scan_fused_f32": ("k_scan_fused_bdt",),
                 "sru_fwd_bf16": ("k_sru_fwd<unsigned short",),
                 "sru_fwd_save_bf16": ("k_sru_fwd<unsigned short",),
