@@ -174,6 +174,32 @@ def test_validation_before_any_launch(lib):
                                 64, 0, 0, null, 0, null) == b.LRS_ERR_INVALID_ARG
     assert lib.lrs_scan_fwd_bwd(big[0], big[1], null, big[2], big[5], big[3], big[4], null, 1, 1,
                                 1 << 20, 0, 0, null, 0, null) == b.LRS_ERR_WORKSPACE
+    # SRU by DEER: missing v_f or c_states, bad dtype, k_max 0, saved states
+    # overlapping an input, missing workspace
+    cf = ctypes.c_float(1e-5)
+    assert lib.lrs_sru_deer_fwd(p, p, p, p, p, null, null, null, p, p, null, 4, 1, 1, 1, cf, 5,
+                                None, None, None, null, 0, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_sru_deer_fwd(p, p, p, p, p, p, null, null, p, null, null, 4, 1, 1, 1, cf, 5,
+                                None, None, None, null, 0, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_sru_deer_fwd(p, p, p, p, p, p, null, null, p, p, null, 4, 1, 1, 3, cf, 5,
+                                None, None, None, null, 0, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_sru_deer_fwd(p, p, p, p, p, p, null, null, p, p, null, 4, 1, 1, 1, cf, 0,
+                                None, None, None, null, 0, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_sru_deer_fwd(big[0], big[1], big[2], big[3], big[4], big[5], null, null,
+                                big[6], big[0], null, 4, 1, 1, 1, cf, 5, None, None, None, null,
+                                0, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_sru_deer_fwd(big[0], big[1], big[2], big[3], big[4], big[5], null, null,
+                                big[6], big[7], null, 4, 1, 1, 1, cf, 5, None, None, None, null,
+                                0, null) == b.LRS_ERR_WORKSPACE
+    assert lib.lrs_sru_deer_workspace_bytes(2048, 32, 1024, 5) >= 32 * 1024 * 2048 * 4
+    # DEER with per-sequence stopping: too many sequences, missing u, missing workspace
+    assert lib.lrs_deer_solve_seq(p, p, null, null, p, 70000, 1, 1, cf, 5, None, None, null, 0,
+                                  null) == b.LRS_ERR_UNSUPPORTED
+    assert lib.lrs_deer_solve_seq(p, null, null, null, p, 2, 1, 4, cf, 5, None, None, null, 0,
+                                  null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_deer_solve_seq(big[0], big[1], null, null, big[2], 2, 1, 4, cf, 5, None, None,
+                                  null, 0, null) == b.LRS_ERR_WORKSPACE
+    assert lib.lrs_deer_seq_workspace_bytes(16, 512, 8192, 5) >= 16 * 512 * 8192 * 4
     assert lib.lrs_deer_stats(p, 1 << 20, 0, None, None, None, null) == b.LRS_ERR_INVALID_ARG
     assert lib.lrs_deer_stats(p, 64, 5, None, None, None, null) == b.LRS_ERR_WORKSPACE
 
