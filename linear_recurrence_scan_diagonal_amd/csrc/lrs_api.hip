@@ -327,11 +327,11 @@ size_t lrs_sru_workspace_bytes(int64_t T, int64_t B, int64_t D) {
   if (!shape_ok(B, D, T, &C, &N) || N == 0) return 0;
   size_t b1 = 0, b2 = 0;
   {
-    const lrs::ColPlan p = lrs::plan_sru(C, T, LRS_BF16);
+    const lrs::ColPlan p = lrs::plan_sru(C, T, LRS_BF16, false);
     b1 = lookback_bytes(lrs::col_status_words(p), p.ncb);
   }
   {
-    const lrs::ColPlan p = lrs::plan_sru(C, T, LRS_F32);
+    const lrs::ColPlan p = lrs::plan_sru(C, T, LRS_F32, false);
     b2 = lookback_bytes(lrs::col_status_words(p), p.ncb);
   }
   return b1 > b2 ? b1 : b2;

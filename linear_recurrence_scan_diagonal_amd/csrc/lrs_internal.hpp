@@ -37,12 +37,19 @@ RowPlan plan_deer_bwd_rows(int64_t C, int64_t T);
 struct ColPlan {
   int nw = 8, l = 8, cpt = 4;
   int64_t ncb = 1, ntb = 1;
-  bool stream = false;  // nontemporal loads and stores (see kStreamFootprint)
+  bool stream = false;   // nontemporal loads and stores (see kStreamFootprint)
+  bool persist = false;  // one workgroup per channel block walks all time tiles (no look-back)
 };
+// Compute units of the current device (cached per device).
+int device_cus();
+// Channel blocks from which the [T,B,D] layer kernels run persistent
+// (device_cus(), or the LRS_PERSIST_MIN_BLOCKS override).
+int64_t persist_min_blocks();
 ColPlan plan_cols(int64_t C, int64_t T, int nw, int l, int cpt);
 ColPlan plan_scan_fwd_tbd(int64_t C, int64_t T);
 ColPlan plan_scan_bwd_tbd(int64_t C, int64_t T);
-ColPlan plan_sru(int64_t C, int64_t T, int io_dtype);
+// allow_persist = false: the look-back tile plan (workspace queries size for it).
+ColPlan plan_sru(int64_t C, int64_t T, int io_dtype, bool allow_persist = true);
 int64_t col_status_words(const ColPlan& p);
 
 // Resets look-back state: status words to "not ready", tickets and the

@@ -25,6 +25,8 @@
 //                    (page "CUDA并行化RNN训练：从O(T)到O(log T)的工程实践与参数调优",
 //                    SRU paragraph and checklist item 2: one kernel for every
 //                    element-wise operation)
+#include <stdlib.h>
+
 #include "lrs_tbd.hpp"
 
 namespace lrs {
@@ -354,6 +356,188 @@ __global__ __launch_bounds__(NW* kWave) void k_sru_fwd(
 }
 
 // ---------------------------------------------------------------------------
+// Persistent SRU forward: one workgroup per channel block walks every time tile
+// in order, carrying the per-channel state in LDS, and loads the next tile's
+// rows while it processes the current one.  No look-back state and no reset
+// kernel; used when the channel blocks alone fill the GPU (B*D large), where
+// it streams about 10% faster than the look-back tiles at B=32 D=1024 T=2048
+// (whose workgroups each load their whole tile before any store).
+// ---------------------------------------------------------------------------
+template <int NW, int CPT>
+struct PersistShared {
+  float A[NW][kWave * CPT];
+  float B[NW][kWave * CPT];
+  float carry[kWave * CPT];
+};
+
+template <typename IO, int L, int CPT, bool FULL, bool NT>
+__device__ __forceinline__ void sru_persist_load(const IO* __restrict__ zf,
+                                                 const IO* __restrict__ zr,
+                                                 const IO* __restrict__ zx, int64_t row0,
+                                                 int64_t T, int64_t C, int64_t cbase,
+                                                 uint32_t off, int nvc, IoRow<IO, CPT> (&fr)[L],
+                                                 IoRow<IO, CPT> (&rr)[L],
+                                                 IoRow<IO, CPT> (&xr)[L]) {
+  const IO* fp = zf + row0 * C + cbase;
+  const IO* rp = zr + row0 * C + cbase;
+  const IO* xp = zx + row0 * C + cbase;
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const int nv = (FULL || row0 + i < T) ? nvc : 0;
+    fr[i].template load<FULL, NT>(fp, off, nv);
+    rr[i].template load<FULL, NT>(rp, off, nv);
+    xr[i].template load<FULL, NT>(xp, off, nv);
+    fp += C;
+    rp += C;
+    xp += C;
+  }
+}
+
+// One tile of the persistent walk: gates of the current rows (fr, rr, xr),
+// then the next tile's rows are loaded into the same arrays (PF: 0 none,
+// 1 full rows, 2 predicated rows), then the waves' maps combine with the
+// carried state, the outputs are written and the carry advances.  FULL: the
+// current tile lies inside the arrays (no predication).
+template <typename IO, int NW, int L, int CPT, bool FULL, int PF, bool SAVE, bool NT>
+__device__ __forceinline__ void sru_persist_tile(
+    const IO* __restrict__ zf, const IO* __restrict__ zr, const IO* __restrict__ zx,
+    IO* __restrict__ h, float* __restrict__ cs, int64_t row0, int64_t T, int64_t C,
+    int64_t cbase, uint32_t off, int nvc, const float (&nbf)[CPT], const float (&nbr)[CPT],
+    IoRow<IO, CPT> (&fr)[L], IoRow<IO, CPT> (&rr)[L], IoRow<IO, CPT> (&xr)[L],
+    PersistShared<NW, CPT>& s, int wid) {
+  constexpr int TW = NW * L;
+  float av[L][CPT], bv[L][CPT];
+  IoRow<IO, CPT> rcur[L], xcur[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    rcur[i] = rr[i];
+    xcur[i] = xr[i];
+    const bool row_ok = FULL || row0 + i < T;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      if (FULL || (row_ok && k < nvc)) {
+        const float f = fast_sigmoid(fr[i].get(k), nbf[k]);
+        const float z = xr[i].get(k);
+        av[i][k] = f;
+        bv[i][k] = __builtin_fmaf(-f, z, z);  // (1 - f) * zx
+      } else {  // identity past the end
+        av[i][k] = 1.0f;
+        bv[i][k] = 0.0f;
+      }
+    }
+  }
+  if (PF == 1)
+    sru_persist_load<IO, L, CPT, true, NT>(zf, zr, zx, row0 + TW, T, C, cbase, off, nvc, fr, rr, xr);
+  else if (PF == 2)
+    sru_persist_load<IO, L, CPT, false, NT>(zf, zr, zx, row0 + TW, T, C, cbase, off, nvc, fr, rr,
+                                            xr);
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    float A = av[0][k], B = bv[0][k];
+#pragma unroll
+    for (int i = 1; i < L; ++i) {
+      B = __builtin_fmaf(av[i][k], B, bv[i][k]);
+      A = A * av[i][k];
+    }
+    s.A[wid][off + k] = A;
+    s.B[wid][off + k] = B;
+  }
+  __syncthreads();
+  float x[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    float PA = 1.0f, PB = 0.0f;
+    for (int w = 0; w < wid; ++w) {
+      PB = __builtin_fmaf(s.A[w][off + k], PB, s.B[w][off + k]);
+      PA = PA * s.A[w][off + k];
+    }
+    x[k] = __builtin_fmaf(PA, s.carry[off + k], PB);
+  }
+  IO* hp = h + row0 * C + cbase;
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    float out[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      x[k] = __builtin_fmaf(av[i][k], x[k], bv[i][k]);
+      const float r = fast_sigmoid(rcur[i].get(k), nbr[k]);
+      const float zxv = xcur[i].get(k);
+      out[k] = __builtin_fmaf(r, fast_tanh(x[k]) - zxv, zxv);  // r tanh(c) + (1 - r) zx
+    }
+    const int nv = (FULL || row0 + i < T) ? nvc : 0;
+    IoRow<IO, CPT>::template store<FULL, NT>(hp, off, nv, out);
+    if (SAVE) store_row<CPT, FULL, NT>(cs + (row0 + i) * C + cbase, off, nv, x);
+    hp += C;
+  }
+  __syncthreads();  // every wave has read s.A, s.B and s.carry
+  if (wid == NW - 1) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) s.carry[off + k] = x[k];  // the state after the tile
+  }
+}
+
+template <typename IO, int NW, int L, int CPT, bool SAVE, bool NT>
+__global__ __launch_bounds__(NW* kWave) void k_sru_fwd_persist(
+    const IO* __restrict__ zf, const IO* __restrict__ zr, const IO* __restrict__ zx,
+    const float* __restrict__ bias_f, const float* __restrict__ bias_r,
+    const float* __restrict__ c0p, IO* __restrict__ h, float* __restrict__ c_last,
+    float* __restrict__ cs, int64_t T, int64_t C, int64_t D, int vec) {
+  constexpr int CW = kWave * CPT, TW = NW * L;
+  __shared__ PersistShared<NW, CPT> s;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t cbase = (int64_t)blockIdx.x * CW;
+  const uint32_t off = (uint32_t)(lane * CPT);
+  const int64_t c0i = cbase + off;
+  const int nvc = clamp_valid(C - c0i, CPT);
+  const bool cfull = vec && cbase + CW <= C;
+  float nbf[CPT], nbr[CPT];
+  {
+    int64_t d = (nvc > 0) ? c0i % D : 0;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int64_t dk = (k < nvc) ? d : 0;
+      nbf[k] = -kLog2e * bias_f[dk];
+      nbr[k] = -kLog2e * bias_r[dk];
+      d = (d + 1 == D) ? 0 : d + 1;
+    }
+  }
+  for (int j = threadIdx.x; j < CW; j += NW * kWave)
+    s.carry[j] = (c0p && cbase + j < C) ? c0p[cbase + j] : 0.0f;
+  const int64_t ntb = (T + TW - 1) / TW, nfull = T / TW;
+  const int64_t w0 = (int64_t)wid * L;
+  IoRow<IO, CPT> fr[L], rr[L], xr[L];
+#define LRS_TILE(FULLT, PFT, TB)                                                               \
+  sru_persist_tile<IO, NW, L, CPT, FULLT, PFT, SAVE, NT>(zf, zr, zx, h, cs, (TB) * TW + w0, T, C, \
+                                                         cbase, off, nvc, nbf, nbr, fr, rr, xr, s, wid)
+  if (cfull && nfull > 0) {
+    // full tiles in a straight loop (each loads the next full tile), then the
+    // last full tile and the ragged tail, if any
+    sru_persist_load<IO, L, CPT, true, NT>(zf, zr, zx, w0, T, C, cbase, off, nvc, fr, rr, xr);
+    for (int64_t tb = 0; tb + 1 < nfull; ++tb) LRS_TILE(true, 1, tb);
+    if (ntb > nfull) {
+      LRS_TILE(true, 2, nfull - 1);
+      LRS_TILE(false, 0, nfull);
+    } else {
+      LRS_TILE(true, 0, nfull - 1);
+    }
+  } else {
+    sru_persist_load<IO, L, CPT, false, NT>(zf, zr, zx, w0, T, C, cbase, off, nvc, fr, rr, xr);
+    for (int64_t tb = 0; tb < ntb; ++tb) {
+      if (tb + 1 < ntb) LRS_TILE(false, 2, tb);
+      else LRS_TILE(false, 0, tb);
+    }
+  }
+#undef LRS_TILE
+  // rows past the end keep the state, so the final carry is c_T
+  if (c_last) {
+    __syncthreads();
+    for (int j = threadIdx.x; j < CW; j += NW * kWave)
+      if (cbase + j < C) c_last[cbase + j] = s.carry[j];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // SRU backward, [T, B, D] (reverse time, as k_scan_bwd_tbd: logical time block
 // 0 is the last physical block, wave 0 takes its latest steps).  With the cell
 // states c saved by the forward pass, the gradient of the cell state runs
@@ -565,7 +749,22 @@ ColPlan plan_cols(int64_t C, int64_t T, int nw, int l, int cpt) {
   return p;
 }
 
-int64_t col_status_words(const ColPlan& p) { return p.ntb > 1 ? p.ncb * p.ntb * kWave * p.cpt : 0; }
+// Channel blocks needed for the persistent kernels: the device's compute
+// units, or LRS_PERSIST_MIN_BLOCKS (read at every call; e.g. 0 = always,
+// a huge value = never).
+int64_t persist_min_blocks() {
+  const char* v = getenv("LRS_PERSIST_MIN_BLOCKS");
+  if (v && *v) {
+    char* end = nullptr;
+    const long long x = strtoll(v, &end, 10);
+    if (end && *end == '\0') return (int64_t)x;
+  }
+  return device_cus();
+}
+
+int64_t col_status_words(const ColPlan& p) {
+  return (p.ntb > 1 && !p.persist) ? p.ncb * p.ntb * kWave * p.cpt : 0;
+}
 
 // Tile shapes (waves along time x steps per lane x channels per lane).
 namespace {
@@ -574,6 +773,7 @@ constexpr int kBwdNW = 8, kBwdL = 16, kBwdCPT = 1;
 constexpr int kSruNW = 4, kSruL = 16, kSruCPT = 2;          // bf16 I/O
 constexpr int kSruF32NW = 8, kSruF32L = 8, kSruF32CPT = 2;  // fp32 I/O
 constexpr int kSruBwdNW = 4, kSruBwdL = 8, kSruBwdCPT = 2;  // backward, both I/O types
+constexpr int kSruPNW = 8, kSruPL = 8, kSruPCPT = 2;        // persistent forward, both I/O types
 }  // namespace
 
 ColPlan plan_scan_fwd_tbd(int64_t C, int64_t T) {
@@ -592,9 +792,14 @@ ColPlan plan_sru_bwd(int64_t C, int64_t T, int io_dtype) {
   p.stream = C * T * (7 * (io_dtype == 1 ? 2 : 4) + 4) >= kStreamFootprint;
   return p;
 }
-ColPlan plan_sru(int64_t C, int64_t T, int io_dtype) {
+ColPlan plan_sru(int64_t C, int64_t T, int io_dtype, bool allow_persist) {
   ColPlan p = io_dtype == 1 ? plan_cols(C, T, kSruNW, kSruL, kSruCPT)
                             : plan_cols(C, T, kSruF32NW, kSruF32L, kSruF32CPT);
+  const int64_t ncb_p = (C + kWave * kSruPCPT - 1) / (kWave * kSruPCPT);
+  if (allow_persist && ncb_p >= persist_min_blocks()) {  // the channel blocks alone fill the GPU
+    p = plan_cols(C, T, kSruPNW, kSruPL, kSruPCPT);
+    p.persist = true;
+  }
   p.stream = 4 * C * T * (io_dtype == 1 ? 2 : 4) >= kStreamFootprint;  // z_f, z_r, z_x, h
   return p;
 }
@@ -637,6 +842,26 @@ hipError_t launch_sru_fwd(const void* zf, const void* zr, const void* zx, const 
                           uint64_t* status, unsigned* tickets, hipStream_t stream) {
   const uint64_t grid = (uint64_t)p.ncb * (uint64_t)p.ntb;
   const int64_t C = B * D;
+  if (p.persist) {
+#define LRS_SRUP(IO, SV, NTF)                                                                     \
+  hipLaunchKernelGGL((k_sru_fwd_persist<IO, kSruPNW, kSruPL, kSruPCPT, SV, NTF>),                \
+                     dim3((unsigned)p.ncb), dim3(kSruPNW * kWave), 0, stream, (const IO*)zf,       \
+                     (const IO*)zr, (const IO*)zx, bias_f, bias_r, c0, (IO*)h, c_last, c_states, T, \
+                     C, D, vec)
+#define LRS_SRUP_SAVE(IO, NTF)                  \
+  if (c_states) LRS_SRUP(IO, true, NTF);        \
+  else LRS_SRUP(IO, false, NTF)
+    if (io_dtype == 1) {
+      if (p.stream) { LRS_SRUP_SAVE(uint16_t, true); }
+      else { LRS_SRUP_SAVE(uint16_t, false); }
+    } else {
+      if (p.stream) { LRS_SRUP_SAVE(float, true); }
+      else { LRS_SRUP_SAVE(float, false); }
+    }
+#undef LRS_SRUP_SAVE
+#undef LRS_SRUP
+    return hipGetLastError();
+  }
 #define LRS_SRU(IO, NW_, L_, CPT_, NTF)                                                          \
   hipLaunchKernelGGL((k_sru_fwd<IO, NW_, L_, CPT_, NTF>), dim3((unsigned)grid), dim3(NW_ * kWave), \
                      0, stream, (const IO*)zf, (const IO*)zr, (const IO*)zx, bias_f, bias_r, c0,  \

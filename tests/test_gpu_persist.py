@@ -1,0 +1,64 @@
+"""The persistent [T,B,D] layer kernels (one workgroup per channel block
+walking all time tiles, chosen when the channel blocks fill the GPU) against
+the fp64 oracle: forced through LRS_PERSIST_MIN_BLOCKS on ragged shapes
+(partial last tile in time, partial last channel block, both I/O types, c0,
+saved cell states and c_T), and at the full B=32 D=1024 T=2048 shape both
+ways, where the two kernel families must agree within the parity bar."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import linear_recurrence_scan_diagonal_amd as lrs
+from linear_recurrence_scan_diagonal_amd import inputs as I
+from conftest import relerr
+from gpu_util import DEV, bf16_dev, log
+
+pytestmark = pytest.mark.gpu
+
+
+def sru_run(w, io, c0=None):
+    s = I.sru_inputs(w)
+    z64 = {k: I.bf16_bits_to_f64(s[k]) for k in ("zf", "zr", "zx")}
+    if io == "bf16":
+        z = {k: bf16_dev(s[k]) for k in ("zf", "zr", "zx")}
+    else:
+        z = {k: torch.from_numpy(z64[k].astype(np.float32)).to(DEV) for k in z64}
+    bf, br = (torch.from_numpy(s[k]).to(DEV) for k in ("bias_f", "bias_r"))
+    c0d = None if c0 is None else torch.from_numpy(c0).to(DEV)
+    cs = torch.empty((w.T, w.B, w.D), dtype=torch.float32, device=DEV)
+    h, cl = lrs.sru_fwd(z["zf"], z["zr"], z["zx"], bf, br, c0d, want_c_last=True, c_states=cs)
+    torch.cuda.synchronize()
+    return h.float().cpu().numpy(), cl.cpu().numpy(), cs.cpu().numpy(), z64, s
+
+
+@pytest.mark.parametrize("B,D,T", [(1, 1, 1), (2, 3, 65), (3, 50, 200), (1, 258, 513),
+                                   (2, 128, 1000), (1, 300, 64)])
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_sru_persistent_ragged(monkeypatch, B, D, T, io):
+    monkeypatch.setenv("LRS_PERSIST_MIN_BLOCKS", "0")
+    w = I.scaled(I.WORKLOADS["sru_fwd"], B=B, D=D, T=T, seed=13000 + B * 7 + D + T)
+    c0 = np.random.default_rng(T).normal(size=(B, D)).astype(np.float32)
+    h, cl, cs, z64, s = sru_run(w, io, c0)
+    ref_h, ref_c = oracle.sru_fwd(z64["zf"], z64["zr"], z64["zx"], s["bias_f"], s["bias_r"], c0)
+    e = {"h": relerr(h, ref_h), "c_last": relerr(cl, ref_c), "cs_last_row": relerr(cs[-1], ref_c)}
+    log(f"persistent sru {io} {B}x{D}x{T}: " + ", ".join(f"{k}={v:.2e}" for k, v in e.items()))
+    assert e["h"] <= (2e-2 if io == "bf16" else 1e-5)
+    assert e["c_last"] <= 1e-5 and e["cs_last_row"] <= 1e-5
+
+
+def test_sru_both_kernels_at_workload_shape(monkeypatch):
+    w = I.WORKLOADS["sru_fwd"]
+    outs = {}
+    for mode, lim in (("persistent", "0"), ("tiles", str(1 << 40))):
+        monkeypatch.setenv("LRS_PERSIST_MIN_BLOCKS", lim)
+        outs[mode] = sru_run(w, "bf16")[:3]
+    s = I.sru_inputs(w)
+    ref_h, ref_c = oracle.sru_fwd(*(I.bf16_bits_to_f64(s[k]) for k in ("zf", "zr", "zx")),
+                                  s["bias_f"], s["bias_r"])
+    for mode, (h, cl, cs) in outs.items():
+        eh, ec = relerr(h, ref_h), relerr(cl, ref_c)
+        log(f"sru_fwd workload, {mode}: h={eh:.2e} c_last={ec:.2e}")
+        assert eh <= 2e-2 and ec <= 1e-5
+    # the saved cell states of the two kernel families agree (fp32 bar)
+    assert relerr(outs["persistent"][2], outs["tiles"][2]) <= 1e-5
