@@ -84,8 +84,9 @@ KERNEL_NAMES = {"scan_fwd_f32": ("k_scan_fwd_bdt", "k_scan_fwd_tbd", "k_scan_fwd
                 "scan_bwd_f32": ("k_scan_bwd_bdt", "k_scan_bwd_tbd", "k_scan_bwd_serial",
                                  "k_scan_bwd_packed"),
                 "scan_fused_f32": ("k_scan_fused_bdt",),
-                "sru_fwd_bf16": ("k_sru_fwd<unsigned short",),
-                "sru_fwd_save_bf16": ("k_sru_fwd<unsigned short",),
+                "sru_fwd_bf16": ("k_sru_fwd<unsigned short", "k_sru_fwd_persist<unsigned short"),
+                "sru_fwd_save_bf16": ("k_sru_fwd<unsigned short",
+                                      "k_sru_fwd_persist<unsigned short"),
                 "sru_bwd_bf16": ("k_sru_bwd<unsigned short",),
                 "deer_solve": ("k_deer_iter",),
                 "sru_deer_bf16": ("k_sru_deer_iter<unsigned short",),
