@@ -49,8 +49,9 @@
  *    limits are measured crossovers, and the environment variables
  *    LRS_PACKED_MAX_T, LRS_SERIAL_FWD_MAX_T and LRS_SERIAL_BWD_MAX_T
  *    (integers, read at every call) override them.
- *  - The SRU forward switches to a persistent kernel (one workgroup per 128
- *    channels walks every time tile, no cross-workgroup look-back) when its
+ *  - The SRU forward and the SRU-by-DEER iterations switch to persistent
+ *    kernels (one workgroup per 128 channels walks every time tile, no
+ *    cross-workgroup look-back and no reset between iterations) when the
  *    128-channel blocks are at least as many as the device's compute units;
  *    LRS_PERSIST_MIN_BLOCKS (an integer, read at every call) replaces that
  *    count (0 = always, a huge value = never).  Both kernels give the same

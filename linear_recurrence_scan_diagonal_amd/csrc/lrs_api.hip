@@ -820,13 +820,14 @@ int lrs_deer_solve_seq(const float* w, const float* u, const float* h0, const fl
 // ------------------------------------------------------- SRU by DEER
 
 // Workspace: the solve record (first, so lrs_deer_stats reads it), a second
-// cell-state buffer and the look-back state of the [T,B,D] tile.
+// cell-state buffer and the look-back state of the [T,B,D] tile (sized for the
+// look-back tile plan; the persistent one needs none).
 size_t lrs_sru_deer_workspace_bytes(int64_t T, int64_t B, int64_t D, int k_max) {
   int64_t C, N;
   if (!shape_ok(B, D, T, &C, &N) || N == 0 || k_max < 1 || k_max > 1000000) return 0;
   size_t need = 0;
   for (int io = 0; io < 2; ++io) {
-    const lrs::ColPlan p = lrs::plan_sru_deer(C, T, io);
+    const lrs::ColPlan p = lrs::plan_sru_deer(C, T, io, false);
     const size_t b = lookback_bytes(lrs::col_status_words(p), p.ncb);
     need = b > need ? b : need;
   }
@@ -873,7 +874,7 @@ int lrs_sru_deer_fwd(const void* z_f, const void* z_r, const void* z_x, const fl
   const size_t need = lrs_sru_deer_workspace_bytes(T, B, D, k_max);
   if (!workspace || workspace_bytes < need) return LRS_ERR_WORKSPACE;
   const lrs::ColPlan p = lrs::plan_sru_deer(C, T, io_dtype);
-  if (!grid_ok(p.ncb * p.ntb, p.nw * 64)) return LRS_ERR_UNSUPPORTED;
+  if (!grid_ok(p.persist ? p.ncb : p.ncb * p.ntb, p.nw * 64)) return LRS_ERR_UNSUPPORTED;
 
   Carve cv(align_ptr(workspace));
   const DeerRecord r = carve_deer_record(cv, k_max);

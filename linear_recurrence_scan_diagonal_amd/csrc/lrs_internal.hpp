@@ -160,7 +160,7 @@ hipError_t launch_lstm_bwd(const void* zf, const void* zi, const void* zc, const
                            unsigned* tickets, hipStream_t stream);
 
 // SRU with v_f * c_{t-1} in the forget gate, by DEER (sru_deer.hip).
-ColPlan plan_sru_deer(int64_t C, int64_t T, int io_dtype);
+ColPlan plan_sru_deer(int64_t C, int64_t T, int io_dtype, bool allow_persist = true);
 hipError_t launch_sru_deer_iter(const void* zf, const void* zx, const float* bias_f,
                                 const float* v_f, const float* c0, const float* y, float* yn,
                                 int64_t T, int64_t C, int64_t D, int io_dtype, const ColPlan& p,

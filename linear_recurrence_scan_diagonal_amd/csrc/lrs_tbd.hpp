@@ -2,7 +2,8 @@
 // kernels: row loads and stores in fp32 and bf16 (default or nontemporal
 // cache policy), the per-tile geometry, the block combine plus lane-parallel
 // look-back that yields each channel's entering state, the time-block ticket,
-// and the gate activations.  Included by scan_tbd.hip and gated_cell.hip only.
+// the LDS carry of persistent walks and the gate activations.  Included by
+// scan_tbd.hip, gated_cell.hip and sru_deer.hip.
 #pragma once
 
 #include "lrs_device.hpp"
@@ -235,6 +236,53 @@ __device__ __forceinline__ int col_ticket(bool multi, unsigned* tickets, int cb,
 
 __device__ __forceinline__ int clamp_valid(int64_t n, int cpt) {
   return n <= 0 ? 0 : (n >= cpt ? cpt : (int)n);
+}
+
+// ---- persistent walks ------------------------------------------------------
+// One workgroup per channel block visits every time tile in order and keeps
+// the per-channel state entering the current tile in LDS (`carry`), so no
+// look-back state is needed.
+template <int NW, int CPT>
+struct PersistShared {
+  float A[NW][kWave * CPT];
+  float B[NW][kWave * CPT];
+  float carry[kWave * CPT];
+};
+
+// Publish this wave's per-channel maps (A, B) and return in x the state
+// entering this wave's first step: the maps of the earlier waves of the tile,
+// in order, applied to the carry.
+template <int NW, int CPT>
+__device__ __forceinline__ void persist_enter(const float (&A)[CPT], const float (&B)[CPT],
+                                              PersistShared<NW, CPT>& s, int wid, uint32_t off,
+                                              float (&x)[CPT]) {
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    s.A[wid][off + k] = A[k];
+    s.B[wid][off + k] = B[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    float PA = 1.0f, PB = 0.0f;
+    for (int w = 0; w < wid; ++w) {
+      PB = __builtin_fmaf(s.A[w][off + k], PB, s.B[w][off + k]);
+      PA = PA * s.A[w][off + k];
+    }
+    x[k] = __builtin_fmaf(PA, s.carry[off + k], PB);
+  }
+}
+
+// Once every wave has read the tile's maps and the carry: the last wave stores
+// its final state (the state after the tile) as the next carry.
+template <int NW, int CPT>
+__device__ __forceinline__ void persist_advance(const float (&x)[CPT], PersistShared<NW, CPT>& s,
+                                                int wid, uint32_t off) {
+  __syncthreads();
+  if (wid == NW - 1) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) s.carry[off + k] = x[k];
+  }
 }
 
 // Geometry of one thread inside its workgroup tile.

@@ -363,13 +363,6 @@ __global__ __launch_bounds__(NW* kWave) void k_sru_fwd(
 // it streams about 10% faster than the look-back tiles at B=32 D=1024 T=2048
 // (whose workgroups each load their whole tile before any store).
 // ---------------------------------------------------------------------------
-template <int NW, int CPT>
-struct PersistShared {
-  float A[NW][kWave * CPT];
-  float B[NW][kWave * CPT];
-  float carry[kWave * CPT];
-};
-
 template <typename IO, int L, int CPT, bool FULL, bool NT>
 __device__ __forceinline__ void sru_persist_load(const IO* __restrict__ zf,
                                                  const IO* __restrict__ zr,
@@ -431,28 +424,18 @@ __device__ __forceinline__ void sru_persist_tile(
   else if (PF == 2)
     sru_persist_load<IO, L, CPT, false, NT>(zf, zr, zx, row0 + TW, T, C, cbase, off, nvc, fr, rr,
                                             xr);
+  float A[CPT], B[CPT], x[CPT];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
-    float A = av[0][k], B = bv[0][k];
+    A[k] = av[0][k];
+    B[k] = bv[0][k];
 #pragma unroll
     for (int i = 1; i < L; ++i) {
-      B = __builtin_fmaf(av[i][k], B, bv[i][k]);
-      A = A * av[i][k];
+      B[k] = __builtin_fmaf(av[i][k], B[k], bv[i][k]);
+      A[k] = A[k] * av[i][k];
     }
-    s.A[wid][off + k] = A;
-    s.B[wid][off + k] = B;
   }
-  __syncthreads();
-  float x[CPT];
-#pragma unroll
-  for (int k = 0; k < CPT; ++k) {
-    float PA = 1.0f, PB = 0.0f;
-    for (int w = 0; w < wid; ++w) {
-      PB = __builtin_fmaf(s.A[w][off + k], PB, s.B[w][off + k]);
-      PA = PA * s.A[w][off + k];
-    }
-    x[k] = __builtin_fmaf(PA, s.carry[off + k], PB);
-  }
+  persist_enter<NW, CPT>(A, B, s, wid, off, x);
   IO* hp = h + row0 * C + cbase;
 #pragma unroll
   for (int i = 0; i < L; ++i) {
@@ -469,11 +452,7 @@ __device__ __forceinline__ void sru_persist_tile(
     if (SAVE) store_row<CPT, FULL, NT>(cs + (row0 + i) * C + cbase, off, nv, x);
     hp += C;
   }
-  __syncthreads();  // every wave has read s.A, s.B and s.carry
-  if (wid == NW - 1) {
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) s.carry[off + k] = x[k];  // the state after the tile
-  }
+  persist_advance<NW, CPT>(x, s, wid, off);
 }
 
 template <typename IO, int NW, int L, int CPT, bool SAVE, bool NT>

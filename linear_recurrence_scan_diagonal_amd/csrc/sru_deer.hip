@@ -25,6 +25,60 @@ struct DeltaShared {
   uint32_t wmax[NW];
 };
 
+// Start of iteration iter > 0: fold the norm of iteration iter - 1 (completed
+// by the previous launch) from its slot set; workgroup 0 records it and clears
+// the set the next iteration uses (the sets rotate over three iterations).
+// True when that norm met the stop rule: the same decision in every workgroup.
+template <int NW>
+__device__ __forceinline__ bool sru_deer_prev_converged(uint32_t* __restrict__ delta_bits,
+                                                        uint32_t* __restrict__ delta_out,
+                                                        int iter, float eps,
+                                                        DeltaShared<NW>& ds) {
+  if (iter == 0) return false;
+  constexpr int64_t kSet = kDeltaSlots * kDeltaStride;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (threadIdx.x < kWave) {
+    uint32_t v = delta_bits[((iter - 1) % 3) * kSet + lane * kDeltaStride];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const uint32_t o = (uint32_t)__shfl_xor((int)v, off, kWave);
+      v = v > o ? v : o;
+    }
+    if (blockIdx.x == 0) {
+      delta_bits[((iter + 1) % 3) * kSet + lane * kDeltaStride] = 0u;
+      if (lane == 0) delta_out[iter - 1] = v;
+    }
+    if (lane == 0) ds.wmax[0] = v;
+  }
+  __syncthreads();
+  const float prev_delta = as_f32(ds.wmax[0]);
+  __syncthreads();
+  return prev_delta < eps;
+}
+
+// End of an iteration: this workgroup's max |y' - y| (dmax, per lane) into its
+// slot of the iteration's set.
+template <int NW>
+__device__ __forceinline__ void sru_deer_fold_norm(uint32_t dmax, uint32_t* __restrict__ delta_bits,
+                                                   int iter, DeltaShared<NW>& ds) {
+  constexpr int64_t kSet = kDeltaSlots * kDeltaStride;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)dmax, off, kWave);
+    dmax = dmax > o ? dmax : o;
+  }
+  if (lane == 0) ds.wmax[wid] = dmax;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) m = ds.wmax[w] > m ? ds.wmax[w] : m;
+    uint32_t* slot = delta_bits + (iter % 3) * kSet + (blockIdx.x % kDeltaSlots) * kDeltaStride;
+    __hip_atomic_fetch_max(slot, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 template <typename IO, int NW, int L, int CPT, bool FULL, bool NT>
 __device__ __forceinline__ void sru_deer_tile(const IO* __restrict__ zf, const IO* __restrict__ zx,
                                               const float* __restrict__ bias_f,
@@ -143,27 +197,7 @@ __global__ __launch_bounds__(NW* kWave) void k_sru_deer_iter(
   constexpr int CW = kWave * CPT, TW = NW * L;
   __shared__ ColShared<NW, CPT> s;
   __shared__ DeltaShared<NW> ds;
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  constexpr int64_t kSet = kDeltaSlots * kDeltaStride;
-  if (iter > 0) {
-    if (threadIdx.x < kWave) {
-      uint32_t v = delta_bits[((iter - 1) % 3) * kSet + lane * kDeltaStride];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const uint32_t o = (uint32_t)__shfl_xor((int)v, off, kWave);
-        v = v > o ? v : o;
-      }
-      if (blockIdx.x == 0) {
-        delta_bits[((iter + 1) % 3) * kSet + lane * kDeltaStride] = 0u;
-        if (lane == 0) delta_out[iter - 1] = v;
-      }
-      if (lane == 0) ds.wmax[0] = v;
-    }
-    __syncthreads();
-    const float prev_delta = as_f32(ds.wmax[0]);
-    __syncthreads();
-    if (prev_delta < eps) return;  // the same decision in every workgroup
-  }
+  if (sru_deer_prev_converged<NW>(delta_bits, delta_out, iter, eps, ds)) return;
   const bool multi = ntb > 1;
   const int cb = (int)(blockIdx.x % (unsigned)ncb);
   const int tb = col_ticket<NW, CPT>(multi, tickets, cb, s);
@@ -176,21 +210,177 @@ __global__ __launch_bounds__(NW* kWave) void k_sru_deer_iter(
   else
     sru_deer_tile<IO, NW, L, CPT, false, NT>(zf, zx, bias_f, v_f, c0p, y, yn, T, C, D, tb, cb,
                                              multi, st, s, dmax);
-  // this workgroup's max |y' - y| into its slot of the iteration's set
+  sru_deer_fold_norm<NW>(dmax, delta_bits, iter, ds);
+}
+
+// ---------------------------------------------------------------------------
+// Persistent form of the iteration, used when the channel blocks alone fill the
+// GPU: one workgroup per channel block walks every time tile in order with the
+// state entering the tile in LDS, loading the next tile's rows while it
+// processes the current one.  No look-back state, so no reset kernel between
+// iterations.  Same per-step map and norm as sru_deer_tile.
+// ---------------------------------------------------------------------------
+template <typename IO, int L, int CPT>
+struct SdRows {
+  IoRow<IO, CPT> f[L], x[L];
+  float y[L][CPT];  // the iterate at the rows
+  float yp[CPT];    // the iterate just before the first row (c0 before step 0)
+};
+
+template <typename IO, int L, int CPT, bool FULL, bool NT>
+__device__ __forceinline__ void sru_deer_persist_load(
+    const IO* __restrict__ zf, const IO* __restrict__ zx, const float* __restrict__ c0p,
+    const float* __restrict__ y, int64_t row0, int64_t T, int64_t C, int64_t cbase, uint32_t off,
+    int nvc, SdRows<IO, L, CPT>& w) {
+  const IO* fp = zf + row0 * C + cbase;
+  const IO* xp = zx + row0 * C + cbase;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t o = (uint32_t)__shfl_xor((int)dmax, off, kWave);
-    dmax = dmax > o ? dmax : o;
-  }
-  if (lane == 0) ds.wmax[wid] = dmax;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t m = 0;
+  for (int i = 0; i < L; ++i) {
+    const int nv = (FULL || row0 + i < T) ? nvc : 0;
+    w.f[i].template load<FULL, NT>(fp, off, nv);
+    w.x[i].template load<FULL, NT>(xp, off, nv);
+    if (y) {
+      load_row<CPT, FULL, NT>(y + (row0 + i) * C + cbase, off, nv, 0.0f, w.y[i]);
+    } else {
 #pragma unroll
-    for (int w = 0; w < NW; ++w) m = ds.wmax[w] > m ? ds.wmax[w] : m;
-    uint32_t* slot = delta_bits + (iter % 3) * kSet + (blockIdx.x % kDeltaSlots) * kDeltaStride;
-    __hip_atomic_fetch_max(slot, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int k = 0; k < CPT; ++k) w.y[i][k] = 0.0f;
+    }
+    fp += C;
+    xp += C;
   }
+  if (row0 == 0) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) w.yp[k] = (c0p && k < nvc) ? c0p[cbase + off + k] : 0.0f;
+  } else if (y && row0 <= T) {
+    load_row<CPT, false, false>(y + (row0 - 1) * C + cbase, off, nvc, 0.0f, w.yp);
+  } else {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) w.yp[k] = 0.0f;
+  }
+}
+
+// One tile of the walk (PF as in the persistent SRU forward: 0 no prefetch,
+// 1 full rows, 2 predicated rows of the next tile; FULL: no predication).
+template <typename IO, int NW, int L, int CPT, bool FULL, int PF, bool NT>
+__device__ __forceinline__ void sru_deer_persist_tile(
+    const IO* __restrict__ zf, const IO* __restrict__ zx, const float* __restrict__ c0p,
+    const float* __restrict__ y, float* __restrict__ yn, int64_t row0, int64_t T, int64_t C,
+    int64_t cbase, uint32_t off, int nvc, const float (&nbf)[CPT], const float (&vf)[CPT],
+    SdRows<IO, L, CPT>& w, PersistShared<NW, CPT>& s, int wid, uint32_t& dmax) {
+  constexpr int TW = NW * L;
+  float Jv[L][CPT], Bv[L][CPT], yo[L][CPT];
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const bool row_ok = FULL || row0 + i < T;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const float prev = (i > 0) ? w.y[i - 1][k] : w.yp[k];
+      yo[i][k] = w.y[i][k];
+      if (FULL || (row_ok && k < nvc)) {
+        const float xv = w.x[i].get(k);
+        const float f = fast_sigmoid(__builtin_fmaf(vf[k], prev, w.f[i].get(k)), nbf[k]);
+        const float dx = prev - xv;
+        const float F = __builtin_fmaf(f, dx, xv);
+        const float J = __builtin_fmaf(dx * (f - f * f), vf[k], f);
+        Jv[i][k] = J;
+        Bv[i][k] = __builtin_fmaf(-J, prev, F);
+      } else {  // identity map past the end
+        Jv[i][k] = 1.0f;
+        Bv[i][k] = 0.0f;
+      }
+    }
+  }
+  if (PF == 1)
+    sru_deer_persist_load<IO, L, CPT, true, NT>(zf, zx, c0p, y, row0 + TW, T, C, cbase, off, nvc,
+                                                w);
+  else if (PF == 2)
+    sru_deer_persist_load<IO, L, CPT, false, NT>(zf, zx, c0p, y, row0 + TW, T, C, cbase, off, nvc,
+                                                 w);
+  float A[CPT], B[CPT], x[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    A[k] = Jv[0][k];
+    B[k] = Bv[0][k];
+#pragma unroll
+    for (int i = 1; i < L; ++i) {
+      B[k] = __builtin_fmaf(Jv[i][k], B[k], Bv[i][k]);
+      A[k] = A[k] * Jv[i][k];
+    }
+  }
+  persist_enter<NW, CPT>(A, B, s, wid, off, x);
+  float* op = yn + row0 * C + cbase;
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const bool row_ok = FULL || row0 + i < T;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      x[k] = __builtin_fmaf(Jv[i][k], x[k], Bv[i][k]);
+      const uint32_t d = as_u32(fabsf(x[k] - yo[i][k]));
+      if (FULL || (row_ok && k < nvc)) dmax = d > dmax ? d : dmax;
+    }
+    store_row<CPT, FULL, NT>(op, off, row_ok ? nvc : 0, x);
+    op += C;
+  }
+  persist_advance<NW, CPT>(x, s, wid, off);
+}
+
+template <typename IO, int NW, int L, int CPT, bool NT>
+__global__ __launch_bounds__(NW* kWave) void k_sru_deer_iter_persist(
+    const IO* __restrict__ zf, const IO* __restrict__ zx, const float* __restrict__ bias_f,
+    const float* __restrict__ v_f, const float* __restrict__ c0p, const float* __restrict__ y,
+    float* __restrict__ yn, int64_t T, int64_t C, int64_t D, int vec,
+    uint32_t* __restrict__ delta_bits, uint32_t* __restrict__ delta_out, int iter, float eps) {
+  constexpr int CW = kWave * CPT, TW = NW * L;
+  __shared__ PersistShared<NW, CPT> s;
+  __shared__ DeltaShared<NW> ds;
+  if (sru_deer_prev_converged<NW>(delta_bits, delta_out, iter, eps, ds)) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t cbase = (int64_t)blockIdx.x * CW;
+  const uint32_t off = (uint32_t)(lane * CPT);
+  const int64_t c0i = cbase + off;
+  const int nvc = clamp_valid(C - c0i, CPT);
+  const bool cfull = vec && cbase + CW <= C;
+  float nbf[CPT], vf[CPT];
+  {
+    int64_t d = (nvc > 0) ? c0i % D : 0;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int64_t dk = (k < nvc) ? d : 0;
+      nbf[k] = -kLog2e * bias_f[dk];
+      vf[k] = v_f[dk];
+      d = (d + 1 == D) ? 0 : d + 1;
+    }
+  }
+  for (int j = threadIdx.x; j < CW; j += NW * kWave)
+    s.carry[j] = (c0p && cbase + j < C) ? c0p[cbase + j] : 0.0f;
+  const int64_t ntb = (T + TW - 1) / TW, nfull = T / TW;
+  const int64_t w0 = (int64_t)wid * L;
+  uint32_t dmax = 0;
+  SdRows<IO, L, CPT> w;
+#define LRS_SDT(FULLT, PFT, TB)                                                                  \
+  sru_deer_persist_tile<IO, NW, L, CPT, FULLT, PFT, NT>(zf, zx, c0p, y, yn, (TB) * TW + w0, T, C, \
+                                                        cbase, off, nvc, nbf, vf, w, s, wid, dmax)
+  if (cfull && nfull > 0) {
+    // full tiles in a straight loop (each loads the next full tile), then the
+    // last full tile and the ragged tail, if any
+    sru_deer_persist_load<IO, L, CPT, true, NT>(zf, zx, c0p, y, w0, T, C, cbase, off, nvc, w);
+    for (int64_t tb = 0; tb + 1 < nfull; ++tb) LRS_SDT(true, 1, tb);
+    if (ntb > nfull) {
+      LRS_SDT(true, 2, nfull - 1);
+      LRS_SDT(false, 0, nfull);
+    } else {
+      LRS_SDT(true, 0, nfull - 1);
+    }
+  } else {
+    sru_deer_persist_load<IO, L, CPT, false, NT>(zf, zx, c0p, y, w0, T, C, cbase, off, nvc, w);
+    for (int64_t tb = 0; tb < ntb; ++tb) {
+      if (tb + 1 < ntb) LRS_SDT(false, 2, tb);
+      else LRS_SDT(false, 0, tb);
+    }
+  }
+#undef LRS_SDT
+  sru_deer_fold_norm<NW>(dmax, delta_bits, iter, ds);
 }
 
 // h = r tanh(c) + (1 - r) z_x with r = sigmoid(z_r + b_r), and c_T, from the
@@ -271,10 +461,16 @@ __global__ __launch_bounds__(256) void k_sru_deer_out(const IO* __restrict__ zr,
 // ---------------------------------------------------------------------------
 namespace {
 constexpr int kSdNW = 8, kSdL = 8, kSdCPT = 2;
+// persistent walk: 16 steps per lane for bf16 I/O (229 VGPRs), 8 for fp32
+constexpr int kSdPNW = 8, kSdPL16 = 16, kSdPL32 = 8, kSdPCPT = 2;
 }
 
-ColPlan plan_sru_deer(int64_t C, int64_t T, int io_dtype) {
+ColPlan plan_sru_deer(int64_t C, int64_t T, int io_dtype, bool allow_persist) {
   ColPlan p = plan_cols(C, T, kSdNW, kSdL, kSdCPT);
+  if (allow_persist && p.ncb >= persist_min_blocks()) {  // the channel blocks alone fill the GPU
+    p = plan_cols(C, T, kSdPNW, io_dtype == 1 ? kSdPL16 : kSdPL32, kSdPCPT);
+    p.persist = true;
+  }
   // z_f, z_x (io type), the iterate and the next iterate
   p.stream = C * T * (2 * (io_dtype == 1 ? 2 : 4) + 8) >= kStreamFootprint;
   return p;
@@ -286,6 +482,22 @@ hipError_t launch_sru_deer_iter(const void* zf, const void* zx, const float* bia
                                 int vec, uint64_t* status, unsigned* tickets,
                                 uint32_t* delta_bits, uint32_t* delta_out, int iter, float eps,
                                 hipStream_t stream) {
+  if (p.persist) {
+#define LRS_SDP(IO, L, NTF)                                                                    \
+  hipLaunchKernelGGL((k_sru_deer_iter_persist<IO, kSdPNW, L, kSdPCPT, NTF>),                   \
+                     dim3((unsigned)p.ncb), dim3(kSdPNW * kWave), 0, stream, (const IO*)zf,     \
+                     (const IO*)zx, bias_f, v_f, c0, y, yn, T, C, D, vec, delta_bits,           \
+                     delta_out, iter, eps)
+    if (io_dtype == 1) {
+      if (p.stream) LRS_SDP(uint16_t, kSdPL16, true);
+      else LRS_SDP(uint16_t, kSdPL16, false);
+    } else {
+      if (p.stream) LRS_SDP(float, kSdPL32, true);
+      else LRS_SDP(float, kSdPL32, false);
+    }
+#undef LRS_SDP
+    return hipGetLastError();
+  }
   const uint64_t grid = (uint64_t)p.ncb * (uint64_t)p.ntb;
 #define LRS_SD(IO, NTF)                                                                        \
   hipLaunchKernelGGL((k_sru_deer_iter<IO, kSdNW, kSdL, kSdCPT, NTF>), dim3((unsigned)grid),   \

@@ -1,9 +1,11 @@
-"""The persistent [T,B,D] layer kernels (one workgroup per channel block
-walking all time tiles, chosen when the channel blocks fill the GPU) against
-the fp64 oracle: forced through LRS_PERSIST_MIN_BLOCKS on ragged shapes
-(partial last tile in time, partial last channel block, both I/O types, c0,
-saved cell states and c_T), and at the full B=32 D=1024 T=2048 shape both
-ways, where the two kernel families must agree within the parity bar."""
+"""The persistent [T,B,D] kernels (one workgroup per channel block walking
+all time tiles, chosen when the channel blocks fill the GPU): the SRU forward
+and the SRU-by-DEER iteration, against the fp64 oracle, forced through
+LRS_PERSIST_MIN_BLOCKS on ragged shapes (partial last tile in time, partial
+last channel block, both I/O types, c0, saved cell states and c_T), and at the
+full B=32 D=1024 T=2048 shape both ways, where the two kernel families must
+agree within the parity bar; the persistent DEER solve also replays from a HIP
+graph."""
 import numpy as np
 import pytest
 import torch
@@ -13,6 +15,8 @@ import linear_recurrence_scan_diagonal_amd as lrs
 from linear_recurrence_scan_diagonal_amd import inputs as I
 from conftest import relerr
 from gpu_util import DEV, bf16_dev, log
+from test_gpu_graph_more import replay_matches
+from test_gpu_sru_nl import check as sru_deer_check, run as sru_deer_run
 
 pytestmark = pytest.mark.gpu
 
@@ -62,3 +66,38 @@ def test_sru_both_kernels_at_workload_shape(monkeypatch):
         assert eh <= 2e-2 and ec <= 1e-5
     # the saved cell states of the two kernel families agree (fp32 bar)
     assert relerr(outs["persistent"][2], outs["tiles"][2]) <= 1e-5
+
+
+@pytest.mark.parametrize("B,D,T", [(1, 1, 1), (1, 3, 7), (2, 5, 64), (3, 50, 200),
+                                   (1, 258, 513), (2, 128, 1000)])
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_sru_deer_persistent_ragged(monkeypatch, B, D, T, io):
+    monkeypatch.setenv("LRS_PERSIST_MIN_BLOCKS", "0")
+    w = I.scaled(I.WORKLOADS["sru_deer"], B=B, D=D, T=T, seed=13200 + B * 13 + D * 5 + T)
+    c0 = np.random.default_rng(T + D + 1).normal(size=(B, D)).astype(np.float32)
+    sru_deer_check(*sru_deer_run(w, io, c0=c0, k_max=8), io, f"persistent sru-deer {io} {B}x{D}x{T}")
+
+
+def test_sru_deer_both_kernels_at_workload_shape(monkeypatch):
+    w = I.WORKLOADS["sru_deer"]
+    for mode, lim in (("persistent", "0"), ("tiles", str(1 << 40))):
+        monkeypatch.setenv("LRS_PERSIST_MIN_BLOCKS", lim)
+        sru_deer_check(*sru_deer_run(w, "bf16"), "bf16", f"sru_deer workload, {mode}")
+
+
+def test_sru_deer_persistent_graph(monkeypatch):
+    monkeypatch.setenv("LRS_PERSIST_MIN_BLOCKS", "0")
+    w = I.scaled(I.WORKLOADS["sru_deer"], B=2, D=128, T=1000, seed=13300)
+    s = I.sru_inputs(w)
+    z = {k: bf16_dev(s[k]) for k in ("zf", "zr", "zx")}
+    bf, br = (torch.from_numpy(s[k]).to(DEV) for k in ("bias_f", "bias_r"))
+    vf = torch.from_numpy(I.sru_vf(w)).to(DEV)
+    h = torch.empty_like(z["zf"])
+    cs = torch.empty((1000, 2, 128), device=DEV)
+    ws = torch.empty(lrs.load().lrs_sru_deer_workspace_bytes(1000, 2, 128, 5), dtype=torch.uint8,
+                     device=DEV)
+
+    def step():
+        lrs.sru_deer_fwd(z["zf"], z["zr"], z["zx"], bf, br, vf, out=h, c_states=cs, workspace=ws,
+                         sync=False)
+    replay_matches(step, [h, cs], False, "persistent sru deer")
