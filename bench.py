@@ -89,7 +89,8 @@ KERNEL_NAMES = {"scan_fwd_f32": ("k_scan_fwd_bdt", "k_scan_fwd_tbd", "k_scan_fwd
                                       "k_sru_fwd_persist<unsigned short"),
                 "sru_bwd_bf16": ("k_sru_bwd<unsigned short",),
                 "deer_solve": ("k_deer_iter",),
-                "sru_deer_bf16": ("k_sru_deer_iter<unsigned short",),
+                "sru_deer_bf16": ("k_sru_deer_iter<unsigned short",
+                                  "k_sru_deer_iter_persist<unsigned short"),
                 "deer_bwd_f32": ("k_deer_bwd",),
                 "lstm_fwd_save_bf16": ("k_lstm_fwd<unsigned short",),
                 "lstm_bwd_bf16": ("k_lstm_bwd<unsigned short",)}

@@ -4,8 +4,8 @@ and the SRU-by-DEER iteration, against the fp64 oracle, forced through
 LRS_PERSIST_MIN_BLOCKS on ragged shapes (partial last tile in time, partial
 last channel block, both I/O types, c0, saved cell states and c_T), and at the
 full B=32 D=1024 T=2048 shape both ways, where the two kernel families must
-agree within the parity bar; the persistent DEER solve also replays from a HIP
-graph."""
+agree within the parity bar; with persistence forced, the SRU and SRU-by-DEER
+graph replays, the K_max cap, warm starts and the asynchronous form."""
 import numpy as np
 import pytest
 import torch
@@ -101,3 +101,22 @@ def test_sru_deer_persistent_graph(monkeypatch):
         lrs.sru_deer_fwd(z["zf"], z["zr"], z["zx"], bf, br, vf, out=h, c_states=cs, workspace=ws,
                          sync=False)
     replay_matches(step, [h, cs], False, "persistent sru deer")
+
+
+@pytest.mark.parametrize("name", ["test_sru_graph_replay", "test_sru_fwd_bwd_graph_replay"])
+def test_sru_persistent_graph(monkeypatch, name):
+    """The SRU graph replays (alone, and with the backward in the same graph)
+    with the persistent forward forced."""
+    import test_gpu_graph
+    monkeypatch.setenv("LRS_PERSIST_MIN_BLOCKS", "0")
+    getattr(test_gpu_graph, name)()
+
+
+@pytest.mark.parametrize("name", ["test_kmax_cap_and_warm_start", "test_async_form_and_stats",
+                                  "test_linear_case_matches_sru_layer"])
+def test_sru_deer_persistent_options(monkeypatch, name):
+    """The K_max cap, warm starts in place, the asynchronous form and the
+    v_f = 0 case with the persistent iteration forced."""
+    import test_gpu_sru_nl
+    monkeypatch.setenv("LRS_PERSIST_MIN_BLOCKS", "0")
+    getattr(test_gpu_sru_nl, name)()
