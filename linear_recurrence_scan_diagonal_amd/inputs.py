@@ -17,6 +17,14 @@ Recipe (the same everywhere):
   * ``normal(mu, s)`` takes the standard deviation ``s``; ``uniform(lo, hi)``
     draws from [lo, hi).
 
+Arrays above 2^31 elements (the size-limit tests) are drawn on the device
+instead, by ``device_draw``: torch's Philox generator seeded with
+``seed``, one call per array, in fp32 (``uniform(lo, hi)`` as
+lo + (hi - lo) * U[0, 1), ``normal(mu, s)`` as mu + s * N(0, 1), each rounded
+to fp32), optionally rounded once more to bf16.  Those device values are the
+canonical inputs of such a test; the oracle receives host copies of the parts
+it checks, widened exactly to float64.
+
 Array tags: a=1, b=2, h0=3, g=4, zf=5, zr=6, zx=7, bias_f=8, bias_r=9, w=10,
 u=11, h_init=12, gh=13, gcl=14, zi=15, zc=16, zo=17, vf=18.
 """
@@ -285,3 +293,24 @@ def deer_inputs(w: Workload, channels=None) -> dict:
     h0 = to_f32(params(w.seed, "h0", w.dists.get("h0", ("const", 0, 0)), (w.C,)))
     out["h0"] = h0[ch]
     return out
+
+
+def device_draw(seed: int, dist, shape, device, bf16: bool = False):
+    """Seeded draw of a (possibly > 2^31-element) array on the device; see the
+    module docstring.  dist as for ``series`` (uniform / normal / const)."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    kind, p, q = dist
+    if kind == "uniform":
+        x = torch.rand(shape, generator=g, device=device, dtype=torch.float32)
+        x.mul_(float(q) - float(p)).add_(float(p))
+    elif kind == "normal":
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        x.mul_(float(q)).add_(float(p))
+    elif kind == "const":
+        x = torch.full(shape, float(p), device=device, dtype=torch.float32)
+    else:
+        raise ValueError(f"unknown distribution {kind!r}")
+    return x.to(torch.bfloat16) if bf16 else x

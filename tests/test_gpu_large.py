@@ -1,0 +1,177 @@
+"""Size limits: every array above 2^31 elements, so that element offsets, chunk
+positions and row offsets only fit 64-bit arithmetic.  Inputs are drawn on the
+device (inputs.device_draw, seeded); the oracle receives host copies of the
+parts it checks.
+
+* scans in both layouts over 262,148 channels of 8192 steps, sampled channels
+  against the oracle (full rows) and the adjoint identity
+  <g, h> = <lam, b> + dh0 * h0 on every channel;
+* two channels of 2^30 + 24,836 steps (look-back over 131,076 chunks),
+  checked on windows against the oracle run over the window plus 40,000 steps
+  of lead-in (and lead-out for the backward) from a zero state: with
+  a <= 0.999 the dropped part is scaled by at most 0.999^40000 < 5e-18, far
+  below the 1e-5 bar, so the window result is the exact one within rounding;
+  windows at the start, in the middle, across element offset 2^31 and at the
+  end;
+* the SRU layer (bf16 I/O) forward with saved cell states and its backward,
+  and a DEER solve (3 Newton iterations, eps = 0 so both sides take exactly
+  K_max), over 2^31 + 32,768 elements, on sampled features against the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import linear_recurrence_scan_diagonal_amd as lrs
+from linear_recurrence_scan_diagonal_amd import inputs as I
+from gpu_util import DEV, log
+from test_gpu_scan import compare
+
+pytestmark = pytest.mark.gpu
+
+B_MANY, D_MANY, T_MANY = 4, 65537, 8192          # 262,148 channels
+N_MANY = B_MANY * D_MANY * T_MANY                  # 2^31 + 32,768
+SCAN = I.WORKLOADS["scan_fwd_bwd"].dists
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def release():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("layout", ["bdt", "tbd"])
+def test_scan_many_channels_past_2_31(layout):
+    B, D, T = B_MANY, D_MANY, T_MANY
+    C = B * D
+    assert N_MANY > 2 ** 31
+    shape = (B, D, T) if layout == "bdt" else (T, B, D)
+    log(f"large scan {layout} B={B} D={D} T={T} ({N_MANY} elements): drawing inputs")
+    a = I.device_draw(21001, SCAN["a"], shape, DEV)
+    b = I.device_draw(21002, SCAN["b"], shape, DEV)
+    g = I.device_draw(21004, SCAN["g"], shape, DEV)
+    h0 = I.device_draw(21003, SCAN["h0"], (B, D), DEV)
+    h = lrs.scan_fwd(a, b, h0, layout=layout)
+    da, db, dh0 = lrs.scan_bwd(a, h, g, h0, layout=layout)
+    torch.cuda.synchronize()
+    log(f"large scan {layout}: kernels done, checking")
+
+    def rows(t):  # [C, T] view in either layout
+        return t.view(C, T) if layout == "bdt" else t.view(T, C).t()
+    sample = [0, 1, 65537, C // 2, C - 3, C - 2, C - 1]
+    sx = {k: host(rows(t)[sample]) for k, t in (("a", a), ("b", b), ("g", g))}
+    sx["h0"] = host(h0.view(-1)[sample])
+    ref_h = oracle.scan_fwd(sx["a"], sx["b"], sx["h0"])
+    ref = {"h": ref_h}
+    ref["da"], ref["db"], ref["dh0"] = oracle.scan_bwd(sx["a"], ref_h, sx["h0"], sx["g"])
+    got = {"h": host(rows(h)[sample]), "da": host(rows(da)[sample]),
+           "db": host(rows(db)[sample]), "dh0": host(dh0.view(-1)[sample])}
+    compare(got, ref, tag=f"large scan {layout}")
+    # every channel: finite outputs and the adjoint identity, in float64 slices
+    worst = 0.0
+    step = 16384
+    for lo in range(0, C, step):
+        hi = min(C, lo + step)
+        hs, gs, bs, das, dbs = (rows(t)[lo:hi] for t in (h, g, b, da, db))
+        assert torch.isfinite(hs).all() and torch.isfinite(das).all() and torch.isfinite(dbs).all()
+        lhs = (gs.double() * hs.double()).sum(-1)
+        rhs = (dbs.double() * bs.double()).sum(-1) + \
+            dh0.view(-1)[lo:hi].double() * h0.view(-1)[lo:hi].double()
+        worst = max(worst, ((lhs - rhs).abs() / (1 + lhs.abs())).max().item())
+    log(f"large scan {layout} adjoint identity rel {worst:.2e}")
+    assert worst < 1e-3
+    del a, b, g, h0, h, da, db, dh0
+    release()
+
+
+def test_scan_long_channels_past_2_31():
+    B, D = 1, 2
+    T = (1 << 30) + 3 * 8192 + 260
+    assert B * D * T > 2 ** 31
+    log(f"large long scan B={B} D={D} T={T}: drawing inputs")
+    a = I.device_draw(22001, SCAN["a"], (B, D, T), DEV)
+    b = I.device_draw(22002, SCAN["b"], (B, D, T), DEV)
+    g = I.device_draw(22004, SCAN["g"], (B, D, T), DEV)
+    h0 = I.device_draw(22003, SCAN["h0"], (B, D), DEV)
+    h = lrs.scan_fwd(a, b, h0)
+    da, db, dh0 = lrs.scan_bwd(a, h, g, h0)
+    torch.cuda.synchronize()
+    assert torch.isfinite(h).all() and torch.isfinite(da).all() and torch.isfinite(db).all()
+    lead = 40000
+    # (channel, first step, steps); channel 1 holds element offset 2^31 at step 2^31 - T
+    windows = [(0, 0, 8192), (0, 1 << 29, 8192), (1, (1 << 31) - T - 4096, 8192),
+               (1, T - 8192, 8192)]
+    for c, s, n in windows:
+        lo, hi = max(0, s - lead), min(T, s + n + lead)
+        wa, wb, wg = (host(t[0, c, lo:hi])[None] for t in (a, b, g))
+        x0 = host(h0[0, c:c + 1]) if lo == 0 else np.zeros(1)
+        ref_h = oracle.scan_fwd(wa, wb, x0)
+        ref_da, ref_db, ref_dh0 = oracle.scan_bwd(wa, ref_h, x0, wg)
+        k = s - lo
+        ref = {"h": ref_h[:, k:k + n], "da": ref_da[:, k:k + n], "db": ref_db[:, k:k + n]}
+        got = {"h": host(h[0, c, s:s + n])[None], "da": host(da[0, c, s:s + n])[None],
+               "db": host(db[0, c, s:s + n])[None]}
+        if lo == 0:
+            ref["dh0"], got["dh0"] = ref_dh0, host(dh0[0, c:c + 1])
+        compare(got, ref, tag=f"large long scan channel {c} steps {s}..{s + n}")
+    del a, b, g, h0, h, da, db, dh0
+    release()
+
+
+def test_sru_fwd_bwd_past_2_31():
+    T, B, D = T_MANY, B_MANY, D_MANY
+    dist = I.WORKLOADS["sru_fwd_bwd"].dists
+    log(f"large SRU T={T} B={B} D={D} ({N_MANY} elements, bf16): drawing inputs")
+    z = {k: I.device_draw(23000 + i, dist[k], (T, B, D), DEV, bf16=True)
+         for i, k in enumerate(("zf", "zr", "zx", "gh"))}
+    bf = I.device_draw(23010, dist["bias_f"], (D,), DEV)
+    br = I.device_draw(23011, dist["bias_r"], (D,), DEV)
+    cs = torch.empty((T, B, D), dtype=torch.float32, device=DEV)
+    h, cl = lrs.sru_fwd(z["zf"], z["zr"], z["zx"], bf, br, want_c_last=True, c_states=cs)
+    grads = lrs.sru_bwd(z["zf"], z["zr"], z["zx"], bf, br, cs, z["gh"])
+    torch.cuda.synchronize()
+    log("large SRU: kernels done, checking")
+    feats = [0, 1, D // 2, D - 1]   # every batch entry of these features
+    zs = {k: host(t[:, :, feats]) for k, t in z.items()}
+    bfs, brs = host(bf[feats]), host(br[feats])
+    ref_h, ref_cl = oracle.sru_fwd(zs["zf"], zs["zr"], zs["zx"], bfs, brs)
+    e = {"h": relerr_bar(host(h[:, :, feats]), ref_h, 2e-2),
+         "c_last": relerr_bar(host(cl[:, feats]), ref_cl, 1e-5)}
+    ref_b = oracle.sru_bwd(zs["zf"], zs["zr"], zs["zx"], bfs, brs, zs["gh"])
+    got_b = dict(zip(("dzf", "dzr", "dzx", "dbf", "dbr", "dc0"), grads))
+    for k in ("dzf", "dzr", "dzx"):
+        e[k] = relerr_bar(host(got_b[k][:, :, feats]), ref_b[k], 2e-2)
+    for k in ("dbf", "dbr"):
+        e[k] = relerr_bar(host(got_b[k][feats]), ref_b[k], 1e-5)
+    e["dc0"] = relerr_bar(host(got_b["dc0"][:, feats]), ref_b["dc0"], 1e-5)
+    log("large SRU errors: " + ", ".join(f"{k}={v:.2e}" for k, v in e.items()))
+    del z, bf, br, cs, h, cl, grads, got_b
+    release()
+
+
+def test_deer_past_2_31():
+    B, D, T = B_MANY, D_MANY, T_MANY
+    dist = I.WORKLOADS["deer"].dists
+    log(f"large DEER B={B} D={D} T={T}: drawing inputs")
+    u = I.device_draw(24001, dist["u"], (B, D, T), DEV)
+    w = I.device_draw(24002, dist["w"], (D,), DEV)
+    h, info = lrs.deer_solve(w, u, eps=0.0, k_max=3)
+    torch.cuda.synchronize()
+    assert info["iters"] == 3
+    feats = [0, 7, D // 2, D - 1]
+    ref_h, ref_it, _ = oracle.deer(host(w[feats]), host(u[:, feats, :]), eps=0.0, k_max=3)
+    assert ref_it == 3
+    e = relerr_bar(host(h[:, feats, :]), ref_h, 1e-5)
+    log(f"large DEER h relerr {e:.2e}")
+    del u, w, h
+    release()
+
+
+def relerr_bar(x, ref, bar):
+    from conftest import relerr
+    e = relerr(x, ref)
+    assert e <= bar, (e, bar)
+    return e
