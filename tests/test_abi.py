@@ -9,7 +9,10 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "lrs.h")
-LIB = os.path.join(ROOT, "linear_recurrence_scan_diagonal_amd", "liblrs.so")
+# LRS_TEST_LIB: run these tests against another build of the same sources
+# (the sanitizer test uses it for a host-instrumented copy)
+LIB = os.environ.get("LRS_TEST_LIB") or os.path.join(ROOT, "linear_recurrence_scan_diagonal_amd",
+                                                     "liblrs.so")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="liblrs.so not built")
 
@@ -27,6 +30,8 @@ def header_constants():
 @pytest.fixture(scope="module")
 def lib():
     from linear_recurrence_scan_diagonal_amd import binding
+    if binding._lib is None:
+        binding.LIB_PATH = LIB
     return binding.load()
 
 
