@@ -6,6 +6,8 @@ parts it checks.
 * scans in both layouts over 262,148 channels of 8192 steps, sampled channels
   against the oracle (full rows) and the adjoint identity
   <g, h> = <lam, b> + dh0 * h0 on every channel;
+* short channels past 2^31 elements: T = 32 (the packed kernels) and T = 4
+  (one lane per channel), sampled channels against the oracle;
 * two channels of 2^30 + 24,836 steps (look-back over 131,076 chunks),
   checked on windows against the oracle run over the window plus 40,000 steps
   of lead-in (and lead-out for the backward) from a zero state: with
@@ -83,6 +85,35 @@ def test_scan_many_channels_past_2_31(layout):
         worst = max(worst, ((lhs - rhs).abs() / (1 + lhs.abs())).max().item())
     log(f"large scan {layout} adjoint identity rel {worst:.2e}")
     assert worst < 1e-3
+    del a, b, g, h0, h, da, db, dh0
+    release()
+
+
+@pytest.mark.parametrize("T", [32, 4])
+def test_scan_short_channels_past_2_31(T):
+    """Short channels (T = 32: whole channels packed into each workgroup; T = 4:
+    one lane per channel) over 2^31/T + 4 channels."""
+    C = (1 << 31) // T + 4
+    B, D = 4, C // 4
+    assert B * D == C and C * T > 2 ** 31
+    log(f"large short scan B={B} D={D} T={T}: drawing inputs")
+    a = I.device_draw(25001 + T, SCAN["a"], (B, D, T), DEV)
+    b = I.device_draw(25002 + T, SCAN["b"], (B, D, T), DEV)
+    g = I.device_draw(25004 + T, SCAN["g"], (B, D, T), DEV)
+    h0 = I.device_draw(25003 + T, SCAN["h0"], (B, D), DEV)
+    h = lrs.scan_fwd(a, b, h0)
+    da, db, dh0 = lrs.scan_bwd(a, h, g, h0)
+    torch.cuda.synchronize()
+    assert torch.isfinite(h).all() and torch.isfinite(da).all() and torch.isfinite(db).all()
+    sample = [0, 1, C // 2, C - 5, C - 2, C - 1]
+    sx = {k: host(t.view(C, T)[sample]) for k, t in (("a", a), ("b", b), ("g", g))}
+    sx["h0"] = host(h0.view(-1)[sample])
+    ref_h = oracle.scan_fwd(sx["a"], sx["b"], sx["h0"])
+    ref = {"h": ref_h}
+    ref["da"], ref["db"], ref["dh0"] = oracle.scan_bwd(sx["a"], ref_h, sx["h0"], sx["g"])
+    got = {"h": host(h.view(C, T)[sample]), "da": host(da.view(C, T)[sample]),
+           "db": host(db.view(C, T)[sample]), "dh0": host(dh0.view(-1)[sample])}
+    compare(got, ref, tag=f"large short scan T={T}")
     del a, b, g, h0, h, da, db, dh0
     release()
 
