@@ -135,7 +135,7 @@ __device__ __forceinline__ void lstm_bwd_tile(
     const IO* __restrict__ gh, const float* __restrict__ gcl, IO* __restrict__ dzf,
     IO* __restrict__ dzi, IO* __restrict__ dzc, IO* __restrict__ dzo, float* __restrict__ dc0,
     int64_t T, int64_t C, int tb, int ntb, int cb, bool multi, uint64_t* st,
-    ColShared<NW, CPT>& s) {
+    ColShared<NW, CPT>& s, float (&crow)[NW][kWave * CPT]) {
   constexpr int CW = kWave * CPT;
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -145,10 +145,9 @@ __device__ __forceinline__ void lstm_bwd_tile(
   const int64_t c0i = cbase + off;
   const int nvc = FULL ? CPT : clamp_valid(C - c0i, CPT);
   const int64_t row0 = (int64_t)ptb * (NW * L) + (int64_t)(NW - 1 - wid) * L;
-  // f at rows row0 .. row0+L-1 and f[L] for the step after the wave (1 at and
-  // beyond the end of the sequence); c at the wave's rows and just before;
-  // e at the wave's rows
-  float f[L + 1][CPT], c[L][CPT], cp[CPT], e[L][CPT];
+  // f, c and e at rows row0 .. row0+L-1 (f = 1 beyond the end of the
+  // sequence), c just before the wave's first row
+  float f[L][CPT], c[L][CPT], cp[CPT], e[L][CPT];
   IoRow<IO, CPT> irow[L], grow[L];
   {
     const IO* fp = zf + row0 * C + cbase;
@@ -189,39 +188,44 @@ __device__ __forceinline__ void lstm_bwd_tile(
       cq += C;
       qo += C;
     }
-    const int64_t tn = row0 + L;
-    if (tn < T) {
-      IoRow<IO, CPT> fr;
-      fr.template load<FULL, false>(zf + tn * C + cbase, off, nvc);
+    // c before the first row: the earlier wave's last row (shared through LDS
+    // below), read from memory only by the wave at the tile's start
+    if (wid == NW - 1) {
+      if (row0 > 0 && row0 <= T) {
+        load_row<CPT, FULL, false>(cs + (row0 - 1) * C + cbase, off, nvc, 0.0f, cp);
+      } else {
 #pragma unroll
-      for (int k = 0; k < CPT; ++k)
-        f[L][k] = (FULL || k < nvc) ? fast_sigmoid(fr.get(k), 0.0f) : 1.0f;
-    } else {
-#pragma unroll
-      for (int k = 0; k < CPT; ++k) f[L][k] = 1.0f;
+        for (int k = 0; k < CPT; ++k) cp[k] = (c0p && k < nvc) ? c0p[c0i + k] : 0.0f;
+      }
     }
-    if (row0 > 0 && row0 <= T) {
-      load_row<CPT, FULL, false>(cs + (row0 - 1) * C + cbase, off, nvc, 0.0f, cp);
-    } else {
 #pragma unroll
-      for (int k = 0; k < CPT; ++k) cp[k] = (c0p && k < nvc) ? c0p[c0i + k] : 0.0f;
-    }
+    for (int k = 0; k < CPT; ++k) crow[wid][off + k] = c[L - 1][k];
   }
+  // The state passed between waves and tiles is y = f_t gc_t at the first row
+  // t of the later wave (y = dL/dc_T past the end, where f = 1), so every
+  // forget gate a wave needs is one of its own rows:
+  //   gc_{L-1} = e_{L-1} + y_in,  gc_i = e_i + f_{i+1} gc_{i+1},  y_out = f_0 gc_0.
   float A[CPT], B[CPT];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
-    A[k] = f[L][k];
+    A[k] = 1.0f;
     B[k] = e[L - 1][k];
 #pragma unroll
     for (int i = L - 2; i >= 0; --i) {
       B[k] = __builtin_fmaf(f[i + 1][k], B[k], e[i][k]);
       A[k] = A[k] * f[i + 1][k];
     }
+    A[k] = A[k] * f[0][k];
+    B[k] = B[k] * f[0][k];
   }
   float x0[CPT], x[CPT];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) x0[k] = (gcl && k < nvc) ? gcl[c0i + k] : 0.0f;
   col_enter_state<NW, CPT>(A, B, multi, tb, x0, gcl, cbase, clamp_valid(C - cbase, CW), st, s, x);
+  if (wid < NW - 1) {  // past col_enter_state's barrier: every wave has written crow
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) cp[k] = crow[wid + 1][off + k];
+  }
   IO* qf = dzf + (row0 + L - 1) * C + cbase;
   IO* qi = dzi + (row0 + L - 1) * C + cbase;
   IO* qc = dzc + (row0 + L - 1) * C + cbase;
@@ -230,7 +234,7 @@ __device__ __forceinline__ void lstm_bwd_tile(
     float of[CPT], oi[CPT], oc[CPT];
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
-      x[k] = __builtin_fmaf(f[i + 1][k], x[k], e[i][k]);  // gc_t
+      x[k] = (i == L - 1) ? x[k] + e[i][k] : __builtin_fmaf(f[i + 1][k], x[k], e[i][k]);  // gc_t
       const float fi = f[i][k];
       const float ig = fast_sigmoid(irow[i].get(k), 0.0f);
       const float g = fast_tanh(grow[i].get(k));
@@ -264,6 +268,7 @@ __global__ __launch_bounds__(NW* kWave) void k_lstm_bwd(
     unsigned* __restrict__ tickets) {
   constexpr int CW = kWave * CPT, TW = NW * L;
   __shared__ ColShared<NW, CPT> s;
+  __shared__ float crow[NW][CW];
   const bool multi = ntb > 1;
   const int cb = (int)(blockIdx.x % (unsigned)ncb);
   const int tb = col_ticket<NW, CPT>(multi, tickets, cb, s);
@@ -272,10 +277,10 @@ __global__ __launch_bounds__(NW* kWave) void k_lstm_bwd(
   const bool full = vec && ((int64_t)(ptb + 1) * TW <= T) && ((int64_t)(cb + 1) * CW <= C);
   if (full)
     lstm_bwd_tile<IO, NW, L, CPT, true, NT>(zf, zi, zc, zo, c0p, cs, gh, gcl, dzf, dzi, dzc, dzo,
-                                            dc0, T, C, tb, ntb, cb, multi, st, s);
+                                            dc0, T, C, tb, ntb, cb, multi, st, s, crow);
   else
     lstm_bwd_tile<IO, NW, L, CPT, false, NT>(zf, zi, zc, zo, c0p, cs, gh, gcl, dzf, dzi, dzc,
-                                             dzo, dc0, T, C, tb, ntb, cb, multi, st, s);
+                                             dzo, dc0, T, C, tb, ntb, cb, multi, st, s, crow);
 }
 
 // ---------------------------------------------------------------------------

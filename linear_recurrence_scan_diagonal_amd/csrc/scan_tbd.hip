@@ -537,7 +537,7 @@ __device__ __forceinline__ void sru_bwd_tile(
     const float* __restrict__ gcl, IO* __restrict__ dzf, IO* __restrict__ dzr,
     IO* __restrict__ dzx, float* __restrict__ dc0, float* __restrict__ part, int64_t T,
     int64_t C, int64_t D, int tb, int ntb, int cb, bool multi, uint64_t* st,
-    ColShared<NW, CPT>& s) {
+    ColShared<NW, CPT>& s, float (&crow)[NW][kWave * CPT]) {
   constexpr int CW = kWave * CPT;
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -558,9 +558,9 @@ __device__ __forceinline__ void sru_bwd_tile(
       d = (d + 1 == D) ? 0 : d + 1;
     }
   }
-  // f at rows row0 .. row0+L-1, and f[L] for the step after the wave (1 at
-  // and beyond the end of the sequence); c at the wave's rows and just before
-  float f[L + 1][CPT], c[L][CPT], cp[CPT];
+  // f and c at rows row0 .. row0+L-1 (f = 1 beyond the end of the sequence),
+  // c just before the wave's first row
+  float f[L][CPT], c[L][CPT], cp[CPT];
   IoRow<IO, CPT> rr[L], xr[L], gr[L];
   {
     const IO* fp = zf + row0 * C + cbase;
@@ -585,22 +585,18 @@ __device__ __forceinline__ void sru_bwd_tile(
       gp += C;
       cq += C;
     }
-    const int64_t tn = row0 + L;
-    if (tn < T) {
-      IoRow<IO, CPT> fr;
-      fr.template load<FULL, false>(zf + tn * C + cbase, off, nvc);
+    // c before the first row: the earlier wave's last row (shared through LDS
+    // below), read from memory only by the wave at the tile's start
+    if (wid == NW - 1) {
+      if (row0 > 0 && row0 <= T) {
+        load_row<CPT, FULL, false>(cs + (row0 - 1) * C + cbase, off, nvc, 0.0f, cp);
+      } else {
 #pragma unroll
-      for (int k = 0; k < CPT; ++k) f[L][k] = (FULL || k < nvc) ? fast_sigmoid(fr.get(k), nbf[k]) : 1.0f;
-    } else {
-#pragma unroll
-      for (int k = 0; k < CPT; ++k) f[L][k] = 1.0f;
+        for (int k = 0; k < CPT; ++k) cp[k] = (c0p && k < nvc) ? c0p[c0i + k] : 0.0f;
+      }
     }
-    if (row0 > 0 && row0 <= T) {
-      load_row<CPT, FULL, false>(cs + (row0 - 1) * C + cbase, off, nvc, 0.0f, cp);
-    } else {
 #pragma unroll
-      for (int k = 0; k < CPT; ++k) cp[k] = (c0p && k < nvc) ? c0p[c0i + k] : 0.0f;
-    }
+    for (int k = 0; k < CPT; ++k) crow[wid][off + k] = c[L - 1][k];
   }
   // e_t with r_t and tanh c_t (rows and channels out of range have gh = 0)
   auto e_at = [&](int i, int k, float& r, float& th) {
@@ -609,22 +605,32 @@ __device__ __forceinline__ void sru_bwd_tile(
     const float gr_ = gr[i].get(k) * r;
     return __builtin_fmaf(-gr_ * th, th, gr_);
   };
+  // The state passed between waves and tiles is y = f_t gc_t at the first row
+  // t of the later wave (y = dL/dc_T past the end, where f = 1), so every
+  // forget gate a wave needs is one of its own rows:
+  //   gc_{L-1} = e_{L-1} + y_in,  gc_i = e_i + f_{i+1} gc_{i+1},  y_out = f_0 gc_0.
   float A[CPT], B[CPT];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
     float r, th;
-    A[k] = f[L][k];
+    A[k] = 1.0f;
     B[k] = e_at(L - 1, k, r, th);
 #pragma unroll
     for (int i = L - 2; i >= 0; --i) {
       B[k] = __builtin_fmaf(f[i + 1][k], B[k], e_at(i, k, r, th));
       A[k] = A[k] * f[i + 1][k];
     }
+    A[k] = A[k] * f[0][k];
+    B[k] = B[k] * f[0][k];
   }
   float x0[CPT], x[CPT];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) x0[k] = (gcl && k < nvc) ? gcl[c0i + k] : 0.0f;
   col_enter_state<NW, CPT>(A, B, multi, tb, x0, gcl, cbase, clamp_valid(C - cbase, CW), st, s, x);
+  if (wid < NW - 1) {  // past col_enter_state's barrier: every wave has written crow
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) cp[k] = crow[wid + 1][off + k];
+  }
   float pf[CPT], pr[CPT];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) { pf[k] = 0.0f; pr[k] = 0.0f; }
@@ -639,7 +645,7 @@ __device__ __forceinline__ void sru_bwd_tile(
     for (int k = 0; k < CPT; ++k) {
       float r, th;
       const float e = e_at(i, k, r, th);
-      x[k] = __builtin_fmaf(f[i + 1][k], x[k], e);  // gc_t
+      x[k] = (i == L - 1) ? x[k] + e : __builtin_fmaf(f[i + 1][k], x[k], e);  // gc_t
       const float g = gr[i].get(k), z = xr[i].get(k), fi = f[i][k];
       const float cprev = (i > 0) ? c[i - 1][k] : cp[k];
       ox[k] = __builtin_fmaf(g, 1.0f - r, x[k] * (1.0f - fi));
@@ -698,6 +704,7 @@ __global__ __launch_bounds__(NW* kWave) void k_sru_bwd(
     unsigned* __restrict__ tickets) {
   constexpr int CW = kWave * CPT, TW = NW * L;
   __shared__ ColShared<NW, CPT> s;
+  __shared__ float crow[NW][CW];
   const bool multi = ntb > 1;
   const int cb = (int)(blockIdx.x % (unsigned)ncb);
   const int tb = col_ticket<NW, CPT>(multi, tickets, cb, s);
@@ -706,11 +713,12 @@ __global__ __launch_bounds__(NW* kWave) void k_sru_bwd(
   const bool full = vec && ((int64_t)(ptb + 1) * TW <= T) && ((int64_t)(cb + 1) * CW <= C);
   if (full)
     sru_bwd_tile<IO, NW, L, CPT, true, NT>(zf, zr, zx, bias_f, bias_r, c0p, cs, gh, gcl, dzf, dzr,
-                                           dzx, dc0, part, T, C, D, tb, ntb, cb, multi, st, s);
+                                           dzx, dc0, part, T, C, D, tb, ntb, cb, multi, st, s,
+                                           crow);
   else
     sru_bwd_tile<IO, NW, L, CPT, false, NT>(zf, zr, zx, bias_f, bias_r, c0p, cs, gh, gcl, dzf,
                                             dzr, dzx, dc0, part, T, C, D, tb, ntb, cb, multi, st,
-                                            s);
+                                            s, crow);
 }
 
 // ---------------------------------------------------------------------------
