@@ -2,6 +2,7 @@
 // workspace carving and launch-plan choice.  All device work is enqueued on
 // the caller's stream; nothing here allocates device memory.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <vector>
@@ -640,6 +641,24 @@ static int read_deer_record(const DeerRecord& r, int k_max, int* iters_out, floa
   return buf[2] ? LRS_ERR_NONFINITE : LRS_OK;
 }
 
+// The fused solve (all Newton iterations in one walk over each channel) applies
+// to channels that one workgroup walks and to k_max <= kDeerFuseMax; it needs
+// one norm slot set per iteration.
+static bool deer_fusable(const lrs::RowPlan& p, int k_max) {
+  return p.nchunk == 1 && k_max <= lrs::kDeerFuseMax;
+}
+
+// LRS_DEER_FUSE=0 (read at every call) runs the iterations one launch each
+// even where the fused solve applies.
+static bool deer_fuse_enabled() {
+  const char* v = getenv("LRS_DEER_FUSE");
+  return !(v && v[0] == '0' && v[1] == '\0');
+}
+
+static size_t deer_fused_set_words(int k_max) {
+  return (size_t)k_max * lrs::kDeltaSlots * lrs::kDeltaStride;
+}
+
 size_t lrs_deer_workspace_bytes(int64_t B, int64_t D, int64_t T, int k_max) {
   int64_t C, N;
   if (!shape_ok(B, D, T, &C, &N) || k_max < 1) return 0;
@@ -647,6 +666,7 @@ size_t lrs_deer_workspace_bytes(int64_t B, int64_t D, int64_t T, int k_max) {
   const lrs::RowPlan p = deer_plan(C, T);
   size_t bytes = kAlign + deer_record_bytes(k_max) + align_up((size_t)N * 4);
   if (p.nchunk > 1) bytes += align_up((size_t)(C * p.nchunk) * 8) + align_up((size_t)C * 4);
+  if (deer_fusable(p, k_max)) bytes += align_up(deer_fused_set_words(k_max) * 4);
   return bytes;
 }
 
@@ -689,13 +709,27 @@ int lrs_deer_solve(const float* w, const float* u, const float* h0, const float*
   }
   if (overlap(ybuf, nb, u, nb) || overlap(ybuf, nb, h, nb) || overlap(ybuf, nb, h_init, nb))
     return LRS_ERR_INVALID_ARG;
+  const int vec = aligned(u, 16) && aligned(h, 16) && aligned(ybuf, 16) &&
+                  (!h_init || aligned(h_init, 16)) && (T % 4 == 0);
+
+  if (deer_fusable(p, k_max) && deer_fuse_enabled()) {
+    uint32_t* sets = cv.take<uint32_t>((int64_t)deer_fused_set_words(k_max));
+    // the pass must not overwrite a starting iterate held in h: a redo may need it
+    float* out = (h_init == h) ? ybuf : h;
+    int rc = hip_status(lrs::launch_reset(nullptr, 0, nullptr, 0, sets,
+                                          (int64_t)deer_fused_set_words(k_max), s));
+    if (rc != LRS_OK) return rc;
+    rc = hip_status(lrs::launch_deer_fused(w, u, h_init, h0, out, h, C, D, T, p, vec, k_max, eps,
+                                           sets, delta_out, r.rec, s));
+    if (rc != LRS_OK) return rc;
+    if (!iters_out && !deltas_out && !converged_out) return LRS_OK;  // asynchronous form
+    return read_deer_record(r, k_max, iters_out, deltas_out, converged_out, s);
+  }
 
   // ping-pong: iteration i writes P[i % 2]; if the starting iterate lives in h,
   // iteration 0 must not write h, so the roles swap
   float* P[2] = {h, ybuf};
   if (h_init == h) { P[0] = ybuf; P[1] = h; }
-  const int vec = aligned(u, 16) && aligned(h, 16) && aligned(ybuf, 16) &&
-                  (!h_init || aligned(h_init, 16)) && (T % 4 == 0);
   int rc = hip_status(lrs::launch_reset(status, p.nchunk > 1 ? C * p.nchunk : 0, tickets,
                                         p.nchunk > 1 ? C : 0, delta_bits,
                                         lrs::kDeltaSetWords + lrs::kDeerRecordWords + k_max, s));

@@ -108,6 +108,17 @@ hipError_t launch_deer_iter(const float* w, const float* u, const float* y, cons
                             uint32_t* delta_out, int iter, float eps, hipStream_t stream,
                             uint32_t* seq_slots = nullptr, const uint32_t* seq_delta = nullptr,
                             int k_max = 0);
+// DEER with the Newton iterations fused into one walk over each channel
+// (single-workgroup channels, k_max <= kDeerFuseMax): the pass over all k_max
+// iterations into `out` (h, or a buffer when h holds the starting iterate),
+// the finish kernel writing the record and norms, the redo launch when the stop
+// rule fired earlier, and the copy into h.  `sets` holds k_max slot sets of
+// kDeltaSlots * kDeltaStride words, cleared beforehand.
+constexpr int kDeerFuseMax = 8;
+hipError_t launch_deer_fused(const float* w, const float* u, const float* y0, const float* h0,
+                             float* out, float* h, int64_t C, int64_t D, int64_t T,
+                             const RowPlan& p, int vec, int k_max, float eps, uint32_t* sets,
+                             uint32_t* delta_out, int* rec, hipStream_t stream);
 hipError_t launch_deer_seq_book(uint32_t* seq_slots, uint32_t* seq_delta, int64_t nseq, int k_max,
                                 int iter, hipStream_t stream);
 hipError_t launch_deer_seq_finish(const uint32_t* seq_delta, int* seq_rec, int64_t nseq,

@@ -29,6 +29,8 @@
 //   k_deer_iter    : one fused DEER Newton iteration for h_t = tanh(w h_{t-1}+u_t)
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include "lrs_device.hpp"
 #include "lrs_internal.hpp"
 
@@ -1056,6 +1058,239 @@ __global__ __launch_bounds__(NW* kWave) void k_deer_iter(
   }
 }
 
+// ---------------------------------------------------------------------------
+// DEER solve with the Newton iterations fused into one walk over each channel
+// (channels that one workgroup walks as sequential sub-chunks).  For every
+// sub-chunk the workgroup loads u, and the starting iterate if there is one,
+// once, then computes iterates 1..m in order, each from the previous one held
+// in registers.  Iteration k's scan state entering a sub-chunk comes from the
+// previous sub-chunk (LDS slot xc[k]); it is also y_k at the step before the
+// sub-chunk, which iteration k+1 needs, and inside a sub-chunk y_{k-1} at the
+// step before a wave's first step is iteration k-1's state entering that wave
+// (from the block combine).  Only the last iterate is stored: 8 bytes per
+// element for the whole solve instead of 8 + 12 (m - 1).  The arithmetic of
+// each iteration is that of k_deer_iter, and iteration k's max |y_k - y_{k-1}|
+// is folded into slot set k - 1.  The global stop rule is known only after the
+// pass, so the pass runs m = k_max iterations; when the rule stops the solve
+// earlier (rec[0] < k_max, written by k_deer_fused_finish), a second launch
+// with `redo` set recomputes exactly rec[0] iterations into h (any other redo
+// launch returns at once).
+// ---------------------------------------------------------------------------
+template <int NW>
+struct FusedShared {
+  float wA[2][NW];
+  float wB[2][NW];
+  float y0w[NW];                       // starting iterate at each wave's last step
+  float xc[kDeerFuseMax + 1];          // iteration k's state entering the sub-chunk
+  uint32_t dmax[kDeerFuseMax][NW];     // per-wave max |y_k - y_{k-1}|
+};
+
+template <int NW>
+__device__ __forceinline__ void fused_combine(float WA, float WB, FusedShared<NW>& s, int par,
+                                              float& PA, float& PB, float& TA, float& TB) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  if (lane == 0) {
+    s.wA[par][wid] = WA;
+    s.wB[par][wid] = WB;
+  }
+  __syncthreads();
+  PA = 1.0f; PB = 0.0f; TA = 1.0f; TB = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const float wa = s.wA[par][w], wb = s.wB[par][w];
+    if (w < wid) {
+      PB = __builtin_fmaf(wa, PB, wb);
+      PA = PA * wa;
+    }
+    TB = __builtin_fmaf(wa, TB, wb);
+    TA = TA * wa;
+  }
+}
+
+// One sub-chunk (index c) of the fused solve: iterations 1..m.  y0last: the
+// starting iterate at the previous sub-chunk's last step (updated for the
+// next one); par: LDS parity of the wave maps (alternates per iteration).
+template <int NW, int R, bool FULL, bool NT>
+__device__ __forceinline__ void deer_fused_sub(const float* __restrict__ urow,
+                                               const float* __restrict__ y0row,
+                                               float* __restrict__ orow, int64_t T, int c,
+                                               int vec, int m, float wd, float x0,
+                                               float& y0last, int& par, FusedShared<NW>& s) {
+  constexpr int S = R * 256, CH = NW * S;
+  constexpr float k2l2e = 2.0f * 1.4426950408889634f;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const int64_t base = (int64_t)c * CH + (int64_t)wid * S + 4 * lane;
+  const float ws = wd * k2l2e;
+  float uv[R][4], yv[R][4];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float4 u4 = ld4<FULL, NT>(urow, base + r * 256, T, vec, 0.0f);
+    const float4 y4 = y0row ? ld4<FULL, NT>(y0row, base + r * 256, T, vec, 0.0f)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    uv[r][0] = u4.x; uv[r][1] = u4.y; uv[r][2] = u4.z; uv[r][3] = u4.w;
+    yv[r][0] = y4.x; yv[r][1] = y4.y; yv[r][2] = y4.z; yv[r][3] = y4.w;
+  }
+  // starting iterate at the step before this wave's first step
+  float ent;
+  if (y0row) {
+    if (lane == kWave - 1) s.y0w[wid] = yv[R - 1][3];
+    __syncthreads();
+    ent = wid > 0 ? s.y0w[wid - 1] : (c == 0 ? x0 : y0last);
+    y0last = s.y0w[NW - 1];  // read before any later write: the next writes follow a barrier
+  } else {
+    ent = (c == 0 && wid == 0) ? x0 : 0.0f;
+    if (c > 0) __syncthreads();  // the previous sub-chunk's last carry write (m = 1) is seen
+  }
+#pragma unroll 1
+  for (int k = 1; k <= m; ++k) {
+    const float xin = s.xc[k];
+    float z[R][4], yf[R], Ai[R], Bi[R], RA[R], RB[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float fy = (r > 0) ? readlane_f(yv[r - 1][3], kWave - 1) : ent;
+      yf[r] = wave_shift_up(yv[r][3], fy);
+      const float yp[4] = {yf[r], yv[r][0], yv[r][1], yv[r][2]};
+      float J[4], rh[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(ws, yp[j], k2l2e * uv[r][j]));
+        z[r][j] = __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + e), 1.0f);
+        J[j] = __builtin_fmaf(-wd * z[r][j], z[r][j], wd);  // w (1 - z^2)
+        rh[j] = __builtin_fmaf(-J[j], yp[j], z[r][j]);      // z - J y_{t-1}
+      }
+      if (!FULL) {
+        const int64_t p = base + r * 256;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (p + j >= T) { J[j] = 1.0f; rh[j] = 0.0f; }
+      }
+      float A = J[0], B = rh[0];
+#pragma unroll
+      for (int j = 1; j < 4; ++j) {
+        B = __builtin_fmaf(J[j], B, rh[j]);
+        A = A * J[j];
+      }
+      wave_scan(A, B);
+      Ai[r] = A; Bi[r] = B;
+      RA[r] = readlane_f(A, kWave - 1);
+      RB[r] = readlane_f(B, kWave - 1);
+    }
+    float WA, WB, PA, PB, TA, TB;
+    chain_rows<R>(RA, RB, WA, WB);
+    fused_combine<NW>(WA, WB, s, par, PA, PB, TA, TB);
+    par ^= 1;
+    if (threadIdx.x == 0) s.xc[k] = __builtin_fmaf(TA, xin, TB);  // every thread read xin above
+    float xr = __builtin_fmaf(PA, xin, PB);  // y_k at the step before this wave's first step
+    ent = xr;
+    uint32_t dm = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float x = wave_shift_up(__builtin_fmaf(Ai[r], xr, Bi[r]), xr);
+      const int64_t p = base + r * 256;
+      const float yp[4] = {yf[r], yv[r][0], yv[r][1], yv[r][2]};
+      float o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float Jj = __builtin_fmaf(-wd * z[r][j], z[r][j], wd);
+        x = __builtin_fmaf(Jj, x - yp[j], z[r][j]);
+        o[j] = x;
+        const uint32_t d = as_u32(fabsf(x - yv[r][j]));
+        if (FULL || p + j < T) dm = d > dm ? d : dm;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) yv[r][j] = o[j];
+      xr = __builtin_fmaf(RA[r], xr, RB[r]);
+    }
+    dm = wave_max_u32(dm);
+    if (lane == 0 && dm > s.dmax[k - 1][wid]) s.dmax[k - 1][wid] = dm;
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    st4<FULL, NT>(orow, base + r * 256, T, vec, make_float4(yv[r][0], yv[r][1], yv[r][2], yv[r][3]));
+}
+
+// sets: k_max slot sets of kDeltaSlots words, kDeltaStride apart (redo: unused).
+template <int NW, int R, bool NT>
+__global__ __launch_bounds__(NW* kWave) void k_deer_fused(
+    const float* __restrict__ w, const float* __restrict__ u, const float* __restrict__ y0,
+    const float* __restrict__ h0, float* __restrict__ out, int64_t T, int64_t D, int vec,
+    int k_max, uint32_t* __restrict__ sets, const int* __restrict__ rec, int redo) {
+  constexpr int CH = NW * R * 256;
+  __shared__ FusedShared<NW> s;
+  int m = k_max;
+  if (redo) {
+    m = rec[0];
+    if (m < 1 || m >= k_max) return;  // the pass already holds the answer
+  }
+  const int64_t ch = blockIdx.x;
+  const float wd = w[ch % D];
+  const float x0 = h0 ? h0[ch] : 0.0f;
+  if (threadIdx.x <= (unsigned)m) s.xc[threadIdx.x] = x0;  // every iteration starts from h0
+  for (int i = threadIdx.x; i < kDeerFuseMax * NW; i += NW * kWave) s.dmax[i / NW][i % NW] = 0u;
+  __syncthreads();
+  const float* urow = u + ch * T;
+  const float* y0row = y0 ? y0 + ch * T : nullptr;
+  float* orow = out + ch * T;
+  const int64_t nsub = (T + CH - 1) / CH;
+  float y0last = x0;
+  int par = 0;
+#pragma unroll 1
+  for (int64_t c = 0; c < nsub; ++c) {
+    if (vec && (c + 1) * CH <= T)
+      deer_fused_sub<NW, R, true, NT>(urow, y0row, orow, T, (int)c, vec, m, wd, x0, y0last, par, s);
+    else
+      deer_fused_sub<NW, R, false, NT>(urow, y0row, orow, T, (int)c, vec, m, wd, x0, y0last, par, s);
+  }
+  if (redo) return;
+  __syncthreads();
+  if (threadIdx.x < (unsigned)m) {
+    const int k = threadIdx.x;
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) v = s.dmax[k][i] > v ? s.dmax[k][i] : v;
+    uint32_t* slot = sets + (int64_t)k * (kDeltaSlots * kDeltaStride) +
+                     (blockIdx.x % kDeltaSlots) * kDeltaStride;
+    __hip_atomic_fetch_max(slot, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// After the fused pass (one wave): fold iteration k's slots into out[k], write
+// the solve record as k_deer_finish does, and zero the norms of the
+// iterations past the stop (the record reports only those performed).
+__global__ __launch_bounds__(kWave) void k_deer_fused_finish(const uint32_t* __restrict__ sets,
+                                                             uint32_t* __restrict__ out,
+                                                             int* __restrict__ rec, int k_max,
+                                                             float eps) {
+  const int lane = threadIdx.x;
+  int first = k_max;
+  for (int k = 0; k < k_max; ++k) {
+    const uint32_t v = wave_max_u32(sets[(int64_t)k * (kDeltaSlots * kDeltaStride) +
+                                         lane * kDeltaStride]);
+    if (lane == 0) out[k] = v;
+    if (first == k_max && as_f32(v) < eps) first = k;
+  }
+  if (lane == 0) {
+    const int iters = first < k_max ? first + 1 : k_max;
+    const float d = as_f32(out[iters - 1]);
+    for (int k = iters; k < k_max; ++k) out[k] = 0u;
+    rec[0] = iters;
+    rec[1] = d < eps ? 1 : 0;
+    rec[2] = (d - d != 0.0f) ? 1 : 0;  // NaN or infinite
+  }
+}
+
+// The fused pass wrote k_max iterations into src; leave them in h unless the
+// redo launch already wrote the (earlier) answer there.
+__global__ __launch_bounds__(256) void k_deer_fused_select(const float* __restrict__ src,
+                                                           float* __restrict__ h, int64_t n,
+                                                           const int* __restrict__ rec,
+                                                           int k_max) {
+  if (src == h || rec[0] != k_max) return;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    h[i] = src[i];
+}
+
 // Per-sequence bookkeeping before iteration iter (and once after the last):
 // fold each sequence's slots of iteration iter - 1 into seq_delta[seq][iter - 1]
 // and clear its slots of the set iteration iter + 1 will use.
@@ -1439,6 +1674,51 @@ hipError_t launch_deer_iter(const float* w, const float* u, const float* y, cons
   }
 #undef LRS_DEER
   return hipErrorInvalidValue;
+}
+
+// Fused solve (see k_deer_fused): the pass, the finish, the redo and the select.
+hipError_t launch_deer_fused(const float* w, const float* u, const float* y0, const float* h0,
+                             float* out, float* h, int64_t C, int64_t D, int64_t T,
+                             const RowPlan& p, int vec, int k_max, float eps, uint32_t* sets,
+                             uint32_t* delta_out, int* rec, hipStream_t stream) {
+  const dim3 grid((unsigned)C);
+#define LRS_FUSED_DEER(NTF, OUT, REDO)                                                         \
+  hipLaunchKernelGGL((k_deer_fused<NW, RR, NTF>), grid, dim3(NW * kWave), 0, stream, w, u, y0, h0, \
+                     OUT, T, D, vec, k_max, sets, rec, REDO)
+#define LRS_FUSED_SHAPES(OUT, REDO)                                 \
+  if (p.stream) {                                                   \
+    LRS_SHAPE_CASE(1, 1, LRS_FUSED_DEER(true, OUT, REDO))           \
+    LRS_SHAPE_CASE(2, 1, LRS_FUSED_DEER(true, OUT, REDO))           \
+    LRS_SHAPE_CASE(4, 1, LRS_FUSED_DEER(true, OUT, REDO))           \
+    LRS_SHAPE_CASE(8, 1, LRS_FUSED_DEER(true, OUT, REDO))           \
+    LRS_SHAPE_CASE(8, 2, LRS_FUSED_DEER(true, OUT, REDO))           \
+  } else {                                                          \
+    LRS_SHAPE_CASE(1, 1, LRS_FUSED_DEER(false, OUT, REDO))          \
+    LRS_SHAPE_CASE(2, 1, LRS_FUSED_DEER(false, OUT, REDO))          \
+    LRS_SHAPE_CASE(4, 1, LRS_FUSED_DEER(false, OUT, REDO))          \
+    LRS_SHAPE_CASE(8, 1, LRS_FUSED_DEER(false, OUT, REDO))          \
+    LRS_SHAPE_CASE(8, 2, LRS_FUSED_DEER(false, OUT, REDO))          \
+  }                                                                 \
+  return hipErrorInvalidValue;
+  auto pass = [&]() -> hipError_t { LRS_FUSED_SHAPES(out, 0) };
+  auto redo = [&]() -> hipError_t { LRS_FUSED_SHAPES(h, 1) };
+#undef LRS_FUSED_SHAPES
+#undef LRS_FUSED_DEER
+  hipError_t e = pass();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_deer_fused_finish, dim3(1), dim3(kWave), 0, stream, sets, delta_out, rec,
+                     k_max, eps);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  e = redo();
+  if (e != hipSuccess) return e;
+  if (out != h) {
+    const int64_t n = C * T;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_deer_fused_select, dim3((unsigned)blocks), dim3(256), 0, stream, out, h,
+                       n, rec, k_max);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 hipError_t launch_deer_seq_book(uint32_t* seq_slots, uint32_t* seq_delta, int64_t nseq, int k_max,

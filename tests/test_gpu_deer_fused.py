@@ -1,0 +1,98 @@
+"""The fused DEER solve (all Newton iterations in one walk over each channel,
+used for channels one workgroup walks and K_max <= 8) against the fp64 oracle
+and against the one-launch-per-iteration path (LRS_DEER_FUSE=0) on the same
+inputs: the full B=16 D=512 T=8192 shape, ragged and unaligned lengths,
+h0 given, K_max = 1 and 8, and early stops (a large eps, a warm start near the
+solution, the warm start held in h itself), where the pass's K_max iterations
+are replaced by a recompute with exactly the iterations the stop rule allows."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import linear_recurrence_scan_diagonal_amd as lrs
+from linear_recurrence_scan_diagonal_amd import inputs as I
+from conftest import relerr
+from gpu_util import DEV, log
+
+pytestmark = pytest.mark.gpu
+
+
+def solve(x, B, D, T, eps, k_max, h_init=None, in_place=False):
+    w = torch.from_numpy(x["w"]).to(DEV)
+    u = torch.from_numpy(x["u"].reshape(B, D, T)).to(DEV)
+    h0 = torch.from_numpy(x["h0"].reshape(B, D)).to(DEV)
+    hi = None if h_init is None else torch.from_numpy(h_init.astype(np.float32)).to(DEV)
+    h, info = lrs.deer_solve(w, u, h0, hi, eps=eps, k_max=k_max, out=hi if in_place else None)
+    torch.cuda.synchronize()
+    return h.cpu().numpy(), info
+
+
+def both_paths(monkeypatch, x, B, D, T, eps, k_max, h_init=None, in_place=False):
+    out = {}
+    for mode, flag in (("fused", "1"), ("per-iteration", "0")):
+        monkeypatch.setenv("LRS_DEER_FUSE", flag)
+        out[mode] = solve(x, B, D, T, eps, k_max, h_init, in_place)
+    return out
+
+
+@pytest.mark.parametrize("B,D,T,eps,k_max,h0,warm,in_place", [
+    (16, 512, 8192, 1e-5, 5, False, False, False),   # the DEER workload
+    (2, 5, 8192, 1e-5, 5, True, False, False),       # two sub-chunks, h0
+    (2, 3, 8190, 1e-5, 5, True, False, False),       # partial sub-chunk, T % 4 != 0
+    (1, 7, 6001, 1e-5, 8, True, False, False),       # K_max = 8, odd length
+    (3, 4, 4096, 1e-5, 1, True, False, False),       # K_max = 1 (one sub-chunk)
+    (3, 4, 5000, 1e-5, 1, False, False, False),      # K_max = 1, two sub-chunks
+    (2, 6, 8192, 1e-2, 6, True, False, False),       # early stop: recomputed
+    (2, 6, 7777, 1e-5, 6, True, True, False),        # warm start, early stop
+    (2, 6, 8192, 1e-5, 6, True, True, True),         # warm start held in h, early stop
+    (2, 6, 3000, 1e-5, 3, True, True, True),         # warm start in h, stops at K_max
+    (1, 1, 1, 1e-5, 5, True, False, False),          # one step
+])
+def test_fused_matches_oracle_and_per_iteration(monkeypatch, B, D, T, eps, k_max, h0, warm,
+                                                in_place):
+    w = I.scaled(I.WORKLOADS["deer"], B=B, D=D, T=T, seed=16000 + B * 31 + D * 7 + T + k_max)
+    x = I.deer_inputs(w)
+    if h0:
+        x["h0"] = np.random.default_rng(T).normal(0, 0.5, B * D).astype(np.float32)
+    u = x["u"].reshape(B, D, T)
+    h_init = None
+    if warm:  # near the solution: the sequential loop with u perturbed
+        pert = np.random.default_rng(T + 1).normal(0, 0.02, u.shape)
+        h_init = oracle.rnn_seq(x["w"], u + pert, x["h0"].reshape(B, D)).astype(np.float32)
+    ref_h, ref_it, ref_d = oracle.deer(x["w"], u, x["h0"].reshape(B, D), h_init, eps=eps,
+                                       k_max=k_max)
+    got = both_paths(monkeypatch, x, B, D, T, eps, k_max, h_init, in_place)
+    tag = f"deer fused {B}x{D}x{T} eps={eps} k_max={k_max} h0={h0} warm={warm} in_place={in_place}"
+    (hf, inf_), (hp, inp) = got["fused"], got["per-iteration"]
+    ef, ep, efp = relerr(hf, ref_h), relerr(hp, ref_h), relerr(hf, hp)
+    log(f"{tag}: iters fused {inf_['iters']} per-iteration {inp['iters']} oracle {ref_it}; "
+        f"deltas {inf_['deltas']} vs {list(ref_d)}; relerr fused {ef:.2e} per-iteration {ep:.2e} "
+        f"fused vs per-iteration {efp:.2e}")
+    assert inf_["iters"] == inp["iters"] == ref_it
+    assert inf_["converged"] == inp["converged"]
+    assert ef <= 1e-5 and ep <= 1e-5 and efp <= 1e-5
+    assert len(inf_["deltas"]) == len(inp["deltas"])
+    for df, dp, do in zip(inf_["deltas"], inp["deltas"], ref_d):
+        assert abs(df - do) <= 1e-5 + 1e-3 * do and abs(df - dp) <= 1e-6 + 1e-4 * dp
+
+
+def test_fused_async_and_repeat(monkeypatch):
+    """The asynchronous form gives the same iterate and record, and repeated
+    solves into the same workspace agree bit for bit."""
+    monkeypatch.setenv("LRS_DEER_FUSE", "1")
+    B, D, T = 4, 64, 8192
+    x = I.deer_inputs(I.scaled(I.WORKLOADS["deer"], B=B, D=D, T=T, seed=16500))
+    w = torch.from_numpy(x["w"]).to(DEV)
+    u = torch.from_numpy(x["u"].reshape(B, D, T)).to(DEV)
+    h_sync, info = lrs.deer_solve(w, u)
+    outs = []
+    ws = None
+    for _ in range(3):
+        h, ws = lrs.deer_solve(w, u, workspace=ws, sync=False)
+        outs.append(h)
+    torch.cuda.synchronize()
+    st = lrs.deer_stats(ws, 5)
+    assert st["iters"] == info["iters"] and st["converged"] == info["converged"]
+    for h in outs:
+        assert torch.equal(h, h_sync)
