@@ -45,6 +45,7 @@ BYTES_PER_ELEM = {"scan_fwd_f32": 12, "scan_bwd_f32": 20, "sru_fwd_bf16": 8,
                   "sru_bwd_bf16": 18,       # z_f, z_r, z_x, dL/dh, c in; three gradients out
                   "scan_fused_f32": 24,     # a, b, dL/dh in; h, dL/da, dL/db out
                   "deer_iter_first": 8, "deer_iter": 12,
+                  "deer_fused": 8,          # u in, the last iterate out, all iterations in one pass
                   "deer_bwd_f32": 12,       # h, dL/dh in; dL/du out
                   "sru_deer_iter_first": 8,  # z_f, z_x in; c' out (from c = 0)
                   "sru_deer_iter": 12,       # z_f, z_x, c in; c' out
@@ -52,6 +53,12 @@ BYTES_PER_ELEM = {"scan_fwd_f32": 12, "scan_bwd_f32": 20, "sru_fwd_bf16": 8,
                   "lstm_fwd_save_bf16": 14,  # four pre-activations in; h and c out
                   "lstm_bwd_bf16": 22}       # four pre-activations, dL/dh, c in; four gradients out
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
+
+
+def deer_fused_applies(T: int, k_max: int) -> bool:
+    """The library's rule for the fused DEER solve: channels one workgroup walks
+    (at most 8192 steps), K_max <= 8, not disabled by LRS_DEER_FUSE=0."""
+    return T <= 8192 and k_max <= 8 and os.environ.get("LRS_DEER_FUSE") != "0"
 
 
 def csrc_hash() -> str:
@@ -88,7 +95,7 @@ KERNEL_NAMES = {"scan_fwd_f32": ("k_scan_fwd_bdt", "k_scan_fwd_tbd", "k_scan_fwd
                 "sru_fwd_save_bf16": ("k_sru_fwd<unsigned short",
                                       "k_sru_fwd_persist<unsigned short"),
                 "sru_bwd_bf16": ("k_sru_bwd<unsigned short",),
-                "deer_solve": ("k_deer_iter",),
+                "deer_solve": ("k_deer_fused<", "k_deer_iter"),
                 "sru_deer_bf16": ("k_sru_deer_iter<unsigned short",
                                   "k_sru_deer_iter_persist<unsigned short"),
                 "deer_bwd_f32": ("k_deer_bwd",),
@@ -214,7 +221,12 @@ def summarize(args):
                 continue
             hbm = f_ * factor["FETCH_SIZE"] + w_ * factor["WRITE_SIZE"]
             a = BYTES_PER_ELEM[key] * w.N if key in BYTES_PER_ELEM else None
-            if key in SOLVE_KEYS:
+            if pat == "k_deer_fused<":
+                # one launch per solve (all iterations)
+                a = BYTES_PER_ELEM["deer_fused"] * w.N
+                rec[f"{tag}/{key}"] = {"hbm_bytes_per_launch": round(hbm), "csrc_hash": src_hash,
+                                      "algorithmic_bytes": a}
+            elif key in SOLVE_KEYS:
                 # one launch per Newton iteration: first iteration 8 B/elem, then 12 B/elem
                 n_it = len([r for r in pmc["FETCH_SIZE"] if pat in r["Kernel_Name"]])
                 a = None
@@ -597,7 +609,13 @@ def main():
         extra["deer_deltas"] = info["deltas"]
     else:
         iters = info["iters"]
-        solve_bytes = (BYTES_PER_ELEM["deer_iter_first"] + (iters - 1) * BYTES_PER_ELEM["deer_iter"]) * N
+        if deer_fused_applies(w.T, 5):
+            # one pass over all K_max iterations, and a second one when the stop
+            # rule fired earlier
+            solve_bytes = BYTES_PER_ELEM["deer_fused"] * N * (1 if iters == 5 else 2)
+        else:
+            solve_bytes = (BYTES_PER_ELEM["deer_iter_first"] + (iters - 1) *
+                           BYTES_PER_ELEM["deer_iter"]) * N
         bytes_step = solve_bytes + sum(BYTES_PER_ELEM[k] * N for k in kernels if k != "deer_solve")
         dom, dom_bytes, dom_ms = "deer_solve", solve_bytes, per_kernel["deer_solve"]
         extra["deer_iters"] = iters

@@ -1211,12 +1211,12 @@ __device__ __forceinline__ void deer_fused_sub(const float* __restrict__ urow,
 
 // sets: k_max slot sets of kDeltaSlots words, kDeltaStride apart (redo: unused).
 template <int NW, int R, bool NT>
-__global__ __launch_bounds__(NW* kWave) void k_deer_fused(
+__device__ __forceinline__ void deer_fused_body(
     const float* __restrict__ w, const float* __restrict__ u, const float* __restrict__ y0,
     const float* __restrict__ h0, float* __restrict__ out, int64_t T, int64_t D, int vec,
-    int k_max, uint32_t* __restrict__ sets, const int* __restrict__ rec, int redo) {
+    int k_max, uint32_t* __restrict__ sets, const int* __restrict__ rec, bool redo,
+    FusedShared<NW>& s) {
   constexpr int CH = NW * R * 256;
-  __shared__ FusedShared<NW> s;
   int m = k_max;
   if (redo) {
     m = rec[0];
@@ -1252,6 +1252,27 @@ __global__ __launch_bounds__(NW* kWave) void k_deer_fused(
                      (blockIdx.x % kDeltaSlots) * kDeltaStride;
     __hip_atomic_fetch_max(slot, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+// The pass over all k_max iterations.
+template <int NW, int R, bool NT>
+__global__ __launch_bounds__(NW* kWave) void k_deer_fused(
+    const float* __restrict__ w, const float* __restrict__ u, const float* __restrict__ y0,
+    const float* __restrict__ h0, float* __restrict__ out, int64_t T, int64_t D, int vec,
+    int k_max, uint32_t* __restrict__ sets) {
+  __shared__ FusedShared<NW> s;
+  deer_fused_body<NW, R, NT>(w, u, y0, h0, out, T, D, vec, k_max, sets, nullptr, false, s);
+}
+
+// The recompute with the iteration count the stop rule gave (rec[0]); returns
+// at once when that count is k_max (the pass already holds the answer).
+template <int NW, int R, bool NT>
+__global__ __launch_bounds__(NW* kWave) void k_deer_redo(
+    const float* __restrict__ w, const float* __restrict__ u, const float* __restrict__ y0,
+    const float* __restrict__ h0, float* __restrict__ out, int64_t T, int64_t D, int vec,
+    int k_max, const int* __restrict__ rec) {
+  __shared__ FusedShared<NW> s;
+  deer_fused_body<NW, R, NT>(w, u, y0, h0, out, T, D, vec, k_max, nullptr, rec, true, s);
 }
 
 // After the fused pass (one wave): fold iteration k's slots into out[k], write
@@ -1361,6 +1382,10 @@ constexpr Shape kScanFwdMulti = {8, 4};
 constexpr Shape kScanBwdMulti = {16, 4};
 constexpr Shape kDeerSingle[] = {{1, 1}, {2, 1}, {4, 1}, {8, 1}, {8, 2}};
 constexpr Shape kDeerMulti = {8, 2};
+// sub-chunk shape of the fused solve for channels of more than 2048 steps:
+// measured at B=16 D=512 T=8192 (solve time): 4x4 300 us, 1x4 301, 2x4 302,
+// 2x2 306, 4x2 309-319, 4x1 331, 8x2 342, 8x1 364, 16x1 534
+constexpr Shape kDeerFused = {4, 4};
 // a DEER channel of up to kDeerSub chunks of the largest single shape stays in
 // one workgroup, walked as sequential sub-chunks
 constexpr int kDeerSub = 2;
@@ -1679,12 +1704,24 @@ hipError_t launch_deer_iter(const float* w, const float* u, const float* y, cons
 // Fused solve (see k_deer_fused): the pass, the finish, the redo and the select.
 hipError_t launch_deer_fused(const float* w, const float* u, const float* y0, const float* h0,
                              float* out, float* h, int64_t C, int64_t D, int64_t T,
-                             const RowPlan& p, int vec, int k_max, float eps, uint32_t* sets,
+                             const RowPlan& plan, int vec, int k_max, float eps, uint32_t* sets,
                              uint32_t* delta_out, int* rec, hipStream_t stream) {
   const dim3 grid((unsigned)C);
-#define LRS_FUSED_DEER(NTF, OUT, REDO)                                                         \
-  hipLaunchKernelGGL((k_deer_fused<NW, RR, NTF>), grid, dim3(NW * kWave), 0, stream, w, u, y0, h0, \
-                     OUT, T, D, vec, k_max, sets, rec, REDO)
+  // channels of more than 2048 steps take the fused shape (walking it as
+  // sub-chunks past 4096 steps); shorter ones keep the plan's smallest
+  // covering shape
+  RowPlan p = plan;
+  if (T > 2048) {
+    p.nw = kDeerFused.nw;
+    p.r = kDeerFused.r;
+  }
+#define LRS_FUSED_DEER(NTF, OUT, REDO)                                                       \
+  if (REDO)                                                                                    \
+    hipLaunchKernelGGL((k_deer_redo<NW, RR, NTF>), grid, dim3(NW * kWave), 0, stream, w, u, y0, \
+                       h0, OUT, T, D, vec, k_max, rec);                                        \
+  else                                                                                         \
+    hipLaunchKernelGGL((k_deer_fused<NW, RR, NTF>), grid, dim3(NW * kWave), 0, stream, w, u,   \
+                       y0, h0, OUT, T, D, vec, k_max, sets)
 #define LRS_FUSED_SHAPES(OUT, REDO)                                 \
   if (p.stream) {                                                   \
     LRS_SHAPE_CASE(1, 1, LRS_FUSED_DEER(true, OUT, REDO))           \
@@ -1692,12 +1729,16 @@ hipError_t launch_deer_fused(const float* w, const float* u, const float* y0, co
     LRS_SHAPE_CASE(4, 1, LRS_FUSED_DEER(true, OUT, REDO))           \
     LRS_SHAPE_CASE(8, 1, LRS_FUSED_DEER(true, OUT, REDO))           \
     LRS_SHAPE_CASE(8, 2, LRS_FUSED_DEER(true, OUT, REDO))           \
+    LRS_SHAPE_CASE(4, 4, LRS_FUSED_DEER(true, OUT, REDO))           \
+    LRS_SHAPE_CASE(4, 4, LRS_FUSED_DEER(true, OUT, REDO))          \
   } else {                                                          \
     LRS_SHAPE_CASE(1, 1, LRS_FUSED_DEER(false, OUT, REDO))          \
     LRS_SHAPE_CASE(2, 1, LRS_FUSED_DEER(false, OUT, REDO))          \
     LRS_SHAPE_CASE(4, 1, LRS_FUSED_DEER(false, OUT, REDO))          \
     LRS_SHAPE_CASE(8, 1, LRS_FUSED_DEER(false, OUT, REDO))          \
     LRS_SHAPE_CASE(8, 2, LRS_FUSED_DEER(false, OUT, REDO))          \
+    LRS_SHAPE_CASE(4, 4, LRS_FUSED_DEER(false, OUT, REDO))          \
+    LRS_SHAPE_CASE(4, 4, LRS_FUSED_DEER(false, OUT, REDO))          \
   }                                                                 \
   return hipErrorInvalidValue;
   auto pass = [&]() -> hipError_t { LRS_FUSED_SHAPES(out, 0) };

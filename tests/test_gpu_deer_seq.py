@@ -54,17 +54,23 @@ def test_async_matches_sync():
     assert torch.equal(h1, h2)
 
 
-def test_uniform_sequences_match_global_solve():
+def test_uniform_sequences_match_global_solve(monkeypatch):
     """When every sequence needs the same iterations the result is the global
-    solve's."""
+    solve's: bit for bit against the global solve run one launch per iteration
+    (the same kernel), and within the parity bar against the fused global
+    solve (same iterations, another rounding order at wave edges)."""
     w, u, h0 = make(2, 16, 2048, 11200, [1.0, 1.0])
     wd, ud, h0d = (torch.from_numpy(v).to(DEV) for v in (w, u, h0))
     hs, its, _ = lrs.deer_solve_seq(wd, ud, h0d, k_max=8)
+    hf, info_f = lrs.deer_solve(wd, ud, h0d, k_max=8)
+    monkeypatch.setenv("LRS_DEER_FUSE", "0")
     hg, info = lrs.deer_solve(wd, ud, h0d, k_max=8)
     itg = info["iters"]
     torch.cuda.synchronize()
-    log(f"per-sequence {its}, global {itg}")
+    log(f"per-sequence {its}, global {itg}, fused global {info_f['iters']}")
+    assert info_f["iters"] == itg
     if len(set(its)) == 1 and its[0] == itg:
         assert torch.equal(hs, hg)
+        assert relerr(hf.cpu().numpy(), hs.cpu().numpy()) <= 1e-5
     else:
         assert max(its) == itg
