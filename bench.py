@@ -50,6 +50,7 @@ BYTES_PER_ELEM = {"scan_fwd_f32": 12, "scan_bwd_f32": 20, "sru_fwd_bf16": 8,
                   "sru_deer_iter_first": 8,  # z_f, z_x in; c' out (from c = 0)
                   "sru_deer_iter": 12,       # z_f, z_x, c in; c' out
                   "sru_deer_out": 10,        # z_r, z_x, c in; h out
+                  "sru_deer_fused": 8,       # z_f, z_x in; the last iterate out (all iterations)
                   "lstm_fwd_save_bf16": 14,  # four pre-activations in; h and c out
                   "lstm_bwd_bf16": 22}       # four pre-activations, dL/dh, c in; four gradients out
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
@@ -59,6 +60,20 @@ def deer_fused_applies(T: int, k_max: int) -> bool:
     """The library's rule for the fused DEER solve: channels one workgroup walks
     (at most 8192 steps), K_max <= 8, not disabled by LRS_DEER_FUSE=0."""
     return T <= 8192 and k_max <= 8 and os.environ.get("LRS_DEER_FUSE") != "0"
+
+
+def sru_deer_fused_applies(C: int, k_max: int) -> bool:
+    """The library's rule for the fused SRU-by-DEER walk: the persistent plan
+    (at least one 128-channel block per compute unit; 256 on MI355X, or
+    LRS_PERSIST_MIN_BLOCKS), K_max <= 8, not disabled by LRS_DEER_FUSE=0."""
+    env = os.environ.get("LRS_PERSIST_MIN_BLOCKS")
+    if env and env.lstrip("-").isdigit():
+        min_blocks = int(env)
+    else:
+        import torch
+        min_blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    return ((C + 127) // 128 >= min_blocks and k_max <= 8
+            and os.environ.get("LRS_DEER_FUSE") != "0")
 
 
 def csrc_hash() -> str:
@@ -96,7 +111,7 @@ KERNEL_NAMES = {"scan_fwd_f32": ("k_scan_fwd_bdt", "k_scan_fwd_tbd", "k_scan_fwd
                                       "k_sru_fwd_persist<unsigned short"),
                 "sru_bwd_bf16": ("k_sru_bwd<unsigned short",),
                 "deer_solve": ("k_deer_fused<", "k_deer_iter"),
-                "sru_deer_bf16": ("k_sru_deer_iter<unsigned short",
+                "sru_deer_bf16": ("k_sru_deer_fused<unsigned short", "k_sru_deer_iter<unsigned short",
                                   "k_sru_deer_iter_persist<unsigned short"),
                 "deer_bwd_f32": ("k_deer_bwd",),
                 "lstm_fwd_save_bf16": ("k_lstm_fwd<unsigned short",),
@@ -221,9 +236,9 @@ def summarize(args):
                 continue
             hbm = f_ * factor["FETCH_SIZE"] + w_ * factor["WRITE_SIZE"]
             a = BYTES_PER_ELEM[key] * w.N if key in BYTES_PER_ELEM else None
-            if pat == "k_deer_fused<":
+            if pat in ("k_deer_fused<", "k_sru_deer_fused<unsigned short"):
                 # one launch per solve (all iterations)
-                a = BYTES_PER_ELEM["deer_fused"] * w.N
+                a = BYTES_PER_ELEM["deer_fused" if pat == "k_deer_fused<" else "sru_deer_fused"] * w.N
                 rec[f"{tag}/{key}"] = {"hbm_bytes_per_launch": round(hbm), "csrc_hash": src_hash,
                                       "algorithmic_bytes": a}
             elif key in SOLVE_KEYS:
@@ -602,8 +617,14 @@ def main():
         dom_bytes, dom_ms = BYTES_PER_ELEM[dom] * N, per_kernel[dom]
     elif w.kind == "sru_deer":
         iters = info["iters"]
-        bytes_step = (BYTES_PER_ELEM["sru_deer_iter_first"] + (iters - 1) *
-                      BYTES_PER_ELEM["sru_deer_iter"] + BYTES_PER_ELEM["sru_deer_out"]) * N
+        if sru_deer_fused_applies(w.B * w.D, 5):
+            # one pass over all K_max iterations (a second when the stop rule
+            # fired earlier), then the output kernel
+            bytes_step = (BYTES_PER_ELEM["sru_deer_fused"] * (1 if iters == 5 else 2) +
+                          BYTES_PER_ELEM["sru_deer_out"]) * N
+        else:
+            bytes_step = (BYTES_PER_ELEM["sru_deer_iter_first"] + (iters - 1) *
+                          BYTES_PER_ELEM["sru_deer_iter"] + BYTES_PER_ELEM["sru_deer_out"]) * N
         dom, dom_bytes, dom_ms = "sru_deer_bf16", bytes_step, per_kernel["sru_deer_bf16"]
         extra["deer_iters"] = iters
         extra["deer_deltas"] = info["deltas"]

@@ -865,6 +865,8 @@ size_t lrs_sru_deer_workspace_bytes(int64_t T, int64_t B, int64_t D, int k_max) 
     const size_t b = lookback_bytes(lrs::col_status_words(p), p.ncb);
     need = b > need ? b : need;
   }
+  // norm slot sets of the fused solve (used when the persistent plan applies)
+  if (k_max <= lrs::kDeerFuseMax) need += align_up(deer_fused_set_words(k_max) * 4);
   return kAlign + deer_record_bytes(k_max) + align_up((size_t)N * 4) + need;
 }
 
@@ -933,6 +935,28 @@ int lrs_sru_deer_fwd(const void* z_f, const void* z_r, const void* z_x, const fl
   const int vec = aligned(z_f, rowbytes) && aligned(z_x, rowbytes) &&
                   aligned(c_states, (size_t)p.cpt * 4) && aligned(ybuf, (size_t)p.cpt * 4) &&
                   (!c_init || aligned(c_init, (size_t)p.cpt * 4)) && (C % p.cpt == 0);
+  const int vec4 = (C % 4 == 0) && aligned(z_r, 4 * es) && aligned(z_x, 4 * es) &&
+                   aligned(h, 4 * es) && aligned(c_states, 16);
+
+  if (p.persist && k_max <= lrs::kDeerFuseMax && deer_fuse_enabled()) {
+    // all iterations in one walk (see lrs_deer_solve); the pass must not
+    // overwrite a starting iterate held in c_states: a redo may need it
+    uint32_t* sets = cv.take<uint32_t>((int64_t)deer_fused_set_words(k_max));
+    float* out = (c_init == c_states) ? ybuf : c_states;
+    int rc = hip_status(lrs::launch_reset(nullptr, 0, nullptr, 0, sets,
+                                          (int64_t)deer_fused_set_words(k_max), s));
+    if (rc != LRS_OK) return rc;
+    rc = hip_status(lrs::launch_sru_deer_fused(z_f, z_x, bias_f, v_f, c0, c_init, out, c_states,
+                                               T, C, D, io_dtype, p, vec, k_max, eps, sets,
+                                               r.delta_out, r.rec, s));
+    if (rc != LRS_OK) return rc;
+    rc = hip_status(lrs::launch_sru_deer_out(z_r, z_x, bias_r, c_states, h, c_last, N, C, D,
+                                             io_dtype, vec4, s));
+    if (rc != LRS_OK) return rc;
+    if (!iters_out && !deltas_out && !converged_out) return LRS_OK;  // asynchronous form
+    return read_deer_record(r, k_max, iters_out, deltas_out, converged_out, s);
+  }
+
   int rc = hip_status(lrs::launch_reset(status, nst, tickets, nst > 0 ? p.ncb : 0, r.delta_bits,
                                         lrs::kDeltaSetWords + lrs::kDeerRecordWords + k_max, s));
   if (rc != LRS_OK) return rc;
@@ -951,8 +975,6 @@ int lrs_sru_deer_fwd(const void* z_f, const void* z_r, const void* z_x, const fl
   if (rc != LRS_OK) return rc;
   rc = hip_status(lrs::launch_deer_select(P[0], P[1], c_states, N, r.rec, s));
   if (rc != LRS_OK) return rc;
-  const int vec4 = (C % 4 == 0) && aligned(z_r, 4 * es) && aligned(z_x, 4 * es) &&
-                   aligned(h, 4 * es) && aligned(c_states, 16);
   rc = hip_status(lrs::launch_sru_deer_out(z_r, z_x, bias_r, c_states, h, c_last, N, C, D,
                                            io_dtype, vec4, s));
   if (rc != LRS_OK) return rc;

@@ -119,6 +119,12 @@ hipError_t launch_deer_fused(const float* w, const float* u, const float* y0, co
                              float* out, float* h, int64_t C, int64_t D, int64_t T,
                              const RowPlan& p, int vec, int k_max, float eps, uint32_t* sets,
                              uint32_t* delta_out, int* rec, hipStream_t stream);
+// Pieces shared by the fused solves: the record from the norm sets, and the
+// copy of the pass's result into h unless a redo wrote h.
+hipError_t launch_deer_fused_finish(const uint32_t* sets, uint32_t* delta_out, int* rec,
+                                    int k_max, float eps, hipStream_t stream);
+hipError_t launch_deer_fused_select(const float* src, float* h, int64_t n, const int* rec,
+                                    int k_max, hipStream_t stream);
 hipError_t launch_deer_seq_book(uint32_t* seq_slots, uint32_t* seq_delta, int64_t nseq, int k_max,
                                 int iter, hipStream_t stream);
 hipError_t launch_deer_seq_finish(const uint32_t* seq_delta, int* seq_rec, int64_t nseq,
@@ -178,6 +184,14 @@ hipError_t launch_sru_deer_iter(const void* zf, const void* zx, const float* bia
                                 int vec, uint64_t* status, unsigned* tickets,
                                 uint32_t* delta_bits, uint32_t* delta_out, int iter, float eps,
                                 hipStream_t stream);
+// SRU-by-DEER with the iterations fused into the persistent walk (plan.persist,
+// k_max <= kDeerFuseMax): pass into `out`, finish, redo into c_states, select.
+hipError_t launch_sru_deer_fused(const void* zf, const void* zx, const float* bias_f,
+                                 const float* v_f, const float* c0, const float* c_init,
+                                 float* out, float* c_states, int64_t T, int64_t C, int64_t D,
+                                 int io_dtype, const ColPlan& p, int vec, int k_max, float eps,
+                                 uint32_t* sets, uint32_t* delta_out, int* rec,
+                                 hipStream_t stream);
 hipError_t launch_sru_deer_out(const void* zr, const void* zx, const float* bias_r,
                                const float* c, void* h, float* c_last, int64_t N, int64_t C,
                                int64_t D, int io_dtype, int vec, hipStream_t stream);

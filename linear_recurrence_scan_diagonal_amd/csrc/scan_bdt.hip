@@ -1747,19 +1747,27 @@ hipError_t launch_deer_fused(const float* w, const float* u, const float* y0, co
 #undef LRS_FUSED_DEER
   hipError_t e = pass();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_deer_fused_finish, dim3(1), dim3(kWave), 0, stream, sets, delta_out, rec,
-                     k_max, eps);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_deer_fused_finish(sets, delta_out, rec, k_max, eps, stream)) != hipSuccess)
+    return e;
   e = redo();
   if (e != hipSuccess) return e;
-  if (out != h) {
-    const int64_t n = C * T;
-    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
-    hipLaunchKernelGGL(k_deer_fused_select, dim3((unsigned)blocks), dim3(256), 0, stream, out, h,
-                       n, rec, k_max);
-    e = hipGetLastError();
-  }
-  return e;
+  return launch_deer_fused_select(out, h, C * T, rec, k_max, stream);
+}
+
+hipError_t launch_deer_fused_finish(const uint32_t* sets, uint32_t* delta_out, int* rec,
+                                    int k_max, float eps, hipStream_t stream) {
+  hipLaunchKernelGGL(k_deer_fused_finish, dim3(1), dim3(kWave), 0, stream, sets, delta_out, rec,
+                     k_max, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_deer_fused_select(const float* src, float* h, int64_t n, const int* rec,
+                                    int k_max, hipStream_t stream) {
+  if (src == h) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_deer_fused_select, dim3((unsigned)blocks), dim3(256), 0, stream, src, h, n,
+                     rec, k_max);
+  return hipGetLastError();
 }
 
 hipError_t launch_deer_seq_book(uint32_t* seq_slots, uint32_t* seq_delta, int64_t nseq, int k_max,

@@ -383,6 +383,239 @@ __global__ __launch_bounds__(NW* kWave) void k_sru_deer_iter_persist(
   sru_deer_fold_norm<NW>(dmax, delta_bits, iter, ds);
 }
 
+// ---------------------------------------------------------------------------
+// SRU-by-DEER with the Newton iterations fused into the persistent walk (as
+// k_deer_fused does for the tanh RNN): one workgroup per channel block visits
+// the time tiles in order and, for each tile, loads z_f, z_x and the starting
+// iterate once and computes iterates 1..m, each from the previous one in
+// registers.  Iteration k's per-channel state entering the tile sits in LDS
+// (ck[k]); c_{k-1} at the step before a wave's first row is iteration k-1's
+// state entering that wave (for k = 1: the starting iterate, from memory
+// inside the tile and from ck[0] across tiles).  Same per-step map and norm as
+// sru_deer_persist_tile; only the last iterate is stored.  Pass (sets) and
+// redo (rec) forms as in k_deer_fused.
+// ---------------------------------------------------------------------------
+template <int NW, int CPT>
+struct SdFusedShared {
+  float A[NW][kWave * CPT];
+  float B[NW][kWave * CPT];
+  float ck[kDeerFuseMax + 1][kWave * CPT];
+  uint32_t dm[kDeerFuseMax][NW];
+};
+
+template <typename IO, int NW, int L, int CPT, bool FULL, bool NT>
+__device__ __forceinline__ void sru_deer_fused_tile(
+    const IO* __restrict__ zf, const IO* __restrict__ zx, const float* __restrict__ c0p,
+    const float* __restrict__ y0, float* __restrict__ out, int64_t row0, int64_t T, int64_t C,
+    int64_t cbase, uint32_t off, int nvc, int m, const float (&nbf)[CPT], const float (&vf)[CPT],
+    SdFusedShared<NW, CPT>& s, int wid) {
+  IoRow<IO, CPT> fr[L], xr[L];
+  float y[L][CPT];
+  {
+    const IO* fp = zf + row0 * C + cbase;
+    const IO* xp = zx + row0 * C + cbase;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int nv = (FULL || row0 + i < T) ? nvc : 0;
+      fr[i].template load<FULL, NT>(fp, off, nv);
+      xr[i].template load<FULL, NT>(xp, off, nv);
+      if (y0) {
+        load_row<CPT, FULL, NT>(y0 + (row0 + i) * C + cbase, off, nv, 0.0f, y[i]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) y[i][k] = 0.0f;
+      }
+      fp += C;
+      xp += C;
+    }
+  }
+  // starting iterate at the step before this wave's first row
+  float ent[CPT];
+  if (row0 == 0) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) ent[k] = (c0p && k < nvc) ? c0p[cbase + off + k] : 0.0f;
+  } else if (!y0) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) ent[k] = 0.0f;
+  } else if (wid == 0) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) ent[k] = s.ck[0][off + k];
+  } else if (row0 <= T) {  // inside the tile: not yet overwritten, even in place
+    load_row<CPT, false, false>(y0 + (row0 - 1) * C + cbase, off, nvc, 0.0f, ent);
+  } else {  // a wave wholly past the end (its rows are not stored)
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) ent[k] = 0.0f;
+  }
+#pragma unroll 1
+  for (int lev = 1; lev <= m; ++lev) {
+    float Jv[L][CPT], Bv[L][CPT];
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const bool row_ok = FULL || row0 + i < T;
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        const float prev = (i > 0) ? y[i - 1][k] : ent[k];
+        if (FULL || (row_ok && k < nvc)) {
+          const float xv = xr[i].get(k);
+          const float f = fast_sigmoid(__builtin_fmaf(vf[k], prev, fr[i].get(k)), nbf[k]);
+          const float dx = prev - xv;
+          const float F = __builtin_fmaf(f, dx, xv);
+          const float J = __builtin_fmaf(dx * (f - f * f), vf[k], f);
+          Jv[i][k] = J;
+          Bv[i][k] = __builtin_fmaf(-J, prev, F);
+        } else {  // identity map past the end
+          Jv[i][k] = 1.0f;
+          Bv[i][k] = 0.0f;
+        }
+      }
+    }
+    float A[CPT], B[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      A[k] = Jv[0][k];
+      B[k] = Bv[0][k];
+#pragma unroll
+      for (int i = 1; i < L; ++i) {
+        B[k] = __builtin_fmaf(Jv[i][k], B[k], Bv[i][k]);
+        A[k] = A[k] * Jv[i][k];
+      }
+    }
+    // the earlier waves' maps applied to iteration lev's state entering the tile
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      s.A[wid][off + k] = A[k];
+      s.B[wid][off + k] = B[k];
+    }
+    __syncthreads();
+    float x[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      float PA = 1.0f, PB = 0.0f;
+      for (int w = 0; w < wid; ++w) {
+        PB = __builtin_fmaf(s.A[w][off + k], PB, s.B[w][off + k]);
+        PA = PA * s.A[w][off + k];
+      }
+      x[k] = __builtin_fmaf(PA, s.ck[lev][off + k], PB);
+    }
+    // every wave has read ck[0] (before the barrier above): the last wave now
+    // keeps the starting iterate at the tile's last row for the next tile
+    if (lev == 1 && wid == NW - 1 && y0) {
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) s.ck[0][off + k] = y[L - 1][k];
+    }
+    uint32_t dmax = 0;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) ent[k] = x[k];  // c_lev before this wave's first row
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const bool row_ok = FULL || row0 + i < T;
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        x[k] = __builtin_fmaf(Jv[i][k], x[k], Bv[i][k]);
+        const uint32_t d = as_u32(fabsf(x[k] - y[i][k]));
+        if (FULL || (row_ok && k < nvc)) dmax = d > dmax ? d : dmax;
+        y[i][k] = x[k];
+      }
+    }
+    dmax = wave_max_u32(dmax);
+    if ((threadIdx.x & (kWave - 1)) == 0 && dmax > s.dm[lev - 1][wid]) s.dm[lev - 1][wid] = dmax;
+    __syncthreads();  // every wave has read ck[lev] and this level's maps
+    if (wid == NW - 1) {
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) s.ck[lev][off + k] = x[k];
+    }
+  }
+  float* op = out + row0 * C + cbase;
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    store_row<CPT, FULL, NT>(op, off, (FULL || row0 + i < T) ? nvc : 0, y[i]);
+    op += C;
+  }
+}
+
+template <typename IO, int NW, int L, int CPT, bool NT>
+__device__ __forceinline__ void sru_deer_fused_body(
+    const IO* __restrict__ zf, const IO* __restrict__ zx, const float* __restrict__ bias_f,
+    const float* __restrict__ v_f, const float* __restrict__ c0p, const float* __restrict__ y0,
+    float* __restrict__ out, int64_t T, int64_t C, int64_t D, int vec, int k_max,
+    uint32_t* __restrict__ sets, const int* __restrict__ rec, bool redo,
+    SdFusedShared<NW, CPT>& s) {
+  constexpr int CW = kWave * CPT, TW = NW * L;
+  int m = k_max;
+  if (redo) {
+    m = rec[0];
+    if (m < 1 || m >= k_max) return;  // the pass already holds the answer
+  }
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t cbase = (int64_t)blockIdx.x * CW;
+  const uint32_t off = (uint32_t)(lane * CPT);
+  const int64_t c0i = cbase + off;
+  const int nvc = clamp_valid(C - c0i, CPT);
+  const bool cfull = vec && cbase + CW <= C;
+  float nbf[CPT], vf[CPT];
+  {
+    int64_t d = (nvc > 0) ? c0i % D : 0;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int64_t dk = (k < nvc) ? d : 0;
+      nbf[k] = -kLog2e * bias_f[dk];
+      vf[k] = v_f[dk];
+      d = (d + 1 == D) ? 0 : d + 1;
+    }
+  }
+  for (int j = threadIdx.x; j < (kDeerFuseMax + 1) * CW; j += NW * kWave) {
+    const int c = j % CW;
+    s.ck[j / CW][c] = (c0p && cbase + c < C) ? c0p[cbase + c] : 0.0f;  // every level starts at c0
+  }
+  for (int j = threadIdx.x; j < kDeerFuseMax * NW; j += NW * kWave) s.dm[j / NW][j % NW] = 0u;
+  __syncthreads();
+  const int64_t ntb = (T + TW - 1) / TW, nfull = T / TW;
+  const int64_t w0 = (int64_t)wid * L;
+#pragma unroll 1
+  for (int64_t tb = 0; tb < ntb; ++tb) {
+    if (cfull && tb < nfull)
+      sru_deer_fused_tile<IO, NW, L, CPT, true, NT>(zf, zx, c0p, y0, out, tb * TW + w0, T, C,
+                                                    cbase, off, nvc, m, nbf, vf, s, wid);
+    else
+      sru_deer_fused_tile<IO, NW, L, CPT, false, NT>(zf, zx, c0p, y0, out, tb * TW + w0, T, C,
+                                                     cbase, off, nvc, m, nbf, vf, s, wid);
+  }
+  if (redo) return;
+  __syncthreads();
+  if (threadIdx.x < (unsigned)m) {
+    const int k = threadIdx.x;
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) v = s.dm[k][i] > v ? s.dm[k][i] : v;
+    uint32_t* slot = sets + (int64_t)k * (kDeltaSlots * kDeltaStride) +
+                     (blockIdx.x % kDeltaSlots) * kDeltaStride;
+    __hip_atomic_fetch_max(slot, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <typename IO, int NW, int L, int CPT, bool NT>
+__global__ __launch_bounds__(NW* kWave) void k_sru_deer_fused(
+    const IO* __restrict__ zf, const IO* __restrict__ zx, const float* __restrict__ bias_f,
+    const float* __restrict__ v_f, const float* __restrict__ c0p, const float* __restrict__ y0,
+    float* __restrict__ out, int64_t T, int64_t C, int64_t D, int vec, int k_max,
+    uint32_t* __restrict__ sets) {
+  __shared__ SdFusedShared<NW, CPT> s;
+  sru_deer_fused_body<IO, NW, L, CPT, NT>(zf, zx, bias_f, v_f, c0p, y0, out, T, C, D, vec, k_max,
+                                          sets, nullptr, false, s);
+}
+
+template <typename IO, int NW, int L, int CPT, bool NT>
+__global__ __launch_bounds__(NW* kWave) void k_sru_deer_redo(
+    const IO* __restrict__ zf, const IO* __restrict__ zx, const float* __restrict__ bias_f,
+    const float* __restrict__ v_f, const float* __restrict__ c0p, const float* __restrict__ y0,
+    float* __restrict__ out, int64_t T, int64_t C, int64_t D, int vec, int k_max,
+    const int* __restrict__ rec) {
+  __shared__ SdFusedShared<NW, CPT> s;
+  sru_deer_fused_body<IO, NW, L, CPT, NT>(zf, zx, bias_f, v_f, c0p, y0, out, T, C, D, vec, k_max,
+                                          nullptr, rec, true, s);
+}
+
 // h = r tanh(c) + (1 - r) z_x with r = sigmoid(z_r + b_r), and c_T, from the
 // solved cell states.  Each thread takes groups of 4 consecutive elements
 // (16-byte state loads, 8- or 16-byte I/O loads) when VEC, else single
@@ -513,6 +746,43 @@ hipError_t launch_sru_deer_iter(const void* zf, const void* zx, const float* bia
   }
 #undef LRS_SD
   return hipGetLastError();
+}
+
+// Tile of the fused SRU-by-DEER walk: 8 waves x kSdFL rows x 2 channels.  Solve
+// time at B=32 D=1024 T=2048 (bf16, with the output kernel): 16 rows 442 us,
+// 8 rows 520, 4 rows 682, 2 rows 1036 (199 VGPRs at 16 rows, no spills; one
+// 8-wave workgroup per compute unit needs only 2 waves per SIMD).
+constexpr int kSdFL = 16;
+
+hipError_t launch_sru_deer_fused(const void* zf, const void* zx, const float* bias_f,
+                                 const float* v_f, const float* c0, const float* c_init,
+                                 float* out, float* c_states, int64_t T, int64_t C, int64_t D,
+                                 int io_dtype, const ColPlan& p, int vec, int k_max, float eps,
+                                 uint32_t* sets, uint32_t* delta_out, int* rec,
+                                 hipStream_t stream) {
+  const dim3 grid((unsigned)((C + kWave * kSdPCPT - 1) / (kWave * kSdPCPT)));
+#define LRS_SDF(KER, IO, NTF, OUT, LAST)                                                        \
+  hipLaunchKernelGGL((KER<IO, kSdPNW, kSdFL, kSdPCPT, NTF>), grid, dim3(kSdPNW * kWave), 0,    \
+                     stream, (const IO*)zf, (const IO*)zx, bias_f, v_f, c0, c_init, OUT, T, C, D, \
+                     vec, k_max, LAST)
+#define LRS_SDF_IO(KER, OUT, LAST)                                        \
+  if (io_dtype == 1) {                                                    \
+    if (p.stream) LRS_SDF(KER, uint16_t, true, OUT, LAST);                \
+    else LRS_SDF(KER, uint16_t, false, OUT, LAST);                        \
+  } else {                                                                \
+    if (p.stream) LRS_SDF(KER, float, true, OUT, LAST);                   \
+    else LRS_SDF(KER, float, false, OUT, LAST);                           \
+  }
+  LRS_SDF_IO(k_sru_deer_fused, out, sets)
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = launch_deer_fused_finish(sets, delta_out, rec, k_max, eps, stream)) != hipSuccess)
+    return e;
+  LRS_SDF_IO(k_sru_deer_redo, c_states, (const int*)rec)
+#undef LRS_SDF_IO
+#undef LRS_SDF
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return launch_deer_fused_select(out, c_states, C * T, rec, k_max, stream);
 }
 
 hipError_t launch_sru_deer_out(const void* zr, const void* zx, const float* bias_r,

@@ -96,3 +96,52 @@ def test_fused_async_and_repeat(monkeypatch):
     assert st["iters"] == info["iters"] and st["converged"] == info["converged"]
     for h in outs:
         assert torch.equal(h, h_sync)
+
+
+# SRU whose forget gate reads v_f * c_{t-1}: the fused persistent walk (forced
+# with LRS_PERSIST_MIN_BLOCKS=0) against the oracle and the per-iteration path.
+@pytest.mark.parametrize("B,D,T,io,eps,k_max,warm,in_place", [
+    (2, 64, 1000, "bf16", 1e-5, 5, False, False),
+    (1, 258, 513, "f32", 1e-5, 8, False, False),     # partial channel block, ragged tiles
+    (3, 50, 200, "bf16", 1e-5, 1, False, False),     # K_max = 1
+    (2, 64, 777, "f32", 1e-2, 6, False, False),      # early stop: recomputed
+    (2, 64, 900, "bf16", 1e-5, 6, True, False),      # warm start
+    (2, 64, 900, "f32", 1e-5, 6, True, True),        # warm start held in c_states
+])
+def test_sru_deer_fused_matches_oracle_and_per_iteration(monkeypatch, B, D, T, io, eps, k_max,
+                                                          warm, in_place):
+    from test_gpu_sru_nl import setup
+    monkeypatch.setenv("LRS_PERSIST_MIN_BLOCKS", "0")
+    w = I.scaled(I.WORKLOADS["sru_deer"], B=B, D=D, T=T, seed=16800 + B * 13 + D + T + k_max)
+    z, z64, p, pd = setup(w, io)
+    c0 = np.random.default_rng(T).normal(0, 0.5, (B, D)).astype(np.float32)
+    c_init = None
+    if warm:  # near the solution: the sequential loop on perturbed pre-activations
+        pert = np.random.default_rng(T + 1).normal(0, 0.02, z64["zf"].shape)
+        _, c_seq = oracle.sru_nl_seq(z64["zf"] + pert, z64["zr"], z64["zx"], p["bf"], p["br"],
+                                     p["vf"], c0)
+        c_init = c_seq.astype(np.float32)
+    hr, cr, it, dl = oracle.sru_deer(z64["zf"], z64["zr"], z64["zx"], p["bf"], p["br"], p["vf"],
+                                     c0=c0, c_init=c_init, eps=eps, k_max=k_max)
+    got = {}
+    for mode, flag in (("fused", "1"), ("per-iteration", "0")):
+        monkeypatch.setenv("LRS_DEER_FUSE", flag)
+        ci = None if c_init is None else torch.from_numpy(c_init).to(DEV)
+        h, cs, cl, info = lrs.sru_deer_fwd(z["zf"], z["zr"], z["zx"], pd["bf"], pd["br"],
+                                           pd["vf"], torch.from_numpy(c0).to(DEV), ci, eps=eps,
+                                           k_max=k_max, want_c_last=True,
+                                           c_states=ci if in_place else None)
+        torch.cuda.synchronize()
+        got[mode] = (h.float().cpu().numpy(), cs.cpu().numpy(), cl.cpu().numpy(), info)
+    (hf, cf, clf, inf_), (hp, cp, clp, inp) = got["fused"], got["per-iteration"]
+    e = {"c fused": relerr(cf, cr), "c per-iteration": relerr(cp, cr),
+         "c fused vs per-iteration": relerr(cf, cp), "c_last": relerr(clf, cr[-1]),
+         "h fused": relerr(hf, hr)}
+    log(f"sru-deer fused {io} {B}x{D}x{T} eps={eps} k_max={k_max} warm={warm} in_place={in_place}: "
+        f"iters {inf_['iters']} / {inp['iters']} / oracle {it}; "
+        + ", ".join(f"{k}={v:.2e}" for k, v in e.items()))
+    assert inf_["iters"] == inp["iters"] == it
+    assert inf_["converged"] == inp["converged"]
+    assert e["c fused"] <= 1e-5 and e["c per-iteration"] <= 1e-5
+    assert e["c fused vs per-iteration"] <= 1e-5 and e["c_last"] <= 1e-5
+    assert e["h fused"] <= (2e-2 if io == "bf16" else 1e-5)
