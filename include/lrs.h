@@ -56,6 +56,9 @@
  *    LRS_PERSIST_MIN_BLOCKS (an integer, read at every call) replaces that
  *    count (0 = always, a huge value = never).  Both kernels give the same
  *    results to within fp32 rounding; the workspace size does not change.
+ *    With the persistent plan and k_max <= 8, the SRU-by-DEER solve runs all
+ *    its Newton iterations in that one walk (as lrs_deer_solve does; the same
+ *    LRS_DEER_FUSE=0 switch selects one launch per iteration).
  */
 #ifndef LRS_H
 #define LRS_H
@@ -303,7 +306,15 @@ LRS_API size_t lrs_deer_workspace_bytes(int64_t B, int64_t D, int64_t T, int k_m
  * returns LRS_ERR_NONFINITE, with all outputs written, when the last delta is
  * NaN or infinite.  If all three are NULL the call is asynchronous: it returns
  * LRS_OK once everything is enqueued (and may be captured in a HIP graph);
- * lrs_deer_stats reads the record later. */
+ * lrs_deer_stats reads the record later.
+ * When one workgroup walks each channel (T <= 8192) and k_max <= 8, all
+ * iterations run in one pass over each channel (u read once, the last iterate
+ * written once; the norms of every iteration are kept), and when the stop rule
+ * ends the solve before k_max a second pass recomputes exactly that many
+ * iterations; the record, the iteration count and the result (within fp32
+ * rounding) are those of the one-launch-per-iteration path, which
+ * LRS_DEER_FUSE=0 (read at every call) selects.  Solves that share a
+ * workspace must be ordered. */
 LRS_API int lrs_deer_solve(const float *w, const float *u, const float *h0, const float *h_init, float *h,
                    int64_t B, int64_t D, int64_t T, float eps, int k_max, int *iters_out,
                    float *deltas_out, int *converged_out, void *workspace,
