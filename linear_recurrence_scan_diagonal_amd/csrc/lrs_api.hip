@@ -819,23 +819,31 @@ int lrs_deer_solve_seq(const float* w, const float* u, const float* h0, const fl
                                         (int64_t)((char*)(seq_rec + B * 4) - (char*)seq_slots) / 4,
                                         s));
   if (rc != LRS_OK) return rc;
-  for (int i = 0; i < k_max; ++i) {
-    if (i > 0) {
-      rc = hip_status(lrs::launch_deer_seq_book(seq_slots, seq_delta, B, k_max, i, s));
-      if (rc == LRS_OK && p.nchunk > 1)
-        rc = hip_status(lrs::launch_reset(status, C * p.nchunk, tickets, C, nullptr, 0, s));
+  if (deer_fusable(p, k_max) && deer_fuse_enabled()) {
+    // all iterations in one pass, each sequence's norms folded into seq_delta
+    float* out = (h_init == h) ? ybuf : h;
+    rc = hip_status(lrs::launch_deer_fused(w, u, h_init, h0, out, h, C, D, T, p, vec, k_max, eps,
+                                           nullptr, nullptr, nullptr, s, seq_delta, seq_rec));
+    if (rc != LRS_OK) return rc;
+  } else {
+    for (int i = 0; i < k_max; ++i) {
+      if (i > 0) {
+        rc = hip_status(lrs::launch_deer_seq_book(seq_slots, seq_delta, B, k_max, i, s));
+        if (rc == LRS_OK && p.nchunk > 1)
+          rc = hip_status(lrs::launch_reset(status, C * p.nchunk, tickets, C, nullptr, 0, s));
+        if (rc != LRS_OK) return rc;
+      }
+      const float* y = (i == 0) ? h_init : P[(i - 1) & 1];
+      rc = hip_status(lrs::launch_deer_iter(w, u, y, h0, P[i & 1], C, D, T, p, vec, status, tickets,
+                                            nullptr, nullptr, i, eps, s, seq_slots, seq_delta,
+                                            k_max));
       if (rc != LRS_OK) return rc;
     }
-    const float* y = (i == 0) ? h_init : P[(i - 1) & 1];
-    rc = hip_status(lrs::launch_deer_iter(w, u, y, h0, P[i & 1], C, D, T, p, vec, status, tickets,
-                                          nullptr, nullptr, i, eps, s, seq_slots, seq_delta,
-                                          k_max));
+    rc = hip_status(lrs::launch_deer_seq_book(seq_slots, seq_delta, B, k_max, k_max, s));
+    if (rc == LRS_OK) rc = hip_status(lrs::launch_deer_seq_finish(seq_delta, seq_rec, B, k_max, eps, s));
+    if (rc == LRS_OK) rc = hip_status(lrs::launch_deer_seq_select(P[0], P[1], h, B, D * T, seq_rec, s));
     if (rc != LRS_OK) return rc;
   }
-  rc = hip_status(lrs::launch_deer_seq_book(seq_slots, seq_delta, B, k_max, k_max, s));
-  if (rc == LRS_OK) rc = hip_status(lrs::launch_deer_seq_finish(seq_delta, seq_rec, B, k_max, eps, s));
-  if (rc == LRS_OK) rc = hip_status(lrs::launch_deer_seq_select(P[0], P[1], h, B, D * T, seq_rec, s));
-  if (rc != LRS_OK) return rc;
   if (!iters_out && !converged_out) return LRS_OK;  // asynchronous form
   std::vector<int> rec((size_t)B * 4);
   if (hipMemcpyAsync(rec.data(), seq_rec, sizeof(int) * rec.size(), hipMemcpyDeviceToHost, s) !=

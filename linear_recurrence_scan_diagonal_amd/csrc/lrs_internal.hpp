@@ -113,12 +113,15 @@ hipError_t launch_deer_iter(const float* w, const float* u, const float* y, cons
 // iterations into `out` (h, or a buffer when h holds the starting iterate),
 // the finish kernel writing the record and norms, the redo launch when the stop
 // rule fired earlier, and the copy into h.  `sets` holds k_max slot sets of
-// kDeltaSlots * kDeltaStride words, cleared beforehand.
+// kDeltaSlots * kDeltaStride words, cleared beforehand.  Per-sequence
+// stopping: seq_delta (B * k_max norms, cleared) and seq_rec (4 words per
+// sequence) replace sets, delta_out and rec.
 constexpr int kDeerFuseMax = 8;
 hipError_t launch_deer_fused(const float* w, const float* u, const float* y0, const float* h0,
                              float* out, float* h, int64_t C, int64_t D, int64_t T,
                              const RowPlan& p, int vec, int k_max, float eps, uint32_t* sets,
-                             uint32_t* delta_out, int* rec, hipStream_t stream);
+                             uint32_t* delta_out, int* rec, hipStream_t stream,
+                             uint32_t* seq_delta = nullptr, int* seq_rec = nullptr);
 // Pieces shared by the fused solves: the record from the norm sets, and the
 // copy of the pass's result into h unless a redo wrote h.
 hipError_t launch_deer_fused_finish(const uint32_t* sets, uint32_t* delta_out, int* rec,

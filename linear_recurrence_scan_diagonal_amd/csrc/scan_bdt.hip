@@ -1210,19 +1210,22 @@ __device__ __forceinline__ void deer_fused_sub(const float* __restrict__ urow,
 }
 
 // sets: k_max slot sets of kDeltaSlots words, kDeltaStride apart (redo: unused).
+// Per-sequence stopping (seq != 0): the norms go to seq_delta[b * k_max + k]
+// of the channel's sequence b (batch entry) and the redo reads that
+// sequence's record rec[4 b] (as written by k_deer_seq_finish).
 template <int NW, int R, bool NT>
 __device__ __forceinline__ void deer_fused_body(
     const float* __restrict__ w, const float* __restrict__ u, const float* __restrict__ y0,
     const float* __restrict__ h0, float* __restrict__ out, int64_t T, int64_t D, int vec,
-    int k_max, uint32_t* __restrict__ sets, const int* __restrict__ rec, bool redo,
+    int k_max, uint32_t* __restrict__ sets, const int* __restrict__ rec, bool redo, bool seq,
     FusedShared<NW>& s) {
   constexpr int CH = NW * R * 256;
+  const int64_t ch = blockIdx.x;
   int m = k_max;
   if (redo) {
-    m = rec[0];
+    m = seq ? rec[4 * (ch / D)] : rec[0];
     if (m < 1 || m >= k_max) return;  // the pass already holds the answer
   }
-  const int64_t ch = blockIdx.x;
   const float wd = w[ch % D];
   const float x0 = h0 ? h0[ch] : 0.0f;
   if (threadIdx.x <= (unsigned)m) s.xc[threadIdx.x] = x0;  // every iteration starts from h0
@@ -1248,8 +1251,9 @@ __device__ __forceinline__ void deer_fused_body(
     uint32_t v = 0;
 #pragma unroll
     for (int i = 0; i < NW; ++i) v = s.dmax[k][i] > v ? s.dmax[k][i] : v;
-    uint32_t* slot = sets + (int64_t)k * (kDeltaSlots * kDeltaStride) +
-                     (blockIdx.x % kDeltaSlots) * kDeltaStride;
+    uint32_t* slot = seq ? sets + (ch / D) * k_max + k
+                         : sets + (int64_t)k * (kDeltaSlots * kDeltaStride) +
+                               (blockIdx.x % kDeltaSlots) * kDeltaStride;
     __hip_atomic_fetch_max(slot, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -1259,20 +1263,36 @@ template <int NW, int R, bool NT>
 __global__ __launch_bounds__(NW* kWave) void k_deer_fused(
     const float* __restrict__ w, const float* __restrict__ u, const float* __restrict__ y0,
     const float* __restrict__ h0, float* __restrict__ out, int64_t T, int64_t D, int vec,
-    int k_max, uint32_t* __restrict__ sets) {
+    int k_max, uint32_t* __restrict__ sets, int seq) {
   __shared__ FusedShared<NW> s;
-  deer_fused_body<NW, R, NT>(w, u, y0, h0, out, T, D, vec, k_max, sets, nullptr, false, s);
+  deer_fused_body<NW, R, NT>(w, u, y0, h0, out, T, D, vec, k_max, sets, nullptr, false, seq != 0,
+                             s);
 }
 
-// The recompute with the iteration count the stop rule gave (rec[0]); returns
-// at once when that count is k_max (the pass already holds the answer).
+// The recompute with the iteration count the stop rule gave (rec[0], or the
+// sequence's rec[4 b]); returns at once when that count is k_max (the pass
+// already holds the answer).
 template <int NW, int R, bool NT>
 __global__ __launch_bounds__(NW* kWave) void k_deer_redo(
     const float* __restrict__ w, const float* __restrict__ u, const float* __restrict__ y0,
     const float* __restrict__ h0, float* __restrict__ out, int64_t T, int64_t D, int vec,
-    int k_max, const int* __restrict__ rec) {
+    int k_max, const int* __restrict__ rec, int seq) {
   __shared__ FusedShared<NW> s;
-  deer_fused_body<NW, R, NT>(w, u, y0, h0, out, T, D, vec, k_max, nullptr, rec, true, s);
+  deer_fused_body<NW, R, NT>(w, u, y0, h0, out, T, D, vec, k_max, nullptr, rec, true, seq != 0,
+                             s);
+}
+
+// Per-sequence form of k_deer_fused_select (blockIdx.y = sequence of n floats):
+// copy the pass's result for the sequences that ran to k_max.
+__global__ __launch_bounds__(256) void k_deer_fused_seq_select(const float* __restrict__ src,
+                                                               float* __restrict__ h, int64_t n,
+                                                               const int* __restrict__ seq_rec,
+                                                               int k_max) {
+  const int64_t b = blockIdx.y;
+  if (src == h || seq_rec[4 * b] != k_max) return;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    h[b * n + i] = src[b * n + i];
 }
 
 // After the fused pass (one wave): fold iteration k's slots into out[k], write
@@ -1705,8 +1725,10 @@ hipError_t launch_deer_iter(const float* w, const float* u, const float* y, cons
 hipError_t launch_deer_fused(const float* w, const float* u, const float* y0, const float* h0,
                              float* out, float* h, int64_t C, int64_t D, int64_t T,
                              const RowPlan& plan, int vec, int k_max, float eps, uint32_t* sets,
-                             uint32_t* delta_out, int* rec, hipStream_t stream) {
+                             uint32_t* delta_out, int* rec, hipStream_t stream,
+                             uint32_t* seq_delta, int* seq_rec) {
   const dim3 grid((unsigned)C);
+  if (seq_rec) rec = seq_rec;  // the redo reads the per-sequence records
   // channels of more than 2048 steps take the fused shape (walking it as
   // sub-chunks past 4096 steps); shorter ones keep the plan's smallest
   // covering shape
@@ -1718,10 +1740,11 @@ hipError_t launch_deer_fused(const float* w, const float* u, const float* y0, co
 #define LRS_FUSED_DEER(NTF, OUT, REDO)                                                       \
   if (REDO)                                                                                    \
     hipLaunchKernelGGL((k_deer_redo<NW, RR, NTF>), grid, dim3(NW * kWave), 0, stream, w, u, y0, \
-                       h0, OUT, T, D, vec, k_max, rec);                                        \
+                       h0, OUT, T, D, vec, k_max, rec, seq_rec ? 1 : 0);                       \
   else                                                                                         \
     hipLaunchKernelGGL((k_deer_fused<NW, RR, NTF>), grid, dim3(NW * kWave), 0, stream, w, u,   \
-                       y0, h0, OUT, T, D, vec, k_max, sets)
+                       y0, h0, OUT, T, D, vec, k_max, seq_rec ? seq_delta : sets,              \
+                       seq_rec ? 1 : 0)
 #define LRS_FUSED_SHAPES(OUT, REDO)                                 \
   if (p.stream) {                                                   \
     LRS_SHAPE_CASE(1, 1, LRS_FUSED_DEER(true, OUT, REDO))           \
@@ -1747,6 +1770,18 @@ hipError_t launch_deer_fused(const float* w, const float* u, const float* y0, co
 #undef LRS_FUSED_DEER
   hipError_t e = pass();
   if (e != hipSuccess) return e;
+  if (seq_rec) {  // per-sequence stopping
+    const int64_t nseq = C / D;
+    if ((e = launch_deer_seq_finish(seq_delta, seq_rec, nseq, k_max, eps, stream)) != hipSuccess)
+      return e;
+    e = redo();
+    if (e != hipSuccess || out == h) return e;
+    const int64_t n = D * T;
+    const dim3 sgrid((unsigned)std::min<int64_t>((n + 255) / 256, 1024), (unsigned)nseq);
+    hipLaunchKernelGGL(k_deer_fused_seq_select, sgrid, dim3(256), 0, stream, out, h, n, seq_rec,
+                       k_max);
+    return hipGetLastError();
+  }
   if ((e = launch_deer_fused_finish(sets, delta_out, rec, k_max, eps, stream)) != hipSuccess)
     return e;
   e = redo();

@@ -145,3 +145,53 @@ def test_sru_deer_fused_matches_oracle_and_per_iteration(monkeypatch, B, D, T, i
     assert e["c fused"] <= 1e-5 and e["c per-iteration"] <= 1e-5
     assert e["c fused vs per-iteration"] <= 1e-5 and e["c_last"] <= 1e-5
     assert e["h fused"] <= (2e-2 if io == "bf16" else 1e-5)
+
+
+# Per-sequence stopping (lrs_deer_solve_seq) on the fused pass: sequences that
+# converge at different speeds, so some stop early (recomputed) and some run
+# to K_max; each against the oracle run on that sequence alone and against the
+# one-launch-per-iteration path.
+@pytest.mark.parametrize("B,D,T,warm,in_place", [(4, 3, 100, False, False),
+                                                 (3, 64, 4096, False, False),
+                                                 (2, 40, 8000, True, False),
+                                                 (4, 8, 6000, True, True)])
+def test_per_sequence_fused(monkeypatch, B, D, T, warm, in_place):
+    from test_gpu_deer_seq import make
+    scales = [0.05, 1.0, 3.0, 0.5][:B]
+    w, u, h0 = make(B, D, T, 17000 + T, scales)
+    eps, k_max = 1e-5, 8
+    h_init = None
+    if warm:
+        pert = np.random.default_rng(T).normal(0, 0.02, u.shape)
+        h_init = oracle.rnn_seq(w, u + pert, h0).astype(np.float32)
+    ref = [oracle.deer(w, u[b:b + 1], h0[b:b + 1], None if h_init is None else h_init[b:b + 1],
+                       eps=eps, k_max=k_max) for b in range(B)]
+    got = {}
+    for mode, flag in (("fused", "1"), ("per-iteration", "0")):
+        monkeypatch.setenv("LRS_DEER_FUSE", flag)
+        hi = None if h_init is None else torch.from_numpy(h_init).to(DEV)
+        h, iters, conv = lrs.deer_solve_seq(torch.from_numpy(w).to(DEV),
+                                            torch.from_numpy(u).to(DEV),
+                                            torch.from_numpy(h0).to(DEV), hi, eps=eps,
+                                            k_max=k_max, out=hi if in_place else None)
+        torch.cuda.synchronize()
+        got[mode] = (h.cpu().numpy(), list(iters), list(conv))
+    (hf, itf, cvf), (hp, itp, cvp) = got["fused"], got["per-iteration"]
+    log(f"per-sequence fused {B}x{D}x{T} warm={warm} in_place={in_place}: iters fused {itf} "
+        f"per-iteration {itp} oracle {[r[1] for r in ref]}")
+    assert itf == itp == [r[1] for r in ref]
+    assert cvf == cvp
+    for b in range(B):
+        assert relerr(hf[b:b + 1], ref[b][0]) <= 1e-5
+        assert relerr(hf[b:b + 1], hp[b:b + 1]) <= 1e-5
+
+
+def test_per_sequence_fused_async(monkeypatch):
+    monkeypatch.setenv("LRS_DEER_FUSE", "1")
+    from test_gpu_deer_seq import make
+    w, u, h0 = make(3, 16, 3000, 17500, [0.05, 1.0, 3.0])
+    wd, ud, h0d = (torch.from_numpy(v).to(DEV) for v in (w, u, h0))
+    h_sync, iters, conv = lrs.deer_solve_seq(wd, ud, h0d, k_max=8)
+    h_async, ws = lrs.deer_solve_seq(wd, ud, h0d, k_max=8, sync=False)
+    torch.cuda.synchronize()
+    assert torch.equal(h_sync, h_async)
