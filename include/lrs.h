@@ -332,7 +332,11 @@ LRS_API size_t lrs_deer_seq_workspace_bytes(int64_t B, int64_t D, int64_t T, int
  * ints, each may be NULL) receive the per-sequence iteration counts and
  * convergence flags; with both NULL the call only enqueues work.  Other
  * arguments as for lrs_deer_solve.  B is limited to 65535.  Returns
- * LRS_ERR_NONFINITE when some sequence's last update was NaN or infinite. */
+ * LRS_ERR_NONFINITE when some sequence's last update was NaN or infinite.
+ * Under the same conditions as lrs_deer_solve (T <= 8192, k_max <= 8,
+ * LRS_DEER_FUSE not "0") all iterations run in one pass that keeps each
+ * sequence's norms per iteration; sequences whose stop rule fired before
+ * k_max are recomputed to their own count in a second pass. */
 LRS_API int lrs_deer_solve_seq(const float *w, const float *u, const float *h0,
                                const float *h_init, float *h, int64_t B, int64_t D, int64_t T,
                                float eps, int k_max, int *iters_out, int *converged_out,
