@@ -29,29 +29,31 @@ __device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(
 __device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
 
 // One Hillis-Steele step across lanes: lane i combines with the lane that the
-// DPP control selects (an earlier lane in scan order).  Lanes whose source is
-// outside the selected rows keep the identity (1, 0), via DPP's "old" value.
-// The earlier element is the left operand:
+// DPP control selects (an earlier lane in scan order):
 //   (A_e, B_e) o (A, B) = (A_e*A, A*B_e + B).
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void dpp_combine(float& A, float& B) {
-  const float Ae = as_f32((uint32_t)__builtin_amdgcn_update_dpp(
-      (int)as_u32(1.0f), (int)as_u32(A), CTRL, ROW_MASK, 0xf, false));
-  const float Be = as_f32((uint32_t)__builtin_amdgcn_update_dpp(
-      0, (int)as_u32(B), CTRL, ROW_MASK, 0xf, false));
-  B = __builtin_fmaf(A, Be, B);
-  A = Ae * A;
-}
+// Written as two DPP-modified VALU ops (the earlier lane's value is read
+// through DPP as src0).  With bound control off, a lane whose source lies
+// outside the selected rows, or outside the row mask, is not written and so
+// keeps (A, B): the result of combining with the identity (1, 0).  Each valid
+// lane computes exactly fma(B_e, A, B) and A_e*A.  The leading s_nop gives the
+// two wait states that a DPP read of a VGPR written by the preceding VALU op
+// requires (the compiler does not look inside the asm for that hazard).
+#define LRS_DPP_STEP(CTRL)                                                     \
+  asm("s_nop 1\n\t"                                                          \
+      "v_fmac_f32_dpp %1, %1, %0 " CTRL "\n\t"                               \
+      "v_mul_f32_dpp %0, %0, %0 " CTRL                                        \
+      : "+v"(A), "+v"(B))
 
 // Inclusive scan of (A, B) over the 64 lanes of a wave, lane order = scan order.
 __device__ __forceinline__ void wave_scan(float& A, float& B) {
-  dpp_combine<0x111, 0xf>(A, B);  // row_shr:1
-  dpp_combine<0x112, 0xf>(A, B);  // row_shr:2
-  dpp_combine<0x114, 0xf>(A, B);  // row_shr:4
-  dpp_combine<0x118, 0xf>(A, B);  // row_shr:8
-  dpp_combine<0x142, 0xa>(A, B);  // row_bcast:15 into rows 1 and 3
-  dpp_combine<0x143, 0xc>(A, B);  // row_bcast:31 into rows 2 and 3
+  LRS_DPP_STEP("row_shr:1 row_mask:0xf bank_mask:0xf");
+  LRS_DPP_STEP("row_shr:2 row_mask:0xf bank_mask:0xf");
+  LRS_DPP_STEP("row_shr:4 row_mask:0xf bank_mask:0xf");
+  LRS_DPP_STEP("row_shr:8 row_mask:0xf bank_mask:0xf");
+  LRS_DPP_STEP("row_bcast:15 row_mask:0xa bank_mask:0xf");  // into rows 1 and 3
+  LRS_DPP_STEP("row_bcast:31 row_mask:0xc bank_mask:0xf");  // into rows 2 and 3
 }
+#undef LRS_DPP_STEP
 
 // Value of the previous lane (wave_shr:1); lane 0 receives `lane0`.
 __device__ __forceinline__ float wave_shift_up(float x, float lane0) {
