@@ -62,14 +62,20 @@ __device__ __forceinline__ float wave_shift_up(float x, float lane0) {
 }
 
 // Maximum of a 32-bit unsigned value over the 64 lanes of a wave.
+// Six DPP max steps leave the maximum over the wave in lane 63 (lanes whose
+// source is out of range keep their value, and max is idempotent); it is then
+// broadcast from there.  s_nop: the DPP read-after-VALU-write wait states.
+#define LRS_DPP_MAX(CTRL) asm("s_nop 1\n\tv_max_u32_dpp %0, %0, %0 " CTRL : "+v"(v))
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t o = (uint32_t)__shfl_xor((int)v, off, kWave);
-    v = v > o ? v : o;
-  }
-  return v;
+  LRS_DPP_MAX("row_shr:1 row_mask:0xf bank_mask:0xf");
+  LRS_DPP_MAX("row_shr:2 row_mask:0xf bank_mask:0xf");
+  LRS_DPP_MAX("row_shr:4 row_mask:0xf bank_mask:0xf");
+  LRS_DPP_MAX("row_shr:8 row_mask:0xf bank_mask:0xf");
+  LRS_DPP_MAX("row_bcast:15 row_mask:0xa bank_mask:0xf");
+  LRS_DPP_MAX("row_bcast:31 row_mask:0xc bank_mask:0xf");
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
 }
+#undef LRS_DPP_MAX
 
 // ---------------------------------------------------------------------------
 // Look-back status words.  One 64-bit word per (channel, chunk), written and

@@ -823,10 +823,10 @@ __device__ __forceinline__ float deer_chunk(const float* __restrict__ w, const f
   // y just before the wave's segment (h0 at the start of the sequence)
   const float y_before = (wbeg > 0) ? ((yrow && wbeg - 1 < T) ? yrow[wbeg - 1] : 0.0f) : x0;
 
-  // Only z = tanh(w y_{t-1} + u_t) and the first y_{t-1} of each group are kept
-  // for the output pass, which recomputes J = w (1 - z^2) and uses
-  // y'_t = J (y'_{t-1} - y_{t-1}) + z (the same recurrence with rhs = z - J y_{t-1}).
-  float z[R][4], yf[R], Ai[R], Bi[R], RA[R], RB[R];
+  // J = w (1 - z^2) and rhs = z - J y_{t-1} (z = tanh(w y_{t-1} + u_t)) are
+  // kept for the output pass, which applies y'_t = J y'_{t-1} + rhs in lane
+  // order from the scanned state.
+  float Jv[R][4], rv[R][4], yf[R], Ai[R], Bi[R], RA[R], RB[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const float fy = (r > 0) ? readlane_f(y4[r - 1].w, kWave - 1) : y_before;
@@ -837,9 +837,9 @@ __device__ __forceinline__ float deer_chunk(const float* __restrict__ w, const f
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(ws, yp[j], k2l2e * uv[j]));
-      z[r][j] = __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + e), 1.0f);
-      J[j] = __builtin_fmaf(-wd * z[r][j], z[r][j], wd);  // w (1 - z^2)
-      rh[j] = __builtin_fmaf(-J[j], yp[j], z[r][j]);      // z - J y_{t-1}
+      const float z = __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + e), 1.0f);
+      J[j] = __builtin_fmaf(-wd * z, z, wd);    // w (1 - z^2)
+      rh[j] = __builtin_fmaf(-J[j], yp[j], z);  // z - J y_{t-1}
     }
     if (!FULL) {
       const int64_t p = base + r * 256;
@@ -849,6 +849,8 @@ __device__ __forceinline__ float deer_chunk(const float* __restrict__ w, const f
           if (p + j >= T) { J[j] = 1.0f; rh[j] = 0.0f; }
       }
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { Jv[r][j] = J[j]; rv[r][j] = rh[j]; }
     float A = J[0], B = rh[0];
 #pragma unroll
     for (int j = 1; j < 4; ++j) {
@@ -872,12 +874,10 @@ __device__ __forceinline__ float deer_chunk(const float* __restrict__ w, const f
     float x = wave_shift_up(__builtin_fmaf(Ai[r], xr, Bi[r]), xr);
     const int64_t p = base + r * 256;
     const float yo[4] = {y4[r].x, y4[r].y, y4[r].z, y4[r].w};
-    const float yp[4] = {yf[r], y4[r].x, y4[r].y, y4[r].z};
     float o[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float Jj = __builtin_fmaf(-wd * z[r][j], z[r][j], wd);
-      x = __builtin_fmaf(Jj, x - yp[j], z[r][j]);
+      x = __builtin_fmaf(Jv[r][j], x, rv[r][j]);
       o[j] = x;
       const uint32_t d = as_u32(fabsf(x - yo[j]));
       if (FULL || p + j < T) dmax = d > dmax ? d : dmax;
@@ -1144,7 +1144,7 @@ __device__ __forceinline__ void deer_fused_sub(const float* __restrict__ urow,
 #pragma unroll 1
   for (int k = 1; k <= m; ++k) {
     const float xin = s.xc[k];
-    float z[R][4], yf[R], Ai[R], Bi[R], RA[R], RB[R];
+    float Jv[R][4], rv[R][4], yf[R], Ai[R], Bi[R], RA[R], RB[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float fy = (r > 0) ? readlane_f(yv[r - 1][3], kWave - 1) : ent;
@@ -1154,9 +1154,9 @@ __device__ __forceinline__ void deer_fused_sub(const float* __restrict__ urow,
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(ws, yp[j], k2l2e * uv[r][j]));
-        z[r][j] = __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + e), 1.0f);
-        J[j] = __builtin_fmaf(-wd * z[r][j], z[r][j], wd);  // w (1 - z^2)
-        rh[j] = __builtin_fmaf(-J[j], yp[j], z[r][j]);      // z - J y_{t-1}
+        const float z = __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + e), 1.0f);
+        J[j] = __builtin_fmaf(-wd * z, z, wd);  // w (1 - z^2)
+        rh[j] = __builtin_fmaf(-J[j], yp[j], z);  // z - J y_{t-1}
       }
       if (!FULL) {
         const int64_t p = base + r * 256;
@@ -1164,6 +1164,8 @@ __device__ __forceinline__ void deer_fused_sub(const float* __restrict__ urow,
         for (int j = 0; j < 4; ++j)
           if (p + j >= T) { J[j] = 1.0f; rh[j] = 0.0f; }
       }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { Jv[r][j] = J[j]; rv[r][j] = rh[j]; }
       float A = J[0], B = rh[0];
 #pragma unroll
       for (int j = 1; j < 4; ++j) {
@@ -1187,12 +1189,10 @@ __device__ __forceinline__ void deer_fused_sub(const float* __restrict__ urow,
     for (int r = 0; r < R; ++r) {
       float x = wave_shift_up(__builtin_fmaf(Ai[r], xr, Bi[r]), xr);
       const int64_t p = base + r * 256;
-      const float yp[4] = {yf[r], yv[r][0], yv[r][1], yv[r][2]};
       float o[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float Jj = __builtin_fmaf(-wd * z[r][j], z[r][j], wd);
-        x = __builtin_fmaf(Jj, x - yp[j], z[r][j]);
+        x = __builtin_fmaf(Jv[r][j], x, rv[r][j]);
         o[j] = x;
         const uint32_t d = as_u32(fabsf(x - yv[r][j]));
         if (FULL || p + j < T) dm = d > dm ? d : dm;
