@@ -55,6 +55,18 @@ BYTES_PER_ELEM = {"scan_fwd_f32": 12, "scan_bwd_f32": 20, "sru_fwd_bf16": 8,
                   "lstm_bwd_bf16": 22}       # four pre-activations, dL/dh, c in; four gradients out
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
 
+# The fused DEER solve is bound by vector-ALU issue, not by HBM: its roofline
+# counts the floating-point work of the method's per-element Newton step
+# (y'_t = z_t + J_t (y'_{t-1} - y_{t-1}), z_t = tanh(w y_{t-1} + u_t),
+# J_t = w (1 - z_t^2), and the update norm):
+#   pre-activation fma 2, tanh as exp + add + reciprocal + fma 5, J: mul + fma 3,
+#   the update: sub + fma 3, |y' - y| folded into the max: sub + max 2.
+DEER_FLOPS_PER_ELEM_ITER = 15
+# MI355X published fp32 vector peak (256 CUs x 4 SIMDs x 16 lanes x 2 flops per
+# FMA x 2 for packed fp32, 2.4 GHz); code built without packed fp32 issues at
+# most half of it.
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+
 
 def deer_fused_applies(T: int, k_max: int) -> bool:
     """The library's rule for the fused DEER solve: channels one workgroup walks
@@ -187,6 +199,16 @@ def summarize(args):
         if "lrs::" in r["Name"] or CALIB_NAME in r["Name"]:
             lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
                          f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} |")
+    fused = [r for r in stats if "lrs::k_deer_fused<" in r["Name"]]
+    if fused:
+        from linear_recurrence_scan_diagonal_amd import inputs as I
+        us = float(fused[0]["AverageNs"]) / 1e3
+        n = I.WORKLOADS[wl].N
+        tf = DEER_FLOPS_PER_ELEM_ITER * n * 5 / (us * 1e-6) / 1e12
+        lines += ["", f"ALU view of `k_deer_fused` (vector-ALU bound): {DEER_FLOPS_PER_ELEM_ITER} flops "
+                  f"per element and Newton iteration x {n} elements x 5 iterations / {us:.2f} us = "
+                  f"{tf:.2f} TFLOP/s, {100 * tf / FP32_VECTOR_PEAK_TFLOPS:.1f}% of the "
+                  f"{FP32_VECTOR_PEAK_TFLOPS} TFLOP/s fp32 vector peak."]
     # an entry point that needs look-back state launches the reset kernel
     # first; bench.py's events bracket the whole call
     reset = [r for r in stats if "k_reset" in r["Name"]]
@@ -647,6 +669,16 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes": dom_bytes,
                 "avg_launch_ms": round(dom_ms, 5)}
+    if w.kind == "deer" and deer_fused_applies(w.T, 5):
+        # vector-ALU bound: the method's flops over the iterations it performed
+        flops = DEER_FLOPS_PER_ELEM_ITER * N * iters
+        tflops = flops / (dom_ms / 1e3) / 1e12
+        roofline = {"bound": "alu", "kernel": dom, "achieved": round(tflops, 2),
+                    "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": traffic,
+                    "algorithmic_flops": flops, "algorithmic_bytes": dom_bytes,
+                    "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "avg_launch_ms": round(dom_ms, 5)}
     extra["per_kernel_ms"] = {k: round(v, 5) for k, v in per_kernel.items()}
     extra["step_hbm_frac"] = round(bytes_step / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4)
     cold_ms = sum(cold.values())
