@@ -52,6 +52,9 @@ __device__ __forceinline__ void wave_scan(float& A, float& B) {
   LRS_DPP_STEP("row_shr:8 row_mask:0xf bank_mask:0xf");
   LRS_DPP_STEP("row_bcast:15 row_mask:0xa bank_mask:0xf");  // into rows 1 and 3
   LRS_DPP_STEP("row_bcast:31 row_mask:0xc bank_mask:0xf");  // into rows 2 and 3
+  // The compiler does not count the asm above as a VALU write of A and B, so
+  // a DPP read of them that it places next would miss its wait states.
+  asm("s_nop 1" : "+v"(A), "+v"(B));
 }
 #undef LRS_DPP_STEP
 
@@ -73,6 +76,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   LRS_DPP_MAX("row_shr:8 row_mask:0xf bank_mask:0xf");
   LRS_DPP_MAX("row_bcast:15 row_mask:0xa bank_mask:0xf");
   LRS_DPP_MAX("row_bcast:31 row_mask:0xc bank_mask:0xf");
+  asm("s_nop 1" : "+v"(v));  // wait states for a DPP read of v (see wave_scan)
   return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
 }
 #undef LRS_DPP_MAX

@@ -1107,33 +1107,39 @@ __device__ __forceinline__ void fused_combine(float WA, float WB, FusedShared<NW
   }
 }
 
-// One sub-chunk (index c) of the fused solve: iterations 1..m.  y0last: the
-// starting iterate at the previous sub-chunk's last step (updated for the
-// next one); par: LDS parity of the wave maps (alternates per iteration).
-template <int NW, int R, bool FULL, bool NT>
+// One sub-chunk (index c) of the fused solve: iterations 1..m.  Each lane
+// takes E consecutive steps (4 or 8) of each of the wave's R rows of 64 E
+// steps.  y0last: the starting iterate at the previous sub-chunk's last step
+// (updated for the next one); par: LDS parity of the wave maps (alternates per
+// iteration).
+template <int NW, int R, int E, bool FULL, bool NT>
 __device__ __forceinline__ void deer_fused_sub(const float* __restrict__ urow,
                                                const float* __restrict__ y0row,
                                                float* __restrict__ orow, int64_t T, int c,
                                                int vec, int m, float wd, float x0,
                                                float& y0last, int& par, FusedShared<NW>& s) {
-  constexpr int S = R * 256, CH = NW * S;
+  static_assert(E == 4 || E == 8, "4 or 8 steps per lane");
+  constexpr int RS = kWave * E, S = R * RS, CH = NW * S;
   constexpr float k2l2e = 2.0f * 1.4426950408889634f;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  const int64_t base = (int64_t)c * CH + (int64_t)wid * S + 4 * lane;
+  const int64_t base = (int64_t)c * CH + (int64_t)wid * S + E * lane;
   const float ws = wd * k2l2e;
-  float uv[R][4], yv[R][4];
+  float uv[R][E], yv[R][E];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const float4 u4 = ld4<FULL, NT>(urow, base + r * 256, T, vec, 0.0f);
-    const float4 y4 = y0row ? ld4<FULL, NT>(y0row, base + r * 256, T, vec, 0.0f)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
-    uv[r][0] = u4.x; uv[r][1] = u4.y; uv[r][2] = u4.z; uv[r][3] = u4.w;
-    yv[r][0] = y4.x; yv[r][1] = y4.y; yv[r][2] = y4.z; yv[r][3] = y4.w;
+#pragma unroll
+    for (int q = 0; q < E; q += 4) {
+      const float4 u4 = ld4<FULL, NT>(urow, base + r * RS + q, T, vec, 0.0f);
+      const float4 y4 = y0row ? ld4<FULL, NT>(y0row, base + r * RS + q, T, vec, 0.0f)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+      uv[r][q] = u4.x; uv[r][q + 1] = u4.y; uv[r][q + 2] = u4.z; uv[r][q + 3] = u4.w;
+      yv[r][q] = y4.x; yv[r][q + 1] = y4.y; yv[r][q + 2] = y4.z; yv[r][q + 3] = y4.w;
+    }
   }
   // starting iterate at the step before this wave's first step
   float ent;
   if (y0row) {
-    if (lane == kWave - 1) s.y0w[wid] = yv[R - 1][3];
+    if (lane == kWave - 1) s.y0w[wid] = yv[R - 1][E - 1];
     __syncthreads();
     ent = wid > 0 ? s.y0w[wid - 1] : (c == 0 ? x0 : y0last);
     y0last = s.y0w[NW - 1];  // read before any later write: the next writes follow a barrier
@@ -1144,33 +1150,31 @@ __device__ __forceinline__ void deer_fused_sub(const float* __restrict__ urow,
 #pragma unroll 1
   for (int k = 1; k <= m; ++k) {
     const float xin = s.xc[k];
-    float Jv[R][4], rv[R][4], yf[R], Ai[R], Bi[R], RA[R], RB[R];
+    // J = w (1 - z^2) and rhs = z - J y_{t-1} per step, kept for the output pass
+    float Jv[R][E], rv[R][E], Ai[R], Bi[R], RA[R], RB[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float fy = (r > 0) ? readlane_f(yv[r - 1][3], kWave - 1) : ent;
-      yf[r] = wave_shift_up(yv[r][3], fy);
-      const float yp[4] = {yf[r], yv[r][0], yv[r][1], yv[r][2]};
-      float J[4], rh[4];
+      const float fy = (r > 0) ? readlane_f(yv[r - 1][E - 1], kWave - 1) : ent;
+      const float yf = wave_shift_up(yv[r][E - 1], fy);  // y_{t-1} at the lane's first step
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(ws, yp[j], k2l2e * uv[r][j]));
+      for (int j = 0; j < E; ++j) {
+        const float yp = j == 0 ? yf : yv[r][j - 1];
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(ws, yp, k2l2e * uv[r][j]));
         const float z = __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + e), 1.0f);
-        J[j] = __builtin_fmaf(-wd * z, z, wd);  // w (1 - z^2)
-        rh[j] = __builtin_fmaf(-J[j], yp[j], z);  // z - J y_{t-1}
+        Jv[r][j] = __builtin_fmaf(-wd * z, z, wd);    // w (1 - z^2)
+        rv[r][j] = __builtin_fmaf(-Jv[r][j], yp, z);  // z - J y_{t-1}
       }
       if (!FULL) {
-        const int64_t p = base + r * 256;
+        const int64_t p = base + r * RS;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (p + j >= T) { J[j] = 1.0f; rh[j] = 0.0f; }
+        for (int j = 0; j < E; ++j)
+          if (p + j >= T) { Jv[r][j] = 1.0f; rv[r][j] = 0.0f; }
       }
+      float A = Jv[r][0], B = rv[r][0];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) { Jv[r][j] = J[j]; rv[r][j] = rh[j]; }
-      float A = J[0], B = rh[0];
-#pragma unroll
-      for (int j = 1; j < 4; ++j) {
-        B = __builtin_fmaf(J[j], B, rh[j]);
-        A = A * J[j];
+      for (int j = 1; j < E; ++j) {
+        B = __builtin_fmaf(Jv[r][j], B, rv[r][j]);
+        A = A * Jv[r][j];
       }
       wave_scan(A, B);
       Ai[r] = A; Bi[r] = B;
@@ -1188,17 +1192,14 @@ __device__ __forceinline__ void deer_fused_sub(const float* __restrict__ urow,
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float x = wave_shift_up(__builtin_fmaf(Ai[r], xr, Bi[r]), xr);
-      const int64_t p = base + r * 256;
-      float o[4];
+      const int64_t p = base + r * RS;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < E; ++j) {
         x = __builtin_fmaf(Jv[r][j], x, rv[r][j]);
-        o[j] = x;
         const uint32_t d = as_u32(fabsf(x - yv[r][j]));
         if (FULL || p + j < T) dm = d > dm ? d : dm;
+        yv[r][j] = x;
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) yv[r][j] = o[j];
       xr = __builtin_fmaf(RA[r], xr, RB[r]);
     }
     dm = wave_max_u32(dm);
@@ -1206,20 +1207,23 @@ __device__ __forceinline__ void deer_fused_sub(const float* __restrict__ urow,
   }
 #pragma unroll
   for (int r = 0; r < R; ++r)
-    st4<FULL, NT>(orow, base + r * 256, T, vec, make_float4(yv[r][0], yv[r][1], yv[r][2], yv[r][3]));
+#pragma unroll
+    for (int q = 0; q < E; q += 4)
+      st4<FULL, NT>(orow, base + r * RS + q, T, vec,
+                    make_float4(yv[r][q], yv[r][q + 1], yv[r][q + 2], yv[r][q + 3]));
 }
 
 // sets: k_max slot sets of kDeltaSlots words, kDeltaStride apart (redo: unused).
 // Per-sequence stopping (seq != 0): the norms go to seq_delta[b * k_max + k]
 // of the channel's sequence b (batch entry) and the redo reads that
 // sequence's record rec[4 b] (as written by k_deer_seq_finish).
-template <int NW, int R, bool NT>
+template <int NW, int R, int E, bool NT>
 __device__ __forceinline__ void deer_fused_body(
     const float* __restrict__ w, const float* __restrict__ u, const float* __restrict__ y0,
     const float* __restrict__ h0, float* __restrict__ out, int64_t T, int64_t D, int vec,
     int k_max, uint32_t* __restrict__ sets, const int* __restrict__ rec, bool redo, bool seq,
     FusedShared<NW>& s) {
-  constexpr int CH = NW * R * 256;
+  constexpr int CH = NW * R * kWave * E;
   const int64_t ch = blockIdx.x;
   int m = k_max;
   if (redo) {
@@ -1240,9 +1244,11 @@ __device__ __forceinline__ void deer_fused_body(
 #pragma unroll 1
   for (int64_t c = 0; c < nsub; ++c) {
     if (vec && (c + 1) * CH <= T)
-      deer_fused_sub<NW, R, true, NT>(urow, y0row, orow, T, (int)c, vec, m, wd, x0, y0last, par, s);
+      deer_fused_sub<NW, R, E, true, NT>(urow, y0row, orow, T, (int)c, vec, m, wd, x0, y0last, par,
+                                         s);
     else
-      deer_fused_sub<NW, R, false, NT>(urow, y0row, orow, T, (int)c, vec, m, wd, x0, y0last, par, s);
+      deer_fused_sub<NW, R, E, false, NT>(urow, y0row, orow, T, (int)c, vec, m, wd, x0, y0last,
+                                          par, s);
   }
   if (redo) return;
   __syncthreads();
@@ -1259,27 +1265,27 @@ __device__ __forceinline__ void deer_fused_body(
 }
 
 // The pass over all k_max iterations.
-template <int NW, int R, bool NT>
+template <int NW, int R, int E, bool NT>
 __global__ __launch_bounds__(NW* kWave) void k_deer_fused(
     const float* __restrict__ w, const float* __restrict__ u, const float* __restrict__ y0,
     const float* __restrict__ h0, float* __restrict__ out, int64_t T, int64_t D, int vec,
     int k_max, uint32_t* __restrict__ sets, int seq) {
   __shared__ FusedShared<NW> s;
-  deer_fused_body<NW, R, NT>(w, u, y0, h0, out, T, D, vec, k_max, sets, nullptr, false, seq != 0,
-                             s);
+  deer_fused_body<NW, R, E, NT>(w, u, y0, h0, out, T, D, vec, k_max, sets, nullptr, false,
+                                seq != 0, s);
 }
 
 // The recompute with the iteration count the stop rule gave (rec[0], or the
 // sequence's rec[4 b]); returns at once when that count is k_max (the pass
 // already holds the answer).
-template <int NW, int R, bool NT>
+template <int NW, int R, int E, bool NT>
 __global__ __launch_bounds__(NW* kWave) void k_deer_redo(
     const float* __restrict__ w, const float* __restrict__ u, const float* __restrict__ y0,
     const float* __restrict__ h0, float* __restrict__ out, int64_t T, int64_t D, int vec,
     int k_max, const int* __restrict__ rec, int seq) {
   __shared__ FusedShared<NW> s;
-  deer_fused_body<NW, R, NT>(w, u, y0, h0, out, T, D, vec, k_max, nullptr, rec, true, seq != 0,
-                             s);
+  deer_fused_body<NW, R, E, NT>(w, u, y0, h0, out, T, D, vec, k_max, nullptr, rec, true,
+                                seq != 0, s);
 }
 
 // Per-sequence form of k_deer_fused_select (blockIdx.y = sequence of n floats):
@@ -1402,10 +1408,14 @@ constexpr Shape kScanFwdMulti = {8, 4};
 constexpr Shape kScanBwdMulti = {16, 4};
 constexpr Shape kDeerSingle[] = {{1, 1}, {2, 1}, {4, 1}, {8, 1}, {8, 2}};
 constexpr Shape kDeerMulti = {8, 2};
-// sub-chunk shape of the fused solve for channels of more than 2048 steps:
-// measured at B=16 D=512 T=8192 (solve time): 4x4 300 us, 1x4 301, 2x4 302,
-// 2x2 306, 4x2 309-319, 4x1 331, 8x2 342, 8x1 364, 16x1 534
-constexpr Shape kDeerFused = {4, 4};
+// sub-chunk shape of the fused solve for channels of more than 2048 steps
+// (waves x rows).  With 4 steps per lane, measured at B=16 D=512 T=8192
+// (solve time): 4x4 300 us, 1x4 301, 2x4 302, 2x2 306, 4x2 309-319, 4x1 331,
+// 8x2 342, 8x1 364, 16x1 534.  The pass is bound by VALU issue; 8 steps per
+// lane on 4x2 (the same 4096-step sub-chunk) halves the wave-scan work per
+// step: 309 instead of 355 VALU per wave and iteration, 0.23 instead of
+// 0.25 ms per solve.
+constexpr Shape kDeerFused = {4, 2};  // with 8 steps per lane
 // a DEER channel of up to kDeerSub chunks of the largest single shape stays in
 // one workgroup, walked as sequential sub-chunks
 constexpr int kDeerSub = 2;
@@ -1729,44 +1739,48 @@ hipError_t launch_deer_fused(const float* w, const float* u, const float* y0, co
                              uint32_t* seq_delta, int* seq_rec) {
   const dim3 grid((unsigned)C);
   if (seq_rec) rec = seq_rec;  // the redo reads the per-sequence records
-  // channels of more than 2048 steps take the fused shape (walking it as
-  // sub-chunks past 4096 steps); shorter ones keep the plan's smallest
-  // covering shape
+  // channels of more than 2048 steps take the fused shape (4 waves of 2 rows
+  // of 8 steps per lane, walking the channel as 4096-step sub-chunks);
+  // shorter ones keep the plan's smallest covering shape with 4 steps per lane
   RowPlan p = plan;
-  if (T > 2048) {
-    p.nw = kDeerFused.nw;
-    p.r = kDeerFused.r;
-  }
-#define LRS_FUSED_DEER(NTF, OUT, REDO)                                                       \
-  if (REDO)                                                                                    \
-    hipLaunchKernelGGL((k_deer_redo<NW, RR, NTF>), grid, dim3(NW * kWave), 0, stream, w, u, y0, \
-                       h0, OUT, T, D, vec, k_max, rec, seq_rec ? 1 : 0);                       \
-  else                                                                                         \
-    hipLaunchKernelGGL((k_deer_fused<NW, RR, NTF>), grid, dim3(NW * kWave), 0, stream, w, u,   \
-                       y0, h0, OUT, T, D, vec, k_max, seq_rec ? seq_delta : sets,              \
+  const bool wide = T > 2048;
+#define LRS_FUSED_DEER(E, NTF, OUT, REDO)                                                         \
+  if (REDO)                                                                                        \
+    hipLaunchKernelGGL((k_deer_redo<NW, RR, E, NTF>), grid, dim3(NW * kWave), 0, stream, w, u, y0, \
+                       h0, OUT, T, D, vec, k_max, rec, seq_rec ? 1 : 0);                           \
+  else                                                                                             \
+    hipLaunchKernelGGL((k_deer_fused<NW, RR, E, NTF>), grid, dim3(NW * kWave), 0, stream, w, u,   \
+                       y0, h0, OUT, T, D, vec, k_max, seq_rec ? seq_delta : sets,                  \
                        seq_rec ? 1 : 0)
+#define LRS_FUSED_WIDE(NTF, OUT, REDO)                                             \
+  {                                                                                \
+    constexpr int NW = kDeerFused.nw, RR = kDeerFused.r;                           \
+    LRS_FUSED_DEER(8, NTF, OUT, REDO);                                             \
+    return hipGetLastError();                                                      \
+  }
 #define LRS_FUSED_SHAPES(OUT, REDO)                                 \
   if (p.stream) {                                                   \
-    LRS_SHAPE_CASE(1, 1, LRS_FUSED_DEER(true, OUT, REDO))           \
-    LRS_SHAPE_CASE(2, 1, LRS_FUSED_DEER(true, OUT, REDO))           \
-    LRS_SHAPE_CASE(4, 1, LRS_FUSED_DEER(true, OUT, REDO))           \
-    LRS_SHAPE_CASE(8, 1, LRS_FUSED_DEER(true, OUT, REDO))           \
-    LRS_SHAPE_CASE(8, 2, LRS_FUSED_DEER(true, OUT, REDO))           \
-    LRS_SHAPE_CASE(4, 4, LRS_FUSED_DEER(true, OUT, REDO))           \
-    LRS_SHAPE_CASE(4, 4, LRS_FUSED_DEER(true, OUT, REDO))          \
+    if (wide) LRS_FUSED_WIDE(true, OUT, REDO)                       \
+    LRS_SHAPE_CASE(1, 1, LRS_FUSED_DEER(4, true, OUT, REDO))        \
+    LRS_SHAPE_CASE(2, 1, LRS_FUSED_DEER(4, true, OUT, REDO))        \
+    LRS_SHAPE_CASE(4, 1, LRS_FUSED_DEER(4, true, OUT, REDO))        \
+    LRS_SHAPE_CASE(8, 1, LRS_FUSED_DEER(4, true, OUT, REDO))        \
+    LRS_SHAPE_CASE(8, 2, LRS_FUSED_DEER(4, true, OUT, REDO))        \
+    LRS_SHAPE_CASE(4, 4, LRS_FUSED_DEER(4, true, OUT, REDO))        \
   } else {                                                          \
-    LRS_SHAPE_CASE(1, 1, LRS_FUSED_DEER(false, OUT, REDO))          \
-    LRS_SHAPE_CASE(2, 1, LRS_FUSED_DEER(false, OUT, REDO))          \
-    LRS_SHAPE_CASE(4, 1, LRS_FUSED_DEER(false, OUT, REDO))          \
-    LRS_SHAPE_CASE(8, 1, LRS_FUSED_DEER(false, OUT, REDO))          \
-    LRS_SHAPE_CASE(8, 2, LRS_FUSED_DEER(false, OUT, REDO))          \
-    LRS_SHAPE_CASE(4, 4, LRS_FUSED_DEER(false, OUT, REDO))          \
-    LRS_SHAPE_CASE(4, 4, LRS_FUSED_DEER(false, OUT, REDO))          \
+    if (wide) LRS_FUSED_WIDE(false, OUT, REDO)                      \
+    LRS_SHAPE_CASE(1, 1, LRS_FUSED_DEER(4, false, OUT, REDO))       \
+    LRS_SHAPE_CASE(2, 1, LRS_FUSED_DEER(4, false, OUT, REDO))       \
+    LRS_SHAPE_CASE(4, 1, LRS_FUSED_DEER(4, false, OUT, REDO))       \
+    LRS_SHAPE_CASE(8, 1, LRS_FUSED_DEER(4, false, OUT, REDO))       \
+    LRS_SHAPE_CASE(8, 2, LRS_FUSED_DEER(4, false, OUT, REDO))       \
+    LRS_SHAPE_CASE(4, 4, LRS_FUSED_DEER(4, false, OUT, REDO))       \
   }                                                                 \
   return hipErrorInvalidValue;
   auto pass = [&]() -> hipError_t { LRS_FUSED_SHAPES(out, 0) };
   auto redo = [&]() -> hipError_t { LRS_FUSED_SHAPES(h, 1) };
 #undef LRS_FUSED_SHAPES
+#undef LRS_FUSED_WIDE
 #undef LRS_FUSED_DEER
   hipError_t e = pass();
   if (e != hipSuccess) return e;
