@@ -48,6 +48,9 @@ def both_paths(monkeypatch, x, B, D, T, eps, k_max, h_init=None, in_place=False)
     (2, 6, 8192, 1e-5, 6, True, True, True),         # warm start held in h, early stop
     (2, 6, 3000, 1e-5, 3, True, True, True),         # warm start in h, stops at K_max
     (1, 1, 1, 1e-5, 5, True, False, False),          # one step
+    (2, 3, 2048, 1e-5, 5, True, False, False),       # longest channel of 4 steps per lane
+    (2, 3, 2049, 1e-5, 5, True, True, False),        # first of 8 steps per lane, partial
+    (2, 3, 4097, 1e-5, 5, True, False, False),       # second sub-chunk of one step
 ])
 def test_fused_matches_oracle_and_per_iteration(monkeypatch, B, D, T, eps, k_max, h0, warm,
                                                 in_place):
