@@ -44,7 +44,8 @@ __device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(
       "v_mul_f32_dpp %0, %0, %0 " CTRL                                        \
       : "+v"(A), "+v"(B))
 
-// Inclusive scan of (A, B) over the 64 lanes of a wave, lane order = scan order.
+// Inclusive scan of (A, B) over the 64 lanes of a wave, lane order = scan order
+// (called with all 64 lanes active).
 __device__ __forceinline__ void wave_scan(float& A, float& B) {
   LRS_DPP_STEP("row_shr:1 row_mask:0xf bank_mask:0xf");
   LRS_DPP_STEP("row_shr:2 row_mask:0xf bank_mask:0xf");
@@ -65,6 +66,7 @@ __device__ __forceinline__ float wave_shift_up(float x, float lane0) {
 }
 
 // Maximum of a 32-bit unsigned value over the 64 lanes of a wave.
+// Called with all 64 lanes active.
 // Six DPP max steps leave the maximum over the wave in lane 63 (lanes whose
 // source is out of range keep their value, and max is idempotent); it is then
 // broadcast from there.  s_nop: the DPP read-after-VALU-write wait states.
