@@ -313,6 +313,22 @@ constexpr float kLog2e = 1.4426950408889634f;
 template <typename IO, int CPT>
 struct IoRow;
 
+// One channel per lane: a single bf16, widened on use.
+template <>
+struct IoRow<uint16_t, 1> {
+  uint32_t w;
+  template <bool FULL, bool NT>
+  __device__ __forceinline__ void load(const uint16_t* p, uint32_t off, int nv) {
+    w = (FULL || nv > 0) ? (uint32_t)p[off] : 0u;
+  }
+  __device__ __forceinline__ float get(int) const { return bf16_lo(w); }
+  template <bool FULL, bool NT>
+  static __device__ __forceinline__ void store(uint16_t* p, uint32_t off, int nv,
+                                               const float (&x)[1]) {
+    if (FULL || nv > 0) p[off] = (uint16_t)(pack_bf16x2(x[0], 0.0f) & 0xFFFFu);
+  }
+};
+
 template <int CPT>
 struct IoRow<uint16_t, CPT> {
   uint32_t w[CPT / 2];

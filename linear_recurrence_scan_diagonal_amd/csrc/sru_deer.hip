@@ -748,11 +748,14 @@ hipError_t launch_sru_deer_iter(const void* zf, const void* zx, const float* bia
   return hipGetLastError();
 }
 
-// Tile of the fused SRU-by-DEER walk: 8 waves x kSdFL rows x 2 channels.  Solve
-// time at B=32 D=1024 T=2048 (bf16, with the output kernel): 16 rows 442 us,
-// 8 rows 520, 4 rows 682, 2 rows 1036 (199 VGPRs at 16 rows, no spills; one
-// 8-wave workgroup per compute unit needs only 2 waves per SIMD).
-constexpr int kSdFL = 16;
+// Tile of the fused SRU-by-DEER walk: 8 waves x kSdFL rows x kSdFCPT channels
+// per lane, one workgroup per block of 64 kSdFCPT channels walking all of T.
+// Solve time at B=32 D=1024 T=2048 (bf16, with the output kernel), 2 channels
+// per lane: 16 rows 442 us, 8 rows 520, 4 rows 682, 2 rows 1036 (192-199 VGPRs
+// at 16 rows; 256 workgroups of 8 waves leave 2 waves per SIMD, VALU busy
+// 64%).  One channel per lane: 102 VGPRs, 512 workgroups, 4 waves per SIMD,
+// 396 instead of 435 us.
+constexpr int kSdFL = 16, kSdFCPT = 1;
 
 hipError_t launch_sru_deer_fused(const void* zf, const void* zx, const float* bias_f,
                                  const float* v_f, const float* c0, const float* c_init,
@@ -760,9 +763,9 @@ hipError_t launch_sru_deer_fused(const void* zf, const void* zx, const float* bi
                                  int io_dtype, const ColPlan& p, int vec, int k_max, float eps,
                                  uint32_t* sets, uint32_t* delta_out, int* rec,
                                  hipStream_t stream) {
-  const dim3 grid((unsigned)((C + kWave * kSdPCPT - 1) / (kWave * kSdPCPT)));
+  const dim3 grid((unsigned)((C + kWave * kSdFCPT - 1) / (kWave * kSdFCPT)));
 #define LRS_SDF(KER, IO, NTF, OUT, LAST)                                                        \
-  hipLaunchKernelGGL((KER<IO, kSdPNW, kSdFL, kSdPCPT, NTF>), grid, dim3(kSdPNW * kWave), 0,    \
+  hipLaunchKernelGGL((KER<IO, kSdPNW, kSdFL, kSdFCPT, NTF>), grid, dim3(kSdPNW * kWave), 0,    \
                      stream, (const IO*)zf, (const IO*)zx, bias_f, v_f, c0, c_init, OUT, T, C, D, \
                      vec, k_max, LAST)
 #define LRS_SDF_IO(KER, OUT, LAST)                                        \
