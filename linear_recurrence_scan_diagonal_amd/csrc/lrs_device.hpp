@@ -110,147 +110,109 @@ __device__ __forceinline__ uint64_t status_load(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Single-lane look-back: returns the state entering chunk `c`, given the status
-// words of chunks 0..c-1 of one channel (st points at chunk 0, consecutive
-// chunks `stride` words apart).  Walks back over aggregates until it meets an
-// inclusive state.  Chunk indices come from a per-channel ticket, so every
-// predecessor is resident or finished and the spin terminates.
+// Carry rule.  The chunks of a channel are taken G at a time ("groups").
+// With g0 = c - c % G the first chunk of chunk c's group, the state entering
+// chunk c is
+//     x_in(c) = M_{c-1}( ... M_{g0}( x_end(g0 - 1) ) ... )
+// where M_k is chunk k's aggregate map and x_end(g0 - 1) the state at the end
+// of the previous group (the channel's initial state for the first group).
+// Every chunk except the last one of a group publishes its aggregate as soon
+// as it has it; the last chunk of a group publishes nothing but its inclusive
+// state, once its own x_in is known.  Every reader therefore combines the
+// same words in the same order, whatever had been published when it looked:
+// the association order, and so every rounding, is fixed by the launch shape
+// alone and results are bitwise reproducible from run to run.  A reader waits
+// for at most G words (the G-1 aggregates before it in its group and one
+// inclusive state).  Chunk indices come from a per-channel ticket, so every
+// chunk waited on is resident or finished and the wait terminates.
 //
-// Safety net: a predecessor publishes its aggregate within microseconds of
-// starting, so a wait of kSpinLimit polls (~0.1 s) can only mean corrupted
-// status words; the carry then becomes NaN, which poisons the outputs of this
-// channel instead of hanging the device.
+// Safety net: a predecessor publishes within microseconds of starting, so a
+// wait of kSpinLimit polls (~0.1 s) can only mean corrupted status words; the
+// carry then becomes NaN, which poisons the outputs of this channel instead
+// of hanging the device.
 constexpr uint32_t kSpinLimit = 1u << 22;
 
-__device__ __forceinline__ float lookback_carry(const uint64_t* st, int c, int64_t stride) {
-  float accA = 1.0f, accB = 0.0f;  // composition of chunks p+1 .. c-1
-  int p = c - 1;
-  uint32_t spins = 0;
-  while (true) {
-    const uint64_t v = status_load(st + (int64_t)p * stride);
-    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-    if (v == kStatusEmpty) {
-      if (++spins > kSpinLimit) return __builtin_nanf("");
-      __builtin_amdgcn_s_sleep(1);
-      continue;
-    }
-    if (lo == kIncTag) return __builtin_fmaf(accA, as_f32(hi), accB);
-    // the aggregate of chunk p precedes the chunks accumulated so far
-    accB = __builtin_fmaf(accA, as_f32(hi), accB);
-    accA = accA * as_f32(lo);
-    --p;
-  }
-}
+__device__ __forceinline__ bool group_end(int c, int G) { return c % G == G - 1; }
 
-// Wave-wide look-back, run by all 64 lanes of one wave: lane j inspects the
-// status of chunk p - j, so one poll covers 64 predecessors.  Aggregates of
-// the nearest predecessors are folded in order (nearest first) until an
-// inclusive state is found; if the nearest unfolded predecessor has published
-// nothing yet, the wave sleeps and polls again.  Returns the state entering
-// chunk c (uniform across the wave).
-__device__ __forceinline__ float lookback_carry_wave(const uint64_t* st, int c, int64_t stride) {
+// Wave-wide form, run by all 64 lanes of one wave, groups of 64 chunks: lane
+// l < j loads the aggregate of chunk g0 + l, lane 63 the inclusive state at
+// the end of the previous group; a poll re-loads only the words still
+// unpublished.  The aggregates are composed by the wave scan (identity maps
+// in the unused lanes, which leave every value unchanged) and the composite
+// of the first j applied to the previous group's end state.  st points at
+// chunk 0 of the channel, consecutive chunks `stride` words apart; x0 is the
+// channel's initial state.  Returns x_in(c), uniform across the wave.
+constexpr int kWaveGroup = kWave;
+__device__ __forceinline__ float lookback_group_wave(const uint64_t* st, int c, int64_t stride,
+                                                     float x0) {
   const int lane = threadIdx.x & (kWave - 1);
-  float accA = 1.0f, accB = 0.0f;  // composition of the chunks already folded
-  int p = c - 1;                   // nearest predecessor not yet folded
+  const int g0 = c - c % kWaveGroup;
+  const int j = c - g0;  // 0 .. 63 aggregates to compose
+  int idx = -1;
+  if (lane < j) idx = g0 + lane;
+  else if (lane == kWave - 1 && g0 > 0) idx = g0 - 1;
+  uint64_t v = kStatusEmpty;
   uint32_t spins = 0;
   while (true) {
-    const int idx = p - lane;
-    const uint64_t v = (idx >= 0) ? status_load(st + (int64_t)idx * stride) : kStatusEmpty;
-    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-    const uint64_t inc = __ballot(v != kStatusEmpty && lo == kIncTag);
-    const uint64_t emp = __ballot(v == kStatusEmpty);
-    const int first_inc = inc ? (int)__builtin_ctzll(inc) : kWave;
-    const int first_emp = emp ? (int)__builtin_ctzll(emp) : kWave;
-    const int n = first_inc < first_emp ? first_inc : first_emp;  // lanes 0..n-1: aggregates
-    for (int j = 0; j < n; ++j) {
-      const float A = as_f32((uint32_t)__builtin_amdgcn_readlane((int)lo, j));
-      const float B = as_f32((uint32_t)__builtin_amdgcn_readlane((int)hi, j));
-      accB = __builtin_fmaf(accA, B, accB);
-      accA = accA * A;
-    }
-    if (first_inc < first_emp)
-      return __builtin_fmaf(accA, as_f32((uint32_t)__builtin_amdgcn_readlane((int)hi, n)), accB);
-    p -= n;
-    if (n == 0) {
-      if (++spins > kSpinLimit) return __builtin_nanf("");
-      __builtin_amdgcn_s_sleep(1);
-    }
+    if (idx >= 0 && v == kStatusEmpty) v = status_load(st + (int64_t)idx * stride);
+    if (__ballot(idx >= 0 && v == kStatusEmpty) == 0) break;
+    if (++spins > kSpinLimit) return __builtin_nanf("");
+    __builtin_amdgcn_s_sleep(1);
   }
+  float xs = x0;
+  if (g0 > 0) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, kWave - 1);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), kWave - 1);
+    xs = (lo == kIncTag) ? as_f32(hi) : __builtin_nanf("");
+  }
+  if (j == 0) return xs;
+  float A = 1.0f, B = 0.0f;
+  if (lane < j) {
+    A = as_f32((uint32_t)v);
+    B = as_f32((uint32_t)(v >> 32));
+  }
+  wave_scan(A, B);
+  const float PA = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(A), j - 1));
+  const float PB = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(B), j - 1));
+  return __builtin_fmaf(PA, xs, PB);
 }
 
-// Look-back for the CPT channels of one lane together.  Channel k's status
-// words for blocks 0, 1, ... are st[k], st[k + stride], ...  Each poll loads
-// the W nearest unfolded predecessors of every unresolved channel at once, so
-// the usual case (nearest predecessor has its aggregate, the one before it is
-// inclusive) costs a single round trip.  `seen[k][i]` is an earlier snapshot
-// of block c-1-i (kStatusEmpty where none was taken) and serves as the first
-// poll; a snapshot is always safe to use, since a published word never
-// changes except from aggregate to inclusive.  Writes the state entering
-// block c of channels k < nv into carry[k]; NaN after kSpinLimit polls that
-// found a channel's nearest unfolded predecessor unpublished.
-template <int CPT, int W>
-__device__ __forceinline__ void lookback_cols(const uint64_t* st, int64_t stride, int c, int nv,
-                                              const uint64_t (&seen)[CPT][W],
-                                              float (&carry)[CPT]) {
-  float accA[CPT], accB[CPT];
-  int p[CPT];
-  bool done[CPT];
-  uint64_t v[CPT][W];
+// Lane-parallel form for the feature-contiguous kernels: each lane resolves
+// one channel of its own, groups of G blocks.  The lane loads every word it
+// needs at once (v[i], i < j: aggregate of block g0 + i; v[G-1]: inclusive
+// state of block g0 - 1), re-polls only the missing ones, then applies the
+// aggregates in ascending block order to the previous group's end state.
+// st points at block 0 of the lane's channel, consecutive blocks `stride`
+// words apart; x0 is the channel's initial state.
+template <int G>
+__device__ __forceinline__ float lookback_group_lane(const uint64_t* st, int64_t stride, int c,
+                                                     float x0) {
+  const int g0 = c - c % G;
+  const int j = c - g0;
+  if (j == 0 && g0 == 0) return x0;
+  uint64_t v[G];
 #pragma unroll
-  for (int k = 0; k < CPT; ++k) {
-    accA[k] = 1.0f;
-    accB[k] = 0.0f;
-    p[k] = c - 1;
-    done[k] = k >= nv;
-#pragma unroll
-    for (int i = 0; i < W; ++i) v[k][i] = seen[k][i];
-  }
+  for (int i = 0; i < G; ++i) v[i] = kStatusEmpty;
   uint32_t spins = 0;
   while (true) {
-    bool pending = false, stalled = false;
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      bool stop = done[k];
+    for (int i = 0; i < G - 1; ++i)
+      if (i < j && v[i] == kStatusEmpty) v[i] = status_load(st + (int64_t)(g0 + i) * stride);
+    if (g0 > 0 && v[G - 1] == kStatusEmpty) v[G - 1] = status_load(st + (int64_t)(g0 - 1) * stride);
+    bool missing = g0 > 0 && v[G - 1] == kStatusEmpty;
 #pragma unroll
-      for (int i = 0; i < W; ++i) {
-        if (stop) continue;
-        const uint64_t s = v[k][i];
-        const uint32_t lo = (uint32_t)s, hi = (uint32_t)(s >> 32);
-        if (s == kStatusEmpty) {
-          stop = true;
-          stalled |= (i == 0);
-        } else if (lo == kIncTag) {
-          carry[k] = __builtin_fmaf(accA[k], as_f32(hi), accB[k]);
-          done[k] = true;
-          stop = true;
-        } else {  // aggregate of block p[k], which precedes those folded so far
-          accB[k] = __builtin_fmaf(accA[k], as_f32(hi), accB[k]);
-          accA[k] = accA[k] * as_f32(lo);
-          --p[k];
-        }
-      }
-      pending |= !done[k];
-    }
-    if (!pending) return;
-    if (stalled) {
-      if (++spins > kSpinLimit) {
-#pragma unroll
-        for (int k = 0; k < CPT; ++k)
-          if (!done[k]) carry[k] = __builtin_nanf("");
-        return;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-    // block 0 is always published inclusive, so a walk never passes it
-#pragma unroll
-    for (int k = 0; k < CPT; ++k)
-#pragma unroll
-      for (int i = 0; i < W; ++i) {
-        const int idx = p[k] - i;
-        v[k][i] = (!done[k] && idx >= 0) ? status_load(st + (int64_t)idx * stride + k)
-                                         : kStatusEmpty;
-      }
+    for (int i = 0; i < G - 1; ++i) missing |= (i < j && v[i] == kStatusEmpty);
+    if (!missing) break;
+    if (++spins > kSpinLimit) return __builtin_nanf("");
+    __builtin_amdgcn_s_sleep(1);
   }
+  float x = x0;
+  if (g0 > 0)
+    x = ((uint32_t)v[G - 1] == kIncTag) ? as_f32((uint32_t)(v[G - 1] >> 32)) : __builtin_nanf("");
+#pragma unroll
+  for (int i = 0; i < G - 1; ++i)
+    if (i < j) x = __builtin_fmaf(as_f32((uint32_t)v[i]), x, as_f32((uint32_t)(v[i] >> 32)));
+  return x;
 }
 
 __device__ __forceinline__ unsigned take_ticket(unsigned* counter) {

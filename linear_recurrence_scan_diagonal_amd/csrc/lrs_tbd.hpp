@@ -144,8 +144,9 @@ __device__ __forceinline__ void store_row_bf16(uint16_t* __restrict__ p, uint32_
 
 // ---- block-level pieces ----------------------------------------------------
 
-// Look-back window: predecessors polled per channel at once.
-constexpr int kColWindow = 2;
+// Look-back group (time blocks) of the feature-contiguous kernels: a block
+// reads at most this many status words per channel.
+constexpr int kColGroup = 8;
 
 // Per channel, the state entering this wave's first step.  Each wave publishes
 // its per-channel maps in LDS; the last CPT waves compose them into the block's
@@ -185,21 +186,11 @@ __device__ __forceinline__ void col_enter_state(const float (&A)[CPT], const flo
       }
       float x_in = 0.0f;
       if (j < cvalid) {
-        if (tb > 0) {
-          status_store(st + (int64_t)tb * CW + j, pack_agg(TA, TB));
-          uint64_t seen[1][kColWindow];
-#pragma unroll
-          for (int i = 0; i < kColWindow; ++i) {
-            const int idx = tb - 1 - i;
-            seen[0][i] = idx >= 0 ? status_load(st + (int64_t)idx * CW + j) : kStatusEmpty;
-          }
-          float xr[1];
-          lookback_cols<1, kColWindow>(st + j, CW, tb, 1, seen, xr);
-          x_in = xr[0];
-        } else if (x0p) {
-          x_in = x0p[cbase + j];
-        }
-        status_store(st + (int64_t)tb * CW + j, pack_inc(__builtin_fmaf(TA, x_in, TB)));
+        const bool gend = group_end(tb, kColGroup);
+        if (!gend) status_store(st + (int64_t)tb * CW + j, pack_agg(TA, TB));
+        const float xs = x0p ? x0p[cbase + j] : 0.0f;
+        x_in = lookback_group_lane<kColGroup>(st + j, CW, tb, xs);
+        if (gend) status_store(st + (int64_t)tb * CW + j, pack_inc(__builtin_fmaf(TA, x_in, TB)));
       }
       s.carry[j] = x_in;
     }

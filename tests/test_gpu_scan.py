@@ -129,44 +129,12 @@ def test_exact_integer_inputs_bitwise(layout):
     assert np.array_equal(got["da"], ref["da"].astype(np.float32))
 
 
-def test_scan_long_workload():
-    """Million-step channels: every channel crosses 256 look-back chunks.
-    Compared on sampled channels (full rows) against the oracle."""
-    w = I.WORKLOADS["scan_long"]
-    log(f"scan_long B={w.B} D={w.D} T={w.T}: generating inputs")
-    x = I.scan_inputs(w)
-    B, D, T = w.B, w.D, w.T
-    log("scan_long: running on GPU")
-    a = to_dev(x["a"], B, D, T, "bdt")
-    b = to_dev(x["b"], B, D, T, "bdt")
-    g = to_dev(x["g"], B, D, T, "bdt")
-    h = lrs.scan_fwd(a, b, None)
-    da, db, dh0 = lrs.scan_bwd(a, h, g, None)
-    torch.cuda.synchronize()
-    sample = [0, 1, 2, 255, 256, 300, 510, 511]
-    sx = {k: x[k][sample] for k in ("a", "b", "g")}
-    sx["h0"] = x["h0"][sample]
-    ref = oracle_scan(sx, h0=False)
-    got = {"h": h.view(-1, T)[sample].cpu().numpy(), "da": da.view(-1, T)[sample].cpu().numpy(),
-           "db": db.view(-1, T)[sample].cpu().numpy(),
-           "dh0": dh0.view(-1)[sample].cpu().numpy()}
-    compare(got, ref, tag="scan_long")
-    # whole-array invariants: finite everywhere, and the adjoint identity
-    # <g, h> = <lam, b> per channel (h0 = 0) on every channel, in float64
-    assert torch.isfinite(h).all() and torch.isfinite(da).all() and torch.isfinite(db).all()
-    lhs = (g.double() * h.double()).sum(-1).view(-1)
-    rhs = (db.double() * b.double()).sum(-1).view(-1)
-    rel = ((lhs - rhs).abs() / (1 + lhs.abs())).max().item()
-    log(f"scan_long adjoint identity rel {rel:.2e}")
-    assert rel < 1e-3
-
-
 @pytest.mark.parametrize("layout", ["bdt", "tbd"])
 def test_streamed(layout):
     """Calls whose arrays total 512 MiB or more take the nontemporal (streaming)
-    variants: 16384 channels of 4096 steps, 256 MiB per array.  Sampled
-    channels are compared with the oracle; the adjoint identity is checked on
-    all of them."""
+    variants: 16384 channels of 4096 steps, 256 MiB per array.  Every channel
+    is compared with the oracle (on the device, against the uploaded fp64
+    reference); the adjoint identity is checked on all of them too."""
     B, D, T = 16, 1024, 4096
     w = I.scaled(I.WORKLOADS["scan_fwd_bwd"], B=B, D=D, T=T, seed=8202)
     log(f"streamed {layout} B={B} D={D} T={T}: generating inputs")
@@ -182,12 +150,15 @@ def test_streamed(layout):
 
     def rows(t):  # [C, T] view of a device array in either layout
         return t.view(C, T) if layout == "bdt" else t.view(T, C).t()
-    sample = [0, 1, 77, 4095, 4096, 9000, C - 2, C - 1]
-    sx = {k: x[k][sample] for k in ("a", "b", "g", "h0")}
-    ref = oracle_scan(sx)
-    got = {"h": rows(h)[sample].cpu().numpy(), "da": rows(da)[sample].cpu().numpy(),
-           "db": rows(db)[sample].cpu().numpy(), "dh0": dh0.view(-1)[sample].cpu().numpy()}
-    compare(got, ref, tag=f"streamed/{layout}")
+    log(f"streamed {layout}: oracle over all {C} channels")
+    ref = oracle_scan(x)
+    errs = {}
+    for k, t in (("h", rows(h)), ("da", rows(da)), ("db", rows(db)), ("dh0", dh0.view(-1))):
+        r = torch.from_numpy(ref[k]).to(DEV)
+        errs[k] = ((t.double() - r).abs() / (1.0 + r.abs())).max().item()
+    log(f"streamed/{layout} errors: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= TOL, f"streamed/{layout}: {k} relerr {v:.3e} > {TOL}"
     # <g, h> = <lam, b> + dh0 * h0 per channel
     lhs = (rows(g).double() * rows(h).double()).sum(-1)
     rhs = (rows(db).double() * rows(b).double()).sum(-1) + (dh0.double() * h0.double()).view(-1)
@@ -198,13 +169,16 @@ def test_streamed(layout):
 
 def test_layouts_agree_and_repeat():
     """The two layouts give the same results within the bar, and repeated runs
-    of the multi-chunk path stay within the bar of each other."""
+    of the multi-chunk path give the same bits (the carry between chunks is
+    combined in a fixed order)."""
     B, D, T = 2, 64, 20000
     w = I.scaled(I.WORKLOADS["scan_fwd_bwd"], B=B, D=D, T=T, seed=9090)
     x = I.scan_inputs(w)
     r1 = run_scan(x, B, D, T, "bdt")
     r2 = run_scan(x, B, D, T, "tbd")
     r3 = run_scan(x, B, D, T, "bdt")
+    r4 = run_scan(x, B, D, T, "tbd")
     for k in r1:
         assert relerr(r2[k], r1[k]) <= 2 * TOL
-        assert relerr(r3[k], r1[k]) <= 2 * TOL
+        assert np.array_equal(r3[k], r1[k]), k
+        assert np.array_equal(r4[k], r2[k]), k
