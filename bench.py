@@ -1,11 +1,13 @@
 #!/usr/bin/env python3
 """Benchmark of the diagonal linear-recurrence scan on one MI355X.
 
-Default workload (the headline metric): forward + backward fp32 scan,
-B=8, D=512, T=4096, [B,D,T] layout.  One step = lrs_scan_fwd then
-lrs_scan_bwd over the same resident inputs.  Other workloads (--workload):
-scan_fused (the same step as one lrs_scan_fwd_bwd call), scan_short (T = 32,
-sequential kernels), scan_long (T = 2^20),
+Default workload (the headline metric): the very long forward + backward
+fp32 scan, B=2, D=256, T=2^20, [B,D,T] layout (the largest forward+backward
+fp32 configuration); one step = lrs_scan_fwd then lrs_scan_bwd over the same
+resident inputs.  The same run also measures scan_fwd_bwd (B=8, D=512,
+T=4096) and reports it inside the line under "also".  Other workloads
+(--workload): scan_fwd_bwd, scan_fused (that step as one lrs_scan_fwd_bwd
+call), scan_short (T = 32, sequential kernels),
 sru_fwd / sru_fwd_bwd (bf16 SRU layer), sru_deer (SRU with v_f*c_{t-1}
 by DEER), lstm_fwd_bwd
 (bf16 LSTM cell-state layer with input-only gates), deer / deer_fwd_bwd
@@ -69,23 +71,18 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3
 
 
 def deer_fused_applies(T: int, k_max: int) -> bool:
-    """The library's rule for the fused DEER solve: channels one workgroup walks
-    (at most 8192 steps), K_max <= 8, not disabled by LRS_DEER_FUSE=0."""
-    return T <= 8192 and k_max <= 8 and os.environ.get("LRS_DEER_FUSE") != "0"
+    """The library's default rule for the fused DEER solve: channels one
+    workgroup walks (at most 8192 steps) and K_max <= 8."""
+    return T <= 8192 and k_max <= 8
 
 
 def sru_deer_fused_applies(C: int, k_max: int) -> bool:
-    """The library's rule for the fused SRU-by-DEER walk: the persistent plan
-    (at least one 128-channel block per compute unit; 256 on MI355X, or
-    LRS_PERSIST_MIN_BLOCKS), K_max <= 8, not disabled by LRS_DEER_FUSE=0."""
-    env = os.environ.get("LRS_PERSIST_MIN_BLOCKS")
-    if env and env.lstrip("-").isdigit():
-        min_blocks = int(env)
-    else:
-        import torch
-        min_blocks = torch.cuda.get_device_properties(0).multi_processor_count
-    return ((C + 127) // 128 >= min_blocks and k_max <= 8
-            and os.environ.get("LRS_DEER_FUSE") != "0")
+    """The library's default rule for the fused SRU-by-DEER walk: the
+    persistent plan (at least one 128-channel block per compute unit, 256 on
+    MI355X) and K_max <= 8."""
+    import torch
+    min_blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    return (C + 127) // 128 >= min_blocks and k_max <= 8
 
 
 def csrc_hash() -> str:
@@ -291,11 +288,15 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="scan_fwd_bwd",
+    p.add_argument("--workload", default="scan_long",
                    choices=["scan_fwd_bwd", "scan_fused", "scan_short", "scan_long", "sru_fwd",
                             "sru_deer", "sru_fwd_bwd", "lstm_fwd_bwd",
                             "deer", "deer_fwd_bwd", "scan_fwd_small"])
     p.add_argument("--layout", default="bdt", choices=["bdt", "tbd"])
+    p.add_argument("--also", default=None,
+                   help="comma-separated workloads also measured in the same run and reported "
+                        "inside the line under 'also' (default: scan_fwd_bwd when the workload "
+                        "is scan_long, else none; 'none' disables)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", action="store_true",
                    help="also time the step captured as a HIP graph and replayed")
@@ -428,6 +429,32 @@ def main():
     if args.crossover:
         crossover(args, np, torch, lrs, I, dev)
         return
+    line, w = measure(args, np, torch, lrs, I, dev)
+    also = args.also
+    if also is None:
+        also = "scan_fwd_bwd" if args.workload == "scan_long" else "none"
+    extra_lines = {}
+    for name in [x for x in also.split(",") if x and x != "none"]:
+        torch.cuda.empty_cache()
+        sub = argparse.Namespace(**vars(args))
+        sub.workload, sub.layout, sub.graph, sub.no_stream_ref = name, "bdt", False, True
+        sl, _ = measure(sub, np, torch, lrs, I, dev)
+        extra_lines[name] = {k: sl[k] for k in ("value", "unit", "ms_per_step", "config",
+                                                "roofline", "per_kernel_ms", "step_hbm_frac",
+                                                "cold") if k in sl}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args, np, I)
+    line["cpu_baseline"] = cpu
+    if extra_lines:
+        line["also"] = extra_lines
+    line["csrc_hash"] = csrc_hash()
+    print(json.dumps(line), flush=True)
+
+
+def measure(args, np, torch, lrs, I, dev):
+    """Time one workload (args.workload, args.layout): returns the bench line
+    (without the CPU baseline) and the workload."""
     w = I.WORKLOADS[args.workload]
     B, D, T = w.B, w.D, w.T
     N = w.N
@@ -692,25 +719,21 @@ def main():
     if not args.no_stream_ref:
         extra["stream_ref"] = stream_reference(torch, dev)
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args, np, I)
-
     line = {"metric": METRIC, "value": value, "unit": "elements/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
-            "data": "synthetic", "config": config, "roofline": roofline, "cpu_baseline": cpu,
-            **extra, "csrc_hash": csrc_hash()}
-    print(json.dumps(line), flush=True)
+            "data": "synthetic", "config": config, "roofline": roofline, "cpu_baseline": None,
+            **extra}
+    return line, w
 
 
 def crossover(args, np, torch, lrs, I, dev):
     """Kernel families for short channels: sequential (one lane per channel),
     packed (whole channels per workgroup) and one channel per workgroup, on
-    the headline workload's 2^24 elements of a, b, dL/dh regrouped as
-    [1, 2^24/T, T] for T = 4 .. 8192, each forced through the overrides the
-    library reads (LRS_SERIAL_FWD_MAX_T, LRS_SERIAL_BWD_MAX_T,
-    LRS_PACKED_MAX_T), timed with HIP events over --steps calls."""
+    the B=8 D=512 T=4096 workload's 2^24 elements of a, b, dL/dh regrouped as
+    [1, 2^24/T, T] for T = 4 .. 8192, each forced through the plan options
+    (serial_fwd_max_t, serial_bwd_max_t, packed_max_t), timed with HIP events
+    over --steps calls."""
     w = I.WORKLOADS["scan_fwd_bwd"]
     x = I.scan_inputs(w)
     N = w.N
@@ -733,12 +756,9 @@ def crossover(args, np, torch, lrs, I, dev):
         torch.cuda.synchronize()
         return s.elapsed_time(e) * 1e3 / args.steps
 
-    env = os.environ
-    keys = ("LRS_SERIAL_FWD_MAX_T", "LRS_SERIAL_BWD_MAX_T", "LRS_PACKED_MAX_T")
-    big = str(1 << 40)
-    modes = (("sequential", (big, big, "0")), ("packed", ("0", "0", big)),
-             ("one channel per workgroup", ("0", "0", "0")))
-    saved = {k: env.get(k) for k in keys}
+    big = 1 << 40
+    modes = (("sequential", (big, big, 0)), ("packed", (0, 0, big)),
+             ("one channel per workgroup", (0, 0, 0)))
     rows = []
     T = 4
     while T <= 8192:
@@ -746,20 +766,16 @@ def crossover(args, np, torch, lrs, I, dev):
         a, b, g = (flat[k].view(1, D, T) for k in ("a", "b", "g"))
         hv, gav, gbv = h.view(1, D, T), ga.view(1, D, T), gb.view(1, D, T)
         res = {}
-        for mode, lims in modes:
+        for mode, (sf, sb, pk) in modes:
             if mode == "packed" and T > 2048:
                 res[mode] = None  # no channel fits a packed workgroup
                 continue
-            for k, lim in zip(keys, lims):
-                env[k] = lim
-            res[mode] = (timed(lambda: lrs.scan_fwd(a, b, None, out=hv, workspace=ws)),
+            opts = {"serial_fwd_max_t": sf, "serial_bwd_max_t": sb, "packed_max_t": pk}
+            res[mode] = (timed(lambda: lrs.scan_fwd(a, b, None, out=hv, workspace=ws,
+                                                    options=opts)),
                          timed(lambda: lrs.scan_bwd(a, hv, g, None, need_grad_h0=False,
-                                                    grad_a=gav, grad_b=gbv, workspace=ws)))
-        for k in keys:
-            if saved[k] is None:
-                env.pop(k, None)
-            else:
-                env[k] = saved[k]
+                                                    grad_a=gav, grad_b=gbv, workspace=ws,
+                                                    options=opts)))
         rows.append((T, D, res))
         T *= 2
     pct = lambda us, bpe: 100.0 * bpe * N / (us * 1e-6) / 1e9 / HBM_PEAK_GBS
@@ -816,10 +832,10 @@ def cpu_baseline(w, args, np, I):
         h0 = x["h0"].astype(np.float64)
         g = x["g"].astype(np.float64) if "g" in x else None
 
-        def once():
-            h = oracle.scan_fwd(a, b, h0, nthreads=threads)
+        def once(nt=threads):
+            h = oracle.scan_fwd(a, b, h0, nthreads=nt)
             if g is not None:
-                oracle.scan_bwd(a, h, h0, g, nthreads=threads)
+                oracle.scan_bwd(a, h, h0, g, nthreads=nt)
         sample = f"{nch} of {C} channels x T={T}, fwd{'+bwd' if g is not None else ''}"
         n_el = nch * T
     elif w.kind == "sru":
@@ -830,10 +846,10 @@ def cpu_baseline(w, args, np, I):
         with_bwd = w.name == "sru_fwd_bwd"
         gh64 = I.bf16_bits_to_f64(I.sru_grad_inputs(sub)["gh"]) if with_bwd else None
 
-        def once():
-            oracle.sru_fwd(*z, s["bias_f"], s["bias_r"], nthreads=threads)
+        def once(nt=threads):
+            oracle.sru_fwd(*z, s["bias_f"], s["bias_r"], nthreads=nt)
             if with_bwd:
-                oracle.sru_bwd(*z, s["bias_f"], s["bias_r"], gh64, nthreads=threads)
+                oracle.sru_bwd(*z, s["bias_f"], s["bias_r"], gh64, nthreads=nt)
         sample = (f"B=1 of {w.B}, D={sub.D}, T={T} (same recipe), "
                   f"fwd{'+bwd' if with_bwd else ''}")
         n_el = sub.N
@@ -843,8 +859,8 @@ def cpu_baseline(w, args, np, I):
         z = [I.bf16_bits_to_f64(s[k]) for k in ("zf", "zr", "zx")]
         vf = I.sru_vf(sub)
 
-        def once():
-            oracle.sru_deer(*z, s["bias_f"], s["bias_r"], vf, eps=1e-5, k_max=5, nthreads=threads)
+        def once(nt=threads):
+            oracle.sru_deer(*z, s["bias_f"], s["bias_r"], vf, eps=1e-5, k_max=5, nthreads=nt)
         sample = f"B=1 of {w.B}, D={sub.D}, T={T} (same recipe), eps=1e-5, K_max=5"
         n_el = sub.N
     elif w.kind == "lstm":
@@ -853,9 +869,9 @@ def cpu_baseline(w, args, np, I):
         z = [I.bf16_bits_to_f64(s[k]) for k in ("zf", "zi", "zc", "zo")]
         gh64 = I.bf16_bits_to_f64(I.sru_grad_inputs(sub)["gh"])
 
-        def once():
-            oracle.lstm_fwd(*z, nthreads=threads)
-            oracle.lstm_bwd(*z, gh64, nthreads=threads)
+        def once(nt=threads):
+            oracle.lstm_fwd(*z, nthreads=nt)
+            oracle.lstm_bwd(*z, gh64, nthreads=nt)
         sample = f"B=1 of {w.B}, D={sub.D}, T={T} (same recipe), fwd+bwd"
         n_el = sub.N
     else:
@@ -867,21 +883,41 @@ def cpu_baseline(w, args, np, I):
         g64 = (I.series(w.seed, "g", w.dists["g"], np.arange(sub.C), T).reshape(1, sub.D, T)
                if with_bwd else None)
 
-        def once():
-            hs, _, _ = oracle.deer(x["w"], u, None, eps=1e-5, k_max=5, nthreads=threads)
+        def once(nt=threads):
+            hs, _, _ = oracle.deer(x["w"], u, None, eps=1e-5, k_max=5, nthreads=nt)
             if with_bwd:
-                oracle.deer_bwd(x["w"], hs, g64, nthreads=threads)
+                oracle.deer_bwd(x["w"], hs, g64, nthreads=nt)
         sample = (f"B=1 of {w.B}, D={sub.D}, T={T}, eps=1e-5, K_max=5"
                   f"{', solve+bwd' if with_bwd else ''}")
         n_el = sub.N
-    reps, t_total = 0, 0.0
-    while t_total < args.cpu_seconds and reps < 10000:
-        t0 = time.perf_counter()
-        once()
-        t_total += time.perf_counter() - t0
-        reps += 1
+    def time_it(nt):
+        reps, t_total = 0, 0.0
+        while t_total < args.cpu_seconds and reps < 10000:
+            t0 = time.perf_counter()
+            once(nt)
+            t_total += time.perf_counter() - t0
+            reps += 1
+        return reps, t_total
+
+    reps, t_total = time_it(threads)
+    reps1, t1 = time_it(1)
     return {"value": n_el * reps / t_total, "unit": "elements/s", "cores": threads,
-            "kind": "oracle", "sample": f"{sample}; {reps} repetitions, {t_total:.1f} s"}
+            "kind": "oracle", "sample": f"{sample}; {reps} repetitions, {t_total:.1f} s",
+            "single_thread": {"value": n_el * reps1 / t1, "unit": "elements/s", "cores": 1,
+                              "sample": f"{sample}; {reps1} repetitions, {t1:.1f} s"},
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first 'model name' entry of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":

@@ -44,21 +44,36 @@
  *    (B*D*T == 0) is valid and does nothing.
  *  - Output arrays must not overlap input arrays unless a function says so.
  *  - Calls that share a workspace must be ordered (same stream or synchronised).
- *  - [B,D,T] scans of short channels pack whole channels into each workgroup
- *    (T <= 64) or, for the shortest (T <= 4), run one lane per channel; the
- *    limits are measured crossovers, and the environment variables
- *    LRS_PACKED_MAX_T, LRS_SERIAL_FWD_MAX_T and LRS_SERIAL_BWD_MAX_T
- *    (integers, read at every call) override them.
- *  - The SRU forward and the SRU-by-DEER iterations switch to persistent
- *    kernels (one workgroup per 128 channels walks every time tile, no
- *    cross-workgroup look-back and no reset between iterations) when the
- *    128-channel blocks are at least as many as the device's compute units;
- *    LRS_PERSIST_MIN_BLOCKS (an integer, read at every call) replaces that
- *    count (0 = always, a huge value = never).  Both kernels give the same
- *    results to within fp32 rounding; the workspace size does not change.
- *    With the persistent plan and k_max <= 8, the SRU-by-DEER solve runs all
- *    its Newton iterations in that one walk (as lrs_deer_solve does; the same
- *    LRS_DEER_FUSE=0 switch selects one launch per iteration).
+ *  - Plans.  [B,D,T] scans of short channels pack whole channels into each
+ *    workgroup (T <= 64) or, for the shortest (T <= 4), run one lane per
+ *    channel; the limits are measured crossovers.  The SRU forward and the
+ *    SRU-by-DEER iterations switch to persistent kernels (one workgroup per
+ *    128 channels walks every time tile, no cross-workgroup look-back and no
+ *    reset between iterations) when the 128-channel blocks are at least as
+ *    many as the device's compute units; with the persistent plan and
+ *    k_max <= 8, the SRU-by-DEER solve runs all its Newton iterations in that
+ *    one walk, and DEER solves whose channels one workgroup walks do the same.
+ *    The entry points with the suffix _ex take an lrs_options argument that
+ *    moves these choices explicitly (for comparing kernel families on the
+ *    same inputs, or measuring crossovers); the library keeps no global or
+ *    environment-driven state.  Every plan gives the same results within
+ *    fp32 rounding, and the workspace queries cover every plan.
+ *  - Reproducibility.  A channel longer than one workgroup's chunk (time
+ *    block) is split into chunks whose states are combined by a fixed rule:
+ *    chunks are grouped (64 per group for [B,D,T] scans, 8 for [T,B,D]
+ *    kernels), the state entering a chunk is the previous group's end state
+ *    carried through the aggregates of the chunks before it in its group, in
+ *    ascending order, and only the last chunk of a group publishes an end
+ *    state.  The association order of every result therefore depends on the
+ *    launch shape alone (shape, layout, dtype and options), not on timing:
+ *    repeated calls with the same arguments give the same bits.
+ *  - Look-back time-out.  A workgroup that waits on a predecessor's status
+ *    word gives up after about 2^22 polls (only corrupted or foreign
+ *    workspace contents can cause that) and then writes NaN for the channels
+ *    it serves instead of hanging; the call still returns LRS_OK, so a NaN
+ *    in outputs whose inputs are finite signals such a time-out.  Calls that
+ *    share a workspace concurrently (not ordered on one stream) are the usual
+ *    cause, and are not allowed.
  */
 #ifndef LRS_H
 #define LRS_H
@@ -98,6 +113,31 @@ LRS_API const char *lrs_status_string(int status);
 /* Library ABI version (major*100 + minor). */
 LRS_API int lrs_version(void);
 
+/* ------------------------------------------------------ plan options --- */
+
+/* Explicit plan choices for the _ex entry points.  A negative field keeps the
+ * library's measured default; lrs_options_default sets every field so.
+ * Passing NULL options, or the defaults, selects exactly the plan of the
+ * entry point without the suffix. */
+typedef struct lrs_options {
+  int64_t serial_fwd_max_t;   /* [B,D,T] forward scan: one lane per channel for
+                                 T <= this (default 4; 0 = never) */
+  int64_t serial_bwd_max_t;   /* [B,D,T] backward scan: the same (default 4) */
+  int64_t packed_max_t;       /* [B,D,T] scans: whole channels packed into each
+                                 2048-step workgroup for T <= this (default 64) */
+  int64_t persist_min_blocks; /* SRU forward, SRU by DEER: persistent walk when
+                                 the 128-channel blocks number at least this
+                                 (default: the device's compute units; 0 =
+                                 always, a huge value = never) */
+  int32_t deer_fuse;          /* DEER and SRU-by-DEER solves: 0 = one launch per
+                                 Newton iteration; otherwise all iterations in
+                                 one pass where that applies (default) */
+  int32_t reserved;           /* set to 0 */
+} lrs_options;
+
+/* Fill *options with the defaults (every field -1, reserved 0); NULL is a no-op. */
+LRS_API void lrs_options_default(lrs_options *options);
+
 /* ---------------------------------------------------------------- scan --- */
 
 /* Workspace bytes needed by lrs_scan_fwd / lrs_scan_bwd for this shape
@@ -110,10 +150,15 @@ LRS_API size_t lrs_scan_workspace_bytes(int64_t B, int64_t D, int64_t T, int lay
  * a, b, h : [B,D,T] or [T,B,D] per `layout`, element type `dtype` (LRS_F32).
  * h0      : [B,D] fp32, or NULL for a zero initial state.
  * h must not overlap a, b or h0.  Arithmetic is fp32 with fused multiply-add;
- * the association order of the scan is fixed by the launch shape. */
+ * the association order of the scan is fixed by the launch shape (see
+ * Reproducibility above), so repeated calls give the same bits. */
 LRS_API int lrs_scan_fwd(const void *a, const void *b, const float *h0, void *h, int64_t B, int64_t D,
                  int64_t T, int layout, int dtype, void *workspace, size_t workspace_bytes,
                  void *stream);
+/* lrs_scan_fwd with explicit plan options (NULL = the defaults). */
+LRS_API int lrs_scan_fwd_ex(const void *a, const void *b, const float *h0, void *h, int64_t B,
+                            int64_t D, int64_t T, int layout, int dtype, void *workspace,
+                            size_t workspace_bytes, void *stream, const lrs_options *options);
 
 /* Backward scan: reverse-time adjoint of lrs_scan_fwd for a loss L whose
  * gradient with respect to h is grad_h ([P1]: the backward pass is also a
@@ -128,6 +173,11 @@ LRS_API int lrs_scan_fwd(const void *a, const void *b, const float *h0, void *h,
 LRS_API int lrs_scan_bwd(const void *a, const void *h, const float *h0, const void *grad_h, void *grad_a,
                  void *grad_b, float *grad_h0, int64_t B, int64_t D, int64_t T, int layout,
                  int dtype, void *workspace, size_t workspace_bytes, void *stream);
+/* lrs_scan_bwd with explicit plan options (NULL = the defaults). */
+LRS_API int lrs_scan_bwd_ex(const void *a, const void *h, const float *h0, const void *grad_h,
+                            void *grad_a, void *grad_b, float *grad_h0, int64_t B, int64_t D,
+                            int64_t T, int layout, int dtype, void *workspace,
+                            size_t workspace_bytes, void *stream, const lrs_options *options);
 
 /* Forward and backward scan in one call: the results of lrs_scan_fwd followed
  * by lrs_scan_bwd on the same inputs ([P1] parallel-scan paragraph: both
@@ -144,6 +194,12 @@ LRS_API int lrs_scan_fwd_bwd(const void *a, const void *b, const float *h0, cons
                              void *h, void *grad_a, void *grad_b, float *grad_h0, int64_t B,
                              int64_t D, int64_t T, int layout, int dtype, void *workspace,
                              size_t workspace_bytes, void *stream);
+/* lrs_scan_fwd_bwd with explicit plan options (NULL = the defaults). */
+LRS_API int lrs_scan_fwd_bwd_ex(const void *a, const void *b, const float *h0,
+                                const void *grad_h, void *h, void *grad_a, void *grad_b,
+                                float *grad_h0, int64_t B, int64_t D, int64_t T, int layout,
+                                int dtype, void *workspace, size_t workspace_bytes, void *stream,
+                                const lrs_options *options);
 
 /* ----------------------------------------------------------------- SRU --- */
 
@@ -167,6 +223,12 @@ LRS_API int lrs_sru_fwd(const void *z_f, const void *z_r, const void *z_x, const
                 const float *bias_r, const float *c0, void *h, float *c_last, float *c_states,
                 int64_t T, int64_t B, int64_t D, int io_dtype, void *workspace,
                 size_t workspace_bytes, void *stream);
+/* lrs_sru_fwd with explicit plan options (NULL = the defaults). */
+LRS_API int lrs_sru_fwd_ex(const void *z_f, const void *z_r, const void *z_x,
+                           const float *bias_f, const float *bias_r, const float *c0, void *h,
+                           float *c_last, float *c_states, int64_t T, int64_t B, int64_t D,
+                           int io_dtype, void *workspace, size_t workspace_bytes, void *stream,
+                           const lrs_options *options);
 
 /* Workspace bytes needed by lrs_sru_bwd for this shape (0 for an invalid one). */
 LRS_API size_t lrs_sru_bwd_workspace_bytes(int64_t T, int64_t B, int64_t D);
@@ -228,6 +290,14 @@ LRS_API int lrs_sru_deer_fwd(const void *z_f, const void *z_r, const void *z_x,
                              float eps, int k_max, int *iters_out, float *deltas_out,
                              int *converged_out, void *workspace, size_t workspace_bytes,
                              void *stream);
+/* lrs_sru_deer_fwd with explicit plan options (NULL = the defaults). */
+LRS_API int lrs_sru_deer_fwd_ex(const void *z_f, const void *z_r, const void *z_x,
+                                const float *bias_f, const float *bias_r, const float *v_f,
+                                const float *c0, const float *c_init, void *h, float *c_states,
+                                float *c_last, int64_t T, int64_t B, int64_t D, int io_dtype,
+                                float eps, int k_max, int *iters_out, float *deltas_out,
+                                int *converged_out, void *workspace, size_t workspace_bytes,
+                                void *stream, const lrs_options *options);
 
 /* ---------------------------------------------------------------- LSTM --- */
 
@@ -313,12 +383,18 @@ LRS_API size_t lrs_deer_workspace_bytes(int64_t B, int64_t D, int64_t T, int k_m
  * ends the solve before k_max a second pass recomputes exactly that many
  * iterations; the record, the iteration count and the result (within fp32
  * rounding) are those of the one-launch-per-iteration path, which
- * LRS_DEER_FUSE=0 (read at every call) selects.  Solves that share a
+ * lrs_deer_solve_ex with options->deer_fuse = 0 selects.  Solves that share a
  * workspace must be ordered. */
 LRS_API int lrs_deer_solve(const float *w, const float *u, const float *h0, const float *h_init, float *h,
                    int64_t B, int64_t D, int64_t T, float eps, int k_max, int *iters_out,
                    float *deltas_out, int *converged_out, void *workspace,
                    size_t workspace_bytes, void *stream);
+/* lrs_deer_solve with explicit plan options (NULL = the defaults). */
+LRS_API int lrs_deer_solve_ex(const float *w, const float *u, const float *h0,
+                              const float *h_init, float *h, int64_t B, int64_t D, int64_t T,
+                              float eps, int k_max, int *iters_out, float *deltas_out,
+                              int *converged_out, void *workspace, size_t workspace_bytes,
+                              void *stream, const lrs_options *options);
 
 /* Workspace bytes needed by lrs_deer_solve_seq (0 for an invalid or empty shape). */
 LRS_API size_t lrs_deer_seq_workspace_bytes(int64_t B, int64_t D, int64_t T, int k_max);
@@ -334,13 +410,19 @@ LRS_API size_t lrs_deer_seq_workspace_bytes(int64_t B, int64_t D, int64_t T, int
  * arguments as for lrs_deer_solve.  B is limited to 65535.  Returns
  * LRS_ERR_NONFINITE when some sequence's last update was NaN or infinite.
  * Under the same conditions as lrs_deer_solve (T <= 8192, k_max <= 8,
- * LRS_DEER_FUSE not "0") all iterations run in one pass that keeps each
+ * deer_fuse not 0) all iterations run in one pass that keeps each
  * sequence's norms per iteration; sequences whose stop rule fired before
  * k_max are recomputed to their own count in a second pass. */
 LRS_API int lrs_deer_solve_seq(const float *w, const float *u, const float *h0,
                                const float *h_init, float *h, int64_t B, int64_t D, int64_t T,
                                float eps, int k_max, int *iters_out, int *converged_out,
                                void *workspace, size_t workspace_bytes, void *stream);
+/* lrs_deer_solve_seq with explicit plan options (NULL = the defaults). */
+LRS_API int lrs_deer_solve_seq_ex(const float *w, const float *u, const float *h0,
+                                  const float *h_init, float *h, int64_t B, int64_t D,
+                                  int64_t T, float eps, int k_max, int *iters_out,
+                                  int *converged_out, void *workspace, size_t workspace_bytes,
+                                  void *stream, const lrs_options *options);
 
 /* Record of the most recent lrs_deer_solve or lrs_sru_deer_fwd that used this
  * workspace with this k_max (same meaning of iters_out, deltas_out, converged_out as there; each
@@ -350,6 +432,16 @@ LRS_API int lrs_deer_solve_seq(const float *w, const float *u, const float *h0,
  * LRS_ERR_HIP if the workspace holds no finished solve record. */
 LRS_API int lrs_deer_stats(const void *workspace, size_t workspace_bytes, int k_max,
                    int *iters_out, float *deltas_out, int *converged_out, void *stream);
+
+/* Newton tolerance for training step `step` of `total_steps` ([P4]
+ * engineering section: relax the stop tolerance early in training, tighten it
+ * late): log-linear interpolation from `early` at step 0 to `late` at step
+ * total_steps - 1,
+ *   eps(step) = early * (late / early)^(step / (total_steps - 1)),
+ * with step clamped to [0, total_steps - 1]; total_steps <= 1 gives `late`.
+ * Computed in double precision and rounded once to float.  Returns NaN when
+ * early or late is not a positive finite number. */
+LRS_API float lrs_deer_eps_schedule(int64_t step, int64_t total_steps, float early, float late);
 
 /* Workspace bytes needed by lrs_deer_bwd (0 for an invalid or empty shape). */
 LRS_API size_t lrs_deer_bwd_workspace_bytes(int64_t B, int64_t D, int64_t T);

@@ -8,8 +8,10 @@ missing library raises at once.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
+import threading
 from typing import Optional
 
 import torch
@@ -28,6 +30,56 @@ EXPORTS = ("lrs_status_string", "lrs_version", "lrs_scan_workspace_bytes", "lrs_
            "lrs_deer_bwd_workspace_bytes", "lrs_deer_bwd", "lrs_lstm_workspace_bytes",
            "lrs_lstm_fwd", "lrs_lstm_bwd", "lrs_scan_fwd_bwd", "lrs_sru_deer_workspace_bytes",
            "lrs_sru_deer_fwd", "lrs_deer_seq_workspace_bytes", "lrs_deer_solve_seq")
+
+# entry points that have an _ex variant taking lrs_options
+_EX_BASES = ("lrs_scan_fwd", "lrs_scan_bwd", "lrs_scan_fwd_bwd", "lrs_sru_fwd", "lrs_sru_deer_fwd",
+             "lrs_deer_solve", "lrs_deer_solve_seq")
+EXPORTS = EXPORTS + tuple(n + "_ex" for n in _EX_BASES) + ("lrs_options_default",
+                                                            "lrs_deer_eps_schedule")
+
+
+class LrsOptions(ctypes.Structure):
+    """lrs_options (include/lrs.h): explicit plan choices, -1 = the default."""
+    _fields_ = [("serial_fwd_max_t", ctypes.c_int64), ("serial_bwd_max_t", ctypes.c_int64),
+                ("packed_max_t", ctypes.c_int64), ("persist_min_blocks", ctypes.c_int64),
+                ("deer_fuse", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_plan = threading.local()
+
+
+@contextlib.contextmanager
+def plan_options(**fields):
+    """Inside the block, calls that accept `options` and get none pass these
+    lrs_options fields (merged over those of an enclosing block) to the
+    library's _ex entry point.  The choice still travels as an explicit
+    argument of every call; the library itself keeps no state."""
+    prev = getattr(_plan, "opts", None)
+    merged = dict(prev or {})
+    merged.update(fields)
+    _plan.opts = merged
+    try:
+        yield
+    finally:
+        _plan.opts = prev
+
+
+def _opts(options):
+    """None, or a dict of lrs_options fields (others keep the defaults), ->
+    the pointer argument of an _ex entry point."""
+    if options is None:
+        options = getattr(_plan, "opts", None)
+    if options is None:
+        return None
+    o = LrsOptions()
+    load().lrs_options_default(ctypes.byref(o))
+    for k, v in dict(options).items():
+        if k not in ("serial_fwd_max_t", "serial_bwd_max_t", "packed_max_t",
+                     "persist_min_blocks", "deer_fuse"):
+            raise ValueError(f"unknown option {k!r}")
+        setattr(o, k, int(v))
+    return ctypes.byref(o)
+
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -103,6 +155,15 @@ def load():
     lib.lrs_deer_bwd_workspace_bytes.restype = _sz
     lib.lrs_deer_bwd.argtypes = [_vp] * 7 + [_i64, _i64, _i64, _vp, _sz, _vp]
     lib.lrs_deer_bwd.restype = _int
+    lib.lrs_options_default.argtypes = [ctypes.POINTER(LrsOptions)]
+    lib.lrs_options_default.restype = None
+    for name in _EX_BASES:
+        base = getattr(lib, name)
+        ex = getattr(lib, name + "_ex")
+        ex.argtypes = list(base.argtypes) + [ctypes.POINTER(LrsOptions)]
+        ex.restype = _int
+    lib.lrs_deer_eps_schedule.argtypes = [_i64, _i64, ctypes.c_float, ctypes.c_float]
+    lib.lrs_deer_eps_schedule.restype = ctypes.c_float
     _lib = lib
     return lib
 
@@ -159,7 +220,7 @@ def scan_workspace_bytes(B, D, T, layout="bdt", dtype=torch.float32) -> int:
     return int(load().lrs_scan_workspace_bytes(B, D, T, LAYOUTS[layout], DTYPES[dtype]))
 
 
-def scan_fwd(a, b, h0=None, layout: str = "bdt", out=None, workspace=None):
+def scan_fwd(a, b, h0=None, layout: str = "bdt", out=None, workspace=None, options=None):
     """h_t = a_t*h_{t-1} + b_t.  a, b: [B,D,T] ('bdt') or [T,B,D] ('tbd'); h0: [B,D]."""
     lib = load()
     B, D, T = _dims(a, layout)
@@ -170,13 +231,13 @@ def scan_fwd(a, b, h0=None, layout: str = "bdt", out=None, workspace=None):
     _check_dev("out", h, a.dtype, a.shape)
     nbytes = lib.lrs_scan_workspace_bytes(B, D, T, LAYOUTS[layout], DTYPES[a.dtype])
     ws = _workspace(nbytes, a.device, workspace)
-    _call(lib.lrs_scan_fwd(_ptr(a), _ptr(b), _ptr(h0), _ptr(h), B, D, T, LAYOUTS[layout],
-                           DTYPES[a.dtype], _ptr(ws), nbytes, _stream(a.device)), "lrs_scan_fwd")
+    _call(lib.lrs_scan_fwd_ex(_ptr(a), _ptr(b), _ptr(h0), _ptr(h), B, D, T, LAYOUTS[layout],
+                           DTYPES[a.dtype], _ptr(ws), nbytes, _stream(a.device), _opts(options)), "lrs_scan_fwd")
     return h
 
 
 def scan_bwd(a, h, grad_h, h0=None, layout: str = "bdt", need_grad_h0: bool = True,
-             grad_a=None, grad_b=None, grad_h0=None, workspace=None):
+             grad_a=None, grad_b=None, grad_h0=None, workspace=None, options=None):
     """Reverse-time adjoint.  Returns (grad_a, grad_b, grad_h0 or None).
     grad_b may be passed as grad_h itself (in-place)."""
     lib = load()
@@ -194,14 +255,14 @@ def scan_bwd(a, h, grad_h, h0=None, layout: str = "bdt", need_grad_h0: bool = Tr
     _check_dev("grad_h0", gh0, torch.float32, (B, D))
     nbytes = lib.lrs_scan_workspace_bytes(B, D, T, LAYOUTS[layout], DTYPES[a.dtype])
     ws = _workspace(nbytes, a.device, workspace)
-    _call(lib.lrs_scan_bwd(_ptr(a), _ptr(h), _ptr(h0), _ptr(grad_h), _ptr(ga), _ptr(gb), _ptr(gh0),
+    _call(lib.lrs_scan_bwd_ex(_ptr(a), _ptr(h), _ptr(h0), _ptr(grad_h), _ptr(ga), _ptr(gb), _ptr(gh0),
                            B, D, T, LAYOUTS[layout], DTYPES[a.dtype], _ptr(ws), nbytes,
-                           _stream(a.device)), "lrs_scan_bwd")
+                           _stream(a.device), _opts(options)), "lrs_scan_bwd")
     return ga, gb, gh0
 
 
 def scan_fwd_bwd(a, b, grad_h, h0=None, layout: str = "bdt", want_h: bool = True,
-                 need_grad_h0: bool = True, out=None, workspace=None):
+                 need_grad_h0: bool = True, out=None, workspace=None, options=None):
     """scan_fwd then scan_bwd in one call (one kernel for [B,D,T] channels of
     up to 8192 steps).  Returns (h or None, grad_a, grad_b, grad_h0 or None).
     want_h=False skips writing h (only where one kernel does both passes).
@@ -220,14 +281,14 @@ def scan_fwd_bwd(a, b, grad_h, h0=None, layout: str = "bdt", want_h: bool = True
     _check_dev("grad_h0", gh0, torch.float32, (B, D))
     nbytes = lib.lrs_scan_workspace_bytes(B, D, T, LAYOUTS[layout], DTYPES[a.dtype])
     ws = _workspace(nbytes, a.device, workspace)
-    _call(lib.lrs_scan_fwd_bwd(_ptr(a), _ptr(b), _ptr(h0), _ptr(grad_h), _ptr(h), _ptr(ga),
+    _call(lib.lrs_scan_fwd_bwd_ex(_ptr(a), _ptr(b), _ptr(h0), _ptr(grad_h), _ptr(h), _ptr(ga),
                                _ptr(gb), _ptr(gh0), B, D, T, LAYOUTS[layout], DTYPES[a.dtype],
-                               _ptr(ws), nbytes, _stream(a.device)), "lrs_scan_fwd_bwd")
+                               _ptr(ws), nbytes, _stream(a.device), _opts(options)), "lrs_scan_fwd_bwd")
     return h, ga, gb, gh0
 
 
 def sru_fwd(z_f, z_r, z_x, bias_f, bias_r, c0=None, want_c_last: bool = False, out=None,
-            workspace=None, c_states=None):
+            workspace=None, c_states=None, options=None):
     """Fused SRU layer on [T,B,D] pre-activations (bf16 or fp32).  Returns h or
     (h, c_last).  c_states, if given, is a [T,B,D] fp32 tensor that receives
     every cell state (the input sru_bwd needs)."""
@@ -247,9 +308,9 @@ def sru_fwd(z_f, z_r, z_x, bias_f, bias_r, c0=None, want_c_last: bool = False, o
     c_last = torch.empty((B, D), dtype=torch.float32, device=z_f.device) if want_c_last else None
     nbytes = lib.lrs_sru_workspace_bytes(T, B, D)
     ws = _workspace(nbytes, z_f.device, workspace)
-    _call(lib.lrs_sru_fwd(_ptr(z_f), _ptr(z_r), _ptr(z_x), _ptr(bias_f), _ptr(bias_r), _ptr(c0),
+    _call(lib.lrs_sru_fwd_ex(_ptr(z_f), _ptr(z_r), _ptr(z_x), _ptr(bias_f), _ptr(bias_r), _ptr(c0),
                           _ptr(h), _ptr(c_last), _ptr(c_states), T, B, D, DTYPES[io], _ptr(ws),
-                          nbytes, _stream(z_f.device)), "lrs_sru_fwd")
+                          nbytes, _stream(z_f.device), _opts(options)), "lrs_sru_fwd")
     return (h, c_last) if want_c_last else h
 
 
@@ -286,7 +347,7 @@ def sru_bwd(z_f, z_r, z_x, bias_f, bias_r, c_states, grad_h, c0=None, grad_c_las
 
 def sru_deer_fwd(z_f, z_r, z_x, bias_f, bias_r, v_f, c0=None, c_init=None, eps: float = 1e-5,
                  k_max: int = 5, want_c_last: bool = False, out=None, c_states=None,
-                 workspace=None, sync: bool = True):
+                 workspace=None, sync: bool = True, options=None):
     """SRU layer with v_f * c_{t-1} in the forget gate, by DEER.  sync=True:
     returns (h, c_states, c_last or None, info), info = {"iters", "deltas",
     "converged", "status"} as for deer_solve.  sync=False: returns
@@ -314,20 +375,20 @@ def sru_deer_fwd(z_f, z_r, z_x, bias_f, bias_r, v_f, c0=None, c_init=None, eps: 
         iters = ctypes.c_int(0)
         conv = ctypes.c_int(0)
         deltas = (ctypes.c_float * max(1, int(k_max)))()
-        rc = lib.lrs_sru_deer_fwd(_ptr(z_f), _ptr(z_r), _ptr(z_x), _ptr(bias_f), _ptr(bias_r),
+        rc = lib.lrs_sru_deer_fwd_ex(_ptr(z_f), _ptr(z_r), _ptr(z_x), _ptr(bias_f), _ptr(bias_r),
                                   _ptr(v_f), _ptr(c0), _ptr(c_init), _ptr(h), _ptr(cs),
                                   _ptr(c_last), T, B, D, DTYPES[io], float(eps), int(k_max),
                                   ctypes.byref(iters), deltas, ctypes.byref(conv), _ptr(ws),
-                                  nbytes, _stream(z_f.device))
+                                  nbytes, _stream(z_f.device), _opts(options))
         if rc not in (LRS_OK, LRS_ERR_NONFINITE):
             raise LrsError(rc, "lrs_sru_deer_fwd")
         info = {"iters": iters.value, "deltas": [float(deltas[i]) for i in range(iters.value)],
                 "converged": bool(conv.value), "status": int(rc)}
         return h, cs, c_last, info
-    _call(lib.lrs_sru_deer_fwd(_ptr(z_f), _ptr(z_r), _ptr(z_x), _ptr(bias_f), _ptr(bias_r),
+    _call(lib.lrs_sru_deer_fwd_ex(_ptr(z_f), _ptr(z_r), _ptr(z_x), _ptr(bias_f), _ptr(bias_r),
                                _ptr(v_f), _ptr(c0), _ptr(c_init), _ptr(h), _ptr(cs),
                                _ptr(c_last), T, B, D, DTYPES[io], float(eps), int(k_max), None,
-                               None, None, _ptr(ws), nbytes, _stream(z_f.device)),
+                               None, None, _ptr(ws), nbytes, _stream(z_f.device), _opts(options)),
           "lrs_sru_deer_fwd")
     return h, cs, c_last, ws
 
@@ -389,7 +450,7 @@ def lstm_bwd(z_f, z_i, z_c, z_o, c_states, grad_h, c0=None, grad_c_last=None,
 
 
 def deer_solve(w, u, h0=None, h_init=None, eps: float = 1e-5, k_max: int = 5, out=None,
-               workspace=None, sync: bool = True):
+               workspace=None, sync: bool = True, options=None):
     """DEER Newton solve of h_t = tanh(w h_{t-1} + u_t); u: [B,D,T] fp32, w: [D].
 
     sync=True: returns (h, info) with info = {"iters", "deltas", "converged",
@@ -407,18 +468,18 @@ def deer_solve(w, u, h0=None, h_init=None, eps: float = 1e-5, k_max: int = 5, ou
     nbytes = lib.lrs_deer_workspace_bytes(B, D, T, k_max)
     ws = _workspace(nbytes, u.device, workspace)
     if not sync:
-        rc = lib.lrs_deer_solve(_ptr(w), _ptr(u), _ptr(h0), _ptr(h_init), _ptr(h), B, D, T,
+        rc = lib.lrs_deer_solve_ex(_ptr(w), _ptr(u), _ptr(h0), _ptr(h_init), _ptr(h), B, D, T,
                                 float(eps), int(k_max), None, None, None, _ptr(ws), nbytes,
-                                _stream(u.device))
+                                _stream(u.device), _opts(options))
         if rc != LRS_OK:
             raise LrsError(rc, "lrs_deer_solve")
         return h, ws
     iters = ctypes.c_int(0)
     conv = ctypes.c_int(0)
     deltas = (ctypes.c_float * max(k_max, 1))()
-    rc = lib.lrs_deer_solve(_ptr(w), _ptr(u), _ptr(h0), _ptr(h_init), _ptr(h), B, D, T,
+    rc = lib.lrs_deer_solve_ex(_ptr(w), _ptr(u), _ptr(h0), _ptr(h_init), _ptr(h), B, D, T,
                             float(eps), int(k_max), ctypes.byref(iters), deltas,
-                            ctypes.byref(conv), _ptr(ws), nbytes, _stream(u.device))
+                            ctypes.byref(conv), _ptr(ws), nbytes, _stream(u.device), _opts(options))
     if rc not in (LRS_OK, LRS_ERR_NONFINITE):
         raise LrsError(rc, "lrs_deer_solve")
     info = {"iters": iters.value, "deltas": [float(deltas[i]) for i in range(iters.value)],
@@ -427,7 +488,7 @@ def deer_solve(w, u, h0=None, h_init=None, eps: float = 1e-5, k_max: int = 5, ou
 
 
 def deer_solve_seq(w, u, h0=None, h_init=None, eps: float = 1e-5, k_max: int = 5, out=None,
-                   workspace=None, sync: bool = True):
+                   workspace=None, sync: bool = True, options=None):
     """deer_solve with per-sequence stopping (each batch entry stops on its own
     norm).  Returns (h, iters[B], converged[B]) when sync, else (h, workspace)."""
     lib = load()
@@ -443,26 +504,23 @@ def deer_solve_seq(w, u, h0=None, h_init=None, eps: float = 1e-5, k_max: int = 5
     if sync:
         iters = (ctypes.c_int * max(B, 1))()
         conv = (ctypes.c_int * max(B, 1))()
-        rc = lib.lrs_deer_solve_seq(_ptr(w), _ptr(u), _ptr(h0), _ptr(h_init), _ptr(h), B, D, T,
+        rc = lib.lrs_deer_solve_seq_ex(_ptr(w), _ptr(u), _ptr(h0), _ptr(h_init), _ptr(h), B, D, T,
                                     float(eps), int(k_max), iters, conv, _ptr(ws), nbytes,
-                                    _stream(u.device))
+                                    _stream(u.device), _opts(options))
         if rc not in (LRS_OK, LRS_ERR_NONFINITE):  # non-finite updates show as not converged
             raise LrsError(rc, "lrs_deer_solve_seq")
         return h, [int(iters[b]) for b in range(B)], [bool(conv[b]) for b in range(B)]
-    _call(lib.lrs_deer_solve_seq(_ptr(w), _ptr(u), _ptr(h0), _ptr(h_init), _ptr(h), B, D, T,
+    _call(lib.lrs_deer_solve_seq_ex(_ptr(w), _ptr(u), _ptr(h0), _ptr(h_init), _ptr(h), B, D, T,
                                  float(eps), int(k_max), None, None, _ptr(ws), nbytes,
-                                 _stream(u.device)), "lrs_deer_solve_seq")
+                                 _stream(u.device), _opts(options)), "lrs_deer_solve_seq")
     return h, ws
 
 
 def deer_eps_schedule(step: int, total_steps: int, early: float = 1e-4, late: float = 1e-6) -> float:
-    """Tolerance for training step `step` of `total_steps`: the DEER page's
-    engineering section suggests a loose eps early in training and a tight one
-    late; this interpolates log-linearly from `early` to `late`."""
-    if total_steps <= 1:
-        return float(late)
-    frac = min(max(step / (total_steps - 1), 0.0), 1.0)
-    return float(early * (late / early) ** frac)
+    """Newton tolerance for training step `step` of `total_steps`
+    (lrs_deer_eps_schedule: log-linear from `early` to `late`)."""
+    return float(load().lrs_deer_eps_schedule(int(step), int(total_steps), float(early),
+                                              float(late)))
 
 
 def deer_bwd(w, h, grad_h, h0=None, want_grad_h0: bool = True, out=None, workspace=None):

@@ -2,7 +2,6 @@
 // workspace carving and launch-plan choice.  All device work is enqueued on
 // the caller's stream; nothing here allocates device memory.
 #include <math.h>
-#include <stdlib.h>
 #include <string.h>
 
 #include <vector>
@@ -140,9 +139,10 @@ static int scan_common_checks(int64_t B, int64_t D, int64_t T, int layout, int d
   return LRS_OK;
 }
 
-int lrs_scan_fwd(const void* a, const void* b, const float* h0, void* h, int64_t B, int64_t D,
+static int scan_fwd_impl(const void* a, const void* b, const float* h0, void* h, int64_t B, int64_t D,
                  int64_t T, int layout, int dtype, void* workspace, size_t workspace_bytes,
-                 void* stream) {
+                 void* stream,
+    const lrs::Opts& opt) {
   int64_t C, N;
   int rc = scan_common_checks(B, D, T, layout, dtype, &C, &N);
   if (rc != LRS_OK) return rc;
@@ -161,7 +161,7 @@ int lrs_scan_fwd(const void* a, const void* b, const float* h0, void* h, int64_t
   const bool al16 = aligned(a, 16) && aligned(b, 16) && aligned(h, 16);
 
   if (layout == LRS_LAYOUT_BDT) {
-    const lrs::RowPlan p = lrs::plan_scan_fwd_rows(C, T);
+    const lrs::RowPlan p = lrs::plan_scan_fwd_rows(C, T, opt);
     if (!rows_grid_ok(p, C)) return LRS_ERR_UNSUPPORTED;
     uint64_t* status = nullptr;
     unsigned* tickets = nullptr;
@@ -194,9 +194,10 @@ int lrs_scan_fwd(const void* a, const void* b, const float* h0, void* h, int64_t
                                              p, vec, status, tickets, s));
 }
 
-int lrs_scan_bwd(const void* a, const void* h, const float* h0, const void* grad_h, void* grad_a,
+static int scan_bwd_impl(const void* a, const void* h, const float* h0, const void* grad_h, void* grad_a,
                  void* grad_b, float* grad_h0, int64_t B, int64_t D, int64_t T, int layout,
-                 int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                 int dtype, void* workspace, size_t workspace_bytes, void* stream,
+    const lrs::Opts& opt) {
   int64_t C, N;
   int rc = scan_common_checks(B, D, T, layout, dtype, &C, &N);
   if (rc != LRS_OK) return rc;
@@ -230,7 +231,7 @@ int lrs_scan_bwd(const void* a, const void* h, const float* h0, const void* grad
                     aligned(grad_a, 16) && aligned(grad_b, 16);
 
   if (layout == LRS_LAYOUT_BDT) {
-    const lrs::RowPlan p = lrs::plan_scan_bwd_rows(C, T);
+    const lrs::RowPlan p = lrs::plan_scan_bwd_rows(C, T, opt);
     if (!rows_grid_ok(p, C)) return LRS_ERR_UNSUPPORTED;
     uint64_t* status = nullptr;
     unsigned* tickets = nullptr;
@@ -265,10 +266,11 @@ int lrs_scan_bwd(const void* a, const void* h, const float* h0, const void* grad
                                              grad_h0, C, T, p, vec, status, tickets, s));
 }
 
-int lrs_scan_fwd_bwd(const void* a, const void* b, const float* h0, const void* grad_h, void* h,
+static int scan_fwd_bwd_impl(const void* a, const void* b, const float* h0, const void* grad_h, void* h,
                      void* grad_a, void* grad_b, float* grad_h0, int64_t B, int64_t D, int64_t T,
                      int layout, int dtype, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+                     void* stream,
+    const lrs::Opts& opt) {
   int64_t C, N;
   int rc = scan_common_checks(B, D, T, layout, dtype, &C, &N);
   if (rc != LRS_OK) return rc;
@@ -299,7 +301,7 @@ int lrs_scan_fwd_bwd(const void* a, const void* b, const float* h0, const void* 
   const lrs::RowPlan p = lrs::plan_scan_fused_rows(C, T);
   // short channels run the sequential or packed passes when h is wanted anyway
   // (the one-kernel form gives each channel a mostly idle workgroup)
-  const lrs::RowPlan pf = lrs::plan_scan_fwd_rows(C, T);
+  const lrs::RowPlan pf = lrs::plan_scan_fwd_rows(C, T, opt);
   const bool short_pair = h && (pf.serial || pf.packed);
   if (layout == LRS_LAYOUT_BDT && p.nchunk == 1 && !short_pair) {
     if (!grid_ok(C, p.threads())) return LRS_ERR_UNSUPPORTED;
@@ -315,10 +317,10 @@ int lrs_scan_fwd_bwd(const void* a, const void* b, const float* h0, const void* 
   size_t need = 0;
   scan_ws_needs(C, T, layout, &need);
   if (need && (!workspace || workspace_bytes < need)) return LRS_ERR_WORKSPACE;
-  rc = lrs_scan_fwd(a, b, h0, h, B, D, T, layout, dtype, workspace, workspace_bytes, stream);
+  rc = scan_fwd_impl(a, b, h0, h, B, D, T, layout, dtype, workspace, workspace_bytes, stream, opt);
   if (rc != LRS_OK) return rc;
-  return lrs_scan_bwd(a, h, h0, grad_h, grad_a, grad_b, grad_h0, B, D, T, layout, dtype,
-                      workspace, workspace_bytes, stream);
+  return scan_bwd_impl(a, h, h0, grad_h, grad_a, grad_b, grad_h0, B, D, T, layout, dtype,
+                       workspace, workspace_bytes, stream, opt);
 }
 
 // -------------------------------------------------------------------- SRU
@@ -338,10 +340,11 @@ size_t lrs_sru_workspace_bytes(int64_t T, int64_t B, int64_t D) {
   return b1 > b2 ? b1 : b2;
 }
 
-int lrs_sru_fwd(const void* z_f, const void* z_r, const void* z_x, const float* bias_f,
+static int sru_fwd_impl(const void* z_f, const void* z_r, const void* z_x, const float* bias_f,
                 const float* bias_r, const float* c0, void* h, float* c_last, float* c_states,
                 int64_t T, int64_t B, int64_t D, int io_dtype, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                size_t workspace_bytes, void* stream,
+    const lrs::Opts& opt) {
   int64_t C, N;
   if (!shape_ok(B, D, T, &C, &N)) return LRS_ERR_INVALID_ARG;
   if (io_dtype != LRS_F32 && io_dtype != LRS_BF16) return LRS_ERR_INVALID_ARG;
@@ -366,7 +369,7 @@ int lrs_sru_fwd(const void* z_f, const void* z_r, const void* z_x, const float* 
   if (overlap(h, nb, c_last, cb) || overlap(h, nb, c_states, sb) ||
       overlap(c_last, cb, c_states, sb))
     return LRS_ERR_INVALID_ARG;
-  const lrs::ColPlan p = lrs::plan_sru(C, T, io_dtype);
+  const lrs::ColPlan p = lrs::plan_sru(C, T, io_dtype, true, opt);
   if (!grid_ok(p.ncb * p.ntb, p.nw * 64)) return LRS_ERR_UNSUPPORTED;
   const int64_t nst = lrs::col_status_words(p);
   const size_t need = lookback_bytes(nst, p.ncb);
@@ -648,12 +651,9 @@ static bool deer_fusable(const lrs::RowPlan& p, int k_max) {
   return p.nchunk == 1 && k_max <= lrs::kDeerFuseMax;
 }
 
-// LRS_DEER_FUSE=0 (read at every call) runs the iterations one launch each
+// deer_fuse = 0 in the caller's options runs the iterations one launch each
 // even where the fused solve applies.
-static bool deer_fuse_enabled() {
-  const char* v = getenv("LRS_DEER_FUSE");
-  return !(v && v[0] == '0' && v[1] == '\0');
-}
+static bool deer_fuse_enabled(const lrs::Opts& opt) { return opt.deer_fuse != 0; }
 
 static size_t deer_fused_set_words(int k_max) {
   return (size_t)k_max * lrs::kDeltaSlots * lrs::kDeltaStride;
@@ -670,10 +670,11 @@ size_t lrs_deer_workspace_bytes(int64_t B, int64_t D, int64_t T, int k_max) {
   return bytes;
 }
 
-int lrs_deer_solve(const float* w, const float* u, const float* h0, const float* h_init, float* h,
+static int deer_solve_impl(const float* w, const float* u, const float* h0, const float* h_init, float* h,
                    int64_t B, int64_t D, int64_t T, float eps, int k_max, int* iters_out,
                    float* deltas_out, int* converged_out, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+                   size_t workspace_bytes, void* stream,
+    const lrs::Opts& opt) {
   int64_t C, N;
   if (!shape_ok(B, D, T, &C, &N) || k_max < 1 || k_max > 1000000) return LRS_ERR_INVALID_ARG;
   if (N == 0) {
@@ -712,7 +713,7 @@ int lrs_deer_solve(const float* w, const float* u, const float* h0, const float*
   const int vec = aligned(u, 16) && aligned(h, 16) && aligned(ybuf, 16) &&
                   (!h_init || aligned(h_init, 16)) && (T % 4 == 0);
 
-  if (deer_fusable(p, k_max) && deer_fuse_enabled()) {
+  if (deer_fusable(p, k_max) && deer_fuse_enabled(opt)) {
     uint32_t* sets = cv.take<uint32_t>((int64_t)deer_fused_set_words(k_max));
     // the pass must not overwrite a starting iterate held in h: a redo may need it
     float* out = (h_init == h) ? ybuf : h;
@@ -767,10 +768,11 @@ size_t lrs_deer_seq_workspace_bytes(int64_t B, int64_t D, int64_t T, int k_max) 
   return bytes;
 }
 
-int lrs_deer_solve_seq(const float* w, const float* u, const float* h0, const float* h_init,
+static int deer_solve_seq_impl(const float* w, const float* u, const float* h0, const float* h_init,
                        float* h, int64_t B, int64_t D, int64_t T, float eps, int k_max,
                        int* iters_out, int* converged_out, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       size_t workspace_bytes, void* stream,
+    const lrs::Opts& opt) {
   int64_t C, N;
   if (!shape_ok(B, D, T, &C, &N) || k_max < 1 || k_max > 1000000) return LRS_ERR_INVALID_ARG;
   if (N == 0) {
@@ -819,7 +821,7 @@ int lrs_deer_solve_seq(const float* w, const float* u, const float* h0, const fl
                                         (int64_t)((char*)(seq_rec + B * 4) - (char*)seq_slots) / 4,
                                         s));
   if (rc != LRS_OK) return rc;
-  if (deer_fusable(p, k_max) && deer_fuse_enabled()) {
+  if (deer_fusable(p, k_max) && deer_fuse_enabled(opt)) {
     // all iterations in one pass, each sequence's norms folded into seq_delta
     float* out = (h_init == h) ? ybuf : h;
     rc = hip_status(lrs::launch_deer_fused(w, u, h_init, h0, out, h, C, D, T, p, vec, k_max, eps,
@@ -878,11 +880,12 @@ size_t lrs_sru_deer_workspace_bytes(int64_t T, int64_t B, int64_t D, int k_max) 
   return kAlign + deer_record_bytes(k_max) + align_up((size_t)N * 4) + need;
 }
 
-int lrs_sru_deer_fwd(const void* z_f, const void* z_r, const void* z_x, const float* bias_f,
+static int sru_deer_fwd_impl(const void* z_f, const void* z_r, const void* z_x, const float* bias_f,
                      const float* bias_r, const float* v_f, const float* c0, const float* c_init,
                      void* h, float* c_states, float* c_last, int64_t T, int64_t B, int64_t D,
                      int io_dtype, float eps, int k_max, int* iters_out, float* deltas_out,
-                     int* converged_out, void* workspace, size_t workspace_bytes, void* stream) {
+                     int* converged_out, void* workspace, size_t workspace_bytes, void* stream,
+    const lrs::Opts& opt) {
   int64_t C, N;
   if (!shape_ok(B, D, T, &C, &N) || k_max < 1 || k_max > 1000000) return LRS_ERR_INVALID_ARG;
   if (io_dtype != LRS_F32 && io_dtype != LRS_BF16) return LRS_ERR_INVALID_ARG;
@@ -917,7 +920,7 @@ int lrs_sru_deer_fwd(const void* z_f, const void* z_r, const void* z_x, const fl
   }
   const size_t need = lrs_sru_deer_workspace_bytes(T, B, D, k_max);
   if (!workspace || workspace_bytes < need) return LRS_ERR_WORKSPACE;
-  const lrs::ColPlan p = lrs::plan_sru_deer(C, T, io_dtype);
+  const lrs::ColPlan p = lrs::plan_sru_deer(C, T, io_dtype, true, opt);
   if (!grid_ok(p.persist ? p.ncb : p.ncb * p.ntb, p.nw * 64)) return LRS_ERR_UNSUPPORTED;
 
   Carve cv(align_ptr(workspace));
@@ -946,16 +949,20 @@ int lrs_sru_deer_fwd(const void* z_f, const void* z_r, const void* z_x, const fl
   const int vec4 = (C % 4 == 0) && aligned(z_r, 4 * es) && aligned(z_x, 4 * es) &&
                    aligned(h, 4 * es) && aligned(c_states, 16);
 
-  if (p.persist && k_max <= lrs::kDeerFuseMax && deer_fuse_enabled()) {
+  if (p.persist && k_max <= lrs::kDeerFuseMax && deer_fuse_enabled(opt)) {
     // all iterations in one walk (see lrs_deer_solve); the pass must not
-    // overwrite a starting iterate held in c_states: a redo may need it
+    // overwrite a starting iterate held in c_states: a redo may need it.
+    // The walk holds one channel per lane (one workgroup per 64 channels), so
+    // its grid is checked on its own, and the element alignment checked
+    // above is all its full tiles need (vec = 1).
+    if (!grid_ok((C + 63) / 64, p.nw * 64)) return LRS_ERR_UNSUPPORTED;
     uint32_t* sets = cv.take<uint32_t>((int64_t)deer_fused_set_words(k_max));
     float* out = (c_init == c_states) ? ybuf : c_states;
     int rc = hip_status(lrs::launch_reset(nullptr, 0, nullptr, 0, sets,
                                           (int64_t)deer_fused_set_words(k_max), s));
     if (rc != LRS_OK) return rc;
     rc = hip_status(lrs::launch_sru_deer_fused(z_f, z_x, bias_f, v_f, c0, c_init, out, c_states,
-                                               T, C, D, io_dtype, p, vec, k_max, eps, sets,
+                                               T, C, D, io_dtype, p, 1, k_max, eps, sets,
                                                r.delta_out, r.rec, s));
     if (rc != LRS_OK) return rc;
     rc = hip_status(lrs::launch_sru_deer_out(z_r, z_x, bias_r, c_states, h, c_last, N, C, D,
@@ -1058,6 +1065,137 @@ int lrs_deer_stats(const void* workspace, size_t workspace_bytes, int k_max, int
   Carve cv(align_ptr(const_cast<void*>(workspace)));
   const DeerRecord r = carve_deer_record(cv, k_max);
   return read_deer_record(r, k_max, iters_out, deltas_out, converged_out, (hipStream_t)stream);
+}
+
+
+// ------------------------------------------------- plan overrides
+
+void lrs_options_default(lrs_options* opt) {
+  if (!opt) return;
+  opt->serial_fwd_max_t = -1;
+  opt->serial_bwd_max_t = -1;
+  opt->packed_max_t = -1;
+  opt->persist_min_blocks = -1;
+  opt->deer_fuse = -1;
+  opt->reserved = 0;
+}
+
+static lrs::Opts to_opts(const lrs_options* o) {
+  lrs::Opts r;
+  if (o) {
+    r.serial_fwd_max_t = o->serial_fwd_max_t;
+    r.serial_bwd_max_t = o->serial_bwd_max_t;
+    r.packed_max_t = o->packed_max_t;
+    r.persist_min_blocks = o->persist_min_blocks;
+    r.deer_fuse = o->deer_fuse;
+  }
+  return r;
+}
+
+int lrs_scan_fwd(const void* a, const void* b, const float* h0, void* h, int64_t B, int64_t D,
+                 int64_t T, int layout, int dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  return scan_fwd_impl(a, b, h0, h, B, D, T, layout, dtype, workspace, workspace_bytes, stream, lrs::Opts());
+}
+int lrs_scan_fwd_ex(const void* a, const void* b, const float* h0, void* h, int64_t B, int64_t D,
+                 int64_t T, int layout, int dtype, void* workspace, size_t workspace_bytes,
+                 void* stream,
+    const lrs_options* options) {
+  return scan_fwd_impl(a, b, h0, h, B, D, T, layout, dtype, workspace, workspace_bytes, stream, to_opts(options));
+}
+
+int lrs_scan_bwd(const void* a, const void* h, const float* h0, const void* grad_h, void* grad_a,
+                 void* grad_b, float* grad_h0, int64_t B, int64_t D, int64_t T, int layout,
+                 int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return scan_bwd_impl(a, h, h0, grad_h, grad_a, grad_b, grad_h0, B, D, T, layout, dtype, workspace, workspace_bytes, stream, lrs::Opts());
+}
+int lrs_scan_bwd_ex(const void* a, const void* h, const float* h0, const void* grad_h, void* grad_a,
+                 void* grad_b, float* grad_h0, int64_t B, int64_t D, int64_t T, int layout,
+                 int dtype, void* workspace, size_t workspace_bytes, void* stream,
+    const lrs_options* options) {
+  return scan_bwd_impl(a, h, h0, grad_h, grad_a, grad_b, grad_h0, B, D, T, layout, dtype, workspace, workspace_bytes, stream, to_opts(options));
+}
+
+int lrs_scan_fwd_bwd(const void* a, const void* b, const float* h0, const void* grad_h, void* h,
+                     void* grad_a, void* grad_b, float* grad_h0, int64_t B, int64_t D, int64_t T,
+                     int layout, int dtype, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return scan_fwd_bwd_impl(a, b, h0, grad_h, h, grad_a, grad_b, grad_h0, B, D, T, layout, dtype, workspace, workspace_bytes, stream, lrs::Opts());
+}
+int lrs_scan_fwd_bwd_ex(const void* a, const void* b, const float* h0, const void* grad_h, void* h,
+                     void* grad_a, void* grad_b, float* grad_h0, int64_t B, int64_t D, int64_t T,
+                     int layout, int dtype, void* workspace, size_t workspace_bytes,
+                     void* stream,
+    const lrs_options* options) {
+  return scan_fwd_bwd_impl(a, b, h0, grad_h, h, grad_a, grad_b, grad_h0, B, D, T, layout, dtype, workspace, workspace_bytes, stream, to_opts(options));
+}
+
+int lrs_sru_fwd(const void* z_f, const void* z_r, const void* z_x, const float* bias_f,
+                const float* bias_r, const float* c0, void* h, float* c_last, float* c_states,
+                int64_t T, int64_t B, int64_t D, int io_dtype, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  return sru_fwd_impl(z_f, z_r, z_x, bias_f, bias_r, c0, h, c_last, c_states, T, B, D, io_dtype, workspace, workspace_bytes, stream, lrs::Opts());
+}
+int lrs_sru_fwd_ex(const void* z_f, const void* z_r, const void* z_x, const float* bias_f,
+                const float* bias_r, const float* c0, void* h, float* c_last, float* c_states,
+                int64_t T, int64_t B, int64_t D, int io_dtype, void* workspace,
+                size_t workspace_bytes, void* stream,
+    const lrs_options* options) {
+  return sru_fwd_impl(z_f, z_r, z_x, bias_f, bias_r, c0, h, c_last, c_states, T, B, D, io_dtype, workspace, workspace_bytes, stream, to_opts(options));
+}
+
+int lrs_sru_deer_fwd(const void* z_f, const void* z_r, const void* z_x, const float* bias_f,
+                     const float* bias_r, const float* v_f, const float* c0, const float* c_init,
+                     void* h, float* c_states, float* c_last, int64_t T, int64_t B, int64_t D,
+                     int io_dtype, float eps, int k_max, int* iters_out, float* deltas_out,
+                     int* converged_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return sru_deer_fwd_impl(z_f, z_r, z_x, bias_f, bias_r, v_f, c0, c_init, h, c_states, c_last, T, B, D, io_dtype, eps, k_max, iters_out, deltas_out, converged_out, workspace, workspace_bytes, stream, lrs::Opts());
+}
+int lrs_sru_deer_fwd_ex(const void* z_f, const void* z_r, const void* z_x, const float* bias_f,
+                     const float* bias_r, const float* v_f, const float* c0, const float* c_init,
+                     void* h, float* c_states, float* c_last, int64_t T, int64_t B, int64_t D,
+                     int io_dtype, float eps, int k_max, int* iters_out, float* deltas_out,
+                     int* converged_out, void* workspace, size_t workspace_bytes, void* stream,
+    const lrs_options* options) {
+  return sru_deer_fwd_impl(z_f, z_r, z_x, bias_f, bias_r, v_f, c0, c_init, h, c_states, c_last, T, B, D, io_dtype, eps, k_max, iters_out, deltas_out, converged_out, workspace, workspace_bytes, stream, to_opts(options));
+}
+
+int lrs_deer_solve(const float* w, const float* u, const float* h0, const float* h_init, float* h,
+                   int64_t B, int64_t D, int64_t T, float eps, int k_max, int* iters_out,
+                   float* deltas_out, int* converged_out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return deer_solve_impl(w, u, h0, h_init, h, B, D, T, eps, k_max, iters_out, deltas_out, converged_out, workspace, workspace_bytes, stream, lrs::Opts());
+}
+int lrs_deer_solve_ex(const float* w, const float* u, const float* h0, const float* h_init, float* h,
+                   int64_t B, int64_t D, int64_t T, float eps, int k_max, int* iters_out,
+                   float* deltas_out, int* converged_out, void* workspace,
+                   size_t workspace_bytes, void* stream,
+    const lrs_options* options) {
+  return deer_solve_impl(w, u, h0, h_init, h, B, D, T, eps, k_max, iters_out, deltas_out, converged_out, workspace, workspace_bytes, stream, to_opts(options));
+}
+
+int lrs_deer_solve_seq(const float* w, const float* u, const float* h0, const float* h_init,
+                       float* h, int64_t B, int64_t D, int64_t T, float eps, int k_max,
+                       int* iters_out, int* converged_out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return deer_solve_seq_impl(w, u, h0, h_init, h, B, D, T, eps, k_max, iters_out, converged_out, workspace, workspace_bytes, stream, lrs::Opts());
+}
+int lrs_deer_solve_seq_ex(const float* w, const float* u, const float* h0, const float* h_init,
+                       float* h, int64_t B, int64_t D, int64_t T, float eps, int k_max,
+                       int* iters_out, int* converged_out, void* workspace,
+                       size_t workspace_bytes, void* stream,
+    const lrs_options* options) {
+  return deer_solve_seq_impl(w, u, h0, h_init, h, B, D, T, eps, k_max, iters_out, converged_out, workspace, workspace_bytes, stream, to_opts(options));
+}
+
+// ------------------------------------------------- DEER tolerance schedule
+
+float lrs_deer_eps_schedule(int64_t step, int64_t total_steps, float early, float late) {
+  if (!(early > 0.0f) || !(late > 0.0f) || !isfinite(early) || !isfinite(late)) return NAN;
+  if (total_steps <= 1) return late;
+  double frac = (double)step / (double)(total_steps - 1);
+  frac = frac < 0.0 ? 0.0 : (frac > 1.0 ? 1.0 : frac);
+  return (float)((double)early * pow((double)late / (double)early, frac));
 }
 
 }  // extern "C"

@@ -14,6 +14,16 @@ namespace lrs {
 // that e.g. a backward pass finds part of the forward pass's data in cache.
 constexpr int64_t kStreamFootprint = (int64_t)512 << 20;
 
+// Plan overrides of one call (the C ABI's lrs_options); a negative field
+// keeps the measured default.
+struct Opts {
+  int64_t serial_fwd_max_t = -1;    // one lane per channel for T <= this ([B,D,T] forward)
+  int64_t serial_bwd_max_t = -1;    // the same for the backward
+  int64_t packed_max_t = -1;        // whole channels packed per workgroup for T <= this
+  int64_t persist_min_blocks = -1;  // [T,B,D] layers: persistent walk from this many blocks
+  int deer_fuse = -1;               // 0: one launch per Newton iteration
+};
+
 // Time-contiguous kernels: chunks of nw waves x r rows x 256 steps, nchunk
 // chunks per channel.
 struct RowPlan {
@@ -27,8 +37,8 @@ struct RowPlan {
   int threads() const { return nw * 64; }
   int64_t chunk() const { return (int64_t)nw * r * 256; }
 };
-RowPlan plan_scan_fwd_rows(int64_t C, int64_t T);
-RowPlan plan_scan_bwd_rows(int64_t C, int64_t T);
+RowPlan plan_scan_fwd_rows(int64_t C, int64_t T, const Opts& o = Opts());
+RowPlan plan_scan_bwd_rows(int64_t C, int64_t T, const Opts& o = Opts());
 RowPlan plan_deer_rows(int64_t C, int64_t T);
 RowPlan plan_scan_fused_rows(int64_t C, int64_t T);
 RowPlan plan_deer_bwd_rows(int64_t C, int64_t T);
@@ -43,13 +53,14 @@ struct ColPlan {
 // Compute units of the current device (cached per device).
 int device_cus();
 // Channel blocks from which the [T,B,D] layer kernels run persistent
-// (device_cus(), or the LRS_PERSIST_MIN_BLOCKS override).
-int64_t persist_min_blocks();
+// (device_cus(), or the caller's override).
+int64_t persist_min_blocks(const Opts& o = Opts());
 ColPlan plan_cols(int64_t C, int64_t T, int nw, int l, int cpt);
 ColPlan plan_scan_fwd_tbd(int64_t C, int64_t T);
 ColPlan plan_scan_bwd_tbd(int64_t C, int64_t T);
 // allow_persist = false: the look-back tile plan (workspace queries size for it).
-ColPlan plan_sru(int64_t C, int64_t T, int io_dtype, bool allow_persist = true);
+ColPlan plan_sru(int64_t C, int64_t T, int io_dtype, bool allow_persist = true,
+                 const Opts& o = Opts());
 int64_t col_status_words(const ColPlan& p);
 
 // Resets look-back state: status words to "not ready", tickets and the
@@ -180,7 +191,8 @@ hipError_t launch_lstm_bwd(const void* zf, const void* zi, const void* zc, const
                            unsigned* tickets, hipStream_t stream);
 
 // SRU with v_f * c_{t-1} in the forget gate, by DEER (sru_deer.hip).
-ColPlan plan_sru_deer(int64_t C, int64_t T, int io_dtype, bool allow_persist = true);
+ColPlan plan_sru_deer(int64_t C, int64_t T, int io_dtype, bool allow_persist = true,
+                      const Opts& o = Opts());
 hipError_t launch_sru_deer_iter(const void* zf, const void* zx, const float* bias_f,
                                 const float* v_f, const float* c0, const float* y, float* yn,
                                 int64_t T, int64_t C, int64_t D, int io_dtype, const ColPlan& p,

@@ -27,8 +27,6 @@
 //   k_scan_fused_bdt: both of the above in one pass for channels that fit one
 //                    workgroup (h kept in registers between the two scans)
 //   k_deer_iter    : one fused DEER Newton iteration for h_t = tanh(w h_{t-1}+u_t)
-#include <stdlib.h>
-
 #include <algorithm>
 
 #include "lrs_device.hpp"
@@ -71,21 +69,20 @@ __device__ __forceinline__ void block_combine(float WA, float WB, BlockShared<NW
 }
 
 // State entering logical chunk c of a channel.  Single-chunk channels use x0
-// directly; otherwise wave 0 publishes this chunk's aggregate, looks back over
-// up to 64 predecessors per poll, publishes the inclusive state and shares the
-// carry through LDS.
+// directly; otherwise wave 0 publishes this chunk's aggregate (or, for the
+// last chunk of a 64-chunk group, its inclusive state once known), resolves
+// the carry by the fixed-order group rule of lookback_group_wave and shares
+// it through LDS.
 template <int NW>
 __device__ __forceinline__ float chunk_carry(bool multi, int c, float TA, float TB, float x0,
                                              uint64_t* st, BlockShared<NW>& s) {
   if (!multi) return x0;
   if (threadIdx.x < kWave) {
-    float x_in = x0;
-    if (c > 0) {
-      if (threadIdx.x == 0) status_store(st + c, pack_agg(TA, TB));
-      x_in = lookback_carry_wave(st, c, 1);
-    }
+    const bool gend = group_end(c, kWaveGroup);
+    if (!gend && threadIdx.x == 0) status_store(st + c, pack_agg(TA, TB));
+    const float x_in = lookback_group_wave(st, c, 1, x0);
     if (threadIdx.x == 0) {
-      status_store(st + c, pack_inc(__builtin_fmaf(TA, x_in, TB)));
+      if (gend) status_store(st + c, pack_inc(__builtin_fmaf(TA, x_in, TB)));
       s.carry = x_in;
     }
   }
@@ -1448,21 +1445,14 @@ RowPlan pick(int64_t T, const Shape (&single)[N], Shape multi) {
 // peak forward and 62-69% backward for every T up to 2048, against 3-43% /
 // 4-53% for one channel per workgroup below T = 128 (T = 64: 31 vs 58 us
 // forward, 63 vs 79 us backward; at T = 128 both forms are within 4%); the
-// sequential kernels (one lane per channel) only beat them at T <= 4.
-// LRS_SERIAL_FWD_MAX_T, LRS_SERIAL_BWD_MAX_T and LRS_PACKED_MAX_T override
-// the limits (read at every call, e.g. 0 = never).
+// sequential kernels (one lane per channel) only beat them at T <= 4.  The
+// caller's options may move both limits (e.g. 0 = never).
 constexpr int64_t kSerialFwdMaxT = 4;
 constexpr int64_t kSerialBwdMaxT = 4;
 constexpr int64_t kPackedMaxT = 64;
 constexpr int64_t kPackedSteps = 2048;  // 8 waves x 1 row of 256 steps
 
-static int64_t env_max_t(const char* name, int64_t dflt) {
-  const char* v = getenv(name);
-  if (!v || !*v) return dflt;
-  char* end = nullptr;
-  const long long x = strtoll(v, &end, 10);
-  return (end && *end == '\0') ? (int64_t)x : dflt;
-}
+static int64_t limit_or(int64_t v, int64_t dflt) { return v >= 0 ? v : dflt; }
 
 // Channels per packed workgroup: as many as fit, a multiple that keeps every
 // block 16-byte aligned (k*T divisible by 4); 0 if none fits.
@@ -1474,9 +1464,9 @@ static int packed_channels(int64_t T) {
   return (int)k;
 }
 
-static void plan_short(RowPlan& p, int64_t T, const char* serial_env, int64_t serial_dflt) {
-  p.serial = T <= env_max_t(serial_env, serial_dflt);
-  if (!p.serial && T <= env_max_t("LRS_PACKED_MAX_T", kPackedMaxT)) p.packed = packed_channels(T);
+static void plan_short(RowPlan& p, int64_t T, int64_t serial_max, int64_t packed_max) {
+  p.serial = T <= serial_max;
+  if (!p.serial && T <= packed_max) p.packed = packed_channels(T);
   if (p.serial || p.packed) {
     p.nchunk = 1;
     p.nw = 8;
@@ -1484,17 +1474,19 @@ static void plan_short(RowPlan& p, int64_t T, const char* serial_env, int64_t se
   }
 }
 
-RowPlan plan_scan_fwd_rows(int64_t C, int64_t T) {
+RowPlan plan_scan_fwd_rows(int64_t C, int64_t T, const Opts& o) {
   RowPlan p = pick(T, kScanSingle, kScanFwdMulti);
   p.stream = 3 * C * T * 4 >= kStreamFootprint;  // a, b, h
-  plan_short(p, T, "LRS_SERIAL_FWD_MAX_T", kSerialFwdMaxT);
+  plan_short(p, T, limit_or(o.serial_fwd_max_t, kSerialFwdMaxT),
+             limit_or(o.packed_max_t, kPackedMaxT));
   return p;
 }
 
-RowPlan plan_scan_bwd_rows(int64_t C, int64_t T) {
+RowPlan plan_scan_bwd_rows(int64_t C, int64_t T, const Opts& o) {
   RowPlan p = pick(T, kScanSingle, kScanBwdMulti);
   p.stream = 5 * C * T * 4 >= kStreamFootprint;  // a, h, g, grad_a, grad_b
-  plan_short(p, T, "LRS_SERIAL_BWD_MAX_T", kSerialBwdMaxT);
+  plan_short(p, T, limit_or(o.serial_bwd_max_t, kSerialBwdMaxT),
+             limit_or(o.packed_max_t, kPackedMaxT));
   return p;
 }
 

@@ -737,16 +737,9 @@ ColPlan plan_cols(int64_t C, int64_t T, int nw, int l, int cpt) {
 }
 
 // Channel blocks needed for the persistent kernels: the device's compute
-// units, or LRS_PERSIST_MIN_BLOCKS (read at every call; e.g. 0 = always,
-// a huge value = never).
-int64_t persist_min_blocks() {
-  const char* v = getenv("LRS_PERSIST_MIN_BLOCKS");
-  if (v && *v) {
-    char* end = nullptr;
-    const long long x = strtoll(v, &end, 10);
-    if (end && *end == '\0') return (int64_t)x;
-  }
-  return device_cus();
+// units, or the caller's override (0 = always, a huge value = never).
+int64_t persist_min_blocks(const Opts& o) {
+  return o.persist_min_blocks >= 0 ? o.persist_min_blocks : device_cus();
 }
 
 int64_t col_status_words(const ColPlan& p) {
@@ -779,11 +772,11 @@ ColPlan plan_sru_bwd(int64_t C, int64_t T, int io_dtype) {
   p.stream = C * T * (7 * (io_dtype == 1 ? 2 : 4) + 4) >= kStreamFootprint;
   return p;
 }
-ColPlan plan_sru(int64_t C, int64_t T, int io_dtype, bool allow_persist) {
+ColPlan plan_sru(int64_t C, int64_t T, int io_dtype, bool allow_persist, const Opts& o) {
   ColPlan p = io_dtype == 1 ? plan_cols(C, T, kSruNW, kSruL, kSruCPT)
                             : plan_cols(C, T, kSruF32NW, kSruF32L, kSruF32CPT);
   const int64_t ncb_p = (C + kWave * kSruPCPT - 1) / (kWave * kSruPCPT);
-  if (allow_persist && ncb_p >= persist_min_blocks()) {  // the channel blocks alone fill the GPU
+  if (allow_persist && ncb_p >= persist_min_blocks(o)) {  // the channel blocks alone fill the GPU
     p = plan_cols(C, T, kSruPNW, kSruPL, kSruPCPT);
     p.persist = true;
   }

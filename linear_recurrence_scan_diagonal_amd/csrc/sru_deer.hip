@@ -698,9 +698,9 @@ constexpr int kSdNW = 8, kSdL = 8, kSdCPT = 2;
 constexpr int kSdPNW = 8, kSdPL16 = 16, kSdPL32 = 8, kSdPCPT = 2;
 }
 
-ColPlan plan_sru_deer(int64_t C, int64_t T, int io_dtype, bool allow_persist) {
+ColPlan plan_sru_deer(int64_t C, int64_t T, int io_dtype, bool allow_persist, const Opts& o) {
   ColPlan p = plan_cols(C, T, kSdNW, kSdL, kSdCPT);
-  if (allow_persist && p.ncb >= persist_min_blocks()) {  // the channel blocks alone fill the GPU
+  if (allow_persist && p.ncb >= persist_min_blocks(o)) {  // the channel blocks alone fill the GPU
     p = plan_cols(C, T, kSdPNW, io_dtype == 1 ? kSdPL16 : kSdPL32, kSdPCPT);
     p.persist = true;
   }

@@ -29,3 +29,16 @@ def oracle_mod():
     import oracle
     oracle.build(force=False)
     return oracle
+
+
+@pytest.fixture
+def plan():
+    """plan(**fields): from here to the end of the test, library calls made
+    without explicit options pass these lrs_options fields (see
+    binding.plan_options); later calls override earlier fields."""
+    import contextlib
+    import linear_recurrence_scan_diagonal_amd as lrs
+    with contextlib.ExitStack() as stack:
+        def set_fields(**fields):
+            stack.enter_context(lrs.plan_options(**fields))
+        yield set_fields

@@ -37,7 +37,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 31, names
     raw = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(raw, n), f"{n} declared in lrs.h but not exported"
@@ -228,11 +228,54 @@ def test_product_path_has_no_fallback():
 
 
 def test_deer_eps_schedule():
-    """Log-linear from the loose to the tight tolerance over training."""
+    """Log-linear from the loose to the tight tolerance over training, computed
+    by the library (lrs_deer_eps_schedule), clamped outside the run, NaN for
+    tolerances that are not positive and finite."""
+    import math
     from linear_recurrence_scan_diagonal_amd import binding as b
-    assert b.deer_eps_schedule(0, 101) == pytest.approx(1e-4)
-    assert b.deer_eps_schedule(100, 101) == pytest.approx(1e-6)
-    assert b.deer_eps_schedule(50, 101) == pytest.approx(1e-5)
+    assert b.deer_eps_schedule(0, 101) == pytest.approx(1e-4, rel=1e-6)
+    assert b.deer_eps_schedule(100, 101) == pytest.approx(1e-6, rel=1e-6)
+    assert b.deer_eps_schedule(50, 101) == pytest.approx(1e-5, rel=1e-6)
     vals = [b.deer_eps_schedule(i, 11) for i in range(11)]
     assert all(x > y for x, y in zip(vals, vals[1:]))
-    assert b.deer_eps_schedule(5, 1) == 1e-6 and b.deer_eps_schedule(500, 101) == pytest.approx(1e-6)
+    # each step multiplies by the same factor (late/early)^(1/10)
+    ratios = [y / x for x, y in zip(vals, vals[1:])]
+    assert all(r == pytest.approx(0.01 ** 0.1, rel=1e-6) for r in ratios)
+    assert b.deer_eps_schedule(5, 1) == pytest.approx(1e-6, rel=1e-6)
+    assert b.deer_eps_schedule(500, 101) == pytest.approx(1e-6, rel=1e-6)
+    assert b.deer_eps_schedule(-3, 101) == pytest.approx(1e-4, rel=1e-6)
+    assert b.deer_eps_schedule(3, 7, early=2e-3, late=2e-3) == pytest.approx(2e-3, rel=1e-6)
+    assert math.isnan(b.deer_eps_schedule(3, 7, early=0.0, late=1e-6))
+    assert math.isnan(b.deer_eps_schedule(3, 7, early=1e-4, late=-1.0))
+    assert math.isnan(b.deer_eps_schedule(3, 7, early=float("inf"), late=1e-6))
+
+
+def test_options_struct_and_ex_validation(lib):
+    """lrs_options_default sets every field to -1 (reserved 0); the _ex entry
+    points validate exactly as the plain ones, with or without options."""
+    from linear_recurrence_scan_diagonal_amd import binding as b
+    assert ctypes.sizeof(b.LrsOptions) == 40
+    o = b.LrsOptions()
+    o.reserved = 99
+    lib.lrs_options_default(ctypes.byref(o))
+    assert (o.serial_fwd_max_t, o.serial_bwd_max_t, o.packed_max_t, o.persist_min_blocks,
+            o.deer_fuse, o.reserved) == (-1, -1, -1, -1, -1, 0)
+    lib.lrs_options_default(None)  # a no-op
+    null = None
+    p = ctypes.c_void_p(1 << 20)
+    for opt in (None, ctypes.byref(o)):
+        assert lib.lrs_scan_fwd_ex(null, p, null, p, 1, 1, 8, 0, 0, null, 0, null,
+                                   opt) == b.LRS_ERR_INVALID_ARG
+        assert lib.lrs_scan_bwd_ex(p, p, null, p, p, p, null, 1, 1, -8, 0, 0, null, 0, null,
+                                   opt) == b.LRS_ERR_INVALID_ARG
+        assert lib.lrs_scan_fwd_bwd_ex(p, p, null, p, p, p, p, null, 1, 1, 8, 5, 0, null, 0, null,
+                                       opt) == b.LRS_ERR_INVALID_ARG
+        assert lib.lrs_sru_fwd_ex(p, null, p, p, p, null, p, null, null, 4, 1, 8, 1, null, 0,
+                                  null, opt) == b.LRS_ERR_INVALID_ARG
+        assert lib.lrs_deer_solve_ex(p, p, null, null, p, 1, 1, 8, ctypes.c_float(1e-5), 0, None,
+                                     None, None, null, 0, null, opt) == b.LRS_ERR_INVALID_ARG
+        assert lib.lrs_deer_solve_seq_ex(p, null, null, null, p, 2, 1, 4, ctypes.c_float(1e-5), 5,
+                                         None, None, null, 0, null, opt) == b.LRS_ERR_INVALID_ARG
+        assert lib.lrs_sru_deer_fwd_ex(p, p, p, p, p, p, null, null, p, p, null, 4, 1, 8, 9,
+                                       ctypes.c_float(1e-5), 5, None, None, None, null, 0, null,
+                                       opt) == b.LRS_ERR_INVALID_ARG

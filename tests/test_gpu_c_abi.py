@@ -1,16 +1,22 @@
 """The C ABI from plain C: tests/c_abi_driver (built by __graft_entry__.build())
-allocates with hipMalloc, creates its own stream, sizes the workspace with
-lrs_scan_workspace_bytes, checks that bad arguments and a missing workspace
-are rejected, and runs lrs_scan_fwd + lrs_scan_bwd; its outputs must match the
-fp64 oracle to the fp32 bar.  One shape fits a workgroup per channel, the other
-spans several look-back chunks (and so needs the workspace)."""
+allocates with hipMalloc, creates its own stream, sizes each workspace with its
+query, checks that bad arguments and a missing or short workspace are
+rejected, and runs
+  * lrs_scan_fwd + lrs_scan_bwd (and lrs_scan_fwd_ex with default options,
+    which must give the same bits), one shape that fits a workgroup per
+    channel and one that spans several look-back chunks;
+  * lrs_sru_fwd with bf16 I/O on a [T,B,D] layer;
+  * lrs_deer_solve with its host record, and lrs_deer_eps_schedule;
+every output against the fp64 oracle to its bar (1e-5 fp32, 2e-2 bf16)."""
 import os
 import subprocess
 
 import numpy as np
 import pytest
 
+import oracle
 from linear_recurrence_scan_diagonal_amd import inputs as I
+from conftest import relerr
 from gpu_util import log
 from test_gpu_scan import compare, oracle_scan
 
@@ -20,24 +26,72 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 DRIVER = os.path.join(ROOT, "tests", "c_abi_driver")
 
 
-@pytest.mark.parametrize("B,D,T", [(2, 3, 1000), (1, 3, 20000)])
-def test_c_driver_matches_oracle(tmp_path, B, D, T):
+def drive(mode, dims, tmp_path, payload):
     assert os.path.exists(DRIVER), "tests/c_abi_driver is not built; run __graft_entry__.build()"
+    src, dst = tmp_path / "in.bin", tmp_path / "out.bin"
+    with open(src, "wb") as f:
+        for arr in payload:
+            f.write(np.ascontiguousarray(arr).tobytes())
+    log(f"c_abi_driver {mode} {dims}")
+    res = subprocess.run([DRIVER, mode, *map(str, dims), str(src), str(dst)],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stderr
+    return dst
+
+
+@pytest.mark.parametrize("B,D,T", [(2, 3, 1000), (1, 3, 20000)])
+def test_c_driver_scan_matches_oracle(tmp_path, B, D, T):
     w = I.scaled(I.WORKLOADS["scan_fwd_bwd"], B=B, D=D, T=T, seed=15000 + T)
     x = I.scan_inputs(w)
     C = B * D
-    src, dst = tmp_path / "in.bin", tmp_path / "out.bin"
-    with open(src, "wb") as f:
-        for k in ("a", "b", "g"):
-            f.write(np.ascontiguousarray(x[k], dtype=np.float32).tobytes())
-        f.write(np.ascontiguousarray(x["h0"], dtype=np.float32).tobytes())
-    log(f"c_abi_driver {B} {D} {T}")
-    res = subprocess.run([DRIVER, str(B), str(D), str(T), str(src), str(dst)],
-                         capture_output=True, text=True, timeout=120)
-    assert res.returncode == 0, res.stderr
+    dst = drive("scan", (B, D, T), tmp_path,
+                [x[k].astype(np.float32) for k in ("a", "b", "g", "h0")])
     out = np.fromfile(dst, dtype=np.float32)
     assert out.size == 3 * C * T + C
     n = C * T
     got = {"h": out[:n].reshape(C, T), "da": out[n:2 * n].reshape(C, T),
            "db": out[2 * n:3 * n].reshape(C, T), "dh0": out[3 * n:]}
-    compare(got, oracle_scan(x), tag=f"c driver {B}x{D}x{T}")
+    compare(got, oracle_scan(x), tag=f"c driver scan {B}x{D}x{T}")
+
+
+def test_c_driver_sru_matches_oracle(tmp_path):
+    T, B, D = 300, 2, 96
+    w = I.scaled(I.WORKLOADS["sru_fwd"], B=B, D=D, T=T, seed=15100)
+    s = I.sru_inputs(w)
+    dst = drive("sru", (T, B, D), tmp_path,
+                [s["zf"], s["zr"], s["zx"], s["bias_f"], s["bias_r"]])
+    raw = np.fromfile(dst, dtype=np.uint8)
+    n = T * B * D
+    h = I.bf16_bits_to_f64(raw[:2 * n].view(np.uint16)).reshape(T, B, D)
+    c_last = raw[2 * n:].view(np.float32).reshape(B, D)
+    ref_h, ref_c = oracle.sru_fwd(*(I.bf16_bits_to_f64(s[k]) for k in ("zf", "zr", "zx")),
+                                  s["bias_f"], s["bias_r"])
+    eh, ec = relerr(h, ref_h), relerr(c_last, ref_c)
+    log(f"c driver sru: h={eh:.2e} c_last={ec:.2e}")
+    assert eh <= 2e-2 and ec <= 1e-5
+
+
+def test_c_driver_deer_matches_oracle(tmp_path):
+    B, D, T = 2, 24, 3000
+    w = I.scaled(I.WORKLOADS["deer"], B=B, D=D, T=T, seed=15200)
+    x = I.deer_inputs(w)
+    x["h0"] = np.random.default_rng(15200).normal(0, 0.5, B * D).astype(np.float32)
+    dst = drive("deer", (B, D, T), tmp_path, [x["w"], x["u"], x["h0"]])
+    raw = np.fromfile(dst, dtype=np.uint8)
+    n = B * D * T
+    h = raw[:4 * n].view(np.float32).reshape(B, D, T)
+    iters, conv = (int(v) for v in raw[4 * n:4 * n + 8].view(np.int32))
+    deltas = raw[4 * n + 8:4 * n + 28].view(np.float32)
+    sched = raw[4 * n + 28:4 * n + 48].view(np.float32)
+    ref_h, ref_it, ref_d = oracle.deer(x["w"], x["u"].reshape(B, D, T), x["h0"].reshape(B, D),
+                                       eps=1e-5, k_max=5)
+    e = relerr(h, ref_h)
+    log(f"c driver deer: iters {iters} (oracle {ref_it}) converged {conv} h={e:.2e} "
+        f"deltas {deltas[:iters]} vs {np.asarray(ref_d)[:ref_it]}")
+    assert iters == ref_it and e <= 1e-5
+    assert conv == (1 if ref_d[ref_it - 1] < 1e-5 else 0)
+    for i in range(iters):
+        assert abs(deltas[i] - ref_d[i]) <= 1e-5 * (1 + abs(ref_d[i]))
+    # the schedule: log-linear from 1e-4 at step 0 to 1e-6 at step 4
+    want = 1e-4 * (1e-6 / 1e-4) ** (np.arange(5) / 4)
+    assert np.allclose(sched, want, rtol=1e-6)

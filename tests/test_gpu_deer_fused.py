@@ -1,6 +1,6 @@
 """The fused DEER solve (all Newton iterations in one walk over each channel,
 used for channels one workgroup walks and K_max <= 8) against the fp64 oracle
-and against the one-launch-per-iteration path (LRS_DEER_FUSE=0) on the same
+and against the one-launch-per-iteration path (plan option deer_fuse = 0) on the same
 inputs: the full B=16 D=512 T=8192 shape, ragged and unaligned lengths,
 h0 given, K_max = 1 and 8, and early stops (a large eps, a warm start near the
 solution, the warm start held in h itself), where the pass's K_max iterations
@@ -28,10 +28,10 @@ def solve(x, B, D, T, eps, k_max, h_init=None, in_place=False):
     return h.cpu().numpy(), info
 
 
-def both_paths(monkeypatch, x, B, D, T, eps, k_max, h_init=None, in_place=False):
+def both_paths(plan, x, B, D, T, eps, k_max, h_init=None, in_place=False):
     out = {}
     for mode, flag in (("fused", "1"), ("per-iteration", "0")):
-        monkeypatch.setenv("LRS_DEER_FUSE", flag)
+        plan(deer_fuse=int(flag))
         out[mode] = solve(x, B, D, T, eps, k_max, h_init, in_place)
     return out
 
@@ -52,7 +52,7 @@ def both_paths(monkeypatch, x, B, D, T, eps, k_max, h_init=None, in_place=False)
     (2, 3, 2049, 1e-5, 5, True, True, False),        # first of 8 steps per lane, partial
     (2, 3, 4097, 1e-5, 5, True, False, False),       # second sub-chunk of one step
 ])
-def test_fused_matches_oracle_and_per_iteration(monkeypatch, B, D, T, eps, k_max, h0, warm,
+def test_fused_matches_oracle_and_per_iteration(plan, B, D, T, eps, k_max, h0, warm,
                                                 in_place):
     w = I.scaled(I.WORKLOADS["deer"], B=B, D=D, T=T, seed=16000 + B * 31 + D * 7 + T + k_max)
     x = I.deer_inputs(w)
@@ -65,7 +65,7 @@ def test_fused_matches_oracle_and_per_iteration(monkeypatch, B, D, T, eps, k_max
         h_init = oracle.rnn_seq(x["w"], u + pert, x["h0"].reshape(B, D)).astype(np.float32)
     ref_h, ref_it, ref_d = oracle.deer(x["w"], u, x["h0"].reshape(B, D), h_init, eps=eps,
                                        k_max=k_max)
-    got = both_paths(monkeypatch, x, B, D, T, eps, k_max, h_init, in_place)
+    got = both_paths(plan, x, B, D, T, eps, k_max, h_init, in_place)
     tag = f"deer fused {B}x{D}x{T} eps={eps} k_max={k_max} h0={h0} warm={warm} in_place={in_place}"
     (hf, inf_), (hp, inp) = got["fused"], got["per-iteration"]
     ef, ep, efp = relerr(hf, ref_h), relerr(hp, ref_h), relerr(hf, hp)
@@ -80,10 +80,10 @@ def test_fused_matches_oracle_and_per_iteration(monkeypatch, B, D, T, eps, k_max
         assert abs(df - do) <= 1e-5 + 1e-3 * do and abs(df - dp) <= 1e-6 + 1e-4 * dp
 
 
-def test_fused_async_and_repeat(monkeypatch):
+def test_fused_async_and_repeat(plan):
     """The asynchronous form gives the same iterate and record, and repeated
     solves into the same workspace agree bit for bit."""
-    monkeypatch.setenv("LRS_DEER_FUSE", "1")
+    plan(deer_fuse=1)
     B, D, T = 4, 64, 8192
     x = I.deer_inputs(I.scaled(I.WORKLOADS["deer"], B=B, D=D, T=T, seed=16500))
     w = torch.from_numpy(x["w"]).to(DEV)
@@ -102,7 +102,7 @@ def test_fused_async_and_repeat(monkeypatch):
 
 
 # SRU whose forget gate reads v_f * c_{t-1}: the fused persistent walk (forced
-# with LRS_PERSIST_MIN_BLOCKS=0) against the oracle and the per-iteration path.
+# with the plan option persist_min_blocks = 0) against the oracle and the per-iteration path.
 @pytest.mark.parametrize("B,D,T,io,eps,k_max,warm,in_place", [
     (2, 64, 1000, "bf16", 1e-5, 5, False, False),
     (1, 258, 513, "f32", 1e-5, 8, False, False),     # partial channel block, ragged tiles
@@ -111,10 +111,10 @@ def test_fused_async_and_repeat(monkeypatch):
     (2, 64, 900, "bf16", 1e-5, 6, True, False),      # warm start
     (2, 64, 900, "f32", 1e-5, 6, True, True),        # warm start held in c_states
 ])
-def test_sru_deer_fused_matches_oracle_and_per_iteration(monkeypatch, B, D, T, io, eps, k_max,
+def test_sru_deer_fused_matches_oracle_and_per_iteration(plan, B, D, T, io, eps, k_max,
                                                           warm, in_place):
     from test_gpu_sru_nl import setup
-    monkeypatch.setenv("LRS_PERSIST_MIN_BLOCKS", "0")
+    plan(persist_min_blocks=0)
     w = I.scaled(I.WORKLOADS["sru_deer"], B=B, D=D, T=T, seed=16800 + B * 13 + D + T + k_max)
     z, z64, p, pd = setup(w, io)
     c0 = np.random.default_rng(T).normal(0, 0.5, (B, D)).astype(np.float32)
@@ -128,7 +128,7 @@ def test_sru_deer_fused_matches_oracle_and_per_iteration(monkeypatch, B, D, T, i
                                      c0=c0, c_init=c_init, eps=eps, k_max=k_max)
     got = {}
     for mode, flag in (("fused", "1"), ("per-iteration", "0")):
-        monkeypatch.setenv("LRS_DEER_FUSE", flag)
+        plan(deer_fuse=int(flag))
         ci = None if c_init is None else torch.from_numpy(c_init).to(DEV)
         h, cs, cl, info = lrs.sru_deer_fwd(z["zf"], z["zr"], z["zx"], pd["bf"], pd["br"],
                                            pd["vf"], torch.from_numpy(c0).to(DEV), ci, eps=eps,
@@ -158,7 +158,7 @@ def test_sru_deer_fused_matches_oracle_and_per_iteration(monkeypatch, B, D, T, i
                                                  (3, 64, 4096, False, False),
                                                  (2, 40, 8000, True, False),
                                                  (4, 8, 6000, True, True)])
-def test_per_sequence_fused(monkeypatch, B, D, T, warm, in_place):
+def test_per_sequence_fused(plan, B, D, T, warm, in_place):
     from test_gpu_deer_seq import make
     scales = [0.05, 1.0, 3.0, 0.5][:B]
     w, u, h0 = make(B, D, T, 17000 + T, scales)
@@ -171,7 +171,7 @@ def test_per_sequence_fused(monkeypatch, B, D, T, warm, in_place):
                        eps=eps, k_max=k_max) for b in range(B)]
     got = {}
     for mode, flag in (("fused", "1"), ("per-iteration", "0")):
-        monkeypatch.setenv("LRS_DEER_FUSE", flag)
+        plan(deer_fuse=int(flag))
         hi = None if h_init is None else torch.from_numpy(h_init).to(DEV)
         h, iters, conv = lrs.deer_solve_seq(torch.from_numpy(w).to(DEV),
                                             torch.from_numpy(u).to(DEV),
@@ -189,8 +189,8 @@ def test_per_sequence_fused(monkeypatch, B, D, T, warm, in_place):
         assert relerr(hf[b:b + 1], hp[b:b + 1]) <= 1e-5
 
 
-def test_per_sequence_fused_async(monkeypatch):
-    monkeypatch.setenv("LRS_DEER_FUSE", "1")
+def test_per_sequence_fused_async(plan):
+    plan(deer_fuse=1)
     from test_gpu_deer_seq import make
     w, u, h0 = make(3, 16, 3000, 17500, [0.05, 1.0, 3.0])
     wd, ud, h0d = (torch.from_numpy(v).to(DEV) for v in (w, u, h0))

@@ -54,7 +54,7 @@ def test_async_matches_sync():
     assert torch.equal(h1, h2)
 
 
-def test_uniform_sequences_match_global_solve(monkeypatch):
+def test_uniform_sequences_match_global_solve(plan):
     """When every sequence needs the same iterations the result is the global
     solve's: bit for bit between like paths (fused pass against fused pass,
     one launch per iteration against the same), and within the parity bar
@@ -64,7 +64,7 @@ def test_uniform_sequences_match_global_solve(monkeypatch):
     wd, ud, h0d = (torch.from_numpy(v).to(DEV) for v in (w, u, h0))
     hs_f, its_f, _ = lrs.deer_solve_seq(wd, ud, h0d, k_max=8)
     hg_f, info_f = lrs.deer_solve(wd, ud, h0d, k_max=8)
-    monkeypatch.setenv("LRS_DEER_FUSE", "0")
+    plan(deer_fuse=0)
     hs_u, its_u, _ = lrs.deer_solve_seq(wd, ud, h0d, k_max=8)
     hg_u, info_u = lrs.deer_solve(wd, ud, h0d, k_max=8)
     torch.cuda.synchronize()

@@ -1,7 +1,7 @@
 """The persistent [T,B,D] kernels (one workgroup per channel block walking
 all time tiles, chosen when the channel blocks fill the GPU): the SRU forward
 and the SRU-by-DEER iteration, against the fp64 oracle, forced through
-LRS_PERSIST_MIN_BLOCKS on ragged shapes (partial last tile in time, partial
+the persist_min_blocks plan option on ragged shapes (partial last tile in time, partial
 last channel block, both I/O types, c0, saved cell states and c_T), and at the
 full B=32 D=1024 T=2048 shape both ways, where the two kernel families must
 agree within the parity bar; with persistence forced, the SRU and SRU-by-DEER
@@ -39,8 +39,8 @@ def sru_run(w, io, c0=None):
 @pytest.mark.parametrize("B,D,T", [(1, 1, 1), (2, 3, 65), (3, 50, 200), (1, 258, 513),
                                    (2, 128, 1000), (1, 300, 64)])
 @pytest.mark.parametrize("io", ["bf16", "f32"])
-def test_sru_persistent_ragged(monkeypatch, B, D, T, io):
-    monkeypatch.setenv("LRS_PERSIST_MIN_BLOCKS", "0")
+def test_sru_persistent_ragged(plan, B, D, T, io):
+    plan(persist_min_blocks=0)
     w = I.scaled(I.WORKLOADS["sru_fwd"], B=B, D=D, T=T, seed=13000 + B * 7 + D + T)
     c0 = np.random.default_rng(T).normal(size=(B, D)).astype(np.float32)
     h, cl, cs, z64, s = sru_run(w, io, c0)
@@ -51,11 +51,11 @@ def test_sru_persistent_ragged(monkeypatch, B, D, T, io):
     assert e["c_last"] <= 1e-5 and e["cs_last_row"] <= 1e-5
 
 
-def test_sru_both_kernels_at_workload_shape(monkeypatch):
+def test_sru_both_kernels_at_workload_shape(plan):
     w = I.WORKLOADS["sru_fwd"]
     outs = {}
-    for mode, lim in (("persistent", "0"), ("tiles", str(1 << 40))):
-        monkeypatch.setenv("LRS_PERSIST_MIN_BLOCKS", lim)
+    for mode, lim in (("persistent", 0), ("tiles", 1 << 40)):
+        plan(persist_min_blocks=lim)
         outs[mode] = sru_run(w, "bf16")[:3]
     s = I.sru_inputs(w)
     ref_h, ref_c = oracle.sru_fwd(*(I.bf16_bits_to_f64(s[k]) for k in ("zf", "zr", "zx")),
@@ -71,22 +71,22 @@ def test_sru_both_kernels_at_workload_shape(monkeypatch):
 @pytest.mark.parametrize("B,D,T", [(1, 1, 1), (1, 3, 7), (2, 5, 64), (3, 50, 200),
                                    (1, 258, 513), (2, 128, 1000)])
 @pytest.mark.parametrize("io", ["bf16", "f32"])
-def test_sru_deer_persistent_ragged(monkeypatch, B, D, T, io):
-    monkeypatch.setenv("LRS_PERSIST_MIN_BLOCKS", "0")
+def test_sru_deer_persistent_ragged(plan, B, D, T, io):
+    plan(persist_min_blocks=0)
     w = I.scaled(I.WORKLOADS["sru_deer"], B=B, D=D, T=T, seed=13200 + B * 13 + D * 5 + T)
     c0 = np.random.default_rng(T + D + 1).normal(size=(B, D)).astype(np.float32)
     sru_deer_check(*sru_deer_run(w, io, c0=c0, k_max=8), io, f"persistent sru-deer {io} {B}x{D}x{T}")
 
 
-def test_sru_deer_both_kernels_at_workload_shape(monkeypatch):
+def test_sru_deer_both_kernels_at_workload_shape(plan):
     w = I.WORKLOADS["sru_deer"]
-    for mode, lim in (("persistent", "0"), ("tiles", str(1 << 40))):
-        monkeypatch.setenv("LRS_PERSIST_MIN_BLOCKS", lim)
+    for mode, lim in (("persistent", 0), ("tiles", 1 << 40)):
+        plan(persist_min_blocks=lim)
         sru_deer_check(*sru_deer_run(w, "bf16"), "bf16", f"sru_deer workload, {mode}")
 
 
-def test_sru_deer_persistent_graph(monkeypatch):
-    monkeypatch.setenv("LRS_PERSIST_MIN_BLOCKS", "0")
+def test_sru_deer_persistent_graph(plan):
+    plan(persist_min_blocks=0)
     w = I.scaled(I.WORKLOADS["sru_deer"], B=2, D=128, T=1000, seed=13300)
     s = I.sru_inputs(w)
     z = {k: bf16_dev(s[k]) for k in ("zf", "zr", "zx")}
@@ -104,19 +104,19 @@ def test_sru_deer_persistent_graph(monkeypatch):
 
 
 @pytest.mark.parametrize("name", ["test_sru_graph_replay", "test_sru_fwd_bwd_graph_replay"])
-def test_sru_persistent_graph(monkeypatch, name):
+def test_sru_persistent_graph(plan, name):
     """The SRU graph replays (alone, and with the backward in the same graph)
     with the persistent forward forced."""
     import test_gpu_graph
-    monkeypatch.setenv("LRS_PERSIST_MIN_BLOCKS", "0")
+    plan(persist_min_blocks=0)
     getattr(test_gpu_graph, name)()
 
 
 @pytest.mark.parametrize("name", ["test_kmax_cap_and_warm_start", "test_async_form_and_stats",
                                   "test_linear_case_matches_sru_layer"])
-def test_sru_deer_persistent_options(monkeypatch, name):
+def test_sru_deer_persistent_options(plan, name):
     """The K_max cap, warm starts in place, the asynchronous form and the
     v_f = 0 case with the persistent iteration forced."""
     import test_gpu_sru_nl
-    monkeypatch.setenv("LRS_PERSIST_MIN_BLOCKS", "0")
+    plan(persist_min_blocks=0)
     getattr(test_gpu_sru_nl, name)()

@@ -30,15 +30,13 @@ def test_short_channels(B, D, T):
 
 @pytest.mark.parametrize("mode", ["serial", "packed", "parallel"])
 @pytest.mark.parametrize("T", [3, 6, 16, 40, 300, 1000, 2047, 4096])
-def test_forced_kernel(monkeypatch, mode, T):
-    """Each kernel family at any T through LRS_SERIAL_FWD_MAX_T,
-    LRS_SERIAL_BWD_MAX_T and LRS_PACKED_MAX_T (packed falls back to one
-    channel per workgroup where no channel fits a packed block)."""
-    big = str(1 << 40)
-    ser = big if mode == "serial" else "0"
-    monkeypatch.setenv("LRS_SERIAL_FWD_MAX_T", ser)
-    monkeypatch.setenv("LRS_SERIAL_BWD_MAX_T", ser)
-    monkeypatch.setenv("LRS_PACKED_MAX_T", big if mode == "packed" else "0")
+def test_forced_kernel(plan, mode, T):
+    """Each kernel family at any T through the plan options serial_fwd_max_t,
+    serial_bwd_max_t and packed_max_t (packed falls back to one channel per
+    workgroup where no channel fits a packed block)."""
+    big = 1 << 40
+    ser = big if mode == "serial" else 0
+    plan(serial_fwd_max_t=ser, serial_bwd_max_t=ser, packed_max_t=big if mode == "packed" else 0)
     B, D = 2, 333
     w = I.scaled(I.WORKLOADS["scan_fwd_bwd"], B=B, D=D, T=T, seed=9600 + T)
     x = I.scan_inputs(w)
