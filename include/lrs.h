@@ -201,6 +201,32 @@ LRS_API int lrs_scan_fwd_bwd_ex(const void *a, const void *b, const float *h0,
                                 int dtype, void *workspace, size_t workspace_bytes, void *stream,
                                 const lrs_options *options);
 
+/* Bytes of the fixed device array that lrs_scan_fwd_bwd_noalloc uses in place
+ * of a workspace (one copy per GPU). */
+#define LRS_STATIC_SCRATCH_BYTES (8u << 20)
+
+/* lrs_scan_fwd_bwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The look-back state lives in a fixed
+ * array of LRS_STATIC_SCRATCH_BYTES (8 MiB) inside the library, one copy per
+ * GPU, allocated when the library's device code is loaded and held until the
+ * process ends; the call itself allocates and frees nothing.  Inputs, outputs
+ * and their rules are those of lrs_scan_fwd_bwd (h may not be NULL where that
+ * function needs it), and the results are bit for bit the same.
+ * Limit: shapes whose lrs_scan_workspace_bytes exceeds LRS_STATIC_SCRATCH_BYTES
+ * return LRS_ERR_WORKSPACE before any launch ([B,D,T]: up to about one
+ * million look-back chunks, e.g. 4096 channels of 2^20 steps; [T,B,D]: B*D*T
+ * up to about 2^27).  The array belongs to the current device, and `stream` must be
+ * a stream of that device.  Every call on one GPU shares the array: calls
+ * that may overlap in time on one GPU (different streams, or different host
+ * threads, without ordering between them) race on it and give wrong results,
+ * so they must be ordered.  The first call on each device looks up the
+ * array's address (hipGetSymbolAddress); make it outside graph capture. */
+LRS_API int lrs_scan_fwd_bwd_noalloc(const void *a, const void *b, const float *h0,
+                                     const void *grad_h, void *h, void *grad_a, void *grad_b,
+                                     float *grad_h0, int64_t B, int64_t D, int64_t T, int layout,
+                                     int dtype, void *stream);
+
 /* ----------------------------------------------------------------- SRU --- */
 
 /* Workspace bytes needed by lrs_sru_fwd for this shape (0 for an invalid one). */

@@ -35,7 +35,8 @@ EXPORTS = ("lrs_status_string", "lrs_version", "lrs_scan_workspace_bytes", "lrs_
 _EX_BASES = ("lrs_scan_fwd", "lrs_scan_bwd", "lrs_scan_fwd_bwd", "lrs_sru_fwd", "lrs_sru_deer_fwd",
              "lrs_deer_solve", "lrs_deer_solve_seq")
 EXPORTS = EXPORTS + tuple(n + "_ex" for n in _EX_BASES) + ("lrs_options_default",
-                                                            "lrs_deer_eps_schedule")
+                                                            "lrs_deer_eps_schedule",
+                                                            "lrs_scan_fwd_bwd_noalloc")
 
 
 class LrsOptions(ctypes.Structure):
@@ -162,6 +163,8 @@ def load():
         ex = getattr(lib, name + "_ex")
         ex.argtypes = list(base.argtypes) + [ctypes.POINTER(LrsOptions)]
         ex.restype = _int
+    lib.lrs_scan_fwd_bwd_noalloc.argtypes = [_vp] * 8 + [_i64, _i64, _i64, _int, _int, _vp]
+    lib.lrs_scan_fwd_bwd_noalloc.restype = _int
     lib.lrs_deer_eps_schedule.argtypes = [_i64, _i64, ctypes.c_float, ctypes.c_float]
     lib.lrs_deer_eps_schedule.restype = ctypes.c_float
     _lib = lib

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/lrs.h"
@@ -100,6 +101,34 @@ hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStrea
   return hipGetLastError();
 }
 }  // namespace lrs
+
+// Device array behind lrs_scan_fwd_bwd_noalloc: the look-back status words
+// and tickets of its calls live here instead of in a caller's workspace.
+// Each GPU the library runs on holds its own copy until the process ends.  In
+// host code the array's name is not a device address: the address is looked
+// up once per device with hipGetSymbolAddress (that device current) and kept
+// in scratch_dev[], and only that pointer is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[LRS_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices];
+
+// Device address of the current device's copy of `scratch`.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LRS_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LRS_ERR_HIP;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return LRS_OK;
+}
+}  // namespace
 
 extern "C" {
 
@@ -1196,6 +1225,27 @@ float lrs_deer_eps_schedule(int64_t step, int64_t total_steps, float early, floa
   double frac = (double)step / (double)(total_steps - 1);
   frac = frac < 0.0 ? 0.0 : (frac > 1.0 ? 1.0 : frac);
   return (float)((double)early * pow((double)late / (double)early, frac));
+}
+
+// ------------------------------------------------- allocation-free form
+
+int lrs_scan_fwd_bwd_noalloc(const void* a, const void* b, const float* h0, const void* grad_h,
+                             void* h, void* grad_a, void* grad_b, float* grad_h0, int64_t B,
+                             int64_t D, int64_t T, int layout, int dtype, void* stream) {
+  // the workspace this shape needs (0 for one that needs none, or an invalid
+  // one, which the common path then rejects)
+  const size_t need = lrs_scan_workspace_bytes(B, D, T, layout, dtype);
+  if (need > (size_t)LRS_STATIC_SCRATCH_BYTES) return LRS_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    const int rc = scratch_address(&ws);
+    if (rc != LRS_OK) return rc;
+  }
+  // the look-back state is cleared by a reset kernel at the start of every
+  // pass that uses it, so whatever an earlier call left there is harmless
+  return scan_fwd_bwd_impl(a, b, h0, grad_h, h, grad_a, grad_b, grad_h0, B, D, T, layout, dtype,
+                           ws, need > 0 ? (size_t)LRS_STATIC_SCRATCH_BYTES : 0, stream,
+                           lrs::Opts());
 }
 
 }  // extern "C"
