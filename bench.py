@@ -153,7 +153,8 @@ def summarize(args):
     d = args.summarize
     wl = args.workload
     tag = wl if args.layout == "bdt" else f"{wl}_{args.layout}"  # output and record name
-    cmd_base = f"python3 bench.py --workload {wl}" + (f" --layout {args.layout}" if args.layout != "bdt" else "")
+    cmd_base = (f"python3 bench.py --workload {wl}" +
+                (f" --layout {args.layout}" if args.layout != "bdt" else "") + " --also none")
 
     def rows(pattern):
         out = []

@@ -748,7 +748,7 @@ int64_t col_status_words(const ColPlan& p) {
 
 // Tile shapes (waves along time x steps per lane x channels per lane).
 namespace {
-constexpr int kFwdNW = 8, kFwdL = 16, kFwdCPT = 1;
+constexpr int kFwdNW = 8, kFwdL = 32, kFwdCPT = 1;
 constexpr int kBwdNW = 8, kBwdL = 16, kBwdCPT = 1;
 constexpr int kSruNW = 4, kSruL = 16, kSruCPT = 2;          // bf16 I/O
 constexpr int kSruF32NW = 8, kSruF32L = 8, kSruF32CPT = 2;  // fp32 I/O
