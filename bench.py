@@ -123,7 +123,8 @@ KERNEL_NAMES = {"scan_fwd_f32": ("k_scan_fwd_bdt", "k_scan_fwd_tbd", "k_scan_fwd
                 "sru_deer_bf16": ("k_sru_deer_fused<unsigned short", "k_sru_deer_iter<unsigned short",
                                   "k_sru_deer_iter_persist<unsigned short"),
                 "deer_bwd_f32": ("k_deer_bwd",),
-                "lstm_fwd_save_bf16": ("k_lstm_fwd<unsigned short",),
+                "lstm_fwd_save_bf16": ("k_lstm_fwd<unsigned short",
+                                       "k_lstm_fwd_persist<unsigned short"),
                 "lstm_bwd_bf16": ("k_lstm_bwd<unsigned short",)}
 # entry points timed by each workload
 WORKLOAD_KERNELS = {"scan_fwd_small": ("scan_fwd_f32",),

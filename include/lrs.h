@@ -46,7 +46,7 @@
  *  - Calls that share a workspace must be ordered (same stream or synchronised).
  *  - Plans.  [B,D,T] scans of short channels pack whole channels into each
  *    workgroup (T <= 64) or, for the shortest (T <= 4), run one lane per
- *    channel; the limits are measured crossovers.  The SRU forward and the
+ *    channel; the limits are measured crossovers.  The SRU and LSTM forward and the
  *    SRU-by-DEER iterations switch to persistent kernels (one workgroup per
  *    128 channels walks every time tile, no cross-workgroup look-back and no
  *    reset between iterations) when the 128-channel blocks are at least as
@@ -125,7 +125,7 @@ typedef struct lrs_options {
   int64_t serial_bwd_max_t;   /* [B,D,T] backward scan: the same (default 4) */
   int64_t packed_max_t;       /* [B,D,T] scans: whole channels packed into each
                                  2048-step workgroup for T <= this (default 64) */
-  int64_t persist_min_blocks; /* SRU forward, SRU by DEER: persistent walk when
+  int64_t persist_min_blocks; /* SRU forward, SRU by DEER, LSTM forward: persistent walk when
                                  the 128-channel blocks number at least this
                                  (default: the device's compute units; 0 =
                                  always, a huge value = never) */
@@ -349,6 +349,11 @@ LRS_API int lrs_lstm_fwd(const void *z_f, const void *z_i, const void *z_c, cons
                          const float *c0, void *h, float *c_last, float *c_states, int64_t T,
                          int64_t B, int64_t D, int io_dtype, void *workspace,
                          size_t workspace_bytes, void *stream);
+/* lrs_lstm_fwd with explicit plan options (NULL = the defaults). */
+LRS_API int lrs_lstm_fwd_ex(const void *z_f, const void *z_i, const void *z_c, const void *z_o,
+                            const float *c0, void *h, float *c_last, float *c_states, int64_t T,
+                            int64_t B, int64_t D, int io_dtype, void *workspace,
+                            size_t workspace_bytes, void *stream, const lrs_options *options);
 
 /* LSTM cell-state layer backward (the chain rule of lrs_lstm_fwd; the
  * cell-state gradient is a reverse-time linear recurrence, [P1] parallel-scan

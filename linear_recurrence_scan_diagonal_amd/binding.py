@@ -33,7 +33,7 @@ EXPORTS = ("lrs_status_string", "lrs_version", "lrs_scan_workspace_bytes", "lrs_
 
 # entry points that have an _ex variant taking lrs_options
 _EX_BASES = ("lrs_scan_fwd", "lrs_scan_bwd", "lrs_scan_fwd_bwd", "lrs_sru_fwd", "lrs_sru_deer_fwd",
-             "lrs_deer_solve", "lrs_deer_solve_seq")
+             "lrs_deer_solve", "lrs_deer_solve_seq", "lrs_lstm_fwd")
 EXPORTS = EXPORTS + tuple(n + "_ex" for n in _EX_BASES) + ("lrs_options_default",
                                                             "lrs_deer_eps_schedule",
                                                             "lrs_scan_fwd_bwd_noalloc")
@@ -397,7 +397,7 @@ def sru_deer_fwd(z_f, z_r, z_x, bias_f, bias_r, v_f, c0=None, c_init=None, eps: 
 
 
 def lstm_fwd(z_f, z_i, z_c, z_o, c0=None, want_c_last: bool = False, out=None, workspace=None,
-             c_states=None):
+             c_states=None, options=None):
     """LSTM cell-state layer with input-only gates on [T,B,D] pre-activations
     (bf16 or fp32).  Returns h or (h, c_last).  c_states, if given, is a
     [T,B,D] fp32 tensor that receives every cell state (lstm_bwd's input)."""
@@ -415,9 +415,9 @@ def lstm_fwd(z_f, z_i, z_c, z_o, c0=None, want_c_last: bool = False, out=None, w
     c_last = torch.empty((B, D), dtype=torch.float32, device=z_f.device) if want_c_last else None
     nbytes = lib.lrs_lstm_workspace_bytes(T, B, D)
     ws = _workspace(nbytes, z_f.device, workspace)
-    _call(lib.lrs_lstm_fwd(_ptr(z_f), _ptr(z_i), _ptr(z_c), _ptr(z_o), _ptr(c0), _ptr(h),
-                           _ptr(c_last), _ptr(c_states), T, B, D, DTYPES[io], _ptr(ws), nbytes,
-                           _stream(z_f.device)), "lrs_lstm_fwd")
+    _call(lib.lrs_lstm_fwd_ex(_ptr(z_f), _ptr(z_i), _ptr(z_c), _ptr(z_o), _ptr(c0), _ptr(h),
+                              _ptr(c_last), _ptr(c_states), T, B, D, DTYPES[io], _ptr(ws), nbytes,
+                              _stream(z_f.device), _opts(options)), "lrs_lstm_fwd")
     return (h, c_last) if want_c_last else h
 
 

@@ -117,6 +117,156 @@ __global__ __launch_bounds__(NW* kWave) void k_lstm_fwd(
 }
 
 // ---------------------------------------------------------------------------
+// persistent forward: one workgroup per channel block visits every time tile
+// in order, the state entering the tile carried in LDS (persist_enter /
+// persist_advance), so there is no look-back state and no reset kernel; the
+// next tile's rows are loaded into registers while the current one is
+// processed.  Used when the channel blocks alone fill the GPU (B*D large),
+// as for the SRU forward.
+// ---------------------------------------------------------------------------
+template <typename IO, int L, int CPT, bool FULL, bool NT>
+__device__ __forceinline__ void lstm_persist_load(const IO* __restrict__ zf,
+                                                  const IO* __restrict__ zi,
+                                                  const IO* __restrict__ zc,
+                                                  const IO* __restrict__ zo, int64_t row0,
+                                                  int64_t T, int64_t C, int64_t cbase,
+                                                  uint32_t off, int nvc, IoRow<IO, CPT> (&fr)[L],
+                                                  IoRow<IO, CPT> (&ir)[L],
+                                                  IoRow<IO, CPT> (&gr)[L],
+                                                  IoRow<IO, CPT> (&orr)[L]) {
+  const IO* fp = zf + row0 * C + cbase;
+  const IO* ip = zi + row0 * C + cbase;
+  const IO* gp = zc + row0 * C + cbase;
+  const IO* op = zo + row0 * C + cbase;
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const int nv = (FULL || row0 + i < T) ? nvc : 0;
+    fr[i].template load<FULL, NT>(fp, off, nv);
+    ir[i].template load<FULL, NT>(ip, off, nv);
+    gr[i].template load<FULL, NT>(gp, off, nv);
+    orr[i].template load<FULL, NT>(op, off, nv);
+    fp += C;
+    ip += C;
+    gp += C;
+    op += C;
+  }
+}
+
+// One tile of the walk: the gates of the current rows, then the next tile's
+// rows into the same registers (PF: 0 none, 1 full rows, 2 predicated rows),
+// then the waves' maps combine with the carried state and the outputs are
+// written.  FULL: the current tile lies inside the arrays.
+template <typename IO, int NW, int L, int CPT, bool FULL, int PF, bool SAVE, bool NT>
+__device__ __forceinline__ void lstm_persist_tile(
+    const IO* __restrict__ zf, const IO* __restrict__ zi, const IO* __restrict__ zc,
+    const IO* __restrict__ zo, IO* __restrict__ h, float* __restrict__ cs, int64_t row0,
+    int64_t T, int64_t C, int64_t cbase, uint32_t off, int nvc, IoRow<IO, CPT> (&fr)[L],
+    IoRow<IO, CPT> (&ir)[L], IoRow<IO, CPT> (&gr)[L], IoRow<IO, CPT> (&orr)[L],
+    PersistShared<NW, CPT>& s, int wid) {
+  constexpr int TW = NW * L;
+  float av[L][CPT], bv[L][CPT];
+  IoRow<IO, CPT> ocur[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    ocur[i] = orr[i];
+    const bool row_ok = FULL || row0 + i < T;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      if (FULL || (row_ok && k < nvc)) {
+        av[i][k] = fast_sigmoid(fr[i].get(k), 0.0f);
+        bv[i][k] = fast_sigmoid(ir[i].get(k), 0.0f) * fast_tanh(gr[i].get(k));
+      } else {  // identity past the end
+        av[i][k] = 1.0f;
+        bv[i][k] = 0.0f;
+      }
+    }
+  }
+  if (PF == 1)
+    lstm_persist_load<IO, L, CPT, true, NT>(zf, zi, zc, zo, row0 + TW, T, C, cbase, off, nvc, fr,
+                                            ir, gr, orr);
+  else if (PF == 2)
+    lstm_persist_load<IO, L, CPT, false, NT>(zf, zi, zc, zo, row0 + TW, T, C, cbase, off, nvc, fr,
+                                             ir, gr, orr);
+  float A[CPT], B[CPT], x[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    A[k] = av[0][k];
+    B[k] = bv[0][k];
+#pragma unroll
+    for (int i = 1; i < L; ++i) {
+      B[k] = __builtin_fmaf(av[i][k], B[k], bv[i][k]);
+      A[k] = A[k] * av[i][k];
+    }
+  }
+  persist_enter<NW, CPT>(A, B, s, wid, off, x);
+  IO* hp = h + row0 * C + cbase;
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    float out[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      x[k] = __builtin_fmaf(av[i][k], x[k], bv[i][k]);
+      out[k] = fast_sigmoid(ocur[i].get(k), 0.0f) * fast_tanh(x[k]);
+    }
+    const int nv = (FULL || row0 + i < T) ? nvc : 0;
+    IoRow<IO, CPT>::template store<FULL, NT>(hp, off, nv, out);
+    if (SAVE) store_row<CPT, FULL, NT>(cs + (row0 + i) * C + cbase, off, nv, x);
+    hp += C;
+  }
+  persist_advance<NW, CPT>(x, s, wid, off);
+}
+
+template <typename IO, int NW, int L, int CPT, bool SAVE, bool NT>
+__global__ __launch_bounds__(NW* kWave) void k_lstm_fwd_persist(
+    const IO* __restrict__ zf, const IO* __restrict__ zi, const IO* __restrict__ zc,
+    const IO* __restrict__ zo, const float* __restrict__ c0p, IO* __restrict__ h,
+    float* __restrict__ c_last, float* __restrict__ cs, int64_t T, int64_t C, int vec) {
+  constexpr int CW = kWave * CPT, TW = NW * L;
+  __shared__ PersistShared<NW, CPT> s;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t cbase = (int64_t)blockIdx.x * CW;
+  const uint32_t off = (uint32_t)(lane * CPT);
+  const int nvc = clamp_valid(C - (cbase + off), CPT);
+  const bool cfull = vec && cbase + CW <= C;
+  for (int j = threadIdx.x; j < CW; j += NW * kWave)
+    s.carry[j] = (c0p && cbase + j < C) ? c0p[cbase + j] : 0.0f;
+  const int64_t ntb = (T + TW - 1) / TW, nfull = T / TW;
+  const int64_t w0 = (int64_t)wid * L;
+  IoRow<IO, CPT> fr[L], ir[L], gr[L], orr[L];
+#define LRS_TILE(FULLT, PFT, TB)                                                                 \
+  lstm_persist_tile<IO, NW, L, CPT, FULLT, PFT, SAVE, NT>(zf, zi, zc, zo, h, cs, (TB) * TW + w0, T, \
+                                                          C, cbase, off, nvc, fr, ir, gr, orr, s, wid)
+  if (cfull && nfull > 0) {
+    // full tiles in a straight loop (each loads the next full tile), then the
+    // last full tile and the ragged tail, if any
+    lstm_persist_load<IO, L, CPT, true, NT>(zf, zi, zc, zo, w0, T, C, cbase, off, nvc, fr, ir, gr,
+                                            orr);
+    for (int64_t tb = 0; tb + 1 < nfull; ++tb) LRS_TILE(true, 1, tb);
+    if (ntb > nfull) {
+      LRS_TILE(true, 2, nfull - 1);
+      LRS_TILE(false, 0, nfull);
+    } else {
+      LRS_TILE(true, 0, nfull - 1);
+    }
+  } else {
+    lstm_persist_load<IO, L, CPT, false, NT>(zf, zi, zc, zo, w0, T, C, cbase, off, nvc, fr, ir, gr,
+                                             orr);
+    for (int64_t tb = 0; tb < ntb; ++tb) {
+      if (tb + 1 < ntb) LRS_TILE(false, 2, tb);
+      else LRS_TILE(false, 0, tb);
+    }
+  }
+#undef LRS_TILE
+  // rows past the end keep the state, so the final carry is c_T
+  if (c_last) {
+    __syncthreads();
+    for (int j = threadIdx.x; j < CW; j += NW * kWave)
+      if (cbase + j < C) c_last[cbase + j] = s.carry[j];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // backward (reverse time, as k_sru_bwd: logical time block 0 is the last
 // physical block, wave 0 takes its latest steps).  With the cell states c
 // saved by the forward pass, the cell-state gradient runs
@@ -290,11 +440,18 @@ namespace {
 constexpr int kLstmNW = 4, kLstmL = 16, kLstmCPT = 2;          // forward, bf16 I/O
 constexpr int kLstmF32NW = 8, kLstmF32L = 8, kLstmF32CPT = 2;  // forward, fp32 I/O
 constexpr int kLstmBwdNW = 4, kLstmBwdL = 8, kLstmBwdCPT = 2;  // backward, both I/O types
+constexpr int kLstmPNW = 8, kLstmPL = 8, kLstmPCPT = 2;        // persistent forward
 }  // namespace
 
-ColPlan plan_lstm(int64_t C, int64_t T, int io_dtype, bool save) {
+ColPlan plan_lstm(int64_t C, int64_t T, int io_dtype, bool save, bool allow_persist,
+                  const Opts& o) {
   ColPlan p = io_dtype == 1 ? plan_cols(C, T, kLstmNW, kLstmL, kLstmCPT)
                             : plan_cols(C, T, kLstmF32NW, kLstmF32L, kLstmF32CPT);
+  const int64_t ncb_p = (C + kWave * kLstmPCPT - 1) / (kWave * kLstmPCPT);
+  if (allow_persist && ncb_p >= persist_min_blocks(o)) {  // the channel blocks alone fill the GPU
+    p = plan_cols(C, T, kLstmPNW, kLstmPL, kLstmPCPT);
+    p.persist = true;
+  }
   // z_f, z_i, z_c, z_o, h (+ the cell states)
   p.stream = C * T * (5 * (io_dtype == 1 ? 2 : 4) + (save ? 4 : 0)) >= kStreamFootprint;
   return p;
@@ -312,6 +469,26 @@ hipError_t launch_lstm_fwd(const void* zf, const void* zi, const void* zc, const
                            int64_t C, int io_dtype, const ColPlan& p, int vec, uint64_t* status,
                            unsigned* tickets, hipStream_t stream) {
   const uint64_t grid = (uint64_t)p.ncb * (uint64_t)p.ntb;
+  if (p.persist) {
+#define LRS_LSTMP(IO, SV, NTF)                                                                   \
+  hipLaunchKernelGGL((k_lstm_fwd_persist<IO, kLstmPNW, kLstmPL, kLstmPCPT, SV, NTF>),             \
+                     dim3((unsigned)p.ncb), dim3(kLstmPNW * kWave), 0, stream, (const IO*)zf,      \
+                     (const IO*)zi, (const IO*)zc, (const IO*)zo, c0, (IO*)h, c_last, c_states, T, \
+                     C, vec)
+#define LRS_LSTMP_SAVE(IO, NTF)                  \
+  if (c_states) LRS_LSTMP(IO, true, NTF);        \
+  else LRS_LSTMP(IO, false, NTF)
+    if (io_dtype == 1) {
+      if (p.stream) { LRS_LSTMP_SAVE(uint16_t, true); }
+      else { LRS_LSTMP_SAVE(uint16_t, false); }
+    } else {
+      if (p.stream) { LRS_LSTMP_SAVE(float, true); }
+      else { LRS_LSTMP_SAVE(float, false); }
+    }
+#undef LRS_LSTMP_SAVE
+#undef LRS_LSTMP
+    return hipGetLastError();
+  }
 #define LRS_LSTM(IO, NW_, L_, CPT_, NTF)                                                        \
   hipLaunchKernelGGL((k_lstm_fwd<IO, NW_, L_, CPT_, NTF>), dim3((unsigned)grid),               \
                      dim3(NW_ * kWave), 0, stream, (const IO*)zf, (const IO*)zi, (const IO*)zc, \

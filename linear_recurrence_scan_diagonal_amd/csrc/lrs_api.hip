@@ -511,7 +511,8 @@ size_t lrs_lstm_workspace_bytes(int64_t T, int64_t B, int64_t D) {
   if (!shape_ok(B, D, T, &C, &N) || N == 0) return 0;
   size_t need = 0;
   for (int io = 0; io < 2; ++io) {
-    const lrs::ColPlan ps[3] = {lrs::plan_lstm(C, T, io, false), lrs::plan_lstm(C, T, io, true),
+    const lrs::ColPlan ps[3] = {lrs::plan_lstm(C, T, io, false, false),
+                                lrs::plan_lstm(C, T, io, true, false),
                                 lrs::plan_lstm_bwd(C, T, io)};
     for (const lrs::ColPlan& p : ps) {
       const size_t b = lookback_bytes(lrs::col_status_words(p), p.ncb);
@@ -536,9 +537,10 @@ static int col_lookback(const lrs::ColPlan& p, void* workspace, size_t workspace
   return hip_status(lrs::launch_reset(*status, nst, *tickets, p.ncb, nullptr, 0, s));
 }
 
-int lrs_lstm_fwd(const void* z_f, const void* z_i, const void* z_c, const void* z_o,
-                 const float* c0, void* h, float* c_last, float* c_states, int64_t T, int64_t B,
-                 int64_t D, int io_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+static int lstm_fwd_impl(const void* z_f, const void* z_i, const void* z_c, const void* z_o,
+                         const float* c0, void* h, float* c_last, float* c_states, int64_t T,
+                         int64_t B, int64_t D, int io_dtype, void* workspace,
+                         size_t workspace_bytes, void* stream, const lrs::Opts& opt) {
   int64_t C, N;
   if (!shape_ok(B, D, T, &C, &N)) return LRS_ERR_INVALID_ARG;
   if (io_dtype != LRS_F32 && io_dtype != LRS_BF16) return LRS_ERR_INVALID_ARG;
@@ -563,8 +565,8 @@ int lrs_lstm_fwd(const void* z_f, const void* z_i, const void* z_c, const void* 
   if (overlap(h, nb, c_last, cb) || overlap(h, nb, c_states, sb) ||
       overlap(c_last, cb, c_states, sb))
     return LRS_ERR_INVALID_ARG;
-  const lrs::ColPlan p = lrs::plan_lstm(C, T, io_dtype, c_states != nullptr);
-  if (!grid_ok(p.ncb * p.ntb, p.nw * 64)) return LRS_ERR_UNSUPPORTED;
+  const lrs::ColPlan p = lrs::plan_lstm(C, T, io_dtype, c_states != nullptr, true, opt);
+  if (!grid_ok(p.persist ? p.ncb : p.ncb * p.ntb, p.nw * 64)) return LRS_ERR_UNSUPPORTED;
   uint64_t* status;
   unsigned* tickets;
   const int rc = col_lookback(p, workspace, workspace_bytes, s, &status, &tickets);
@@ -1215,6 +1217,20 @@ int lrs_deer_solve_seq_ex(const float* w, const float* u, const float* h0, const
                        size_t workspace_bytes, void* stream,
     const lrs_options* options) {
   return deer_solve_seq_impl(w, u, h0, h_init, h, B, D, T, eps, k_max, iters_out, converged_out, workspace, workspace_bytes, stream, to_opts(options));
+}
+
+int lrs_lstm_fwd(const void* z_f, const void* z_i, const void* z_c, const void* z_o,
+                 const float* c0, void* h, float* c_last, float* c_states, int64_t T, int64_t B,
+                 int64_t D, int io_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return lstm_fwd_impl(z_f, z_i, z_c, z_o, c0, h, c_last, c_states, T, B, D, io_dtype, workspace,
+                       workspace_bytes, stream, lrs::Opts());
+}
+int lrs_lstm_fwd_ex(const void* z_f, const void* z_i, const void* z_c, const void* z_o,
+                    const float* c0, void* h, float* c_last, float* c_states, int64_t T,
+                    int64_t B, int64_t D, int io_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream, const lrs_options* options) {
+  return lstm_fwd_impl(z_f, z_i, z_c, z_o, c0, h, c_last, c_states, T, B, D, io_dtype, workspace,
+                       workspace_bytes, stream, to_opts(options));
 }
 
 // ------------------------------------------------- DEER tolerance schedule

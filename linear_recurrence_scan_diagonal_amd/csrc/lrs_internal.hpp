@@ -178,7 +178,9 @@ hipError_t launch_sru_bwd(const void* zf, const void* zr, const void* zx, const 
 
 // LSTM cell-state layer with input-only gates (gated_cell.hip).  `save`: the
 // forward also writes the cell states.
-ColPlan plan_lstm(int64_t C, int64_t T, int io_dtype, bool save);
+// allow_persist = false: the look-back tile plan (workspace queries size for it).
+ColPlan plan_lstm(int64_t C, int64_t T, int io_dtype, bool save, bool allow_persist = true,
+                  const Opts& o = Opts());
 ColPlan plan_lstm_bwd(int64_t C, int64_t T, int io_dtype);
 hipError_t launch_lstm_fwd(const void* zf, const void* zi, const void* zc, const void* zo,
                            const float* c0, void* h, float* c_last, float* c_states, int64_t T,

@@ -1,6 +1,6 @@
 """The persistent [T,B,D] kernels (one workgroup per channel block walking
-all time tiles, chosen when the channel blocks fill the GPU): the SRU forward
-and the SRU-by-DEER iteration, against the fp64 oracle, forced through
+all time tiles, chosen when the channel blocks fill the GPU): the SRU forward,
+the LSTM forward and the SRU-by-DEER iteration, against the fp64 oracle, forced through
 the persist_min_blocks plan option on ragged shapes (partial last tile in time, partial
 last channel block, both I/O types, c0, saved cell states and c_T), and at the
 full B=32 D=1024 T=2048 shape both ways, where the two kernel families must
@@ -120,3 +120,46 @@ def test_sru_deer_persistent_options(plan, name):
     import test_gpu_sru_nl
     plan(persist_min_blocks=0)
     getattr(test_gpu_sru_nl, name)()
+
+
+# LSTM cell-state layer: the persistent forward (chosen at the workload shape,
+# forced here on ragged shapes) against the oracle, the backward fed its saved
+# cell states, and both forward kernel families at the workload shape.
+@pytest.mark.parametrize("B,D,T", [(1, 1, 1), (2, 3, 65), (3, 50, 200), (1, 258, 513),
+                                   (2, 128, 1000), (1, 300, 64)])
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_lstm_persistent_ragged(plan, B, D, T, io):
+    from test_gpu_lstm import check, run_case
+    plan(persist_min_blocks=0)
+    w = I.scaled(I.WORKLOADS["lstm_fwd_bwd"], B=B, D=D, T=T, seed=13500 + B * 11 + D * 3 + T)
+    rng = np.random.default_rng(T + 7 * D)
+    c0 = rng.normal(size=(B, D)).astype(np.float32)
+    gcl = rng.normal(size=(B, D)).astype(np.float32)
+    check(run_case(w, io, c0=c0, gcl=gcl), io, f"persistent lstm {io} {B}x{D}x{T}")
+
+
+def test_lstm_both_kernels_at_workload_shape(plan):
+    from test_gpu_lstm import dev_inputs
+    w = I.WORKLOADS["lstm_fwd_bwd"]
+    z, z64 = dev_inputs(w, "bf16")
+    outs = {}
+    for mode, lim in (("persistent", 0), ("tiles", 1 << 40)):
+        plan(persist_min_blocks=lim)
+        cs = torch.empty((w.T, w.B, w.D), dtype=torch.float32, device=DEV)
+        h, cl = lrs.lstm_fwd(z["zf"], z["zi"], z["zc"], z["zo"], want_c_last=True, c_states=cs)
+        torch.cuda.synchronize()
+        outs[mode] = (h.float().cpu().numpy(), cl.cpu().numpy(), cs.cpu().numpy())
+    ref_h, ref_c = oracle.lstm_fwd(*(z64[k] for k in ("zf", "zi", "zc", "zo")))
+    for mode, (h, cl, cs) in outs.items():
+        eh, ec = relerr(h, ref_h), relerr(cl, ref_c)
+        log(f"lstm_fwd workload, {mode}: h={eh:.2e} c_last={ec:.2e}")
+        assert eh <= 2e-2 and ec <= 1e-5
+        assert relerr(cs[-1], ref_c) <= 1e-5
+    assert relerr(outs["persistent"][2], outs["tiles"][2]) <= 1e-5
+
+
+def test_lstm_persistent_graph(plan):
+    """The LSTM forward + backward graph replays with the persistent forward."""
+    import test_gpu_graph_more
+    plan(persist_min_blocks=0)
+    test_gpu_graph_more.test_lstm_graph()
