@@ -1091,30 +1091,105 @@ struct FusedShared {
 template <int NW>
 __device__ __forceinline__ void fused_combine(float WA, float WB, FusedShared<NW>& s, int par,
                                               float& PA, float& PB, float& TA, float& TB) {
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   if (lane == 0) {
     s.wA[par][wid] = WA;
     s.wB[par][wid] = WB;
   }
   __syncthreads();
-  PA = 1.0f; PB = 0.0f; TA = 1.0f; TB = 0.0f;
+  // the block's map in wave order; the prefix before this wave is the partial
+  // map when the loop reaches it (wid is uniform)
+  TA = 1.0f; TB = 0.0f; PA = 1.0f; PB = 0.0f;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    const float wa = s.wA[par][w], wb = s.wB[par][w];
-    if (w < wid) {
-      PB = __builtin_fmaf(wa, PB, wb);
-      PA = PA * wa;
+    if (w == wid) {
+      PA = TA;
+      PB = TB;
     }
-    TB = __builtin_fmaf(wa, TB, wb);
+    const float wa = s.wA[par][w];
+    TB = __builtin_fmaf(wa, TB, s.wB[par][w]);
     TA = TA * wa;
   }
+}
+
+// One Newton iteration k of a sub-chunk of the fused solve: y_k (yout) from
+// y_{k-1} (yin, held in registers); ent is y_{k-1} at the step before this
+// wave's first step on entry and y_k there on exit.  max |y_k - y_{k-1}| over
+// the wave's steps is folded into s.dmax[k - 1] with the NaN-propagating
+// maximum (v_maximum3_f32), so a non-finite step still reads as the largest
+// update: the bit pattern of a non-negative float or a NaN orders as unsigned.
+template <int NW, int R, int E, bool FULL>
+__device__ __forceinline__ void deer_fused_iter(int k, const float (&us)[R][E],
+                                                const float (&yin)[R][E], float (&yout)[R][E],
+                                                int64_t base, int64_t T, float ws, float wd,
+                                                float& ent, int& par, FusedShared<NW>& s) {
+  constexpr int RS = kWave * E;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const float xin = s.xc[k];
+  // J = w (1 - z^2) and rhs = z - J y_{t-1} per step, kept for the output pass
+  float Jv[R][E], rv[R][E], Ai[R], Bi[R], RA[R], RB[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float fy = (r > 0) ? readlane_f(yin[r - 1][E - 1], kWave - 1) : ent;
+    const float yf = wave_shift_up(yin[r][E - 1], fy);  // y_{t-1} at the lane's first step
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const float yp = j == 0 ? yf : yin[r][j - 1];
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(ws, yp, us[r][j]));
+      const float z = __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + e), 1.0f);
+      Jv[r][j] = __builtin_fmaf(-wd * z, z, wd);    // w (1 - z^2)
+      rv[r][j] = __builtin_fmaf(-Jv[r][j], yp, z);  // z - J y_{t-1}
+    }
+    if (!FULL) {
+      const int64_t p = base + r * RS;
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        if (p + j >= T) { Jv[r][j] = 1.0f; rv[r][j] = 0.0f; }
+    }
+    float A = Jv[r][0], B = rv[r][0];
+#pragma unroll
+    for (int j = 1; j < E; ++j) {
+      B = __builtin_fmaf(Jv[r][j], B, rv[r][j]);
+      A = A * Jv[r][j];
+    }
+    wave_scan(A, B);
+    Ai[r] = A; Bi[r] = B;
+    RA[r] = readlane_f(A, kWave - 1);
+    RB[r] = readlane_f(B, kWave - 1);
+  }
+  float WA, WB, PA, PB, TA, TB;
+  chain_rows<R>(RA, RB, WA, WB);
+  fused_combine<NW>(WA, WB, s, par, PA, PB, TA, TB);
+  par ^= 1;
+  if (threadIdx.x == 0) s.xc[k] = __builtin_fmaf(TA, xin, TB);  // every thread read xin above
+  float xr = __builtin_fmaf(PA, xin, PB);  // y_k at the step before this wave's first step
+  ent = xr;
+  float dmf = 0.0f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float x = wave_shift_up(__builtin_fmaf(Ai[r], xr, Bi[r]), xr);
+    const int64_t p = base + r * RS;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      x = __builtin_fmaf(Jv[r][j], x, rv[r][j]);
+      const float d = __builtin_elementwise_maximum(dmf, fabsf(x - yin[r][j]));
+      dmf = (FULL || p + j < T) ? d : dmf;
+      yout[r][j] = x;
+    }
+    xr = __builtin_fmaf(RA[r], xr, RB[r]);
+  }
+  const uint32_t dm = wave_max_u32(as_u32(dmf));
+  if (lane == 0 && dm > s.dmax[k - 1][wid]) s.dmax[k - 1][wid] = dm;
 }
 
 // One sub-chunk (index c) of the fused solve: iterations 1..m.  Each lane
 // takes E consecutive steps (4 or 8) of each of the wave's R rows of 64 E
 // steps.  y0last: the starting iterate at the previous sub-chunk's last step
 // (updated for the next one); par: LDS parity of the wave maps (alternates per
-// iteration).
+// iteration).  Iterates alternate between two register sets, so each
+// iteration writes its result in place of the one before the previous.
 template <int NW, int R, int E, bool FULL, bool NT>
 __device__ __forceinline__ void deer_fused_sub(const float* __restrict__ urow,
                                                const float* __restrict__ y0row,
@@ -1127,7 +1202,7 @@ __device__ __forceinline__ void deer_fused_sub(const float* __restrict__ urow,
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   const int64_t base = (int64_t)c * CH + (int64_t)wid * S + E * lane;
   const float ws = wd * k2l2e;
-  float uv[R][E], yv[R][E];
+  float us[R][E], ya[R][E], yb[R][E];  // us: u scaled by 2 log2(e)
 #pragma unroll
   for (int r = 0; r < R; ++r) {
 #pragma unroll
@@ -1135,14 +1210,15 @@ __device__ __forceinline__ void deer_fused_sub(const float* __restrict__ urow,
       const float4 u4 = ld4<FULL, NT>(urow, base + r * RS + q, T, vec, 0.0f);
       const float4 y4 = y0row ? ld4<FULL, NT>(y0row, base + r * RS + q, T, vec, 0.0f)
                               : make_float4(0.f, 0.f, 0.f, 0.f);
-      uv[r][q] = u4.x; uv[r][q + 1] = u4.y; uv[r][q + 2] = u4.z; uv[r][q + 3] = u4.w;
-      yv[r][q] = y4.x; yv[r][q + 1] = y4.y; yv[r][q + 2] = y4.z; yv[r][q + 3] = y4.w;
+      us[r][q] = k2l2e * u4.x; us[r][q + 1] = k2l2e * u4.y;
+      us[r][q + 2] = k2l2e * u4.z; us[r][q + 3] = k2l2e * u4.w;
+      ya[r][q] = y4.x; ya[r][q + 1] = y4.y; ya[r][q + 2] = y4.z; ya[r][q + 3] = y4.w;
     }
   }
   // starting iterate at the step before this wave's first step
   float ent;
   if (y0row) {
-    if (lane == kWave - 1) s.y0w[wid] = yv[R - 1][E - 1];
+    if (lane == kWave - 1) s.y0w[wid] = ya[R - 1][E - 1];
     __syncthreads();
     ent = wid > 0 ? s.y0w[wid - 1] : (c == 0 ? x0 : y0last);
     y0last = s.y0w[NW - 1];  // read before any later write: the next writes follow a barrier
@@ -1150,70 +1226,25 @@ __device__ __forceinline__ void deer_fused_sub(const float* __restrict__ urow,
     ent = (c == 0 && wid == 0) ? x0 : 0.0f;
     if (c > 0) __syncthreads();  // the previous sub-chunk's last carry write (m = 1) is seen
   }
+  int k = 1;
 #pragma unroll 1
-  for (int k = 1; k <= m; ++k) {
-    const float xin = s.xc[k];
-    // J = w (1 - z^2) and rhs = z - J y_{t-1} per step, kept for the output pass
-    float Jv[R][E], rv[R][E], Ai[R], Bi[R], RA[R], RB[R];
+  for (; k + 1 <= m; k += 2) {
+    deer_fused_iter<NW, R, E, FULL>(k, us, ya, yb, base, T, ws, wd, ent, par, s);
+    deer_fused_iter<NW, R, E, FULL>(k + 1, us, yb, ya, base, T, ws, wd, ent, par, s);
+  }
+  if (k <= m) {  // odd count: the last iterate goes to yb
+    deer_fused_iter<NW, R, E, FULL>(k, us, ya, yb, base, T, ws, wd, ent, par, s);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float fy = (r > 0) ? readlane_f(yv[r - 1][E - 1], kWave - 1) : ent;
-      const float yf = wave_shift_up(yv[r][E - 1], fy);  // y_{t-1} at the lane's first step
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int j = 0; j < E; ++j) {
-        const float yp = j == 0 ? yf : yv[r][j - 1];
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(ws, yp, k2l2e * uv[r][j]));
-        const float z = __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + e), 1.0f);
-        Jv[r][j] = __builtin_fmaf(-wd * z, z, wd);    // w (1 - z^2)
-        rv[r][j] = __builtin_fmaf(-Jv[r][j], yp, z);  // z - J y_{t-1}
-      }
-      if (!FULL) {
-        const int64_t p = base + r * RS;
-#pragma unroll
-        for (int j = 0; j < E; ++j)
-          if (p + j >= T) { Jv[r][j] = 1.0f; rv[r][j] = 0.0f; }
-      }
-      float A = Jv[r][0], B = rv[r][0];
-#pragma unroll
-      for (int j = 1; j < E; ++j) {
-        B = __builtin_fmaf(Jv[r][j], B, rv[r][j]);
-        A = A * Jv[r][j];
-      }
-      wave_scan(A, B);
-      Ai[r] = A; Bi[r] = B;
-      RA[r] = readlane_f(A, kWave - 1);
-      RB[r] = readlane_f(B, kWave - 1);
-    }
-    float WA, WB, PA, PB, TA, TB;
-    chain_rows<R>(RA, RB, WA, WB);
-    fused_combine<NW>(WA, WB, s, par, PA, PB, TA, TB);
-    par ^= 1;
-    if (threadIdx.x == 0) s.xc[k] = __builtin_fmaf(TA, xin, TB);  // every thread read xin above
-    float xr = __builtin_fmaf(PA, xin, PB);  // y_k at the step before this wave's first step
-    ent = xr;
-    uint32_t dm = 0;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float x = wave_shift_up(__builtin_fmaf(Ai[r], xr, Bi[r]), xr);
-      const int64_t p = base + r * RS;
-#pragma unroll
-      for (int j = 0; j < E; ++j) {
-        x = __builtin_fmaf(Jv[r][j], x, rv[r][j]);
-        const uint32_t d = as_u32(fabsf(x - yv[r][j]));
-        if (FULL || p + j < T) dm = d > dm ? d : dm;
-        yv[r][j] = x;
-      }
-      xr = __builtin_fmaf(RA[r], xr, RB[r]);
-    }
-    dm = wave_max_u32(dm);
-    if (lane == 0 && dm > s.dmax[k - 1][wid]) s.dmax[k - 1][wid] = dm;
+      for (int j = 0; j < E; ++j) ya[r][j] = yb[r][j];
   }
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int q = 0; q < E; q += 4)
       st4<FULL, NT>(orow, base + r * RS + q, T, vec,
-                    make_float4(yv[r][q], yv[r][q + 1], yv[r][q + 2], yv[r][q + 3]));
+                    make_float4(ya[r][q], ya[r][q + 1], ya[r][q + 2], ya[r][q + 3]));
 }
 
 // sets: k_max slot sets of kDeltaSlots words, kDeltaStride apart (redo: unused).
