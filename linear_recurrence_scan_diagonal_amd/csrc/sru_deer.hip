@@ -79,6 +79,18 @@ __device__ __forceinline__ void sru_deer_fold_norm(uint32_t dmax, uint32_t* __re
   }
 }
 
+// Forget gate of an SRU-by-DEER step, sigmoid(v_f c_{t-1} + z_f + b_f), as
+// 1 / (1 + 2^(vs c_{t-1} + zq)) with vs = -log2(e) v_f and
+// zq = -log2(e) (z_f + b_f) = fma(z_f, -log2 e, nbf), nbf = -log2(e) b_f: zq
+// does not depend on the iterate, so a walk over several Newton iterations
+// computes it once per element.
+__device__ __forceinline__ float sd_zq(float zf, float nbf) {
+  return __builtin_fmaf(zf, -kLog2e, nbf);
+}
+__device__ __forceinline__ float sd_gate(float vs, float prev, float zq) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(vs, prev, zq)));
+}
+
 template <typename IO, int NW, int L, int CPT, bool FULL, bool NT>
 __device__ __forceinline__ void sru_deer_tile(const IO* __restrict__ zf, const IO* __restrict__ zx,
                                               const float* __restrict__ bias_f,
@@ -138,8 +150,7 @@ __device__ __forceinline__ void sru_deer_tile(const IO* __restrict__ zf, const I
       for (int k = 0; k < CPT; ++k) {
         const float prev = (i > 0) ? yo[i - 1][k] : yp[k];
         if (FULL || k < nv) {
-          const float z = __builtin_fmaf(vf[k], prev, fr.get(k));
-          const float f = fast_sigmoid(z, nbf[k]);
+          const float f = sd_gate(-kLog2e * vf[k], prev, sd_zq(fr.get(k), nbf[k]));
           const float dx = prev - xr.get(k);
           const float F = __builtin_fmaf(f, dx, xr.get(k));
           const float J = __builtin_fmaf(dx * (f - f * f), vf[k], f);
@@ -278,7 +289,7 @@ __device__ __forceinline__ void sru_deer_persist_tile(
       yo[i][k] = w.y[i][k];
       if (FULL || (row_ok && k < nvc)) {
         const float xv = w.x[i].get(k);
-        const float f = fast_sigmoid(__builtin_fmaf(vf[k], prev, w.f[i].get(k)), nbf[k]);
+        const float f = sd_gate(-kLog2e * vf[k], prev, sd_zq(w.f[i].get(k), nbf[k]));
         const float dx = prev - xv;
         const float F = __builtin_fmaf(f, dx, xv);
         const float J = __builtin_fmaf(dx * (f - f * f), vf[k], f);
@@ -403,27 +414,121 @@ struct SdFusedShared {
   uint32_t dm[kDeerFuseMax][NW];
 };
 
+// Newton iteration lev over one tile of the fused walk: the iterate c_lev
+// (yout) from c_{lev-1} (yin) in registers; ent holds c_{lev-1} at the step
+// before this wave's first row on entry and c_lev there on exit.  zq and xv:
+// the tile's gate inputs (sd_zq) and z_x, unpacked once.  The update norm
+// folds |c_lev - c_{lev-1}| with the NaN-propagating maximum (v_maximum3_f32):
+// a non-finite step still reads as the largest update, since the bits of a
+// non-negative float or a NaN order as unsigned integers.
+template <int NW, int L, int CPT, bool FULL>
+__device__ __forceinline__ void sru_deer_fused_level(
+    int lev, const float (&zq)[L][CPT], const float (&xv)[L][CPT], const float (&yin)[L][CPT],
+    float (&yout)[L][CPT], float (&ent)[CPT], int64_t row0, int64_t T, uint32_t off, int nvc,
+    const float (&vf)[CPT], bool keep_start, SdFusedShared<NW, CPT>& s, int wid) {
+  float Jv[L][CPT], Bv[L][CPT];
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const bool row_ok = FULL || row0 + i < T;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const float prev = (i > 0) ? yin[i - 1][k] : ent[k];
+      if (FULL || (row_ok && k < nvc)) {
+        const float f = sd_gate(-kLog2e * vf[k], prev, zq[i][k]);
+        const float dx = prev - xv[i][k];
+        const float F = __builtin_fmaf(f, dx, xv[i][k]);
+        const float J = __builtin_fmaf(dx * (f - f * f), vf[k], f);
+        Jv[i][k] = J;
+        Bv[i][k] = __builtin_fmaf(-J, prev, F);
+      } else {  // identity map past the end
+        Jv[i][k] = 1.0f;
+        Bv[i][k] = 0.0f;
+      }
+    }
+  }
+  float A[CPT], B[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    A[k] = Jv[0][k];
+    B[k] = Bv[0][k];
+#pragma unroll
+    for (int i = 1; i < L; ++i) {
+      B[k] = __builtin_fmaf(Jv[i][k], B[k], Bv[i][k]);
+      A[k] = A[k] * Jv[i][k];
+    }
+  }
+  // the earlier waves' maps applied to iteration lev's state entering the tile
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    s.A[wid][off + k] = A[k];
+    s.B[wid][off + k] = B[k];
+  }
+  __syncthreads();
+  float x[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    float PA = 1.0f, PB = 0.0f;
+    for (int w = 0; w < wid; ++w) {
+      PB = __builtin_fmaf(s.A[w][off + k], PB, s.B[w][off + k]);
+      PA = PA * s.A[w][off + k];
+    }
+    x[k] = __builtin_fmaf(PA, s.ck[lev][off + k], PB);
+  }
+  // every wave has read ck[0] (before the barrier above): the last wave now
+  // keeps the starting iterate at the tile's last row for the next tile
+  if (keep_start && wid == NW - 1) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) s.ck[0][off + k] = yin[L - 1][k];
+  }
+  float dmf = 0.0f;
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) ent[k] = x[k];  // c_lev before this wave's first row
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const bool row_ok = FULL || row0 + i < T;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      x[k] = __builtin_fmaf(Jv[i][k], x[k], Bv[i][k]);
+      const float d = __builtin_elementwise_maximum(dmf, fabsf(x[k] - yin[i][k]));
+      dmf = (FULL || (row_ok && k < nvc)) ? d : dmf;
+      yout[i][k] = x[k];
+    }
+  }
+  const uint32_t dmax = wave_max_u32(as_u32(dmf));
+  if ((threadIdx.x & (kWave - 1)) == 0 && dmax > s.dm[lev - 1][wid]) s.dm[lev - 1][wid] = dmax;
+  __syncthreads();  // every wave has read ck[lev] and this level's maps
+  if (wid == NW - 1) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) s.ck[lev][off + k] = x[k];
+  }
+}
+
 template <typename IO, int NW, int L, int CPT, bool FULL, bool NT>
 __device__ __forceinline__ void sru_deer_fused_tile(
     const IO* __restrict__ zf, const IO* __restrict__ zx, const float* __restrict__ c0p,
     const float* __restrict__ y0, float* __restrict__ out, int64_t row0, int64_t T, int64_t C,
     int64_t cbase, uint32_t off, int nvc, int m, const float (&nbf)[CPT], const float (&vf)[CPT],
     SdFusedShared<NW, CPT>& s, int wid) {
-  IoRow<IO, CPT> fr[L], xr[L];
-  float y[L][CPT];
+  float zq[L][CPT], xv[L][CPT], ya[L][CPT], yb[L][CPT];
   {
     const IO* fp = zf + row0 * C + cbase;
     const IO* xp = zx + row0 * C + cbase;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       const int nv = (FULL || row0 + i < T) ? nvc : 0;
-      fr[i].template load<FULL, NT>(fp, off, nv);
-      xr[i].template load<FULL, NT>(xp, off, nv);
+      IoRow<IO, CPT> fr, xr;
+      fr.template load<FULL, NT>(fp, off, nv);
+      xr.template load<FULL, NT>(xp, off, nv);
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        zq[i][k] = sd_zq(fr.get(k), nbf[k]);
+        xv[i][k] = xr.get(k);
+      }
       if (y0) {
-        load_row<CPT, FULL, NT>(y0 + (row0 + i) * C + cbase, off, nv, 0.0f, y[i]);
+        load_row<CPT, FULL, NT>(y0 + (row0 + i) * C + cbase, off, nv, 0.0f, ya[i]);
       } else {
 #pragma unroll
-        for (int k = 0; k < CPT; ++k) y[i][k] = 0.0f;
+        for (int k = 0; k < CPT; ++k) ya[i][k] = 0.0f;
       }
       fp += C;
       xp += C;
@@ -446,89 +551,28 @@ __device__ __forceinline__ void sru_deer_fused_tile(
 #pragma unroll
     for (int k = 0; k < CPT; ++k) ent[k] = 0.0f;
   }
+  // iterates alternate between the two register sets
+  const bool keep = y0 != nullptr;
+  int lev = 1;
 #pragma unroll 1
-  for (int lev = 1; lev <= m; ++lev) {
-    float Jv[L][CPT], Bv[L][CPT];
+  for (; lev + 1 <= m; lev += 2) {
+    sru_deer_fused_level<NW, L, CPT, FULL>(lev, zq, xv, ya, yb, ent, row0, T, off, nvc, vf,
+                                           keep && lev == 1, s, wid);
+    sru_deer_fused_level<NW, L, CPT, FULL>(lev + 1, zq, xv, yb, ya, ent, row0, T, off, nvc, vf,
+                                           false, s, wid);
+  }
+  if (lev <= m) {
+    sru_deer_fused_level<NW, L, CPT, FULL>(lev, zq, xv, ya, yb, ent, row0, T, off, nvc, vf,
+                                           keep && lev == 1, s, wid);
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
-      const bool row_ok = FULL || row0 + i < T;
+    for (int i = 0; i < L; ++i)
 #pragma unroll
-      for (int k = 0; k < CPT; ++k) {
-        const float prev = (i > 0) ? y[i - 1][k] : ent[k];
-        if (FULL || (row_ok && k < nvc)) {
-          const float xv = xr[i].get(k);
-          const float f = fast_sigmoid(__builtin_fmaf(vf[k], prev, fr[i].get(k)), nbf[k]);
-          const float dx = prev - xv;
-          const float F = __builtin_fmaf(f, dx, xv);
-          const float J = __builtin_fmaf(dx * (f - f * f), vf[k], f);
-          Jv[i][k] = J;
-          Bv[i][k] = __builtin_fmaf(-J, prev, F);
-        } else {  // identity map past the end
-          Jv[i][k] = 1.0f;
-          Bv[i][k] = 0.0f;
-        }
-      }
-    }
-    float A[CPT], B[CPT];
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      A[k] = Jv[0][k];
-      B[k] = Bv[0][k];
-#pragma unroll
-      for (int i = 1; i < L; ++i) {
-        B[k] = __builtin_fmaf(Jv[i][k], B[k], Bv[i][k]);
-        A[k] = A[k] * Jv[i][k];
-      }
-    }
-    // the earlier waves' maps applied to iteration lev's state entering the tile
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      s.A[wid][off + k] = A[k];
-      s.B[wid][off + k] = B[k];
-    }
-    __syncthreads();
-    float x[CPT];
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      float PA = 1.0f, PB = 0.0f;
-      for (int w = 0; w < wid; ++w) {
-        PB = __builtin_fmaf(s.A[w][off + k], PB, s.B[w][off + k]);
-        PA = PA * s.A[w][off + k];
-      }
-      x[k] = __builtin_fmaf(PA, s.ck[lev][off + k], PB);
-    }
-    // every wave has read ck[0] (before the barrier above): the last wave now
-    // keeps the starting iterate at the tile's last row for the next tile
-    if (lev == 1 && wid == NW - 1 && y0) {
-#pragma unroll
-      for (int k = 0; k < CPT; ++k) s.ck[0][off + k] = y[L - 1][k];
-    }
-    uint32_t dmax = 0;
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) ent[k] = x[k];  // c_lev before this wave's first row
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-      const bool row_ok = FULL || row0 + i < T;
-#pragma unroll
-      for (int k = 0; k < CPT; ++k) {
-        x[k] = __builtin_fmaf(Jv[i][k], x[k], Bv[i][k]);
-        const uint32_t d = as_u32(fabsf(x[k] - y[i][k]));
-        if (FULL || (row_ok && k < nvc)) dmax = d > dmax ? d : dmax;
-        y[i][k] = x[k];
-      }
-    }
-    dmax = wave_max_u32(dmax);
-    if ((threadIdx.x & (kWave - 1)) == 0 && dmax > s.dm[lev - 1][wid]) s.dm[lev - 1][wid] = dmax;
-    __syncthreads();  // every wave has read ck[lev] and this level's maps
-    if (wid == NW - 1) {
-#pragma unroll
-      for (int k = 0; k < CPT; ++k) s.ck[lev][off + k] = x[k];
-    }
+      for (int k = 0; k < CPT; ++k) ya[i][k] = yb[i][k];
   }
   float* op = out + row0 * C + cbase;
 #pragma unroll
   for (int i = 0; i < L; ++i) {
-    store_row<CPT, FULL, NT>(op, off, (FULL || row0 + i < T) ? nvc : 0, y[i]);
+    store_row<CPT, FULL, NT>(op, off, (FULL || row0 + i < T) ? nvc : 0, ya[i]);
     op += C;
   }
 }
