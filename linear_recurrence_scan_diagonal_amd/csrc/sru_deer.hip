@@ -400,17 +400,20 @@ __global__ __launch_bounds__(NW* kWave) void k_sru_deer_iter_persist(
 // the time tiles in order and, for each tile, loads z_f, z_x and the starting
 // iterate once and computes iterates 1..m, each from the previous one in
 // registers.  Iteration k's per-channel state entering the tile sits in LDS
-// (ck[k]); c_{k-1} at the step before a wave's first row is iteration k-1's
-// state entering that wave (for k = 1: the starting iterate, from memory
-// inside the tile and from ck[0] across tiles).  Same per-step map and norm as
+// (ck, two copies that alternate by tile); c_{k-1} at the step before a wave's
+// first row is iteration k-1's state entering that wave (for k = 1: the
+// starting iterate, from memory inside the tile and from y0c across tiles).
+// The wave maps alternate by iteration parity, so each iteration needs one
+// barrier, and each tile one more at its end.  Same per-step map and norm as
 // sru_deer_persist_tile; only the last iterate is stored.  Pass (sets) and
 // redo (rec) forms as in k_deer_fused.
 // ---------------------------------------------------------------------------
 template <int NW, int CPT>
 struct SdFusedShared {
-  float A[NW][kWave * CPT];
-  float B[NW][kWave * CPT];
-  float ck[kDeerFuseMax + 1][kWave * CPT];
+  float A[2][NW][kWave * CPT];                // wave maps, by level parity
+  float B[2][NW][kWave * CPT];
+  float y0c[kWave * CPT];                     // starting iterate at the last row before the tile
+  float ck[2][kDeerFuseMax][kWave * CPT];     // [tile parity][lev - 1]: state entering the tile
   uint32_t dm[kDeerFuseMax][NW];
 };
 
@@ -425,7 +428,8 @@ template <int NW, int L, int CPT, bool FULL>
 __device__ __forceinline__ void sru_deer_fused_level(
     int lev, const float (&zq)[L][CPT], const float (&xv)[L][CPT], const float (&yin)[L][CPT],
     float (&yout)[L][CPT], float (&ent)[CPT], int64_t row0, int64_t T, uint32_t off, int nvc,
-    const float (&vf)[CPT], bool keep_start, SdFusedShared<NW, CPT>& s, int wid) {
+    const float (&vf)[CPT], bool keep_start, int tpar, SdFusedShared<NW, CPT>& s, int wid) {
+  const int lp = lev & 1;
   float Jv[L][CPT], Bv[L][CPT];
 #pragma unroll
   for (int i = 0; i < L; ++i) {
@@ -460,8 +464,8 @@ __device__ __forceinline__ void sru_deer_fused_level(
   // the earlier waves' maps applied to iteration lev's state entering the tile
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
-    s.A[wid][off + k] = A[k];
-    s.B[wid][off + k] = B[k];
+    s.A[lp][wid][off + k] = A[k];
+    s.B[lp][wid][off + k] = B[k];
   }
   __syncthreads();
   float x[CPT];
@@ -469,16 +473,16 @@ __device__ __forceinline__ void sru_deer_fused_level(
   for (int k = 0; k < CPT; ++k) {
     float PA = 1.0f, PB = 0.0f;
     for (int w = 0; w < wid; ++w) {
-      PB = __builtin_fmaf(s.A[w][off + k], PB, s.B[w][off + k]);
-      PA = PA * s.A[w][off + k];
+      PB = __builtin_fmaf(s.A[lp][w][off + k], PB, s.B[lp][w][off + k]);
+      PA = PA * s.A[lp][w][off + k];
     }
-    x[k] = __builtin_fmaf(PA, s.ck[lev][off + k], PB);
+    x[k] = __builtin_fmaf(PA, s.ck[tpar][lev - 1][off + k], PB);
   }
-  // every wave has read ck[0] (before the barrier above): the last wave now
+  // every wave has read y0c (before the barrier above): the last wave now
   // keeps the starting iterate at the tile's last row for the next tile
   if (keep_start && wid == NW - 1) {
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) s.ck[0][off + k] = yin[L - 1][k];
+    for (int k = 0; k < CPT; ++k) s.y0c[off + k] = yin[L - 1][k];
   }
   float dmf = 0.0f;
 #pragma unroll
@@ -496,10 +500,13 @@ __device__ __forceinline__ void sru_deer_fused_level(
   }
   const uint32_t dmax = wave_max_u32(as_u32(dmf));
   if ((threadIdx.x & (kWave - 1)) == 0 && dmax > s.dm[lev - 1][wid]) s.dm[lev - 1][wid] = dmax;
-  __syncthreads();  // every wave has read ck[lev] and this level's maps
+  // the state after the tile goes to the other tile-parity slot, which no wave
+  // reads before the barrier that ends this tile; the maps of level lev + 2
+  // (same parity) are written after every wave has passed level lev + 1's
+  // barrier, so after it has read these
   if (wid == NW - 1) {
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) s.ck[lev][off + k] = x[k];
+    for (int k = 0; k < CPT; ++k) s.ck[tpar ^ 1][lev - 1][off + k] = x[k];
   }
 }
 
@@ -508,7 +515,7 @@ __device__ __forceinline__ void sru_deer_fused_tile(
     const IO* __restrict__ zf, const IO* __restrict__ zx, const float* __restrict__ c0p,
     const float* __restrict__ y0, float* __restrict__ out, int64_t row0, int64_t T, int64_t C,
     int64_t cbase, uint32_t off, int nvc, int m, const float (&nbf)[CPT], const float (&vf)[CPT],
-    SdFusedShared<NW, CPT>& s, int wid) {
+    int tpar, SdFusedShared<NW, CPT>& s, int wid) {
   float zq[L][CPT], xv[L][CPT], ya[L][CPT], yb[L][CPT];
   {
     const IO* fp = zf + row0 * C + cbase;
@@ -544,7 +551,7 @@ __device__ __forceinline__ void sru_deer_fused_tile(
     for (int k = 0; k < CPT; ++k) ent[k] = 0.0f;
   } else if (wid == 0) {
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) ent[k] = s.ck[0][off + k];
+    for (int k = 0; k < CPT; ++k) ent[k] = s.y0c[off + k];
   } else if (row0 <= T) {  // inside the tile: not yet overwritten, even in place
     load_row<CPT, false, false>(y0 + (row0 - 1) * C + cbase, off, nvc, 0.0f, ent);
   } else {  // a wave wholly past the end (its rows are not stored)
@@ -557,13 +564,13 @@ __device__ __forceinline__ void sru_deer_fused_tile(
 #pragma unroll 1
   for (; lev + 1 <= m; lev += 2) {
     sru_deer_fused_level<NW, L, CPT, FULL>(lev, zq, xv, ya, yb, ent, row0, T, off, nvc, vf,
-                                           keep && lev == 1, s, wid);
+                                           keep && lev == 1, tpar, s, wid);
     sru_deer_fused_level<NW, L, CPT, FULL>(lev + 1, zq, xv, yb, ya, ent, row0, T, off, nvc, vf,
-                                           false, s, wid);
+                                           false, tpar, s, wid);
   }
   if (lev <= m) {
     sru_deer_fused_level<NW, L, CPT, FULL>(lev, zq, xv, ya, yb, ent, row0, T, off, nvc, vf,
-                                           keep && lev == 1, s, wid);
+                                           keep && lev == 1, tpar, s, wid);
 #pragma unroll
     for (int i = 0; i < L; ++i)
 #pragma unroll
@@ -575,6 +582,9 @@ __device__ __forceinline__ void sru_deer_fused_tile(
     store_row<CPT, FULL, NT>(op, off, (FULL || row0 + i < T) ? nvc : 0, ya[i]);
     op += C;
   }
+  // the next tile reads y0c and this tile's states after the tile, and
+  // rewrites the wave maps of level 1
+  __syncthreads();
 }
 
 template <typename IO, int NW, int L, int CPT, bool NT>
@@ -609,8 +619,10 @@ __device__ __forceinline__ void sru_deer_fused_body(
     }
   }
   for (int j = threadIdx.x; j < (kDeerFuseMax + 1) * CW; j += NW * kWave) {
-    const int c = j % CW;
-    s.ck[j / CW][c] = (c0p && cbase + c < C) ? c0p[cbase + c] : 0.0f;  // every level starts at c0
+    const int c = j % CW, lv = j / CW;
+    const float v = (c0p && cbase + c < C) ? c0p[cbase + c] : 0.0f;  // every level starts at c0
+    if (lv == 0) s.y0c[c] = v;
+    else s.ck[0][lv - 1][c] = v;
   }
   for (int j = threadIdx.x; j < kDeerFuseMax * NW; j += NW * kWave) s.dm[j / NW][j % NW] = 0u;
   __syncthreads();
@@ -618,12 +630,13 @@ __device__ __forceinline__ void sru_deer_fused_body(
   const int64_t w0 = (int64_t)wid * L;
 #pragma unroll 1
   for (int64_t tb = 0; tb < ntb; ++tb) {
+    const int tpar = (int)(tb & 1);
     if (cfull && tb < nfull)
       sru_deer_fused_tile<IO, NW, L, CPT, true, NT>(zf, zx, c0p, y0, out, tb * TW + w0, T, C,
-                                                    cbase, off, nvc, m, nbf, vf, s, wid);
+                                                    cbase, off, nvc, m, nbf, vf, tpar, s, wid);
     else
       sru_deer_fused_tile<IO, NW, L, CPT, false, NT>(zf, zx, c0p, y0, out, tb * TW + w0, T, C,
-                                                     cbase, off, nvc, m, nbf, vf, s, wid);
+                                                     cbase, off, nvc, m, nbf, vf, tpar, s, wid);
   }
   if (redo) return;
   __syncthreads();
