@@ -911,15 +911,24 @@ def cpu_baseline(w, args, np, I):
 
 
 def cpu_model() -> str:
-    """The host CPU's model name (first 'model name' entry of /proc/cpuinfo)."""
+    """The host CPU's model name (first processor entry of /proc/cpuinfo), with
+    its family / model / stepping numbers, which identify the core generation
+    where a virtual machine reports only a generic name."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.lower().startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    if fields:
+                        break  # end of the first processor entry
+                    continue
+                key, _, val = line.partition(":")
+                fields.setdefault(key.strip().lower(), val.strip())
     except OSError:
         pass
-    return "unknown"
+    name = fields.get("model name", "unknown")
+    ids = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields]
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
 if __name__ == "__main__":
