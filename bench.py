@@ -7,7 +7,8 @@ fp32 configuration); one step = lrs_scan_fwd then lrs_scan_bwd over the same
 resident inputs.  The same run also measures scan_fwd_bwd (B=8, D=512,
 T=4096) and reports it inside the line under "also".  Other workloads
 (--workload): scan_fwd_bwd, scan_fused (that step as one lrs_scan_fwd_bwd
-call), scan_short (T = 32, sequential kernels),
+call), scan_short (T = 32, sequential kernels), scan_fwd_bwd_bf16 and
+scan_long_bf16 (the scans with bf16 arrays, fp32 state),
 sru_fwd / sru_fwd_bwd (bf16 SRU layer), sru_deer (SRU with v_f*c_{t-1}
 by DEER), lstm_fwd_bwd
 (bf16 LSTM cell-state layer with input-only gates), deer / deer_fwd_bwd
@@ -43,6 +44,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
 # algorithmic bytes per element of each kernel (every input read once, every
 # output written once; per-channel vectors are negligible)
 BYTES_PER_ELEM = {"scan_fwd_f32": 12, "scan_bwd_f32": 20, "sru_fwd_bf16": 8,
+                  "scan_fwd_bf16": 6, "scan_bwd_bf16": 10,  # the scans with bf16 arrays
                   "sru_fwd_save_bf16": 12,  # + the fp32 cell states for the backward
                   "sru_bwd_bf16": 18,       # z_f, z_r, z_x, dL/dh, c in; three gradients out
                   "scan_fused_f32": 24,     # a, b, dL/dh in; h, dL/da, dL/db out
@@ -110,11 +112,17 @@ def measured_traffic(workload: str, kernel_key: str):
 
 
 # rocprof kernel names of each timed entry point (substring match)
-KERNEL_NAMES = {"scan_fwd_f32": ("k_scan_fwd_bdt", "k_scan_fwd_tbd", "k_scan_fwd_serial",
-                                 "k_scan_fwd_packed"),
-                "scan_bwd_f32": ("k_scan_bwd_bdt", "k_scan_bwd_tbd", "k_scan_bwd_serial",
-                                 "k_scan_bwd_packed"),
-                "scan_fused_f32": ("k_scan_fused_bdt",),
+KERNEL_NAMES = {"scan_fwd_f32": ("k_scan_fwd_bdt<float", "k_scan_fwd_tbd<float",
+                                 "k_scan_fwd_serial<float", "k_scan_fwd_packed<float"),
+                "scan_bwd_f32": ("k_scan_bwd_bdt<float", "k_scan_bwd_tbd<float",
+                                 "k_scan_bwd_serial<float", "k_scan_bwd_packed<float"),
+                "scan_fwd_bf16": ("k_scan_fwd_bdt<unsigned short", "k_scan_fwd_tbd<unsigned short",
+                                  "k_scan_fwd_serial<unsigned short",
+                                  "k_scan_fwd_packed<unsigned short"),
+                "scan_bwd_bf16": ("k_scan_bwd_bdt<unsigned short", "k_scan_bwd_tbd<unsigned short",
+                                  "k_scan_bwd_serial<unsigned short",
+                                  "k_scan_bwd_packed<unsigned short"),
+                "scan_fused_f32": ("k_scan_fused_bdt<float",),
                 "sru_fwd_bf16": ("k_sru_fwd<unsigned short", "k_sru_fwd_persist<unsigned short"),
                 "sru_fwd_save_bf16": ("k_sru_fwd<unsigned short",
                                       "k_sru_fwd_persist<unsigned short"),
@@ -130,6 +138,8 @@ KERNEL_NAMES = {"scan_fwd_f32": ("k_scan_fwd_bdt", "k_scan_fwd_tbd", "k_scan_fwd
 WORKLOAD_KERNELS = {"scan_fwd_small": ("scan_fwd_f32",),
                     "scan_fwd_bwd": ("scan_fwd_f32", "scan_bwd_f32"),
                     "scan_long": ("scan_fwd_f32", "scan_bwd_f32"),
+                    "scan_fwd_bwd_bf16": ("scan_fwd_bf16", "scan_bwd_bf16"),
+                    "scan_long_bf16": ("scan_fwd_bf16", "scan_bwd_bf16"),
                     "scan_fused": ("scan_fused_f32",),
                     "scan_short": ("scan_fwd_f32", "scan_bwd_f32"),
                     "sru_fwd": ("sru_fwd_bf16",),
@@ -291,7 +301,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="scan_long",
-                   choices=["scan_fwd_bwd", "scan_fused", "scan_short", "scan_long", "sru_fwd",
+                   choices=["scan_fwd_bwd", "scan_fused", "scan_short", "scan_long",
+                            "scan_fwd_bwd_bf16", "scan_long_bf16", "sru_fwd",
                             "sru_deer", "sru_fwd_bwd", "lstm_fwd_bwd",
                             "deer", "deer_fwd_bwd", "scan_fwd_small"])
     p.add_argument("--layout", default="bdt", choices=["bdt", "tbd"])
@@ -472,28 +483,37 @@ def measure(args, np, torch, lrs, I, dev):
         layout = args.layout
         fwd_only = args.workload == "scan_fwd_small"
         x = I.scan_inputs(w, with_grad=not fwd_only)
-        a, b = to_dev(x["a"], layout), to_dev(x["b"], layout)
-        g = None if fwd_only else to_dev(x["g"], layout)
+        bf16 = w.io == "bf16"
+        if bf16:  # a, b, dL/dh rounded to bf16 (uploaded as bit patterns)
+            def to_dev16(x_ct, layout):
+                return to_dev(I.to_bf16_bits(x_ct).view(np.int16), layout).view(torch.bfloat16)
+            a, b = to_dev16(x["a"], layout), to_dev16(x["b"], layout)
+            g = None if fwd_only else to_dev16(x["g"], layout)
+        else:
+            a, b = to_dev(x["a"], layout), to_dev(x["b"], layout)
+            g = None if fwd_only else to_dev(x["g"], layout)
         h0 = torch.from_numpy(x["h0"].reshape(B, D)).to(dev)
         h = torch.empty_like(a)
         ga, gb = torch.empty_like(a), torch.empty_like(a)
         gh0 = torch.empty((B, D), dtype=torch.float32, device=dev)
-        ws_bytes = lrs.scan_workspace_bytes(B, D, T, layout)
+        ws_bytes = lrs.scan_workspace_bytes(B, D, T, layout, a.dtype)
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        sfx = "bf16" if bf16 else "f32"
 
-        calls = {"scan_fwd_f32": lambda: lrs.scan_fwd(a, b, h0, layout=layout, out=h, workspace=ws)}
+        calls = {f"scan_fwd_{sfx}": lambda: lrs.scan_fwd(a, b, h0, layout=layout, out=h,
+                                                          workspace=ws)}
         if args.workload == "scan_fused":
             calls = {"scan_fused_f32": lambda: lrs.scan_fwd_bwd(a, b, g, h0, layout=layout,
                                                                 out=(h, ga, gb, gh0), workspace=ws)}
         elif not fwd_only:
-            calls["scan_bwd_f32"] = lambda: lrs.scan_bwd(a, h, g, h0, layout=layout, grad_a=ga,
-                                                         grad_b=gb, grad_h0=gh0, workspace=ws)
+            calls[f"scan_bwd_{sfx}"] = lambda: lrs.scan_bwd(a, h, g, h0, layout=layout, grad_a=ga,
+                                                            grad_b=gb, grad_h0=gh0, workspace=ws)
 
         def step():
             for fn in calls.values():
                 fn()
         kernels = list(calls)
-        dtype = "f32"
+        dtype = "bf16 I/O, f32 state" if bf16 else "f32"
         config = {"workload": w.name, "B": B, "D": D, "T": T, "layout": layout,
                   "pass": "fwd" if fwd_only else ("fwd+bwd, one call" if args.workload == "scan_fused"
                                                    else "fwd+bwd")}

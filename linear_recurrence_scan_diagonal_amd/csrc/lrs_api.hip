@@ -70,14 +70,15 @@ bool rows_grid_ok(const lrs::RowPlan& p, int64_t C) {
   return grid_ok(C * p.nchunk, p.threads());
 }
 
-int scan_ws_needs(int64_t C, int64_t T, int layout, size_t* bytes) {
+int scan_ws_needs(int64_t C, int64_t T, int layout, int dtype, size_t* bytes) {
   if (layout == LRS_LAYOUT_BDT) {
-    const lrs::RowPlan f = lrs::plan_scan_fwd_rows(C, T), b = lrs::plan_scan_bwd_rows(C, T);
+    const lrs::RowPlan f = lrs::plan_scan_fwd_rows(C, T, lrs::Opts(), dtype),
+                       b = lrs::plan_scan_bwd_rows(C, T, lrs::Opts(), dtype);
     const size_t bf = f.nchunk > 1 ? lookback_bytes(C * f.nchunk, C) : 0;
     const size_t bb = b.nchunk > 1 ? lookback_bytes(C * b.nchunk, C) : 0;
     *bytes = bf > bb ? bf : bb;
   } else {
-    const lrs::ColPlan f = lrs::plan_scan_fwd_tbd(C, T), b = lrs::plan_scan_bwd_tbd(C, T);
+    const lrs::ColPlan f = lrs::plan_scan_fwd_tbd(C, T, dtype), b = lrs::plan_scan_bwd_tbd(C, T, dtype);
     const size_t bf = lookback_bytes(lrs::col_status_words(f), f.ncb);
     const size_t bb = lookback_bytes(lrs::col_status_words(b), b.ncb);
     *bytes = bf > bb ? bf : bb;
@@ -155,7 +156,7 @@ size_t lrs_scan_workspace_bytes(int64_t B, int64_t D, int64_t T, int layout, int
     return 0;
   if (N == 0) return 0;
   size_t bytes = 0;
-  scan_ws_needs(C, T, layout, &bytes);
+  scan_ws_needs(C, T, layout, dtype, &bytes);
   return bytes;
 }
 
@@ -164,7 +165,6 @@ static int scan_common_checks(int64_t B, int64_t D, int64_t T, int layout, int d
   if (!shape_ok(B, D, T, C, N)) return LRS_ERR_INVALID_ARG;
   if (layout != LRS_LAYOUT_BDT && layout != LRS_LAYOUT_TBD) return LRS_ERR_INVALID_ARG;
   if (dtype != LRS_F32 && dtype != LRS_BF16) return LRS_ERR_INVALID_ARG;
-  if (dtype != LRS_F32) return LRS_ERR_UNSUPPORTED;
   return LRS_OK;
 }
 
@@ -177,20 +177,22 @@ static int scan_fwd_impl(const void* a, const void* b, const float* h0, void* h,
   if (rc != LRS_OK) return rc;
   if (N == 0) return LRS_OK;
   if (!a || !b || !h) return LRS_ERR_INVALID_ARG;
-  if (!aligned(a, 4) || !aligned(b, 4) || !aligned(h, 4) || (h0 && !aligned(h0, 4)))
+  const size_t es = (size_t)lrs::io_bytes(dtype);
+  if (!aligned(a, es) || !aligned(b, es) || !aligned(h, es) || (h0 && !aligned(h0, 4)))
     return LRS_ERR_INVALID_ARG;
-  const size_t nbytes = (size_t)N * 4;
+  const size_t nbytes = (size_t)N * es;
   if (overlap(h, nbytes, a, nbytes) || overlap(h, nbytes, b, nbytes) ||
       overlap(h, nbytes, h0, (size_t)C * 4))
     return LRS_ERR_INVALID_ARG;
   size_t need = 0;
-  scan_ws_needs(C, T, layout, &need);
+  scan_ws_needs(C, T, layout, dtype, &need);
   if (need && (!workspace || workspace_bytes < need)) return LRS_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  const bool al16 = aligned(a, 16) && aligned(b, 16) && aligned(h, 16);
+  // 4-element groups: 16-byte (fp32) or 8-byte (bf16) accesses
+  const bool al16 = aligned(a, 4 * es) && aligned(b, 4 * es) && aligned(h, 4 * es);
 
   if (layout == LRS_LAYOUT_BDT) {
-    const lrs::RowPlan p = lrs::plan_scan_fwd_rows(C, T, opt);
+    const lrs::RowPlan p = lrs::plan_scan_fwd_rows(C, T, opt, dtype);
     if (!rows_grid_ok(p, C)) return LRS_ERR_UNSUPPORTED;
     uint64_t* status = nullptr;
     unsigned* tickets = nullptr;
@@ -201,12 +203,12 @@ static int scan_fwd_impl(const void* a, const void* b, const float* h0, void* h,
       rc = hip_status(lrs::launch_reset(status, C * p.nchunk, tickets, C, nullptr, 0, s));
       if (rc != LRS_OK) return rc;
     }
-    // packed blocks start 16-byte aligned whatever T is
+    // packed blocks start group-aligned whatever T is
     const int vec = al16 && (p.packed || T % 4 == 0);
-    return hip_status(lrs::launch_scan_fwd_bdt((const float*)a, (const float*)b, h0, (float*)h, C,
-                                               T, p, vec, status, tickets, s));
+    return hip_status(lrs::launch_scan_fwd_bdt(a, b, h0, h, dtype, C, T, p, vec, status, tickets,
+                                               s));
   }
-  const lrs::ColPlan p = lrs::plan_scan_fwd_tbd(C, T);
+  const lrs::ColPlan p = lrs::plan_scan_fwd_tbd(C, T, dtype);
   if (!grid_ok(p.ncb * p.ntb, p.nw * 64)) return LRS_ERR_UNSUPPORTED;
   uint64_t* status = nullptr;
   unsigned* tickets = nullptr;
@@ -219,8 +221,7 @@ static int scan_fwd_impl(const void* a, const void* b, const float* h0, void* h,
     if (rc != LRS_OK) return rc;
   }
   const int vec = al16 && (C % p.cpt == 0);
-  return hip_status(lrs::launch_scan_fwd_tbd((const float*)a, (const float*)b, h0, (float*)h, C, T,
-                                             p, vec, status, tickets, s));
+  return hip_status(lrs::launch_scan_fwd_tbd(a, b, h0, h, dtype, C, T, p, vec, status, tickets, s));
 }
 
 static int scan_bwd_impl(const void* a, const void* h, const float* h0, const void* grad_h, void* grad_a,
@@ -237,10 +238,11 @@ static int scan_bwd_impl(const void* a, const void* h, const float* h0, const vo
     return LRS_OK;
   }
   if (!a || !h || !grad_h || !grad_a || !grad_b) return LRS_ERR_INVALID_ARG;
-  if (!aligned(a, 4) || !aligned(h, 4) || !aligned(grad_h, 4) || !aligned(grad_a, 4) ||
-      !aligned(grad_b, 4) || (h0 && !aligned(h0, 4)) || (grad_h0 && !aligned(grad_h0, 4)))
+  const size_t es = (size_t)lrs::io_bytes(dtype);
+  if (!aligned(a, es) || !aligned(h, es) || !aligned(grad_h, es) || !aligned(grad_a, es) ||
+      !aligned(grad_b, es) || (h0 && !aligned(h0, 4)) || (grad_h0 && !aligned(grad_h0, 4)))
     return LRS_ERR_INVALID_ARG;
-  const size_t nb = (size_t)N * 4, cb = (size_t)C * 4;
+  const size_t nb = (size_t)N * es, cb = (size_t)C * 4;
   // outputs must not overlap inputs, except grad_b == grad_h exactly
   const void* ins[4] = {a, h, h0, grad_h};
   const size_t insz[4] = {nb, nb, cb, nb};
@@ -254,13 +256,13 @@ static int scan_bwd_impl(const void* a, const void* h, const float* h0, const vo
       overlap(grad_h0, cb, grad_b, nb))
     return LRS_ERR_INVALID_ARG;
   size_t need = 0;
-  scan_ws_needs(C, T, layout, &need);
+  scan_ws_needs(C, T, layout, dtype, &need);
   if (need && (!workspace || workspace_bytes < need)) return LRS_ERR_WORKSPACE;
-  const bool al16 = aligned(a, 16) && aligned(h, 16) && aligned(grad_h, 16) &&
-                    aligned(grad_a, 16) && aligned(grad_b, 16);
+  const bool al16 = aligned(a, 4 * es) && aligned(h, 4 * es) && aligned(grad_h, 4 * es) &&
+                    aligned(grad_a, 4 * es) && aligned(grad_b, 4 * es);
 
   if (layout == LRS_LAYOUT_BDT) {
-    const lrs::RowPlan p = lrs::plan_scan_bwd_rows(C, T, opt);
+    const lrs::RowPlan p = lrs::plan_scan_bwd_rows(C, T, opt, dtype);
     if (!rows_grid_ok(p, C)) return LRS_ERR_UNSUPPORTED;
     uint64_t* status = nullptr;
     unsigned* tickets = nullptr;
@@ -272,12 +274,10 @@ static int scan_bwd_impl(const void* a, const void* h, const float* h0, const vo
       if (rc != LRS_OK) return rc;
     }
     const int vec = al16 && (p.packed || T % 4 == 0);
-    return hip_status(lrs::launch_scan_bwd_bdt((const float*)a, (const float*)h, h0,
-                                               (const float*)grad_h, (float*)grad_a,
-                                               (float*)grad_b, grad_h0, C, T, p, vec, status,
-                                               tickets, s));
+    return hip_status(lrs::launch_scan_bwd_bdt(a, h, h0, grad_h, grad_a, grad_b, grad_h0, dtype, C,
+                                               T, p, vec, status, tickets, s));
   }
-  const lrs::ColPlan p = lrs::plan_scan_bwd_tbd(C, T);
+  const lrs::ColPlan p = lrs::plan_scan_bwd_tbd(C, T, dtype);
   if (!grid_ok(p.ncb * p.ntb, p.nw * 64)) return LRS_ERR_UNSUPPORTED;
   uint64_t* status = nullptr;
   unsigned* tickets = nullptr;
@@ -290,9 +290,8 @@ static int scan_bwd_impl(const void* a, const void* h, const float* h0, const vo
     if (rc != LRS_OK) return rc;
   }
   const int vec = al16 && (C % p.cpt == 0);
-  return hip_status(lrs::launch_scan_bwd_tbd((const float*)a, (const float*)h, h0,
-                                             (const float*)grad_h, (float*)grad_a, (float*)grad_b,
-                                             grad_h0, C, T, p, vec, status, tickets, s));
+  return hip_status(lrs::launch_scan_bwd_tbd(a, h, h0, grad_h, grad_a, grad_b, grad_h0, dtype, C, T,
+                                             p, vec, status, tickets, s));
 }
 
 static int scan_fwd_bwd_impl(const void* a, const void* b, const float* h0, const void* grad_h, void* h,
@@ -309,11 +308,12 @@ static int scan_fwd_bwd_impl(const void* a, const void* b, const float* h0, cons
     return LRS_OK;
   }
   if (!a || !b || !grad_h || !grad_a || !grad_b) return LRS_ERR_INVALID_ARG;
-  if (!aligned(a, 4) || !aligned(b, 4) || !aligned(grad_h, 4) || !aligned(grad_a, 4) ||
-      !aligned(grad_b, 4) || (h && !aligned(h, 4)) || (h0 && !aligned(h0, 4)) ||
+  const size_t es = (size_t)lrs::io_bytes(dtype);
+  if (!aligned(a, es) || !aligned(b, es) || !aligned(grad_h, es) || !aligned(grad_a, es) ||
+      !aligned(grad_b, es) || (h && !aligned(h, es)) || (h0 && !aligned(h0, 4)) ||
       (grad_h0 && !aligned(grad_h0, 4)))
     return LRS_ERR_INVALID_ARG;
-  const size_t nb = (size_t)N * 4, cb = (size_t)C * 4;
+  const size_t nb = (size_t)N * es, cb = (size_t)C * 4;
   // outputs must not overlap inputs or each other, except grad_b == grad_h exactly
   const void* ins[4] = {a, b, h0, grad_h};
   const size_t insz[4] = {nb, nb, cb, nb};
@@ -327,24 +327,24 @@ static int scan_fwd_bwd_impl(const void* a, const void* b, const float* h0, cons
     for (int o2 = o + 1; o2 < 4; ++o2)
       if (overlap(outs[o], outsz[o], outs[o2], outsz[o2])) return LRS_ERR_INVALID_ARG;
   }
-  const lrs::RowPlan p = lrs::plan_scan_fused_rows(C, T);
+  const lrs::RowPlan p = lrs::plan_scan_fused_rows(C, T, dtype);
   // short channels run the sequential or packed passes when h is wanted anyway
   // (the one-kernel form gives each channel a mostly idle workgroup)
-  const lrs::RowPlan pf = lrs::plan_scan_fwd_rows(C, T, opt);
+  const lrs::RowPlan pf = lrs::plan_scan_fwd_rows(C, T, opt, dtype);
   const bool short_pair = h && (pf.serial || pf.packed);
   if (layout == LRS_LAYOUT_BDT && p.nchunk == 1 && !short_pair) {
     if (!grid_ok(C, p.threads())) return LRS_ERR_UNSUPPORTED;
-    const bool al16 = aligned(a, 16) && aligned(b, 16) && aligned(grad_h, 16) &&
-                      aligned(grad_a, 16) && aligned(grad_b, 16) && (!h || aligned(h, 16));
+    const bool al16 = aligned(a, 4 * es) && aligned(b, 4 * es) && aligned(grad_h, 4 * es) &&
+                      aligned(grad_a, 4 * es) && aligned(grad_b, 4 * es) &&
+                      (!h || aligned(h, 4 * es));
     const int vec = al16 && (T % 4 == 0);
-    return hip_status(lrs::launch_scan_fused_bdt((const float*)a, (const float*)b, h0,
-                                                 (const float*)grad_h, (float*)h, (float*)grad_a,
-                                                 (float*)grad_b, grad_h0, C, T, p, vec, s));
+    return hip_status(lrs::launch_scan_fused_bdt(a, b, h0, grad_h, h, grad_a, grad_b, grad_h0, dtype,
+                                                 C, T, p, vec, s));
   }
   // the two passes, h stored between them (both validated before the first launch)
   if (!h) return LRS_ERR_UNSUPPORTED;
   size_t need = 0;
-  scan_ws_needs(C, T, layout, &need);
+  scan_ws_needs(C, T, layout, dtype, &need);
   if (need && (!workspace || workspace_bytes < need)) return LRS_ERR_WORKSPACE;
   rc = scan_fwd_impl(a, b, h0, h, B, D, T, layout, dtype, workspace, workspace_bytes, stream, opt);
   if (rc != LRS_OK) return rc;

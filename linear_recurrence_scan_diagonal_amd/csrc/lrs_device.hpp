@@ -28,6 +28,35 @@ constexpr int kWave = 64;
 __device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
 
+// ---- I/O element types ------------------------------------------------------
+// Arrays are fp32 or bf16 (stored as uint16_t bit patterns); arithmetic and
+// carried state are always fp32.  bf16 values widen exactly; results round to
+// bf16 nearest-even with gfx950's v_cvt_pk_bf16_f32.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return as_f32(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return as_f32(w & 0xFFFF0000u); }
+
+// Round a pair of fp32 to bf16 (nearest-even), packed low | high << 16.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t f = {lo, hi};
+  const bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+// One element of an fp32 or bf16 array, widened to fp32 / rounded from fp32.
+__device__ __forceinline__ float io_ld(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float io_ld(const uint16_t* p, int64_t i) {
+  return as_f32((uint32_t)p[i] << 16);
+}
+__device__ __forceinline__ void io_st(float* p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void io_st(uint16_t* p, int64_t i, float v) {
+  p[i] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+}
+
 // One Hillis-Steele step across lanes: lane i combines with the lane that the
 // DPP control selects (an earlier lane in scan order):
 //   (A_e, B_e) o (A, B) = (A_e*A, A*B_e + B).
@@ -285,14 +314,57 @@ __device__ __forceinline__ void store_group(float* __restrict__ row, int64_t p, 
   if (p + 3 < T) row[p + 3] = v.w;
 }
 
-// FULL selects the unchecked access; otherwise the checked one above.
-template <bool FULL, bool NT>
-__device__ __forceinline__ float4 ld4(const float* __restrict__ row, int64_t p, int64_t T, bool vec,
+// bf16 groups: the 4 consecutive elements starting at p as one 8-byte access
+// (`vec`: row starts and base pointers 8-byte aligned, p a multiple of 4).
+template <bool NT = false>
+__device__ __forceinline__ float4 load_group_full(const uint16_t* __restrict__ row, int64_t p) {
+  const u32x2_t* q = reinterpret_cast<const u32x2_t*>(row + p);
+  const u32x2_t w = NT ? __builtin_nontemporal_load(q) : *q;
+  return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+}
+
+template <bool NT = false>
+__device__ __forceinline__ float4 load_group(const uint16_t* __restrict__ row, int64_t p, int64_t T,
+                                             bool vec, float fill) {
+  if (vec && p + 4 <= T) return load_group_full<NT>(row, p);
+  float4 v;
+  v.x = (p < T) ? io_ld(row, p) : fill;
+  v.y = (p + 1 < T) ? io_ld(row, p + 1) : fill;
+  v.z = (p + 2 < T) ? io_ld(row, p + 2) : fill;
+  v.w = (p + 3 < T) ? io_ld(row, p + 3) : fill;
+  return v;
+}
+
+template <bool NT = false>
+__device__ __forceinline__ void store_group_full(uint16_t* __restrict__ row, int64_t p, float4 v) {
+  const u32x2_t w = {pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+  u32x2_t* q = reinterpret_cast<u32x2_t*>(row + p);
+  if (NT) __builtin_nontemporal_store(w, q);
+  else *q = w;
+}
+
+template <bool NT = false>
+__device__ __forceinline__ void store_group(uint16_t* __restrict__ row, int64_t p, int64_t T,
+                                            bool vec, float4 v) {
+  if (vec && p + 4 <= T) {
+    store_group_full<NT>(row, p, v);
+    return;
+  }
+  if (p < T) io_st(row, p, v.x);
+  if (p + 1 < T) io_st(row, p + 1, v.y);
+  if (p + 2 < T) io_st(row, p + 2, v.z);
+  if (p + 3 < T) io_st(row, p + 3, v.w);
+}
+
+// FULL selects the unchecked access; otherwise the checked one above (either
+// element type; IO = float or uint16_t for bf16).
+template <bool FULL, bool NT, typename IO>
+__device__ __forceinline__ float4 ld4(const IO* __restrict__ row, int64_t p, int64_t T, bool vec,
                                       float fill) {
   return FULL ? load_group_full<NT>(row, p) : load_group<NT>(row, p, T, vec, fill);
 }
-template <bool FULL, bool NT>
-__device__ __forceinline__ void st4(float* __restrict__ row, int64_t p, int64_t T, bool vec,
+template <bool FULL, bool NT, typename IO>
+__device__ __forceinline__ void st4(IO* __restrict__ row, int64_t p, int64_t T, bool vec,
                                     float4 v) {
   if (FULL) store_group_full<NT>(row, p, v);
   else store_group<NT>(row, p, T, vec, v);

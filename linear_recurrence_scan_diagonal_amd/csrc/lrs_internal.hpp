@@ -37,10 +37,14 @@ struct RowPlan {
   int threads() const { return nw * 64; }
   int64_t chunk() const { return (int64_t)nw * r * 256; }
 };
-RowPlan plan_scan_fwd_rows(int64_t C, int64_t T, const Opts& o = Opts());
-RowPlan plan_scan_bwd_rows(int64_t C, int64_t T, const Opts& o = Opts());
+// Element type of the scan arrays (the C ABI's LRS_F32 / LRS_BF16); state and
+// arithmetic are fp32 either way.
+constexpr int kIoF32 = 0, kIoBf16 = 1;
+constexpr int64_t io_bytes(int io) { return io == kIoBf16 ? 2 : 4; }
+RowPlan plan_scan_fwd_rows(int64_t C, int64_t T, const Opts& o = Opts(), int io = kIoF32);
+RowPlan plan_scan_bwd_rows(int64_t C, int64_t T, const Opts& o = Opts(), int io = kIoF32);
 RowPlan plan_deer_rows(int64_t C, int64_t T);
-RowPlan plan_scan_fused_rows(int64_t C, int64_t T);
+RowPlan plan_scan_fused_rows(int64_t C, int64_t T, int io = kIoF32);
 RowPlan plan_deer_bwd_rows(int64_t C, int64_t T);
 
 // Feature-contiguous kernels: blocks of 64*cpt channels x nw*l steps.
@@ -56,8 +60,8 @@ int device_cus();
 // (device_cus(), or the caller's override).
 int64_t persist_min_blocks(const Opts& o = Opts());
 ColPlan plan_cols(int64_t C, int64_t T, int nw, int l, int cpt);
-ColPlan plan_scan_fwd_tbd(int64_t C, int64_t T);
-ColPlan plan_scan_bwd_tbd(int64_t C, int64_t T);
+ColPlan plan_scan_fwd_tbd(int64_t C, int64_t T, int io = kIoF32);
+ColPlan plan_scan_bwd_tbd(int64_t C, int64_t T, int io = kIoF32);
 // allow_persist = false: the look-back tile plan (workspace queries size for it).
 ColPlan plan_sru(int64_t C, int64_t T, int io_dtype, bool allow_persist = true,
                  const Opts& o = Opts());
@@ -69,29 +73,32 @@ int64_t col_status_words(const ColPlan& p);
 hipError_t launch_reset(uint64_t* status, int64_t nstatus, unsigned* tickets, int64_t ntickets,
                         uint32_t* zero, int64_t nzero, hipStream_t stream);
 
-hipError_t launch_scan_fwd_bdt(const float* a, const float* b, const float* h0, float* h,
+// Scan launchers: a, b, h, g, da, db are arrays of element type `io` (kIoF32
+// or kIoBf16); h0 and dh0 are fp32.  `vec`: rows and base pointers allow
+// 4-element accesses (T % 4 == 0, pointers aligned to 4 elements).
+hipError_t launch_scan_fwd_bdt(const void* a, const void* b, const float* h0, void* h, int io,
                                int64_t C, int64_t T, const RowPlan& p, int vec, uint64_t* status,
                                unsigned* tickets, hipStream_t stream);
-hipError_t launch_scan_bwd_bdt(const float* a, const float* h, const float* h0, const float* g,
-                               float* da, float* db, float* dh0, int64_t C, int64_t T,
+hipError_t launch_scan_bwd_bdt(const void* a, const void* h, const float* h0, const void* g,
+                               void* da, void* db, float* dh0, int io, int64_t C, int64_t T,
                                const RowPlan& p, int vec, uint64_t* status, unsigned* tickets,
                                hipStream_t stream);
 // Sequential per-channel scans (one lane per channel) for short channels.
-hipError_t launch_scan_fwd_serial(const float* a, const float* b, const float* h0, float* h,
+hipError_t launch_scan_fwd_serial(const void* a, const void* b, const float* h0, void* h, int io,
                                   int64_t C, int64_t T, int vec, hipStream_t stream);
-hipError_t launch_scan_bwd_serial(const float* a, const float* h, const float* h0, const float* g,
-                                  float* da, float* db, float* dh0, int64_t C, int64_t T, int vec,
-                                  hipStream_t stream);
-// Packed short channels (plan.packed = channels per workgroup).
-hipError_t launch_scan_fwd_packed(const float* a, const float* b, const float* h0, float* h,
-                                  int64_t C, int64_t T, int k, int vec, hipStream_t stream);
-hipError_t launch_scan_bwd_packed(const float* a, const float* h, const float* h0, const float* g,
-                                  float* da, float* db, float* dh0, int64_t C, int64_t T, int k,
+hipError_t launch_scan_bwd_serial(const void* a, const void* h, const float* h0, const void* g,
+                                  void* da, void* db, float* dh0, int io, int64_t C, int64_t T,
                                   int vec, hipStream_t stream);
+// Packed short channels (plan.packed = channels per workgroup).
+hipError_t launch_scan_fwd_packed(const void* a, const void* b, const float* h0, void* h, int io,
+                                  int64_t C, int64_t T, int k, int vec, hipStream_t stream);
+hipError_t launch_scan_bwd_packed(const void* a, const void* h, const float* h0, const void* g,
+                                  void* da, void* db, float* dh0, int io, int64_t C, int64_t T,
+                                  int k, int vec, hipStream_t stream);
 // Forward and backward scan in one pass; the plan must be single-chunk.
-hipError_t launch_scan_fused_bdt(const float* a, const float* b, const float* h0, const float* g,
-                                 float* h, float* da, float* db, float* dh0, int64_t C, int64_t T,
-                                 const RowPlan& p, int vec, hipStream_t stream);
+hipError_t launch_scan_fused_bdt(const void* a, const void* b, const float* h0, const void* g,
+                                 void* h, void* da, void* db, float* dh0, int io, int64_t C,
+                                 int64_t T, const RowPlan& p, int vec, hipStream_t stream);
 // DEER update norms: three rotating sets of kDeltaSlots words, kDeltaStride
 // words apart (one cache line per slot).
 constexpr int kDeltaSlots = 64;
@@ -146,11 +153,11 @@ hipError_t launch_deer_seq_finish(const uint32_t* seq_delta, int* seq_rec, int64
 hipError_t launch_deer_seq_select(const float* p0, const float* p1, float* h, int64_t nseq,
                                   int64_t n, const int* seq_rec, hipStream_t stream);
 
-hipError_t launch_scan_fwd_tbd(const float* a, const float* b, const float* h0, float* h,
+hipError_t launch_scan_fwd_tbd(const void* a, const void* b, const float* h0, void* h, int io,
                                int64_t C, int64_t T, const ColPlan& p, int vec, uint64_t* status,
                                unsigned* tickets, hipStream_t stream);
-hipError_t launch_scan_bwd_tbd(const float* a, const float* h, const float* h0, const float* g,
-                               float* da, float* db, float* dh0, int64_t C, int64_t T,
+hipError_t launch_scan_bwd_tbd(const void* a, const void* h, const float* h0, const void* g,
+                               void* da, void* db, float* dh0, int io, int64_t C, int64_t T,
                                const ColPlan& p, int vec, uint64_t* status, unsigned* tickets,
                                hipStream_t stream);
 hipError_t launch_sru_fwd(const void* zf, const void* zr, const void* zx, const float* bias_f,

@@ -25,10 +25,6 @@ struct ColShared {
 // (0 for a row past the end) and the rest read as `fill` / are not written.
 // NT selects the nontemporal (streaming) cache policy for FULL rows.
 
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
 template <bool NT, typename V>
 __device__ __forceinline__ V ldv(const V* p) {
   if constexpr (NT) return __builtin_nontemporal_load(p);
@@ -79,6 +75,49 @@ __device__ __forceinline__ void store_row(float* __restrict__ p, uint32_t off, i
   }
 }
 
+// bf16 rows widened to fp32 values, with the fp32 rows' fill semantics (the
+// scan kernels take either element type through these overloads).
+template <int CPT, bool FULL, bool NT = false>
+__device__ __forceinline__ void load_row(const uint16_t* __restrict__ p, uint32_t off, int nvalid,
+                                         float fill, float (&v)[CPT]) {
+  if (FULL) {
+    if constexpr (CPT == 4) {
+      const u32x2_t x = ldv<NT>(reinterpret_cast<const u32x2_t*>(p + off));
+      v[0] = bf16_lo(x.x); v[1] = bf16_hi(x.x); v[2] = bf16_lo(x.y); v[3] = bf16_hi(x.y);
+    } else if constexpr (CPT == 2) {
+      const uint32_t x = ldv<NT>(reinterpret_cast<const uint32_t*>(p + off));
+      v[0] = bf16_lo(x); v[1] = bf16_hi(x);
+    } else {
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) v[k] = bf16_lo((uint32_t)ldv<NT>(p + off + k));
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) v[k] = (k < nvalid) ? io_ld(p, off + k) : fill;
+  }
+}
+
+template <int CPT, bool FULL, bool NT = false>
+__device__ __forceinline__ void store_row(uint16_t* __restrict__ p, uint32_t off, int nvalid,
+                                          const float (&v)[CPT]) {
+  if (FULL) {
+    if constexpr (CPT == 4) {
+      stv<NT>(reinterpret_cast<u32x2_t*>(p + off),
+              u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
+    } else if constexpr (CPT == 2) {
+      stv<NT>(reinterpret_cast<uint32_t*>(p + off), pack_bf16x2(v[0], v[1]));
+    } else {
+#pragma unroll
+      for (int k = 0; k < CPT; ++k)
+        stv<NT>(p + off + k, (uint16_t)(pack_bf16x2(v[k], 0.0f) & 0xFFFFu));
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k)
+      if (k < nvalid) io_st(p, off + k, v[k]);
+  }
+}
+
 // bf16 rows are kept as packed pairs (CPT/2 words) and widened on use.
 template <int CPT, bool FULL, bool NT = false>
 __device__ __forceinline__ void load_row_bf16(const uint16_t* __restrict__ p, uint32_t off,
@@ -105,20 +144,9 @@ __device__ __forceinline__ void load_row_bf16(const uint16_t* __restrict__ p, ui
   }
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return as_f32(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return as_f32(w & 0xFFFF0000u); }
 template <int CPT>
 __device__ __forceinline__ float bf16_get(const uint32_t (&w)[CPT / 2], int k) {
   return (k & 1) ? bf16_hi(w[k >> 1]) : bf16_lo(w[k >> 1]);
-}
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// Round pairs of fp32 to bf16 (nearest-even, gfx950 v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const f32x2_t f = {lo, hi};
-  const bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
-  return __builtin_bit_cast(uint32_t, b);
 }
 
 template <int CPT, bool FULL, bool NT = false>

@@ -141,18 +141,18 @@ __device__ __forceinline__ void chain_rows(const float (&RA)[R], const float (&R
 // ---------------------------------------------------------------------------
 // forward scan
 // ---------------------------------------------------------------------------
-template <int NW, int R, bool NTL, bool NTS, bool FULL>
-__device__ __forceinline__ void scan_fwd_chunk(const float* __restrict__ a,
-                                               const float* __restrict__ b,
+template <typename IO, int NW, int R, bool NTL, bool NTS, bool FULL>
+__device__ __forceinline__ void scan_fwd_chunk(const IO* __restrict__ a,
+                                               const IO* __restrict__ b,
                                                const float* __restrict__ h0,
-                                               float* __restrict__ h, int64_t T, int64_t ch, int c,
+                                               IO* __restrict__ h, int64_t T, int64_t ch, int c,
                                                bool multi, int vec, uint64_t* st,
                                                BlockShared<NW>& s) {
   constexpr int S = R * 256, CH = NW * S;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   const int64_t base = (int64_t)c * CH + (int64_t)wid * S + 4 * lane;
-  const float* arow = a + ch * T;
-  const float* brow = b + ch * T;
+  const IO* arow = a + ch * T;
+  const IO* brow = b + ch * T;
 
   // A chunk of a long channel loads its rows one at a time: each wave waits for
   // a row's loads before it issues the next row's, so at most 2 KiB per wave
@@ -185,7 +185,7 @@ __device__ __forceinline__ void scan_fwd_chunk(const float* __restrict__ a,
   const float x_in = chunk_carry<NW>(multi, c, TA, TB, x0, st, s);
 
   float xr = __builtin_fmaf(PA, x_in, PB);  // state entering this wave's first row
-  float* hrow = h + ch * T;
+  IO* hrow = h + ch * T;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     float x = wave_shift_up(__builtin_fmaf(Ai[r], xr, Bi[r]), xr);  // entering this lane's group
@@ -201,10 +201,10 @@ __device__ __forceinline__ void scan_fwd_chunk(const float* __restrict__ a,
 
 // MULTI: channels span several chunks (look-back compiled in); otherwise each
 // channel is one chunk and the kernel carries no look-back code at all.
-template <int NW, int R, bool NTL = false, bool NTS = false, bool MULTI = false>
+template <typename IO, int NW, int R, bool NTL = false, bool NTS = false, bool MULTI = false>
 __global__ __launch_bounds__(NW* kWave) void k_scan_fwd_bdt(
-    const float* __restrict__ a, const float* __restrict__ b, const float* __restrict__ h0,
-    float* __restrict__ h, int64_t T, int64_t C, int nchunk, int vec,
+    const IO* __restrict__ a, const IO* __restrict__ b, const float* __restrict__ h0,
+    IO* __restrict__ h, int64_t T, int64_t C, int nchunk, int vec,
     uint64_t* __restrict__ status, unsigned* __restrict__ tickets) {
   constexpr int CH = NW * R * 256;
   __shared__ BlockShared<NW> s;
@@ -213,9 +213,9 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_fwd_bdt(
   const int c = chunk_ticket<NW>(multi, tickets, ch, s);
   uint64_t* st = status + ch * nchunk;
   if (vec && (int64_t)(c + 1) * CH <= T)
-    scan_fwd_chunk<NW, R, NTL, NTS, true>(a, b, h0, h, T, ch, c, multi, vec, st, s);
+    scan_fwd_chunk<IO, NW, R, NTL, NTS, true>(a, b, h0, h, T, ch, c, multi, vec, st, s);
   else
-    scan_fwd_chunk<NW, R, NTL, NTS, false>(a, b, h0, h, T, ch, c, multi, vec, st, s);
+    scan_fwd_chunk<IO, NW, R, NTL, NTS, false>(a, b, h0, h, T, ch, c, multi, vec, st, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -226,11 +226,11 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_fwd_bdt(
 // combine applies unchanged.  grad_b may alias grad_h: each element of g is
 // read by the thread that writes the same element of grad_b, before it writes.
 // ---------------------------------------------------------------------------
-template <int NW, int R, bool NTL, bool NTS, bool FULL>
-__device__ __forceinline__ void scan_bwd_chunk(const float* __restrict__ a,
-                                               const float* __restrict__ h,
-                                               const float* __restrict__ h0, const float* g,
-                                               float* __restrict__ da, float* db,
+template <typename IO, int NW, int R, bool NTL, bool NTS, bool FULL>
+__device__ __forceinline__ void scan_bwd_chunk(const IO* __restrict__ a,
+                                               const IO* __restrict__ h,
+                                               const float* __restrict__ h0, const IO* g,
+                                               IO* __restrict__ da, IO* db,
                                                float* __restrict__ dh0, int64_t T, int64_t ch,
                                                int c, int pc, bool multi, int vec, uint64_t* st,
                                                BlockShared<NW>& s) {
@@ -238,9 +238,9 @@ __device__ __forceinline__ void scan_bwd_chunk(const float* __restrict__ a,
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   const int64_t wend = (int64_t)(pc + 1) * CH - (int64_t)wid * S;  // physical end of the segment
   const int64_t wbeg = wend - S;
-  const float* arow = a + ch * T;
-  const float* hrow = h + ch * T;
-  const float* grow = g + ch * T;
+  const IO* arow = a + ch * T;
+  const IO* hrow = h + ch * T;
+  const IO* grow = g + ch * T;
 
   // Step p has coefficient alpha_p = a_{p+1}.  Reading a as 0 at and past
   // index T makes every step past the end a reset to zero, so the state
@@ -256,8 +256,8 @@ __device__ __forceinline__ void scan_bwd_chunk(const float* __restrict__ a,
   }
   const float x0h = h0 ? h0[ch] : 0.0f;
   // wave-edge halos (uniform): a just past the segment, h just before it
-  const float a_after = (wend < T) ? arow[wend] : 0.0f;
-  const float h_before = (wbeg > 0) ? ((wbeg - 1 < T) ? hrow[wbeg - 1] : 0.0f) : x0h;
+  const float a_after = (wend < T) ? io_ld(arow, wend) : 0.0f;
+  const float h_before = (wbeg > 0) ? ((wbeg - 1 < T) ? io_ld(hrow, wbeg - 1) : 0.0f) : x0h;
 
   float an[R], hp[R], Ai[R], Bi[R], RA[R], RB[R];
 #pragma unroll
@@ -283,8 +283,8 @@ __device__ __forceinline__ void scan_bwd_chunk(const float* __restrict__ a,
   const float x_in = chunk_carry<NW>(multi, c, TA, TB, 0.0f, st, s);
 
   float xr = __builtin_fmaf(PA, x_in, PB);
-  float* darow = da + ch * T;
-  float* dbrow = db + ch * T;
+  IO* darow = da + ch * T;
+  IO* dbrow = db + ch * T;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const float x = wave_shift_up(__builtin_fmaf(Ai[r], xr, Bi[r]), xr);  // lam past the group
@@ -302,10 +302,10 @@ __device__ __forceinline__ void scan_bwd_chunk(const float* __restrict__ a,
 }
 
 
-template <int NW, int R, bool NTL = false, bool NTS = false, bool MULTI = false>
+template <typename IO, int NW, int R, bool NTL = false, bool NTS = false, bool MULTI = false>
 __global__ __launch_bounds__(NW* kWave) void k_scan_bwd_bdt(
-    const float* __restrict__ a, const float* __restrict__ h, const float* __restrict__ h0,
-    const float* g, float* __restrict__ da, float* db, float* __restrict__ dh0, int64_t T,
+    const IO* __restrict__ a, const IO* __restrict__ h, const float* __restrict__ h0,
+    const IO* g, IO* __restrict__ da, IO* db, float* __restrict__ dh0, int64_t T,
     int64_t C, int nchunk, int vec, uint64_t* __restrict__ status,
     unsigned* __restrict__ tickets) {
   constexpr int CH = NW * R * 256;
@@ -316,9 +316,11 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_bwd_bdt(
   const int pc = nchunk - 1 - c;
   uint64_t* st = status + ch * nchunk;
   if (vec && (int64_t)(pc + 1) * CH <= T)
-    scan_bwd_chunk<NW, R, NTL, NTS, true>(a, h, h0, g, da, db, dh0, T, ch, c, pc, multi, vec, st, s);
+    scan_bwd_chunk<IO, NW, R, NTL, NTS, true>(a, h, h0, g, da, db, dh0, T, ch, c, pc, multi, vec,
+                                              st, s);
   else
-    scan_bwd_chunk<NW, R, NTL, NTS, false>(a, h, h0, g, da, db, dh0, T, ch, c, pc, multi, vec, st, s);
+    scan_bwd_chunk<IO, NW, R, NTL, NTS, false>(a, h, h0, g, da, db, dh0, T, ch, c, pc, multi,
+                                               vec, st, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -371,19 +373,19 @@ __device__ __forceinline__ void block_combine_down(float WA, float WB, BlockShar
   }
 }
 
-template <int NW, int R, bool NTL, bool NTS, bool FULL>
-__device__ __forceinline__ void scan_fused_chunk(const float* __restrict__ a, const float* b,
-                                                 const float* __restrict__ h0, const float* g,
-                                                 float* h, float* __restrict__ da, float* db,
+template <typename IO, int NW, int R, bool NTL, bool NTS, bool FULL>
+__device__ __forceinline__ void scan_fused_chunk(const IO* __restrict__ a, const IO* b,
+                                                 const float* __restrict__ h0, const IO* g,
+                                                 IO* h, IO* __restrict__ da, IO* db,
                                                  float* __restrict__ dh0, int64_t T, int64_t ch,
                                                  int vec, BlockShared<NW>& s,
                                                  BlockShared<NW>& s2) {
   constexpr int S = R * 256;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   const int64_t base = (int64_t)wid * S + 4 * lane;
-  const float* arow = a + ch * T;
-  const float* brow = b + ch * T;
-  const float* grow = g + ch * T;
+  const IO* arow = a + ch * T;
+  const IO* brow = b + ch * T;
+  const IO* grow = g + ch * T;
 
   // a reads as 0 past the end: harmless for the forward (those steps are not
   // written) and the zero coefficient the backward needs after step T-1
@@ -412,7 +414,7 @@ __device__ __forceinline__ void scan_fused_chunk(const float* __restrict__ a, co
   block_combine<NW>(WA, WB, s, PA, PB, TA, TB);
   const float x0 = h0 ? h0[ch] : 0.0f;
   const float h_before = __builtin_fmaf(PA, x0, PB);  // h entering this wave
-  float* hrow = h ? h + ch * T : nullptr;
+  IO* hrow = h ? h + ch * T : nullptr;
   {
     float xr = h_before;
 #pragma unroll
@@ -429,7 +431,7 @@ __device__ __forceinline__ void scan_fused_chunk(const float* __restrict__ a, co
   // ---- backward: step p has coefficient a_{p+1}
   // a just past this wave's segment (the next wave's first step, 0 past T)
   const int64_t wend = base - 4 * lane + S;
-  const float a_after = (wend < T) ? arow[wend] : 0.0f;
+  const float a_after = (wend < T) ? io_ld(arow, wend) : 0.0f;
   float an[R], hp[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -455,8 +457,8 @@ __device__ __forceinline__ void scan_fused_chunk(const float* __restrict__ a, co
   }
   block_combine_down<NW>(WA, WB, s2, PA, PB);
   float xr = PB;  // lam just past this wave's segment (lam past the channel is 0)
-  float* darow = da + ch * T;
-  float* dbrow = db + ch * T;
+  IO* darow = da + ch * T;
+  IO* dbrow = db + ch * T;
 #pragma unroll
   for (int r = R - 1; r >= 0; --r) {
     const float x = wave_shift_down(__builtin_fmaf(Ai[r], xr, Bi[r]), xr);  // lam past the group
@@ -473,17 +475,17 @@ __device__ __forceinline__ void scan_fused_chunk(const float* __restrict__ a, co
   }
 }
 
-template <int NW, int R, bool NTL = false, bool NTS = false>
+template <typename IO, int NW, int R, bool NTL = false, bool NTS = false>
 __global__ __launch_bounds__(NW* kWave) void k_scan_fused_bdt(
-    const float* __restrict__ a, const float* b, const float* __restrict__ h0, const float* g,
-    float* h, float* __restrict__ da, float* db, float* __restrict__ dh0, int64_t T, int vec) {
+    const IO* __restrict__ a, const IO* b, const float* __restrict__ h0, const IO* g,
+    IO* h, IO* __restrict__ da, IO* db, float* __restrict__ dh0, int64_t T, int vec) {
   constexpr int CH = NW * R * 256;
   __shared__ BlockShared<NW> s, s2;
   const int64_t ch = (int64_t)blockIdx.x;
   if (vec && (int64_t)CH <= T)
-    scan_fused_chunk<NW, R, NTL, NTS, true>(a, b, h0, g, h, da, db, dh0, T, ch, vec, s, s2);
+    scan_fused_chunk<IO, NW, R, NTL, NTS, true>(a, b, h0, g, h, da, db, dh0, T, ch, vec, s, s2);
   else
-    scan_fused_chunk<NW, R, NTL, NTS, false>(a, b, h0, g, h, da, db, dh0, T, ch, vec, s, s2);
+    scan_fused_chunk<IO, NW, R, NTL, NTS, false>(a, b, h0, g, h, da, db, dh0, T, ch, vec, s, s2);
 }
 
 // ---------------------------------------------------------------------------
@@ -504,18 +506,18 @@ __device__ __forceinline__ float get4(const float4& v, int j) {
   return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
 }
 
-template <int NW, int R>
+template <typename IO, int NW, int R>
 __global__ __launch_bounds__(NW* kWave) void k_scan_fwd_packed(
-    const float* __restrict__ a, const float* __restrict__ b, const float* __restrict__ h0,
-    float* __restrict__ h, int64_t T, int64_t C, int k, int vec) {
+    const IO* __restrict__ a, const IO* __restrict__ b, const float* __restrict__ h0,
+    IO* __restrict__ h, int64_t T, int64_t C, int k, int vec) {
   constexpr int S = R * 256;
   __shared__ BlockShared<NW> s;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   const int64_t c0 = (int64_t)blockIdx.x * k;
   const int64_t nch = (C - c0 < k) ? C - c0 : k;
   const int64_t len = nch * T;
-  const float* arow = a + c0 * T;
-  const float* brow = b + c0 * T;
+  const IO* arow = a + c0 * T;
+  const IO* brow = b + c0 * T;
   const uint32_t Tu = (uint32_t)T;
   const int64_t base = (int64_t)wid * S + 4 * lane;
   float4 a4[R], b4[R];
@@ -551,7 +553,7 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_fwd_packed(
   chain_rows<R>(RA, RB, WA, WB);
   block_combine<NW>(WA, WB, s, PA, PB, TA, TB);
   float xr = PB;  // the block starts with a reset: no carry in
-  float* hrow = h + c0 * T;
+  IO* hrow = h + c0 * T;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     float x = wave_shift_up(__builtin_fmaf(Ai[r], xr, Bi[r]), xr);
@@ -565,10 +567,10 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_fwd_packed(
   }
 }
 
-template <int NW, int R>
+template <typename IO, int NW, int R>
 __global__ __launch_bounds__(NW* kWave) void k_scan_bwd_packed(
-    const float* __restrict__ a, const float* __restrict__ h, const float* __restrict__ h0,
-    const float* g, float* __restrict__ da, float* db, float* __restrict__ dh0, int64_t T,
+    const IO* __restrict__ a, const IO* __restrict__ h, const float* __restrict__ h0,
+    const IO* g, IO* __restrict__ da, IO* db, float* __restrict__ dh0, int64_t T,
     int64_t C, int k, int vec) {
   constexpr int S = R * 256, CH = NW * S;
   __shared__ BlockShared<NW> s;
@@ -576,9 +578,9 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_bwd_packed(
   const int64_t c0 = (int64_t)blockIdx.x * k;
   const int64_t nch = (C - c0 < k) ? C - c0 : k;
   const int64_t len = nch * T;
-  const float* arow = a + c0 * T;
-  const float* hrow = h + c0 * T;
-  const float* grow = g + c0 * T;
+  const IO* arow = a + c0 * T;
+  const IO* hrow = h + c0 * T;
+  const IO* grow = g + c0 * T;
   const uint32_t Tu = (uint32_t)T;
   const int64_t wend = (int64_t)CH - (int64_t)wid * S;  // end of this wave's segment
   const int64_t wbeg = wend - S;
@@ -597,8 +599,8 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_bwd_packed(
       if (++m == Tu) m = 0;
     }
   }
-  const float a_after = (wend < len && (uint32_t)wend % Tu != 0) ? arow[wend] : 0.0f;
-  const float h_before = (wbeg > 0 && wbeg - 1 < len) ? hrow[wbeg - 1] : 0.0f;
+  const float a_after = (wend < len && (uint32_t)wend % Tu != 0) ? io_ld(arow, wend) : 0.0f;
+  const float h_before = (wbeg > 0 && wbeg - 1 < len) ? io_ld(hrow, wbeg - 1) : 0.0f;
   float an[R], hp[R], Ai[R], Bi[R], RA[R], RB[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -619,8 +621,8 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_bwd_packed(
   chain_rows<R>(RA, RB, WA, WB);
   block_combine<NW>(WA, WB, s, PA, PB, TA, TB);
   float xr = PB;  // lam past the block is 0
-  float* darow = da + c0 * T;
-  float* dbrow = db + c0 * T;
+  IO* darow = da + c0 * T;
+  IO* dbrow = db + c0 * T;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const float x = wave_shift_up(__builtin_fmaf(Ai[r], xr, Bi[r]), xr);
@@ -637,7 +639,7 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_bwd_packed(
       if (m == 0 && p + j < len) {  // a channel's first step: h before it is its h0
         const float x0 = h0 ? h0[c0 + cl] : 0.0f;
         hv[j] = x0;
-        if (dh0) dh0[c0 + cl] = arow[p + j] * l[j];
+        if (dh0) dh0[c0 + cl] = io_ld(arow, p + j) * l[j];
       }
       if (++m == Tu) { m = 0; ++cl; }
     }
@@ -1511,17 +1513,17 @@ static void plan_short(RowPlan& p, int64_t T, int64_t serial_max, int64_t packed
   }
 }
 
-RowPlan plan_scan_fwd_rows(int64_t C, int64_t T, const Opts& o) {
+RowPlan plan_scan_fwd_rows(int64_t C, int64_t T, const Opts& o, int io) {
   RowPlan p = pick(T, kScanSingle, kScanFwdMulti);
-  p.stream = 3 * C * T * 4 >= kStreamFootprint;  // a, b, h
+  p.stream = 3 * C * T * io_bytes(io) >= kStreamFootprint;  // a, b, h
   plan_short(p, T, limit_or(o.serial_fwd_max_t, kSerialFwdMaxT),
              limit_or(o.packed_max_t, kPackedMaxT));
   return p;
 }
 
-RowPlan plan_scan_bwd_rows(int64_t C, int64_t T, const Opts& o) {
+RowPlan plan_scan_bwd_rows(int64_t C, int64_t T, const Opts& o, int io) {
   RowPlan p = pick(T, kScanSingle, kScanBwdMulti);
-  p.stream = 5 * C * T * 4 >= kStreamFootprint;  // a, h, g, grad_a, grad_b
+  p.stream = 5 * C * T * io_bytes(io) >= kStreamFootprint;  // a, h, g, grad_a, grad_b
   plan_short(p, T, limit_or(o.serial_bwd_max_t, kSerialBwdMaxT),
              limit_or(o.packed_max_t, kPackedMaxT));
   return p;
@@ -1534,9 +1536,9 @@ RowPlan plan_deer_bwd_rows(int64_t C, int64_t T) {
 }
 
 // Fused forward + backward: single-chunk shapes only (nchunk > 1 = not fusable).
-RowPlan plan_scan_fused_rows(int64_t C, int64_t T) {
+RowPlan plan_scan_fused_rows(int64_t C, int64_t T, int io) {
   RowPlan p = pick(T, kScanSingle, kScanFwdMulti);
-  p.stream = 6 * C * T * 4 >= kStreamFootprint;  // a, b, g, h, grad_a, grad_b
+  p.stream = 6 * C * T * io_bytes(io) >= kStreamFootprint;  // a, b, g, h, grad_a, grad_b
   return p;
 }
 
@@ -1556,13 +1558,12 @@ RowPlan plan_deer_rows(int64_t C, int64_t T) {
 #define LRS_SHAPE_CASE(NW_, R_, ...) \
   if (p.nw == NW_ && p.r == R_) { constexpr int NW = NW_, RR = R_; __VA_ARGS__; return hipGetLastError(); }
 
-hipError_t launch_scan_fwd_bdt(const float* a, const float* b, const float* h0, float* h,
-                               int64_t C, int64_t T, const RowPlan& p, int vec,
-                               uint64_t* status, unsigned* tickets, hipStream_t stream) {
-  if (p.serial) return launch_scan_fwd_serial(a, b, h0, h, C, T, vec, stream);
-  if (p.packed) return launch_scan_fwd_packed(a, b, h0, h, C, T, p.packed, vec, stream);
+template <typename IO>
+static hipError_t scan_fwd_bdt_io(const IO* a, const IO* b, const float* h0, IO* h, int64_t C,
+                                  int64_t T, const RowPlan& p, int vec, uint64_t* status,
+                                  unsigned* tickets, hipStream_t stream) {
   const dim3 grid((unsigned)((uint64_t)C * (uint64_t)p.nchunk));
-#define LRS_FWD(NTF, M) hipLaunchKernelGGL((k_scan_fwd_bdt<NW, RR, NTF, NTF, M>), grid, dim3(NW * kWave), \
+#define LRS_FWD(NTF, M) hipLaunchKernelGGL((k_scan_fwd_bdt<IO, NW, RR, NTF, NTF, M>), grid, dim3(NW * kWave), \
                                            0, stream, a, b, h0, h, T, C, (int)p.nchunk, vec, status, \
                                            tickets)
   if (p.nchunk > 1) {
@@ -1587,14 +1588,25 @@ hipError_t launch_scan_fwd_bdt(const float* a, const float* b, const float* h0, 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_scan_bwd_bdt(const float* a, const float* h, const float* h0, const float* g,
-                               float* da, float* db, float* dh0, int64_t C, int64_t T,
-                               const RowPlan& p, int vec, uint64_t* status, unsigned* tickets,
-                               hipStream_t stream) {
-  if (p.serial) return launch_scan_bwd_serial(a, h, h0, g, da, db, dh0, C, T, vec, stream);
-  if (p.packed) return launch_scan_bwd_packed(a, h, h0, g, da, db, dh0, C, T, p.packed, vec, stream);
+hipError_t launch_scan_fwd_bdt(const void* a, const void* b, const float* h0, void* h, int io,
+                               int64_t C, int64_t T, const RowPlan& p, int vec,
+                               uint64_t* status, unsigned* tickets, hipStream_t stream) {
+  if (p.serial) return launch_scan_fwd_serial(a, b, h0, h, io, C, T, vec, stream);
+  if (p.packed) return launch_scan_fwd_packed(a, b, h0, h, io, C, T, p.packed, vec, stream);
+  if (io == kIoBf16)
+    return scan_fwd_bdt_io((const uint16_t*)a, (const uint16_t*)b, h0, (uint16_t*)h, C, T, p, vec,
+                           status, tickets, stream);
+  return scan_fwd_bdt_io((const float*)a, (const float*)b, h0, (float*)h, C, T, p, vec, status,
+                         tickets, stream);
+}
+
+template <typename IO>
+static hipError_t scan_bwd_bdt_io(const IO* a, const IO* h, const float* h0, const IO* g, IO* da,
+                                  IO* db, float* dh0, int64_t C, int64_t T, const RowPlan& p,
+                                  int vec, uint64_t* status, unsigned* tickets,
+                                  hipStream_t stream) {
   const dim3 grid((unsigned)((uint64_t)C * (uint64_t)p.nchunk));
-#define LRS_BWD(NTF, M) hipLaunchKernelGGL((k_scan_bwd_bdt<NW, RR, NTF, NTF, M>), grid, dim3(NW * kWave), \
+#define LRS_BWD(NTF, M) hipLaunchKernelGGL((k_scan_bwd_bdt<IO, NW, RR, NTF, NTF, M>), grid, dim3(NW * kWave), \
                                            0, stream, a, h, h0, g, da, db, dh0, T, C, (int)p.nchunk, \
                                            vec, status, tickets)
   if (p.nchunk > 1) {
@@ -1624,32 +1636,57 @@ hipError_t launch_scan_bwd_bdt(const float* a, const float* h, const float* h0, 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_scan_fwd_packed(const float* a, const float* b, const float* h0, float* h,
+hipError_t launch_scan_bwd_bdt(const void* a, const void* h, const float* h0, const void* g,
+                               void* da, void* db, float* dh0, int io, int64_t C, int64_t T,
+                               const RowPlan& p, int vec, uint64_t* status, unsigned* tickets,
+                               hipStream_t stream) {
+  if (p.serial) return launch_scan_bwd_serial(a, h, h0, g, da, db, dh0, io, C, T, vec, stream);
+  if (p.packed)
+    return launch_scan_bwd_packed(a, h, h0, g, da, db, dh0, io, C, T, p.packed, vec, stream);
+  if (io == kIoBf16)
+    return scan_bwd_bdt_io((const uint16_t*)a, (const uint16_t*)h, h0, (const uint16_t*)g,
+                           (uint16_t*)da, (uint16_t*)db, dh0, C, T, p, vec, status, tickets,
+                           stream);
+  return scan_bwd_bdt_io((const float*)a, (const float*)h, h0, (const float*)g, (float*)da,
+                         (float*)db, dh0, C, T, p, vec, status, tickets, stream);
+}
+
+hipError_t launch_scan_fwd_packed(const void* a, const void* b, const float* h0, void* h, int io,
                                   int64_t C, int64_t T, int k, int vec, hipStream_t stream) {
   const dim3 grid((unsigned)((C + k - 1) / k));
-  hipLaunchKernelGGL((k_scan_fwd_packed<8, 1>), grid, dim3(8 * kWave), 0, stream, a, b, h0, h, T,
-                     C, k, vec);
+  if (io == kIoBf16)
+    hipLaunchKernelGGL((k_scan_fwd_packed<uint16_t, 8, 1>), grid, dim3(8 * kWave), 0, stream,
+                       (const uint16_t*)a, (const uint16_t*)b, h0, (uint16_t*)h, T, C, k, vec);
+  else
+    hipLaunchKernelGGL((k_scan_fwd_packed<float, 8, 1>), grid, dim3(8 * kWave), 0, stream,
+                       (const float*)a, (const float*)b, h0, (float*)h, T, C, k, vec);
   return hipGetLastError();
 }
 
-hipError_t launch_scan_bwd_packed(const float* a, const float* h, const float* h0, const float* g,
-                                  float* da, float* db, float* dh0, int64_t C, int64_t T, int k,
-                                  int vec, hipStream_t stream) {
+hipError_t launch_scan_bwd_packed(const void* a, const void* h, const float* h0, const void* g,
+                                  void* da, void* db, float* dh0, int io, int64_t C, int64_t T,
+                                  int k, int vec, hipStream_t stream) {
   const dim3 grid((unsigned)((C + k - 1) / k));
-  hipLaunchKernelGGL((k_scan_bwd_packed<8, 1>), grid, dim3(8 * kWave), 0, stream, a, h, h0, g, da,
-                     db, dh0, T, C, k, vec);
+  if (io == kIoBf16)
+    hipLaunchKernelGGL((k_scan_bwd_packed<uint16_t, 8, 1>), grid, dim3(8 * kWave), 0, stream,
+                       (const uint16_t*)a, (const uint16_t*)h, h0, (const uint16_t*)g,
+                       (uint16_t*)da, (uint16_t*)db, dh0, T, C, k, vec);
+  else
+    hipLaunchKernelGGL((k_scan_bwd_packed<float, 8, 1>), grid, dim3(8 * kWave), 0, stream,
+                       (const float*)a, (const float*)h, h0, (const float*)g, (float*)da,
+                       (float*)db, dh0, T, C, k, vec);
   return hipGetLastError();
 }
 
-hipError_t launch_scan_fused_bdt(const float* a, const float* b, const float* h0, const float* g,
-                                 float* h, float* da, float* db, float* dh0, int64_t C, int64_t T,
-                                 const RowPlan& p, int vec, hipStream_t stream) {
-  if (p.nchunk != 1) return hipErrorInvalidValue;
+template <typename IO>
+static hipError_t scan_fused_bdt_io(const IO* a, const IO* b, const float* h0, const IO* g, IO* h,
+                                    IO* da, IO* db, float* dh0, int64_t C, int64_t T,
+                                    const RowPlan& p, int vec, hipStream_t stream) {
   const dim3 grid((unsigned)C);
   // nontemporal loads always (cold and warm calls measured no slower, warm
   // B=8 D=512 T=4096 calls 19% faster); nontemporal stores only for calls far
   // larger than the caches (steady-state 74% vs 70% of peak at 1.5 GiB)
-#define LRS_FUSED(NTF) hipLaunchKernelGGL((k_scan_fused_bdt<NW, RR, true, NTF>), grid, \
+#define LRS_FUSED(NTF) hipLaunchKernelGGL((k_scan_fused_bdt<IO, NW, RR, true, NTF>), grid, \
                                           dim3(NW * kWave), 0, stream, a, b, h0, g, h, da, db, dh0, T, vec)
   if (p.stream) {
     LRS_SHAPE_CASE(1, 1, LRS_FUSED(true))
@@ -1668,6 +1705,18 @@ hipError_t launch_scan_fused_bdt(const float* a, const float* b, const float* h0
   }
 #undef LRS_FUSED
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_scan_fused_bdt(const void* a, const void* b, const float* h0, const void* g,
+                                 void* h, void* da, void* db, float* dh0, int io, int64_t C,
+                                 int64_t T, const RowPlan& p, int vec, hipStream_t stream) {
+  if (p.nchunk != 1) return hipErrorInvalidValue;
+  if (io == kIoBf16)
+    return scan_fused_bdt_io((const uint16_t*)a, (const uint16_t*)b, h0, (const uint16_t*)g,
+                             (uint16_t*)h, (uint16_t*)da, (uint16_t*)db, dh0, C, T, p, vec,
+                             stream);
+  return scan_fused_bdt_io((const float*)a, (const float*)b, h0, (const float*)g, (float*)h,
+                           (float*)da, (float*)db, dh0, C, T, p, vec, stream);
 }
 
 hipError_t launch_deer_bwd(const float* w, const float* h, const float* h0, const float* g,

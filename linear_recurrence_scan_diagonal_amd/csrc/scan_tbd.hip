@@ -34,17 +34,17 @@ namespace lrs {
 // ---------------------------------------------------------------------------
 // forward scan, [T, B, D]
 // ---------------------------------------------------------------------------
-template <int NW, int L, int CPT, bool FULL, bool NT>
-__device__ __forceinline__ void scan_fwd_tile(const float* __restrict__ a,
-                                              const float* __restrict__ b,
-                                              const float* __restrict__ h0, float* __restrict__ h,
+template <typename IO, int NW, int L, int CPT, bool FULL, bool NT>
+__device__ __forceinline__ void scan_fwd_tile(const IO* __restrict__ a,
+                                              const IO* __restrict__ b,
+                                              const float* __restrict__ h0, IO* __restrict__ h,
                                               int64_t T, int64_t C, int tb, int cb, bool multi,
                                               uint64_t* st, ColShared<NW, CPT>& s) {
   const ColPos q = col_pos<NW, L, CPT>(tb, cb, C);
   const int64_t cbase = (int64_t)cb * (kWave * CPT);
   float av[L][CPT], bv[L][CPT];
-  const float* ap = a + q.row0 * C + cbase;
-  const float* bp = b + q.row0 * C + cbase;
+  const IO* ap = a + q.row0 * C + cbase;
+  const IO* bp = b + q.row0 * C + cbase;
 #pragma unroll
   for (int i = 0; i < L; ++i) {
     const int nv = (FULL || q.row0 + i < T) ? q.nvc : 0;
@@ -69,7 +69,7 @@ __device__ __forceinline__ void scan_fwd_tile(const float* __restrict__ a,
   for (int k = 0; k < CPT; ++k) x0[k] = (h0 && k < q.nvc) ? h0[q.c0 + k] : 0.0f;
   col_enter_state<NW, CPT>(A, B, multi, tb, x0, h0, cbase, clamp_valid(C - cbase, kWave * CPT),
                            st, s, x);
-  float* hp = h + q.row0 * C + cbase;
+  IO* hp = h + q.row0 * C + cbase;
 #pragma unroll
   for (int i = 0; i < L; ++i) {
 #pragma unroll
@@ -83,10 +83,10 @@ __device__ __forceinline__ void scan_fwd_tile(const float* __restrict__ a,
   }
 }
 
-template <int NW, int L, int CPT, bool NT>
+template <typename IO, int NW, int L, int CPT, bool NT>
 __global__ __launch_bounds__(NW* kWave) void k_scan_fwd_tbd(
-    const float* __restrict__ a, const float* __restrict__ b, const float* __restrict__ h0,
-    float* __restrict__ h, int64_t T, int64_t C, int ncb, int ntb, int vec,
+    const IO* __restrict__ a, const IO* __restrict__ b, const float* __restrict__ h0,
+    IO* __restrict__ h, int64_t T, int64_t C, int ncb, int ntb, int vec,
     uint64_t* __restrict__ status, unsigned* __restrict__ tickets) {
   constexpr int CW = kWave * CPT, TW = NW * L;
   __shared__ ColShared<NW, CPT> s;
@@ -96,9 +96,9 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_fwd_tbd(
   uint64_t* st = status + (int64_t)cb * ntb * CW;
   const bool full = vec && ((int64_t)(tb + 1) * TW <= T) && ((int64_t)(cb + 1) * CW <= C);
   if (full)
-    scan_fwd_tile<NW, L, CPT, true, NT>(a, b, h0, h, T, C, tb, cb, multi, st, s);
+    scan_fwd_tile<IO, NW, L, CPT, true, NT>(a, b, h0, h, T, C, tb, cb, multi, st, s);
   else
-    scan_fwd_tile<NW, L, CPT, false, NT>(a, b, h0, h, T, C, tb, cb, multi, st, s);
+    scan_fwd_tile<IO, NW, L, CPT, false, NT>(a, b, h0, h, T, C, tb, cb, multi, st, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -107,11 +107,11 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_fwd_tbd(
 // grad_b may alias grad_h (each element of g is read by the thread that
 // writes the same element of grad_b, before it writes).
 // ---------------------------------------------------------------------------
-template <int NW, int L, int CPT, bool FULL, bool NT>
-__device__ __forceinline__ void scan_bwd_tile(const float* __restrict__ a,
-                                              const float* __restrict__ h,
-                                              const float* __restrict__ h0, const float* g,
-                                              float* __restrict__ da, float* db,
+template <typename IO, int NW, int L, int CPT, bool FULL, bool NT>
+__device__ __forceinline__ void scan_bwd_tile(const IO* __restrict__ a,
+                                              const IO* __restrict__ h,
+                                              const float* __restrict__ h0, const IO* g,
+                                              IO* __restrict__ da, IO* db,
                                               float* __restrict__ dh0, int64_t T, int64_t C,
                                               int tb, int ntb, int cb, bool multi, uint64_t* st,
                                               ColShared<NW, CPT>& s) {
@@ -126,9 +126,9 @@ __device__ __forceinline__ void scan_bwd_tile(const float* __restrict__ a,
 
   float av[L + 1][CPT], hv[L][CPT], gv[L][CPT], hp[CPT];
   {
-    const float* ap = a + row0 * C + cbase;
-    const float* hpp = h + row0 * C + cbase;
-    const float* gp = g + row0 * C + cbase;
+    const IO* ap = a + row0 * C + cbase;
+    const IO* hpp = h + row0 * C + cbase;
+    const IO* gp = g + row0 * C + cbase;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       const int nv = (FULL || row0 + i < T) ? nvc : 0;
@@ -179,8 +179,8 @@ __device__ __forceinline__ void scan_bwd_tile(const float* __restrict__ a,
   for (int k = 0; k < CPT; ++k) zero[k] = 0.0f;
   col_enter_state<NW, CPT>(A, B, multi, tb, zero, nullptr, cbase,
                            clamp_valid(C - cbase, kWave * CPT), st, s, x);
-  float* dap = da + (row0 + L - 1) * C + cbase;
-  float* dbp = db + (row0 + L - 1) * C + cbase;
+  IO* dap = da + (row0 + L - 1) * C + cbase;
+  IO* dbp = db + (row0 + L - 1) * C + cbase;
 #pragma unroll
   for (int i = L - 1; i >= 0; --i) {
     float dav[CPT];
@@ -203,10 +203,10 @@ __device__ __forceinline__ void scan_bwd_tile(const float* __restrict__ a,
   }
 }
 
-template <int NW, int L, int CPT, bool NT>
+template <typename IO, int NW, int L, int CPT, bool NT>
 __global__ __launch_bounds__(NW* kWave) void k_scan_bwd_tbd(
-    const float* __restrict__ a, const float* __restrict__ h, const float* __restrict__ h0,
-    const float* g, float* __restrict__ da, float* db, float* __restrict__ dh0, int64_t T,
+    const IO* __restrict__ a, const IO* __restrict__ h, const float* __restrict__ h0,
+    const IO* g, IO* __restrict__ da, IO* db, float* __restrict__ dh0, int64_t T,
     int64_t C, int ncb, int ntb, int vec, uint64_t* __restrict__ status,
     unsigned* __restrict__ tickets) {
   constexpr int CW = kWave * CPT, TW = NW * L;
@@ -218,10 +218,10 @@ __global__ __launch_bounds__(NW* kWave) void k_scan_bwd_tbd(
   const int ptb = ntb - 1 - tb;
   const bool full = vec && ((int64_t)(ptb + 1) * TW <= T) && ((int64_t)(cb + 1) * CW <= C);
   if (full)
-    scan_bwd_tile<NW, L, CPT, true, NT>(a, h, h0, g, da, db, dh0, T, C, tb, ntb, cb, multi, st,
+    scan_bwd_tile<IO, NW, L, CPT, true, NT>(a, h, h0, g, da, db, dh0, T, C, tb, ntb, cb, multi, st,
                                         s);
   else
-    scan_bwd_tile<NW, L, CPT, false, NT>(a, h, h0, g, da, db, dh0, T, C, tb, ntb, cb, multi, st,
+    scan_bwd_tile<IO, NW, L, CPT, false, NT>(a, h, h0, g, da, db, dh0, T, C, tb, ntb, cb, multi, st,
                                          s);
 }
 
@@ -750,20 +750,25 @@ int64_t col_status_words(const ColPlan& p) {
 namespace {
 constexpr int kFwdNW = 8, kFwdL = 32, kFwdCPT = 1;
 constexpr int kBwdNW = 8, kBwdL = 16, kBwdCPT = 1;
+// bf16 I/O: two channels per lane (4-byte row accesses instead of 2-byte)
+constexpr int kFwd16NW = 8, kFwd16L = 16, kFwd16CPT = 2;
+constexpr int kBwd16NW = 8, kBwd16L = 8, kBwd16CPT = 2;
 constexpr int kSruNW = 4, kSruL = 16, kSruCPT = 2;          // bf16 I/O
 constexpr int kSruF32NW = 8, kSruF32L = 8, kSruF32CPT = 2;  // fp32 I/O
 constexpr int kSruBwdNW = 4, kSruBwdL = 8, kSruBwdCPT = 2;  // backward, both I/O types
 constexpr int kSruPNW = 8, kSruPL = 8, kSruPCPT = 2;        // persistent forward, both I/O types
 }  // namespace
 
-ColPlan plan_scan_fwd_tbd(int64_t C, int64_t T) {
-  ColPlan p = plan_cols(C, T, kFwdNW, kFwdL, kFwdCPT);
-  p.stream = 3 * C * T * 4 >= kStreamFootprint;  // a, b, h
+ColPlan plan_scan_fwd_tbd(int64_t C, int64_t T, int io) {
+  ColPlan p = io == kIoBf16 ? plan_cols(C, T, kFwd16NW, kFwd16L, kFwd16CPT)
+                            : plan_cols(C, T, kFwdNW, kFwdL, kFwdCPT);
+  p.stream = 3 * C * T * io_bytes(io) >= kStreamFootprint;  // a, b, h
   return p;
 }
-ColPlan plan_scan_bwd_tbd(int64_t C, int64_t T) {
-  ColPlan p = plan_cols(C, T, kBwdNW, kBwdL, kBwdCPT);
-  p.stream = 5 * C * T * 4 >= kStreamFootprint;  // a, h, g, grad_a, grad_b
+ColPlan plan_scan_bwd_tbd(int64_t C, int64_t T, int io) {
+  ColPlan p = io == kIoBf16 ? plan_cols(C, T, kBwd16NW, kBwd16L, kBwd16CPT)
+                            : plan_cols(C, T, kBwdNW, kBwdL, kBwdCPT);
+  p.stream = 5 * C * T * io_bytes(io) >= kStreamFootprint;  // a, h, g, grad_a, grad_b
   return p;
 }
 ColPlan plan_sru_bwd(int64_t C, int64_t T, int io_dtype) {
@@ -784,34 +789,61 @@ ColPlan plan_sru(int64_t C, int64_t T, int io_dtype, bool allow_persist, const O
   return p;
 }
 
-hipError_t launch_scan_fwd_tbd(const float* a, const float* b, const float* h0, float* h,
-                               int64_t C, int64_t T, const ColPlan& p, int vec, uint64_t* status,
-                               unsigned* tickets, hipStream_t stream) {
+template <typename IO, int NW, int L, int CPT>
+static void scan_fwd_tbd_io(const IO* a, const IO* b, const float* h0, IO* h, int64_t C, int64_t T,
+                            const ColPlan& p, int vec, uint64_t* status, unsigned* tickets,
+                            hipStream_t stream) {
   const uint64_t grid = (uint64_t)p.ncb * (uint64_t)p.ntb;
   if (p.stream)
-    hipLaunchKernelGGL((k_scan_fwd_tbd<kFwdNW, kFwdL, kFwdCPT, true>), dim3((unsigned)grid),
-                       dim3(kFwdNW * kWave), 0, stream, a, b, h0, h, T, C, (int)p.ncb, (int)p.ntb,
+    hipLaunchKernelGGL((k_scan_fwd_tbd<IO, NW, L, CPT, true>), dim3((unsigned)grid),
+                       dim3(NW * kWave), 0, stream, a, b, h0, h, T, C, (int)p.ncb, (int)p.ntb,
                        vec, status, tickets);
   else
-    hipLaunchKernelGGL((k_scan_fwd_tbd<kFwdNW, kFwdL, kFwdCPT, false>), dim3((unsigned)grid),
-                       dim3(kFwdNW * kWave), 0, stream, a, b, h0, h, T, C, (int)p.ncb, (int)p.ntb,
+    hipLaunchKernelGGL((k_scan_fwd_tbd<IO, NW, L, CPT, false>), dim3((unsigned)grid),
+                       dim3(NW * kWave), 0, stream, a, b, h0, h, T, C, (int)p.ncb, (int)p.ntb,
                        vec, status, tickets);
+}
+
+hipError_t launch_scan_fwd_tbd(const void* a, const void* b, const float* h0, void* h, int io,
+                               int64_t C, int64_t T, const ColPlan& p, int vec, uint64_t* status,
+                               unsigned* tickets, hipStream_t stream) {
+  if (io == kIoBf16)
+    scan_fwd_tbd_io<uint16_t, kFwd16NW, kFwd16L, kFwd16CPT>(
+        (const uint16_t*)a, (const uint16_t*)b, h0, (uint16_t*)h, C, T, p, vec, status, tickets,
+        stream);
+  else
+    scan_fwd_tbd_io<float, kFwdNW, kFwdL, kFwdCPT>((const float*)a, (const float*)b, h0, (float*)h,
+                                                   C, T, p, vec, status, tickets, stream);
   return hipGetLastError();
 }
 
-hipError_t launch_scan_bwd_tbd(const float* a, const float* h, const float* h0, const float* g,
-                               float* da, float* db, float* dh0, int64_t C, int64_t T,
-                               const ColPlan& p, int vec, uint64_t* status, unsigned* tickets,
-                               hipStream_t stream) {
+template <typename IO, int NW, int L, int CPT>
+static void scan_bwd_tbd_io(const IO* a, const IO* h, const float* h0, const IO* g, IO* da, IO* db,
+                            float* dh0, int64_t C, int64_t T, const ColPlan& p, int vec,
+                            uint64_t* status, unsigned* tickets, hipStream_t stream) {
   const uint64_t grid = (uint64_t)p.ncb * (uint64_t)p.ntb;
   if (p.stream)
-    hipLaunchKernelGGL((k_scan_bwd_tbd<kBwdNW, kBwdL, kBwdCPT, true>), dim3((unsigned)grid),
-                       dim3(kBwdNW * kWave), 0, stream, a, h, h0, g, da, db, dh0, T, C,
-                       (int)p.ncb, (int)p.ntb, vec, status, tickets);
+    hipLaunchKernelGGL((k_scan_bwd_tbd<IO, NW, L, CPT, true>), dim3((unsigned)grid),
+                       dim3(NW * kWave), 0, stream, a, h, h0, g, da, db, dh0, T, C, (int)p.ncb,
+                       (int)p.ntb, vec, status, tickets);
   else
-    hipLaunchKernelGGL((k_scan_bwd_tbd<kBwdNW, kBwdL, kBwdCPT, false>), dim3((unsigned)grid),
-                       dim3(kBwdNW * kWave), 0, stream, a, h, h0, g, da, db, dh0, T, C,
-                       (int)p.ncb, (int)p.ntb, vec, status, tickets);
+    hipLaunchKernelGGL((k_scan_bwd_tbd<IO, NW, L, CPT, false>), dim3((unsigned)grid),
+                       dim3(NW * kWave), 0, stream, a, h, h0, g, da, db, dh0, T, C, (int)p.ncb,
+                       (int)p.ntb, vec, status, tickets);
+}
+
+hipError_t launch_scan_bwd_tbd(const void* a, const void* h, const float* h0, const void* g,
+                               void* da, void* db, float* dh0, int io, int64_t C, int64_t T,
+                               const ColPlan& p, int vec, uint64_t* status, unsigned* tickets,
+                               hipStream_t stream) {
+  if (io == kIoBf16)
+    scan_bwd_tbd_io<uint16_t, kBwd16NW, kBwd16L, kBwd16CPT>(
+        (const uint16_t*)a, (const uint16_t*)h, h0, (const uint16_t*)g, (uint16_t*)da,
+        (uint16_t*)db, dh0, C, T, p, vec, status, tickets, stream);
+  else
+    scan_bwd_tbd_io<float, kBwdNW, kBwdL, kBwdCPT>((const float*)a, (const float*)h, h0,
+                                                   (const float*)g, (float*)da, (float*)db, dh0, C,
+                                                   T, p, vec, status, tickets, stream);
   return hipGetLastError();
 }
 

@@ -132,6 +132,7 @@ class Workload:
     seed: int
     dists: dict = field(default_factory=dict)
     desc: str = ""
+    io: str = "f32"           # element type of the scan arrays: "f32" or "bf16"
 
     @property
     def C(self) -> int:
@@ -201,6 +202,15 @@ WORKLOADS = {
          "zo": ("normal", 0.0, 1.0), "gh": ("normal", 0.0, 1.0)},
         "LSTM cell-state layer (input-only gates) forward + backward, bf16 I/O fp32 state, "
         "B=32 D=1024 T=2048, z_f,z_i,z_c,z_o~N(0,1), c0=0, dL/dh~N(0,1)"),
+    # the forward + backward scan with bf16 arrays (fp32 state): scan_fwd_bwd's
+    # shape and distributions, a, b and dL/dh rounded to bf16
+    "scan_fwd_bwd_bf16": Workload(
+        "scan_fwd_bwd_bf16", "scan", 8, 512, 4096, 1011,
+        {"a": ("uniform", 0.8, 0.999), "b": ("normal", 0.0, 1.0), "h0": ("normal", 0.0, 1.0),
+         "g": ("normal", 0.0, 1.0)},
+        "forward+backward linear scan, bf16 arrays with fp32 state, B=8 D=512 T=4096, "
+        "a~U(0.8,0.999), b~N(0,1), h0~N(0,1), dL/dh~N(0,1) (a, b, dL/dh rounded to bf16)",
+        io="bf16"),
     # very long forward + backward scan, fp32
     "scan_long": Workload(
         "scan_long", "scan", 2, 256, 1 << 20, 1004,
@@ -208,6 +218,14 @@ WORKLOADS = {
          "g": ("normal", 0.0, 1.0)},
         "long forward+backward linear scan, fp32, B=2 D=256 T=2^20, a~U(0.9,0.9999), "
         "b~N(0,0.1), h0=0, dL/dh~N(0,1)"),
+    # the long scan with bf16 arrays (fp32 state)
+    "scan_long_bf16": Workload(
+        "scan_long_bf16", "scan", 2, 256, 1 << 20, 1012,
+        {"a": ("uniform", 0.9, 0.9999), "b": ("normal", 0.0, 0.1), "h0": ("const", 0.0, 0.0),
+         "g": ("normal", 0.0, 1.0)},
+        "long forward+backward linear scan, bf16 arrays with fp32 state, B=2 D=256 T=2^20, "
+        "a~U(0.9,0.9999), b~N(0,0.1), h0=0, dL/dh~N(0,1) (a, b, dL/dh rounded to bf16)",
+        io="bf16"),
     # DEER Newton solve of h_t = tanh(w h_{t-1} + u_t)
     "deer": Workload(
         "deer", "deer", 16, 512, 8192, 1005,
@@ -227,7 +245,7 @@ WORKLOADS = {
 def scaled(w: Workload, B=None, D=None, T=None, seed=None) -> Workload:
     """Same distributions, other sizes (for small parity cases)."""
     return Workload(w.name, w.kind, B or w.B, D or w.D, T or w.T,
-                    w.seed if seed is None else seed, dict(w.dists), w.desc)
+                    w.seed if seed is None else seed, dict(w.dists), w.desc, w.io)
 
 
 def scan_inputs(w: Workload, channels=None, with_grad: bool = True) -> dict:

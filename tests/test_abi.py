@@ -92,11 +92,16 @@ def test_validation_before_any_launch(lib):
     from linear_recurrence_scan_diagonal_amd import binding as b
     p = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
     null = None
-    # negative size, bad layout, bad dtype, unsupported dtype, null pointers, misalignment
+    # negative size, bad layout, bad dtype, null pointers, misalignment
     assert lib.lrs_scan_fwd(p, p, null, p, -1, 1, 1, 0, 0, null, 0, null) == b.LRS_ERR_INVALID_ARG
     assert lib.lrs_scan_fwd(p, p, null, p, 1, 1, 1, 5, 0, null, 0, null) == b.LRS_ERR_INVALID_ARG
     assert lib.lrs_scan_fwd(p, p, null, p, 1, 1, 1, 0, 9, null, 0, null) == b.LRS_ERR_INVALID_ARG
-    assert lib.lrs_scan_fwd(p, p, null, p, 1, 1, 4, 0, 1, null, 0, null) == b.LRS_ERR_UNSUPPORTED
+    # bf16 arrays: 2-byte alignment, and extents of 2 bytes per element (h six
+    # bytes past a overlaps a's four elements)
+    assert lib.lrs_scan_fwd(ctypes.c_void_p(0x1001), ctypes.c_void_p(0x2000), null,
+                            ctypes.c_void_p(0x9000), 1, 1, 4, 0, 1, null, 0, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_scan_fwd(p, ctypes.c_void_p(0x2000), null, ctypes.c_void_p(0x1006), 1, 1, 4, 0, 1,
+                            null, 0, null) == b.LRS_ERR_INVALID_ARG
     assert lib.lrs_scan_fwd(null, p, null, p, 1, 1, 4, 0, 0, null, 0, null) == b.LRS_ERR_INVALID_ARG
     assert lib.lrs_scan_fwd(ctypes.c_void_p(0x1002), p, null, ctypes.c_void_p(0x9000), 1, 1, 4, 0, 0,
                             null, 0, null) == b.LRS_ERR_INVALID_ARG
