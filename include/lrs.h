@@ -140,17 +140,20 @@ LRS_API void lrs_options_default(lrs_options *options);
 
 /* ---------------------------------------------------------------- scan --- */
 
-/* Workspace bytes needed by lrs_scan_fwd / lrs_scan_bwd for this shape
- * (look-back status words when a channel spans more than one workgroup).
- * Returns 0 for an invalid shape. */
+/* Workspace bytes needed by lrs_scan_fwd / lrs_scan_bwd for this shape, layout
+ * and element type (look-back status words when a channel spans more than one
+ * workgroup).  Returns 0 for an invalid shape. */
 LRS_API size_t lrs_scan_workspace_bytes(int64_t B, int64_t D, int64_t T, int layout, int dtype);
 
 /* Forward scan ([P1] parallel-scan paragraph; [P2] cell-state paragraph):
  *   h_t = a_t * h_{t-1} + b_t  for t = 1..T, every channel independently.
- * a, b, h : [B,D,T] or [T,B,D] per `layout`, element type `dtype` (LRS_F32).
+ * a, b, h : [B,D,T] or [T,B,D] per `layout`, element type `dtype`: LRS_F32, or
+ *           LRS_BF16 (bf16 bit patterns, aligned to 2 bytes).
  * h0      : [B,D] fp32, or NULL for a zero initial state.
- * h must not overlap a, b or h0.  Arithmetic is fp32 with fused multiply-add;
- * the association order of the scan is fixed by the launch shape (see
+ * h must not overlap a, b or h0.  Arithmetic and the carried state are fp32
+ * with fused multiply-add whatever `dtype` is; bf16 inputs widen exactly and
+ * each h_t is rounded to bf16 (nearest-even) only when stored.  The
+ * association order of the scan is fixed by the launch shape (see
  * Reproducibility above), so repeated calls give the same bits. */
 LRS_API int lrs_scan_fwd(const void *a, const void *b, const float *h0, void *h, int64_t B, int64_t D,
                  int64_t T, int layout, int dtype, void *workspace, size_t workspace_bytes,
@@ -167,7 +170,8 @@ LRS_API int lrs_scan_fwd_ex(const void *a, const void *b, const float *h0, void 
  *   grad_b_t = lam_t,  grad_a_t = lam_t * h_{t-1} (h0 at t = 1),
  *   grad_h0 = a_1 * lam_1.
  * h is the forward output; h0 as in lrs_scan_fwd (NULL = zero).
- * grad_a, grad_b: same shape/layout/dtype as a.  grad_h0: [B,D] fp32 or NULL.
+ * grad_h, grad_a, grad_b: same shape/layout/dtype as a (bf16 outputs are
+ * rounded from fp32 values).  grad_h0: [B,D] fp32 or NULL.
  * grad_b may be the same buffer as grad_h (lam overwrites the incoming
  * gradient); no other overlap is allowed. */
 LRS_API int lrs_scan_bwd(const void *a, const void *h, const float *h0, const void *grad_h, void *grad_a,
