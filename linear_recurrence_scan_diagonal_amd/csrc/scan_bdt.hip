@@ -154,17 +154,18 @@ __device__ __forceinline__ void scan_fwd_chunk(const IO* __restrict__ a,
   const IO* arow = a + ch * T;
   const IO* brow = b + ch * T;
 
-  // A chunk of a long channel loads its rows one at a time: each wave waits for
-  // a row's loads before it issues the next row's, so at most 2 KiB per wave
-  // are in flight.  At B=2, D=256, T=2^20 that streams 2% faster (1064 against
-  // 1088 us) than issuing all rows at once; single-chunk channels see no
-  // difference and issue all rows at once.
+  // A chunk of a long channel loads its rows a few at a time: each wave waits
+  // for the loads of one fp32 row (two bf16 rows) before it issues the next,
+  // so at most 2 KiB per wave are in flight.  At B=2, D=256, T=2^20 that
+  // streams 2% faster (1064 against 1088 us) than issuing all rows at once;
+  // single-chunk channels see no difference and issue all rows at once.
+  constexpr int kRowsPerWait = sizeof(IO) == 2 ? 2 : 1;
   float4 a4[R], b4[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     a4[r] = ld4<FULL, NTL>(arow, base + r * 256, T, vec, 1.0f);
     b4[r] = ld4<FULL, NTL>(brow, base + r * 256, T, vec, 0.0f);
-    if (multi) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (multi && (r + 1) % kRowsPerWait == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   float Ai[R], Bi[R], RA[R], RB[R];
 #pragma unroll
@@ -1442,6 +1443,14 @@ struct Shape { int nw, r; };
 constexpr Shape kScanSingle[] = {{1, 1}, {2, 1}, {4, 1}, {8, 1}, {8, 2}, {8, 4}};
 constexpr Shape kScanFwdMulti = {8, 4};
 constexpr Shape kScanBwdMulti = {16, 4};
+// bf16 arrays (B=2, D=256, T=2^20): forward chunks of 8 x 8 rows with a wait
+// every two rows, 582-594 us against 612-629 us for 8 x 4 (and 680 us for
+// 8 x 8 waiting every row, 795-806 us for 16 x 4); the backward keeps 16 x 4
+// (8 x 8: the same time, 16 x 2: 24% slower)
+constexpr Shape kScanFwdMulti16 = {8, 8};
+constexpr Shape kScanBwdMulti16 = {16, 4};
+template <typename IO> constexpr Shape fwd_multi() { return sizeof(IO) == 2 ? kScanFwdMulti16 : kScanFwdMulti; }
+template <typename IO> constexpr Shape bwd_multi() { return sizeof(IO) == 2 ? kScanBwdMulti16 : kScanBwdMulti; }
 constexpr Shape kDeerSingle[] = {{1, 1}, {2, 1}, {4, 1}, {8, 1}, {8, 2}};
 constexpr Shape kDeerMulti = {8, 2};
 // sub-chunk shape of the fused solve for channels of more than 2048 steps
@@ -1514,7 +1523,7 @@ static void plan_short(RowPlan& p, int64_t T, int64_t serial_max, int64_t packed
 }
 
 RowPlan plan_scan_fwd_rows(int64_t C, int64_t T, const Opts& o, int io) {
-  RowPlan p = pick(T, kScanSingle, kScanFwdMulti);
+  RowPlan p = pick(T, kScanSingle, io == kIoBf16 ? kScanFwdMulti16 : kScanFwdMulti);
   p.stream = 3 * C * T * io_bytes(io) >= kStreamFootprint;  // a, b, h
   plan_short(p, T, limit_or(o.serial_fwd_max_t, kSerialFwdMaxT),
              limit_or(o.packed_max_t, kPackedMaxT));
@@ -1522,7 +1531,7 @@ RowPlan plan_scan_fwd_rows(int64_t C, int64_t T, const Opts& o, int io) {
 }
 
 RowPlan plan_scan_bwd_rows(int64_t C, int64_t T, const Opts& o, int io) {
-  RowPlan p = pick(T, kScanSingle, kScanBwdMulti);
+  RowPlan p = pick(T, kScanSingle, io == kIoBf16 ? kScanBwdMulti16 : kScanBwdMulti);
   p.stream = 5 * C * T * io_bytes(io) >= kStreamFootprint;  // a, h, g, grad_a, grad_b
   plan_short(p, T, limit_or(o.serial_bwd_max_t, kSerialBwdMaxT),
              limit_or(o.packed_max_t, kPackedMaxT));
@@ -1566,9 +1575,15 @@ static hipError_t scan_fwd_bdt_io(const IO* a, const IO* b, const float* h0, IO*
 #define LRS_FWD(NTF, M) hipLaunchKernelGGL((k_scan_fwd_bdt<IO, NW, RR, NTF, NTF, M>), grid, dim3(NW * kWave), \
                                            0, stream, a, b, h0, h, T, C, (int)p.nchunk, vec, status, \
                                            tickets)
-  if (p.nchunk > 1) {
-    if (p.stream) { LRS_SHAPE_CASE(kScanFwdMulti.nw, kScanFwdMulti.r, LRS_FWD(true, true)) }
-    else { LRS_SHAPE_CASE(kScanFwdMulti.nw, kScanFwdMulti.r, LRS_FWD(false, true)) }
+  constexpr Shape M = fwd_multi<IO>();
+  if (p.nchunk > 1) {  // the multi shape, or 8x4 chunks for channels under two of them
+    if (p.stream) {
+      LRS_SHAPE_CASE(M.nw, M.r, LRS_FWD(true, true))
+      LRS_SHAPE_CASE(8, 4, LRS_FWD(true, true))
+    } else {
+      LRS_SHAPE_CASE(M.nw, M.r, LRS_FWD(false, true))
+      LRS_SHAPE_CASE(8, 4, LRS_FWD(false, true))
+    }
   } else if (p.stream) {
     LRS_SHAPE_CASE(1, 1, LRS_FWD(true, false))
     LRS_SHAPE_CASE(2, 1, LRS_FWD(true, false))
@@ -1609,12 +1624,13 @@ static hipError_t scan_bwd_bdt_io(const IO* a, const IO* h, const float* h0, con
 #define LRS_BWD(NTF, M) hipLaunchKernelGGL((k_scan_bwd_bdt<IO, NW, RR, NTF, NTF, M>), grid, dim3(NW * kWave), \
                                            0, stream, a, h, h0, g, da, db, dh0, T, C, (int)p.nchunk, \
                                            vec, status, tickets)
-  if (p.nchunk > 1) {
+  constexpr Shape M = bwd_multi<IO>();
+  if (p.nchunk > 1) {  // the multi shape, or 8x4 chunks for channels under two of them
     if (p.stream) {
-      LRS_SHAPE_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_BWD(true, true))
+      LRS_SHAPE_CASE(M.nw, M.r, LRS_BWD(true, true))
       LRS_SHAPE_CASE(8, 4, LRS_BWD(true, true))
     } else {
-      LRS_SHAPE_CASE(kScanBwdMulti.nw, kScanBwdMulti.r, LRS_BWD(false, true))
+      LRS_SHAPE_CASE(M.nw, M.r, LRS_BWD(false, true))
       LRS_SHAPE_CASE(8, 4, LRS_BWD(false, true))
     }
   } else if (p.stream) {
