@@ -51,6 +51,28 @@ def test_sru_persistent_ragged(plan, B, D, T, io):
     assert e["c_last"] <= 1e-5 and e["cs_last_row"] <= 1e-5
 
 
+@pytest.mark.parametrize("T", [64, 127, 128, 191, 192, 256, 257, 449])
+def test_sru_persistent_tile_counts(plan, T):
+    """bf16, B*D a multiple of 8 with a partial last 128-channel block: one to
+    seven full tiles of 64 steps, with and without a ragged tail; with saved
+    cell states and without them (the walk then computes the same h, bit for
+    bit)."""
+    plan(persist_min_blocks=0)
+    B, D = 2, 132
+    w = I.scaled(I.WORKLOADS["sru_fwd"], B=B, D=D, T=T, seed=13100 + T)
+    c0 = np.random.default_rng(T + 7).normal(size=(B, D)).astype(np.float32)
+    h, cl, cs, z64, s = sru_run(w, "bf16", c0)
+    ref_h, ref_c = oracle.sru_fwd(z64["zf"], z64["zr"], z64["zx"], s["bias_f"], s["bias_r"], c0)
+    e = {"h": relerr(h, ref_h), "c_last": relerr(cl, ref_c), "cs": relerr(cs[-1], ref_c)}
+    z = {k: bf16_dev(s[k]) for k in ("zf", "zr", "zx")}
+    bf, br = (torch.from_numpy(s[k]).to(DEV) for k in ("bias_f", "bias_r"))
+    h2 = lrs.sru_fwd(z["zf"], z["zr"], z["zx"], bf, br, torch.from_numpy(c0).to(DEV))
+    torch.cuda.synchronize()
+    log(f"persistent sru bf16 {B}x{D}x{T}: " + ", ".join(f"{k}={v:.2e}" for k, v in e.items()))
+    assert e["h"] <= 2e-2 and e["c_last"] <= 1e-5 and e["cs"] <= 1e-5
+    assert np.array_equal(h2.float().cpu().numpy(), h)
+
+
 def test_sru_both_kernels_at_workload_shape(plan):
     w = I.WORKLOADS["sru_fwd"]
     outs = {}

@@ -85,6 +85,36 @@ def test_sru_gate_limits():
     assert torch.equal(h, z)
 
 
+def test_sru_output_extremes():
+    """The output h = r tanh(c) + (1 - r) z_x at its limits (fp32 I/O), with
+    f = 1 so c stays c0 (bias_f 800): per feature r = 0 (bias_r -800) with z_x
+    up to 3e38 in size, r = 1 (bias_r 800) with z_x ~ N(0, 3), and r = sigmoid(z_r)
+    with z_x up to 3e38; cell states 0, -0, +-1e-30, +-20, +-1e4 and random
+    sizes up to 1e4.  Against the oracle at the fp32 bar; c_T equals c0 bit for bit."""
+    T, B, D = 9, 2, 63
+    rng = np.random.default_rng(11)
+    cls = np.arange(D) % 3
+    big = rng.normal(size=(T, B, D)) * 10.0 ** rng.integers(-3, 39, size=(T, B, D))
+    zx = np.where(cls == 1, rng.normal(size=(T, B, D)) * 3.0, np.clip(big, -3e38, 3e38))
+    zx = zx.astype(np.float32)
+    zr = rng.normal(size=(T, B, D)).astype(np.float32)
+    zf = np.zeros((T, B, D), np.float32)
+    c0 = (rng.normal(size=(B, D)) * 10.0 ** rng.integers(-4, 5, size=(B, D))).astype(np.float32)
+    c0[0, :24] = np.repeat([0.0, -0.0, 1e-30, -1e-30, 20.0, -20.0, 1e4, -1e4], 3)
+    bias_f = np.full(D, 800.0, np.float32)
+    bias_r = np.choose(cls, [-800.0, 800.0, 0.0]).astype(np.float32)
+    d = lambda x: torch.from_numpy(x).to(DEV)
+    h, c = lrs.sru_fwd(d(zf), d(zr), d(zx), d(bias_f), d(bias_r), d(c0), want_c_last=True)
+    torch.cuda.synchronize()
+    f64 = lambda x: x.astype(np.float64)
+    ref_h, ref_c = oracle.sru_fwd(f64(zf), f64(zr), f64(zx), f64(bias_f), f64(bias_r), f64(c0))
+    h = h.cpu().numpy().astype(np.float64)
+    e = relerr(h, ref_h)
+    log(f"sru output extremes: h relerr {e:.2e}")
+    assert np.isfinite(h).all() and e <= 1e-5
+    assert np.array_equal(c.cpu().numpy(), c0)
+
+
 def deer_case(w, h_init=None, eps=1e-5, k_max=5, alias=False):
     x = I.deer_inputs(w)
     B, D, T = w.B, w.D, w.T
