@@ -157,7 +157,8 @@ CALIB_WRITE = 4 * (1 << 26)
 
 def summarize(args):
     """Turn rocprofv3 CSV output (kernel trace + stats, and one --pmc run each
-    for FETCH_SIZE and WRITE_SIZE) into profiles/<kernel>__<workload>.md and
+    for FETCH_SIZE and WRITE_SIZE) into profiles/<workload>.md (every kernel the
+    workload launches) and
     the per-launch HBM traffic record in profiles/hbm_counters.json."""
     import csv
     import glob
