@@ -2,13 +2,17 @@
  * c_abi_driver.c -- exercises liblrs.so from plain C, the way a caller with no
  * Python or PyTorch would: device buffers from hipMalloc, a stream of its own,
  * workspaces sized by the queries, error returns checked before the real
- * calls.  Three modes:
+ * calls.  Four modes:
  *
  *   c_abi_driver scan B D T in.bin out.bin
  *     lrs_scan_fwd + lrs_scan_bwd on [B,D,T] fp32 arrays, and lrs_scan_fwd_ex
  *     with default options, which must give the same bits as lrs_scan_fwd.
  *     in.bin : a, b, grad_h (B*D*T floats each) then h0 (B*D floats)
  *     out.bin: h, grad_a, grad_b (B*D*T floats each) then grad_h0 (B*D floats)
+ *
+ *   c_abi_driver scan16 B D T in.bin out.bin
+ *     the same with bf16 arrays: a, b, grad_h, h, grad_a, grad_b as bf16 bit
+ *     patterns (2 bytes per element), h0 and grad_h0 fp32.
  *
  *   c_abi_driver sru T B D in.bin out.bin
  *     lrs_sru_fwd with bf16 I/O on [T,B,D] arrays, c_T requested.
@@ -70,24 +74,28 @@ static int write_file(const char *path, const void *buf, size_t n) {
   return put == n ? 0 : 1;
 }
 
-static int run_scan(int64_t B, int64_t D, int64_t T, const char *in, const char *out) {
+static int run_scan(int64_t B, int64_t D, int64_t T, int dtype, const char *in,
+                    const char *out) {
   const int64_t C = B * D, N = C * T;
-  const size_t nb = (size_t)N * sizeof(float), cb = (size_t)C * sizeof(float);
-  float *host = (float *)malloc(7 * nb + 2 * cb);
+  const size_t es = dtype == LRS_BF16 ? 2 : 4;
+  const size_t nb = (size_t)N * es, cb = (size_t)C * sizeof(float);
+  char *host = (char *)malloc(7 * nb + 2 * cb);
   if (!host) return 1;
-  float *a = host, *b = a + N, *g = b + N, *h0 = g + N;
+  char *a = host, *b = a + nb, *g = b + nb;
+  float *h0 = (float *)(g + nb);
   if (read_file(in, host, 3 * nb + cb)) return 1;
 
   hipStream_t st;
   CK(hipStreamCreate(&st));
-  float *da, *db, *dg, *dh0, *dh, *dh2, *dga, *dgb, *dgh0;
-  CK(hipMalloc((void **)&da, nb));
-  CK(hipMalloc((void **)&db, nb));
-  CK(hipMalloc((void **)&dg, nb));
-  CK(hipMalloc((void **)&dh, nb));
-  CK(hipMalloc((void **)&dh2, nb));
-  CK(hipMalloc((void **)&dga, nb));
-  CK(hipMalloc((void **)&dgb, nb));
+  void *da, *db, *dg, *dh, *dh2, *dga, *dgb;
+  float *dh0, *dgh0;
+  CK(hipMalloc(&da, nb));
+  CK(hipMalloc(&db, nb));
+  CK(hipMalloc(&dg, nb));
+  CK(hipMalloc(&dh, nb));
+  CK(hipMalloc(&dh2, nb));
+  CK(hipMalloc(&dga, nb));
+  CK(hipMalloc(&dgb, nb));
   CK(hipMalloc((void **)&dh0, cb));
   CK(hipMalloc((void **)&dgh0, cb));
   CK(hipMemcpy(da, a, nb, hipMemcpyHostToDevice));
@@ -95,32 +103,36 @@ static int run_scan(int64_t B, int64_t D, int64_t T, const char *in, const char 
   CK(hipMemcpy(dg, g, nb, hipMemcpyHostToDevice));
   CK(hipMemcpy(dh0, h0, cb, hipMemcpyHostToDevice));
 
-  const size_t ws = lrs_scan_workspace_bytes(B, D, T, LRS_LAYOUT_BDT, LRS_F32);
+  const size_t ws = lrs_scan_workspace_bytes(B, D, T, LRS_LAYOUT_BDT, dtype);
   void *dws = NULL;
   if (ws) CK(hipMalloc(&dws, ws));
 
   /* rejected before any launch */
-  LK(lrs_scan_fwd(NULL, db, dh0, dh, B, D, T, LRS_LAYOUT_BDT, LRS_F32, dws, ws, st),
+  LK(lrs_scan_fwd(NULL, db, dh0, dh, B, D, T, LRS_LAYOUT_BDT, dtype, dws, ws, st),
      LRS_ERR_INVALID_ARG);
-  LK(lrs_scan_fwd(da, db, dh0, da, B, D, T, LRS_LAYOUT_BDT, LRS_F32, dws, ws, st),
+  LK(lrs_scan_fwd(da, db, dh0, da, B, D, T, LRS_LAYOUT_BDT, dtype, dws, ws, st),
      LRS_ERR_INVALID_ARG);  /* h aliases a */
-  LK(lrs_scan_fwd(da, db, dh0, dh, B, D, -T, LRS_LAYOUT_BDT, LRS_F32, dws, ws, st),
+  LK(lrs_scan_fwd(da, db, dh0, dh, B, D, -T, LRS_LAYOUT_BDT, dtype, dws, ws, st),
      LRS_ERR_INVALID_ARG);
+  LK(lrs_scan_fwd(da, db, dh0, dh, B, D, T, LRS_LAYOUT_BDT, 7, dws, ws, st),
+     LRS_ERR_INVALID_ARG);  /* unknown element type */
   if (ws)
-    LK(lrs_scan_fwd(da, db, dh0, dh, B, D, T, LRS_LAYOUT_BDT, LRS_F32, NULL, 0, st),
+    LK(lrs_scan_fwd(da, db, dh0, dh, B, D, T, LRS_LAYOUT_BDT, dtype, NULL, 0, st),
        LRS_ERR_WORKSPACE);
 
-  LK(lrs_scan_fwd(da, db, dh0, dh, B, D, T, LRS_LAYOUT_BDT, LRS_F32, dws, ws, st), LRS_OK);
-  LK(lrs_scan_bwd(da, dh, dh0, dg, dga, dgb, dgh0, B, D, T, LRS_LAYOUT_BDT, LRS_F32, dws, ws, st),
+  LK(lrs_scan_fwd(da, db, dh0, dh, B, D, T, LRS_LAYOUT_BDT, dtype, dws, ws, st), LRS_OK);
+  LK(lrs_scan_bwd(da, dh, dh0, dg, dga, dgb, dgh0, B, D, T, LRS_LAYOUT_BDT, dtype, dws, ws, st),
      LRS_OK);
   /* the same forward through the options entry point, default options */
   lrs_options opt;
   lrs_options_default(&opt);
-  LK(lrs_scan_fwd_ex(da, db, dh0, dh2, B, D, T, LRS_LAYOUT_BDT, LRS_F32, dws, ws, st, &opt),
+  LK(lrs_scan_fwd_ex(da, db, dh0, dh2, B, D, T, LRS_LAYOUT_BDT, dtype, dws, ws, st, &opt),
      LRS_OK);
   CK(hipStreamSynchronize(st));
 
-  float *h = h0 + C, *ga = h + N, *gb = ga + N, *gh0 = gb + N, *h2 = gh0 + C;
+  char *h = (char *)(h0 + C), *ga = h + nb, *gb = ga + nb;
+  float *gh0 = (float *)(gb + nb);
+  char *h2 = (char *)(gh0 + C);
   CK(hipMemcpy(h, dh, nb, hipMemcpyDeviceToHost));
   CK(hipMemcpy(ga, dga, nb, hipMemcpyDeviceToHost));
   CK(hipMemcpy(gb, dgb, nb, hipMemcpyDeviceToHost));
@@ -250,12 +262,13 @@ static int run_deer(int64_t B, int64_t D, int64_t T, const char *in, const char 
 
 int main(int argc, char **argv) {
   if (argc != 7) {
-    fprintf(stderr, "usage: %s scan|sru|deer N1 N2 N3 in.bin out.bin\n", argv[0]);
+    fprintf(stderr, "usage: %s scan|scan16|sru|deer N1 N2 N3 in.bin out.bin\n", argv[0]);
     return 1;
   }
   const int64_t n1 = atoll(argv[2]), n2 = atoll(argv[3]), n3 = atoll(argv[4]);
   if (n1 < 1 || n2 < 1 || n3 < 1) return 1;
-  if (strcmp(argv[1], "scan") == 0) return run_scan(n1, n2, n3, argv[5], argv[6]);
+  if (strcmp(argv[1], "scan") == 0) return run_scan(n1, n2, n3, LRS_F32, argv[5], argv[6]);
+  if (strcmp(argv[1], "scan16") == 0) return run_scan(n1, n2, n3, LRS_BF16, argv[5], argv[6]);
   if (strcmp(argv[1], "sru") == 0) return run_sru(n1, n2, n3, argv[5], argv[6]);
   if (strcmp(argv[1], "deer") == 0) return run_deer(n1, n2, n3, argv[5], argv[6]);
   fprintf(stderr, "unknown mode %s\n", argv[1]);

@@ -4,7 +4,8 @@ query, checks that bad arguments and a missing or short workspace are
 rejected, and runs
   * lrs_scan_fwd + lrs_scan_bwd (and lrs_scan_fwd_ex with default options,
     which must give the same bits), one shape that fits a workgroup per
-    channel and one that spans several look-back chunks;
+    channel and one that spans several look-back chunks, with fp32 and with
+    bf16 arrays;
   * lrs_sru_fwd with bf16 I/O on a [T,B,D] layer;
   * lrs_deer_solve with its host record, and lrs_deer_eps_schedule;
 every output against the fp64 oracle to its bar (1e-5 fp32, 2e-2 bf16)."""
@@ -52,6 +53,31 @@ def test_c_driver_scan_matches_oracle(tmp_path, B, D, T):
     got = {"h": out[:n].reshape(C, T), "da": out[n:2 * n].reshape(C, T),
            "db": out[2 * n:3 * n].reshape(C, T), "dh0": out[3 * n:]}
     compare(got, oracle_scan(x), tag=f"c driver scan {B}x{D}x{T}")
+
+
+@pytest.mark.parametrize("B,D,T", [(2, 3, 1000), (1, 3, 20000)])
+def test_c_driver_scan_bf16_matches_oracle(tmp_path, B, D, T):
+    """The scan pair with bf16 arrays from plain C; the backward is checked
+    against the oracle fed the bf16 h the forward stored."""
+    w = I.scaled(I.WORKLOADS["scan_fwd_bwd"], B=B, D=D, T=T, seed=15050 + T)
+    x = I.scan_inputs(w)
+    C, n = B * D, B * D * T
+    bits = {k: I.to_bf16_bits(x[k]) for k in ("a", "b", "g")}
+    h0 = x["h0"].astype(np.float32)
+    dst = drive("scan16", (B, D, T), tmp_path, [bits["a"], bits["b"], bits["g"], h0])
+    raw = np.fromfile(dst, dtype=np.uint8)
+    assert raw.size == 3 * 2 * n + 4 * C
+    out = {k: I.bf16_bits_to_f64(raw[2 * n * i:2 * n * (i + 1)].view(np.uint16)).reshape(C, T)
+           for i, k in enumerate(("h", "da", "db"))}
+    dh0 = raw[6 * n:].view(np.float32).astype(np.float64)
+    v = {k: I.bf16_bits_to_f64(b) for k, b in bits.items()}
+    h0_64 = h0.astype(np.float64).reshape(-1)
+    ref_h = oracle.scan_fwd(v["a"], v["b"], h0_64)
+    ref_da, ref_db, ref_dh0 = oracle.scan_bwd(v["a"], out["h"], h0_64, v["g"])
+    e = {"h": relerr(out["h"], ref_h), "da": relerr(out["da"], ref_da),
+         "db": relerr(out["db"], ref_db), "dh0": relerr(dh0, ref_dh0)}
+    log(f"c driver scan bf16 {B}x{D}x{T}: " + ", ".join(f"{k}={q:.2e}" for k, q in e.items()))
+    assert e["h"] <= 2e-2 and e["da"] <= 2e-2 and e["db"] <= 2e-2 and e["dh0"] <= 1e-5
 
 
 def test_c_driver_sru_matches_oracle(tmp_path):
