@@ -483,11 +483,11 @@ def measure(args, np, torch, lrs, I, dev):
     if w.kind == "scan":
         layout = args.layout
         fwd_only = args.workload == "scan_fwd_small"
-        x = I.scan_inputs(w, with_grad=not fwd_only)
         bf16 = w.io == "bf16"
-        if bf16:  # a, b, dL/dh rounded to bf16 (uploaded as bit patterns)
-            def to_dev16(x_ct, layout):
-                return to_dev(I.to_bf16_bits(x_ct).view(np.int16), layout).view(torch.bfloat16)
+        x = (I.scan_inputs_bf16 if bf16 else I.scan_inputs)(w, with_grad=not fwd_only)
+        if bf16:  # a, b, dL/dh as bf16 bit patterns (one rounding from the fp64 draw)
+            def to_dev16(bits_ct, layout):
+                return to_dev(bits_ct.view(np.int16), layout).view(torch.bfloat16)
             a, b = to_dev16(x["a"], layout), to_dev16(x["b"], layout)
             g = None if fwd_only else to_dev16(x["g"], layout)
         else:
@@ -850,7 +850,11 @@ def cpu_baseline(w, args, np, I):
     if w.kind == "scan":
         nch = C if C * T <= (1 << 26) else max(1, (1 << 26) // T)
         ch = np.arange(nch)
-        x = I.scan_inputs(w, channels=ch, with_grad=w.name != "scan_fwd_small")
+        if w.io == "bf16":  # the oracle on the bf16 values the GPU receives
+            x = I.scan_inputs_bf16(w, channels=ch, with_grad=w.name != "scan_fwd_small")
+            x = {k: (I.bf16_bits_to_f64(v) if k != "h0" else v) for k, v in x.items()}
+        else:
+            x = I.scan_inputs(w, channels=ch, with_grad=w.name != "scan_fwd_small")
         a, b = x["a"].astype(np.float64), x["b"].astype(np.float64)
         h0 = x["h0"].astype(np.float64)
         g = x["g"].astype(np.float64) if "g" in x else None

@@ -263,6 +263,22 @@ def scan_inputs(w: Workload, channels=None, with_grad: bool = True) -> dict:
     return out
 
 
+def scan_inputs_bf16(w: Workload, channels=None, with_grad: bool = True, batch: int = 64) -> dict:
+    """bf16 bit patterns (uint16) of a, b and g, [len(channels), T] channel-major,
+    each value rounded once from its float64 draw; h0 fp32 [len(channels)].
+    Drawn in batches of channels so the float64 rows are never all held."""
+    ch = np.arange(w.C) if channels is None else np.asarray(channels)
+    tags = ("a", "b", "g") if with_grad and "g" in w.dists else ("a", "b")
+    out = {k: np.empty((ch.size, w.T), dtype=np.uint16) for k in tags}
+    for lo in range(0, ch.size, batch):
+        part = ch[lo:lo + batch]
+        for k in tags:
+            out[k][lo:lo + part.size] = to_bf16_bits(series(w.seed, k, w.dists[k], part, w.T))
+    h0 = to_f32(params(w.seed, "h0", w.dists.get("h0", ("const", 0, 0)), (w.C,)))
+    out["h0"] = h0[ch]
+    return out
+
+
 def sru_inputs(w: Workload) -> dict:
     """bf16 bit patterns of zf, zr, zx as [T, B, D] uint16 arrays, fp32 biases [D]."""
     ch = np.arange(w.C)

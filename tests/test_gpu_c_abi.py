@@ -59,10 +59,10 @@ def test_c_driver_scan_matches_oracle(tmp_path, B, D, T):
 def test_c_driver_scan_bf16_matches_oracle(tmp_path, B, D, T):
     """The scan pair with bf16 arrays from plain C; the backward is checked
     against the oracle fed the bf16 h the forward stored."""
-    w = I.scaled(I.WORKLOADS["scan_fwd_bwd"], B=B, D=D, T=T, seed=15050 + T)
-    x = I.scan_inputs(w)
+    w = I.scaled(I.WORKLOADS["scan_fwd_bwd_bf16"], B=B, D=D, T=T, seed=15050 + T)
+    x = I.scan_inputs_bf16(w)
     C, n = B * D, B * D * T
-    bits = {k: I.to_bf16_bits(x[k]) for k in ("a", "b", "g")}
+    bits = {k: x[k] for k in ("a", "b", "g")}
     h0 = x["h0"].astype(np.float32)
     dst = drive("scan16", (B, D, T), tmp_path, [bits["a"], bits["b"], bits["g"], h0])
     raw = np.fromfile(dst, dtype=np.uint8)

@@ -41,14 +41,15 @@ def close(x: torch.Tensor, y: torch.Tensor, tol: float) -> float:
 @pytest.mark.parametrize("layout,B,D,T", [("bdt", 2, 3, 4100), ("bdt", 1, 3, 20000),
                                           ("bdt", 3, 5, 40), ("tbd", 2, 70, 300)])
 def test_scan_shifted(dtype, layout, B, D, T):
-    w = I.scaled(I.WORKLOADS["scan_fwd_bwd"], B=B, D=D, T=T, seed=24000 + T + D)
-    x = I.scan_inputs(w)
+    w = I.scaled(I.WORKLOADS["scan_fwd_bwd" if dtype == "f32" else "scan_fwd_bwd_bf16"], B=B, D=D,
+                 T=T, seed=24000 + T + D)
+    x = I.scan_inputs(w) if dtype == "f32" else I.scan_inputs_bf16(w)
     tol = 1e-5 if dtype == "f32" else 2e-2
     if dtype == "f32":
         vals = {k: x[k].astype(np.float32).astype(np.float64) for k in ("a", "b", "g")}
         dev = {k: to_dev(x[k].astype(np.float32), B, D, T, layout) for k in ("a", "b", "g")}
     else:
-        bits = {k: I.to_bf16_bits(x[k]) for k in ("a", "b", "g")}
+        bits = {k: x[k] for k in ("a", "b", "g")}
         vals = {k: I.bf16_bits_to_f64(v) for k, v in bits.items()}
         dev = {k: to_dev(np.ascontiguousarray(v).view(np.int16), B, D, T, layout).view(torch.bfloat16)
                for k, v in bits.items()}

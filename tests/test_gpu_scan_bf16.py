@@ -40,9 +40,10 @@ def down16(t, B, D, T, layout):
 
 
 def bf16_case(B, D, T, seed):
-    w = I.scaled(I.WORKLOADS["scan_fwd_bwd"], B=B, D=D, T=T, seed=seed)
-    x = I.scan_inputs(w)
-    bits = {k: I.to_bf16_bits(x[k]) for k in ("a", "b", "g")}
+    """The bf16 scan recipe (each value rounded once from its fp64 draw)."""
+    w = I.scaled(I.WORKLOADS["scan_fwd_bwd_bf16"], B=B, D=D, T=T, seed=seed)
+    x = I.scan_inputs_bf16(w)
+    bits = {k: x[k] for k in ("a", "b", "g")}
     vals = {k: I.bf16_bits_to_f64(v) for k, v in bits.items()}
     h0 = x["h0"].astype(np.float32)
     return bits, vals, h0
@@ -162,3 +163,42 @@ def test_scan_bf16_workload_shape_sampled():
         eda = relerr(down16(da, B, D, T, layout)[1][rows], ref_da)
         log(f"bf16 scan workload shape {layout}: sampled h={eh:.2e} da={eda:.2e} db={edb:.2e}")
         assert eh <= TOL16 and eda <= TOL16 and edb <= TOL16
+
+
+def test_scan_long_bf16_every_channel():
+    """The bf16 long workload (B=2, D=256, T=2^20, [B,D,T], 128 forward and 64
+    backward look-back chunks per channel): every one of its 512 channels
+    against the oracle run on the bf16 values, in 32-channel batches compared
+    on the device; a second run gives the same bits."""
+    from test_gpu_scan_long import relerr_dev, rows_of, upload
+    w = I.WORKLOADS["scan_long_bf16"]
+    B, D, T = w.B, w.D, w.T
+    C = B * D
+    log(f"scan_long_bf16 B={B} D={D} T={T}: generating inputs")
+    x = I.scan_inputs_bf16(w)
+    a, b, g = (upload(x[k].view(np.int16), B, D, T, "bdt").view(torch.bfloat16)
+               for k in ("a", "b", "g"))
+    runs = []
+    for _ in range(2):
+        h = lrs.scan_fwd(a, b, None)
+        da, db, dh0 = lrs.scan_bwd(a, h, g, None)
+        torch.cuda.synchronize()
+        runs.append({"h": h, "da": da, "db": db, "dh0": dh0})
+    got, again = runs
+    for k in got:
+        assert torch.equal(got[k], again[k]), f"scan_long_bf16: {k} differs between two runs"
+    del again, runs
+    worst = {"h": 0.0, "da": 0.0, "db": 0.0, "dh0": 0.0}
+    for lo in range(0, C, 32):
+        sl = slice(lo, lo + 32)
+        av, bv, gv = (I.bf16_bits_to_f64(x[k][sl]) for k in ("a", "b", "g"))
+        h_dev = rows_of(got["h"], C, T, "bdt")[sl]
+        worst["h"] = max(worst["h"], relerr_dev(h_dev, oracle.scan_fwd(av, bv, None)))
+        h64 = h_dev.double().cpu().numpy()  # the bf16 h the backward consumed
+        ref_da, ref_db, ref_dh0 = oracle.scan_bwd(av, h64, None, gv)
+        worst["da"] = max(worst["da"], relerr_dev(rows_of(got["da"], C, T, "bdt")[sl], ref_da))
+        worst["db"] = max(worst["db"], relerr_dev(rows_of(got["db"], C, T, "bdt")[sl], ref_db))
+        worst["dh0"] = max(worst["dh0"], relerr_dev(got["dh0"].view(-1)[sl], ref_dh0))
+    log("scan_long_bf16: all 512 channels, errors " + ", ".join(f"{k}={v:.2e}" for k, v in worst.items()))
+    assert worst["h"] <= TOL16 and worst["da"] <= TOL16 and worst["db"] <= TOL16
+    assert worst["dh0"] <= TOL32

@@ -77,10 +77,10 @@ def test_noalloc_bf16_matches_workspace_form(layout, big, small):
     bit the workspace form (whose bf16 parity with the oracle is tested with
     the other bf16 scans)."""
     for (B, D, T) in (big, small):
-        w = I.scaled(I.WORKLOADS["scan_fwd_bwd"], B=B, D=D, T=T, seed=18200 + T)
-        x = I.scan_inputs(w)
-        a, b, g = (to_dev(np.ascontiguousarray(I.to_bf16_bits(x[k])).view(np.int16), B, D, T,
-                          layout).view(torch.bfloat16) for k in ("a", "b", "g"))
+        w = I.scaled(I.WORKLOADS["scan_fwd_bwd_bf16"], B=B, D=D, T=T, seed=18200 + T)
+        x = I.scan_inputs_bf16(w)
+        a, b, g = (to_dev(x[k].view(np.int16), B, D, T, layout).view(torch.bfloat16)
+                   for k in ("a", "b", "g"))
         h0 = torch.from_numpy(x["h0"].reshape(B, D).astype(np.float32)).to(DEV)
         got = noalloc(a, b, h0, g, layout)
         ref = lrs.scan_fwd_bwd(a, b, g, h0, layout=layout)
