@@ -113,3 +113,32 @@ def test_deer_seq_graph():
                      device=DEV)
     replay_matches(lambda: lrs.deer_solve_seq(wd, ud, out=h, workspace=ws, sync=False), [h], True,
                    "deer per-sequence")
+
+
+@pytest.mark.parametrize("layout,B,D,T", [("bdt", 2, 3, 20000), ("bdt", 4, 8, 300),
+                                          ("tbd", 2, 70, 3000)])
+def test_bf16_scan_graph(layout, B, D, T):
+    """The scan pair and the one-call forward + backward with bf16 arrays,
+    captured once and replayed: look-back chunks ([B,D,T], 20000 steps),
+    single-chunk channels and [T,B,D] time blocks; every replay bit for bit
+    the eager result (the carry order is fixed)."""
+    w = I.scaled(I.WORKLOADS["scan_fwd_bwd_bf16"], B=B, D=D, T=T, seed=19500 + T)
+    x = I.scan_inputs_bf16(w)
+    a, b, g = (to_dev(x[k].view(np.int16), B, D, T, layout).view(torch.bfloat16)
+               for k in ("a", "b", "g"))
+    h0 = torch.from_numpy(x["h0"].reshape(B, D)).to(DEV)
+    h, ga, gb = (torch.empty_like(a) for _ in range(3))
+    gh0 = torch.empty((B, D), device=DEV)
+    ws = torch.empty(lrs.scan_workspace_bytes(B, D, T, layout, torch.bfloat16) + 4096,
+                     dtype=torch.uint8, device=DEV)
+
+    def step():
+        lrs.scan_fwd(a, b, h0, layout=layout, out=h, workspace=ws)
+        lrs.scan_bwd(a, h, g, h0, layout=layout, grad_a=ga, grad_b=gb, grad_h0=gh0, workspace=ws)
+    replay_matches(step, (h, ga, gb, gh0), exact=True, tag=f"bf16 scan graph {layout} {B}x{D}x{T}")
+    if layout == "bdt":
+        out = tuple(torch.empty_like(t) for t in (h, ga, gb, gh0))
+
+        def fused():
+            lrs.scan_fwd_bwd(a, b, g, h0, out=out, workspace=ws)
+        replay_matches(fused, out, exact=True, tag=f"bf16 fused scan graph {B}x{D}x{T}")
