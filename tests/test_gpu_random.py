@@ -14,7 +14,7 @@ import oracle
 import linear_recurrence_scan_diagonal_amd as lrs
 from linear_recurrence_scan_diagonal_amd import inputs as I
 from conftest import relerr
-from gpu_util import DEV, log
+from gpu_util import DEV, from_dev, log, to_dev
 from test_gpu_deer_bwd import grads_vs_oracle
 from test_gpu_lstm import check as lstm_check, run_case as lstm_case
 from test_gpu_scan import compare, oracle_scan, run_scan
@@ -46,6 +46,41 @@ def test_scan_random(B, D, T, layout, h0, seed):
     x = I.scan_inputs(w)
     compare(run_scan(x, B, D, T, layout, h0=h0), oracle_scan(x, h0=h0),
             tag=f"random scan {layout} {B}x{D}x{T} h0={h0} seed={seed}")
+
+
+@cases(30)
+@given(B=st.integers(1, 4), D=st.integers(1, 300), T=steps, layout=st.sampled_from(["bdt", "tbd"]),
+       h0=st.booleans(), fused=st.booleans(), seed=seeds)
+def test_scan_bf16_random(B, D, T, layout, h0, fused, seed):
+    """bf16 arrays: the scan pair (or, in [B,D,T], the one-call form); the
+    backward against the oracle fed the bf16 h the GPU stored."""
+    assume(B * D * T <= MAX_ELEMS)
+    if fused:
+        assume(layout == "bdt")
+    w = I.scaled(I.WORKLOADS["scan_fwd_bwd_bf16"], B=B, D=D, T=T, seed=seed)
+    x = I.scan_inputs_bf16(w)
+    C = B * D
+    dev = {k: to_dev(x[k].view(np.int16), B, D, T, layout).view(torch.bfloat16) for k in ("a", "b", "g")}
+    h0v = x["h0"].astype(np.float32) if h0 else np.zeros(C, np.float32)
+    h0d = torch.from_numpy(h0v.reshape(B, D)).to(DEV) if h0 else None
+    if fused:
+        h, da, db, dh0 = lrs.scan_fwd_bwd(dev["a"], dev["b"], dev["g"], h0d)
+    else:
+        h = lrs.scan_fwd(dev["a"], dev["b"], h0d, layout=layout)
+        da, db, dh0 = lrs.scan_bwd(dev["a"], h, dev["g"], h0d, layout=layout)
+    torch.cuda.synchronize()
+    f64 = {k: I.bf16_bits_to_f64(x[k]) for k in ("a", "b", "g")}
+    back = lambda t: I.bf16_bits_to_f64(from_dev(t.view(torch.int16), B, D, T, layout).view(np.uint16))
+    h64 = back(h)
+    ref_h = oracle.scan_fwd(f64["a"], f64["b"], h0v.astype(np.float64))
+    # the one-call form keeps h in fp32 between its passes when a channel fits one kernel
+    h_used = ref_h if (fused and T <= 8192) else h64
+    ref_da, ref_db, ref_dh0 = oracle.scan_bwd(f64["a"], h_used, h0v.astype(np.float64), f64["g"])
+    e = {"h": relerr(h64, ref_h), "da": relerr(back(da), ref_da), "db": relerr(back(db), ref_db),
+         "dh0": relerr(dh0.cpu().numpy().reshape(-1).astype(np.float64), ref_dh0)}
+    tag = f"random bf16 scan {layout} {B}x{D}x{T} h0={h0} fused={fused} seed={seed}"
+    log(tag + ": " + ", ".join(f"{k}={v:.2e}" for k, v in e.items()))
+    assert e["h"] <= 2e-2 and e["da"] <= 2e-2 and e["db"] <= 2e-2 and e["dh0"] <= 1e-5, tag
 
 
 @cases(25)
