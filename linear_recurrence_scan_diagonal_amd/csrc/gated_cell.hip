@@ -162,7 +162,7 @@ __device__ __forceinline__ void lstm_persist_tile(
     const IO* __restrict__ zo, IO* __restrict__ h, float* __restrict__ cs, int64_t row0,
     int64_t T, int64_t C, int64_t cbase, uint32_t off, int nvc, IoRow<IO, CPT> (&fr)[L],
     IoRow<IO, CPT> (&ir)[L], IoRow<IO, CPT> (&gr)[L], IoRow<IO, CPT> (&orr)[L],
-    PersistShared<NW, CPT>& s, int wid) {
+    PersistShared<NW, CPT>& s, int wid, int par) {
   constexpr int TW = NW * L;
   float av[L][CPT], bv[L][CPT];
   IoRow<IO, CPT> ocur[L];
@@ -198,7 +198,7 @@ __device__ __forceinline__ void lstm_persist_tile(
       A[k] = A[k] * av[i][k];
     }
   }
-  persist_enter<NW, CPT>(A, B, s, wid, off, x);
+  persist_enter<NW, CPT>(A, B, s, wid, off, x, par);
   IO* hp = h + row0 * C + cbase;
 #pragma unroll
   for (int i = 0; i < L; ++i) {
@@ -213,7 +213,7 @@ __device__ __forceinline__ void lstm_persist_tile(
     if (SAVE) store_row<CPT, FULL, NT>(cs + (row0 + i) * C + cbase, off, nv, x);
     hp += C;
   }
-  persist_advance<NW, CPT>(x, s, wid, off);
+  persist_advance<NW, CPT>(x, s, wid, off, par);
 }
 
 template <typename IO, int NW, int L, int CPT, bool SAVE, bool NT>
@@ -230,13 +230,14 @@ __global__ __launch_bounds__(NW* kWave) void k_lstm_fwd_persist(
   const int nvc = clamp_valid(C - (cbase + off), CPT);
   const bool cfull = vec && cbase + CW <= C;
   for (int j = threadIdx.x; j < CW; j += NW * kWave)
-    s.carry[j] = (c0p && cbase + j < C) ? c0p[cbase + j] : 0.0f;
+    s.carry[0][j] = (c0p && cbase + j < C) ? c0p[cbase + j] : 0.0f;
   const int64_t ntb = (T + TW - 1) / TW, nfull = T / TW;
   const int64_t w0 = (int64_t)wid * L;
   IoRow<IO, CPT> fr[L], ir[L], gr[L], orr[L];
 #define LRS_TILE(FULLT, PFT, TB)                                                                 \
   lstm_persist_tile<IO, NW, L, CPT, FULLT, PFT, SAVE, NT>(zf, zi, zc, zo, h, cs, (TB) * TW + w0, T, \
-                                                          C, cbase, off, nvc, fr, ir, gr, orr, s, wid)
+                                                          C, cbase, off, nvc, fr, ir, gr, orr, s, wid, \
+                                                          (int)((TB) & 1))
   if (cfull && nfull > 0) {
     // full tiles in a straight loop (each loads the next full tile), then the
     // last full tile and the ragged tail, if any
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(NW* kWave) void k_lstm_fwd_persist(
   if (c_last) {
     __syncthreads();
     for (int j = threadIdx.x; j < CW; j += NW * kWave)
-      if (cbase + j < C) c_last[cbase + j] = s.carry[j];
+      if (cbase + j < C) c_last[cbase + j] = s.carry[ntb & 1][j];
   }
 }
 

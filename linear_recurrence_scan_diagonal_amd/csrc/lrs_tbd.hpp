@@ -260,47 +260,54 @@ __device__ __forceinline__ int clamp_valid(int64_t n, int cpt) {
 // ---- persistent walks ------------------------------------------------------
 // One workgroup per channel block visits every time tile in order and keeps
 // the per-channel state entering the current tile in LDS (`carry`), so no
-// look-back state is needed.
+// look-back state is needed.  The wave maps and the carry alternate between
+// two buffers by tile parity (tile tb uses buffer tb & 1), which leaves one
+// barrier per tile: a buffer is written again only two tiles later, after
+// every wave has passed the barrier of the tile in between.
 template <int NW, int CPT>
 struct PersistShared {
-  float A[NW][kWave * CPT];
-  float B[NW][kWave * CPT];
-  float carry[kWave * CPT];
+  float A[2][NW][kWave * CPT];
+  float B[2][NW][kWave * CPT];
+  float carry[2][kWave * CPT];  // carry[0]: the state entering tile 0
 };
 
 // Publish this wave's per-channel maps (A, B) and return in x the state
 // entering this wave's first step: the maps of the earlier waves of the tile,
-// in order, applied to the carry.
+// in order, applied to the carry.  par: the tile's parity.
 template <int NW, int CPT>
 __device__ __forceinline__ void persist_enter(const float (&A)[CPT], const float (&B)[CPT],
                                               PersistShared<NW, CPT>& s, int wid, uint32_t off,
-                                              float (&x)[CPT]) {
+                                              float (&x)[CPT], int par) {
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
-    s.A[wid][off + k] = A[k];
-    s.B[wid][off + k] = B[k];
+    s.A[par][wid][off + k] = A[k];
+    s.B[par][wid][off + k] = B[k];
   }
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
     float PA = 1.0f, PB = 0.0f;
     for (int w = 0; w < wid; ++w) {
-      PB = __builtin_fmaf(s.A[w][off + k], PB, s.B[w][off + k]);
-      PA = PA * s.A[w][off + k];
+      PB = __builtin_fmaf(s.A[par][w][off + k], PB, s.B[par][w][off + k]);
+      PA = PA * s.A[par][w][off + k];
     }
-    x[k] = __builtin_fmaf(PA, s.carry[off + k], PB);
+    x[k] = __builtin_fmaf(PA, s.carry[par][off + k], PB);
   }
 }
 
-// Once every wave has read the tile's maps and the carry: the last wave stores
-// its final state (the state after the tile) as the next carry.
-template <int NW, int CPT>
+// The last wave stores its final state (the state after the tile) as the
+// next tile's carry, in the other buffer: that buffer was last read in the
+// previous tile, which every wave finished before this tile's barrier.
+// SYNC adds a barrier at the end of the tile, not needed for correctness: it
+// keeps the waves' loads of the next tile behind every wave's stores of this
+// one, which the SRU forward with saved cell states runs faster with.
+template <int NW, int CPT, bool SYNC = false>
 __device__ __forceinline__ void persist_advance(const float (&x)[CPT], PersistShared<NW, CPT>& s,
-                                                int wid, uint32_t off) {
-  __syncthreads();
+                                                int wid, uint32_t off, int par) {
+  if (SYNC) __syncthreads();
   if (wid == NW - 1) {
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) s.carry[off + k] = x[k];
+    for (int k = 0; k < CPT; ++k) s.carry[par ^ 1][off + k] = x[k];
   }
 }
 

@@ -397,7 +397,7 @@ __device__ __forceinline__ void sru_persist_tile(
     IO* __restrict__ h, float* __restrict__ cs, int64_t row0, int64_t T, int64_t C,
     int64_t cbase, uint32_t off, int nvc, const float (&nbf)[CPT], const float (&nbr)[CPT],
     IoRow<IO, CPT> (&fr)[L], IoRow<IO, CPT> (&rr)[L], IoRow<IO, CPT> (&xr)[L],
-    PersistShared<NW, CPT>& s, int wid) {
+    PersistShared<NW, CPT>& s, int wid, int par) {
   constexpr int TW = NW * L;
   float av[L][CPT], bv[L][CPT];
   IoRow<IO, CPT> rcur[L], xcur[L];
@@ -435,7 +435,7 @@ __device__ __forceinline__ void sru_persist_tile(
       A[k] = A[k] * av[i][k];
     }
   }
-  persist_enter<NW, CPT>(A, B, s, wid, off, x);
+  persist_enter<NW, CPT>(A, B, s, wid, off, x, par);
   IO* hp = h + row0 * C + cbase;
 #pragma unroll
   for (int i = 0; i < L; ++i) {
@@ -452,7 +452,7 @@ __device__ __forceinline__ void sru_persist_tile(
     if (SAVE) store_row<CPT, FULL, NT>(cs + (row0 + i) * C + cbase, off, nv, x);
     hp += C;
   }
-  persist_advance<NW, CPT>(x, s, wid, off);
+  persist_advance<NW, CPT, SAVE>(x, s, wid, off, par);
 }
 
 template <typename IO, int NW, int L, int CPT, bool SAVE, bool NT>
@@ -482,13 +482,14 @@ __global__ __launch_bounds__(NW* kWave) void k_sru_fwd_persist(
     }
   }
   for (int j = threadIdx.x; j < CW; j += NW * kWave)
-    s.carry[j] = (c0p && cbase + j < C) ? c0p[cbase + j] : 0.0f;
+    s.carry[0][j] = (c0p && cbase + j < C) ? c0p[cbase + j] : 0.0f;
   const int64_t ntb = (T + TW - 1) / TW, nfull = T / TW;
   const int64_t w0 = (int64_t)wid * L;
   IoRow<IO, CPT> fr[L], rr[L], xr[L];
 #define LRS_TILE(FULLT, PFT, TB)                                                               \
   sru_persist_tile<IO, NW, L, CPT, FULLT, PFT, SAVE, NT>(zf, zr, zx, h, cs, (TB) * TW + w0, T, C, \
-                                                         cbase, off, nvc, nbf, nbr, fr, rr, xr, s, wid)
+                                                         cbase, off, nvc, nbf, nbr, fr, rr, xr, s, wid, \
+                                                         (int)((TB) & 1))
   if (cfull && nfull > 0) {
     // full tiles in a straight loop (each loads the next full tile), then the
     // last full tile and the ragged tail, if any
@@ -512,7 +513,7 @@ __global__ __launch_bounds__(NW* kWave) void k_sru_fwd_persist(
   if (c_last) {
     __syncthreads();
     for (int j = threadIdx.x; j < CW; j += NW * kWave)
-      if (cbase + j < C) c_last[cbase + j] = s.carry[j];
+      if (cbase + j < C) c_last[cbase + j] = s.carry[ntb & 1][j];
   }
 }
 

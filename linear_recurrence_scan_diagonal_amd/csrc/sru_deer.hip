@@ -277,7 +277,7 @@ __device__ __forceinline__ void sru_deer_persist_tile(
     const IO* __restrict__ zf, const IO* __restrict__ zx, const float* __restrict__ c0p,
     const float* __restrict__ y, float* __restrict__ yn, int64_t row0, int64_t T, int64_t C,
     int64_t cbase, uint32_t off, int nvc, const float (&nbf)[CPT], const float (&vf)[CPT],
-    SdRows<IO, L, CPT>& w, PersistShared<NW, CPT>& s, int wid, uint32_t& dmax) {
+    SdRows<IO, L, CPT>& w, PersistShared<NW, CPT>& s, int wid, int par, uint32_t& dmax) {
   constexpr int TW = NW * L;
   float Jv[L][CPT], Bv[L][CPT], yo[L][CPT];
 #pragma unroll
@@ -318,7 +318,7 @@ __device__ __forceinline__ void sru_deer_persist_tile(
       A[k] = A[k] * Jv[i][k];
     }
   }
-  persist_enter<NW, CPT>(A, B, s, wid, off, x);
+  persist_enter<NW, CPT>(A, B, s, wid, off, x, par);
   float* op = yn + row0 * C + cbase;
 #pragma unroll
   for (int i = 0; i < L; ++i) {
@@ -332,7 +332,7 @@ __device__ __forceinline__ void sru_deer_persist_tile(
     store_row<CPT, FULL, NT>(op, off, row_ok ? nvc : 0, x);
     op += C;
   }
-  persist_advance<NW, CPT>(x, s, wid, off);
+  persist_advance<NW, CPT>(x, s, wid, off, par);
 }
 
 template <typename IO, int NW, int L, int CPT, bool NT>
@@ -364,14 +364,15 @@ __global__ __launch_bounds__(NW* kWave) void k_sru_deer_iter_persist(
     }
   }
   for (int j = threadIdx.x; j < CW; j += NW * kWave)
-    s.carry[j] = (c0p && cbase + j < C) ? c0p[cbase + j] : 0.0f;
+    s.carry[0][j] = (c0p && cbase + j < C) ? c0p[cbase + j] : 0.0f;
   const int64_t ntb = (T + TW - 1) / TW, nfull = T / TW;
   const int64_t w0 = (int64_t)wid * L;
   uint32_t dmax = 0;
   SdRows<IO, L, CPT> w;
 #define LRS_SDT(FULLT, PFT, TB)                                                                  \
   sru_deer_persist_tile<IO, NW, L, CPT, FULLT, PFT, NT>(zf, zx, c0p, y, yn, (TB) * TW + w0, T, C, \
-                                                        cbase, off, nvc, nbf, vf, w, s, wid, dmax)
+                                                        cbase, off, nvc, nbf, vf, w, s, wid,      \
+                                                        (int)((TB) & 1), dmax)
   if (cfull && nfull > 0) {
     // full tiles in a straight loop (each loads the next full tile), then the
     // last full tile and the ragged tail, if any
