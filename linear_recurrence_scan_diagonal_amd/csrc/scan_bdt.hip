@@ -1084,42 +1084,39 @@ __global__ __launch_bounds__(NW* kWave) void k_deer_iter(
 // ---------------------------------------------------------------------------
 template <int NW>
 struct FusedShared {
-  float wA[2][NW];
-  float wB[2][NW];
+  float2 wm[2][NW];                    // the waves' maps (A, B), by iteration parity
   float y0w[NW];                       // starting iterate at each wave's last step
   float xc[kDeerFuseMax + 1];          // iteration k's state entering the sub-chunk
-  uint32_t dmax[kDeerFuseMax][NW];     // per-wave max |y_k - y_{k-1}|
+  uint32_t dlane[kDeerFuseMax][NW * kWave];  // per-thread max |y_k - y_{k-1}|
+  uint32_t dmax[kDeerFuseMax][NW];           // per-wave max, folded after the walk
 };
 
+// Applies the waves' maps in wave order to xin, the state entering the
+// sub-chunk: returns the state entering this wave (wid is uniform, so the
+// loop picks it up when it reaches it) and leaves the state after the last
+// wave in xend.
 template <int NW>
-__device__ __forceinline__ void fused_combine(float WA, float WB, FusedShared<NW>& s, int par,
-                                              float& PA, float& PB, float& TA, float& TB) {
+__device__ __forceinline__ float fused_combine(float WA, float WB, FusedShared<NW>& s, int par,
+                                               float xin, float& xend) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  if (lane == 0) {
-    s.wA[par][wid] = WA;
-    s.wB[par][wid] = WB;
-  }
+  if (lane == 0) s.wm[par][wid] = make_float2(WA, WB);
   __syncthreads();
-  // the block's map in wave order; the prefix before this wave is the partial
-  // map when the loop reaches it (wid is uniform)
-  TA = 1.0f; TB = 0.0f; PA = 1.0f; PB = 0.0f;
+  float x = xin, xr = xin;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    if (w == wid) {
-      PA = TA;
-      PB = TB;
-    }
-    const float wa = s.wA[par][w];
-    TB = __builtin_fmaf(wa, TB, s.wB[par][w]);
-    TA = TA * wa;
+    if (w == wid) xr = x;
+    const float2 m = s.wm[par][w];
+    x = __builtin_fmaf(m.x, x, m.y);
   }
+  xend = x;
+  return xr;
 }
 
 // One Newton iteration k of a sub-chunk of the fused solve: y_k (yout) from
 // y_{k-1} (yin, held in registers); ent is y_{k-1} at the step before this
 // wave's first step on entry and y_k there on exit.  max |y_k - y_{k-1}| over
-// the wave's steps is folded into s.dmax[k - 1] with the NaN-propagating
+// the thread's steps is folded into its slot of s.dlane[k - 1] with the NaN-propagating
 // maximum (v_maximum3_f32), so a non-finite step still reads as the largest
 // update: the bit pattern of a non-negative float or a NaN orders as unsigned.
 template <int NW, int R, int E, bool FULL>
@@ -1162,12 +1159,12 @@ __device__ __forceinline__ void deer_fused_iter(int k, const float (&us)[R][E],
     RA[r] = readlane_f(A, kWave - 1);
     RB[r] = readlane_f(B, kWave - 1);
   }
-  float WA, WB, PA, PB, TA, TB;
+  float WA, WB, xend;
   chain_rows<R>(RA, RB, WA, WB);
-  fused_combine<NW>(WA, WB, s, par, PA, PB, TA, TB);
+  // y_k at the step before this wave's first step
+  float xr = fused_combine<NW>(WA, WB, s, par, xin, xend);
   par ^= 1;
-  if (threadIdx.x == 0) s.xc[k] = __builtin_fmaf(TA, xin, TB);  // every thread read xin above
-  float xr = __builtin_fmaf(PA, xin, PB);  // y_k at the step before this wave's first step
+  if (threadIdx.x == 0) s.xc[k] = xend;  // every thread read xin above
   ent = xr;
   float dmf = 0.0f;
 #pragma unroll
@@ -1183,8 +1180,10 @@ __device__ __forceinline__ void deer_fused_iter(int k, const float (&us)[R][E],
     }
     xr = __builtin_fmaf(RA[r], xr, RB[r]);
   }
-  const uint32_t dm = wave_max_u32(as_u32(dmf));
-  if (lane == 0 && dm > s.dmax[k - 1][wid]) s.dmax[k - 1][wid] = dm;
+  // each thread folds into a slot of its own; the wave and block maxima are
+  // taken once, after the last sub-chunk
+  __hip_atomic_fetch_max(&s.dlane[k - 1][threadIdx.x], as_u32(dmf), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // One sub-chunk (index c) of the fused solve: iterations 1..m.  Each lane
@@ -1270,7 +1269,8 @@ __device__ __forceinline__ void deer_fused_body(
   const float wd = w[ch % D];
   const float x0 = h0 ? h0[ch] : 0.0f;
   if (threadIdx.x <= (unsigned)m) s.xc[threadIdx.x] = x0;  // every iteration starts from h0
-  for (int i = threadIdx.x; i < kDeerFuseMax * NW; i += NW * kWave) s.dmax[i / NW][i % NW] = 0u;
+#pragma unroll
+  for (int i = 0; i < kDeerFuseMax; ++i) s.dlane[i][threadIdx.x] = 0u;
   __syncthreads();
   const float* urow = u + ch * T;
   const float* y0row = y0 ? y0 + ch * T : nullptr;
@@ -1288,6 +1288,15 @@ __device__ __forceinline__ void deer_fused_body(
                                           par, s);
   }
   if (redo) return;
+  __syncthreads();
+  {
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+#pragma unroll 1
+    for (int k = 0; k < m; ++k) {
+      const uint32_t v = wave_max_u32(s.dlane[k][threadIdx.x]);
+      if (lane == 0) s.dmax[k][wid] = v;
+    }
+  }
   __syncthreads();
   if (threadIdx.x < (unsigned)m) {
     const int k = threadIdx.x;

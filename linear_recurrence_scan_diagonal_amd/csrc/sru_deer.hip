@@ -415,14 +415,16 @@ struct SdFusedShared {
   float B[2][NW][kWave * CPT];
   float y0c[kWave * CPT];                     // starting iterate at the last row before the tile
   float ck[2][kDeerFuseMax][kWave * CPT];     // [tile parity][lev - 1]: state entering the tile
-  uint32_t dm[kDeerFuseMax][NW];
+  uint32_t dlane[kDeerFuseMax][NW * kWave];  // per-thread max |c_lev - c_{lev-1}|
+  uint32_t dm[kDeerFuseMax][NW];             // per-wave max, folded after the walk
 };
 
 // Newton iteration lev over one tile of the fused walk: the iterate c_lev
 // (yout) from c_{lev-1} (yin) in registers; ent holds c_{lev-1} at the step
 // before this wave's first row on entry and c_lev there on exit.  zq and xv:
 // the tile's gate inputs (sd_zq) and z_x, unpacked once.  The update norm
-// folds |c_lev - c_{lev-1}| with the NaN-propagating maximum (v_maximum3_f32):
+// folds |c_lev - c_{lev-1}| into the thread's slot of s.dlane[lev - 1] with
+// the NaN-propagating maximum (v_maximum3_f32):
 // a non-finite step still reads as the largest update, since the bits of a
 // non-negative float or a NaN order as unsigned integers.
 template <int NW, int L, int CPT, bool FULL>
@@ -499,8 +501,8 @@ __device__ __forceinline__ void sru_deer_fused_level(
       yout[i][k] = x[k];
     }
   }
-  const uint32_t dmax = wave_max_u32(as_u32(dmf));
-  if ((threadIdx.x & (kWave - 1)) == 0 && dmax > s.dm[lev - 1][wid]) s.dm[lev - 1][wid] = dmax;
+  __hip_atomic_fetch_max(&s.dlane[lev - 1][threadIdx.x], as_u32(dmf), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_WORKGROUP);
   // the state after the tile goes to the other tile-parity slot, which no wave
   // reads before the barrier that ends this tile; the maps of level lev + 2
   // (same parity) are written after every wave has passed level lev + 1's
@@ -625,7 +627,8 @@ __device__ __forceinline__ void sru_deer_fused_body(
     if (lv == 0) s.y0c[c] = v;
     else s.ck[0][lv - 1][c] = v;
   }
-  for (int j = threadIdx.x; j < kDeerFuseMax * NW; j += NW * kWave) s.dm[j / NW][j % NW] = 0u;
+#pragma unroll
+  for (int j = 0; j < kDeerFuseMax; ++j) s.dlane[j][threadIdx.x] = 0u;
   __syncthreads();
   const int64_t ntb = (T + TW - 1) / TW, nfull = T / TW;
   const int64_t w0 = (int64_t)wid * L;
@@ -640,6 +643,13 @@ __device__ __forceinline__ void sru_deer_fused_body(
                                                      cbase, off, nvc, m, nbf, vf, tpar, s, wid);
   }
   if (redo) return;
+  __syncthreads();
+  // the wave maxima of each level's slots, then the block's
+#pragma unroll 1
+  for (int k = 0; k < m; ++k) {
+    const uint32_t v = wave_max_u32(s.dlane[k][threadIdx.x]);
+    if (lane == 0) s.dm[k][wid] = v;
+  }
   __syncthreads();
   if (threadIdx.x < (unsigned)m) {
     const int k = threadIdx.x;
