@@ -464,7 +464,7 @@ __device__ __forceinline__ void sru_deer_fused_level(
       A[k] = A[k] * Jv[i][k];
     }
   }
-  // the earlier waves' maps applied to iteration lev's state entering the tile
+  // the earlier waves' maps applied in order to iteration lev's state entering the tile
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
     s.A[lp][wid][off + k] = A[k];
@@ -474,12 +474,9 @@ __device__ __forceinline__ void sru_deer_fused_level(
   float x[CPT];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
-    float PA = 1.0f, PB = 0.0f;
-    for (int w = 0; w < wid; ++w) {
-      PB = __builtin_fmaf(s.A[lp][w][off + k], PB, s.B[lp][w][off + k]);
-      PA = PA * s.A[lp][w][off + k];
-    }
-    x[k] = __builtin_fmaf(PA, s.ck[tpar][lev - 1][off + k], PB);
+    float xk = s.ck[tpar][lev - 1][off + k];
+    for (int w = 0; w < wid; ++w) xk = __builtin_fmaf(s.A[lp][w][off + k], xk, s.B[lp][w][off + k]);
+    x[k] = xk;
   }
   // every wave has read y0c (before the barrier above): the last wave now
   // keeps the starting iterate at the tile's last row for the next tile
