@@ -72,10 +72,11 @@ DEER_FLOPS_PER_ELEM_ITER = 15
 FP32_VECTOR_PEAK_TFLOPS = 157.3
 
 
-def deer_fused_applies(T: int, k_max: int) -> bool:
-    """The library's default rule for the fused DEER solve: channels one
-    workgroup walks (at most 8192 steps) and K_max <= 8."""
-    return T <= 8192 and k_max <= 8
+def deer_fused_applies(T: int, k_max: int, C: int, cus: int) -> bool:
+    """The library's default rule for the fused DEER solve: K_max <= 8 and
+    channels of at most 8192 steps or at least as many channels as the device
+    has compute units (`cus`)."""
+    return k_max <= 8 and (T <= 8192 or C >= cus)
 
 
 def sru_deer_fused_applies(C: int, k_max: int) -> bool:
@@ -319,6 +320,9 @@ def parse():
     p.add_argument("--crossover", action="store_true",
                    help="time the sequential and the parallel scan kernels at T = 4 .. 8192 "
                         "(2^24 elements) and print a table, instead of the bench line")
+    p.add_argument("--deer-crossover", action="store_true",
+                   help="time the DEER solve against the sequential loop (lrs_rnn_seq) over "
+                        "channel counts and lengths and print a table, instead of the bench line")
     p.add_argument("--summarize", metavar="DIR",
                    help="summarise rocprofv3 CSV output under DIR into profiles/ and exit")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -366,8 +370,8 @@ class DeviceEvent:
 
 
 def step_kernel_ms(torch, calls, reps):
-    """Average duration of each entry point of the step, from HIP events
-    recorded on the launch stream after every call of `reps` consecutive
+    """Duration of every call of each entry point (lists of ms), from HIP
+    events recorded on the launch stream after every call of `reps` consecutive
     steps.  A GPU-side spin issued first lets the host queue all of them
     before the device reaches the first, so host launch latency stays out of
     the measurement, and each kernel sees the same cache state as in the
@@ -385,13 +389,13 @@ def step_kernel_ms(torch, calls, reps):
             ev[i].record(stream)
             i += 1
     torch.cuda.synchronize()
-    out = {k: 0.0 for k in calls}
+    per_call = {k: [] for k in calls}
     i = 1
     for _ in range(reps):
         for k in calls:
-            out[k] += ev[i - 1].ms_until(ev[i]) / reps
+            per_call[k].append(ev[i - 1].ms_until(ev[i]))
             i += 1
-    return out
+    return per_call
 
 
 def cold_kernel_ms(torch, calls, reps, flush):
@@ -443,6 +447,9 @@ def main():
     if args.crossover:
         crossover(args, np, torch, lrs, I, dev)
         return
+    if args.deer_crossover:
+        deer_crossover(args, np, torch, lrs, I, dev)
+        return
     line, w = measure(args, np, torch, lrs, I, dev)
     also = args.also
     if also is None:
@@ -454,7 +461,7 @@ def main():
         sub.workload, sub.layout, sub.graph, sub.no_stream_ref = name, "bdt", False, True
         sl, _ = measure(sub, np, torch, lrs, I, dev)
         extra_lines[name] = {k: sl[k] for k in ("value", "unit", "ms_per_step", "config",
-                                                "roofline", "per_kernel_ms", "step_hbm_frac",
+                                                "roofline", "per_kernel_ms", "per_kernel_stats_ms", "step_hbm_frac",
                                                 "cold") if k in sl}
     cpu = None
     if not args.no_cpu_baseline:
@@ -663,15 +670,32 @@ def measure(args, np, torch, lrs, I, dev):
         extra["ms_per_step_graph"] = round(timed(graph.replay, args.steps)[0], 5)
     # (3) per-kernel launch durations for the roofline: `steps` more steps
     #     with a HIP event after every entry point, on its launch stream
-    per_kernel = step_kernel_ms(torch, calls, args.steps)
+    per_call = step_kernel_ms(torch, calls, args.steps)
+    per_kernel = {k: sum(v) / len(v) for k, v in per_call.items()}
+    extra["per_kernel_stats_ms"] = {k: {"median": round(float(np.median(v)), 5),
+                                        "min": round(min(v), 5), "max": round(max(v), 5),
+                                        "calls": len(v)} for k, v in per_call.items()}
     extra["per_kernel_timing"] = ("HIP event (device-scope release) after every call of "
                                   "queued steps")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
     if w.kind == "sru_deer":
         info = lrs.deer_stats(ws, 5)
     if w.kind == "deer":
         # the synchronous form reads the record back after every solve
         extra["ms_per_step_sync"] = round(timed(solve_sync, args.steps)[0], 5)
         info = lrs.deer_stats(ws, 5)
+        # the same recurrence evaluated step after step, one lane per channel
+        # (T dependent steps whatever the channel count): the sequential
+        # reference the solve replaces, with the largest difference between
+        # the two results relative to the largest |h|
+        h_seq = torch.empty_like(u)
+        seq_ms = timed(lambda: lrs.rnn_seq(wd, u, h0, out=h_seq), args.steps)[0]
+        diff = ((h_seq - hd).abs().max() / hd.abs().max().clamp_min(1e-30)).item()
+        extra["seq_ref"] = {"kernel": "rnn_seq, one lane per channel, T dependent steps",
+                            "ms": round(seq_ms, 5), "elements_per_s": N / (seq_ms / 1e3),
+                            "solve_speedup": round(seq_ms / ms_per_step, 3),
+                            "max_rel_diff_vs_solve": diff}
+        del h_seq
     value = N / (ms_per_step / 1e3)
     # (4) the same entry points with cold caches before every call
     flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
@@ -702,7 +726,7 @@ def measure(args, np, torch, lrs, I, dev):
         extra["deer_deltas"] = info["deltas"]
     else:
         iters = info["iters"]
-        if deer_fused_applies(w.T, 5):
+        if deer_fused_applies(w.T, 5, w.C, cus):
             # one pass over all K_max iterations, and a second one when the stop
             # rule fired earlier
             solve_bytes = BYTES_PER_ELEM["deer_fused"] * N * (1 if iters == 5 else 2)
@@ -719,7 +743,7 @@ def measure(args, np, torch, lrs, I, dev):
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes": dom_bytes,
                 "avg_launch_ms": round(dom_ms, 5)}
-    if w.kind == "deer" and deer_fused_applies(w.T, 5):
+    if w.kind == "deer" and deer_fused_applies(w.T, 5, w.C, cus):
         # vector-ALU bound: the method's flops over the iterations it performed
         flops = DEER_FLOPS_PER_ELEM_ITER * N * iters
         tflops = flops / (dom_ms / 1e3) / 1e12
@@ -812,6 +836,55 @@ def crossover(args, np, torch, lrs, I, dev):
             v = res[m]
             cells += [cell(None if v is None else v[0], 12), cell(None if v is None else v[1], 20)]
         print(f"| {T} | {D} | " + " | ".join(cells) + " |", flush=True)
+
+
+def deer_crossover(args, np, torch, lrs, I, dev):
+    """The DEER solve (eps 1e-5, K_max 5, asynchronous form) under the default
+    plan, with the fused pass forced (deer_fuse = 1) and with one launch per
+    iteration (deer_fuse = 0), against the sequential loop (lrs_rnn_seq, one
+    lane per channel), on the DEER workload's distributions (w ~ U(-0.9, 0.9)
+    per feature, u ~ N(0, 1), h0 = 0) drawn on the device, over channel counts
+    and lengths.  HIP events over --steps calls each."""
+    dw = I.WORKLOADS["deer"]
+    shapes = ([(1, c, 8192) for c in (64, 512, 2048)] +
+              [(dw.B, dw.D, T) for T in (1024, 2048, 4096, 8192, 16384, 32768)] +
+              [(1, c, 32768) for c in (256, 512, 1024, 2048)] + [(64, 1024, 8192)])
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(args.steps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) * 1e3 / args.steps
+
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    print(f"| channels | T | DEER default us (iterations) | fused | one launch per iteration | "
+          f"sequential us | sequential / DEER default |")
+    print("|---|---|---|---|---|---|---|")
+    for B, D, T in shapes:
+        u = I.device_draw(dw.seed + T, dw.dists["u"], (B, D, T), dev)
+        wd = I.device_draw(dw.seed + 1, dw.dists["w"], (D,), dev)
+        h, hs = torch.empty_like(u), torch.empty_like(u)
+        ws = torch.empty(max(1, lrs.load().lrs_deer_workspace_bytes(B, D, T, 5)),
+                         dtype=torch.uint8, device=dev)
+        t = {}
+        for mode, opts in (("default", None), ("fused", {"deer_fuse": 1}),
+                           ("per-iteration", {"deer_fuse": 0})):
+            t[mode] = timed(lambda: lrs.deer_solve(wd, u, None, None, eps=1e-5, k_max=5, out=h,
+                                                   workspace=ws, sync=False, options=opts))
+            if mode == "default":
+                iters = lrs.deer_stats(ws, 5)["iters"]
+        t_seq = timed(lambda: lrs.rnn_seq(wd, u, None, out=hs))
+        plan = "fused" if deer_fused_applies(T, 5, B * D, cus) else "per-iteration"
+        print(f"| {B * D} | {T} | {t['default']:.1f} ({iters}, {plan}) | {t['fused']:.1f} | "
+              f"{t['per-iteration']:.1f} | {t_seq:.1f} | {t_seq / t['default']:.2f} |",
+              flush=True)
+        del u, h, hs, ws
 
 
 STREAM_REF_ELEMS = 1 << 26  # 256 MiB per fp32 operand

@@ -52,7 +52,9 @@
  *    reset between iterations) when the 128-channel blocks are at least as
  *    many as the device's compute units; with the persistent plan and
  *    k_max <= 8, the SRU-by-DEER solve runs all its Newton iterations in that
- *    one walk, and DEER solves whose channels one workgroup walks do the same.
+ *    one walk, and DEER solves do the same with one workgroup per channel when
+ *    the channels have at most 8192 steps or number at least the device's
+ *    compute units.
  *    The entry points with the suffix _ex take an lrs_options argument that
  *    moves these choices explicitly (for comparing kernel families on the
  *    same inputs, or measuring crossovers); the library keeps no global or
@@ -130,8 +132,13 @@ typedef struct lrs_options {
                                  (default: the device's compute units; 0 =
                                  always, a huge value = never) */
   int32_t deer_fuse;          /* DEER and SRU-by-DEER solves: 0 = one launch per
-                                 Newton iteration; otherwise all iterations in
-                                 one pass where that applies (default) */
+                                 Newton iteration; > 0 = all iterations in one
+                                 pass whenever k_max <= 8 (SRU by DEER: on the
+                                 persistent plan); otherwise (default) one pass
+                                 where it applies: k_max <= 8 and channels of
+                                 at most 8192 steps or at least as many
+                                 channels as compute units (SRU by DEER: the
+                                 persistent plan) */
   int32_t reserved;           /* set to 0 */
 } lrs_options;
 
@@ -412,8 +419,9 @@ LRS_API size_t lrs_deer_workspace_bytes(int64_t B, int64_t D, int64_t T, int k_m
  * NaN or infinite.  If all three are NULL the call is asynchronous: it returns
  * LRS_OK once everything is enqueued (and may be captured in a HIP graph);
  * lrs_deer_stats reads the record later.
- * When one workgroup walks each channel (T <= 8192) and k_max <= 8, all
- * iterations run in one pass over each channel (u read once, the last iterate
+ * When k_max <= 8 and the channels have at most 8192 steps or number at
+ * least the device's compute units, all iterations run in one pass over each
+ * channel, one workgroup per channel (u read once, the last iterate
  * written once; the norms of every iteration are kept), and when the stop rule
  * ends the solve before k_max a second pass recomputes exactly that many
  * iterations; the record, the iteration count and the result (within fp32
@@ -444,8 +452,7 @@ LRS_API size_t lrs_deer_seq_workspace_bytes(int64_t B, int64_t D, int64_t T, int
  * convergence flags; with both NULL the call only enqueues work.  Other
  * arguments as for lrs_deer_solve.  B is limited to 65535.  Returns
  * LRS_ERR_NONFINITE when some sequence's last update was NaN or infinite.
- * Under the same conditions as lrs_deer_solve (T <= 8192, k_max <= 8,
- * deer_fuse not 0) all iterations run in one pass that keeps each
+ * Under the same conditions as lrs_deer_solve all iterations run in one pass that keeps each
  * sequence's norms per iteration; sequences whose stop rule fired before
  * k_max are recomputed to their own count in a second pass. */
 LRS_API int lrs_deer_solve_seq(const float *w, const float *u, const float *h0,
@@ -498,6 +505,16 @@ LRS_API size_t lrs_deer_bwd_workspace_bytes(int64_t B, int64_t D, int64_t T);
 LRS_API int lrs_deer_bwd(const float *w, const float *h0, const float *h, const float *grad_h,
                  float *grad_u, float *grad_w, float *grad_h0, int64_t B, int64_t D, int64_t T,
                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* The same recurrence h_t = tanh(w_d * h_{t-1} + u_t) evaluated step after
+ * step, one lane per channel: the O(T)-depth loop that DEER replaces by a few
+ * Newton iterations of log-depth scans ([P4] core principle: the solve's fixed
+ * point is this sequential solution).  A reference point for lrs_deer_solve:
+ * its time is T dependent steps whatever the number of channels.
+ * w: [D] fp32.  u: [B,D,T] fp32.  h0: [B,D] fp32 or NULL (zero).
+ * h: [B,D,T] fp32 output; it must not overlap u, w or h0.  No workspace. */
+LRS_API int lrs_rnn_seq(const float *w, const float *u, const float *h0, float *h, int64_t B,
+                        int64_t D, int64_t T, void *stream);
 
 #ifdef __cplusplus
 }

@@ -12,7 +12,7 @@ DEER_DEFAULT_KMAX = 5
 
 _BINDING_NAMES = ("scan_fwd", "scan_bwd", "scan_fwd_bwd", "sru_fwd", "sru_bwd", "deer_solve", "deer_stats",
                   "deer_bwd", "deer_solve_seq", "deer_eps_schedule", "lstm_fwd", "lstm_bwd",
-                  "sru_deer_fwd", "scan_workspace_bytes", "plan_options",
+                  "sru_deer_fwd", "rnn_seq", "scan_workspace_bytes", "plan_options",
                   "LrsError", "load")
 
 __all__ = ["DEER_DEFAULT_EPS", "DEER_DEFAULT_KMAX", *_BINDING_NAMES]

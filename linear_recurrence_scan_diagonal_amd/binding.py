@@ -29,7 +29,8 @@ EXPORTS = ("lrs_status_string", "lrs_version", "lrs_scan_workspace_bytes", "lrs_
            "lrs_deer_solve", "lrs_deer_stats", "lrs_sru_bwd_workspace_bytes", "lrs_sru_bwd",
            "lrs_deer_bwd_workspace_bytes", "lrs_deer_bwd", "lrs_lstm_workspace_bytes",
            "lrs_lstm_fwd", "lrs_lstm_bwd", "lrs_scan_fwd_bwd", "lrs_sru_deer_workspace_bytes",
-           "lrs_sru_deer_fwd", "lrs_deer_seq_workspace_bytes", "lrs_deer_solve_seq")
+           "lrs_sru_deer_fwd", "lrs_deer_seq_workspace_bytes", "lrs_deer_solve_seq",
+           "lrs_rnn_seq")
 
 # entry points that have an _ex variant taking lrs_options
 _EX_BASES = ("lrs_scan_fwd", "lrs_scan_bwd", "lrs_scan_fwd_bwd", "lrs_sru_fwd", "lrs_sru_deer_fwd",
@@ -156,6 +157,8 @@ def load():
     lib.lrs_deer_bwd_workspace_bytes.restype = _sz
     lib.lrs_deer_bwd.argtypes = [_vp] * 7 + [_i64, _i64, _i64, _vp, _sz, _vp]
     lib.lrs_deer_bwd.restype = _int
+    lib.lrs_rnn_seq.argtypes = [_vp] * 4 + [_i64, _i64, _i64, _vp]
+    lib.lrs_rnn_seq.restype = _int
     lib.lrs_options_default.argtypes = [ctypes.POINTER(LrsOptions)]
     lib.lrs_options_default.restype = None
     for name in _EX_BASES:
@@ -545,6 +548,22 @@ def deer_bwd(w, h, grad_h, h0=None, want_grad_h0: bool = True, out=None, workspa
     _call(lib.lrs_deer_bwd(_ptr(w), _ptr(h0), _ptr(h), _ptr(grad_h), _ptr(gu), _ptr(gw), _ptr(gh0),
                            B, D, T, _ptr(ws), nbytes, _stream(dev)), "lrs_deer_bwd")
     return gu, gw, gh0
+
+
+def rnn_seq(w, u, h0=None, out=None):
+    """h_t = tanh(w h_{t-1} + u_t) over u [B,D,T] fp32, evaluated step after
+    step with one lane per channel (lrs_rnn_seq); the sequential reference for
+    deer_solve.  Returns h [B,D,T]."""
+    lib = load()
+    B, D, T = _dims(u, "bdt")
+    _check_dev("u", u, torch.float32, u.shape)
+    _check_dev("w", w, torch.float32, (D,))
+    _check_dev("h0", h0, torch.float32, (B, D))
+    h = torch.empty_like(u) if out is None else out
+    _check_dev("out", h, torch.float32, u.shape)
+    _call(lib.lrs_rnn_seq(_ptr(w), _ptr(u), _ptr(h0), _ptr(h), B, D, T, _stream(u.device)),
+          "lrs_rnn_seq")
+    return h
 
 
 def deer_stats(workspace, k_max: int = 5):

@@ -675,15 +675,25 @@ static int read_deer_record(const DeerRecord& r, int k_max, int* iters_out, floa
   return buf[2] ? LRS_ERR_NONFINITE : LRS_OK;
 }
 
-// The fused solve (all Newton iterations in one walk over each channel) applies
-// to channels that one workgroup walks and to k_max <= kDeerFuseMax; it needs
-// one norm slot set per iteration.
-static bool deer_fusable(const lrs::RowPlan& p, int k_max) {
-  return p.nchunk == 1 && k_max <= lrs::kDeerFuseMax;
+// The fused solve (all Newton iterations in one walk over each channel, one
+// workgroup per channel) needs k_max <= kDeerFuseMax: one norm slot set per
+// iteration.  By default it runs where one workgroup walks the channel in any
+// case (T <= 8192), and for longer channels when there are at least as many
+// channels as compute units.  It moves 8 bytes per element for the whole solve
+// against 56 for one launch per iteration: per 5-iteration solve, 0.35 ms
+// against 1.35 ms at 8192 channels of 16384 steps and 50 us against 122 us at
+// 256 channels of 32768.  With fewer channels each walk is a long serial
+// chain on a mostly idle device, and the per-iteration launches, which spread
+// every channel over many workgroups, take over.  deer_fuse = 0 in the
+// caller's options never fuses; deer_fuse > 0 fuses whenever k_max allows.
+static bool deer_use_fused(const lrs::RowPlan& p, int64_t C, int k_max, const lrs::Opts& opt) {
+  if (k_max > lrs::kDeerFuseMax || opt.deer_fuse == 0) return false;
+  if (opt.deer_fuse > 0) return true;
+  return p.nchunk == 1 || C >= (int64_t)lrs::device_cus();
 }
 
-// deer_fuse = 0 in the caller's options runs the iterations one launch each
-// even where the fused solve applies.
+// deer_fuse = 0 in the caller's options runs the SRU-by-DEER iterations one
+// launch each even where its fused walk applies.
 static bool deer_fuse_enabled(const lrs::Opts& opt) { return opt.deer_fuse != 0; }
 
 static size_t deer_fused_set_words(int k_max) {
@@ -697,7 +707,8 @@ size_t lrs_deer_workspace_bytes(int64_t B, int64_t D, int64_t T, int k_max) {
   const lrs::RowPlan p = deer_plan(C, T);
   size_t bytes = kAlign + deer_record_bytes(k_max) + align_up((size_t)N * 4);
   if (p.nchunk > 1) bytes += align_up((size_t)(C * p.nchunk) * 8) + align_up((size_t)C * 4);
-  if (deer_fusable(p, k_max)) bytes += align_up(deer_fused_set_words(k_max) * 4);
+  // the fused solve's norm sets, whichever plan the call takes
+  if (k_max <= lrs::kDeerFuseMax) bytes += align_up(deer_fused_set_words(k_max) * 4);
   return bytes;
 }
 
@@ -744,7 +755,7 @@ static int deer_solve_impl(const float* w, const float* u, const float* h0, cons
   const int vec = aligned(u, 16) && aligned(h, 16) && aligned(ybuf, 16) &&
                   (!h_init || aligned(h_init, 16)) && (T % 4 == 0);
 
-  if (deer_fusable(p, k_max) && deer_fuse_enabled(opt)) {
+  if (deer_use_fused(p, C, k_max, opt)) {
     uint32_t* sets = cv.take<uint32_t>((int64_t)deer_fused_set_words(k_max));
     // the pass must not overwrite a starting iterate held in h: a redo may need it
     float* out = (h_init == h) ? ybuf : h;
@@ -852,7 +863,7 @@ static int deer_solve_seq_impl(const float* w, const float* u, const float* h0, 
                                         (int64_t)((char*)(seq_rec + B * 4) - (char*)seq_slots) / 4,
                                         s));
   if (rc != LRS_OK) return rc;
-  if (deer_fusable(p, k_max) && deer_fuse_enabled(opt)) {
+  if (deer_use_fused(p, C, k_max, opt)) {
     // all iterations in one pass, each sequence's norms folded into seq_delta
     float* out = (h_init == h) ? ybuf : h;
     rc = hip_status(lrs::launch_deer_fused(w, u, h_init, h0, out, h, C, D, T, p, vec, k_max, eps,
@@ -1026,6 +1037,24 @@ static int sru_deer_fwd_impl(const void* z_f, const void* z_r, const void* z_x, 
   if (rc != LRS_OK) return rc;
   if (!iters_out && !deltas_out && !converged_out) return LRS_OK;  // asynchronous form
   return read_deer_record(r, k_max, iters_out, deltas_out, converged_out, s);
+}
+
+// Sequential tanh RNN: no workspace, one launch.
+int lrs_rnn_seq(const float* w, const float* u, const float* h0, float* h, int64_t B, int64_t D,
+                int64_t T, void* stream) {
+  int64_t C, N;
+  if (!shape_ok(B, D, T, &C, &N)) return LRS_ERR_INVALID_ARG;
+  if (N == 0) return LRS_OK;
+  if (!w || !u || !h) return LRS_ERR_INVALID_ARG;
+  if (!aligned(w, 4) || !aligned(u, 4) || !aligned(h, 4) || (h0 && !aligned(h0, 4)))
+    return LRS_ERR_INVALID_ARG;
+  const size_t nb = (size_t)N * 4;
+  if (overlap(h, nb, u, nb) || overlap(h, nb, w, (size_t)D * 4) ||
+      overlap(h, nb, h0, (size_t)C * 4))
+    return LRS_ERR_INVALID_ARG;
+  if (!grid_ok((C + 63) / 64, 64)) return LRS_ERR_UNSUPPORTED;
+  const int vec = aligned(u, 16) && aligned(h, 16) && T % 4 == 0;
+  return hip_status(lrs::launch_rnn_seq(w, u, h0, h, C, D, T, vec, (hipStream_t)stream));
 }
 
 // DEER backward: look-back state, nchunk * C floats of dL/dw partials and the

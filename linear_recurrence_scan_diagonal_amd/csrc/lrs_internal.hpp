@@ -116,6 +116,10 @@ hipError_t launch_deer_bwd(const float* w, const float* h, const float* h0, cons
                            float* du, float* dw, float* dh0, float* part, double* acc, int64_t B,
                            int64_t D, int64_t T, const RowPlan& p, int vec, uint64_t* status,
                            unsigned* tickets, hipStream_t stream);
+// Sequential tanh RNN (one lane per channel, ceil(C / 64) one-wave workgroups;
+// vec: T % 4 == 0 and u, h 16-byte aligned).
+hipError_t launch_rnn_seq(const float* w, const float* u, const float* h0, float* h, int64_t C,
+                          int64_t D, int64_t T, int vec, hipStream_t stream);
 // One Newton iteration.  seq_slots != nullptr: per-sequence stopping (norm
 // slots kSeqSlots per sequence per set, three sets; seq_delta[seq * k_max + i]
 // holds sequence seq's norm of iteration i once k_deer_seq_book folded it).

@@ -37,7 +37,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 33, names
+    assert len(names) == 34, names
     raw = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(raw, n), f"{n} declared in lrs.h but not exported"
@@ -119,6 +119,12 @@ def test_validation_before_any_launch(lib):
     q = ctypes.c_void_p
     assert lib.lrs_scan_bwd(q(0x10000), q(0x20000), null, q(0x30000), q(0x10000), q(0x40000), null,
                             1, 1, 64, 0, 0, null, 0, null) == b.LRS_ERR_INVALID_ARG
+    # sequential RNN: null u, negative size, misaligned h, h overlapping u; empty is valid
+    assert lib.lrs_rnn_seq(p, null, null, q(0x9000), 1, 1, 4, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_rnn_seq(p, p, null, q(0x9000), 1, -1, 4, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_rnn_seq(q(0x100), q(0x1000), null, q(0x9002), 1, 1, 4, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_rnn_seq(q(0x100), q(0x1000), null, q(0x1008), 1, 1, 4, null) == b.LRS_ERR_INVALID_ARG
+    assert lib.lrs_rnn_seq(null, null, null, null, 2, 3, 0, null) == b.LRS_OK
     # SRU and DEER argument checks
     assert lib.lrs_sru_fwd(p, p, p, p, p, null, p, null, null, 4, 1, 1, 3, null, 0,
                            null) == b.LRS_ERR_INVALID_ARG

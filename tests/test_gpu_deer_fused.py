@@ -51,6 +51,10 @@ def both_paths(plan, x, B, D, T, eps, k_max, h_init=None, in_place=False):
     (2, 3, 2048, 1e-5, 5, True, False, False),       # longest channel of 4 steps per lane
     (2, 3, 2049, 1e-5, 5, True, True, False),        # first of 8 steps per lane, partial
     (2, 3, 4097, 1e-5, 5, True, False, False),       # second sub-chunk of one step
+    (2, 3, 16384, 1e-5, 5, True, False, False),      # four sub-chunks (forced: few channels)
+    (1, 5, 20001, 1e-5, 8, True, False, False),      # five sub-chunks, the last partial
+    (2, 3, 12289, 1e-2, 6, True, False, False),      # long channel, early stop: recomputed
+    (2, 4, 17000, 1e-5, 6, True, True, True),        # long, warm start held in h, early stop
 ])
 def test_fused_matches_oracle_and_per_iteration(plan, B, D, T, eps, k_max, h0, warm,
                                                 in_place):
@@ -157,7 +161,8 @@ def test_sru_deer_fused_matches_oracle_and_per_iteration(plan, B, D, T, io, eps,
 @pytest.mark.parametrize("B,D,T,warm,in_place", [(4, 3, 100, False, False),
                                                  (3, 64, 4096, False, False),
                                                  (2, 40, 8000, True, False),
-                                                 (4, 8, 6000, True, True)])
+                                                 (4, 8, 6000, True, True),
+                                                 (3, 8, 12000, False, False)])
 def test_per_sequence_fused(plan, B, D, T, warm, in_place):
     from test_gpu_deer_seq import make
     scales = [0.05, 1.0, 3.0, 0.5][:B]
@@ -198,3 +203,32 @@ def test_per_sequence_fused_async(plan):
     h_async, ws = lrs.deer_solve_seq(wd, ud, h0d, k_max=8, sync=False)
     torch.cuda.synchronize()
     assert torch.equal(h_sync, h_async)
+
+
+def test_fused_long_channels_by_default():
+    """Channels longer than 8192 steps that number at least the compute units
+    take the fused pass under the default options: the same result,
+    iteration count and norms as forcing it, against the oracle and the
+    one-launch-per-iteration path."""
+    B, D, T = 4, 512, 12288
+    w = I.scaled(I.WORKLOADS["deer"], B=B, D=D, T=T, seed=16900)
+    x = I.deer_inputs(w)
+    wd = torch.from_numpy(x["w"]).to(DEV)
+    u = torch.from_numpy(x["u"].reshape(B, D, T)).to(DEV)
+    cus = torch.cuda.get_device_properties(DEV).multi_processor_count
+    assert B * D >= cus
+    h_def, info_def = lrs.deer_solve(wd, u)
+    with lrs.plan_options(deer_fuse=1):
+        h_f, info_f = lrs.deer_solve(wd, u)
+    with lrs.plan_options(deer_fuse=0):
+        h_p, info_p = lrs.deer_solve(wd, u)
+    torch.cuda.synchronize()
+    ref_h, ref_it, ref_d = oracle.deer(x["w"], x["u"].reshape(B, D, T), x["h0"].reshape(B, D),
+                                       None, eps=1e-5, k_max=5)
+    e = relerr(h_def.cpu().numpy(), ref_h)
+    ep = relerr(h_p.cpu().numpy(), ref_h)
+    log(f"deer {B}x{D}x{T} default plan: iters {info_def['iters']} (oracle {ref_it}), "
+        f"relerr {e:.2e}, per-iteration {ep:.2e}")
+    assert torch.equal(h_def, h_f) and info_def == info_f
+    assert info_def["iters"] == info_p["iters"] == ref_it
+    assert e <= 1e-5 and ep <= 1e-5
