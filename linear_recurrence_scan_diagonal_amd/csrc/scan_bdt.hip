@@ -1841,10 +1841,12 @@ hipError_t launch_deer_fused(const float* w, const float* u, const float* y0, co
   const dim3 grid((unsigned)C);
   if (seq_rec) rec = seq_rec;  // the redo reads the per-sequence records
   // channels of more than 2048 steps take the fused shape (4 waves of 2 rows
-  // of 8 steps per lane, walking the channel as 4096-step sub-chunks);
-  // shorter ones keep the plan's smallest covering shape with 4 steps per lane
+  // of 8 steps per lane, walking the channel as 4096-step sub-chunks); those
+  // of 513 to 2048 steps one sub-chunk of 2 rows of 8 steps per lane on 2
+  // waves or 1 (2048 or 1024 steps); shorter ones keep the plan's smallest
+  // covering shape with 4 steps per lane
   RowPlan p = plan;
-  const bool wide = T > 2048;
+  const int e8 = T > 2048 ? 4 : T > 1024 ? 2 : T > 512 ? 1 : 0;  // waves of the 8-step shape
 #define LRS_FUSED_DEER(E, NTF, OUT, REDO)                                                         \
   if (REDO)                                                                                        \
     hipLaunchKernelGGL((k_deer_redo<NW, RR, E, NTF>), grid, dim3(NW * kWave), 0, stream, w, u, y0, \
@@ -1853,15 +1855,21 @@ hipError_t launch_deer_fused(const float* w, const float* u, const float* y0, co
     hipLaunchKernelGGL((k_deer_fused<NW, RR, E, NTF>), grid, dim3(NW * kWave), 0, stream, w, u,   \
                        y0, h0, OUT, T, D, vec, k_max, seq_rec ? seq_delta : sets,                  \
                        seq_rec ? 1 : 0)
-#define LRS_FUSED_WIDE(NTF, OUT, REDO)                                             \
-  {                                                                                \
-    constexpr int NW = kDeerFused.nw, RR = kDeerFused.r;                           \
+#define LRS_FUSED_E8(NW_, NTF, OUT, REDO)                                           \
+  if (e8 == NW_) {                                                                 \
+    constexpr int NW = NW_, RR = kDeerFused.r;                                     \
     LRS_FUSED_DEER(8, NTF, OUT, REDO);                                             \
     return hipGetLastError();                                                      \
   }
+#define LRS_FUSED_WIDE(NTF, OUT, REDO)                                             \
+  {                                                                                \
+    LRS_FUSED_E8(kDeerFused.nw, NTF, OUT, REDO)                                    \
+    LRS_FUSED_E8(2, NTF, OUT, REDO)                                                \
+    LRS_FUSED_E8(1, NTF, OUT, REDO)                                                \
+  }
 #define LRS_FUSED_SHAPES(OUT, REDO)                                 \
   if (p.stream) {                                                   \
-    if (wide) LRS_FUSED_WIDE(true, OUT, REDO)                       \
+    if (e8) LRS_FUSED_WIDE(true, OUT, REDO)                         \
     LRS_SHAPE_CASE(1, 1, LRS_FUSED_DEER(4, true, OUT, REDO))        \
     LRS_SHAPE_CASE(2, 1, LRS_FUSED_DEER(4, true, OUT, REDO))        \
     LRS_SHAPE_CASE(4, 1, LRS_FUSED_DEER(4, true, OUT, REDO))        \
@@ -1869,7 +1877,7 @@ hipError_t launch_deer_fused(const float* w, const float* u, const float* y0, co
     LRS_SHAPE_CASE(8, 2, LRS_FUSED_DEER(4, true, OUT, REDO))        \
     LRS_SHAPE_CASE(4, 4, LRS_FUSED_DEER(4, true, OUT, REDO))        \
   } else {                                                          \
-    if (wide) LRS_FUSED_WIDE(false, OUT, REDO)                      \
+    if (e8) LRS_FUSED_WIDE(false, OUT, REDO)                        \
     LRS_SHAPE_CASE(1, 1, LRS_FUSED_DEER(4, false, OUT, REDO))       \
     LRS_SHAPE_CASE(2, 1, LRS_FUSED_DEER(4, false, OUT, REDO))       \
     LRS_SHAPE_CASE(4, 1, LRS_FUSED_DEER(4, false, OUT, REDO))       \
@@ -1882,6 +1890,7 @@ hipError_t launch_deer_fused(const float* w, const float* u, const float* y0, co
   auto redo = [&]() -> hipError_t { LRS_FUSED_SHAPES(h, 1) };
 #undef LRS_FUSED_SHAPES
 #undef LRS_FUSED_WIDE
+#undef LRS_FUSED_E8
 #undef LRS_FUSED_DEER
   hipError_t e = pass();
   if (e != hipSuccess) return e;

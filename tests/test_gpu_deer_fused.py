@@ -48,8 +48,12 @@ def both_paths(plan, x, B, D, T, eps, k_max, h_init=None, in_place=False):
     (2, 6, 8192, 1e-5, 6, True, True, True),         # warm start held in h, early stop
     (2, 6, 3000, 1e-5, 3, True, True, True),         # warm start in h, stops at K_max
     (1, 1, 1, 1e-5, 5, True, False, False),          # one step
-    (2, 3, 2048, 1e-5, 5, True, False, False),       # longest channel of 4 steps per lane
-    (2, 3, 2049, 1e-5, 5, True, True, False),        # first of 8 steps per lane, partial
+    (2, 3, 512, 1e-5, 5, True, False, False),        # longest channel of 4 steps per lane
+    (2, 3, 513, 1e-5, 5, True, True, False),         # one wave of 8 steps per lane, partial
+    (1, 4, 1024, 1e-5, 5, True, False, False),       # one wave of 2 rows of 8 steps, full
+    (2, 3, 1500, 1e-2, 6, True, False, False),       # two waves, partial, early stop
+    (2, 3, 2048, 1e-5, 5, True, False, False),       # two waves of 2 rows of 8 steps, full
+    (2, 3, 2049, 1e-5, 5, True, True, False),        # four waves, partial
     (2, 3, 4097, 1e-5, 5, True, False, False),       # second sub-chunk of one step
     (2, 3, 16384, 1e-5, 5, True, False, False),      # four sub-chunks (forced: few channels)
     (1, 5, 20001, 1e-5, 8, True, False, False),      # five sub-chunks, the last partial
