@@ -1,7 +1,8 @@
 """More entry points captured in a HIP graph: the fused forward + backward
 scan, the packed short-channel scans, the LSTM layer forward + backward, the
-asynchronous SRU-by-DEER solve and the asynchronous DEER solve with
-per-sequence stopping.  Every replay (interleaved with unrelated eager work
+asynchronous SRU-by-DEER solve, the asynchronous DEER solve with
+per-sequence stopping and the sequential tanh RNN (both buffer-resource forms:
+T % 4 == 0 and not).  Every replay (interleaved with unrelated eager work
 and host synchronisations, outputs poisoned with NaN before each) must
 reproduce the eager run: bit for bit where the association order is fixed,
 else within the parity bar (1e-5)."""
@@ -142,3 +143,14 @@ def test_bf16_scan_graph(layout, B, D, T):
         def fused():
             lrs.scan_fwd_bwd(a, b, g, h0, out=out, workspace=ws)
         replay_matches(fused, out, exact=True, tag=f"bf16 fused scan graph {B}x{D}x{T}")
+
+
+@pytest.mark.parametrize("T", [4096, 1001])
+def test_rnn_seq_graph(T):
+    B, D = 2, 100
+    x = I.deer_inputs(I.scaled(I.WORKLOADS["deer"], B=B, D=D, T=T, seed=12900 + T))
+    w = torch.from_numpy(x["w"]).to(DEV)
+    u = torch.from_numpy(x["u"].reshape(B, D, T)).to(DEV)
+    h0 = torch.from_numpy(np.full((B, D), 0.25, np.float32)).to(DEV)
+    out = (torch.empty_like(u),)
+    replay_matches(lambda: lrs.rnn_seq(w, u, h0, out=out[0]), out, True, f"rnn_seq T={T}")
