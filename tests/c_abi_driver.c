@@ -25,7 +25,8 @@
  *     in.bin : w (D floats), u (B*D*T floats), h0 (B*D floats)
  *     out.bin: h (B*D*T floats), iterations (int32), converged (int32),
  *              deltas (5 floats), then lrs_deer_eps_schedule(0..4 of 5,
- *              1e-4, 1e-6) (5 floats)
+ *              1e-4, 1e-6) (5 floats), then the sequential loop's h
+ *              (lrs_rnn_seq, B*D*T floats)
  *
  * Exit status 0 on success; 2 for a HIP error, 3 for an unexpected return
  * code of the library, 4 for a mismatch between lrs_scan_fwd and
@@ -210,7 +211,7 @@ static int run_deer(int64_t B, int64_t D, int64_t T, const char *in, const char 
   const int64_t C = B * D, N = C * T;
   const size_t nb = (size_t)N * sizeof(float), cb = (size_t)C * sizeof(float);
   const size_t wb = (size_t)D * sizeof(float);
-  const size_t ob = nb + 2 * sizeof(int32_t) + 2 * KMAX * sizeof(float);
+  const size_t ob = 2 * nb + 2 * sizeof(int32_t) + 2 * KMAX * sizeof(float);
   char *host = (char *)malloc(wb + nb + cb + ob);
   if (!host) return 1;
   if (read_file(in, host, wb + nb + cb)) return 1;
@@ -248,6 +249,13 @@ static int run_deer(int64_t B, int64_t D, int64_t T, const char *in, const char 
   float sched[KMAX];
   for (int i = 0; i < KMAX; ++i) sched[i] = lrs_deer_eps_schedule(i, KMAX, 1e-4f, 1e-6f);
   memcpy(o + nb + sizeof(rec) + sizeof(deltas), sched, sizeof(sched));
+  /* the sequential loop: a null input and an output on top of u are rejected */
+  LK(lrs_rnn_seq(dw, NULL, dh0, dh, B, D, T, st), LRS_ERR_INVALID_ARG);
+  LK(lrs_rnn_seq(dw, du, dh0, du, B, D, T, st), LRS_ERR_INVALID_ARG);
+  LK(lrs_rnn_seq(dw, du, dh0, dh, B, D, T, st), LRS_OK);
+  CK(hipStreamSynchronize(st));
+  CK(hipMemcpy(o + nb + sizeof(rec) + sizeof(deltas) + sizeof(sched), dh, nb,
+               hipMemcpyDeviceToHost));
   if (write_file(out, o, ob)) return 1;
 
   CK(hipFree(dws));

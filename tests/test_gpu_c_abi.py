@@ -121,3 +121,9 @@ def test_c_driver_deer_matches_oracle(tmp_path):
     # the schedule: log-linear from 1e-4 at step 0 to 1e-6 at step 4
     want = 1e-4 * (1e-6 / 1e-4) ** (np.arange(5) / 4)
     assert np.allclose(sched, want, rtol=1e-6)
+    # the sequential loop (lrs_rnn_seq) on the same inputs
+    seq = raw[4 * n + 48:8 * n + 48].view(np.float32).reshape(B, D, T)
+    ref_seq = oracle.rnn_seq(x["w"], x["u"].reshape(B, D, T), x["h0"].reshape(B, D))
+    es = relerr(seq, ref_seq)
+    log(f"c driver rnn_seq: h={es:.2e}")
+    assert es <= 1e-5
