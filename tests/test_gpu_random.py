@@ -130,6 +130,23 @@ def robust_count(deltas, eps):
 
 
 @cases(25)
+@given(B=st.integers(1, 4), D=st.integers(1, 300), T=steps, h0=st.booleans(), seed=seeds)
+def test_rnn_seq_random(B, D, T, h0, seed):
+    assume(B * D * T <= MAX_ELEMS)
+    w = I.scaled(I.WORKLOADS["deer"], B=B, D=D, T=T, seed=seed)
+    x = I.deer_inputs(w)
+    u = x["u"].reshape(B, D, T)
+    hz = (np.random.default_rng(seed).uniform(-1, 1, (B, D)).astype(np.float32) if h0
+          else None)
+    h = lrs.rnn_seq(torch.from_numpy(x["w"]).to(DEV), torch.from_numpy(u).to(DEV),
+                    None if hz is None else torch.from_numpy(hz).to(DEV))
+    torch.cuda.synchronize()
+    e = relerr(h.cpu().numpy(), oracle.rnn_seq(x["w"], u, hz))
+    log(f"random rnn_seq {B}x{D}x{T} h0={h0} seed={seed}: {e:.2e}")
+    assert e <= 1e-5
+
+
+@cases(25)
 @given(B=st.integers(1, 4), D=st.integers(1, 100), T=steps, k_max=st.integers(1, 8),
        eps=st.sampled_from([1e-3, 1e-5, 1e-6]), warm=st.booleans(), seed=seeds)
 def test_deer_random(B, D, T, k_max, eps, warm, seed):
