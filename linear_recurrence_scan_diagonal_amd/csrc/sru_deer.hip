@@ -475,7 +475,9 @@ __device__ __forceinline__ void sru_deer_fused_level(
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
     float xk = s.ck[tpar][lev - 1][off + k];
-    for (int w = 0; w < wid; ++w) xk = __builtin_fmaf(s.A[lp][w][off + k], xk, s.B[lp][w][off + k]);
+#pragma unroll
+    for (int w = 0; w < NW - 1; ++w)
+      if (w < wid) xk = __builtin_fmaf(s.A[lp][w][off + k], xk, s.B[lp][w][off + k]);
     x[k] = xk;
   }
   // every wave has read y0c (before the barrier above): the last wave now
