@@ -424,7 +424,9 @@ LRS_API size_t lrs_deer_workspace_bytes(int64_t B, int64_t D, int64_t T, int k_m
  * channel, one workgroup per channel (u read once, the last iterate
  * written once; the norms of every iteration are kept), and when the stop rule
  * ends the solve before k_max a second pass recomputes exactly that many
- * iterations; the record, the iteration count and the result (within fp32
+ * iterations (an early stop thus costs k_max plus that many iterations of
+ * work: a caller that expects one, as after a warm start, saves time by
+ * passing the count it expects as k_max); the record, the iteration count and the result (within fp32
  * rounding) are those of the one-launch-per-iteration path, which
  * lrs_deer_solve_ex with options->deer_fuse = 0 selects.  Solves that share a
  * workspace must be ordered. */
