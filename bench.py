@@ -323,6 +323,9 @@ def parse():
     p.add_argument("--deer-crossover", action="store_true",
                    help="time the DEER solve against the sequential loop (lrs_rnn_seq) over "
                         "channel counts and lengths and print a table, instead of the bench line")
+    p.add_argument("--deer-warm", action="store_true",
+                   help="time warm-started DEER solves (K_max 5 and K_max matched to the count) "
+                        "against the sequential loop at the DEER workload and print a table")
     p.add_argument("--summarize", metavar="DIR",
                    help="summarise rocprofv3 CSV output under DIR into profiles/ and exit")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -449,6 +452,9 @@ def main():
         return
     if args.deer_crossover:
         deer_crossover(args, np, torch, lrs, I, dev)
+        return
+    if args.deer_warm:
+        deer_warm(args, np, torch, lrs, I, dev)
         return
     line, w = measure(args, np, torch, lrs, I, dev)
     also = args.also
@@ -885,6 +891,49 @@ def deer_crossover(args, np, torch, lrs, I, dev):
               f"{t['per-iteration']:.1f} | {t_seq:.1f} | {t_seq / t['default']:.2f} |",
               flush=True)
         del u, h, hs, ws
+
+
+def deer_warm(args, np, torch, lrs, I, dev):
+    """DEER solves at the DEER workload's shape and distributions (drawn on the
+    device), cold (h_init = 0) and warm-started from the sequential solution of
+    the inputs perturbed by N(0, sigma^2), with K_max 5 and with K_max set to
+    the count the stop rule reaches, against the sequential loop; HIP events
+    over --steps calls each."""
+    dw = I.WORKLOADS["deer"]
+    B, D, T = dw.B, dw.D, dw.T
+    u = I.device_draw(dw.seed + T, dw.dists["u"], (B, D, T), dev)
+    wd = I.device_draw(dw.seed + 1, dw.dists["w"], (D,), dev)
+    h = torch.empty_like(u)
+    ws = torch.empty(lrs.load().lrs_deer_workspace_bytes(B, D, T, 5), dtype=torch.uint8,
+                     device=dev)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(args.steps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) * 1e3 / args.steps
+
+    t_seq = timed(lambda: lrs.rnn_seq(wd, u, None, out=h))
+    print(f"| start | K_max | iterations | solve us | sequential {t_seq:.1f} us / solve |")
+    print("|---|---|---|---|---|")
+    for sigma, k_max in ((0.0, 5), (0.01, 5), (0.01, 3), (0.01, 2), (0.05, 5), (0.05, 4)):
+        h_init = None
+        if sigma > 0:
+            pert = I.device_draw(dw.seed + 2, ("normal", 0.0, 1.0), (B, D, T), dev)
+            h_init = lrs.rnn_seq(wd, u + sigma * pert, None)
+            del pert
+        t = timed(lambda: lrs.deer_solve(wd, u, None, h_init, eps=1e-5, k_max=k_max, out=h,
+                                         workspace=ws, sync=False))
+        st = lrs.deer_stats(ws, k_max)
+        start = "cold" if sigma == 0 else f"warm, inputs perturbed by N(0, {sigma}^2)"
+        print(f"| {start} | {k_max} | {st['iters']} ({'converged' if st['converged'] else 'K_max'}) "
+              f"| {t:.1f} | {t_seq / t:.2f} |", flush=True)
 
 
 STREAM_REF_ELEMS = 1 << 26  # 256 MiB per fp32 operand
